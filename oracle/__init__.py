@@ -1,0 +1,177 @@
+"""fp64 CPU oracle for the gated delta rule forward pass (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no
+code with the HIP library or its binding, and the product path never imports
+it.
+
+The arithmetic lives in ``gdn_oracle.c`` (plain scalar double-precision loops,
+built with gcc by :func:`build`); this module only marshals numpy arrays into
+it.  ``chunkwise_ref`` holds the fp64 chunkwise (WY) form, used by the tests
+to pin the token recurrences by brute force.
+
+Functions (inputs are float32 numpy arrays holding the exact values the GPU
+receives; outputs are float64):
+
+* :func:`gdn_recurrent`            - O1, gated delta rule token by token.
+* :func:`deltaproduct_recurrent`   - O2, gated DeltaProduct token by token.
+* :func:`cam_prep`                 - O3, camera-branch prep per token.
+* :func:`frame_scan`               - O4, frame-synchronous numerator-only scan.
+* :func:`invert_se3`               - closed-form rigid-transform inverse.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libgdn_oracle.so")
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``gdn_oracle.c`` with gcc (-O2, OpenMP, no fast-math)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+           "-Wall", "-Wextra", "-o", _LIB_PATH + ".tmp", _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if (not os.path.exists(_LIB_PATH)
+            or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    D = ctypes.c_double
+    lib.oracle_gdn_recurrent.argtypes = [I, I, I, I, I, P, P, P, P, P, D, P, P, P, I]
+    lib.oracle_deltaproduct_recurrent.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, D, P, P, P, I]
+    lib.oracle_cam_prep.argtypes = [I, I, I, I, P, P, P, P, P, P, P, D, D, P, P, P, P, P, P, I]
+    lib.oracle_frame_scan.argtypes = [I, I, I, I, I, P, P, P, P, P, D, P, P, P, I]
+    lib.oracle_invert_se3.argtypes = [ctypes.c_long, P, P]
+    lib.oracle_invert_se3.restype = None
+    lib.oracle_max_threads.argtypes = []
+    for fn in (lib.oracle_gdn_recurrent, lib.oracle_deltaproduct_recurrent,
+               lib.oracle_cam_prep, lib.oracle_frame_scan, lib.oracle_max_threads):
+        fn.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def max_threads() -> int:
+    return _load().oracle_max_threads()
+
+
+def _f32(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name}: invalid arguments (rc={rc})")
+
+
+def gdn_recurrent(q, k, v, beta, g, scale=1.0, h0=None, nthreads=0):
+    """O1.  q,k (B,T,H,Dk); v (B,T,H,Dv); beta,g (B,T,H); h0 (B,H,Dk,Dv).
+
+    Returns (o (B,T,H,Dv), hT (B,H,Dk,Dv)) in float64.
+    """
+    q, k, v, beta, g, h0 = map(_f32, (q, k, v, beta, g, h0))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape[:3] == (B, T, H)
+    assert beta.shape == (B, T, H) and g.shape == (B, T, H)
+    assert h0 is None or h0.shape == (B, H, Dk, Dv)
+    o = np.zeros((B, T, H, Dv), np.float64)
+    hT = np.zeros((B, H, Dk, Dv), np.float64)
+    rc = _load().oracle_gdn_recurrent(B, T, H, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                      _ptr(g), float(scale), _ptr(h0), _ptr(o), _ptr(hT),
+                                      int(nthreads))
+    _check(rc, "gdn_recurrent")
+    return o, hT
+
+
+def deltaproduct_recurrent(q, k, v, beta, g, mask, scale=1.0, h0=None, nthreads=0):
+    """O2.  q,k (B,T,H,r*dk); v (B,T,H,Dv); beta (B,T,H,r); g (B,T,H);
+    mask (r,r); h0 (B,H,r*dk,Dv).  Returns (o, hT) in float64."""
+    q, k, v, beta, g, h0 = map(_f32, (q, k, v, beta, g, h0))
+    mask = np.ascontiguousarray(mask, dtype=np.float64)
+    B, T, H, K = q.shape
+    r = mask.shape[0]
+    assert mask.shape == (r, r) and K % r == 0
+    dk = K // r
+    Dv = v.shape[-1]
+    assert k.shape == q.shape and beta.shape == (B, T, H, r) and g.shape == (B, T, H)
+    assert h0 is None or h0.shape == (B, H, K, Dv)
+    o = np.zeros((B, T, H, Dv), np.float64)
+    hT = np.zeros((B, H, K, Dv), np.float64)
+    rc = _load().oracle_deltaproduct_recurrent(B, T, H, r, dk, Dv, _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(beta), _ptr(g), _ptr(mask), float(scale),
+                                               _ptr(h0), _ptr(o), _ptr(hT), int(nthreads))
+    _check(rc, "deltaproduct_recurrent")
+    return o, hT
+
+
+def cam_prep(qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin,
+             k_scale, eps, nthreads=0):
+    """O3.  qkv (B,N,3,H,D); weights (H*D,) or None; proj (B,N,4,4);
+    rope tables (N, D/2).  Returns dict of float64 arrays: q, k, v (B,H,N,D)
+    and k_pre_sq, k_post_sq, inflation_sq (B,H,N)."""
+    qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin = map(
+        _f32, (qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin))
+    B, N, three, H, D = qkv.shape
+    assert three == 3
+    assert proj_q.shape == (B, N, 4, 4) and proj_kv.shape == (B, N, 4, 4)
+    assert rope_cos.shape == (N, D // 2) and rope_sin.shape == (N, D // 2)
+    out = {name: np.zeros((B, H, N, D), np.float64) for name in ("q", "k", "v")}
+    for name in ("k_pre_sq", "k_post_sq", "inflation_sq"):
+        out[name] = np.zeros((B, H, N), np.float64)
+    rc = _load().oracle_cam_prep(B, N, H, D, _ptr(qkv), _ptr(q_norm_w), _ptr(k_norm_w),
+                                 _ptr(proj_q), _ptr(proj_kv), _ptr(rope_cos), _ptr(rope_sin),
+                                 float(k_scale), float(eps), _ptr(out["q"]), _ptr(out["k"]),
+                                 _ptr(out["v"]), _ptr(out["k_pre_sq"]), _ptr(out["k_post_sq"]),
+                                 _ptr(out["inflation_sq"]), int(nthreads))
+    _check(rc, "cam_prep")
+    return out
+
+
+def frame_scan(q, k, v, beta, g, F, scale=1.0, h0=None, nthreads=0):
+    """O4.  q,k,v (B,H,N,D) with N = F*S; beta (B,H,N); g (B,H,F) per frame;
+    h0 (B,H,D,D).  Returns (out (B,H,N,D), hT (B,H,D,D)) in float64."""
+    q, k, v, beta, g, h0 = map(_f32, (q, k, v, beta, g, h0))
+    B, H, N, D = q.shape
+    assert N % F == 0
+    S = N // F
+    assert beta.shape == (B, H, N) and g.shape == (B, H, F)
+    out = np.zeros((B, H, N, D), np.float64)
+    hT = np.zeros((B, H, D, D), np.float64)
+    rc = _load().oracle_frame_scan(B, H, F, S, D, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                   float(scale), _ptr(h0), _ptr(out), _ptr(hT), int(nthreads))
+    _check(rc, "frame_scan")
+    return out, hT
+
+
+def invert_se3(P):
+    """Closed-form inverse of rigid transforms; P (..., 4, 4) float64."""
+    P = np.ascontiguousarray(P, dtype=np.float64)
+    out = np.zeros_like(P)
+    n = P.size // 16
+    _load().oracle_invert_se3(n, _ptr(P), _ptr(out))
+    return out

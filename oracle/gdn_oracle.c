@@ -1,0 +1,372 @@
+/*
+ * Plain fp64 CPU oracle for the gated delta rule forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The product path
+ * (the HIP library and its Python binding) never calls, links or imports it,
+ * and it shares no code, header, table or helper with that path.
+ *
+ * Every routine is a slow, literal statement of what the method computes:
+ * scalar loops in double precision, no blocking, no SIMD intrinsics, no
+ * fast-math.  Inputs arrive as float32 arrays (a bf16 input is passed as the
+ * float32 that holds the same value exactly) and are widened to double on
+ * read.  Outputs are double.  The only parallelism is an OpenMP loop over
+ * independent (batch, head) pairs, or over independent tokens for the prep.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [cam]  Sana "fused_cam_gdn.py" - camera-branch prep and scan.
+ *   [dp]   msj19 "gated_deltaproduct" test.py - chunkwise gated DeltaProduct.
+ *   [cp]   Sana "fused_gdn_cp.py" - context-parallel wrappers (state
+ *          conventions in the module docstring).
+ *
+ * State convention throughout: S has shape (Dk, Dv), rows indexed by the key
+ * dimension and columns by the value dimension, as in [cam] _cam_scan_kernel
+ * (comment on the state layout) and [dp] gated_chunk_delta_rule_fwd_kernel_h.
+ * The read-out is o = scale * S^T q.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* O1: gated delta rule, token by token.                                    */
+/*                                                                          */
+/* For one (b, h), starting from S = h0 (or 0), for t = 0 .. T-1:           */
+/*   S <- exp(g_t) S                       (gate the carried state)         */
+/*   p <- S^T k_t                          (what the gated state predicts)  */
+/*   S <- S + beta_t k_t (v_t - p)^T       (delta-rule correction)          */
+/*   o_t <- scale * S^T q_t                (read-out after the update)      */
+/* and finally hT = S.  This is the recurrence                              */
+/*   S_t = exp(g_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T       */
+/* written in the (Dk, Dv) state convention.  Cites: [cam] _cam_scan_kernel */
+/* with one token per frame (decay, predict, correct, read out); [dp] the   */
+/* chunk kernels, whose token-level meaning this is for r = 1.              */
+/* Layouts: q,k (B,T,H,Dk); v (B,T,H,Dv); beta, g (B,T,H);                  */
+/* h0, hT (B,H,Dk,Dv); o (B,T,H,Dv).                                        */
+/* ------------------------------------------------------------------------ */
+int oracle_gdn_recurrent(int B, int T, int H, int Dk, int Dv,
+                         const float *q, const float *k, const float *v,
+                         const float *beta, const float *g, double scale,
+                         const float *h0, double *o, double *hT, int nthreads) {
+    if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return -1;
+    set_threads(nthreads);
+    int npairs = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < npairs; ++bh) {
+        int b = bh / H, h = bh % H;
+        double *S = (double *)calloc((size_t)Dk * Dv, sizeof(double));
+        double *p = (double *)malloc(sizeof(double) * (size_t)Dv);
+        if (h0)
+            for (int i = 0; i < Dk * Dv; ++i) S[i] = (double)h0[(size_t)bh * Dk * Dv + i];
+        for (int t = 0; t < T; ++t) {
+            size_t row = ((size_t)b * T + t) * H + h;
+            const float *qt = q + row * Dk, *kt = k + row * Dk, *vt = v + row * Dv;
+            double decay = exp((double)g[row]);
+            double bt = (double)beta[row];
+            for (int i = 0; i < Dk * Dv; ++i) S[i] *= decay;
+            for (int j = 0; j < Dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < Dk; ++i) acc += S[(size_t)i * Dv + j] * (double)kt[i];
+                p[j] = acc;
+            }
+            for (int i = 0; i < Dk; ++i) {
+                double ki = bt * (double)kt[i];
+                for (int j = 0; j < Dv; ++j) S[(size_t)i * Dv + j] += ki * ((double)vt[j] - p[j]);
+            }
+            for (int j = 0; j < Dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < Dk; ++i) acc += S[(size_t)i * Dv + j] * (double)qt[i];
+                o[row * Dv + j] = scale * acc;
+            }
+        }
+        if (hT)
+            for (int i = 0; i < Dk * Dv; ++i) hT[(size_t)bh * Dk * Dv + i] = S[i];
+        free(S);
+        free(p);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O2: gated DeltaProduct, token by token ([dp]).                           */
+/*                                                                          */
+/* The key of width K = r*dk is split into r sub-keys k_{t,a} (columns      */
+/* a*dk .. (a+1)*dk-1).  Step a of token t writes with the sub-key k_{t,a}  */
+/* into row block a of the state, and erases along the key                  */
+/*   e_{t,a} = sum_b M[a][b] E_b k_{t,b}                                    */
+/* (E_b places a dk-vector into row block b; M is the r x r step mask read  */
+/* as in gated_chunk_scaled_dot_kkt_fwd_kernel, where column b of the mask  */
+/* weights sub-key b for every step a).  Per token:                         */
+/*   P   <- exp(g_t) S                                                      */
+/*   p_a <- P^T e_{t,a}            for every a, all from the same P         */
+/*   S   <- P + sum_a beta_{t,a} E_a k_{t,a} (v_t - p_a)^T                  */
+/*   o_t <- scale * S^T q_t                                                 */
+/* Steps of one token do not see each other's writes: the intra-chunk      */
+/* matrix of [dp] is strictly lower triangular over tokens, so entries      */
+/* between two steps of one token are zero.                                 */
+/* Layouts: q,k (B,T,H,r*dk); v (B,T,H,Dv); beta (B,T,H,r); g (B,T,H);      */
+/* mask (r,r) row-major double; h0,hT (B,H,r*dk,Dv); o (B,T,H,Dv).          */
+/* ------------------------------------------------------------------------ */
+int oracle_deltaproduct_recurrent(int B, int T, int H, int r, int dk, int Dv,
+                                  const float *q, const float *k, const float *v,
+                                  const float *beta, const float *g,
+                                  const double *mask, double scale,
+                                  const float *h0, double *o, double *hT,
+                                  int nthreads) {
+    if (B < 0 || T < 0 || H < 0 || r <= 0 || dk <= 0 || Dv <= 0) return -1;
+    set_threads(nthreads);
+    int K = r * dk;
+    int npairs = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < npairs; ++bh) {
+        int b = bh / H, h = bh % H;
+        double *S = (double *)calloc((size_t)K * Dv, sizeof(double));
+        double *pa = (double *)malloc(sizeof(double) * (size_t)r * Dv);
+        double *e = (double *)malloc(sizeof(double) * (size_t)K);
+        if (h0)
+            for (int i = 0; i < K * Dv; ++i) S[i] = (double)h0[(size_t)bh * K * Dv + i];
+        for (int t = 0; t < T; ++t) {
+            size_t row = ((size_t)b * T + t) * H + h;
+            const float *qt = q + row * K, *kt = k + row * K, *vt = v + row * Dv;
+            const float *bt = beta + row * r;
+            double decay = exp((double)g[row]);
+            for (int i = 0; i < K * Dv; ++i) S[i] *= decay;
+            for (int a = 0; a < r; ++a) {
+                for (int bb = 0; bb < r; ++bb)
+                    for (int c = 0; c < dk; ++c)
+                        e[bb * dk + c] = mask[a * r + bb] * (double)kt[bb * dk + c];
+                for (int j = 0; j < Dv; ++j) {
+                    double acc = 0.0;
+                    for (int i = 0; i < K; ++i) acc += S[(size_t)i * Dv + j] * e[i];
+                    pa[(size_t)a * Dv + j] = acc;
+                }
+            }
+            for (int a = 0; a < r; ++a) {
+                double ba = (double)bt[a];
+                for (int c = 0; c < dk; ++c) {
+                    int i = a * dk + c;
+                    double ki = ba * (double)kt[i];
+                    for (int j = 0; j < Dv; ++j)
+                        S[(size_t)i * Dv + j] += ki * ((double)vt[j] - pa[(size_t)a * Dv + j]);
+                }
+            }
+            for (int j = 0; j < Dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < K; ++i) acc += S[(size_t)i * Dv + j] * (double)qt[i];
+                o[row * Dv + j] = scale * acc;
+            }
+        }
+        if (hT)
+            for (int i = 0; i < K * Dv; ++i) hT[(size_t)bh * K * Dv + i] = S[i];
+        free(S);
+        free(pa);
+        free(e);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O3: camera-branch prep, per token ([cam] _precompute_cam_inv_rms,        */
+/* _cam_prep_kernel, cam_prep_func).                                        */
+/*                                                                          */
+/* For token (b, n), with C = H*D channels:                                 */
+/*   inv_rms_x = 1 / sqrt(sum_c x_c^2 / C + eps)    for x in {q, k}         */
+/* and for every head h, on the D values of that head:                      */
+/*   q~ = relu(q * inv_rms_q * w_q)          (relu(x) = x if x > 0 else 0)  */
+/*   k~ = relu(k * inv_rms_k * w_k) * k_scale                               */
+/*   v~ = v                                  (no norm, relu or scale)       */
+/*   k_pre_sq = ||k~||^2 over all D                                         */
+/*   first D/2 values, in D/8 groups of 4:  y_g = P x_g  (4x4 times 4-vec), */
+/*      P = proj_q for q and proj_kv for k and v (per token)                */
+/*   second D/2 values (index r within that half):                          */
+/*      y[r] = x[r] * cos[n][r] + x[r ^ 1] * sin[n][r]                      */
+/*      (interleaved-pair RoPE tables, [cam] _prepare_ucpe_rope_tables)     */
+/*   k_post_sq = ||k_out||^2 over all D                                     */
+/*   inflation_sq = max(k_post_sq, 1e-12) / max(k_pre_sq, 1e-12)            */
+/* Layouts: qkv (B,N,3,H,D) (slot 0 = q, 1 = k, 2 = v); w (H*D) or NULL for */
+/* all-ones; proj (B,N,4,4) row-major; rope tables (N, D/2);                */
+/* outputs q,k,v (B,H,N,D); k_pre_sq, k_post_sq, inflation_sq (B,H,N).      */
+/* ------------------------------------------------------------------------ */
+static void prep_head(int D, const float *x, double inv_rms, const float *w,
+                      int relu, double post_scale, const float *P, const float *cs,
+                      const float *sn, double *xin, double *out) {
+    int half = D / 2;
+    for (int d = 0; d < D; ++d) {
+        double val = (double)x[d];
+        if (relu) {
+            val = val * inv_rms * (w ? (double)w[d] : 1.0);
+            val = val > 0.0 ? val : 0.0;
+            val *= post_scale;
+        }
+        xin[d] = val;
+    }
+    for (int grp = 0; grp < half / 4; ++grp)
+        for (int i = 0; i < 4; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < 4; ++j) acc += (double)P[i * 4 + j] * xin[grp * 4 + j];
+            out[grp * 4 + i] = acc;
+        }
+    for (int rr = 0; rr < half; ++rr)
+        out[half + rr] = xin[half + rr] * (double)cs[rr] + xin[half + (rr ^ 1)] * (double)sn[rr];
+}
+
+int oracle_cam_prep(int B, int N, int H, int D, const float *qkv,
+                    const float *q_norm_w, const float *k_norm_w,
+                    const float *proj_q, const float *proj_kv,
+                    const float *rope_cos, const float *rope_sin,
+                    double k_scale, double eps,
+                    double *q_out, double *k_out, double *v_out,
+                    double *k_pre_sq, double *k_post_sq, double *inflation_sq,
+                    int nthreads) {
+    if (B < 0 || N < 0 || H <= 0 || D <= 0 || D > 512 || (D % 8) != 0) return -1;
+    set_threads(nthreads);
+    int C = H * D, half = D / 2;
+    long ntok = (long)B * N;
+#pragma omp parallel for schedule(static)
+    for (long bn = 0; bn < ntok; ++bn) {
+        int b = (int)(bn / N), n = (int)(bn % N);
+        const float *tok = qkv + (size_t)bn * 3 * C;
+        const float *xq = tok, *xk = tok + C, *xv = tok + 2 * C;
+        double sq = 0.0, sk = 0.0;
+        for (int c = 0; c < C; ++c) {
+            sq += (double)xq[c] * (double)xq[c];
+            sk += (double)xk[c] * (double)xk[c];
+        }
+        double inv_q = 1.0 / sqrt(sq / C + eps);
+        double inv_k = 1.0 / sqrt(sk / C + eps);
+        const float *Pq = proj_q + (size_t)bn * 16, *Pkv = proj_kv + (size_t)bn * 16;
+        const float *cs = rope_cos + (size_t)n * half, *sn = rope_sin + (size_t)n * half;
+        double xin[512], out[512];
+        for (int h = 0; h < H; ++h) {
+            size_t obase = (((size_t)b * H + h) * N + n) * D;
+            size_t sbase = ((size_t)b * H + h) * N + n;
+            prep_head(D, xq + h * D, inv_q, q_norm_w ? q_norm_w + h * D : NULL, 1, 1.0, Pq, cs, sn, xin, out);
+            for (int d = 0; d < D; ++d) q_out[obase + d] = out[d];
+            prep_head(D, xk + h * D, inv_k, k_norm_w ? k_norm_w + h * D : NULL, 1, k_scale, Pkv, cs, sn, xin, out);
+            double pre = 0.0, post = 0.0;
+            for (int d = 0; d < D; ++d) {
+                pre += xin[d] * xin[d];
+                post += out[d] * out[d];
+                k_out[obase + d] = out[d];
+            }
+            k_pre_sq[sbase] = pre;
+            k_post_sq[sbase] = post;
+            if (inflation_sq)
+                inflation_sq[sbase] = (post > 1e-12 ? post : 1e-12) / (pre > 1e-12 ? pre : 1e-12);
+            prep_head(D, xv + h * D, 0.0, NULL, 0, 1.0, Pkv, cs, sn, xin, out);
+            for (int d = 0; d < D; ++d) v_out[obase + d] = out[d];
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O4: camera-branch numerator-only scan, frame-synchronous ([cam]          */
+/* _cam_scan_kernel, forward direction).                                    */
+/*                                                                          */
+/* Tokens come in F frames of S tokens.  For one (b, h), S = h0 (or 0), for */
+/* frame f = 0 .. F-1:                                                      */
+/*   P <- exp(g_f) S                       (one gate per frame)             */
+/*   S <- P + sum_{s in f} beta_s k_s (v_s - P^T k_s)^T                     */
+/*        (every token of the frame predicts from the same gated state P)   */
+/*   o_s <- scale * S^T q_s   for s in f   (read-out after the frame update)*/
+/* and hT = S after the last frame.  A loaded h0 is the state at the end of */
+/* a prefix; the first frame's gate applies to it ([cam] _cam_scan_kernel   */
+/* docstring on resuming from a saved state).                               */
+/* Layouts: q,k,v (B,H,F*S,D); beta (B,H,F*S); g (B,H,F); h0,hT (B,H,D,D);  */
+/* out (B,H,F*S,D).                                                         */
+/* ------------------------------------------------------------------------ */
+int oracle_frame_scan(int B, int H, int F, int S, int D,
+                      const float *q, const float *k, const float *v,
+                      const float *beta, const float *g, double scale,
+                      const float *h0, double *out, double *hT, int nthreads) {
+    if (B < 0 || H < 0 || F < 0 || S <= 0 || D <= 0) return -1;
+    set_threads(nthreads);
+    int npairs = B * H;
+    size_t N = (size_t)F * S;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < npairs; ++bh) {
+        double *St = (double *)calloc((size_t)D * D, sizeof(double));
+        double *P = (double *)malloc(sizeof(double) * (size_t)D * D);
+        double *p = (double *)malloc(sizeof(double) * (size_t)D);
+        if (h0)
+            for (int i = 0; i < D * D; ++i) St[i] = (double)h0[(size_t)bh * D * D + i];
+        for (int f = 0; f < F; ++f) {
+            double decay = exp((double)g[(size_t)bh * F + f]);
+            for (int i = 0; i < D * D; ++i) {
+                P[i] = decay * St[i];
+                St[i] = P[i];
+            }
+            for (int s = 0; s < S; ++s) {
+                size_t n = (size_t)f * S + s;
+                const float *ks = k + ((size_t)bh * N + n) * D, *vs = v + ((size_t)bh * N + n) * D;
+                double bs = (double)beta[(size_t)bh * N + n];
+                for (int j = 0; j < D; ++j) {
+                    double acc = 0.0;
+                    for (int i = 0; i < D; ++i) acc += P[(size_t)i * D + j] * (double)ks[i];
+                    p[j] = acc;
+                }
+                for (int i = 0; i < D; ++i) {
+                    double ki = bs * (double)ks[i];
+                    for (int j = 0; j < D; ++j) St[(size_t)i * D + j] += ki * ((double)vs[j] - p[j]);
+                }
+            }
+            for (int s = 0; s < S; ++s) {
+                size_t n = (size_t)f * S + s;
+                const float *qs = q + ((size_t)bh * N + n) * D;
+                for (int j = 0; j < D; ++j) {
+                    double acc = 0.0;
+                    for (int i = 0; i < D; ++i) acc += St[(size_t)i * D + j] * (double)qs[i];
+                    out[((size_t)bh * N + n) * D + j] = scale * acc;
+                }
+            }
+        }
+        if (hT)
+            for (int i = 0; i < D * D; ++i) hT[(size_t)bh * D * D + i] = St[i];
+        free(St);
+        free(P);
+        free(p);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Closed-form inverse of a rigid transform ([cam] _invert_SE3):            */
+/*   [R t; 0 1]^-1 = [R^T  -R^T t; 0 1].                                    */
+/* in, out: n row-major 4x4 matrices.                                       */
+/* ------------------------------------------------------------------------ */
+void oracle_invert_se3(long n, const double *in, double *out) {
+    for (long m = 0; m < n; ++m) {
+        const double *A = in + m * 16;
+        double *Y = out + m * 16;
+        for (int i = 0; i < 16; ++i) Y[i] = 0.0;
+        for (int i = 0; i < 3; ++i)
+            for (int j = 0; j < 3; ++j) Y[i * 4 + j] = A[j * 4 + i];
+        for (int i = 0; i < 3; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < 3; ++j) acc += Y[i * 4 + j] * A[j * 4 + 3];
+            Y[i * 4 + 3] = -acc;
+        }
+        Y[15] = 1.0;
+    }
+}
