@@ -1,0 +1,105 @@
+// C ABI: gdn_chunk_fwd and deltaproduct_chunk_fwd (argument checks and
+// dispatch to the chunk kernel instantiations).
+#include <math.h>
+
+#include "api_common.h"
+#include "chunk_dispatch.h"
+
+namespace {
+
+int chunk_common(const void *q, const void *k, const void *v, const float *beta,
+                 const float *log_decay, const float *step_mask, int r, float scale,
+                 const float *h0, float *hT, void *o, int B, int T, int H, int dk, int Dv,
+                 int chunk, int dtype, int out_dtype, void *workspace, size_t workspace_bytes,
+                 void *stream, const char *name) {
+    (void)workspace;
+    (void)workspace_bytes;   // this path needs no scratch memory
+    GDN_REQUIRE(B >= 0 && T >= 0 && H >= 0, GDN_EINVAL, "%s: negative size (B=%d T=%d H=%d)", name, B, T, H);
+    GDN_REQUIRE(dtype == GDN_DTYPE_F32 || dtype == GDN_DTYPE_BF16, GDN_EINVAL, "%s: unknown dtype %d", name, dtype);
+    GDN_REQUIRE(out_dtype == GDN_DTYPE_F32 || out_dtype == GDN_DTYPE_BF16, GDN_EINVAL,
+                "%s: unknown out_dtype %d", name, out_dtype);
+    GDN_REQUIRE(r == 1 || r == 2, GDN_EUNSUPPORTED, "%s: r=%d (supported: 1, 2)", name, r);
+    GDN_REQUIRE(dk == 16 || dk == 32 || dk == 64 || dk == 128 || dk == 256, GDN_EUNSUPPORTED,
+                "%s: key width %d (supported: 16, 32, 64, 128, 256)", name, dk);
+    GDN_REQUIRE(r * dk <= 256, GDN_EUNSUPPORTED, "%s: total key width r*dk=%d exceeds 256", name, r * dk);
+    GDN_REQUIRE(Dv > 0 && Dv % 16 == 0 && Dv <= 256, GDN_EUNSUPPORTED,
+                "%s: Dv=%d (must be a multiple of 16, at most 256)", name, Dv);
+    GDN_REQUIRE(chunk == 16 || chunk == 32 || chunk == 64, GDN_EUNSUPPORTED,
+                "%s: chunk=%d (supported: 16, 32, 64)", name, chunk);
+    GDN_REQUIRE(chunk * r <= 64, GDN_EUNSUPPORTED, "%s: chunk*r=%d exceeds 64", name, chunk * r);
+    GDN_REQUIRE(isfinite(scale), GDN_EINVAL, "%s: scale is not finite", name);
+    const size_t ntok = (size_t)B * T * H;
+    if (ntok > 0) {
+        GDN_REQUIRE(q && k && v && beta && log_decay && o, GDN_EINVAL, "%s: null tensor pointer", name);
+        GDN_REQUIRE(gdn::aligned(q, 16) && gdn::aligned(k, 16) && gdn::aligned(v, 16) && gdn::aligned(o, 16),
+                    GDN_EINVAL, "%s: q, k, v and o must be 16-byte aligned", name);
+        GDN_REQUIRE(gdn::aligned(beta, 4) && gdn::aligned(log_decay, 4), GDN_EINVAL,
+                    "%s: beta and log_decay must be 4-byte aligned", name);
+    }
+    GDN_REQUIRE(!h0 || gdn::aligned(h0, 4), GDN_EINVAL, "%s: h0 misaligned", name);
+    GDN_REQUIRE(!hT || gdn::aligned(hT, 4), GDN_EINVAL, "%s: hT misaligned", name);
+    GDN_REQUIRE(r == 1 || step_mask, GDN_EINVAL, "%s: step_mask is required for r=%d", name, r);
+    if ((size_t)B * H == 0) return GDN_OK;
+
+    gdn::ChunkArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.g = log_decay;
+    a.h0 = h0;
+    a.hT = hT;
+    a.o = o;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.Dv = Dv;
+    a.out_bf16 = out_dtype == GDN_DTYPE_BF16;
+    a.scale = scale;
+    for (int i = 0; i < 4; ++i) a.mask[i] = 0.f;
+    if (r == 1) {
+        a.mask[0] = step_mask ? step_mask[0] : 1.f;
+    } else {
+        for (int i = 0; i < r * r; ++i) {
+            GDN_REQUIRE(isfinite(step_mask[i]), GDN_EINVAL, "%s: step_mask[%d] is not finite", name, i);
+            a.mask[i] = step_mask[i];
+        }
+    }
+    const int KD = r * dk;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    bool found = false;
+    hipError_t e;
+    if (dtype == GDN_DTYPE_F32) e = gdn::dispatch_chunk_f32(KD, chunk, r, a, s, &found);
+    else if (r == 1) e = gdn::dispatch_chunk_bf16_r1(KD, chunk, a, s, &found);
+    else e = gdn::dispatch_chunk_bf16_r2(KD, chunk, a, s, &found);
+    GDN_REQUIRE(found, GDN_EUNSUPPORTED, "%s: no kernel for dtype=%s r=%d key width=%d chunk=%d", name,
+                dtype == GDN_DTYPE_F32 ? "f32" : "bf16", r, KD, chunk);
+    return gdn::check_hip(e, name);
+}
+
+}  // namespace
+
+extern "C" int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *beta,
+                             const float *log_decay, float scale, const float *h0, float *hT, void *o,
+                             int B, int T, int H, int Dk, int Dv, int chunk, int dtype, int out_dtype,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    return chunk_common(q, k, v, beta, log_decay, nullptr, 1, scale, h0, hT, o, B, T, H, Dk, Dv, chunk,
+                        dtype, out_dtype, workspace, workspace_bytes, stream, "gdn_chunk_fwd");
+}
+
+extern "C" size_t gdn_chunk_fwd_workspace_bytes(int, int, int, int, int, int, int) { return 0; }
+
+extern "C" int deltaproduct_chunk_fwd(const void *q, const void *k, const void *v, const float *beta,
+                                      const float *log_decay, const float *step_mask, int r, float scale,
+                                      const float *h0, float *hT, void *o, int B, int T, int H, int dk,
+                                      int Dv, int chunk, int dtype, int out_dtype, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+    if (dk > 128)
+        return gdn::set_error(GDN_EUNSUPPORTED, "deltaproduct_chunk_fwd: dk=%d (supported up to 128)", dk);
+    return chunk_common(q, k, v, beta, log_decay, step_mask, r, scale, h0, hT, o, B, T, H, dk, Dv, chunk,
+                        dtype, out_dtype, workspace, workspace_bytes, stream, "deltaproduct_chunk_fwd");
+}
+
+extern "C" size_t deltaproduct_chunk_fwd_workspace_bytes(int, int, int, int, int, int, int, int) {
+    return 0;
+}

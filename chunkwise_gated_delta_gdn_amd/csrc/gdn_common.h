@@ -1,0 +1,107 @@
+// Device helpers shared by the gfx950 kernels of libgdn: vector types, bf16
+// conversion and hi/lo splitting, and 16x16 MFMA tile products.
+//
+// MFMA lane layouts used throughout (wave64, gfx950):
+//   v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8*(l/16) + e] and
+//     B[8*(l/16) + e][l%16] for e < 8; the accumulator holds
+//     D[4*(l/16) + e][l%16] for e < 4.
+//   v_mfma_f32_16x16x16_bf16: lane l holds A[l%16][4*(l/16) + e] and
+//     B[4*(l/16) + e][l%16] for e < 4 (used for a k remainder of 16);
+//     same accumulator layout.
+//   v_mfma_f32_16x16x4_f32:   lane l holds A[l%16][l/16] and B[l/16][l%16];
+//     same accumulator layout.
+// Every operand buffer is stored "k-contiguous": A as [row][k] and B as
+// [col][k], so one lane's 8 bf16 values are one 16-byte LDS read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+struct alignas(16) U16x8 { u16 v[8]; };
+
+__device__ __forceinline__ u16 bf16_bits(float x) {
+    __bf16 h = (__bf16)x;                    // round to nearest even
+    return __builtin_bit_cast(u16, h);
+}
+__device__ __forceinline__ float bf16_to_f32(u16 b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+// x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi); x - hi is exact in fp32.
+__device__ __forceinline__ void split_bf16(float x, u16 &hi, u16 &lo) {
+    hi = bf16_bits(x);
+    lo = bf16_bits(x - bf16_to_f32(hi));
+}
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---- bf16 tile products ---------------------------------------------------
+// acc += A(16 x kdim) * B(kdim x 16); A at `a` with row stride lda (elements),
+// B stored transposed at `b` ([col][k]) with row stride ldb.  kdim % 16 == 0:
+// 32-wide steps, then one 16-wide step for a remainder of 16.
+__device__ __forceinline__ bf16x8 ld8(const u16 *p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const U16x8 *>(p));
+}
+__device__ __forceinline__ shortx4 ld4(const u16 *p) {
+    return *reinterpret_cast<const shortx4 *>(p);
+}
+
+// Split operands: (ahi + alo)(bhi + blo) ~= ahi bhi + ahi blo + alo bhi.
+// A null `alo` or `blo` means that operand is exact in bf16.
+__device__ __forceinline__ void mma_bf16_split(floatx4 &acc, const u16 *ahi, const u16 *alo, int lda,
+                                               const u16 *bhi, const u16 *blo, int ldb, int kdim) {
+    const int l = lane_id();
+    const int ra = (l & 15) * lda, rb = (l & 15) * ldb;
+    int kk = 0;
+    for (; kk + 32 <= kdim; kk += 32) {
+        const int oa = ra + kk + 8 * (l >> 4), ob = rb + kk + 8 * (l >> 4);
+        bf16x8 ah = ld8(ahi + oa), bh = ld8(bhi + ob);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+        if (blo) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, ld8(blo + ob), acc, 0, 0, 0);
+        if (alo) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld8(alo + oa), bh, acc, 0, 0, 0);
+    }
+    if (kk < kdim) {
+        const int oa = ra + kk + 4 * (l >> 4), ob = rb + kk + 4 * (l >> 4);
+        shortx4 ah = ld4(ahi + oa), bh = ld4(bhi + ob);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
+        if (blo) acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, ld4(blo + ob), acc, 0, 0, 0);
+        if (alo) acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ld4(alo + oa), bh, acc, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void mma_bf16(floatx4 &acc, const u16 *a, int lda, const u16 *b, int ldb,
+                                         int kdim) {
+    mma_bf16_split(acc, a, nullptr, lda, b, nullptr, ldb, kdim);
+}
+
+// ---- fp32 tile products ---------------------------------------------------
+// acc += A(16 x kdim) * B(kdim x 16), A [row][k] stride lda, B [col][k]
+// stride ldb, fp32, kdim % 4 == 0.
+__device__ __forceinline__ void mma_f32(floatx4 &acc, const float *a, int lda, const float *b, int ldb,
+                                        int kdim) {
+    const int l = lane_id();
+    const float *pa = a + (l & 15) * lda + (l >> 4);
+    const float *pb = b + (l & 15) * ldb + (l >> 4);
+    for (int kk = 0; kk < kdim; kk += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[kk], pb[kk], acc, 0, 0, 0);
+}
+
+// acc += A * B with B stored row-major ([k][col], stride ldb).
+__device__ __forceinline__ void mma_f32_bn(floatx4 &acc, const float *a, int lda, const float *b, int ldb,
+                                           int kdim) {
+    const int l = lane_id();
+    const float *pa = a + (l & 15) * lda + (l >> 4);
+    const float *pb = b + (l >> 4) * ldb + (l & 15);
+    for (int kk = 0; kk < kdim; kk += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[kk], pb[kk * ldb], acc, 0, 0, 0);
+}
+
+}  // namespace gdn

@@ -1,0 +1,228 @@
+"""Thin ctypes binding over the libgdn C ABI (``include/gdn.h``).
+
+Argument marshalling only: each function checks that the tensors sit on the
+GPU with the expected dtype and shape, allocates the outputs with torch, and
+passes raw device pointers and the current HIP stream to the library.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback.  Importing this module raises if ``libgdn.so`` has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_DTYPE_F32 = 0
+GDN_DTYPE_BF16 = 1
+
+# every symbol declared in include/gdn.h
+EXPORTS = (
+    "gdn_last_error", "gdn_abi_version",
+    "gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes",
+    "deltaproduct_chunk_fwd", "deltaproduct_chunk_fwd_workspace_bytes",
+    "gdn_recurrent_fwd", "gdn_recurrent_fwd_workspace_bytes",
+    "gdn_prep",
+)
+
+
+class GdnError(RuntimeError):
+    """A non-zero return code from the library, with its message."""
+
+    def __init__(self, name, code, msg):
+        super().__init__(f"{name} failed ({code}): {msg}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it first "
+                          "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_abi_version.restype = I
+    lib.gdn_chunk_fwd.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, I, P, Z, P]
+    lib.gdn_chunk_fwd.restype = I
+    lib.gdn_chunk_fwd_workspace_bytes.argtypes = [I] * 7
+    lib.gdn_chunk_fwd_workspace_bytes.restype = Z
+    lib.deltaproduct_chunk_fwd.argtypes = [P, P, P, P, P, P, I, F, P, P, P, I, I, I, I, I, I, I, I, P, Z, P]
+    lib.deltaproduct_chunk_fwd.restype = I
+    lib.deltaproduct_chunk_fwd_workspace_bytes.argtypes = [I] * 8
+    lib.deltaproduct_chunk_fwd_workspace_bytes.restype = Z
+    lib.gdn_recurrent_fwd.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, P, Z, P]
+    lib.gdn_recurrent_fwd.restype = I
+    lib.gdn_recurrent_fwd_workspace_bytes.argtypes = [I] * 6
+    lib.gdn_recurrent_fwd_workspace_bytes.restype = Z
+    lib.gdn_prep.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P, P, P, P, I, I, I, I, I, P]
+    lib.gdn_prep.restype = I
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _check(name, rc):
+    if rc != 0:
+        raise GdnError(name, rc, _lib.gdn_last_error().decode())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return GDN_DTYPE_F32
+    if t == torch.bfloat16:
+        return GDN_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("libgdn takes GPU tensors only")
+            if not t.is_contiguous():
+                raise ValueError("libgdn takes contiguous tensors only")
+
+
+def _f32(t, name):
+    if t is not None and t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(nbytes, device):
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def gdn_chunk_fwd(q, k, v, beta, log_decay, scale=1.0, h0=None, output_final_state=True,
+                  chunk=64, out_dtype=torch.float32):
+    """Chunkwise gated delta rule forward.  q,k (B,T,H,Dk); v (B,T,H,Dv);
+    beta, log_decay (B,T,H) fp32; h0 (B,H,Dk,Dv) fp32 or None.
+    Returns (o (B,T,H,Dv) out_dtype, hT (B,H,Dk,Dv) fp32 or None)."""
+    _dev(q, k, v, beta, log_decay, h0)
+    _f32(beta, "beta"), _f32(log_decay, "log_decay"), _f32(h0, "h0")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != (B, T, H) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v shapes or dtypes disagree")
+    if beta.shape != (B, T, H) or log_decay.shape != (B, T, H):
+        raise ValueError("beta and log_decay must be (B, T, H)")
+    if h0 is not None and h0.shape != (B, H, Dk, Dv):
+        raise ValueError("h0 must be (B, H, Dk, Dv)")
+    o = torch.empty((B, T, H, Dv), dtype=out_dtype, device=q.device)
+    hT = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device) if output_final_state else None
+    dt = _dtype_code(q.dtype)
+    ws, nws = _workspace(_lib.gdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, dt), q.device)
+    rc = _lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_decay), float(scale),
+                            _ptr(h0), _ptr(hT), _ptr(o), B, T, H, Dk, Dv, int(chunk), dt,
+                            _dtype_code(out_dtype), _ptr(ws), nws, _stream(q.device))
+    _check("gdn_chunk_fwd", rc)
+    return o, hT
+
+
+def deltaproduct_chunk_fwd(q, k, v, beta, log_decay, step_mask, scale=1.0, h0=None,
+                           output_final_state=True, chunk=32, out_dtype=torch.float32):
+    """Chunkwise gated DeltaProduct forward.  q,k (B,T,H,r*dk); v (B,T,H,Dv);
+    beta (B,T,H,r) fp32; log_decay (B,T,H) fp32; step_mask (r,r) host
+    sequence; h0 (B,H,r*dk,Dv) fp32 or None.  Returns (o, hT)."""
+    _dev(q, k, v, beta, log_decay, h0)
+    _f32(beta, "beta"), _f32(log_decay, "log_decay"), _f32(h0, "h0")
+    import numpy as np
+    m = np.ascontiguousarray(np.asarray(step_mask, dtype=np.float32))
+    r = m.shape[0]
+    if m.shape != (r, r):
+        raise ValueError("step_mask must be square")
+    B, T, H, K = q.shape
+    Dv = v.shape[-1]
+    if K % r:
+        raise ValueError("key width must be a multiple of r")
+    dk = K // r
+    if k.shape != q.shape or v.shape[:3] != (B, T, H) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v shapes or dtypes disagree")
+    if beta.shape != (B, T, H, r) or log_decay.shape != (B, T, H):
+        raise ValueError("beta must be (B,T,H,r) and log_decay (B,T,H)")
+    if h0 is not None and h0.shape != (B, H, K, Dv):
+        raise ValueError("h0 must be (B, H, r*dk, Dv)")
+    o = torch.empty((B, T, H, Dv), dtype=out_dtype, device=q.device)
+    hT = torch.empty((B, H, K, Dv), dtype=torch.float32, device=q.device) if output_final_state else None
+    dt = _dtype_code(q.dtype)
+    ws, nws = _workspace(_lib.deltaproduct_chunk_fwd_workspace_bytes(B, T, H, r, dk, Dv, chunk, dt), q.device)
+    rc = _lib.deltaproduct_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_decay),
+                                     m.ctypes.data_as(ctypes.c_void_p), r, float(scale), _ptr(h0),
+                                     _ptr(hT), _ptr(o), B, T, H, dk, Dv, int(chunk), dt,
+                                     _dtype_code(out_dtype), _ptr(ws), nws, _stream(q.device))
+    _check("deltaproduct_chunk_fwd", rc)
+    return o, hT
+
+
+def gdn_recurrent_fwd(q, k, v, beta, log_decay, scale=1.0, h0=None, output_final_state=True):
+    """Camera-branch frame-synchronous numerator-only scan.  q,k,v (B,H,N,D);
+    beta (B,H,N) fp32; log_decay (B,H,F) fp32 (one gate per frame, N = F*S);
+    h0 (B,H,D,D) fp32 or None.  Returns (out (B,H,N,D) fp32, hT or None)."""
+    _dev(q, k, v, beta, log_decay, h0)
+    _f32(beta, "beta"), _f32(log_decay, "log_decay"), _f32(h0, "h0")
+    B, H, N, D = q.shape
+    F = log_decay.shape[-1]
+    if F <= 0 or N % F:
+        raise ValueError("N must be a multiple of the number of frames")
+    S = N // F
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v shapes or dtypes disagree")
+    if beta.shape != (B, H, N) or log_decay.shape != (B, H, F):
+        raise ValueError("beta must be (B,H,N) and log_decay (B,H,F)")
+    out = torch.empty((B, H, N, D), dtype=torch.float32, device=q.device)
+    hT = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device) if output_final_state else None
+    dt = _dtype_code(q.dtype)
+    ws, nws = _workspace(_lib.gdn_recurrent_fwd_workspace_bytes(B, H, F, S, D, dt), q.device)
+    rc = _lib.gdn_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_decay), float(scale),
+                                _ptr(h0), _ptr(hT), _ptr(out), B, H, F, S, D, dt, _ptr(ws), nws,
+                                _stream(q.device))
+    _check("gdn_recurrent_fwd", rc)
+    return out, hT
+
+
+def gdn_prep(qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_scale, norm_eps,
+             want_inflation=True):
+    """Camera-branch prep.  qkv (B,N,3,H,D); norm weights (H*D,) fp32 or None;
+    proj (B,N,4,4) fp32; rope tables (N,D/2) fp32.  Returns a dict with q, k, v
+    (B,H,N,D) in qkv's dtype and k_pre_sq, k_post_sq, inflation_sq (B,H,N)."""
+    _dev(qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin)
+    for t, n in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w"), (proj_q, "proj_q"),
+                 (proj_kv, "proj_kv"), (rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+        _f32(t, n)
+    B, N, three, H, D = qkv.shape
+    if three != 3:
+        raise ValueError("qkv must be (B, N, 3, H, D)")
+    if proj_q.shape != (B, N, 4, 4) or proj_kv.shape != (B, N, 4, 4):
+        raise ValueError("projections must be (B, N, 4, 4)")
+    if rope_cos.shape != (N, D // 2) or rope_sin.shape != (N, D // 2):
+        raise ValueError("rope tables must be (N, D/2)")
+    dev = qkv.device
+    out = {n: torch.empty((B, H, N, D), dtype=qkv.dtype, device=dev) for n in ("q", "k", "v")}
+    for n in ("k_pre_sq", "k_post_sq"):
+        out[n] = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    out["inflation_sq"] = torch.empty((B, H, N), dtype=torch.float32, device=dev) if want_inflation else None
+    rc = _lib.gdn_prep(_ptr(qkv), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(proj_q), _ptr(proj_kv),
+                       _ptr(rope_cos), _ptr(rope_sin), float(k_scale), float(norm_eps),
+                       _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["k_pre_sq"]),
+                       _ptr(out["k_post_sq"]), _ptr(out["inflation_sq"]), B, N, H, D,
+                       _dtype_code(qkv.dtype), _stream(dev))
+    _check("gdn_prep", rc)
+    return out

@@ -1,0 +1,193 @@
+/*
+ * gdn.h - C ABI of the MI355X (gfx950) gated delta rule forward library.
+ *
+ * Four operations, each a forward pass over device-resident tensors:
+ *
+ *   gdn_chunk_fwd           chunkwise gated delta rule (r = 1)
+ *   deltaproduct_chunk_fwd  chunkwise gated DeltaProduct (r sub-keys per token)
+ *   gdn_recurrent_fwd       camera-branch numerator-only scan, frame-synchronous
+ *   gdn_prep                camera-branch per-token prep (RMSNorm over all
+ *                           channels, ReLU, K-scale, UCPE 4x4, RoPE, ||k||^2)
+ *
+ * Sources (web pages, cited by title and section):
+ *   [dp]  msj19 "gated_deltaproduct" test.py: gated_chunk_scaled_dot_kkt_fwd,
+ *         solve_tril, gated_fwd_recompute_w_u, gated_chunk_fwd_h_fn,
+ *         gated_chunk_fwd_o_fn.
+ *   [cam] Sana "fused_cam_gdn.py": cam_prep_func, _cam_prep_kernel,
+ *         cam_scan_func, _cam_scan_kernel.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named as tensors are DEVICE pointers to dense row-major arrays
+ *   with the shapes given below (last index fastest).  The only host pointer
+ *   is `step_mask` of deltaproduct_chunk_fwd.
+ * - `dtype` selects the element type of the q/k/v (and qkv) inputs:
+ *   GDN_DTYPE_F32 or GDN_DTYPE_BF16.  Gates (beta, log_decay), states
+ *   (h0, hT) and the prep's projection and RoPE tables are always float32.
+ * - `out_dtype` selects the element type of the chunk outputs o.
+ * - The state S of one (batch, head) has shape (Dk, Dv): rows follow the key
+ *   dimension, columns the value dimension.  The read-out is o = scale*S^T q.
+ * - h0 (initial state) may be NULL (zero state); hT (final state) may be
+ *   NULL (not stored).  h0 is the state at the end of a prefix: the first
+ *   token's (or frame's) gate applies to it, so running [0,T1) then [T1,T)
+ *   with h0 = hT of the first call equals one call over [0,T).
+ * - Ownership: all buffers belong to the caller.  The library keeps no
+ *   pointer after the call returns, allocates no memory, and enqueues all
+ *   work on `stream` (a hipStream_t passed as void*, NULL = default stream);
+ *   the caller keeps buffers alive until that stream has finished.
+ * - Work space: entry points that need scratch device memory take
+ *   (workspace, workspace_bytes); the matching *_workspace_bytes() query
+ *   returns the size needed (0 means workspace may be NULL).
+ * - Errors: every entry point validates all arguments before launching
+ *   anything and returns GDN_OK (0) or a negative GDN_E* code; nothing is
+ *   launched on error.  gdn_last_error() returns a message for the last
+ *   failing call on the calling thread.  No exception or abort crosses the
+ *   ABI.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    GDN_OK = 0,
+    GDN_EINVAL = -1,        /* null pointer, bad size, misaligned pointer      */
+    GDN_EUNSUPPORTED = -2,  /* a size or option outside the supported set      */
+    GDN_EWORKSPACE = -3,    /* workspace smaller than *_workspace_bytes()      */
+    GDN_EHIP = -4           /* HIP launch or runtime failure                   */
+};
+
+enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 };
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char *gdn_last_error(void);
+
+/* ABI version; bumped on any incompatible change. */
+int gdn_abi_version(void);
+
+/*
+ * gdn_chunk_fwd - chunkwise gated delta rule forward.
+ *
+ * Per (b, h) and token t, with S = h0 (or 0):
+ *   S_t = exp(g_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ *   o_t = scale * S_t^T q_t,          hT = S_T.
+ * Computed chunk by chunk ([dp] the chunk kernels with r = 1): chunk-local
+ * cumsum of g, the strictly-lower intra-chunk matrix
+ * A[t,s] = beta_t (k_t . k_s) exp(G_t - G_s), T = (I + A)^-1 from 16x16
+ * diagonal blocks and exact block merges, the WY form, the sequential
+ * inter-chunk state pass and the output product.
+ *
+ *   q, k      (B, T, H, Dk)  dtype
+ *   v         (B, T, H, Dv)  dtype
+ *   beta      (B, T, H)      float32
+ *   log_decay (B, T, H)      float32, g_t (gate exp(g_t); normally <= 0)
+ *   h0, hT    (B, H, Dk, Dv) float32, nullable
+ *   o         (B, T, H, Dv)  out_dtype
+ * Supported: Dk, Dv in {16, 32, 64, 128, 256} with Dk <= 256 and Dv a
+ * multiple of 16; chunk in {16, 32, 64}; any T >= 0 (a last chunk shorter
+ * than `chunk` is handled).  16-byte aligned tensor pointers.
+ */
+int gdn_chunk_fwd(const void *q, const void *k, const void *v,
+                  const float *beta, const float *log_decay, float scale,
+                  const float *h0, float *hT, void *o,
+                  int B, int T, int H, int Dk, int Dv, int chunk,
+                  int dtype, int out_dtype,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
+                                     int dtype);
+
+/*
+ * deltaproduct_chunk_fwd - chunkwise gated DeltaProduct forward ([dp]).
+ *
+ * The key of width K = r*dk is split into r sub-keys k_{t,a}.  Step a of
+ * token t writes with k_{t,a} into row block a of the (K, Dv) state and
+ * erases along e_{t,a} = sum_b M[a][b] k_{t,b} (placed in row block b).
+ * Per token: P = exp(g_t) S; p_a = P^T e_{t,a} for all a from the same P;
+ * S = P + sum_a beta_{t,a} E_a k_{t,a} (v_t - p_a)^T; o_t = scale S^T q_t.
+ * With r = 1 and M = [[1]] this is gdn_chunk_fwd.
+ *
+ *   q, k       (B, T, H, r*dk) dtype
+ *   v          (B, T, H, Dv)   dtype
+ *   beta       (B, T, H, r)    float32, one per step
+ *   log_decay  (B, T, H)       float32
+ *   step_mask  (r, r)          float32 HOST array, row-major M[a][b]
+ *   h0, hT     (B, H, r*dk, Dv) float32, nullable
+ *   o          (B, T, H, Dv)   out_dtype
+ * Supported: r in {1, 2}; dk in {16, 32, 64, 128}; r*dk <= 256; Dv a
+ * multiple of 16 up to 256; chunk*r <= 64 with chunk in {16, 32, 64}.
+ */
+int deltaproduct_chunk_fwd(const void *q, const void *k, const void *v,
+                           const float *beta, const float *log_decay,
+                           const float *step_mask, int r, float scale,
+                           const float *h0, float *hT, void *o,
+                           int B, int T, int H, int dk, int Dv, int chunk,
+                           int dtype, int out_dtype,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+size_t deltaproduct_chunk_fwd_workspace_bytes(int B, int T, int H, int r, int dk, int Dv,
+                                              int chunk, int dtype);
+
+/*
+ * gdn_recurrent_fwd - camera-branch numerator-only scan ([cam]
+ * _cam_scan_kernel, forward direction), frame-synchronous.
+ *
+ * Tokens come in F frames of S tokens (N = F*S).  Per (b, h), with S = h0:
+ *   P = exp(g_f) S_{f-1};
+ *   S_f = P + sum_{s in f} beta_s k_s (v_s - P^T k_s)^T
+ *       (every token of the frame predicts from the same gated state P);
+ *   out_s = scale * S_f^T q_s for s in f;    hT = S_F.
+ * With S = 1 this is the token-level gated delta rule.
+ *
+ *   q, k, v    (B, H, N, D)  dtype   (the layout gdn_prep writes)
+ *   beta       (B, H, N)     float32
+ *   log_decay  (B, H, F)     float32, one gate per frame
+ *   h0, hT     (B, H, D, D)  float32, nullable
+ *   out        (B, H, N, D)  float32
+ * Supported: D in {16, 32, 64, 128}; F >= 1; S >= 1.
+ */
+int gdn_recurrent_fwd(const void *q, const void *k, const void *v,
+                      const float *beta, const float *log_decay, float scale,
+                      const float *h0, float *hT, float *out,
+                      int B, int H, int F, int S, int D, int dtype,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+size_t gdn_recurrent_fwd_workspace_bytes(int B, int H, int F, int S, int D, int dtype);
+
+/*
+ * gdn_prep - camera-branch prep ([cam] cam_prep_func, _cam_prep_kernel),
+ * one pass over the packed projection.
+ *
+ * For token (b, n) with C = H*D channels: inv_rms_x = 1/sqrt(mean_c x_c^2
+ * + norm_eps) for x in {q, k}; per head: q~ = relu(q inv_rms_q w_q),
+ * k~ = relu(k inv_rms_k w_k) * k_scale, v~ = v; k_pre_sq = ||k~||^2; first
+ * D/2 values in groups of 4: y = P x (P = proj_q for q, proj_kv for k, v);
+ * second D/2 values: y[d] = x[d] rope_cos[n][d] + x[d^1] rope_sin[n][d];
+ * k_post_sq = ||k_out||^2; inflation_sq = max(post,1e-12)/max(pre,1e-12).
+ *
+ *   qkv              (B, N, 3, H, D) dtype (slot 0 q, 1 k, 2 v)
+ *   q_norm_w, k_norm_w (H*D)         float32, nullable (= all ones)
+ *   proj_q, proj_kv  (B, N, 4, 4)    float32, row-major per token
+ *   rope_cos, rope_sin (N, D/2)      float32, interleaved-pair tables
+ *   q_out, k_out, v_out (B, H, N, D) dtype
+ *   k_pre_sq, k_post_sq (B, H, N)    float32
+ *   inflation_sq     (B, H, N)       float32, nullable (not stored)
+ * Supported: D in {16, 32, 64, 128}; H*D <= 4096.
+ */
+int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_norm_w,
+             const float *proj_q, const float *proj_kv,
+             const float *rope_cos, const float *rope_sin,
+             float k_scale, float norm_eps,
+             void *q_out, void *k_out, void *v_out,
+             float *k_pre_sq, float *k_post_sq, float *inflation_sq,
+             int B, int N, int H, int D, int dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

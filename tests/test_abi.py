@@ -1,0 +1,86 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/gdn.h declares, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+LIB = os.path.join(ROOT, "chunkwise_gated_delta_gdn_amd", "libgdn.so")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_\w+|deltaproduct_\w+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libgdn.so is not built: run __graft_entry__.build()")
+    from chunkwise_gated_delta_gdn_amd import gdn
+    return gdn.lib()
+
+
+def test_header_declares_the_four_operations():
+    names = _declared()
+    for op in ("gdn_prep", "gdn_chunk_fwd", "gdn_recurrent_fwd", "deltaproduct_chunk_fwd"):
+        assert op in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from chunkwise_gated_delta_gdn_amd import gdn
+    declared = _declared()
+    assert sorted(gdn.EXPORTS) == declared
+    raw = ctypes.CDLL(LIB)
+    for name in declared:
+        assert hasattr(raw, name), name
+
+
+def test_abi_version(lib):
+    assert lib.gdn_abi_version() == 1
+
+
+def _chunk(lib, **kw):
+    a = dict(q=None, k=None, v=None, beta=None, g=None, scale=1.0, h0=None, hT=None, o=None,
+             B=1, T=8, H=1, Dk=64, Dv=64, chunk=64, dtype=1, out_dtype=0)
+    a.update(kw)
+    return lib.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["beta"], a["g"], a["scale"], a["h0"], a["hT"],
+                             a["o"], a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["chunk"], a["dtype"],
+                             a["out_dtype"], None, 0, None)
+
+
+def test_chunk_rejects_bad_arguments_without_launching(lib):
+    fake = ctypes.c_void_p(4096)        # aligned, never dereferenced: validation fails first
+    assert _chunk(lib, B=-1) == -1
+    assert _chunk(lib) == -1                                     # null pointers
+    assert b"null" in lib.gdn_last_error()
+    assert _chunk(lib, Dk=48) == -2                              # unsupported key width
+    assert _chunk(lib, Dv=24) == -2
+    assert _chunk(lib, chunk=128) == -2
+    assert _chunk(lib, dtype=7) == -1
+    assert _chunk(lib, out_dtype=3) == -1
+    assert _chunk(lib, q=ctypes.c_void_p(4098), k=fake, v=fake, beta=fake, g=fake, o=fake) == -1
+    assert b"aligned" in lib.gdn_last_error()
+    assert _chunk(lib, scale=float("nan"), q=fake, k=fake, v=fake, beta=fake, g=fake, o=fake) == -1
+    # an empty problem is valid and launches nothing
+    assert _chunk(lib, B=0) == 0
+    assert _chunk(lib, H=0) == 0
+
+
+def test_deltaproduct_rejects_bad_arguments(lib):
+    fake = ctypes.c_void_p(4096)
+    mask = (ctypes.c_float * 4)(1, 0, 1, 1)
+
+    def call(r=2, dk=128, chunk=32, m=mask, dtype=1):
+        return lib.deltaproduct_chunk_fwd(fake, fake, fake, fake, fake, m, r, 1.0, None, None, fake,
+                                          1, 8, 1, dk, 128, chunk, dtype, 0, None, 0, None)
+    assert call(r=3) == -2
+    assert call(chunk=64) == -2                                  # chunk*r > 64
+    assert call(dk=256) == -2
+    assert call(m=None) == -1
+    bad = (ctypes.c_float * 4)(1, 0, float("inf"), 1)
+    assert call(m=bad) == -1
