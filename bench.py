@@ -1,0 +1,176 @@
+"""Benchmark: chunkwise gated delta rule forward on one MI355X.
+
+One step = one gdn_chunk_fwd call over the "gdn" workload (B=2, H=16,
+T=4096, Dk=Dv=128, chunk 64, bf16 q/k/v, fp32 gates, fp32 state and output):
+chunk-local cumsum, the intra-chunk beta*K*K^T with decay mask, the (I+A)^-1
+solve, the WY form, the sequential inter-chunk state pass and the output
+product - the whole hot path, in two kernel launches (the parallel per-chunk
+solve, then the state pass with the output).  Inputs are generated once,
+copied to HBM, and stay resident; only the launches are timed.
+
+Prints ONE JSON line (rank 0) with the metric, a roofline object for one
+gdn_chunk_fwd call (both kernels, timed live with HIP events on the launch
+stream), and the fp64 CPU oracle timed on the host as a reported baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+KERNEL_SOURCES = ("chunkwise_gated_delta_gdn_amd/csrc/chunk_kernels.h",
+                  "chunkwise_gated_delta_gdn_amd/csrc/gdn_common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_kernel_gdn_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(B, T, H, Dk, Dv, C, in_bytes=2, out_bytes=4, with_h0=False):
+    """Bytes: every input read once, every output written once.  FLOPs per
+    (token, head): 10*C*d + 6*d^2 + 2*C^2/3 (five C x C x d tile products,
+    three d x d state products, the triangular solve), d = Dk = Dv."""
+    d = Dk
+    nbytes = B * T * H * (2 * Dk + Dv) * in_bytes          # q, k, v
+    nbytes += B * T * H * 2 * 4                             # beta, log_decay
+    nbytes += B * T * H * Dv * out_bytes                    # o
+    nbytes += B * H * Dk * Dv * 4 * (2 if with_h0 else 1)   # hT (and h0)
+    flops = B * T * H * (10 * C * d + 6 * d * d + 2 * C * C / 3)
+    return nbytes, flops
+
+
+def measured_traffic(per_launch_expected_hash):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE and
+    WRITE_SIZE counters, or None if absent or taken on other kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != per_launch_expected_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(d, B, T, H, budget_s=20.0):
+    """Time the fp64 oracle (as it stands) on host cores over a bounded
+    sample of heads of the same workload; scale to tokens/s of the whole."""
+    import numpy as np
+    import oracle
+    threads = min(os.cpu_count() or 1, 16)
+    # estimate: ~7*d^2 fp64 FLOP per token-head at ~1 GFLOP/s per thread
+    per_head = 7 * d["q"].shape[-1] ** 2 * B * T / 1e9
+    nheads = int(max(1, min(H, budget_s * threads / max(per_head, 1e-9))))
+    hs = list(range(nheads))
+    sub = {n: np.ascontiguousarray(d[n][:, :, hs]) for n in ("q", "k", "v", "beta", "g")}
+    t0 = time.perf_counter()
+    oracle.gdn_recurrent(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"], 1.0, None,
+                         nthreads=threads)
+    dt = time.perf_counter() - t0
+    used = min(threads, B * nheads)
+    # tokens/s of the whole workload: B*T tokens need H heads of work
+    value = B * T * (nheads / H) / dt
+    return {"value": value, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"fp64 token recurrence on heads 0..{nheads - 1} of {H} (all B={B}, T={T}), "
+                      f"{dt:.2f} s wall on {used} threads, scaled by {nheads}/{H}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(how the path would shard is described in DESIGN.md)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from chunkwise_gated_delta_gdn_amd import gdn, inputs
+
+    dev = torch.device("cuda:0")
+    wl = inputs.WORKLOADS["gdn"]
+    B, T, H, Dk, Dv, C = wl["B"], wl["T"], wl["H"], wl["Dk"], wl["Dv"], wl["chunk"]
+    d = inputs.workload_inputs("gdn")
+    q, k, v = (torch.from_numpy(d[n]).to(dev).to(torch.bfloat16) for n in ("q", "k", "v"))
+    beta = torch.from_numpy(d["beta"]).to(dev)
+    g = torch.from_numpy(d["g"]).to(dev)
+    torch.cuda.synchronize()
+
+    def step():
+        return gdn.gdn_chunk_fwd(q, k, v, beta, g, 1.0, None, chunk=C, out_dtype=torch.float32)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    kernel_ms = float(np.mean(kern_ms))
+
+    nbytes, flops = algorithmic_work(B, T, H, Dk, Dv, C)
+    achieved_gbs = nbytes / (kernel_ms * 1e-3) / 1e9
+    traffic = measured_traffic(kernel_source_hash())
+    rec = {
+        "metric": "tokens/sec of chunkwise gated-delta fwd (B*T/s) at H=16, D=128",
+        "value": B * T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta sigmoid(N(0,1)), "
+                "log-decay logsigmoid(N(2,0.5)))",
+        "config": {"workload": "gdn: B=2 H=16 T=4096 Dk=Dv=128 chunk=64, bf16 q/k/v, fp32 "
+                               "gates/state/output, h0=0",
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": Dk, "chunk": C,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "gdn_chunk_fwd = chunk_solve_kernel + chunk_chain_kernel "
+                               "<bf16, KD=128, C=64, R=1>",
+                     "kernel_ms": kernel_ms, "algorithmic_bytes": nbytes,
+                     "algorithmic_flops": flops,
+                     "mfma_tflops": flops / (kernel_ms * 1e-3) / 1e12,
+                     "mfma_frac": flops / (kernel_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(d, B, T, H)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,13 +7,18 @@
 
 namespace {
 
+bool find_impl(int dtype, int r, int KD, int chunk, gdn::ChunkImpl *impl) {
+    if (dtype == GDN_DTYPE_F32) return gdn::find_chunk_f32(KD, chunk, r, impl);
+    if (r == 1) return gdn::find_chunk_bf16_r1(KD, chunk, impl);
+    if (r == 2) return gdn::find_chunk_bf16_r2(KD, chunk, impl);
+    return false;
+}
+
 int chunk_common(const void *q, const void *k, const void *v, const float *beta,
                  const float *log_decay, const float *step_mask, int r, float scale,
                  const float *h0, float *hT, void *o, int B, int T, int H, int dk, int Dv,
                  int chunk, int dtype, int out_dtype, void *workspace, size_t workspace_bytes,
                  void *stream, const char *name) {
-    (void)workspace;
-    (void)workspace_bytes;   // this path needs no scratch memory
     GDN_REQUIRE(B >= 0 && T >= 0 && H >= 0, GDN_EINVAL, "%s: negative size (B=%d T=%d H=%d)", name, B, T, H);
     GDN_REQUIRE(dtype == GDN_DTYPE_F32 || dtype == GDN_DTYPE_BF16, GDN_EINVAL, "%s: unknown dtype %d", name, dtype);
     GDN_REQUIRE(out_dtype == GDN_DTYPE_F32 || out_dtype == GDN_DTYPE_BF16, GDN_EINVAL,
@@ -39,7 +44,17 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
     GDN_REQUIRE(!h0 || gdn::aligned(h0, 4), GDN_EINVAL, "%s: h0 misaligned", name);
     GDN_REQUIRE(!hT || gdn::aligned(hT, 4), GDN_EINVAL, "%s: hT misaligned", name);
     GDN_REQUIRE(r == 1 || step_mask, GDN_EINVAL, "%s: step_mask is required for r=%d", name, r);
+    const int KD = r * dk;
+    gdn::ChunkImpl impl;
+    GDN_REQUIRE(find_impl(dtype, r, KD, chunk, &impl), GDN_EUNSUPPORTED,
+                "%s: no kernel for dtype=%s r=%d key width=%d chunk=%d", name,
+                dtype == GDN_DTYPE_F32 ? "f32" : "bf16", r, KD, chunk);
     if ((size_t)B * H == 0) return GDN_OK;
+    const size_t need = impl.workspace(B, T, H);
+    GDN_REQUIRE(workspace_bytes >= need, GDN_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", name,
+                workspace_bytes, need);
+    GDN_REQUIRE(need == 0 || (workspace && gdn::aligned(workspace, 16)), GDN_EINVAL,
+                "%s: workspace must be a 16-byte aligned device pointer", name);
 
     gdn::ChunkArgs a;
     a.q = q;
@@ -50,6 +65,7 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
     a.h0 = h0;
     a.hT = hT;
     a.o = o;
+    a.tmat = workspace;
     a.B = B;
     a.T = T;
     a.H = H;
@@ -65,16 +81,7 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
             a.mask[i] = step_mask[i];
         }
     }
-    const int KD = r * dk;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    bool found = false;
-    hipError_t e;
-    if (dtype == GDN_DTYPE_F32) e = gdn::dispatch_chunk_f32(KD, chunk, r, a, s, &found);
-    else if (r == 1) e = gdn::dispatch_chunk_bf16_r1(KD, chunk, a, s, &found);
-    else e = gdn::dispatch_chunk_bf16_r2(KD, chunk, a, s, &found);
-    GDN_REQUIRE(found, GDN_EUNSUPPORTED, "%s: no kernel for dtype=%s r=%d key width=%d chunk=%d", name,
-                dtype == GDN_DTYPE_F32 ? "f32" : "bf16", r, KD, chunk);
-    return gdn::check_hip(e, name);
+    return gdn::check_hip(impl.launch(a, reinterpret_cast<hipStream_t>(stream)), name);
 }
 
 }  // namespace
@@ -87,7 +94,12 @@ extern "C" int gdn_chunk_fwd(const void *q, const void *k, const void *v, const 
                         dtype, out_dtype, workspace, workspace_bytes, stream, "gdn_chunk_fwd");
 }
 
-extern "C" size_t gdn_chunk_fwd_workspace_bytes(int, int, int, int, int, int, int) { return 0; }
+extern "C" size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, int dtype) {
+    (void)Dv;
+    gdn::ChunkImpl impl;
+    if (B < 0 || T < 0 || H < 0 || !find_impl(dtype, 1, Dk, chunk, &impl)) return 0;
+    return impl.workspace(B, T, H);
+}
 
 extern "C" int deltaproduct_chunk_fwd(const void *q, const void *k, const void *v, const float *beta,
                                       const float *log_decay, const float *step_mask, int r, float scale,
@@ -100,6 +112,10 @@ extern "C" int deltaproduct_chunk_fwd(const void *q, const void *k, const void *
                         dtype, out_dtype, workspace, workspace_bytes, stream, "deltaproduct_chunk_fwd");
 }
 
-extern "C" size_t deltaproduct_chunk_fwd_workspace_bytes(int, int, int, int, int, int, int, int) {
-    return 0;
+extern "C" size_t deltaproduct_chunk_fwd_workspace_bytes(int B, int T, int H, int r, int dk, int Dv,
+                                                         int chunk, int dtype) {
+    (void)Dv;
+    gdn::ChunkImpl impl;
+    if (B < 0 || T < 0 || H < 0 || !find_impl(dtype, r, r * dk, chunk, &impl)) return 0;
+    return impl.workspace(B, T, H);
 }

@@ -82,6 +82,34 @@ __device__ __forceinline__ void mma_bf16(floatx4 &acc, const u16 *a, int lda, co
     mma_bf16_split(acc, a, nullptr, lda, b, nullptr, ldb, kdim);
 }
 
+// acc += A * (bhi + blo) with A exact in bf16 and stored transposed
+// ([k][row], stride lda): each lane gathers its 8 A values one by one.
+__device__ __forceinline__ void mma_bf16_at_split(floatx4 &acc, const u16 *a, int lda, const u16 *bhi,
+                                                  const u16 *blo, int ldb, int kdim) {
+    const int l = lane_id();
+    const int rb = (l & 15) * ldb;
+    int kk = 0;
+    for (; kk + 32 <= kdim; kk += 32) {
+        const u16 *pa = a + (kk + 8 * (l >> 4)) * lda + (l & 15);
+        U16x8 av;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av.v[e] = pa[e * lda];
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, av);
+        const int ob = rb + kk + 8 * (l >> 4);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, ld8(bhi + ob), acc, 0, 0, 0);
+        if (blo) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, ld8(blo + ob), acc, 0, 0, 0);
+    }
+    if (kk < kdim) {
+        const u16 *pa = a + (kk + 4 * (l >> 4)) * lda + (l & 15);
+        shortx4 ah;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ah[e] = (short)pa[e * lda];
+        const int ob = rb + kk + 4 * (l >> 4);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, ld4(bhi + ob), acc, 0, 0, 0);
+        if (blo) acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, ld4(blo + ob), acc, 0, 0, 0);
+    }
+}
+
 // ---- fp32 tile products ---------------------------------------------------
 // acc += A(16 x kdim) * B(kdim x 16), A [row][k] stride lda, B [col][k]
 // stride ldb, fp32, kdim % 4 == 0.

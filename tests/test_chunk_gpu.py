@@ -54,7 +54,7 @@ SMALL = [
     (2, 100, 3, 32, 32, 32, "f32", 0.3),
     (1, 130, 2, 64, 64, 64, "f32", 0.3),
     (1, 90, 1, 128, 32, 32, "f32", 0.1),
-    (1, 77, 2, 128, 64, 64, "f32", 0.1),
+    (1, 77, 2, 128, 64, 32, "f32", 0.1),
     (1, 64, 2, 16, 16, 16, "bf16", 0.0),
     (1, 100, 2, 32, 48, 16, "bf16", 0.3),
     (2, 150, 2, 64, 64, 32, "bf16", 0.3),
