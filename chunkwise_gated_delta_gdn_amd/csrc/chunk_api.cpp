@@ -44,6 +44,9 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
     GDN_REQUIRE(!h0 || gdn::aligned(h0, 4), GDN_EINVAL, "%s: h0 misaligned", name);
     GDN_REQUIRE(!hT || gdn::aligned(hT, 4), GDN_EINVAL, "%s: hT misaligned", name);
     GDN_REQUIRE(r == 1 || step_mask, GDN_EINVAL, "%s: step_mask is required for r=%d", name, r);
+    if (step_mask)
+        for (int i = 0; i < r * r; ++i)
+            GDN_REQUIRE(isfinite(step_mask[i]), GDN_EINVAL, "%s: step_mask[%d] is not finite", name, i);
     const int KD = r * dk;
     gdn::ChunkImpl impl;
     GDN_REQUIRE(find_impl(dtype, r, KD, chunk, &impl), GDN_EUNSUPPORTED,
@@ -76,10 +79,7 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
     if (r == 1) {
         a.mask[0] = step_mask ? step_mask[0] : 1.f;
     } else {
-        for (int i = 0; i < r * r; ++i) {
-            GDN_REQUIRE(isfinite(step_mask[i]), GDN_EINVAL, "%s: step_mask[%d] is not finite", name, i);
-            a.mask[i] = step_mask[i];
-        }
+        for (int i = 0; i < r * r; ++i) a.mask[i] = step_mask[i];
     }
     return gdn::check_hip(impl.launch(a, reinterpret_cast<hipStream_t>(stream)), name);
 }

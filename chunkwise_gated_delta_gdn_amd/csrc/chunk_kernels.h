@@ -145,7 +145,8 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(ChunkArgs args) {
     float *As = reinterpret_cast<float *>(smem + L::OFF_AS);
     float *Ts = reinterpret_cast<float *>(smem + L::OFF_TS);
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     float *Ys = reinterpret_cast<float *>(smem + L::OFF_Y) + w * 16 * LDY;
     const int T = args.T, H = args.H;
     const int NT = (T + C - 1) / C;
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(ChunkArgs args) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int t = ti * 16 + 4 * (l >> 4) + e;
-            const float dec = s < t ? fast_exp2(G2[t] - G2[s]) : 0.f;
+            const float dec = s < t ? fast_exp2(fminf(G2[t] - G2[s], 0.f)) : 0.f;
 #pragma unroll
             for (int a = 0; a < R; ++a)
                 As[(t * R + a) * LDA + s * R + bb] = betas[t * R + a] * args.mask[a * R + bb] * acc[e] * dec;
@@ -300,7 +301,8 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const bool chain = w < 4;
     const int ow = w - 4, otid = tid - 256;     // output-group wave / thread index
     const int nvb = args.Dv / BV;
@@ -344,18 +346,36 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
     constexpr int TROW = NR / VEC;                // T vectors per row
     U16x8 rkq[PKQ], rv[PV], rt[PT];
     float rbeta = 0.f, rg = 0.f;
+    // Per-slot source offsets (bytes) at chunk 0; chunk c adds c*C token rows.
+    const size_t tok_bytes_qk = (size_t)H * KD * S::ESZ, tok_bytes_v = (size_t)H * Dv * S::ESZ;
+    size_t kq_off[PKQ], v_off[PV];
+    int kq_t[PKQ], v_t[PV];
+#pragma unroll
+    for (int p = 0; p < PKQ; ++p) {
+        const int idx = otid + 256 * p;
+        const int rem = idx % (C * NV);
+        kq_t[p] = rem / NV;
+        kq_off[p] = (((size_t)b * T + kq_t[p]) * H + h) * KD * S::ESZ + (size_t)(rem % NV) * 16;
+    }
+#pragma unroll
+    for (int p = 0; p < PV; ++p) {
+        const int idx = otid + 256 * p;
+        v_t[p] = idx / VV;
+        v_off[p] = ((((size_t)b * T + v_t[p]) * H + h) * Dv + v0) * S::ESZ + (size_t)(idx % VV) * 16;
+    }
+    const unsigned char *kbase = reinterpret_cast<const unsigned char *>(args.k);
+    const unsigned char *qbase = reinterpret_cast<const unsigned char *>(args.q);
+    const unsigned char *vbase = reinterpret_cast<const unsigned char *>(args.v);
     auto prefetch = [&](int c) {
         const int t0 = c * C;
+        const bool full = t0 + C <= T;
 #pragma unroll
         for (int p = 0; p < PKQ; ++p) {
             const int idx = otid + 256 * p;
             if (idx < NKQ) {
-                const int which = idx / (C * NV), rem = idx % (C * NV);
-                const int t = rem / NV, cv = rem % NV, tt = t0 + t;
-                if (tt < T) {
-                    const unsigned char *src = reinterpret_cast<const unsigned char *>(which ? args.q : args.k);
-                    const size_t row = ((size_t)b * T + tt) * H + h;
-                    rkq[p] = *reinterpret_cast<const U16x8 *>(src + (row * KD + cv * VEC) * S::ESZ);
+                const unsigned char *src = (idx < C * NV ? kbase : qbase) + kq_off[p] + (size_t)t0 * tok_bytes_qk;
+                if (full || t0 + kq_t[p] < T) {
+                    rkq[p] = *reinterpret_cast<const U16x8 *>(src);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) rkq[p].v[e] = 0;
@@ -366,11 +386,8 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
         for (int p = 0; p < PV; ++p) {
             const int idx = otid + 256 * p;
             if (idx < NVV) {
-                const int t = idx / VV, cv = idx % VV, tt = t0 + t;
-                if (tt < T) {
-                    const size_t off = (((size_t)b * T + tt) * H + h) * Dv + v0 + cv * VEC;
-                    rv[p] = *reinterpret_cast<const U16x8 *>(reinterpret_cast<const unsigned char *>(args.v) +
-                                                             off * S::ESZ);
+                if (full || t0 + v_t[p] < T) {
+                    rv[p] = *reinterpret_cast<const U16x8 *>(vbase + v_off[p] + (size_t)t0 * tok_bytes_v);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) rv[p].v[e] = 0;
@@ -528,7 +545,8 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = ti * 16 + 4 * (l >> 4) + e;
-                    const float val = s <= t ? acc[e] * fast_exp2(G2[t] - G2[s]) : 0.f;
+                    const float dec = fast_exp2(fminf(G2[t] - G2[s], 0.f));
+                    const float val = s <= t ? acc[e] * dec : 0.f;
                     store_op<F32IN>(PqH, PqL, (bb * C + t) * LDPQ + s, val);
                 }
             }

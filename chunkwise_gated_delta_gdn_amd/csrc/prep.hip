@@ -1,0 +1,270 @@
+// Camera-branch prep, one HBM pass: Sana "fused_cam_gdn.py" _cam_prep_kernel
+// and cam_prep_func, with the inverse RMS of _precompute_cam_inv_rms fused
+// in (the page computes it in separate torch reductions that re-read q and k).
+//
+// One wave per token.  The C = H*D channels of q, k and v are cut into
+// 8-element segments; lane l owns segments l, l+64, ... .  A segment lies in
+// one head and in one half of it (D/2 is a multiple of 8), so each lane works
+// either on two UCPE groups of 4 or on four RoPE pairs, in registers:
+//   1. load q, k, v segments (16-byte vector loads), sum q^2 and k^2, reduce
+//      over the wave -> inv_rms_q, inv_rms_k;
+//   2. q~ = relu(q inv_rms_q w_q), k~ = relu(k inv_rms_k w_k) k_scale, v~ = v;
+//   3. first half: y = P x per group of 4 (P = proj_q for q, proj_kv for k, v);
+//      second half: y[d] = x[d] cos[n][d] + x[d^1] sin[n][d];
+//   4. ||k~||^2 and ||k_out||^2 per head: reduction over the D/8 lanes of the
+//      head; inflation = max(post, 1e-12) / max(pre, 1e-12);
+//   5. store q, k, v to (B, H, N, D) (16-byte stores, each head row of a
+//      token is D contiguous values; bf16 or fp32) and the per-head scalars
+//      to (B, H, N).
+#include <math.h>
+
+#include "api_common.h"
+#include "gdn_common.h"
+
+namespace gdn {
+namespace {
+
+struct PrepArgs {
+    const void *qkv;
+    const float *qw, *kw, *proj_q, *proj_kv, *cosv, *sinv;
+    float k_scale, eps;
+    void *qo, *ko, *vo;
+    float *pre, *post, *infl;
+    int B, N, H;
+};
+
+template <bool F32IN>
+__device__ __forceinline__ void load8(const void *base, size_t elem, float (&x)[8]) {
+    if constexpr (F32IN) {
+        const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + elem);
+        const float4 a = p[0], b = p[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+        const U16x8 r = *reinterpret_cast<const U16x8 *>(reinterpret_cast<const u16 *>(base) + elem);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32(r.v[e]);
+    }
+}
+
+template <bool F32IN>
+__device__ __forceinline__ void store8(void *base, size_t elem, const float (&x)[8]) {
+    if constexpr (F32IN) {
+        float4 *p = reinterpret_cast<float4 *>(reinterpret_cast<float *>(base) + elem);
+        p[0] = float4{x[0], x[1], x[2], x[3]};
+        p[1] = float4{x[4], x[5], x[6], x[7]};
+    } else {
+        U16x8 r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r.v[e] = bf16_bits(x[e]);
+        *reinterpret_cast<U16x8 *>(reinterpret_cast<u16 *>(base) + elem) = r;
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+template <int D>
+__device__ __forceinline__ float head_sum(float x) {     // over the D/8 lanes of one head
+#pragma unroll
+    for (int off = (D / 8) / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// NSEG = segments per lane = H*D / 512 (rounded up); one wave per token.
+template <bool F32IN, bool F32OUT, int D, int NSEG>
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+    const int l = threadIdx.x & 63;
+    const long tok = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long ntok = (long)a.B * a.N;
+    if (tok >= ntok) return;
+    const int b = (int)(tok / a.N), n = (int)(tok % a.N);
+    const int H = a.H, C = H * D;
+    const int nseg = C / 8;
+
+    float xq[NSEG][8], xk[NSEG][8], xv[NSEG][8];
+    float sq = 0.f, sk = 0.f;
+    const size_t tbase = (size_t)tok * 3 * C;
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) {
+        const int sg = l + 64 * i;
+        if (sg < nseg) {
+            load8<F32IN>(a.qkv, tbase + sg * 8, xq[i]);
+            load8<F32IN>(a.qkv, tbase + C + sg * 8, xk[i]);
+            load8<F32IN>(a.qkv, tbase + 2 * C + sg * 8, xv[i]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sq += xq[i][e] * xq[i][e];
+                sk += xk[i][e] * xk[i][e];
+            }
+        }
+    }
+    sq = wave_sum(sq);
+    sk = wave_sum(sk);
+    const float inv_q = 1.f / sqrtf(sq / C + a.eps);
+    const float inv_k = 1.f / sqrtf(sk / C + a.eps);
+
+    // per-token projections (wave-uniform addresses)
+    float Pq[16], Pkv[16];
+    const float *pq = a.proj_q + tok * 16, *pkv = a.proj_kv + tok * 16;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        Pq[i] = pq[i];
+        Pkv[i] = pkv[i];
+    }
+    constexpr int HALF = D / 2;
+
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) {
+        const int sg = l + 64 * i;
+        // every lane takes part in the head reductions below
+        const bool act = sg < nseg;
+        const int h = act ? (sg * 8) / D : 0, d0 = act ? (sg * 8) % D : 0;
+        float kpre = 0.f, kpost = 0.f;
+        float yq[8], yk[8], yv[8];
+        if (act) {
+            float qn[8], kn[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = h * D + d0 + e;
+                const float wq = a.qw ? a.qw[c] : 1.f, wk = a.kw ? a.kw[c] : 1.f;
+                const float vq = xq[i][e] * inv_q * wq;
+                const float vk = xk[i][e] * inv_k * wk;
+                qn[e] = vq > 0.f ? vq : 0.f;
+                kn[e] = (vk > 0.f ? vk : 0.f) * a.k_scale;
+                kpre += kn[e] * kn[e];
+            }
+            if (d0 < HALF) {
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float aq = 0.f, ak = 0.f, av = 0.f;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            aq += Pq[r * 4 + c] * qn[g * 4 + c];
+                            ak += Pkv[r * 4 + c] * kn[g * 4 + c];
+                            av += Pkv[r * 4 + c] * xv[i][g * 4 + c];
+                        }
+                        yq[g * 4 + r] = aq;
+                        yk[g * 4 + r] = ak;
+                        yv[g * 4 + r] = av;
+                    }
+            } else {
+                const float *cs = a.cosv + (size_t)n * HALF + (d0 - HALF);
+                const float *sn = a.sinv + (size_t)n * HALF + (d0 - HALF);
+                float cv[8], sv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    cv[e] = cs[e];
+                    sv[e] = sn[e];
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    yq[e] = qn[e] * cv[e] + qn[e ^ 1] * sv[e];
+                    yk[e] = kn[e] * cv[e] + kn[e ^ 1] * sv[e];
+                    yv[e] = xv[i][e] * cv[e] + xv[i][e ^ 1] * sv[e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kpost += yk[e] * yk[e];
+            const size_t o = (((size_t)b * H + h) * a.N + n) * D + d0;
+            store8<F32OUT>(a.qo, o, yq);
+            store8<F32OUT>(a.ko, o, yk);
+            store8<F32OUT>(a.vo, o, yv);
+        }
+        kpre = head_sum<D>(kpre);
+        kpost = head_sum<D>(kpost);
+        if (act && (d0 == 0)) {
+            const size_t so = ((size_t)b * H + h) * a.N + n;
+            a.pre[so] = kpre;
+            a.post[so] = kpost;
+            if (a.infl) a.infl[so] = fmaxf(kpost, 1e-12f) / fmaxf(kpre, 1e-12f);
+        }
+    }
+}
+
+template <bool F32IN, bool F32OUT, int D>
+hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
+    const long ntok = (long)a.B * a.N;
+    const int C = a.H * D;
+    const int nseg = C / 8;
+    const int blocks = (int)((ntok + 3) / 4);
+    if (nseg <= 64) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 1>), dim3(blocks), dim3(256), 0, s, a);
+    else if (nseg <= 128) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 2>), dim3(blocks), dim3(256), 0, s, a);
+    else if (nseg <= 256) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 4>), dim3(blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 8>), dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_norm_w, const float *proj_q,
+                        const float *proj_kv, const float *rope_cos, const float *rope_sin, float k_scale,
+                        float norm_eps, void *q_out, void *k_out, void *v_out, float *k_pre_sq,
+                        float *k_post_sq, float *inflation_sq, int B, int N, int H, int D, int dtype,
+                        int out_dtype, void *stream) {
+    const char *name = "gdn_prep";
+    GDN_REQUIRE(B >= 0 && N >= 0 && H >= 0, GDN_EINVAL, "%s: negative size (B=%d N=%d H=%d)", name, B, N, H);
+    GDN_REQUIRE(dtype == GDN_DTYPE_F32 || dtype == GDN_DTYPE_BF16, GDN_EINVAL, "%s: unknown dtype %d", name, dtype);
+    GDN_REQUIRE(out_dtype == GDN_DTYPE_F32 || out_dtype == GDN_DTYPE_BF16, GDN_EINVAL, "%s: unknown out_dtype %d",
+                name, out_dtype);
+    GDN_REQUIRE(D == 16 || D == 32 || D == 64 || D == 128, GDN_EUNSUPPORTED,
+                "%s: D=%d (supported: 16, 32, 64, 128)", name, D);
+    GDN_REQUIRE((long)H * D <= 4096, GDN_EUNSUPPORTED, "%s: H*D=%d exceeds 4096", name, H * D);
+    GDN_REQUIRE(isfinite(k_scale) && isfinite(norm_eps) && norm_eps >= 0.f, GDN_EINVAL,
+                "%s: k_scale and norm_eps must be finite, norm_eps >= 0", name);
+    if ((long)B * N * H == 0) return GDN_OK;
+    GDN_REQUIRE(qkv && proj_q && proj_kv && rope_cos && rope_sin && q_out && k_out && v_out && k_pre_sq &&
+                    k_post_sq,
+                GDN_EINVAL, "%s: null tensor pointer", name);
+    GDN_REQUIRE(gdn::aligned(qkv, 16) && gdn::aligned(q_out, 16) && gdn::aligned(k_out, 16) &&
+                    gdn::aligned(v_out, 16),
+                GDN_EINVAL, "%s: qkv and the q/k/v outputs must be 16-byte aligned", name);
+    GDN_REQUIRE(gdn::aligned(proj_q, 4) && gdn::aligned(proj_kv, 4) && gdn::aligned(rope_cos, 4) &&
+                    gdn::aligned(rope_sin, 4) && gdn::aligned(k_pre_sq, 4) && gdn::aligned(k_post_sq, 4) &&
+                    (!inflation_sq || gdn::aligned(inflation_sq, 4)) && (!q_norm_w || gdn::aligned(q_norm_w, 4)) &&
+                    (!k_norm_w || gdn::aligned(k_norm_w, 4)),
+                GDN_EINVAL, "%s: float tensors must be 4-byte aligned", name);
+    gdn::PrepArgs a;
+    a.qkv = qkv;
+    a.qw = q_norm_w;
+    a.kw = k_norm_w;
+    a.proj_q = proj_q;
+    a.proj_kv = proj_kv;
+    a.cosv = rope_cos;
+    a.sinv = rope_sin;
+    a.k_scale = k_scale;
+    a.eps = norm_eps;
+    a.qo = q_out;
+    a.ko = k_out;
+    a.vo = v_out;
+    a.pre = k_pre_sq;
+    a.post = k_post_sq;
+    a.infl = inflation_sq;
+    a.B = B;
+    a.N = N;
+    a.H = H;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    const int sel = (dtype == GDN_DTYPE_F32 ? 2 : 0) + (out_dtype == GDN_DTYPE_F32 ? 1 : 0);
+#define GDN_PREP_D(DD)                                                             \
+    switch (sel) {                                                                 \
+        case 0: e = gdn::launch_prep<false, false, DD>(a, s); break;               \
+        case 1: e = gdn::launch_prep<false, true, DD>(a, s); break;                \
+        case 2: e = gdn::launch_prep<true, false, DD>(a, s); break;                \
+        default: e = gdn::launch_prep<true, true, DD>(a, s); break;                \
+    }
+    switch (D) {
+        case 16: GDN_PREP_D(16) break;
+        case 32: GDN_PREP_D(32) break;
+        case 64: GDN_PREP_D(64) break;
+        default: GDN_PREP_D(128) break;
+    }
+#undef GDN_PREP_D
+    return gdn::check_hip(e, name);
+}

@@ -58,7 +58,7 @@ def _load():
     lib.gdn_recurrent_fwd.restype = I
     lib.gdn_recurrent_fwd_workspace_bytes.argtypes = [I] * 6
     lib.gdn_recurrent_fwd_workspace_bytes.restype = Z
-    lib.gdn_prep.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P, P, P, P, I, I, I, I, I, P]
+    lib.gdn_prep.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P, P, P, P, I, I, I, I, I, I, P]
     lib.gdn_prep.restype = I
     return lib
 
@@ -180,9 +180,12 @@ def gdn_recurrent_fwd(q, k, v, beta, log_decay, scale=1.0, h0=None, output_final
     _f32(beta, "beta"), _f32(log_decay, "log_decay"), _f32(h0, "h0")
     B, H, N, D = q.shape
     F = log_decay.shape[-1]
-    if F <= 0 or N % F:
+    if F == 0 and N == 0:
+        S = 1                        # no frames: only hT = h0 is produced
+    elif F <= 0 or N % F:
         raise ValueError("N must be a multiple of the number of frames")
-    S = N // F
+    else:
+        S = N // F
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v shapes or dtypes disagree")
     if beta.shape != (B, H, N) or log_decay.shape != (B, H, F):
@@ -199,10 +202,11 @@ def gdn_recurrent_fwd(q, k, v, beta, log_decay, scale=1.0, h0=None, output_final
 
 
 def gdn_prep(qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_scale, norm_eps,
-             want_inflation=True):
+             want_inflation=True, out_dtype=None):
     """Camera-branch prep.  qkv (B,N,3,H,D); norm weights (H*D,) fp32 or None;
     proj (B,N,4,4) fp32; rope tables (N,D/2) fp32.  Returns a dict with q, k, v
-    (B,H,N,D) in qkv's dtype and k_pre_sq, k_post_sq, inflation_sq (B,H,N)."""
+    (B,H,N,D) in out_dtype (default: qkv's dtype) and k_pre_sq, k_post_sq,
+    inflation_sq (B,H,N) fp32."""
     _dev(qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin)
     for t, n in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w"), (proj_q, "proj_q"),
                  (proj_kv, "proj_kv"), (rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
@@ -215,7 +219,8 @@ def gdn_prep(qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_sca
     if rope_cos.shape != (N, D // 2) or rope_sin.shape != (N, D // 2):
         raise ValueError("rope tables must be (N, D/2)")
     dev = qkv.device
-    out = {n: torch.empty((B, H, N, D), dtype=qkv.dtype, device=dev) for n in ("q", "k", "v")}
+    out_dtype = out_dtype or qkv.dtype
+    out = {n: torch.empty((B, H, N, D), dtype=out_dtype, device=dev) for n in ("q", "k", "v")}
     for n in ("k_pre_sq", "k_post_sq"):
         out[n] = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     out["inflation_sq"] = torch.empty((B, H, N), dtype=torch.float32, device=dev) if want_inflation else None
@@ -223,6 +228,6 @@ def gdn_prep(qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_sca
                        _ptr(rope_cos), _ptr(rope_sin), float(k_scale), float(norm_eps),
                        _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["k_pre_sq"]),
                        _ptr(out["k_post_sq"]), _ptr(out["inflation_sq"]), B, N, H, D,
-                       _dtype_code(qkv.dtype), _stream(dev))
+                       _dtype_code(qkv.dtype), _dtype_code(out_dtype), _stream(dev))
     _check("gdn_prep", rc)
     return out

@@ -173,7 +173,8 @@ size_t gdn_recurrent_fwd_workspace_bytes(int B, int H, int F, int S, int D, int 
  *   q_norm_w, k_norm_w (H*D)         float32, nullable (= all ones)
  *   proj_q, proj_kv  (B, N, 4, 4)    float32, row-major per token
  *   rope_cos, rope_sin (N, D/2)      float32, interleaved-pair tables
- *   q_out, k_out, v_out (B, H, N, D) dtype
+ *   q_out, k_out, v_out (B, H, N, D) out_dtype (the page writes the input
+ *                    dtype; GDN_DTYPE_F32 keeps the full fp32 result)
  *   k_pre_sq, k_post_sq (B, H, N)    float32
  *   inflation_sq     (B, H, N)       float32, nullable (not stored)
  * Supported: D in {16, 32, 64, 128}; H*D <= 4096.
@@ -184,7 +185,7 @@ int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_norm_w,
              float k_scale, float norm_eps,
              void *q_out, void *k_out, void *v_out,
              float *k_pre_sq, float *k_post_sq, float *inflation_sq,
-             int B, int N, int H, int D, int dtype, void *stream);
+             int B, int N, int H, int D, int dtype, int out_dtype, void *stream);
 
 #ifdef __cplusplus
 }

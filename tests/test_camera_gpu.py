@@ -1,0 +1,212 @@
+"""GPU parity of gdn_prep and gdn_recurrent_fwd against the fp64 oracle,
+element by element, through the C ABI (ctypes binding)."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from chunkwise_gated_delta_gdn_amd import inputs as synth
+from tests._helpers import TOL, max_rel_err, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+# A bf16-stored output carries its own rounding: half an ulp, at most 2^-8
+# of the largest magnitude (an element just above a power of two).  Outputs
+# stored in bf16 are held to the input-precision bar plus that bound;
+# outputs stored in fp32 to the bar alone.
+BF16_OUT_ROUNDING = 2.0 ** -8
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from chunkwise_gated_delta_gdn_amd import gdn as g
+    return g
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _prep_gpu(gdn, d, dtype, out_dtype=None):
+    import torch
+    t = {n: to_dev(d[n], "f32") for n in ("q_norm_w", "k_norm_w", "proj_q", "proj_kv", "rope_cos", "rope_sin")}
+    out = gdn.gdn_prep(to_dev(d["qkv"], dtype), t["q_norm_w"], t["k_norm_w"], t["proj_q"], t["proj_kv"],
+                       t["rope_cos"], t["rope_sin"], d["k_scale"], d["eps"], out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return {n: to_np(x) for n, x in out.items()}
+
+
+def _prep_ref(d):
+    return oracle.cam_prep(d["qkv"], d["q_norm_w"], d["k_norm_w"], d["proj_q"], d["proj_kv"], d["rope_cos"],
+                           d["rope_sin"], d["k_scale"], d["eps"])
+
+
+def _check_prep(got, ref, dtype, out_bf16, what):
+    worst = {}
+    for n in ("q", "k", "v", "k_pre_sq", "k_post_sq", "inflation_sq"):
+        bar = TOL[dtype] + (BF16_OUT_ROUNDING if (out_bf16 and n in ("q", "k", "v")) else 0.0)
+        e = max_rel_err(got[n], ref[n])
+        worst[n] = e
+        assert np.all(np.isfinite(got[n])), n
+        assert e <= bar, (what, n, e, bar)
+    _say(f"  {what}: " + " ".join(f"{n}={e:.2e}" for n, e in worst.items()))
+
+
+@pytest.mark.parametrize("case", [
+    # (B, F, S, H, D, dtype)
+    (1, 2, 7, 2, 16, "f32"),
+    (2, 1, 33, 3, 32, "f32"),
+    (1, 3, 50, 4, 64, "f32"),
+    (1, 2, 20, 8, 128, "f32"),
+    (1, 2, 7, 2, 16, "bf16"),
+    (2, 3, 40, 16, 64, "bf16"),
+    (1, 2, 30, 32, 128, "bf16"),
+], ids=lambda c: "B{}F{}S{}H{}D{}{}".format(*c))
+def test_prep_small(gdn, case):
+    import torch
+    B, F, S, H, D, dtype = case
+    _say(f"gdn_prep small case {case}")
+    d = synth.camera_inputs(B, F, S, H, D, seed=500 + S + D, dtype=dtype)
+    rng = np.random.default_rng(S)
+    d["q_norm_w"] = rng.uniform(0.5, 1.5, H * D).astype(np.float32)      # non-trivial weights
+    d["k_norm_w"] = rng.uniform(0.5, 1.5, H * D).astype(np.float32)
+    ref = _prep_ref(d)
+    _check_prep(_prep_gpu(gdn, d, dtype, torch.float32), ref, dtype, False, f"{case} fp32 out")
+    if dtype == "bf16":
+        _check_prep(_prep_gpu(gdn, d, dtype), ref, dtype, True, f"{case} bf16 out")
+
+
+def test_prep_camera_workload(gdn):
+    """B=1, 8 frames of 30x52 tokens, H=16, D=64, bf16: every output."""
+    import torch
+    _say("gdn_prep camera workload, full comparison")
+    d = synth.workload_inputs("camera")
+    ref = _prep_ref(d)
+    _check_prep(_prep_gpu(gdn, d, "bf16", torch.float32), ref, "bf16", False, "camera fp32 out")
+    _check_prep(_prep_gpu(gdn, d, "bf16"), ref, "bf16", True, "camera bf16 out")
+
+
+def test_prep_edge_cases(gdn):
+    import torch
+    _say("gdn_prep edge cases: all-negative keys, identity transforms")
+    d = synth.camera_inputs(1, 1, 9, 4, 32, seed=77, dtype="bf16")
+    d["qkv"][:, :, 1] = -np.abs(d["qkv"][:, :, 1])                       # relu zeroes every key
+    got = _prep_gpu(gdn, d, "bf16", torch.float32)
+    assert np.all(got["k"] == 0) and np.all(got["k_pre_sq"] == 0) and np.all(got["inflation_sq"] == 1.0)
+    ref = _prep_ref(d)
+    _check_prep(got, ref, "bf16", False, "negative keys")
+
+
+# ---------------------------------------------------------------------------
+# frame-synchronous scan
+# ---------------------------------------------------------------------------
+
+def _scan_gpu(gdn, q, k, v, beta, g, dtype, scale=1.0, h0=None):
+    import torch
+    out, hT = gdn.gdn_recurrent_fwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), to_dev(beta, "f32"),
+                                    to_dev(g, "f32"), scale, None if h0 is None else to_dev(h0, "f32"))
+    torch.cuda.synchronize()
+    return to_np(out), to_np(hT)
+
+
+def _scan_inputs(B, H, F, S, D, seed, dtype, h0_std=0.0):
+    """gdn-like synthetic scan inputs in the (B,H,N,D) layout, keys scaled so
+    that a frame's sum of beta k k^T stays below one."""
+    rng = np.random.default_rng(seed)
+    N = F * S
+    q = rng.standard_normal((B, H, N, D))
+    k = rng.standard_normal((B, H, N, D))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True) * np.sqrt(max(S, 1))
+    v = rng.standard_normal((B, H, N, D))
+    beta = 0.5 * (1 + np.tanh(0.5 * rng.standard_normal((B, H, N))))
+    g = -np.logaddexp(0.0, -rng.normal(3.0, 0.5, (B, H, F)))
+    h0 = rng.normal(0, h0_std, (B, H, D, D)).astype(np.float32) if h0_std > 0 else None
+    return (synth.cast(q, dtype), synth.cast(k, dtype), synth.cast(v, dtype), beta.astype(np.float32),
+            g.astype(np.float32), h0)
+
+
+@pytest.mark.parametrize("case", [
+    # (B, H, F, S, D, dtype, h0_std)
+    (1, 2, 3, 5, 16, "f32", 0.3),
+    (2, 2, 4, 33, 32, "f32", 0.0),
+    (1, 3, 5, 70, 64, "f32", 0.2),
+    (1, 2, 2, 40, 128, "f32", 0.1),
+    (1, 2, 3, 5, 16, "bf16", 0.3),
+    (2, 4, 6, 100, 64, "bf16", 0.1),
+    (1, 2, 3, 257, 128, "bf16", 0.1),
+], ids=lambda c: "B{}H{}F{}S{}D{}{}h{}".format(*c))
+def test_scan_small(gdn, case):
+    B, H, F, S, D, dtype, h0s = case
+    _say(f"gdn_recurrent_fwd small case {case}")
+    q, k, v, beta, g, h0 = _scan_inputs(B, H, F, S, D, 600 + S + D, dtype, h0s)
+    out, hT = _scan_gpu(gdn, q, k, v, beta, g, dtype, 0.8, h0)
+    oref, href = oracle.frame_scan(q, k, v, beta, g, F, 0.8, h0)
+    eo, eh = max_rel_err(out, oref), max_rel_err(hT, href)
+    _say(f"  {case}: max rel err out={eo:.2e} hT={eh:.2e}")
+    assert eo <= TOL[dtype] and eh <= TOL[dtype], (eo, eh)
+
+
+def test_scan_camera_workload(gdn):
+    """The camera workload's scan: inputs are the oracle's prep outputs in
+    bf16, beta and per-frame log-decay from the workload; every output."""
+    _say("gdn_recurrent_fwd camera workload, full comparison")
+    d = synth.workload_inputs("camera")
+    pr = _prep_ref(d)
+    q, k, v = (synth.round_bf16(pr[n]) for n in ("q", "k", "v"))
+    out, hT = _scan_gpu(gdn, q, k, v, d["beta"], d["g"], "bf16")
+    oref, href = oracle.frame_scan(q, k, v, d["beta"], d["g"], d["F"], 1.0)
+    eo, eh = max_rel_err(out, oref), max_rel_err(hT, href)
+    # the state grows by ~35x per frame on this workload; check every frame
+    S = d["S"]
+    per_frame = [max_rel_err(out[:, :, f * S:(f + 1) * S], oref[:, :, f * S:(f + 1) * S]) for f in range(d["F"])]
+    _say(f"  camera: out={eo:.2e} hT={eh:.2e} per frame " + " ".join(f"{e:.1e}" for e in per_frame))
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert max(per_frame) <= TOL["bf16"]
+
+
+def test_scan_one_token_per_frame_matches_chunk_path(gdn):
+    """S = 1: the frame scan is the token-level gated delta rule; compare with
+    gdn_chunk_fwd on the same inputs (GPU against GPU) and with the oracle."""
+    import torch
+    _say("gdn_recurrent_fwd S=1 vs gdn_chunk_fwd")
+    dd = synth.gdn_inputs(1, 96, 2, 64, 64, seed=41, dtype="bf16", h0_std=0.1)
+    tr = lambda x: np.ascontiguousarray(np.transpose(x, (0, 2, 1, 3)))
+    out, hT = _scan_gpu(gdn, tr(dd["q"]), tr(dd["k"]), tr(dd["v"]), np.ascontiguousarray(dd["beta"].transpose(0, 2, 1)),
+                        np.ascontiguousarray(dd["g"].transpose(0, 2, 1)), "bf16", 1.0, dd["h0"])
+    o2, h2 = gdn.gdn_chunk_fwd(to_dev(dd["q"], "bf16"), to_dev(dd["k"], "bf16"), to_dev(dd["v"], "bf16"),
+                               to_dev(dd["beta"], "f32"), to_dev(dd["g"], "f32"), 1.0, to_dev(dd["h0"], "f32"))
+    torch.cuda.synchronize()
+    oref, href = oracle.gdn_recurrent(dd["q"], dd["k"], dd["v"], dd["beta"], dd["g"], 1.0, dd["h0"])
+    assert max_rel_err(tr(out), oref) <= TOL["bf16"] and max_rel_err(hT, href) <= TOL["bf16"]
+    assert max_rel_err(tr(out), to_np(o2)) <= TOL["bf16"]
+    assert max_rel_err(hT, to_np(h2)) <= TOL["bf16"]
+
+
+def test_scan_split_resume_and_edges(gdn):
+    _say("gdn_recurrent_fwd split/resume, beta=0, F=0")
+    B, H, F, S, D = 1, 2, 6, 30, 64
+    q, k, v, beta, g, h0 = _scan_inputs(B, H, F, S, D, 42, "bf16", 0.2)
+    out, hT = _scan_gpu(gdn, q, k, v, beta, g, "bf16", 1.0, h0)
+    F1 = 2
+    a = lambda x, lo, hi: np.ascontiguousarray(x[:, :, lo * S:hi * S])
+    o1, h1 = _scan_gpu(gdn, a(q, 0, F1), a(k, 0, F1), a(v, 0, F1), np.ascontiguousarray(beta[..., :F1 * S]),
+                       np.ascontiguousarray(g[..., :F1]), "bf16", 1.0, h0)
+    o2, h2 = _scan_gpu(gdn, a(q, F1, F), a(k, F1, F), a(v, F1, F), np.ascontiguousarray(beta[..., F1 * S:]),
+                       np.ascontiguousarray(g[..., F1:]), "bf16", 1.0, h1)
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=2), out, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(h2, hT, rtol=0, atol=1e-6)
+    # beta = 0: pure decayed carry of h0
+    out, hT = _scan_gpu(gdn, q, k, v, np.zeros_like(beta), g, "bf16", 1.0, h0)
+    oref, href = oracle.frame_scan(q, k, v, np.zeros_like(beta), g, F, 1.0, h0)
+    assert max_rel_err(out, oref) <= TOL["bf16"] and max_rel_err(hT, href) <= TOL["bf16"]
+    # no frames at all: the final state is h0
+    z = np.zeros((B, H, 0, D), np.float32)
+    out, hT = _scan_gpu(gdn, z, z, z, np.zeros((B, H, 0), np.float32), np.zeros((B, H, 0), np.float32), "bf16",
+                        1.0, h0)
+    assert out.shape == (B, H, 0, D)
+    np.testing.assert_array_equal(hT, h0)
