@@ -91,12 +91,78 @@ def cpu_baseline(d, B, T, H, budget_s=20.0):
                       f"{dt:.2f} s wall on {used} threads, scaled by {nheads}/{H}"}
 
 
+def _prepare(name, dev):
+    """Inputs of a workload on the GPU and a step() closure that runs the
+    workload's hot path once through the C ABI."""
+    import torch
+    from chunkwise_gated_delta_gdn_amd import gdn, inputs
+    wl = inputs.WORKLOADS[name]
+    d = inputs.workload_inputs(name)
+    bf = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    f32 = lambda x: torch.from_numpy(x).to(dev)
+    if wl["kind"] == "gdn":
+        q, k, v = bf(d["q"]), bf(d["k"]), bf(d["v"])
+        beta, g = f32(d["beta"]), f32(d["g"])
+        h0 = None if d["h0"] is None else f32(d["h0"])
+
+        def step():
+            return gdn.gdn_chunk_fwd(q, k, v, beta, g, 1.0, h0, chunk=wl["chunk"], out_dtype=torch.float32)
+        B, T, H = wl["B"], wl["T"], wl["H"]
+        nbytes, flops = algorithmic_work(B, T, H, wl["Dk"], wl["Dv"], wl["chunk"], with_h0=h0 is not None)
+        return d, step, B * T, nbytes, flops
+    if wl["kind"] == "deltaproduct":
+        q, k, v = bf(d["q"]), bf(d["k"]), bf(d["v"])
+        beta, g = f32(d["beta"]), f32(d["g"])
+        K = wl["r"] * wl["dk"]
+
+        def step():
+            return gdn.deltaproduct_chunk_fwd(q, k, v, beta, g, d["mask"], K ** -0.5, chunk=wl["chunk"])
+        B, T, H, r, Dv = wl["B"], wl["T"], wl["H"], wl["r"], wl["Dv"]
+        nbytes = B * T * H * (2 * K + Dv) * 2 + B * T * H * (r + 1) * 4 + B * T * H * Dv * 4 + B * H * K * Dv * 4
+        C, dk = wl["chunk"], wl["dk"]
+        NR = C * r
+        # per chunk: Gram r*C^2*dk, W/U NR^2*(K+Dv), state 2*NR*K*Dv, output 2*C*K*Dv + r*C^2*dk, all x2 FLOP
+        per_chunk = 2 * (r * C * C * dk * 2 + NR * NR * (K + Dv) + 2 * NR * K * Dv + C * K * Dv) + 2 * NR ** 3 / 3
+        flops = B * H * (T // C) * per_chunk
+        return d, step, B * T, nbytes, flops
+    # camera: prep, then the frame-synchronous scan on its outputs
+    qkv = bf(d["qkv"])
+    t = {n: f32(d[n]) for n in ("q_norm_w", "k_norm_w", "proj_q", "proj_kv", "rope_cos", "rope_sin", "beta", "g")}
+
+    def step():
+        pr = gdn.gdn_prep(qkv, t["q_norm_w"], t["k_norm_w"], t["proj_q"], t["proj_kv"], t["rope_cos"],
+                          t["rope_sin"], d["k_scale"], d["eps"])
+        return gdn.gdn_recurrent_fwd(pr["q"], pr["k"], pr["v"], t["beta"], t["g"], 1.0)
+    B, F, S, H, D = wl["B"], wl["F"], wl["S"], wl["H"], wl["D"]
+    N = F * S
+    prep_bytes = B * N * 3 * H * D * 2 * 2 + B * N * 32 * 4 + N * D * 4 + B * H * N * 3 * 4
+    scan_bytes = B * H * N * D * 2 * 3 + B * H * N * 4 + B * H * N * D * 4 + B * H * D * D * 4
+    flops = B * H * N * 4 * D * D * 2
+    return d, step, B * N, prep_bytes + scan_bytes, flops
+
+
+def copy_probe(dev, mib=512, reps=5):
+    """A plain device-to-device copy of known size, for scaling the rocprofv3
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": n * 4, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="gdn", choices=("gdn", "gdn_long", "deltaproduct", "camera"),
+                    help="gdn is the headline workload; the others time the other operations")
+    ap.add_argument("--copy-probe", action="store_true", help="run only the copy calibration kernel")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -105,20 +171,13 @@ def main():
 
     import numpy as np
     import torch
-    from chunkwise_gated_delta_gdn_amd import gdn, inputs
 
     dev = torch.device("cuda:0")
-    wl = inputs.WORKLOADS["gdn"]
-    B, T, H, Dk, Dv, C = wl["B"], wl["T"], wl["H"], wl["Dk"], wl["Dv"], wl["chunk"]
-    d = inputs.workload_inputs("gdn")
-    q, k, v = (torch.from_numpy(d[n]).to(dev).to(torch.bfloat16) for n in ("q", "k", "v"))
-    beta = torch.from_numpy(d["beta"]).to(dev)
-    g = torch.from_numpy(d["g"]).to(dev)
+    if args.copy_probe:
+        copy_probe(dev)
+        return
+    d, step, tokens, nbytes, flops = _prepare(args.workload, dev)
     torch.cuda.synchronize()
-
-    def step():
-        return gdn.gdn_chunk_fwd(q, k, v, beta, g, 1.0, None, chunk=C, out_dtype=torch.float32)
-
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -136,13 +195,28 @@ def main():
     kern_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
     ms_per_step = wall * 1e3 / args.steps
     kernel_ms = float(np.mean(kern_ms))
-
-    nbytes, flops = algorithmic_work(B, T, H, Dk, Dv, C)
     achieved_gbs = nbytes / (kernel_ms * 1e-3) / 1e9
-    traffic = measured_traffic(kernel_source_hash())
+    from chunkwise_gated_delta_gdn_amd import inputs
+    wl = inputs.WORKLOADS[args.workload]
+    if args.workload in ("gdn", "gdn_long"):
+        metric = "tokens/sec of chunkwise gated-delta fwd (B*T/s) at H=16, D=128"
+        desc = (f"{args.workload}: B={wl['B']} H={wl['H']} T={wl['T']} Dk=Dv={wl['Dk']} chunk={wl['chunk']}, "
+                f"bf16 q/k/v, fp32 gates/state/output, " + ("h0~N(0,0.02^2)" if wl["h0_std"] else "h0=0"))
+        kernel = "gdn_chunk_fwd = chunk_solve_kernel + chunk_chain_kernel <bf16, KD=128, C=64, R=1>"
+        traffic = measured_traffic(kernel_source_hash()) if args.workload == "gdn" else None
+    elif args.workload == "deltaproduct":
+        metric = "tokens/sec of chunkwise gated DeltaProduct fwd (B*T/s)"
+        desc = "deltaproduct: B=2 H=8 T=2048 K=2x128 Dv=128 chunk=32 r=2, bf16, lower-triangular step mask"
+        kernel = "deltaproduct_chunk_fwd = chunk_solve_kernel + chunk_chain_kernel <bf16, KD=256, C=32, R=2>"
+        traffic = None
+    else:
+        metric = "tokens/sec of camera prep + frame-synchronous scan (B*N/s)"
+        desc = "camera: B=1 F=8 S=30x52 H=16 D=64, bf16 prep output, fp32 scan output"
+        kernel = "gdn_prep + gdn_recurrent_fwd (prep_kernel, frame_gram/state/out kernels)"
+        traffic = None
     rec = {
-        "metric": "tokens/sec of chunkwise gated-delta fwd (B*T/s) at H=16, D=128",
-        "value": B * T / (ms_per_step * 1e-3),
+        "metric": metric,
+        "value": tokens / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -152,23 +226,20 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta sigmoid(N(0,1)), "
-                "log-decay logsigmoid(N(2,0.5)))",
-        "config": {"workload": "gdn: B=2 H=16 T=4096 Dk=Dv=128 chunk=64, bf16 q/k/v, fp32 "
-                               "gates/state/output, h0=0",
-                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": Dk, "chunk": C,
-                   "parallelism": "single GPU"},
+        "data": "synthetic (seeded generators of chunkwise_gated_delta_gdn_amd.inputs)",
+        "config": {"workload": desc, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gdn_chunk_fwd = chunk_solve_kernel + chunk_chain_kernel "
-                               "<bf16, KD=128, C=64, R=1>",
-                     "kernel_ms": kernel_ms, "algorithmic_bytes": nbytes,
+                     "kernel": kernel, "kernel_ms": kernel_ms, "algorithmic_bytes": nbytes,
                      "algorithmic_flops": flops,
                      "mfma_tflops": flops / (kernel_ms * 1e-3) / 1e12,
                      "mfma_frac": flops / (kernel_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
     }
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(d, B, T, H)
+    if args.workload in ("gdn", "gdn_long"):
+        rec["config"].update({"global_batch": wl["B"], "seq_len": wl["T"], "heads": wl["H"],
+                              "head_dim": wl["Dk"], "chunk": wl["chunk"]})
+    if not args.no_cpu_baseline and args.workload == "gdn":
+        rec["cpu_baseline"] = cpu_baseline(d, wl["B"], wl["T"], wl["H"])
     print(json.dumps(rec), flush=True)
 
 
