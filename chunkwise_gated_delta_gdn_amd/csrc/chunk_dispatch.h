@@ -2,9 +2,39 @@
 // and step count, so they compile in parallel).
 #pragma once
 
+#include "chunk_chain1.h"
 #include "chunk_kernels.h"
 
 namespace gdn {
+
+// The single-chain-wave state pass covers bf16 inputs, one step per token,
+// and chunk / key widths that are multiples of 32; everything else runs the
+// general 8-wave state pass.
+template <bool F32IN, int KD, int C, int R>
+constexpr bool use_chain1() {
+    return !F32IN && R == 1 && C % 32 == 0 && KD % 32 == 0;
+}
+
+// Launch both kernels of one instantiation on `stream`.
+template <bool F32IN, int KD, int C, int R>
+hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream) {
+    const int NT = (a.T + C - 1) / C;
+    const int nbh = a.B * a.H;
+    if (nbh == 0) return hipSuccess;
+    if (NT > 0) {
+        hipLaunchKernelGGL((chunk_solve_kernel<F32IN, KD, C, R>), dim3(nbh * NT), dim3(256), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int nvb = a.Dv / 16;
+    const int grid = ((nbh + 7) / 8) * 8 * nvb;
+    if constexpr (use_chain1<F32IN, KD, C, R>()) {
+        hipLaunchKernelGGL((chunk_chain1_kernel<KD, C>), dim3(grid), dim3(Chain1Shape<KD, C>::NTHR), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((chunk_chain_kernel<F32IN, KD, C, R>), dim3(grid), dim3(512), 0, stream, a);
+    }
+    return hipGetLastError();
+}
 
 struct ChunkImpl {
     hipError_t (*launch)(const ChunkArgs &, hipStream_t);

@@ -651,21 +651,4 @@ size_t chunk_workspace_bytes(int B, int T, int H) {
     return (size_t)B * H * NT * S::NR * S::NR * S::ESZ;
 }
 
-// Launch both kernels of one instantiation on `stream`.
-template <bool F32IN, int KD, int C, int R>
-hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream) {
-    const int NT = (a.T + C - 1) / C;
-    const int nbh = a.B * a.H;
-    if (nbh == 0) return hipSuccess;
-    if (NT > 0) {
-        hipLaunchKernelGGL((chunk_solve_kernel<F32IN, KD, C, R>), dim3(nbh * NT), dim3(256), 0, stream, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    const int nvb = a.Dv / 16;
-    const int grid = ((nbh + 7) / 8) * 8 * nvb;
-    hipLaunchKernelGGL((chunk_chain_kernel<F32IN, KD, C, R>), dim3(grid), dim3(512), 0, stream, a);
-    return hipGetLastError();
-}
-
 }  // namespace gdn

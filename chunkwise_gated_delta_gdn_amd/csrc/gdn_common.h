@@ -22,6 +22,7 @@ namespace gdn {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 
 struct alignas(16) U16x8 { u16 v[8]; };
@@ -37,6 +38,19 @@ __device__ __forceinline__ float bf16_to_f32(u16 b) {
 __device__ __forceinline__ void split_bf16(float x, u16 &hi, u16 &lo) {
     hi = bf16_bits(x);
     lo = bf16_bits(x - bf16_to_f32(hi));
+}
+
+// Two floats to two bf16 (round to nearest even) in one 32-bit word, low
+// half first: one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt2_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a, b}, bf16x2));
+}
+// Packed split of two floats: hi = bf16 pair, lo = bf16 pair of the residuals.
+__device__ __forceinline__ void split2_bf16(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = cvt2_bf16(a, b);
+    lo = cvt2_bf16(a - __builtin_bit_cast(float, hi << 16), b - __builtin_bit_cast(float, hi & 0xffff0000u));
 }
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
