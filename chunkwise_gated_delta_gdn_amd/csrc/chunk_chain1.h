@@ -19,16 +19,17 @@
 //   so the sum over k is unchanged.  It publishes V_new and the chunk-start
 //   state to LDS in fp32 for the output waves.
 //
-//   waves 1..C/16 ("out"), one 16-token tile each: P = tril(Q K^T * e^{G_t -
-//   G_s}) computed transposed so that its accumulator tile is directly the A
-//   operand of a 16x16x16 MFMA, Q S_start, P V_new, the output store, and the
-//   staging of the next chunks: a register prefetch one chunk ahead, then K
-//   and K^T (8x8 blocks transposed in registers), T, beta V (transposed) and
-//   the gate tables committed to LDS.
+//   waves 1..C/16 ("out"), one 16-token tile each: the output, transposed,
+//   O^T = S_start^T Q^T e^G + V_new^T P^T (P, the causal intra-chunk scores,
+//   comes from the solve kernel as ready MFMA fragments; the transposed
+//   accumulator gives each lane 4 consecutive values of one token, one
+//   16-byte store), and the staging of the next chunks: a register prefetch
+//   one chunk ahead, then K and K^T (8x8 blocks transposed in registers), T,
+//   beta V (transposed) and the gate tables committed to LDS.
 //
-// One workgroup barrier per chunk.  Iteration c: the chain processes chunk
-// c; the out waves finish the output of chunk c-1, compute P and Q S_start of
-// chunk c, and stage chunk c+1.
+// One workgroup barrier per chunk.  Iteration c: the chain processes chunk c
+// and publishes its start state and V_new; the out waves write the output of
+// chunk c-1 and stage chunk c+1.
 #pragma once
 
 #include "chunk_kernels.h"
@@ -191,7 +192,6 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
                 for (int e = 0; e < 4; ++e) Sreg[ti][e] = hp[(size_t)(ti * 16 + 4 * g + e) * Dv];
             }
         }
-        publish_state(0);
         __syncthreads();
         for (int c = 0; c < NT; ++c) {
             const int p = c & 1;
@@ -208,6 +208,7 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
                 const u16 *kr = ks + (tt * 16 + c16) * LDK;
 #pragma unroll
                 for (int m = 0; m < NKS; ++m) x = mfma32(ld_perm(kr, m * 32, g), sb[m], x);
+                if (tt == 0) publish_state(p);   // S_start of chunk c, while the MFMAs run
                 const floatx4 bvt = *reinterpret_cast<const floatx4 *>(bv + c16 * LDBV + tt * 16 + 4 * g);
                 const floatx4 beg = *reinterpret_cast<const floatx4 *>(gp + tt * 16 + 4 * g);
 #pragma unroll
@@ -253,7 +254,6 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Sreg[ti][e] = gL * Sreg[ti][e] + acc[e];
             }
-            publish_state(p ^ 1);
             __syncthreads();
         }
         __syncthreads();                       // matches the out waves' drain step
@@ -271,19 +271,22 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
     // =====================================================================
     // out waves
     // =====================================================================
-    const int ow = w - 1;                       // token tile of this wave
+    const int ow = NTT - w;                     // token tile of this wave (wave 1: the last)
     const int ltid = tid - 64;                  // loader thread index
-    // Loader roles: threads [0, NB8) stage one 8x8 block of K each; threads
-    // [NLD - 2C, NLD) one 16-byte vector of the V slice; the last wave the
-    // gate table; every thread C/32 vectors of T.
+    // Loader roles: threads [0, NB8) stage one 8x8 block of K each; wave VW
+    // the V slice (C/32 16-byte vectors per lane) and the gate table; every
+    // thread C/32 vectors of T.  The last wave (the lightest output tile)
+    // runs slowest when C = 64 (five waves on four SIMDs: it shares one with
+    // the chain wave), so it only loads T.
     constexpr int NTV = C * C / 8;              // 16-byte vectors of T
     constexpr int PT = NTV / NLD;
-    static_assert(PT * NLD == NTV, "T vectors split evenly over the loaders");
+    constexpr int PV = C / 32;                  // V vectors per lane of wave VW
+    constexpr int VW = NTT >= 3 ? 3 : NTT;
+    static_assert(PT * NLD == NTV && PV * 64 == 2 * C, "loader split");
     const bool kload = ltid < NB8;
     const int kb8 = ltid % (KD / 8), tb8 = min(ltid / (KD / 8), C / 8 - 1);
-    const int vid = ltid - (NLD - 2 * C);       // V vector index when >= 0
-    const int vtok = (vid < 0 ? 0 : vid) % C, vcv = (vid < 0 ? 0 : vid) / C;
-    const bool gwave = ltid >= NLD - 64;
+    // wave-uniform roles
+    const bool kwave = (w - 1) * 64 < NB8, vwave = w == VW;
     const size_t tokq = (size_t)H * KD, tokv = (size_t)H * Dv;
     const u16 *kg = reinterpret_cast<const u16 *>(args.k) + ((size_t)b * T * H + h) * KD;
     const u16 *qg = reinterpret_cast<const u16 *>(args.q) + ((size_t)b * T * H + h) * KD;
@@ -291,29 +294,35 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
     const u16 *tg = reinterpret_cast<const u16 *>(args.tmat) + (size_t)bh * NT * C * C;
     const float *betag = args.beta + (size_t)b * T * H + h, *gg = args.g + (size_t)b * T * H + h;
 
-    // Loads are unconditional (rows past T are clamped to T-1 and zeroed when
-    // committed) into native vector registers, so nothing waits for them
-    // until the commit one chunk later.
-    u32x4 rk[8], rt[PT], rv;
-    float rbv = 0.f, rbeta = 0.f, rg = 0.f;
+    // Within a role the loads are unconditional (rows past T are clamped to
+    // T-1 and zeroed when committed) into native vector registers, so nothing
+    // waits for them until the commit one chunk later.
+    u32x4 rk[8], rt[PT], rv[PV];
+    float rbv[PV], rbeta = 0.f, rg = 0.f;
     auto prefetch = [&](int c) {
         const int t0 = c * C;
+        if (kwave) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int t = min(t0 + tb8 * 8 + j, tlast);
-            rk[j] = *reinterpret_cast<const u32x4 *>(kg + (size_t)t * tokq + kb8 * 8);
+            for (int j = 0; j < 8; ++j) {
+                const int t = min(t0 + tb8 * 8 + j, tlast);
+                rk[j] = *reinterpret_cast<const u32x4 *>(kg + (size_t)t * tokq + kb8 * 8);
+            }
         }
 #pragma unroll
         for (int q = 0; q < PT; ++q)
             rt[q] = reinterpret_cast<const u32x4 *>(tg + (size_t)c * C * C)[ltid + NLD * q];
-        {
-            const int t = min(t0 + vtok, tlast);
-            rv = *reinterpret_cast<const u32x4 *>(vg + (size_t)t * tokv + vcv * 8);
-            rbv = betag[(size_t)t * H];
+        if (vwave) {
+#pragma unroll
+            for (int q = 0; q < PV; ++q) {
+                const int vidx = l + 64 * q;
+                const int t = min(t0 + vidx % C, tlast);
+                rv[q] = *reinterpret_cast<const u32x4 *>(vg + (size_t)t * tokv + (vidx / C) * 8);
+                rbv[q] = betag[(size_t)t * H];
+            }
+            const int tt = min(t0 + l, tlast);
+            rbeta = betag[(size_t)tt * H];
+            rg = gg[(size_t)tt * H];
         }
-        const int tt = min(t0 + l, tlast);
-        rbeta = betag[(size_t)tt * H];
-        rg = gg[(size_t)tt * H];
     };
     auto commit = [&](int c) {
         const int p = c & 1, t0 = c * C;
@@ -337,15 +346,18 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
             const int i = idx / (C / 8), cv = idx % (C / 8);
             *reinterpret_cast<u32x4 *>(tb + i * LDT + cv * 8) = rt[q];
         }
-        if (vid >= 0) {                         // beta V, transposed to [j][t]
-            const float bt = (t0 + vtok < T) ? rbv : 0.f;
+        if (vwave) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t wv = rv[e >> 1];
-                bv[(vcv * 8 + e) * LDBV + vtok] = bt * bf16_to_f32((u16)((e & 1) ? (wv >> 16) : (wv & 0xffffu)));
+            for (int q = 0; q < PV; ++q) {      // beta V, transposed to [j][t]
+                const int vidx = l + 64 * q, vtok = vidx % C, vcv = vidx / C;
+                const float bt = (t0 + vtok < T) ? rbv[q] : 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t wv = rv[q][e >> 1];
+                    bv[(vcv * 8 + e) * LDBV + vtok] = bt * bf16_to_f32((u16)((e & 1) ? (wv >> 16) : (wv & 0xffffu)));
+                }
             }
-        }
-        if (gwave) {                            // the cumsum and the gate table
+            // the cumsum and the gate table
             const bool ok = l < C && t0 + l < T;
             float gs = ok ? rg : 0.f;
 #pragma unroll
@@ -366,81 +378,66 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
         }
     };
 
-    bf16x8 qa[NKS], qn[NKS];                    // Q tile of the current / next chunk (A-operand layout)
-    shortx4 pqh[NTT], pql[NTT];                 // P tiles of the previous chunk (x16 A operand)
-    floatx4 a1 = zero4();                       // Q S_start of the previous chunk
-    floatx4 egp = zero4();                      // e^{G_t} of the previous chunk's rows
-    auto load_q = [&](int c, bf16x8 (&dst)[NKS]) {   // rows past T only feed rows that are not stored
-        const int t = min(c * C + ow * 16 + c16, tlast);
-#pragma unroll
-        for (int m = 0; m < NKS; ++m)
-            dst[m] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)t * tokq + m * 32 + 8 * g);
-    };
-    auto out_iter = [&](int c, bf16x8 (&qcur)[NKS], bf16x8 (&qnext)[NKS]) {
+    constexpr int NLOW = NTT * (NTT + 1) / 2;
+    bf16x8 qf[NKS];                             // Q fragments of chunk c-1 (B operand, token = lane%16)
+    u32x4 pf[NTT];                              // P fragments of chunk c-1, row tile ow: {hi01, hi23, lo01, lo23}
+    float egt = 0.f;                            // e^{G_t} of this lane's token in chunk c-1
+    const uint4 *pfg = reinterpret_cast<const uint4 *>(args.pfrag) + (size_t)bh * NT * NLOW * 64 +
+                       (ow * (ow + 1) / 2) * 64 + l;
+    auto out_iter = [&](int c) {
         const int p = c & 1;
-        // finish the output of chunk c-1
         if (c > 0) {
-            const float *vnp = Vn(p ^ 1);
-            floatx4 a2 = zero4();
-#pragma unroll
-            for (int tj = 0; tj < NTT; ++tj) {
-                if (tj <= ow) {
-                    shortx4 bh4, bl4;
-                    split4(*reinterpret_cast<const floatx4 *>(vnp + c16 * LDVF + tj * 16 + 4 * g), bh4, bl4);
-                    a2 = mfma16(pqh[tj], bh4, a2);
-                    a2 = mfma16(pqh[tj], bl4, a2);
-                    a2 = mfma16(pql[tj], bh4, a2);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tt = (c - 1) * C + ow * 16 + 4 * g + e;
-                if (tt < T) {
-                    const float ov = args.scale * (egp[e] * a1[e] + a2[e]);
-                    const size_t off = (((size_t)b * T + tt) * H + h) * Dv + v0 + c16;
-                    if (args.out_bf16) reinterpret_cast<u16 *>(args.o)[off] = bf16_bits(ov);
-                    else reinterpret_cast<float *>(args.o)[off] = ov;
-                }
-            }
-        }
-        if (c < NT) {
-            if (c + 1 < NT) load_q(c + 1, qnext);
-            // P and Q S_start of chunk c
-            const u16 *ks = Ks(p);
-            const float *gp = gate(p);
-            const int t = ow * 16 + c16;               // this lane's row of P
-            const float g2t = gp[C + t];
-#pragma unroll
-            for (int tj = 0; tj < NTT; ++tj) {
-                if (tj <= ow) {
-                    // P^T tile: rows s of K, columns t of Q (B operand = Q fragments)
-                    floatx4 acc = zero4();
-                    const u16 *krow = ks + (tj * 16 + c16) * LDK;
-#pragma unroll
-                    for (int m = 0; m < NKS; ++m) acc = mfma32(ld8(krow + m * 32 + 8 * g), qcur[m], acc);
-                    const floatx4 g2s = *reinterpret_cast<const floatx4 *>(gp + C + tj * 16 + 4 * g);
-                    floatx4 pv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s = tj * 16 + 4 * g + e;
-                        pv[e] = s <= t ? acc[e] * fast_exp2(fminf(g2t - g2s[e], 0.f)) : 0.f;
-                    }
-                    split4(pv, pqh[tj], pql[tj]);
-                }
-            }
-            const float *st = St(p);
-            a1 = zero4();
+            // O^T of chunk c-1: a1 = S_start^T Q^T, a2 = V_new^T P^T
+            const float *st = St(p ^ 1), *vnp = Vn(p ^ 1);
+            floatx4 a1 = zero4(), a2 = zero4();
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
                 const floatx4 s0 = *reinterpret_cast<const floatx4 *>(st + c16 * LDSF + m * 32 + 8 * g);
                 const floatx4 s1 = *reinterpret_cast<const floatx4 *>(st + c16 * LDSF + m * 32 + 8 * g + 4);
                 bf16x8 sh, sl;
                 frag_split(s0, s1, sh, sl);
-                a1 = mfma32(qcur[m], sh, a1);
-                a1 = mfma32(qcur[m], sl, a1);
+                a1 = mfma32(sh, qf[m], a1);
+                a1 = mfma32(sl, qf[m], a1);
             }
-            egp = *reinterpret_cast<const floatx4 *>(gp + 2 * C + ow * 16 + 4 * g);
-            // stage chunk c+1, start loading chunk c+2
+#pragma unroll
+            for (int tj = 0; tj < NTT; ++tj) {
+                if (tj <= ow) {
+                    shortx4 vh4, vl4;
+                    split4(*reinterpret_cast<const floatx4 *>(vnp + c16 * LDVF + tj * 16 + 4 * g), vh4, vl4);
+                    const shortx4 ph = __builtin_bit_cast(shortx4, uint2{pf[tj][0], pf[tj][1]});
+                    const shortx4 pl = __builtin_bit_cast(shortx4, uint2{pf[tj][2], pf[tj][3]});
+                    a2 = mfma16(vh4, ph, a2);
+                    a2 = mfma16(vh4, pl, a2);
+                    a2 = mfma16(vl4, ph, a2);
+                }
+            }
+            const int tt = (c - 1) * C + ow * 16 + c16;
+            if (tt < T) {
+                const float sc = args.scale;
+                floatx4 ov;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ov[e] = sc * (egt * a1[e] + a2[e]);
+                const size_t off = (((size_t)b * T + tt) * H + h) * Dv + v0 + 4 * g;
+                if (args.out_bf16)
+                    *reinterpret_cast<uint2 *>(reinterpret_cast<u16 *>(args.o) + off) =
+                        uint2{cvt2_bf16(ov[0], ov[1]), cvt2_bf16(ov[2], ov[3])};
+                else
+                    *reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(args.o) + off) = ov;
+            }
+        }
+        if (c < NT) {
+            // operands of chunk c's output (used next iteration), then staging
+            {
+                const int t = min(c * C + ow * 16 + c16, tlast);   // rows past T are never stored
+#pragma unroll
+                for (int m = 0; m < NKS; ++m)
+                    qf[m] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)t * tokq + m * 32 + 8 * g);
+                const uint4 *pc = pfg + (size_t)c * NLOW * 64;
+#pragma unroll
+                for (int tj = 0; tj < NTT; ++tj)
+                    if (tj <= ow) pf[tj] = __builtin_bit_cast(u32x4, pc[tj * 64]);
+            }
+            egt = gate(p)[2 * C + ow * 16 + c16];
             if (c + 1 < NT) commit(c + 1);
             if (c + 2 < NT) prefetch(c + 2);
         }
@@ -450,13 +447,9 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
         prefetch(0);
         commit(0);
         if (NT > 1) prefetch(1);
-        load_q(0, qa);
     }
     __syncthreads();
-    for (int c = 0; c <= NT; c += 2) {
-        out_iter(c, qa, qn);
-        if (c + 1 <= NT) out_iter(c + 1, qn, qa);
-    }
+    for (int c = 0; c <= NT; ++c) out_iter(c);
 }
 
 }  // namespace gdn

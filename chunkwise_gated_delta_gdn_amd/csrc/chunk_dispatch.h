@@ -12,12 +12,16 @@ namespace gdn {
 // general 8-wave state pass.
 template <bool F32IN, int KD, int C, int R>
 constexpr bool use_chain1() {
-    return !F32IN && R == 1 && C % 32 == 0 && KD % 32 == 0;
+    return ChunkShape<F32IN, KD, C, R>::PFRAG;
 }
 
 // Launch both kernels of one instantiation on `stream`.
 template <bool F32IN, int KD, int C, int R>
-hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream) {
+hipError_t launch_chunk_fwd(const ChunkArgs &args, hipStream_t stream) {
+    ChunkArgs a = args;
+    a.pfrag = use_chain1<F32IN, KD, C, R>()
+                  ? static_cast<void *>(static_cast<char *>(a.tmat) + chunk_tmat_bytes<F32IN, KD, C, R>(a.B, a.T, a.H))
+                  : nullptr;
     const int NT = (a.T + C - 1) / C;
     const int nbh = a.B * a.H;
     if (nbh == 0) return hipSuccess;

@@ -58,6 +58,7 @@ struct ChunkArgs {
     float *hT;
     void *o;
     void *tmat;      // work space: T per chunk, [B*H][NT][NR][NR]
+    void *pfrag;     // work space: intra-chunk P tiles as MFMA fragments (PFRAG shapes)
     int B, T, H, Dv;
     int out_bf16;
     float scale;
@@ -106,6 +107,12 @@ struct ChunkShape {
     static constexpr int LDRT = NR + PAD;      // RT:      [BV][NR]
     static constexpr int LDVT = C + PAD;       // Vn/Vt:   [R][BV][C]
     static constexpr int LDY = 17;             // merge scratch [16][17] fp32
+    // bf16 inputs, one step per token, 32-multiple widths: the solve kernel
+    // also writes the causal intra-chunk scores P[t][s] = [s<=t] (q_t.k_s)
+    // e^{G_t - G_s} of the NLOW lower 16x16 tiles, as hi/lo bf16 MFMA
+    // fragments (lane l: row t = 16*ti + l%16, columns s = 16*tj + 4*(l/16)
+    // + e), 64 lanes x 16 bytes per tile, tile (ti, tj) at ti*(ti+1)/2 + tj.
+    static constexpr bool PFRAG = !F32IN && R == 1 && C % 32 == 0 && KD % 32 == 0;
     static constexpr int al(int x) { return (x + 15) & ~15; }
     static_assert(KD % R == 0, "key width must split into R sub-keys");
     static_assert(DK % 16 == 0 && C % 16 == 0, "sizes must be multiples of 16");
@@ -204,6 +211,41 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(ChunkArgs args) {
     }
     __syncthreads();
 
+    // ---- causal scores P, row tile ti (one wave), written as fragments ----
+    auto p_rowtile = [&](int ti) {
+        if constexpr (S::PFRAG) {
+            const int c16 = l & 15, g = l >> 4;
+            const int tq = min(t0 + ti * 16 + c16, T - 1);
+            const u16 *qrow = reinterpret_cast<const u16 *>(args.q) + (((size_t)b * T + tq) * H + h) * KD;
+            bf16x8 qf[KD / 32];
+#pragma unroll
+            for (int m = 0; m < KD / 32; ++m) qf[m] = *reinterpret_cast<const bf16x8 *>(qrow + m * 32 + 8 * g);
+            const float g2t = G2[ti * 16 + c16];
+            uint4 *dst = reinterpret_cast<uint4 *>(args.pfrag) + ((size_t)bh * NT + c) * S::NLOW * 64 +
+                         (ti * (ti + 1) / 2) * 64 + l;
+            for (int tj = 0; tj <= ti; ++tj) {
+                floatx4 acc = zero4();
+                const u16 *krow = reinterpret_cast<const u16 *>(Ks) + (tj * 16 + c16) * LDK;
+#pragma unroll
+                for (int m = 0; m < KD / 32; ++m)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld8(krow + m * 32 + 8 * g), qf[m], acc, 0, 0, 0);
+                float pv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = tj * 16 + 4 * g + e;
+                    pv[e] = s <= ti * 16 + c16 ? acc[e] * fast_exp2(fminf(g2t - G2[s], 0.f)) : 0.f;
+                }
+                uint4 f;
+                split2_bf16(pv[0], pv[1], f.x, f.z);
+                split2_bf16(pv[2], pv[3], f.y, f.w);
+                dst[tj * 64] = f;
+            }
+        }
+    };
+    if constexpr (S::PFRAG) {
+        if (w != 0 && w < S::NTT) p_rowtile(S::NTT - w);   // overlaps wave 0's substitution
+    }
+
     // ---- diagonal 16x16 blocks: forward substitution, one lane per column ----
     if (w == 0) {
         const int ib = l >> 4, col = l & 15;
@@ -221,6 +263,7 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(ChunkArgs args) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) Tc[i * LDA] = x[i];
         }
+        if constexpr (S::PFRAG) p_rowtile(0);
     }
     __syncthreads();
 
@@ -644,11 +687,19 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
     }
 }
 
+// Work space: T of every chunk, then (PFRAG shapes) the P fragments.
+template <bool F32IN, int KD, int C, int R>
+size_t chunk_tmat_bytes(int B, int T, int H) {
+    using S = ChunkShape<F32IN, KD, C, R>;
+    const size_t NT = (size_t)(T + C - 1) / C;
+    return ((size_t)B * H * NT * S::NR * S::NR * S::ESZ + 255) & ~(size_t)255;
+}
 template <bool F32IN, int KD, int C, int R>
 size_t chunk_workspace_bytes(int B, int T, int H) {
     using S = ChunkShape<F32IN, KD, C, R>;
     const size_t NT = (size_t)(T + C - 1) / C;
-    return (size_t)B * H * NT * S::NR * S::NR * S::ESZ;
+    const size_t pbytes = S::PFRAG ? (size_t)B * H * NT * S::NLOW * 64 * 16 : 0;
+    return chunk_tmat_bytes<F32IN, KD, C, R>(B, T, H) + pbytes;
 }
 
 }  // namespace gdn
