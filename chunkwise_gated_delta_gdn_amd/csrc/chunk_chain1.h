@@ -32,6 +32,8 @@
 // chunk c-1 and stage chunk c+1.
 #pragma once
 
+#include <type_traits>
+
 #include "chunk_kernels.h"
 
 namespace gdn {
@@ -271,8 +273,12 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
     // =====================================================================
     // out waves
     // =====================================================================
-    const int ow = NTT - w;                     // token tile of this wave (wave 1: the last)
-    const int ltid = tid - 64;                  // loader thread index
+    // Each out wave runs a copy of the loop specialised for its token tile
+    // OW (wave 1: the last tile) and its loader roles, so that its global
+    // loads are straight-line code: the hardware counter of outstanding loads
+    // is in order, and a load skipped on some path would make the compiler
+    // wait for every load issued after the one it needs.
+    //
     // Loader roles: threads [0, NB8) stage one 8x8 block of K each; wave VW
     // the V slice (C/32 16-byte vectors per lane) and the gate table; every
     // thread C/32 vectors of T.  The last wave (the lightest output tile)
@@ -282,11 +288,11 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
     constexpr int PT = NTV / NLD;
     constexpr int PV = C / 32;                  // V vectors per lane of wave VW
     constexpr int VW = NTT >= 3 ? 3 : NTT;
+    constexpr int NLOW = NTT * (NTT + 1) / 2;
     static_assert(PT * NLD == NTV && PV * 64 == 2 * C, "loader split");
+    const int ltid = tid - 64;                  // loader thread index
     const bool kload = ltid < NB8;
-    const int kb8 = ltid % (KD / 8), tb8 = min(ltid / (KD / 8), C / 8 - 1);
-    // wave-uniform roles
-    const bool kwave = (w - 1) * 64 < NB8, vwave = w == VW;
+    const int kb8 = kload ? ltid % (KD / 8) : 0, tb8 = kload ? ltid / (KD / 8) : 0;
     const size_t tokq = (size_t)H * KD, tokv = (size_t)H * Dv;
     const u16 *kg = reinterpret_cast<const u16 *>(args.k) + ((size_t)b * T * H + h) * KD;
     const u16 *qg = reinterpret_cast<const u16 *>(args.q) + ((size_t)b * T * H + h) * KD;
@@ -294,101 +300,118 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
     const u16 *tg = reinterpret_cast<const u16 *>(args.tmat) + (size_t)bh * NT * C * C;
     const float *betag = args.beta + (size_t)b * T * H + h, *gg = args.g + (size_t)b * T * H + h;
 
-    // Within a role the loads are unconditional (rows past T are clamped to
-    // T-1 and zeroed when committed) into native vector registers, so nothing
-    // waits for them until the commit one chunk later.
-    u32x4 rk[8], rt[PT], rv[PV];
-    float rbv[PV], rbeta = 0.f, rg = 0.f;
-    auto prefetch = [&](int c) {
-        const int t0 = c * C;
-        if (kwave) {
+    auto out_wave = [&](auto owc) {
+        constexpr int OW = decltype(owc)::value;
+        constexpr int WV = NTT - OW;            // this wave's index
+        constexpr bool KW = (WV - 1) * 64 < NB8, VWV = WV == VW;
+        // Rows past T are clamped to T-1 (and zeroed when committed); a chunk
+        // index past the end is clamped to the last chunk (its staging then
+        // lands in a buffer no one reads).
+        u32x4 rk[8], rt[PT], rv[PV];
+        float rbv[PV], rbeta = 0.f, rg = 0.f;
+        auto prefetch = [&](int c) {
+            c = min(c, NT - 1);
+            const int t0 = c * C;
+            if constexpr (KW) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int t = min(t0 + tb8 * 8 + j, tlast);
-                rk[j] = *reinterpret_cast<const u32x4 *>(kg + (size_t)t * tokq + kb8 * 8);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < PT; ++q)
-            rt[q] = reinterpret_cast<const u32x4 *>(tg + (size_t)c * C * C)[ltid + NLD * q];
-        if (vwave) {
-#pragma unroll
-            for (int q = 0; q < PV; ++q) {
-                const int vidx = l + 64 * q;
-                const int t = min(t0 + vidx % C, tlast);
-                rv[q] = *reinterpret_cast<const u32x4 *>(vg + (size_t)t * tokv + (vidx / C) * 8);
-                rbv[q] = betag[(size_t)t * H];
-            }
-            const int tt = min(t0 + l, tlast);
-            rbeta = betag[(size_t)tt * H];
-            rg = gg[(size_t)tt * H];
-        }
-    };
-    auto commit = [&](int c) {
-        const int p = c & 1, t0 = c * C;
-        u16 *ks = Ks(p), *kt = KsT(p), *tb = Tb(p);
-        float *bv = BVs(p), *gp = gate(p);
-        if (kload) {
-            u32x4 rows[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                rows[j] = (t0 + tb8 * 8 + j < T) ? rk[j] : u32x4{0u, 0u, 0u, 0u};
-                *reinterpret_cast<u32x4 *>(ks + (tb8 * 8 + j) * LDK + kb8 * 8) = rows[j];
-            }
-            // row kb8*8+e of K^T: chunk tb8 stored at tb8 ^ (kb8 & SWM)
-            u16 *ktb = kt + (kb8 * 8) * LDKT + ((tb8 ^ (kb8 & SWM)) * 8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4 *>(ktb + e * LDKT) = block_col(rows, e);
-        }
-#pragma unroll
-        for (int q = 0; q < PT; ++q) {
-            const int idx = ltid + NLD * q;
-            const int i = idx / (C / 8), cv = idx % (C / 8);
-            *reinterpret_cast<u32x4 *>(tb + i * LDT + cv * 8) = rt[q];
-        }
-        if (vwave) {
-#pragma unroll
-            for (int q = 0; q < PV; ++q) {      // beta V, transposed to [j][t]
-                const int vidx = l + 64 * q, vtok = vidx % C, vcv = vidx / C;
-                const float bt = (t0 + vtok < T) ? rbv[q] : 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t wv = rv[q][e >> 1];
-                    bv[(vcv * 8 + e) * LDBV + vtok] = bt * bf16_to_f32((u16)((e & 1) ? (wv >> 16) : (wv & 0xffffu)));
+                for (int j = 0; j < 8; ++j) {
+                    const int t = min(t0 + tb8 * 8 + j, tlast);
+                    rk[j] = *reinterpret_cast<const u32x4 *>(kg + (size_t)t * tokq + kb8 * 8);
                 }
             }
-            // the cumsum and the gate table
-            const bool ok = l < C && t0 + l < T;
-            float gs = ok ? rg : 0.f;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(gs, off, 64);
-                if (l >= off) gs += y;
+            for (int q = 0; q < PT; ++q)
+                rt[q] = reinterpret_cast<const u32x4 *>(tg + (size_t)c * C * C)[ltid + NLD * q];
+            if constexpr (VWV) {
+#pragma unroll
+                for (int q = 0; q < PV; ++q) {
+                    const int vidx = l + 64 * q;
+                    const int t = min(t0 + vidx % C, tlast);
+                    rv[q] = *reinterpret_cast<const u32x4 *>(vg + (size_t)t * tokv + (vidx / C) * 8);
+                    rbv[q] = betag[(size_t)t * H];
+                }
+                const int tt = min(t0 + l, tlast);
+                rbeta = betag[(size_t)tt * H];
+                rg = gg[(size_t)tt * H];
             }
-            const float g2 = gs * LOG2E;
-            const float g2l = __shfl(g2, C - 1, 64);
-            if (l < C) {
-                const float eg = fast_exp2(g2);
-                gp[l] = (ok ? rbeta : 0.f) * eg;         // beta e^{G_t}
-                gp[C + l] = g2;                          // G2
-                gp[2 * C + l] = eg;                      // e^{G_t}
-                gp[3 * C + l] = fast_exp2(g2l - g2);     // e^{G_L - G_t}
+        };
+        auto commit = [&](int c) {
+            const int p = c & 1, t0 = c * C;
+            u16 *ks = Ks(p), *kt = KsT(p), *tb = Tb(p);
+            float *bv = BVs(p), *gp = gate(p);
+            if constexpr (KW) {
+                if (kload) {
+                    u32x4 rows[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        rows[j] = (t0 + tb8 * 8 + j < T) ? rk[j] : u32x4{0u, 0u, 0u, 0u};
+                        *reinterpret_cast<u32x4 *>(ks + (tb8 * 8 + j) * LDK + kb8 * 8) = rows[j];
+                    }
+                    // row kb8*8+e of K^T: chunk tb8 stored at tb8 ^ (kb8 & SWM)
+                    u16 *ktb = kt + (kb8 * 8) * LDKT + ((tb8 ^ (kb8 & SWM)) * 8);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4 *>(ktb + e * LDKT) = block_col(rows, e);
+                }
             }
-            if (l == 0) gp[4 * C] = fast_exp2(g2l);     // e^{G_L}
-        }
-    };
+#pragma unroll
+            for (int q = 0; q < PT; ++q) {
+                const int idx = ltid + NLD * q;
+                const int i = idx / (C / 8), cv = idx % (C / 8);
+                *reinterpret_cast<u32x4 *>(tb + i * LDT + cv * 8) = rt[q];
+            }
+            if constexpr (VWV) {
+#pragma unroll
+                for (int q = 0; q < PV; ++q) {  // beta V, transposed to [j][t]
+                    const int vidx = l + 64 * q, vtok = vidx % C, vcv = vidx / C;
+                    const float bt = (t0 + vtok < T) ? rbv[q] : 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t wv = rv[q][e >> 1];
+                        bv[(vcv * 8 + e) * LDBV + vtok] =
+                            bt * bf16_to_f32((u16)((e & 1) ? (wv >> 16) : (wv & 0xffffu)));
+                    }
+                }
+                // the cumsum and the gate table
+                const bool ok = l < C && t0 + l < T;
+                float gs = ok ? rg : 0.f;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float y = __shfl_up(gs, off, 64);
+                    if (l >= off) gs += y;
+                }
+                const float g2 = gs * LOG2E;
+                const float g2l = __shfl(g2, C - 1, 64);
+                if (l < C) {
+                    const float eg = fast_exp2(g2);
+                    gp[l] = (ok ? rbeta : 0.f) * eg;         // beta e^{G_t}
+                    gp[C + l] = g2;                          // G2
+                    gp[2 * C + l] = eg;                      // e^{G_t}
+                    gp[3 * C + l] = fast_exp2(g2l - g2);     // e^{G_L - G_t}
+                }
+                if (l == 0) gp[4 * C] = fast_exp2(g2l);     // e^{G_L}
+            }
+        };
 
-    constexpr int NLOW = NTT * (NTT + 1) / 2;
-    bf16x8 qf[NKS];                             // Q fragments of chunk c-1 (B operand, token = lane%16)
-    u32x4 pf[NTT];                              // P fragments of chunk c-1, row tile ow: {hi01, hi23, lo01, lo23}
-    float egt = 0.f;                            // e^{G_t} of this lane's token in chunk c-1
-    const uint4 *pfg = reinterpret_cast<const uint4 *>(args.pfrag) + (size_t)bh * NT * NLOW * 64 +
-                       (ow * (ow + 1) / 2) * 64 + l;
-    auto out_iter = [&](int c) {
-        const int p = c & 1;
-        if (c > 0) {
-            // O^T of chunk c-1: a1 = S_start^T Q^T, a2 = V_new^T P^T
-            const float *st = St(p ^ 1), *vnp = Vn(p ^ 1);
+        bf16x8 qf[NKS];                         // Q fragments (B operand, token = lane%16)
+        u32x4 pf[OW + 1];                       // P fragments of row tile OW: {hi01, hi23, lo01, lo23}
+        float egt = 0.f;                        // e^{G_t} of this lane's token
+        floatx4 ov = zero4();                   // output of the previous chunk
+        const uint4 *pfg = reinterpret_cast<const uint4 *>(args.pfrag) + (size_t)bh * NT * NLOW * 64 +
+                           (OW * (OW + 1) / 2) * 64 + l;
+        // operands of chunk c's output, used one iteration later
+        auto load_qp = [&](int c) {
+            const int t = min(c * C + OW * 16 + c16, tlast);   // rows past T are never stored
+#pragma unroll
+            for (int m = 0; m < NKS; ++m)
+                qf[m] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)t * tokq + m * 32 + 8 * g);
+            const uint4 *pc = pfg + (size_t)c * NLOW * 64;
+#pragma unroll
+            for (int tj = 0; tj <= OW; ++tj) pf[tj] = __builtin_bit_cast(u32x4, pc[tj * 64]);
+            egt = gate(c & 1)[2 * C + OW * 16 + c16];
+        };
+        // O^T of chunk c: a1 = S_start^T Q^T, a2 = V_new^T P^T (buffers c & 1)
+        auto compute_out = [&](int c) {
+            const float *st = St(c & 1), *vnp = Vn(c & 1);
             floatx4 a1 = zero4(), a2 = zero4();
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
@@ -400,23 +423,22 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
                 a1 = mfma32(sl, qf[m], a1);
             }
 #pragma unroll
-            for (int tj = 0; tj < NTT; ++tj) {
-                if (tj <= ow) {
-                    shortx4 vh4, vl4;
-                    split4(*reinterpret_cast<const floatx4 *>(vnp + c16 * LDVF + tj * 16 + 4 * g), vh4, vl4);
-                    const shortx4 ph = __builtin_bit_cast(shortx4, uint2{pf[tj][0], pf[tj][1]});
-                    const shortx4 pl = __builtin_bit_cast(shortx4, uint2{pf[tj][2], pf[tj][3]});
-                    a2 = mfma16(vh4, ph, a2);
-                    a2 = mfma16(vh4, pl, a2);
-                    a2 = mfma16(vl4, ph, a2);
-                }
+            for (int tj = 0; tj <= OW; ++tj) {
+                shortx4 vh4, vl4;
+                split4(*reinterpret_cast<const floatx4 *>(vnp + c16 * LDVF + tj * 16 + 4 * g), vh4, vl4);
+                const shortx4 ph = __builtin_bit_cast(shortx4, uint2{pf[tj][0], pf[tj][1]});
+                const shortx4 pl = __builtin_bit_cast(shortx4, uint2{pf[tj][2], pf[tj][3]});
+                a2 = mfma16(vh4, ph, a2);
+                a2 = mfma16(vh4, pl, a2);
+                a2 = mfma16(vl4, ph, a2);
             }
-            const int tt = (c - 1) * C + ow * 16 + c16;
-            if (tt < T) {
-                const float sc = args.scale;
-                floatx4 ov;
+            const float sc = args.scale;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ov[e] = sc * (egt * a1[e] + a2[e]);
+            for (int e = 0; e < 4; ++e) ov[e] = sc * (egt * a1[e] + a2[e]);
+        };
+        auto store_out = [&](int c) {
+            const int tt = c * C + OW * 16 + c16;
+            if (tt < T) {
                 const size_t off = (((size_t)b * T + tt) * H + h) * Dv + v0 + 4 * g;
                 if (args.out_bf16)
                     *reinterpret_cast<uint2 *>(reinterpret_cast<u16 *>(args.o) + off) =
@@ -424,32 +446,42 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
                 else
                     *reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(args.o) + off) = ov;
             }
-        }
-        if (c < NT) {
-            // operands of chunk c's output (used next iteration), then staging
-            {
-                const int t = min(c * C + ow * 16 + c16, tlast);   // rows past T are never stored
-#pragma unroll
-                for (int m = 0; m < NKS; ++m)
-                    qf[m] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)t * tokq + m * 32 + 8 * g);
-                const uint4 *pc = pfg + (size_t)c * NLOW * 64;
-#pragma unroll
-                for (int tj = 0; tj < NTT; ++tj)
-                    if (tj <= ow) pf[tj] = __builtin_bit_cast(u32x4, pc[tj * 64]);
-            }
-            egt = gate(p)[2 * C + ow * 16 + c16];
-            if (c + 1 < NT) commit(c + 1);
-            if (c + 2 < NT) prefetch(c + 2);
-        }
-        __syncthreads();
-    };
-    if (NT > 0) {
+        };
+
+        // Iteration c (one barrier each): output of chunk c-1, operands of
+        // chunk c, commit of chunk c+1, prefetch of chunk c+2.
         prefetch(0);
         commit(0);
-        if (NT > 1) prefetch(1);
+        prefetch(1);
+        __syncthreads();
+        load_qp(0);
+        commit(1);
+        prefetch(2);
+        __syncthreads();
+        for (int c = 1; c < NT; ++c) {
+            compute_out(c - 1);
+            load_qp(c);
+            commit(c + 1);
+            prefetch(c + 2);
+            store_out(c - 1);
+            __syncthreads();
+        }
+        compute_out(NT - 1);
+        store_out(NT - 1);
+        __syncthreads();
+    };
+    if (NT == 0) {                              // no chunks: match the chain wave's two barriers
+        __syncthreads();
+        __syncthreads();
+        return;
     }
-    __syncthreads();
-    for (int c = 0; c <= NT; ++c) out_iter(c);
+    const int ow = NTT - w;                     // token tile of this wave (wave 1: the last)
+    if (ow == 0) out_wave(std::integral_constant<int, 0>{});
+    if (ow == 1) out_wave(std::integral_constant<int, 1>{});
+    if constexpr (NTT == 4) {
+        if (ow == 2) out_wave(std::integral_constant<int, 2>{});
+        if (ow == 3) out_wave(std::integral_constant<int, 3>{});
+    }
 }
 
 }  // namespace gdn
