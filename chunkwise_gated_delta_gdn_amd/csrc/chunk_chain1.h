@@ -9,23 +9,28 @@
 // its own registers live):
 //
 //   wave 0 ("chain") owns the (KD x 16) fp32 state slice in MFMA
-//   accumulators and runs the dependent part of every chunk in registers:
-//       X = K S;  R = beta V - (beta e^G) X;  V_new = T R;
+//   accumulators and runs the dependent part of every chunk in registers,
+//   in the page's WY form (u - w h):
+//       V_new = U - W S,  U = T diag(beta) V,  W = T diag(beta e^G) K;
 //       S <- e^{G_L} S + K^T diag(e^{G_L - G}) V_new.
+//   W comes from the solve kernel; U does not depend on S, so its MFMAs
+//   overlap those of W S.
 //   An MFMA accumulator tile (lane l holds rows 4*(l/16)+e, column l%16) is
 //   fed back as the B operand of the next product by reading the k index of
 //   a 32-wide MFMA step in the order {4g..4g+3, 16+4g..16+4g+3} (g = l/16)
-//   instead of 8g..8g+7; the A operand is read from LDS in the same order,
-//   so the sum over k is unchanged.  It publishes V_new and the chunk-start
-//   state to LDS in fp32 for the output waves.
+//   instead of 8g..8g+7; the A operand rows (W, K^T) are stored in that
+//   permuted order by the solve kernel, so each lane reads them as one
+//   16-byte piece and the sum over k is unchanged.  It publishes V_new and
+//   the chunk-start state to LDS in fp32 for the output waves.
 //
 //   waves 1..C/16 ("out"), one 16-token tile each: the output, transposed,
 //   O^T = S_start^T Q^T e^G + V_new^T P^T (P, the causal intra-chunk scores,
 //   comes from the solve kernel as ready MFMA fragments; the transposed
 //   accumulator gives each lane 4 consecutive values of one token, one
 //   16-byte store), and the staging of the next chunks: a register prefetch
-//   one chunk ahead, then K and K^T (8x8 blocks transposed in registers), T,
-//   beta V (transposed) and the gate tables committed to LDS.
+//   one chunk ahead, then W, K^T and T (copied as written by the solve
+//   kernel), beta V (transposed, hi + lo bf16) and the gate table committed
+//   to LDS.
 //
 // One workgroup barrier per chunk.  Iteration c: the chain processes chunk c
 // and publishes its start state and V_new; the out waves write the output of
@@ -41,28 +46,35 @@ namespace gdn {
 template <int KD, int C>
 struct Chain1Shape {
     static constexpr int BV = 16;
-    static constexpr int NTT = C / 16;        // token tiles = out waves
-    static constexpr int NW = 1 + NTT;        // waves per workgroup
+    static constexpr int NTT = C / 16;        // token tiles
+    // Waves (they go to the four SIMDs of a CU in turn):
+    //   C = 64: 0 the chain; 4 idle (it only takes part in the barriers, so
+    //           the chain has its SIMD to itself); 1, 2, 3, 5 the output of
+    //           tiles 3, 2, 1, 0 and the staging of T, V and the gates; 6, 7
+    //           the staging of W and K^T.
+    //   C = 32: 0 the chain; 1, 2 the output of tiles 1, 0 and all staging.
+    static constexpr int IDLE = NTT == 4 ? 4 : -1;
+    static constexpr int NW = NTT == 4 ? 8 : 1 + NTT;
     static constexpr int NTHR = 64 * NW;
-    static constexpr int NLD = 64 * NTT;      // loader threads
+    static constexpr int NLA = 128;           // threads staging W and K^T
+    static constexpr int NLB = 64 * NTT;      // threads staging T and V
     static constexpr int NKS = KD / 32;       // 32-wide steps over the key dim
     static constexpr int NST = KD / 16;       // state row tiles
     static constexpr int NCS = C / 32;        // 32-wide steps over the tokens
-    static constexpr int NB8 = (C / 8) * (KD / 8);   // 8x8 blocks of K per chunk
     static constexpr int SWM = C / 8 - 1;     // K^T chunk swizzle mask
-    static constexpr int LDK = KD + 8;        // Ks  [C][KD]   bf16
-    static constexpr int LDKT = C + 8;        // KsT [KD][C]   bf16, 16-byte chunks swizzled
+    static constexpr int LDK = KD + 8;        // Ws  [C][KD]   bf16, W (permuted k order)
+    static constexpr int LDKT = C + 8;        // KsT [KD][C]   bf16, permuted, 16-byte chunks swizzled
     static constexpr int LDT = C + 8;         // Tb  [C][C]    bf16
-    static constexpr int LDBV = C + 4;        // BVs [BV][C]   fp32, beta V transposed
+    static constexpr int LDBV = C + 8;        // BVs [2][BV][C] bf16 hi, lo of beta V transposed
     static constexpr int LDSF = KD + 4;       // St  [BV][KD]  fp32, S_start transposed
     static constexpr int LDVF = C + 4;        // Vn  [BV][C]   fp32, V_new transposed
-    // gate table: beta e^G [C], G2 [C] (log2-scaled cumsum), e^G [C], e^{G_L-G} [C], e^{G_L}
-    static constexpr int NGATE = 4 * C + 4;
+    // gate table: e^G [C], e^{G_L-G} [C], e^{G_L}
+    static constexpr int NGATE = 2 * C + 4;
     static constexpr int al(int x) { return (x + 15) & ~15; }
     static constexpr int SZ_KS = al(C * LDK * 2);
     static constexpr int SZ_KST = al(KD * LDKT * 2);
     static constexpr int SZ_TB = al(C * LDT * 2);
-    static constexpr int SZ_BV = al(BV * LDBV * 4);
+    static constexpr int SZ_BV = al(2 * BV * LDBV * 2);
     static constexpr int SZ_GATE = al(NGATE * 4);
     static constexpr int SZ_ST = al(BV * LDSF * 4);
     static constexpr int SZ_VN = al(BV * LDVF * 4);
@@ -76,28 +88,8 @@ struct Chain1Shape {
     static constexpr int OFF_VN = OFF_ST + 2 * SZ_ST;
     static constexpr int BYTES = OFF_VN + 2 * SZ_VN;
     static_assert(C % 32 == 0 && C <= 64 && KD % 32 == 0, "32-wide MFMA steps");
-    static_assert(NB8 <= NLD, "one 8x8 block of K per loader thread");
-    static_assert(2 * C <= NLD, "one 16-byte vector of the V slice per loader thread");
     static_assert(BYTES <= 160 * 1024, "LDS budget of one workgroup exceeded");
 };
-
-// 8 bf16 of a k-contiguous row at k = base + {4g..4g+3, 16+4g..16+4g+3}: the
-// permuted k order of an accumulator-fed B operand.
-__device__ __forceinline__ bf16x8 ld_perm(const u16 *rowp, int base, int g) {
-    const uint2 lo = *reinterpret_cast<const uint2 *>(rowp + base + 4 * g);
-    const uint2 hi = *reinterpret_cast<const uint2 *>(rowp + base + 16 + 4 * g);
-    return __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
-}
-
-// The same read from a K^T row whose 16-byte chunks are swizzled: chunk j of
-// row r is stored at chunk j ^ ((r >> 3) & SWM).  `xr` = (r >> 3) & SWM.
-__device__ __forceinline__ bf16x8 ld_perm_swz(const u16 *rowp, int base, int g, int xr) {
-    const int c0 = ((base + 4 * g) >> 3) ^ xr, c1 = ((base + 16 + 4 * g) >> 3) ^ xr;
-    const int o = 4 * (g & 1);
-    const uint2 lo = *reinterpret_cast<const uint2 *>(rowp + c0 * 8 + o);
-    const uint2 hi = *reinterpret_cast<const uint2 *>(rowp + c1 * 8 + o);
-    return __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
-}
 
 // bf16 fragment of two accumulator tiles, in the permuted order (hi only).
 __device__ __forceinline__ bf16x8 frag_hi(const floatx4 &t0, const floatx4 &t1) {
@@ -130,26 +122,12 @@ __device__ __forceinline__ floatx4 mfma16(shortx4 a, shortx4 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// Column e (0..7) of an 8x8 bf16 block held as 8 rows of 4 words: the values
-// rows[0..7][e], packed as 4 words (v_perm_b32 picks one half of each of two
-// words).
-__device__ __forceinline__ u32x4 block_col(const u32x4 (&rows)[8], int e) {
-    const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    const int wd = e >> 1;
-    u32x4 r;
-    r.x = __builtin_amdgcn_perm(rows[1][wd], rows[0][wd], sel);
-    r.y = __builtin_amdgcn_perm(rows[3][wd], rows[2][wd], sel);
-    r.z = __builtin_amdgcn_perm(rows[5][wd], rows[4][wd], sel);
-    r.w = __builtin_amdgcn_perm(rows[7][wd], rows[6][wd], sel);
-    return r;
-}
-
 template <int KD, int C>
-__global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkArgs args) {
+__global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain1_kernel(ChunkArgs args) {
     using S = Chain1Shape<KD, C>;
-    constexpr int BV = S::BV, NTT = S::NTT, NKS = S::NKS, NST = S::NST, NCS = S::NCS, NLD = S::NLD;
+    constexpr int BV = S::BV, NTT = S::NTT, NKS = S::NKS, NST = S::NST, NCS = S::NCS;
     constexpr int LDK = S::LDK, LDKT = S::LDKT, LDT = S::LDT, LDBV = S::LDBV, LDSF = S::LDSF, LDVF = S::LDVF;
-    constexpr int NB8 = S::NB8, SWM = S::SWM;
+    constexpr int SWM = S::SWM;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::BYTES];
 
@@ -160,6 +138,11 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
     const int vb = slot % nvb;
     const int bh = (slot / nvb) * 8 + xcd;      // all value slices of one head share an XCD
     if (bh >= args.B * args.H) return;
+    if (w == S::IDLE) {                         // the chain wave's SIMD partner: barriers only
+        const int nb = (args.T + C - 1) / C + 2;
+        for (int i = 0; i < nb; ++i) __syncthreads();
+        return;
+    }
     const int b = bh / args.H, h = bh % args.H;
     const int v0 = vb * BV;
     const int T = args.T, H = args.H, Dv = args.Dv;
@@ -169,7 +152,7 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
     auto Ks = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_KS + p * S::SZ_KS); };
     auto KsT = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_KST + p * S::SZ_KST); };
     auto Tb = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_TB + p * S::SZ_TB); };
-    auto BVs = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_BV + p * S::SZ_BV); };
+    auto BVs = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_BV + p * S::SZ_BV); };
     auto gate = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_GATE + p * S::SZ_GATE); };
     auto St = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_ST + p * S::SZ_ST); };
     auto Vn = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_VN + p * S::SZ_VN); };
@@ -197,65 +180,87 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
         __syncthreads();
         for (int c = 0; c < NT; ++c) {
             const int p = c & 1;
-            const u16 *ks = Ks(p), *kt = KsT(p), *tb = Tb(p);
-            const float *bv = BVs(p), *gp = gate(p);
+            const u16 *ws = Ks(p), *kt = KsT(p), *tb = Tb(p), *bv = BVs(p);
+            const float *gp = gate(p);
+            // All LDS operands of W S and U first (nothing here depends on the
+            // state), so their latency overlaps; the MFMAs below run over the
+            // token tiles innermost, so consecutive MFMAs are independent.
+            bf16x8 wf[NTT][NKS], tf[NTT][NCS], bvh[NCS], bvl[NCS];
+#pragma unroll
+            for (int m = 0; m < NKS; ++m)
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt) wf[tt][m] = ld8(ws + (tt * 16 + c16) * LDK + m * 32 + 8 * g);
+#pragma unroll
+            for (int m = 0; m < NCS; ++m) {
+                bvh[m] = ld8(bv + c16 * LDBV + m * 32 + 8 * g);
+                bvl[m] = ld8(bv + (BV + c16) * LDBV + m * 32 + 8 * g);
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt)
+                    if (2 * m <= tt) tf[tt][m] = ld8(tb + (tt * 16 + c16) * LDT + m * 32 + 8 * g);
+            }
             bf16x8 sb[NKS];
 #pragma unroll
             for (int m = 0; m < NKS; ++m) sb[m] = frag_hi(Sreg[2 * m], Sreg[2 * m + 1]);
-            // X = K S, then R = beta V - (beta e^G) X, per token tile
-            floatx4 r[NTT];
+            publish_state(p);                    // S_start of chunk c
+            // X = W S and U = T (beta V) (T is block lower triangular)
+            floatx4 x[NTT], u[NTT];
 #pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) {
-                floatx4 x = zero4();
-                const u16 *kr = ks + (tt * 16 + c16) * LDK;
+            for (int tt = 0; tt < NTT; ++tt) x[tt] = u[tt] = zero4();
 #pragma unroll
-                for (int m = 0; m < NKS; ++m) x = mfma32(ld_perm(kr, m * 32, g), sb[m], x);
-                if (tt == 0) publish_state(p);   // S_start of chunk c, while the MFMAs run
-                const floatx4 bvt = *reinterpret_cast<const floatx4 *>(bv + c16 * LDBV + tt * 16 + 4 * g);
-                const floatx4 beg = *reinterpret_cast<const floatx4 *>(gp + tt * 16 + 4 * g);
+            for (int m = 0; m < NKS; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r[tt][e] = bvt[e] - beg[e] * x[e];
+                for (int tt = 0; tt < NTT; ++tt) x[tt] = mfma32(wf[tt][m], sb[m], x[tt]);
+#pragma unroll
+            for (int m = 0; m < NCS; ++m) {
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt)
+                    if (2 * m <= tt) u[tt] = mfma32(tf[tt][m], bvh[m], u[tt]);
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt)
+                    if (2 * m <= tt) u[tt] = mfma32(tf[tt][m], bvl[m], u[tt]);
             }
-            bf16x8 rh[NCS], rl[NCS];
+            // operands of the state update, read while the MFMAs run
+            bf16x8 kf[NST][NCS];
 #pragma unroll
-            for (int m = 0; m < NCS; ++m) frag_split(r[2 * m], r[2 * m + 1], rh[m], rl[m]);
-            // V_new = T R, published fp32 [j][s]; V~ = e^{G_L - G} V_new
+            for (int ti = 0; ti < NST; ++ti) {
+                const int xr = ((ti * 16 + c16) >> 3) & SWM;
+#pragma unroll
+                for (int m = 0; m < NCS; ++m) kf[ti][m] = ld8(kt + (ti * 16 + c16) * LDKT + (((4 * m + g) ^ xr) << 3));
+            }
+            floatx4 el[NTT];
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) el[tt] = *reinterpret_cast<const floatx4 *>(gp + C + tt * 16 + 4 * g);
+            const float gL = gp[2 * C];
+            // V_new = U - X (published fp32 [j][s]); V~ = e^{G_L - G} V_new
             float *vnp = Vn(p);
             floatx4 vt4[NTT];
 #pragma unroll
-            for (int vt = 0; vt < NTT; ++vt) {
-                floatx4 acc = zero4();
-                const u16 *trow = tb + (vt * 16 + c16) * LDT;
+            for (int tt = 0; tt < NTT; ++tt) {
+                floatx4 vn;
 #pragma unroll
-                for (int m = 0; m < NCS; ++m) {
-                    const bf16x8 ta = ld_perm(trow, m * 32, g);
-                    acc = mfma32(ta, rh[m], acc);
-                    acc = mfma32(ta, rl[m], acc);
-                }
-                *reinterpret_cast<floatx4 *>(vnp + c16 * LDVF + vt * 16 + 4 * g) = acc;
-                const floatx4 el = *reinterpret_cast<const floatx4 *>(gp + 3 * C + vt * 16 + 4 * g);
+                for (int e = 0; e < 4; ++e) vn[e] = u[tt][e] - x[tt][e];
+                *reinterpret_cast<floatx4 *>(vnp + c16 * LDVF + tt * 16 + 4 * g) = vn;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) vt4[vt][e] = el[e] * acc[e];
+                for (int e = 0; e < 4; ++e) vt4[tt][e] = el[tt][e] * vn[e];
             }
             bf16x8 vh[NCS], vl[NCS];
 #pragma unroll
             for (int m = 0; m < NCS; ++m) frag_split(vt4[2 * m], vt4[2 * m + 1], vh[m], vl[m]);
             // S <- e^{G_L} S + K^T V~
-            const float gL = gp[4 * C];
+            floatx4 ds[NST];
 #pragma unroll
-            for (int ti = 0; ti < NST; ++ti) {
-                floatx4 acc = zero4();
-                const u16 *krow = kt + (ti * 16 + c16) * LDKT;
-                const int xr = ((ti * 16 + c16) >> 3) & SWM;
+            for (int ti = 0; ti < NST; ++ti) ds[ti] = zero4();
 #pragma unroll
-                for (int m = 0; m < NCS; ++m) {
-                    const bf16x8 ka = ld_perm_swz(krow, m * 32, g, xr);
-                    acc = mfma32(ka, vh[m], acc);
-                    acc = mfma32(ka, vl[m], acc);
-                }
+            for (int m = 0; m < NCS; ++m) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Sreg[ti][e] = gL * Sreg[ti][e] + acc[e];
+                for (int ti = 0; ti < NST; ++ti) ds[ti] = mfma32(kf[ti][m], vh[m], ds[ti]);
+#pragma unroll
+                for (int ti = 0; ti < NST; ++ti) ds[ti] = mfma32(kf[ti][m], vl[m], ds[ti]);
             }
+#pragma unroll
+            for (int ti = 0; ti < NST; ++ti)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Sreg[ti][e] = gL * Sreg[ti][e] + ds[ti][e];
             __syncthreads();
         }
         __syncthreads();                       // matches the out waves' drain step
@@ -273,105 +278,103 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
     // =====================================================================
     // out waves
     // =====================================================================
-    // Each out wave runs a copy of the loop specialised for its token tile
-    // OW (wave 1: the last tile) and its loader roles, so that its global
-    // loads are straight-line code: the hardware counter of outstanding loads
-    // is in order, and a load skipped on some path would make the compiler
-    // wait for every load issued after the one it needs.
+    // Each out wave runs a copy of the loop specialised for its roles, so
+    // that its global loads are straight-line code: the hardware counter of
+    // outstanding loads is in order, and a load skipped on some path would
+    // make the compiler wait for every load issued after the one it needs.
     //
-    // Loader roles: threads [0, NB8) stage one 8x8 block of K each; wave VW
-    // the V slice (C/32 16-byte vectors per lane) and the gate table; every
-    // thread C/32 vectors of T.  The last wave (the lightest output tile)
-    // runs slowest when C = 64 (five waves on four SIMDs: it shares one with
-    // the chain wave), so it only loads T.
+    // Roles: OW = token tile of the output (-1: none); group A (index LA,
+    // NLA threads): C*KD/8/NLA 16-byte vectors each of W and of K^T; group B
+    // (index LB, NLB threads): C*C/8/NLB 16-byte vectors of T and 4 values of
+    // the V slice per thread; GATE: the gate table.
+    constexpr int NLA = S::NLA, NLB = S::NLB;
     constexpr int NTV = C * C / 8;              // 16-byte vectors of T
-    constexpr int PT = NTV / NLD;
-    constexpr int PV = C / 32;                  // V vectors per lane of wave VW
-    constexpr int VW = NTT >= 3 ? 3 : NTT;
+    constexpr int PT = NTV / NLB;
+    constexpr int NWV = C * KD / 8;             // 16-byte vectors of W (and of K^T)
+    constexpr int PW = NWV / NLA;
     constexpr int NLOW = NTT * (NTT + 1) / 2;
-    static_assert(PT * NLD == NTV && PV * 64 == 2 * C, "loader split");
-    const int ltid = tid - 64;                  // loader thread index
-    const bool kload = ltid < NB8;
-    const int kb8 = kload ? ltid % (KD / 8) : 0, tb8 = kload ? ltid / (KD / 8) : 0;
+    static_assert(PT * NLB == NTV && PW * NLA == NWV && C * BV == 4 * NLB, "loader split");
     const size_t tokq = (size_t)H * KD, tokv = (size_t)H * Dv;
-    const u16 *kg = reinterpret_cast<const u16 *>(args.k) + ((size_t)b * T * H + h) * KD;
+    const u16 *ktg = reinterpret_cast<const u16 *>(args.ktmat) + (size_t)bh * NT * KD * C;
     const u16 *qg = reinterpret_cast<const u16 *>(args.q) + ((size_t)b * T * H + h) * KD;
     const u16 *vg = reinterpret_cast<const u16 *>(args.v) + ((size_t)b * T * H + h) * Dv + v0;
     const u16 *tg = reinterpret_cast<const u16 *>(args.tmat) + (size_t)bh * NT * C * C;
+    const u16 *wg = reinterpret_cast<const u16 *>(args.wmat) + (size_t)bh * NT * C * KD;
     const float *betag = args.beta + (size_t)b * T * H + h, *gg = args.g + (size_t)b * T * H + h;
 
-    auto out_wave = [&](auto owc) {
-        constexpr int OW = decltype(owc)::value;
-        constexpr int WV = NTT - OW;            // this wave's index
-        constexpr bool KW = (WV - 1) * 64 < NB8, VWV = WV == VW;
+    auto out_wave = [&](auto owc, auto lac, auto lbc, auto gatec) {
+        constexpr int OW = decltype(owc)::value, LA = decltype(lac)::value, LB = decltype(lbc)::value;
+        constexpr bool TILE = OW >= 0, GA = LA >= 0, GB = LB >= 0, GATE = decltype(gatec)::value;
+        constexpr bool LOAD = GA || GB || GATE;
+        const int ia = (GA ? LA : 0) * 64 + l, ib = (GB ? LB : 0) * 64 + l;   // group thread indices
+        const int vtok = ib % C, vcol = 4 * (ib / C);       // this lane's 4 values of V
         // Rows past T are clamped to T-1 (and zeroed when committed); a chunk
         // index past the end is clamped to the last chunk (its staging then
         // lands in a buffer no one reads).
-        u32x4 rk[8], rt[PT], rv[PV];
-        float rbv[PV], rbeta = 0.f, rg = 0.f;
+        u32x4 rk[PW], rt[PT], rw[PW];
+        uint2 rv;
+        float rbv = 0.f, rg = 0.f;
         auto prefetch = [&](int c) {
             c = min(c, NT - 1);
             const int t0 = c * C;
-            if constexpr (KW) {
+            if constexpr (GA) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int t = min(t0 + tb8 * 8 + j, tlast);
-                    rk[j] = *reinterpret_cast<const u32x4 *>(kg + (size_t)t * tokq + kb8 * 8);
-                }
+                for (int q = 0; q < PW; ++q)
+                    rw[q] = reinterpret_cast<const u32x4 *>(wg + (size_t)c * C * KD)[ia + NLA * q];
+#pragma unroll
+                for (int q = 0; q < PW; ++q)
+                    rk[q] = reinterpret_cast<const u32x4 *>(ktg + (size_t)c * KD * C)[ia + NLA * q];
             }
+            if constexpr (GB) {
 #pragma unroll
-            for (int q = 0; q < PT; ++q)
-                rt[q] = reinterpret_cast<const u32x4 *>(tg + (size_t)c * C * C)[ltid + NLD * q];
-            if constexpr (VWV) {
-#pragma unroll
-                for (int q = 0; q < PV; ++q) {
-                    const int vidx = l + 64 * q;
-                    const int t = min(t0 + vidx % C, tlast);
-                    rv[q] = *reinterpret_cast<const u32x4 *>(vg + (size_t)t * tokv + (vidx / C) * 8);
-                    rbv[q] = betag[(size_t)t * H];
-                }
+                for (int q = 0; q < PT; ++q)
+                    rt[q] = reinterpret_cast<const u32x4 *>(tg + (size_t)c * C * C)[ib + NLB * q];
+                const int t = min(t0 + vtok, tlast);
+                rv = *reinterpret_cast<const uint2 *>(vg + (size_t)t * tokv + vcol);
+                rbv = betag[(size_t)t * H];
+            }
+            if constexpr (GATE) {
                 const int tt = min(t0 + l, tlast);
-                rbeta = betag[(size_t)tt * H];
                 rg = gg[(size_t)tt * H];
             }
         };
         auto commit = [&](int c) {
             const int p = c & 1, t0 = c * C;
-            u16 *ks = Ks(p), *kt = KsT(p), *tb = Tb(p);
-            float *bv = BVs(p), *gp = gate(p);
-            if constexpr (KW) {
-                if (kload) {
-                    u32x4 rows[8];
+            u16 *ws = Ks(p), *kt = KsT(p), *tb = Tb(p), *bv = BVs(p);
+            float *gp = gate(p);
+            if constexpr (GA) {
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        rows[j] = (t0 + tb8 * 8 + j < T) ? rk[j] : u32x4{0u, 0u, 0u, 0u};
-                        *reinterpret_cast<u32x4 *>(ks + (tb8 * 8 + j) * LDK + kb8 * 8) = rows[j];
-                    }
-                    // row kb8*8+e of K^T: chunk tb8 stored at tb8 ^ (kb8 & SWM)
-                    u16 *ktb = kt + (kb8 * 8) * LDKT + ((tb8 ^ (kb8 & SWM)) * 8);
+                for (int q = 0; q < PW; ++q) {  // W rows of tokens past T are zero
+                    const int idx = ia + NLA * q;
+                    *reinterpret_cast<u32x4 *>(ws + (idx / (KD / 8)) * LDK + (idx % (KD / 8)) * 8) = rw[q];
+                }
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4 *>(ktb + e * LDKT) = block_col(rows, e);
+                for (int q = 0; q < PW; ++q) {  // K^T, already swizzled (zero for tokens past T)
+                    const int idx = ia + NLA * q;
+                    *reinterpret_cast<u32x4 *>(kt + (idx / (C / 8)) * LDKT + (idx % (C / 8)) * 8) = rk[q];
                 }
             }
+            if constexpr (GB) {
 #pragma unroll
-            for (int q = 0; q < PT; ++q) {
-                const int idx = ltid + NLD * q;
-                const int i = idx / (C / 8), cv = idx % (C / 8);
-                *reinterpret_cast<u32x4 *>(tb + i * LDT + cv * 8) = rt[q];
-            }
-            if constexpr (VWV) {
-#pragma unroll
-                for (int q = 0; q < PV; ++q) {  // beta V, transposed to [j][t]
-                    const int vidx = l + 64 * q, vtok = vidx % C, vcv = vidx / C;
-                    const float bt = (t0 + vtok < T) ? rbv[q] : 0.f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t wv = rv[q][e >> 1];
-                        bv[(vcv * 8 + e) * LDBV + vtok] =
-                            bt * bf16_to_f32((u16)((e & 1) ? (wv >> 16) : (wv & 0xffffu)));
-                    }
+                for (int q = 0; q < PT; ++q) {
+                    const int idx = ib + NLB * q;
+                    *reinterpret_cast<u32x4 *>(tb + (idx / (C / 8)) * LDT + (idx % (C / 8)) * 8) = rt[q];
                 }
-                // the cumsum and the gate table
+                // beta V as hi + lo bf16, transposed to [j][t]
+                const float bt = (t0 + vtok < T) ? rbv : 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; e += 2) {
+                    const uint32_t wv = e ? rv.y : rv.x;
+                    uint32_t hi, lo;
+                    split2_bf16(bt * bf16_to_f32((u16)(wv & 0xffffu)), bt * bf16_to_f32((u16)(wv >> 16)), hi, lo);
+                    const int j = vcol + e;
+                    bv[j * LDBV + vtok] = (u16)(hi & 0xffffu);
+                    bv[(j + 1) * LDBV + vtok] = (u16)(hi >> 16);
+                    bv[(BV + j) * LDBV + vtok] = (u16)(lo & 0xffffu);
+                    bv[(BV + j + 1) * LDBV + vtok] = (u16)(lo >> 16);
+                }
+            }
+            if constexpr (GATE) {               // the cumsum and the gate table
                 const bool ok = l < C && t0 + l < T;
                 float gs = ok ? rg : 0.f;
 #pragma unroll
@@ -382,32 +385,30 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
                 const float g2 = gs * LOG2E;
                 const float g2l = __shfl(g2, C - 1, 64);
                 if (l < C) {
-                    const float eg = fast_exp2(g2);
-                    gp[l] = (ok ? rbeta : 0.f) * eg;         // beta e^{G_t}
-                    gp[C + l] = g2;                          // G2
-                    gp[2 * C + l] = eg;                      // e^{G_t}
-                    gp[3 * C + l] = fast_exp2(g2l - g2);     // e^{G_L - G_t}
+                    gp[l] = fast_exp2(g2);                   // e^{G_t}
+                    gp[C + l] = fast_exp2(g2l - g2);         // e^{G_L - G_t}
                 }
-                if (l == 0) gp[4 * C] = fast_exp2(g2l);     // e^{G_L}
+                if (l == 0) gp[2 * C] = fast_exp2(g2l);     // e^{G_L}
             }
         };
 
+        constexpr int TW = TILE ? OW : 0;
         bf16x8 qf[NKS];                         // Q fragments (B operand, token = lane%16)
-        u32x4 pf[OW + 1];                       // P fragments of row tile OW: {hi01, hi23, lo01, lo23}
+        u32x4 pf[TW + 1];                       // P fragments of row tile OW: {hi01, hi23, lo01, lo23}
         float egt = 0.f;                        // e^{G_t} of this lane's token
         floatx4 ov = zero4();                   // output of the previous chunk
         const uint4 *pfg = reinterpret_cast<const uint4 *>(args.pfrag) + (size_t)bh * NT * NLOW * 64 +
-                           (OW * (OW + 1) / 2) * 64 + l;
+                           (TW * (TW + 1) / 2) * 64 + l;
         // operands of chunk c's output, used one iteration later
         auto load_qp = [&](int c) {
-            const int t = min(c * C + OW * 16 + c16, tlast);   // rows past T are never stored
+            const int t = min(c * C + TW * 16 + c16, tlast);   // rows past T are never stored
 #pragma unroll
             for (int m = 0; m < NKS; ++m)
                 qf[m] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)t * tokq + m * 32 + 8 * g);
             const uint4 *pc = pfg + (size_t)c * NLOW * 64;
 #pragma unroll
-            for (int tj = 0; tj <= OW; ++tj) pf[tj] = __builtin_bit_cast(u32x4, pc[tj * 64]);
-            egt = gate(c & 1)[2 * C + OW * 16 + c16];
+            for (int tj = 0; tj <= TW; ++tj) pf[tj] = __builtin_bit_cast(u32x4, pc[tj * 64]);
+            egt = gate(c & 1)[TW * 16 + c16];
         };
         // O^T of chunk c: a1 = S_start^T Q^T, a2 = V_new^T P^T (buffers c & 1)
         auto compute_out = [&](int c) {
@@ -423,7 +424,7 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
                 a1 = mfma32(sl, qf[m], a1);
             }
 #pragma unroll
-            for (int tj = 0; tj <= OW; ++tj) {
+            for (int tj = 0; tj <= TW; ++tj) {
                 shortx4 vh4, vl4;
                 split4(*reinterpret_cast<const floatx4 *>(vnp + c16 * LDVF + tj * 16 + 4 * g), vh4, vl4);
                 const shortx4 ph = __builtin_bit_cast(shortx4, uint2{pf[tj][0], pf[tj][1]});
@@ -437,7 +438,7 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
             for (int e = 0; e < 4; ++e) ov[e] = sc * (egt * a1[e] + a2[e]);
         };
         auto store_out = [&](int c) {
-            const int tt = c * C + OW * 16 + c16;
+            const int tt = c * C + TW * 16 + c16;
             if (tt < T) {
                 const size_t off = (((size_t)b * T + tt) * H + h) * Dv + v0 + 4 * g;
                 if (args.out_bf16)
@@ -450,24 +451,34 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
 
         // Iteration c (one barrier each): output of chunk c-1, operands of
         // chunk c, commit of chunk c+1, prefetch of chunk c+2.
-        prefetch(0);
-        commit(0);
-        prefetch(1);
+        if constexpr (LOAD) {
+            prefetch(0);
+            commit(0);
+            prefetch(1);
+        }
         __syncthreads();
-        load_qp(0);
-        commit(1);
-        prefetch(2);
+        if constexpr (TILE) load_qp(0);
+        if constexpr (LOAD) {
+            commit(1);
+            prefetch(2);
+        }
         __syncthreads();
         for (int c = 1; c < NT; ++c) {
-            compute_out(c - 1);
-            load_qp(c);
-            commit(c + 1);
-            prefetch(c + 2);
-            store_out(c - 1);
+            if constexpr (TILE) {
+                compute_out(c - 1);
+                load_qp(c);
+            }
+            if constexpr (LOAD) {
+                commit(c + 1);
+                prefetch(c + 2);
+            }
+            if constexpr (TILE) store_out(c - 1);
             __syncthreads();
         }
-        compute_out(NT - 1);
-        store_out(NT - 1);
+        if constexpr (TILE) {
+            compute_out(NT - 1);
+            store_out(NT - 1);
+        }
         __syncthreads();
     };
     if (NT == 0) {                              // no chunks: match the chain wave's two barriers
@@ -475,12 +486,23 @@ __global__ __launch_bounds__((1 + C / 16) * 64) void chunk_chain1_kernel(ChunkAr
         __syncthreads();
         return;
     }
-    const int ow = NTT - w;                     // token tile of this wave (wave 1: the last)
-    if (ow == 0) out_wave(std::integral_constant<int, 0>{});
-    if (ow == 1) out_wave(std::integral_constant<int, 1>{});
+    using std::integral_constant;
+    using std::false_type;
+    using std::true_type;
+    using none = integral_constant<int, -1>;
     if constexpr (NTT == 4) {
-        if (ow == 2) out_wave(std::integral_constant<int, 2>{});
-        if (ow == 3) out_wave(std::integral_constant<int, 3>{});
+        if (w == 1) out_wave(integral_constant<int, 3>{}, none{}, integral_constant<int, 0>{}, false_type{});
+        if (w == 2) out_wave(integral_constant<int, 2>{}, none{}, integral_constant<int, 1>{}, false_type{});
+        if (w == 3) out_wave(integral_constant<int, 1>{}, none{}, integral_constant<int, 2>{}, true_type{});
+        if (w == 5) out_wave(integral_constant<int, 0>{}, none{}, integral_constant<int, 3>{}, false_type{});
+        if (w == 6) out_wave(none{}, integral_constant<int, 0>{}, none{}, false_type{});
+        if (w == 7) out_wave(none{}, integral_constant<int, 1>{}, none{}, false_type{});
+    } else {
+        static_assert(NTT == 2, "chunk of 32 or 64 tokens");
+        if (w == 1)
+            out_wave(integral_constant<int, 1>{}, integral_constant<int, 0>{}, integral_constant<int, 0>{}, true_type{});
+        if (w == 2)
+            out_wave(integral_constant<int, 0>{}, integral_constant<int, 1>{}, integral_constant<int, 1>{}, false_type{});
     }
 }
 

@@ -53,6 +53,16 @@ __device__ __forceinline__ void split2_bf16(float a, float b, uint32_t &hi, uint
     lo = cvt2_bf16(a - __builtin_bit_cast(float, hi << 16), b - __builtin_bit_cast(float, hi & 0xffff0000u));
 }
 
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i reads 4 bf16 D_i[0..3] at its own 8-byte address; lane j
+// receives {D_{4e + j/4}[j % 4] : e = 0..3}.  So if lane i of a group points
+// at row r0 + i/4, columns c0 + 4*(i%4) of a row-major matrix M, lane j gets
+// the column c0 + j, rows r0 .. r0+3: M^T read as an MFMA operand fragment.
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+__device__ __forceinline__ shortx4 ld_tr16(const u16 *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p));
+}
+
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
