@@ -4,6 +4,7 @@
 
 #include "chunk_chain1.h"
 #include "chunk_kernels.h"
+#include "chunk_prep1.h"
 
 namespace gdn {
 
@@ -13,6 +14,19 @@ namespace gdn {
 template <bool F32IN, int KD, int C, int R>
 constexpr bool use_chain1() {
     return ChunkShape<F32IN, KD, C, R>::PFRAG;
+}
+
+// Compute units of the current device (cached per device).
+inline int num_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
 }
 
 // Launch both kernels of one instantiation on `stream`.
@@ -30,7 +44,14 @@ hipError_t launch_chunk_fwd(const ChunkArgs &args, hipStream_t stream) {
     const int nbh = a.B * a.H;
     if (nbh == 0) return hipSuccess;
     if (NT > 0) {
-        hipLaunchKernelGGL((chunk_solve_kernel<F32IN, KD, C, R>), dim3(nbh * NT), dim3(256), 0, stream, a);
+        if constexpr (use_chain1<F32IN, KD, C, R>()) {
+            // persistent: two workgroups per CU, each walking chunks with the grid stride
+            const int nchunks = nbh * NT;
+            const int grid = nchunks < 2 * num_cus() ? nchunks : 2 * num_cus();
+            hipLaunchKernelGGL((chunk_prep1_kernel<KD, C>), dim3(grid), dim3(256), 0, stream, a);
+        } else {
+            hipLaunchKernelGGL((chunk_solve_kernel<F32IN, KD, C, R>), dim3(nbh * NT), dim3(256), 0, stream, a);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

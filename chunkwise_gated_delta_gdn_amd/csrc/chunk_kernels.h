@@ -119,13 +119,9 @@ struct ChunkShape {
     static constexpr int LDRT = NR + PAD;      // RT:      [BV][NR]
     static constexpr int LDVT = C + PAD;       // Vn/Vt:   [R][BV][C]
     static constexpr int LDY = 17;             // merge scratch [16][17] fp32
-    // bf16 inputs, one step per token, 32-multiple widths: the solve kernel
-    // also writes the causal intra-chunk scores P[t][s] = [s<=t] (q_t.k_s)
-    // e^{G_t - G_s} of the NLOW lower 16x16 tiles, as hi/lo bf16 MFMA
-    // fragments (lane l: row t = 16*ti + l%16, columns s = 16*tj + 4*(l/16)
-    // + e), 64 lanes x 16 bytes per tile, tile (ti, tj) at ti*(ti+1)/2 + tj.
-    // These shapes also get W = T diag(beta e^G) K (the page's w of the WY
-    // form), bf16 [C][KD] per chunk, for the single-chain-wave state pass.
+    // bf16 inputs, one step per token, 32-multiple widths: these shapes run
+    // chunk_prep1_kernel + chunk_chain1_kernel, whose work space also holds
+    // the P fragments, W and K^T of every chunk.
     static constexpr bool PFRAG = !F32IN && R == 1 && C % 32 == 0 && KD % 32 == 0;
     static constexpr int al(int x) { return (x + 15) & ~15; }
     static_assert(KD % R == 0, "key width must split into R sub-keys");
@@ -140,7 +136,7 @@ template <bool F32IN, int KD, int C, int R>
 struct SolveLds {
     using S = ChunkShape<F32IN, KD, C, R>;
     static constexpr int SZ_KS = C * S::LDK * S::ESZ;
-    static constexpr int SZ_GATE = (C * R + 2 * C) * 4;   // beta, G2, beta e^G
+    static constexpr int SZ_GATE = (C * R + C) * 4;
     static constexpr int SZ_A = S::NR * S::LDA * 4;
     static constexpr int SZ_Y = 4 * 16 * S::LDY * 4;
     static constexpr int OFF_KS = 0;
@@ -163,7 +159,6 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(ChunkArgs args) {
     Op *Ks = reinterpret_cast<Op *>(smem + L::OFF_KS);
     float *betas = reinterpret_cast<float *>(smem + L::OFF_GATE);
     float *G2 = betas + C * R;
-    float *BEG = G2 + C;                      // beta e^{G_t} (PFRAG shapes)
     float *As = reinterpret_cast<float *>(smem + L::OFF_AS);
     float *Ts = reinterpret_cast<float *>(smem + L::OFF_TS);
 
@@ -189,17 +184,6 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(ChunkArgs args) {
             for (int e = 0; e < 8; ++e) raw.v[e] = 0;
         }
         *reinterpret_cast<U16x8 *>(Ks + t * LDK + cv * VEC) = raw;
-    }
-    // Q rows of this wave's P row tile (PFRAG shapes), loaded early
-    const int p_ti = w == 0 ? 0 : S::NTT - w;
-    bf16x8 qf[KD >= 32 ? KD / 32 : 1];
-    if constexpr (S::PFRAG) {
-        if (p_ti >= 0) {
-            const int tq = min(t0 + p_ti * 16 + (l & 15), T - 1);
-            const u16 *qrow = reinterpret_cast<const u16 *>(args.q) + (((size_t)b * T + tq) * H + h) * KD;
-#pragma unroll
-            for (int m = 0; m < KD / 32; ++m) qf[m] = *reinterpret_cast<const bf16x8 *>(qrow + m * 32 + 8 * (l >> 4));
-        }
     }
     for (int idx = tid; idx < C * R; idx += 256) {
         const int tt = t0 + idx / R;
@@ -237,41 +221,8 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(ChunkArgs args) {
     }
     __syncthreads();
 
-    // ---- causal scores P, row tile ti (one wave), written as fragments ----
-    auto p_rowtile = [&](int ti) {
-        if constexpr (S::PFRAG) {
-            const int c16 = l & 15, g = l >> 4;
-            const float g2t = G2[ti * 16 + c16];
-            uint4 *dst = reinterpret_cast<uint4 *>(args.pfrag) + ((size_t)bh * NT + c) * S::NLOW * 64 +
-                         (ti * (ti + 1) / 2) * 64 + l;
-            for (int tj = 0; tj <= ti; ++tj) {
-                floatx4 acc = zero4();
-                const u16 *krow = reinterpret_cast<const u16 *>(Ks) + (tj * 16 + c16) * LDK;
-#pragma unroll
-                for (int m = 0; m < KD / 32; ++m)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld8(krow + m * 32 + 8 * g), qf[m], acc, 0, 0, 0);
-                float pv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int s = tj * 16 + 4 * g + e;
-                    pv[e] = s <= ti * 16 + c16 ? acc[e] * fast_exp2(fminf(g2t - G2[s], 0.f)) : 0.f;
-                }
-                uint4 f;
-                split2_bf16(pv[0], pv[1], f.x, f.z);
-                split2_bf16(pv[2], pv[3], f.y, f.w);
-                dst[tj * 64] = f;
-            }
-        }
-    };
-    if constexpr (S::PFRAG) {
-        if (w != 0 && w < S::NTT) p_rowtile(p_ti);         // overlaps wave 0's substitution
-    }
-
     // ---- diagonal 16x16 blocks: forward substitution, one lane per column ----
     if (w == 0) {
-        if constexpr (S::PFRAG) {
-            if (l < C) BEG[l] = betas[l] * fast_exp2(G2[l]);
-        }
         const int ib = l >> 4, col = l & 15;
         if (ib < NB) {
             const float *Ab = As + (ib * 16) * LDA + ib * 16;
@@ -287,7 +238,6 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(ChunkArgs args) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) Tc[i * LDA] = x[i];
         }
-        if constexpr (S::PFRAG) p_rowtile(0);
     }
     __syncthreads();
 
@@ -313,81 +263,13 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(ChunkArgs args) {
         __syncthreads();
     }
 
-    // ---- W = T diag(beta e^G) K, as W^T tiles K^T (T diag(beta e^G))^T ----
-    if constexpr (S::PFRAG) {
-        const int c16 = l & 15, g = l >> 4;
-        u16 *wout = reinterpret_cast<u16 *>(args.wmat) + ((size_t)bh * NT + c) * C * KD;
-        for (int tile = w; tile < S::NTT * (KD / 16); tile += 4) {
-            const int tt = tile % S::NTT, it = tile / S::NTT;
-            const int t = tt * 16 + c16;
-            floatx4 acc = zero4();
-#pragma unroll
-            for (int m = 0; m < C / 32; ++m) {
-                if (m * 2 > tt) break;                       // T is block lower triangular
-                const int s0 = m * 32 + 8 * g;
-                const bool ok = (s0 >> 4) <= tt;             // block (tt, s0/16) inside the triangle
-                const floatx4 x0 = *reinterpret_cast<const floatx4 *>(Ts + t * LDA + s0);
-                const floatx4 x1 = *reinterpret_cast<const floatx4 *>(Ts + t * LDA + s0 + 4);
-                const floatx4 b0 = *reinterpret_cast<const floatx4 *>(BEG + s0);
-                const floatx4 b1 = *reinterpret_cast<const floatx4 *>(BEG + s0 + 4);
-                floatx4 y0, y1;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    y0[e] = ok ? x0[e] * b0[e] : 0.f;
-                    y1[e] = ok ? x1[e] * b1[e] : 0.f;
-                }
-                uint4 hi, lo;
-                split2_bf16(y0[0], y0[1], hi.x, lo.x);
-                split2_bf16(y0[2], y0[3], hi.y, lo.y);
-                split2_bf16(y1[0], y1[1], hi.z, lo.z);
-                split2_bf16(y1[2], y1[3], hi.w, lo.w);
-                // K^T rows it*16 + j, k = s0 .. s0+7: transposed reads of Ks
-                const u16 *kp = reinterpret_cast<const u16 *>(Ks) + (m * 32 + 8 * g + (c16 >> 2)) * LDK +
-                                it * 16 + 4 * (c16 & 3);
-                const shortx4 k0 = ld_tr16(kp), k1 = ld_tr16(kp + 4 * LDK);
-                const bf16x8 ka = __builtin_bit_cast(bf16x8, uint4{__builtin_bit_cast(uint2, k0).x,
-                                                                   __builtin_bit_cast(uint2, k0).y,
-                                                                   __builtin_bit_cast(uint2, k1).x,
-                                                                   __builtin_bit_cast(uint2, k1).y});
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, __builtin_bit_cast(bf16x8, hi), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, __builtin_bit_cast(bf16x8, lo), acc, 0, 0, 0);
-            }
-            // lane: W[t][it*16 + 4g + e], stored in the permuted order
-            *reinterpret_cast<uint2 *>(wout + (size_t)t * KD + perm4_pos(it * 16 + 4 * g)) =
-                uint2{cvt2_bf16(acc[0], acc[1]), cvt2_bf16(acc[2], acc[3])};
-        }
-    }
-
-    // ---- K^T of the chunk, rows of C tokens in the permuted order; the
-    //      16-byte chunk j of row i is stored at chunk j ^ ((i / 8) & (C/8 - 1))
-    //      (the state pass's LDS layout, which spreads its writes over the
-    //      banks) ----
-    if constexpr (S::PFRAG) {
-        u16 *kout = reinterpret_cast<u16 *>(args.ktmat) + ((size_t)bh * NT + c) * KD * C;
-        const int c16 = l & 15, g = l >> 4;
-        // one (16-row block it, 32-token block m) per wave step; lane (g, j):
-        // row i = it*16 + j, stored chunk 4m + g = tokens 32m + 4g + {0..3}
-        // and 32m + 16 + 4g + {0..3}, read transposed from Ks
-        for (int blk = w; blk < (KD / 16) * (C / 32); blk += 4) {
-            const int it = blk / (C / 32), m = blk % (C / 32);
-            const u16 *kp = reinterpret_cast<const u16 *>(Ks) + (m * 32 + 4 * g + (c16 >> 2)) * LDK +
-                            it * 16 + 4 * (c16 & 3);
-            const uint2 lo = __builtin_bit_cast(uint2, ld_tr16(kp));
-            const uint2 hi = __builtin_bit_cast(uint2, ld_tr16(kp + 16 * LDK));
-            const int i = it * 16 + c16;
-            const int js = (4 * m + g) ^ ((i >> 3) & (C / 8 - 1));
-            *reinterpret_cast<uint4 *>(kout + i * C + js * 8) = uint4{lo.x, lo.y, hi.x, hi.y};
-        }
-    }
-
     // ---- write T (zero above the block diagonal) ----
     Op *out = reinterpret_cast<Op *>(args.tmat) + ((size_t)bh * NT + c) * NR * NR;
     for (int idx = tid; idx < NR * NR / 8; idx += 256) {       // 8 consecutive entries of a row
         const int i = idx / (NR / 8), j0 = (idx % (NR / 8)) * 8;
-        const bool keep = (j0 >> 4) <= (i >> 4);
         floatx4 x0 = *reinterpret_cast<const floatx4 *>(Ts + i * LDA + j0);
         floatx4 x1 = *reinterpret_cast<const floatx4 *>(Ts + i * LDA + j0 + 4);
-        if (!keep) x0 = x1 = zero4();
+        if ((j0 >> 4) > (i >> 4)) x0 = x1 = zero4();
         if constexpr (F32IN) {
             *reinterpret_cast<floatx4 *>(out + (size_t)i * NR + j0) = x0;
             *reinterpret_cast<floatx4 *>(out + (size_t)i * NR + j0 + 4) = x1;
@@ -786,7 +668,8 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
     }
 }
 
-// Work space: T of every chunk, then (PFRAG shapes) the P fragments.
+// Work space: T of every chunk, then (PFRAG shapes) the P fragments, W and
+// K^T of every chunk.
 template <bool F32IN, int KD, int C, int R>
 size_t chunk_tmat_bytes(int B, int T, int H) {
     using S = ChunkShape<F32IN, KD, C, R>;

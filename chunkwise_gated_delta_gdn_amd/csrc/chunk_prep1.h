@@ -1,0 +1,302 @@
+// Per-chunk preparation for the single-chain-wave state pass (bf16 inputs,
+// one step per token): everything about a chunk that does not depend on the
+// state, computed in parallel over chunks (msj19 "gated_deltaproduct"
+// test.py with r = 1: gated_chunk_scaled_dot_kkt_fwd_kernel, solve_tril and
+// the block merges, gated_fwd_recompute_w_u_kernel, and the intra-chunk
+// scores of gated_chunk_linear_attn_fwd_kernel_o).  Per chunk of C tokens:
+//
+//   G       chunk-local cumsum of the log-decay (kept in log2 units)
+//   A       [s<t] beta_t (k_t . k_s) e^{G_t - G_s}       (fp32, LDS)
+//   T       (I + A)^-1: 16x16 diagonal blocks by forward substitution, then
+//           block rows T_ij = -T_ii sum_m A_im T_mj                  -> bf16
+//   W       T diag(beta e^G) K, rows in the permuted k order         -> bf16
+//   K^T     rows of C tokens, permuted k order, 16-byte chunks swizzled
+//   P       [s<=t] (q_t . k_s) e^{G_t - G_s} of the lower 16x16 tiles, as
+//           hi/lo bf16 MFMA fragments (lane l: row t = 16 ti + l%16,
+//           columns s = 16 tj + 4 (l/16) + e)
+//
+// Persistent workgroups of 4 waves walk the chunks with a stride of the
+// grid; the next chunk's K, Q, beta and g are loaded into registers while the
+// current one is solved, so the global-load latency stays hidden.
+#pragma once
+
+#include "chunk_kernels.h"
+
+namespace gdn {
+
+template <int KD, int C>
+struct Prep1Shape {
+    static constexpr int NTT = C / 16;        // 16-token tiles (= diagonal blocks)
+    static constexpr int NLOW = NTT * (NTT + 1) / 2;
+    static constexpr int NKS = KD / 32;       // 32-wide k steps over the key dim
+    static constexpr int LDK = KD + 8;        // Ks [C][KD] bf16
+    static constexpr int LDA = C + 4;         // As, Ts [C][C] fp32
+    static constexpr int LDY = 17;            // merge scratch [16][17] fp32 per wave
+    static constexpr int NKV = C * KD / 8;    // 16-byte vectors of K per chunk
+    static constexpr int PK = (NKV + 255) / 256;
+    static constexpr int al(int x) { return (x + 15) & ~15; }
+    static constexpr int OFF_KS = 0;
+    static constexpr int OFF_AS = OFF_KS + al(C * LDK * 2);
+    static constexpr int OFF_TS = OFF_AS + al(C * LDA * 4);
+    static constexpr int OFF_Y = OFF_TS + al(C * LDA * 4);
+    static constexpr int OFF_G = OFF_Y + al(4 * 16 * LDY * 4);
+    static constexpr int BYTES = OFF_G + al(3 * C * 4);   // beta, G2, beta e^G
+    static_assert(C % 32 == 0 && C <= 64 && KD % 32 == 0 && KD <= 256, "shape");
+    static_assert(BYTES <= 80 * 1024, "two workgroups per CU");
+    // Owner wave of lower gram tile k (row-major over ti >= tj), chosen so
+    // that with the P tiles of row tile w on wave w every wave has NLOW*2/4
+    // tiles (C = 64) or close to it (C = 32).
+    static constexpr int gram_owner(int k) {
+        if (NTT == 4) {
+            constexpr int own[10] = {0, 0, 0, 0, 1, 1, 1, 2, 2, 3};
+            return own[k];
+        }
+        constexpr int own2[3] = {2, 3, 0};
+        return own2[k];
+    }
+};
+
+template <int KD, int C>
+__global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
+    using S = Prep1Shape<KD, C>;
+    constexpr int NTT = S::NTT, NLOW = S::NLOW, NKS = S::NKS, LDK = S::LDK, LDA = S::LDA, LDY = S::LDY;
+    constexpr int NKV = S::NKV, PK = S::PK;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[S::BYTES];
+    u16 *Ks = reinterpret_cast<u16 *>(smem + S::OFF_KS);
+    float *As = reinterpret_cast<float *>(smem + S::OFF_AS);
+    float *Ts = reinterpret_cast<float *>(smem + S::OFF_TS);
+    float *betas = reinterpret_cast<float *>(smem + S::OFF_G);
+    float *G2 = betas + C, *BEG = betas + 2 * C;
+
+    const int tid = threadIdx.x, l = tid & 63, c16 = l & 15, g = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    float *Ys = reinterpret_cast<float *>(smem + S::OFF_Y) + w * 16 * LDY;
+    const int T = args.T, H = args.H;
+    const int NT = (T + C - 1) / C;
+    const int total = args.B * H * NT;
+    const u16 *kg = reinterpret_cast<const u16 *>(args.k);
+    const u16 *qg = reinterpret_cast<const u16 *>(args.q);
+
+    // ---- registers of the next chunk ----
+    u32x4 rk[PK];
+    bf16x8 qf[NKS];
+    float rb = 0.f, rg = 0.f;
+    auto prefetch = [&](int ci) {
+        const int bh = ci / NT, c = ci % NT, b = bh / H, h = bh % H, t0 = c * C;
+        const size_t row0 = (size_t)b * T * H + h;
+#pragma unroll
+        for (int q = 0; q < PK; ++q) {
+            const int idx = min(tid + 256 * q, NKV - 1);
+            const int tt = min(t0 + idx / (KD / 8), T - 1);
+            rk[q] = *reinterpret_cast<const u32x4 *>(kg + (row0 + (size_t)tt * H) * KD + (idx % (KD / 8)) * 8);
+        }
+        if (w < NTT) {                          // Q rows of P row tile w
+            const int tq = min(t0 + w * 16 + c16, T - 1);
+#pragma unroll
+            for (int m = 0; m < NKS; ++m)
+                qf[m] = *reinterpret_cast<const bf16x8 *>(qg + (row0 + (size_t)tq * H) * KD + m * 32 + 8 * g);
+        }
+        if (w == 0) {
+            const int tt = min(t0 + l, T - 1);
+            rb = args.beta[row0 + (size_t)tt * H];
+            rg = args.g[row0 + (size_t)tt * H];
+        }
+    };
+
+    if ((int)blockIdx.x < total) prefetch(blockIdx.x);
+    for (int ci = blockIdx.x; ci < total; ci += gridDim.x) {
+        const int bh = ci / NT, c = ci % NT, t0 = c * C;
+
+        // ---- K rows (zero past T), beta, cumsum ----
+#pragma unroll
+        for (int q = 0; q < PK; ++q) {
+            const int idx = tid + 256 * q;
+            if (idx < NKV) {
+                const int t = idx / (KD / 8);
+                *reinterpret_cast<u32x4 *>(Ks + t * LDK + (idx % (KD / 8)) * 8) =
+                    t0 + t < T ? rk[q] : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        if (w == 0) {
+            const bool ok = l < C && t0 + l < T;
+            float gs = ok ? rg : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(gs, off, 64);
+                if (l >= off) gs += y;
+            }
+            if (l < C) {
+                const float g2 = gs * LOG2E;
+                const float bt = ok ? rb : 0.f;
+                betas[l] = bt;
+                G2[l] = g2;
+                BEG[l] = bt * fast_exp2(g2);
+            }
+        }
+        __syncthreads();
+
+        // ---- P row tile w (fragments to the work space) ----
+        if (w < NTT) {
+            const float g2t = G2[w * 16 + c16];
+            uint4 *dst = reinterpret_cast<uint4 *>(args.pfrag) + ((size_t)bh * NT + c) * NLOW * 64 +
+                         (w * (w + 1) / 2) * 64 + l;
+            for (int tj = 0; tj <= w; ++tj) {
+                floatx4 acc = zero4();
+                const u16 *krow = Ks + (tj * 16 + c16) * LDK;
+#pragma unroll
+                for (int m = 0; m < NKS; ++m) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                                   ld8(krow + m * 32 + 8 * g), qf[m], acc, 0, 0, 0);
+                const floatx4 g2s = *reinterpret_cast<const floatx4 *>(G2 + tj * 16 + 4 * g);
+                float pv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = tj * 16 + 4 * g + e;
+                    pv[e] = s <= w * 16 + c16 ? acc[e] * fast_exp2(fminf(g2t - g2s[e], 0.f)) : 0.f;
+                }
+                uint4 f;
+                split2_bf16(pv[0], pv[1], f.x, f.z);
+                split2_bf16(pv[2], pv[3], f.y, f.w);
+                dst[tj * 64] = f;
+            }
+        }
+        // ---- gram tiles of this wave: As[t][s] = [s<t] beta_t (k_t.k_s) e^{G_t-G_s} ----
+#pragma unroll
+        for (int kk = 0; kk < NLOW; ++kk) {
+            if (S::gram_owner(kk) != w) continue;
+            int ti = 0, p = kk;
+            while (p > ti) { p -= ti + 1; ++ti; }
+            const int tj = p;
+            floatx4 acc = zero4();
+            const u16 *ar = Ks + (ti * 16 + c16) * LDK, *br = Ks + (tj * 16 + c16) * LDK;
+#pragma unroll
+            for (int m = 0; m < NKS; ++m)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld8(ar + m * 32 + 8 * g), ld8(br + m * 32 + 8 * g), acc,
+                                                              0, 0, 0);
+            const int s = tj * 16 + c16;
+            const float g2s = G2[s];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = ti * 16 + 4 * g + e;
+                As[t * LDA + s] = s < t ? betas[t] * acc[e] * fast_exp2(fminf(G2[t] - g2s, 0.f)) : 0.f;
+            }
+        }
+        // registers are free: start loading the next chunk
+        if (ci + (int)gridDim.x < total) prefetch(ci + gridDim.x);
+        __syncthreads();
+
+        // ---- diagonal blocks by forward substitution (wave 0); K^T out (others) ----
+        if (w == 0) {
+            const int ib = l >> 4, col = l & 15;
+            if (ib < NTT) {
+                const float *Ab = As + (ib * 16) * LDA + ib * 16;
+                float x[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float acc = (i == col) ? 1.f : 0.f;
+#pragma unroll
+                    for (int j = 0; j < i; ++j) acc -= Ab[i * LDA + j] * x[j];
+                    x[i] = acc;
+                }
+                float *Tc = Ts + (ib * 16) * LDA + ib * 16 + col;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) Tc[i * LDA] = x[i];
+            }
+        } else {
+            // lane (g, j) of block (it, m): K^T row i = 16 it + j, stored chunk 4m + g =
+            // tokens 32m + 4g + {0..3} and 32m + 16 + 4g + {0..3}, read transposed from Ks
+            u16 *kout = reinterpret_cast<u16 *>(args.ktmat) + ((size_t)bh * NT + c) * KD * C;
+            for (int blk = w - 1; blk < (KD / 16) * (C / 32); blk += 3) {
+                const int it = blk / (C / 32), m = blk % (C / 32);
+                const u16 *kp = Ks + (m * 32 + 4 * g + (c16 >> 2)) * LDK + it * 16 + 4 * (c16 & 3);
+                const uint2 lo = __builtin_bit_cast(uint2, ld_tr16(kp));
+                const uint2 hi = __builtin_bit_cast(uint2, ld_tr16(kp + 16 * LDK));
+                const int i = it * 16 + c16;
+                const int js = (4 * m + g) ^ ((i >> 3) & (C / 8 - 1));
+                *reinterpret_cast<uint4 *>(kout + i * C + js * 8) = uint4{lo.x, lo.y, hi.x, hi.y};
+            }
+        }
+        __syncthreads();
+
+        // ---- block rows: T_ij = -T_ii sum_{j<=m<i} A_im T_mj, one column block per wave ----
+#pragma unroll
+        for (int st = 1; st < NTT; ++st) {
+            const int jb = w, ib = w + st;
+            const bool act = ib < NTT;
+            if (act) {
+                floatx4 y = zero4();
+                for (int m = jb; m < ib; ++m)
+                    mma_f32_bn(y, As + (ib * 16) * LDA + m * 16, LDA, Ts + (m * 16) * LDA + jb * 16, LDA, 16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Ys[(4 * g + e) * LDY + c16] = y[e];
+            }
+            __syncthreads();
+            if (act) {
+                floatx4 t2 = zero4();
+                mma_f32_bn(t2, Ts + (ib * 16) * LDA + ib * 16, LDA, Ys, LDY, 16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Ts[(ib * 16 + 4 * g + e) * LDA + jb * 16 + c16] = -t2[e];
+            }
+            __syncthreads();
+        }
+
+        // ---- W = T diag(beta e^G) K as W^T tiles K^T (T diag(beta e^G))^T ----
+        {
+            u16 *wout = reinterpret_cast<u16 *>(args.wmat) + ((size_t)bh * NT + c) * C * KD;
+            for (int it = w; it < KD / 16; it += 4) {
+                // K^T fragments of rows 16 it + j, k = 32 m + 8 g + {0..7}
+                bf16x8 ka[C / 32];
+#pragma unroll
+                for (int m = 0; m < C / 32; ++m) {
+                    const u16 *kp = Ks + (m * 32 + 8 * g + (c16 >> 2)) * LDK + it * 16 + 4 * (c16 & 3);
+                    const uint2 k0 = __builtin_bit_cast(uint2, ld_tr16(kp));
+                    const uint2 k1 = __builtin_bit_cast(uint2, ld_tr16(kp + 4 * LDK));
+                    ka[m] = __builtin_bit_cast(bf16x8, uint4{k0.x, k0.y, k1.x, k1.y});
+                }
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt) {
+                    const int t = tt * 16 + c16;
+                    floatx4 acc = zero4();
+#pragma unroll
+                    for (int m = 0; m < C / 32; ++m) {
+                        if (2 * m > tt) break;                  // T is block lower triangular
+                        const int s0 = m * 32 + 8 * g;
+                        const bool ok = (s0 >> 4) <= tt;
+                        const floatx4 x0 = *reinterpret_cast<const floatx4 *>(Ts + t * LDA + s0);
+                        const floatx4 x1 = *reinterpret_cast<const floatx4 *>(Ts + t * LDA + s0 + 4);
+                        const floatx4 b0 = *reinterpret_cast<const floatx4 *>(BEG + s0);
+                        const floatx4 b1 = *reinterpret_cast<const floatx4 *>(BEG + s0 + 4);
+                        uint4 hi, lo;
+                        split2_bf16(ok ? x0[0] * b0[0] : 0.f, ok ? x0[1] * b0[1] : 0.f, hi.x, lo.x);
+                        split2_bf16(ok ? x0[2] * b0[2] : 0.f, ok ? x0[3] * b0[3] : 0.f, hi.y, lo.y);
+                        split2_bf16(ok ? x1[0] * b1[0] : 0.f, ok ? x1[1] * b1[1] : 0.f, hi.z, lo.z);
+                        split2_bf16(ok ? x1[2] * b1[2] : 0.f, ok ? x1[3] * b1[3] : 0.f, hi.w, lo.w);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], __builtin_bit_cast(bf16x8, hi), acc,
+                                                                      0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], __builtin_bit_cast(bf16x8, lo), acc,
+                                                                      0, 0, 0);
+                    }
+                    // lane: W[t][16 it + 4g + e], stored in the permuted order
+                    *reinterpret_cast<uint2 *>(wout + (size_t)t * KD + perm4_pos(it * 16 + 4 * g)) =
+                        uint2{cvt2_bf16(acc[0], acc[1]), cvt2_bf16(acc[2], acc[3])};
+                }
+            }
+        }
+        // ---- T (zero above the block diagonal), bf16 ----
+        {
+            u16 *out = reinterpret_cast<u16 *>(args.tmat) + ((size_t)bh * NT + c) * C * C;
+            for (int idx = tid; idx < C * C / 8; idx += 256) {
+                const int i = idx / (C / 8), j0 = (idx % (C / 8)) * 8;
+                floatx4 x0 = *reinterpret_cast<const floatx4 *>(Ts + i * LDA + j0);
+                floatx4 x1 = *reinterpret_cast<const floatx4 *>(Ts + i * LDA + j0 + 4);
+                if ((j0 >> 4) > (i >> 4)) x0 = x1 = zero4();
+                *reinterpret_cast<uint4 *>(out + (size_t)i * C + j0) =
+                    uint4{cvt2_bf16(x0[0], x0[1]), cvt2_bf16(x0[2], x0[3]), cvt2_bf16(x1[0], x1[1]),
+                          cvt2_bf16(x1[2], x1[3])};
+            }
+        }
+        __syncthreads();                       // Ks, As, Ts are rewritten by the next chunk
+    }
+}
+
+}  // namespace gdn
