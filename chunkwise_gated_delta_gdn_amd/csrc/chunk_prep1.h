@@ -17,7 +17,9 @@
 //
 // Persistent workgroups of 4 waves walk the chunks with a stride of the
 // grid; the next chunk's K, Q, beta and g are loaded into registers while the
-// current one is solved, so the global-load latency stays hidden.
+// current one is solved, so the global-load latency stays hidden.  While
+// wave 0 runs the (sequential) forward substitution, waves 1..3 compute the
+// P tiles and write K^T.
 #pragma once
 
 #include "chunk_kernels.h"
@@ -43,17 +45,11 @@ struct Prep1Shape {
     static constexpr int BYTES = OFF_G + al(3 * C * 4);   // beta, G2, beta e^G
     static_assert(C % 32 == 0 && C <= 64 && KD % 32 == 0 && KD <= 256, "shape");
     static_assert(BYTES <= 80 * 1024, "two workgroups per CU");
-    // Owner wave of lower gram tile k (row-major over ti >= tj), chosen so
-    // that with the P tiles of row tile w on wave w every wave has NLOW*2/4
-    // tiles (C = 64) or close to it (C = 32).
-    static constexpr int gram_owner(int k) {
-        if (NTT == 4) {
-            constexpr int own[10] = {0, 0, 0, 0, 1, 1, 1, 2, 2, 3};
-            return own[k];
-        }
-        constexpr int own2[3] = {2, 3, 0};
-        return own2[k];
-    }
+    // P row tiles during the substitution (waves 1..3; wave 0 substitutes):
+    // wave w takes rows prow0(w) and prow1(w) (-1: none), so that the
+    // 1 + 2 + ... + NTT tiles spread evenly.
+    static constexpr int prow0(int w) { return NTT == 4 ? (w == 1 ? 3 : w == 2 ? 2 : w == 3 ? 1 : -1) : (w == 1 ? 1 : w == 2 ? 0 : -1); }
+    static constexpr int prow1(int w) { return NTT == 4 && w == 2 ? 0 : -1; }
 };
 
 template <int KD, int C>
@@ -80,8 +76,9 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
 
     // ---- registers of the next chunk ----
     u32x4 rk[PK];
-    bf16x8 qf[NKS];
+    bf16x8 qf[NKS], qf1[NKS];                 // Q fragments of P row tiles prow0(w), prow1(w)
     float rb = 0.f, rg = 0.f;
+    const int pr0 = S::prow0(w), pr1 = S::prow1(w);
     auto prefetch = [&](int ci) {
         const int bh = ci / NT, c = ci % NT, b = bh / H, h = bh % H, t0 = c * C;
         const size_t row0 = (size_t)b * T * H + h;
@@ -91,11 +88,17 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
             const int tt = min(t0 + idx / (KD / 8), T - 1);
             rk[q] = *reinterpret_cast<const u32x4 *>(kg + (row0 + (size_t)tt * H) * KD + (idx % (KD / 8)) * 8);
         }
-        if (w < NTT) {                          // Q rows of P row tile w
-            const int tq = min(t0 + w * 16 + c16, T - 1);
+        if (pr0 >= 0) {                         // Q rows of the P row tiles of this wave
+            const int tq = min(t0 + pr0 * 16 + c16, T - 1);
 #pragma unroll
             for (int m = 0; m < NKS; ++m)
                 qf[m] = *reinterpret_cast<const bf16x8 *>(qg + (row0 + (size_t)tq * H) * KD + m * 32 + 8 * g);
+        }
+        if (pr1 >= 0) {
+            const int tq = min(t0 + pr1 * 16 + c16, T - 1);
+#pragma unroll
+            for (int m = 0; m < NKS; ++m)
+                qf1[m] = *reinterpret_cast<const bf16x8 *>(qg + (row0 + (size_t)tq * H) * KD + m * 32 + 8 * g);
         }
         if (w == 0) {
             const int tt = min(t0 + l, T - 1);
@@ -136,34 +139,10 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
         }
         __syncthreads();
 
-        // ---- P row tile w (fragments to the work space) ----
-        if (w < NTT) {
-            const float g2t = G2[w * 16 + c16];
-            uint4 *dst = reinterpret_cast<uint4 *>(args.pfrag) + ((size_t)bh * NT + c) * NLOW * 64 +
-                         (w * (w + 1) / 2) * 64 + l;
-            for (int tj = 0; tj <= w; ++tj) {
-                floatx4 acc = zero4();
-                const u16 *krow = Ks + (tj * 16 + c16) * LDK;
-#pragma unroll
-                for (int m = 0; m < NKS; ++m) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                                   ld8(krow + m * 32 + 8 * g), qf[m], acc, 0, 0, 0);
-                const floatx4 g2s = *reinterpret_cast<const floatx4 *>(G2 + tj * 16 + 4 * g);
-                float pv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int s = tj * 16 + 4 * g + e;
-                    pv[e] = s <= w * 16 + c16 ? acc[e] * fast_exp2(fminf(g2t - g2s[e], 0.f)) : 0.f;
-                }
-                uint4 f;
-                split2_bf16(pv[0], pv[1], f.x, f.z);
-                split2_bf16(pv[2], pv[3], f.y, f.w);
-                dst[tj * 64] = f;
-            }
-        }
-        // ---- gram tiles of this wave: As[t][s] = [s<t] beta_t (k_t.k_s) e^{G_t-G_s} ----
+        // ---- gram tiles (round robin): As[t][s] = [s<t] beta_t (k_t.k_s) e^{G_t-G_s} ----
 #pragma unroll
         for (int kk = 0; kk < NLOW; ++kk) {
-            if (S::gram_owner(kk) != w) continue;
+            if (kk % 4 != w) continue;
             int ti = 0, p = kk;
             while (p > ti) { p -= ti + 1; ++ti; }
             const int tj = p;
@@ -175,14 +154,14 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
                                                               0, 0, 0);
             const int s = tj * 16 + c16;
             const float g2s = G2[s];
+            const floatx4 g2t = *reinterpret_cast<const floatx4 *>(G2 + ti * 16 + 4 * g);
+            const floatx4 bt = *reinterpret_cast<const floatx4 *>(betas + ti * 16 + 4 * g);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = ti * 16 + 4 * g + e;
-                As[t * LDA + s] = s < t ? betas[t] * acc[e] * fast_exp2(fminf(G2[t] - g2s, 0.f)) : 0.f;
+                As[t * LDA + s] = s < t ? bt[e] * acc[e] * fast_exp2(fminf(g2t[e] - g2s, 0.f)) : 0.f;
             }
         }
-        // registers are free: start loading the next chunk
-        if (ci + (int)gridDim.x < total) prefetch(ci + gridDim.x);
         __syncthreads();
 
         // ---- diagonal blocks by forward substitution (wave 0); K^T out (others) ----
@@ -195,7 +174,12 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
                 for (int i = 0; i < 16; ++i) {
                     float acc = (i == col) ? 1.f : 0.f;
 #pragma unroll
-                    for (int j = 0; j < i; ++j) acc -= Ab[i * LDA + j] * x[j];
+                    for (int j4 = 0; j4 < i; j4 += 4) {        // row i of the block, 4 entries per read
+                        const floatx4 a4 = *reinterpret_cast<const floatx4 *>(Ab + i * LDA + j4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (j4 + e < i) acc -= a4[e] * x[j4 + e];
+                    }
                     x[i] = acc;
                 }
                 float *Tc = Ts + (ib * 16) * LDA + ib * 16 + col;
@@ -203,6 +187,32 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
                 for (int i = 0; i < 16; ++i) Tc[i * LDA] = x[i];
             }
         } else {
+            // P row tiles of this wave (fragments to the work space)
+            auto p_row = [&](int ti, const bf16x8 (&q)[NKS]) {
+                const float g2t = G2[ti * 16 + c16];
+                uint4 *dst = reinterpret_cast<uint4 *>(args.pfrag) + ((size_t)bh * NT + c) * NLOW * 64 +
+                             (ti * (ti + 1) / 2) * 64 + l;
+                for (int tj = 0; tj <= ti; ++tj) {
+                    floatx4 acc = zero4();
+                    const u16 *krow = Ks + (tj * 16 + c16) * LDK;
+#pragma unroll
+                    for (int m = 0; m < NKS; ++m) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                                       ld8(krow + m * 32 + 8 * g), q[m], acc, 0, 0, 0);
+                    const floatx4 g2s = *reinterpret_cast<const floatx4 *>(G2 + tj * 16 + 4 * g);
+                    float pv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = tj * 16 + 4 * g + e;
+                        pv[e] = s <= ti * 16 + c16 ? acc[e] * fast_exp2(fminf(g2t - g2s[e], 0.f)) : 0.f;
+                    }
+                    uint4 f;
+                    split2_bf16(pv[0], pv[1], f.x, f.z);
+                    split2_bf16(pv[2], pv[3], f.y, f.w);
+                    dst[tj * 64] = f;
+                }
+            };
+            if (pr0 >= 0) p_row(pr0, qf);
+            if (pr1 >= 0) p_row(pr1, qf1);
             // lane (g, j) of block (it, m): K^T row i = 16 it + j, stored chunk 4m + g =
             // tokens 32m + 4g + {0..3} and 32m + 16 + 4g + {0..3}, read transposed from Ks
             u16 *kout = reinterpret_cast<u16 *>(args.ktmat) + ((size_t)bh * NT + c) * KD * C;
@@ -216,6 +226,8 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
                 *reinterpret_cast<uint4 *>(kout + i * C + js * 8) = uint4{lo.x, lo.y, hi.x, hi.y};
             }
         }
+        // registers are free: start loading the next chunk
+        if (ci + (int)gridDim.x < total) prefetch(ci + gridDim.x);
         __syncthreads();
 
         // ---- block rows: T_ij = -T_ii sum_{j<=m<i} A_im T_mj, one column block per wave ----
@@ -243,6 +255,30 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
         // ---- W = T diag(beta e^G) K as W^T tiles K^T (T diag(beta e^G))^T ----
         {
             u16 *wout = reinterpret_cast<u16 *>(args.wmat) + ((size_t)bh * NT + c) * C * KD;
+            // B operands (T diag(beta e^G))^T, hi + lo, of every (tt, m) inside
+            // the block triangle: the same for all key tiles it of this wave
+            bf16x8 bh[NTT][C / 32], bl[NTT][C / 32];
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) {
+                const int t = tt * 16 + c16;
+#pragma unroll
+                for (int m = 0; m < C / 32; ++m) {
+                    if (2 * m > tt) break;                      // T is block lower triangular
+                    const int s0 = m * 32 + 8 * g;
+                    const bool ok = (s0 >> 4) <= tt;
+                    const floatx4 x0 = *reinterpret_cast<const floatx4 *>(Ts + t * LDA + s0);
+                    const floatx4 x1 = *reinterpret_cast<const floatx4 *>(Ts + t * LDA + s0 + 4);
+                    const floatx4 b0 = *reinterpret_cast<const floatx4 *>(BEG + s0);
+                    const floatx4 b1 = *reinterpret_cast<const floatx4 *>(BEG + s0 + 4);
+                    uint4 hi, lo;
+                    split2_bf16(ok ? x0[0] * b0[0] : 0.f, ok ? x0[1] * b0[1] : 0.f, hi.x, lo.x);
+                    split2_bf16(ok ? x0[2] * b0[2] : 0.f, ok ? x0[3] * b0[3] : 0.f, hi.y, lo.y);
+                    split2_bf16(ok ? x1[0] * b1[0] : 0.f, ok ? x1[1] * b1[1] : 0.f, hi.z, lo.z);
+                    split2_bf16(ok ? x1[2] * b1[2] : 0.f, ok ? x1[3] * b1[3] : 0.f, hi.w, lo.w);
+                    bh[tt][m] = __builtin_bit_cast(bf16x8, hi);
+                    bl[tt][m] = __builtin_bit_cast(bf16x8, lo);
+                }
+            }
             for (int it = w; it < KD / 16; it += 4) {
                 // K^T fragments of rows 16 it + j, k = 32 m + 8 g + {0..7}
                 bf16x8 ka[C / 32];
@@ -259,22 +295,9 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
                     floatx4 acc = zero4();
 #pragma unroll
                     for (int m = 0; m < C / 32; ++m) {
-                        if (2 * m > tt) break;                  // T is block lower triangular
-                        const int s0 = m * 32 + 8 * g;
-                        const bool ok = (s0 >> 4) <= tt;
-                        const floatx4 x0 = *reinterpret_cast<const floatx4 *>(Ts + t * LDA + s0);
-                        const floatx4 x1 = *reinterpret_cast<const floatx4 *>(Ts + t * LDA + s0 + 4);
-                        const floatx4 b0 = *reinterpret_cast<const floatx4 *>(BEG + s0);
-                        const floatx4 b1 = *reinterpret_cast<const floatx4 *>(BEG + s0 + 4);
-                        uint4 hi, lo;
-                        split2_bf16(ok ? x0[0] * b0[0] : 0.f, ok ? x0[1] * b0[1] : 0.f, hi.x, lo.x);
-                        split2_bf16(ok ? x0[2] * b0[2] : 0.f, ok ? x0[3] * b0[3] : 0.f, hi.y, lo.y);
-                        split2_bf16(ok ? x1[0] * b1[0] : 0.f, ok ? x1[1] * b1[1] : 0.f, hi.z, lo.z);
-                        split2_bf16(ok ? x1[2] * b1[2] : 0.f, ok ? x1[3] * b1[3] : 0.f, hi.w, lo.w);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], __builtin_bit_cast(bf16x8, hi), acc,
-                                                                      0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], __builtin_bit_cast(bf16x8, lo), acc,
-                                                                      0, 0, 0);
+                        if (2 * m > tt) break;
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], bh[tt][m], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], bl[tt][m], acc, 0, 0, 0);
                     }
                     // lane: W[t][16 it + 4g + e], stored in the permuted order
                     *reinterpret_cast<uint2 *>(wout + (size_t)t * KD + perm4_pos(it * 16 + 4 * g)) =
