@@ -11,7 +11,7 @@
 //   wave 0 ("chain") owns the (KD x 16) fp32 state slice in MFMA
 //   accumulators and runs the dependent part of every chunk in registers,
 //   in the page's WY form (u - w h):
-//       V_new = U - W S,  U = T diag(beta) V,  W = T diag(beta e^G) K;
+//       V_new = U - W S,  U = (T diag(beta)) V,  W = T diag(beta e^G) K;
 //       S <- e^{G_L} S + K^T diag(e^{G_L - G}) V_new.
 //   W comes from the solve kernel; U does not depend on S, so its MFMAs
 //   overlap those of W S.
@@ -20,17 +20,17 @@
 //   a 32-wide MFMA step in the order {4g..4g+3, 16+4g..16+4g+3} (g = l/16)
 //   instead of 8g..8g+7; the A operand rows (W, K^T) are stored in that
 //   permuted order by the solve kernel, so each lane reads them as one
-//   16-byte piece and the sum over k is unchanged.  It publishes V_new and
-//   the chunk-start state to LDS in fp32 for the output waves.
+//   16-byte piece and the sum over k is unchanged.  It publishes V_new
+//   (fp32) and the chunk-start state (hi + lo bf16) to LDS for the output
+//   waves.
 //
 //   waves 1..C/16 ("out"), one 16-token tile each: the output, transposed,
 //   O^T = S_start^T Q^T e^G + V_new^T P^T (P, the causal intra-chunk scores,
 //   comes from the solve kernel as ready MFMA fragments; the transposed
 //   accumulator gives each lane 4 consecutive values of one token, one
 //   16-byte store), and the staging of the next chunks: a register prefetch
-//   one chunk ahead, then W, K^T and T (copied as written by the solve
-//   kernel), beta V (transposed, hi + lo bf16) and the gate table committed
-//   to LDS.
+//   one chunk ahead, then W, K^T, T diag(beta) and the gate table (copied as
+//   written by the prep kernel) and the V slice committed to LDS.
 //
 // One workgroup barrier per chunk.  Iteration c: the chain processes chunk c
 // and publishes its start state and V_new; the out waves write the output of
@@ -65,8 +65,8 @@ struct Chain1Shape {
     static constexpr int LDK = KD + 8;        // Ws  [C][KD]   bf16, W (permuted k order)
     static constexpr int LDKT = C + 8;        // KsT [KD][C]   bf16, permuted, 16-byte chunks swizzled
     static constexpr int LDT = C + 8;         // Tb  [C][C]    bf16
-    static constexpr int LDBV = C + 8;        // BVs [2][BV][C] bf16 hi, lo of beta V transposed
-    static constexpr int LDSF = KD + 4;       // St  [BV][KD]  fp32, S_start transposed
+    static constexpr int LDV = BV + 8;        // Vs  [C][BV]   bf16, the V slice (row-major)
+    static constexpr int LDSH = KD + 8;       // St  [2][BV][KD] bf16 hi, lo of S_start transposed
     static constexpr int LDVF = C + 4;        // Vn  [BV][C]   fp32, V_new transposed
     // gate table: e^G [C], e^{G_L-G} [C], e^{G_L}
     static constexpr int NGATE = 2 * C + 4;
@@ -74,9 +74,9 @@ struct Chain1Shape {
     static constexpr int SZ_KS = al(C * LDK * 2);
     static constexpr int SZ_KST = al(KD * LDKT * 2);
     static constexpr int SZ_TB = al(C * LDT * 2);
-    static constexpr int SZ_BV = al(2 * BV * LDBV * 2);
+    static constexpr int SZ_BV = al(C * LDV * 2);
     static constexpr int SZ_GATE = al(NGATE * 4);
-    static constexpr int SZ_ST = al(BV * LDSF * 4);
+    static constexpr int SZ_ST = al(2 * BV * LDSH * 2);
     static constexpr int SZ_VN = al(BV * LDVF * 4);
     // every buffer is double: index p = chunk & 1
     static constexpr int OFF_KS = 0;
@@ -126,7 +126,7 @@ template <int KD, int C>
 __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain1_kernel(ChunkArgs args) {
     using S = Chain1Shape<KD, C>;
     constexpr int BV = S::BV, NTT = S::NTT, NKS = S::NKS, NST = S::NST, NCS = S::NCS;
-    constexpr int LDK = S::LDK, LDKT = S::LDKT, LDT = S::LDT, LDBV = S::LDBV, LDSF = S::LDSF, LDVF = S::LDVF;
+    constexpr int LDK = S::LDK, LDKT = S::LDKT, LDT = S::LDT, LDV = S::LDV, LDSH = S::LDSH, LDVF = S::LDVF;
     constexpr int SWM = S::SWM;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::BYTES];
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
     auto Tb = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_TB + p * S::SZ_TB); };
     auto BVs = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_BV + p * S::SZ_BV); };
     auto gate = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_GATE + p * S::SZ_GATE); };
-    auto St = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_ST + p * S::SZ_ST); };
+    auto St = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_ST + p * S::SZ_ST); };
     auto Vn = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_VN + p * S::SZ_VN); };
 
     if (w == 0) {
@@ -162,11 +162,29 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
         // chain wave
         // =================================================================
         floatx4 Sreg[NST];
-        auto publish_state = [&](int p) {      // S_start, fp32 [j][i]
-            float *st = St(p);
+        // S_start as hi + lo bf16, transposed to [j][i], for the output
+        // waves; hi[m] is the W S operand (the state rounded once).  A
+        // fragment holds rows {4g..4g+3} and {16+4g..16+4g+3} of 32-row
+        // block m: two 8-byte pieces each.
+        auto publish_state = [&](int p, const bf16x8 (&hi)[NKS]) {
+            u16 *sh = St(p) + c16 * LDSH, *sl = sh + BV * LDSH;
 #pragma unroll
-            for (int ti = 0; ti < NST; ++ti)
-                *reinterpret_cast<floatx4 *>(st + c16 * LDSF + ti * 16 + 4 * g) = Sreg[ti];
+            for (int m = 0; m < NKS; ++m) {
+                const uint4 h = __builtin_bit_cast(uint4, hi[m]);
+                uint4 o;
+                o.x = cvt2_bf16(Sreg[2 * m][0] - __builtin_bit_cast(float, h.x << 16),
+                                Sreg[2 * m][1] - __builtin_bit_cast(float, h.x & 0xffff0000u));
+                o.y = cvt2_bf16(Sreg[2 * m][2] - __builtin_bit_cast(float, h.y << 16),
+                                Sreg[2 * m][3] - __builtin_bit_cast(float, h.y & 0xffff0000u));
+                o.z = cvt2_bf16(Sreg[2 * m + 1][0] - __builtin_bit_cast(float, h.z << 16),
+                                Sreg[2 * m + 1][1] - __builtin_bit_cast(float, h.z & 0xffff0000u));
+                o.w = cvt2_bf16(Sreg[2 * m + 1][2] - __builtin_bit_cast(float, h.w << 16),
+                                Sreg[2 * m + 1][3] - __builtin_bit_cast(float, h.w & 0xffff0000u));
+                *reinterpret_cast<uint2 *>(sh + m * 32 + 4 * g) = uint2{h.x, h.y};
+                *reinterpret_cast<uint2 *>(sh + m * 32 + 16 + 4 * g) = uint2{h.z, h.w};
+                *reinterpret_cast<uint2 *>(sl + m * 32 + 4 * g) = uint2{o.x, o.y};
+                *reinterpret_cast<uint2 *>(sl + m * 32 + 16 + 4 * g) = uint2{o.z, o.w};
+            }
         };
 #pragma unroll
         for (int ti = 0; ti < NST; ++ti) {
@@ -185,15 +203,18 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
             // All LDS operands of W S and U first (nothing here depends on the
             // state), so their latency overlaps; the MFMAs below run over the
             // token tiles innermost, so consecutive MFMAs are independent.
-            bf16x8 wf[NTT][NKS], tf[NTT][NCS], bvh[NCS], bvl[NCS];
+            bf16x8 wf[NTT][NKS], tf[NTT][NCS], vf[NCS];
 #pragma unroll
             for (int m = 0; m < NKS; ++m)
 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt) wf[tt][m] = ld8(ws + (tt * 16 + c16) * LDK + m * 32 + 8 * g);
 #pragma unroll
             for (int m = 0; m < NCS; ++m) {
-                bvh[m] = ld8(bv + c16 * LDBV + m * 32 + 8 * g);
-                bvl[m] = ld8(bv + (BV + c16) * LDBV + m * 32 + 8 * g);
+                // V rows 32m + 8g + {0..7}, column j = lane%16: transposed reads
+                const u16 *vp = bv + (m * 32 + 8 * g + (c16 >> 2)) * LDV + 4 * (c16 & 3);
+                const uint2 v0 = __builtin_bit_cast(uint2, ld_tr16(vp));
+                const uint2 v1 = __builtin_bit_cast(uint2, ld_tr16(vp + 4 * LDV));
+                vf[m] = __builtin_bit_cast(bf16x8, uint4{v0.x, v0.y, v1.x, v1.y});
 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt)
                     if (2 * m <= tt) tf[tt][m] = ld8(tb + (tt * 16 + c16) * LDT + m * 32 + 8 * g);
@@ -201,8 +222,8 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
             bf16x8 sb[NKS];
 #pragma unroll
             for (int m = 0; m < NKS; ++m) sb[m] = frag_hi(Sreg[2 * m], Sreg[2 * m + 1]);
-            publish_state(p);                    // S_start of chunk c
-            // X = W S and U = T (beta V) (T is block lower triangular)
+            publish_state(p, sb);                // S_start of chunk c
+            // X = W S and U = (T diag(beta)) V (T is block lower triangular)
             floatx4 x[NTT], u[NTT];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) x[tt] = u[tt] = zero4();
@@ -214,10 +235,7 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
             for (int m = 0; m < NCS; ++m) {
 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt)
-                    if (2 * m <= tt) u[tt] = mfma32(tf[tt][m], bvh[m], u[tt]);
-#pragma unroll
-                for (int tt = 0; tt < NTT; ++tt)
-                    if (2 * m <= tt) u[tt] = mfma32(tf[tt][m], bvl[m], u[tt]);
+                    if (2 * m <= tt) u[tt] = mfma32(tf[tt][m], vf[m], u[tt]);
             }
             // operands of the state update, read while the MFMAs run
             bf16x8 kf[NST][NCS];
@@ -285,35 +303,37 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
     //
     // Roles: OW = token tile of the output (-1: none); group A (index LA,
     // NLA threads): C*KD/8/NLA 16-byte vectors each of W and of K^T; group B
-    // (index LB, NLB threads): C*C/8/NLB 16-byte vectors of T and 4 values of
-    // the V slice per thread; GATE: the gate table.
+    // (index LB, NLB threads): C*C/8/NLB 16-byte vectors of T diag(beta), and
+    // (the last 2C of them) the 16-byte pieces of the V slice; GATE: the gate
+    // table.
     constexpr int NLA = S::NLA, NLB = S::NLB;
     constexpr int NTV = C * C / 8;              // 16-byte vectors of T
     constexpr int PT = NTV / NLB;
     constexpr int NWV = C * KD / 8;             // 16-byte vectors of W (and of K^T)
     constexpr int PW = NWV / NLA;
     constexpr int NLOW = NTT * (NTT + 1) / 2;
-    static_assert(PT * NLB == NTV && PW * NLA == NWV && C * BV == 4 * NLB, "loader split");
+    constexpr int NGV = (2 * C + 4) / 4;        // 16-byte vectors of a gate table
+    static_assert(PT * NLB == NTV && PW * NLA == NWV && 2 * C <= NLB && NGV <= 64, "loader split");
     const size_t tokq = (size_t)H * KD, tokv = (size_t)H * Dv;
     const u16 *ktg = reinterpret_cast<const u16 *>(args.ktmat) + (size_t)bh * NT * KD * C;
     const u16 *qg = reinterpret_cast<const u16 *>(args.q) + ((size_t)b * T * H + h) * KD;
     const u16 *vg = reinterpret_cast<const u16 *>(args.v) + ((size_t)b * T * H + h) * Dv + v0;
     const u16 *tg = reinterpret_cast<const u16 *>(args.tmat) + (size_t)bh * NT * C * C;
     const u16 *wg = reinterpret_cast<const u16 *>(args.wmat) + (size_t)bh * NT * C * KD;
-    const float *betag = args.beta + (size_t)b * T * H + h, *gg = args.g + (size_t)b * T * H + h;
+    const float *gtg = reinterpret_cast<const float *>(args.gtab) + (size_t)bh * NT * (2 * C + 4);
 
     auto out_wave = [&](auto owc, auto lac, auto lbc, auto gatec) {
         constexpr int OW = decltype(owc)::value, LA = decltype(lac)::value, LB = decltype(lbc)::value;
         constexpr bool TILE = OW >= 0, GA = LA >= 0, GB = LB >= 0, GATE = decltype(gatec)::value;
         constexpr bool LOAD = GA || GB || GATE;
         const int ia = (GA ? LA : 0) * 64 + l, ib = (GB ? LB : 0) * 64 + l;   // group thread indices
-        const int vtok = ib % C, vcol = 4 * (ib / C);       // this lane's 4 values of V
+        // the last 2C threads of group B (the lighter output tiles) stage V:
+        // token vi / 2, columns 8 (vi % 2) ..
+        const int vi = ib - (NLB - 2 * C), vtok = max(vi, 0) >> 1, vcol = 8 * (max(vi, 0) & 1);
         // Rows past T are clamped to T-1 (and zeroed when committed); a chunk
         // index past the end is clamped to the last chunk (its staging then
         // lands in a buffer no one reads).
-        u32x4 rk[PW], rt[PT], rw[PW];
-        uint2 rv;
-        float rbv = 0.f, rg = 0.f;
+        u32x4 rk[PW], rt[PT], rw[PW], rv, rg;
         auto prefetch = [&](int c) {
             c = min(c, NT - 1);
             const int t0 = c * C;
@@ -330,13 +350,10 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
                 for (int q = 0; q < PT; ++q)
                     rt[q] = reinterpret_cast<const u32x4 *>(tg + (size_t)c * C * C)[ib + NLB * q];
                 const int t = min(t0 + vtok, tlast);
-                rv = *reinterpret_cast<const uint2 *>(vg + (size_t)t * tokv + vcol);
-                rbv = betag[(size_t)t * H];
+                rv = *reinterpret_cast<const u32x4 *>(vg + (size_t)t * tokv + vcol);
             }
-            if constexpr (GATE) {
-                const int tt = min(t0 + l, tlast);
-                rg = gg[(size_t)tt * H];
-            }
+            if constexpr (GATE)
+                rg = reinterpret_cast<const u32x4 *>(gtg + (size_t)c * (2 * C + 4))[min(l, NGV - 1)];
         };
         auto commit = [&](int c) {
             const int p = c & 1, t0 = c * C;
@@ -360,35 +377,11 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
                     const int idx = ib + NLB * q;
                     *reinterpret_cast<u32x4 *>(tb + (idx / (C / 8)) * LDT + (idx % (C / 8)) * 8) = rt[q];
                 }
-                // beta V as hi + lo bf16, transposed to [j][t]
-                const float bt = (t0 + vtok < T) ? rbv : 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; e += 2) {
-                    const uint32_t wv = e ? rv.y : rv.x;
-                    uint32_t hi, lo;
-                    split2_bf16(bt * bf16_to_f32((u16)(wv & 0xffffu)), bt * bf16_to_f32((u16)(wv >> 16)), hi, lo);
-                    const int j = vcol + e;
-                    bv[j * LDBV + vtok] = (u16)(hi & 0xffffu);
-                    bv[(j + 1) * LDBV + vtok] = (u16)(hi >> 16);
-                    bv[(BV + j) * LDBV + vtok] = (u16)(lo & 0xffffu);
-                    bv[(BV + j + 1) * LDBV + vtok] = (u16)(lo >> 16);
-                }
+                if (vi >= 0)                    // V rows of tokens past T are zero
+                    *reinterpret_cast<u32x4 *>(bv + vtok * LDV + vcol) = t0 + vtok < T ? rv : u32x4{0u, 0u, 0u, 0u};
             }
-            if constexpr (GATE) {               // the cumsum and the gate table
-                const bool ok = l < C && t0 + l < T;
-                float gs = ok ? rg : 0.f;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float y = __shfl_up(gs, off, 64);
-                    if (l >= off) gs += y;
-                }
-                const float g2 = gs * LOG2E;
-                const float g2l = __shfl(g2, C - 1, 64);
-                if (l < C) {
-                    gp[l] = fast_exp2(g2);                   // e^{G_t}
-                    gp[C + l] = fast_exp2(g2l - g2);         // e^{G_L - G_t}
-                }
-                if (l == 0) gp[2 * C] = fast_exp2(g2l);     // e^{G_L}
+            if constexpr (GATE) {               // the gate table
+                if (l < NGV) reinterpret_cast<u32x4 *>(gp)[l] = rg;
             }
         };
 
@@ -412,16 +405,13 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
         };
         // O^T of chunk c: a1 = S_start^T Q^T, a2 = V_new^T P^T (buffers c & 1)
         auto compute_out = [&](int c) {
-            const float *st = St(c & 1), *vnp = Vn(c & 1);
+            const u16 *sh = St(c & 1) + c16 * LDSH, *sl = sh + BV * LDSH;
+            const float *vnp = Vn(c & 1);
             floatx4 a1 = zero4(), a2 = zero4();
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
-                const floatx4 s0 = *reinterpret_cast<const floatx4 *>(st + c16 * LDSF + m * 32 + 8 * g);
-                const floatx4 s1 = *reinterpret_cast<const floatx4 *>(st + c16 * LDSF + m * 32 + 8 * g + 4);
-                bf16x8 sh, sl;
-                frag_split(s0, s1, sh, sl);
-                a1 = mfma32(sh, qf[m], a1);
-                a1 = mfma32(sl, qf[m], a1);
+                a1 = mfma32(ld8(sh + m * 32 + 8 * g), qf[m], a1);
+                a1 = mfma32(ld8(sl + m * 32 + 8 * g), qf[m], a1);
             }
 #pragma unroll
             for (int tj = 0; tj <= TW; ++tj) {

@@ -61,6 +61,7 @@ struct ChunkArgs {
     void *pfrag;     // work space: intra-chunk P tiles as MFMA fragments (PFRAG shapes)
     void *wmat;      // work space: W = T diag(beta e^G) K per chunk, bf16 [C][KD] (PFRAG shapes)
     void *ktmat;     // work space: K^T per chunk, bf16 [KD][C], 16-byte chunks swizzled (PFRAG shapes)
+    void *gtab;      // work space: e^{G_t} [C], e^{G_L - G_t} [C], e^{G_L}, 0, 0, 0 per chunk, fp32 (PFRAG shapes)
     int B, T, H, Dv;
     int out_bf16;
     float scale;
@@ -687,7 +688,9 @@ size_t chunk_workspace_bytes(int B, int T, int H) {
     using S = ChunkShape<F32IN, KD, C, R>;
     const size_t NT = (size_t)(T + C - 1) / C;
     const size_t wbytes = S::PFRAG ? 2 * (size_t)B * H * NT * C * KD * 2 : 0;   // W and K^T
-    return chunk_tmat_bytes<F32IN, KD, C, R>(B, T, H) + chunk_pfrag_bytes<F32IN, KD, C, R>(B, T, H) + wbytes;
+    const size_t gbytes = S::PFRAG ? (size_t)B * H * NT * (2 * C + 4) * 4 : 0;  // gate tables
+    return chunk_tmat_bytes<F32IN, KD, C, R>(B, T, H) + chunk_pfrag_bytes<F32IN, KD, C, R>(B, T, H) + wbytes +
+           gbytes;
 }
 
 }  // namespace gdn

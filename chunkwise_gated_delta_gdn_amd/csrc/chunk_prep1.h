@@ -8,12 +8,14 @@
 //   G       chunk-local cumsum of the log-decay (kept in log2 units)
 //   A       [s<t] beta_t (k_t . k_s) e^{G_t - G_s}       (fp32, LDS)
 //   T       (I + A)^-1: 16x16 diagonal blocks by forward substitution, then
-//           block rows T_ij = -T_ii sum_m A_im T_mj                  -> bf16
+//           block rows T_ij = -T_ii sum_m A_im T_mj; stored as T diag(beta)
+//           (so the state pass forms U = T diag(beta) V from exact V) -> bf16
 //   W       T diag(beta e^G) K, rows in the permuted k order         -> bf16
 //   K^T     rows of C tokens, permuted k order, 16-byte chunks swizzled
 //   P       [s<=t] (q_t . k_s) e^{G_t - G_s} of the lower 16x16 tiles, as
 //           hi/lo bf16 MFMA fragments (lane l: row t = 16 ti + l%16,
 //           columns s = 16 tj + 4 (l/16) + e)
+//   gates   e^{G_t}, e^{G_L - G_t}, e^{G_L}                           -> fp32
 //
 // Persistent workgroups of 4 waves walk the chunks with a stride of the
 // grid; the next chunk's K, Q, beta and g are loaded into registers while the
@@ -129,12 +131,18 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
                 const float y = __shfl_up(gs, off, 64);
                 if (l >= off) gs += y;
             }
+            const float g2 = gs * LOG2E;
+            const float g2l = __shfl(g2, C - 1, 64);
             if (l < C) {
-                const float g2 = gs * LOG2E;
                 const float bt = ok ? rb : 0.f;
+                const float eg = fast_exp2(g2);
                 betas[l] = bt;
                 G2[l] = g2;
-                BEG[l] = bt * fast_exp2(g2);
+                BEG[l] = bt * eg;
+                float *gt = reinterpret_cast<float *>(args.gtab) + ((size_t)bh * NT + c) * (2 * C + 4);
+                gt[l] = eg;                          // e^{G_t}
+                gt[C + l] = fast_exp2(g2l - g2);     // e^{G_L - G_t}
+                if (l < 4) gt[2 * C + l] = l == 0 ? fast_exp2(g2l) : 0.f;   // e^{G_L}
             }
         }
         __syncthreads();
@@ -305,13 +313,20 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
                 }
             }
         }
-        // ---- T (zero above the block diagonal), bf16 ----
+        // ---- T diag(beta) (zero above the block diagonal), bf16 ----
         {
             u16 *out = reinterpret_cast<u16 *>(args.tmat) + ((size_t)bh * NT + c) * C * C;
             for (int idx = tid; idx < C * C / 8; idx += 256) {
                 const int i = idx / (C / 8), j0 = (idx % (C / 8)) * 8;
                 floatx4 x0 = *reinterpret_cast<const floatx4 *>(Ts + i * LDA + j0);
                 floatx4 x1 = *reinterpret_cast<const floatx4 *>(Ts + i * LDA + j0 + 4);
+                const floatx4 b0 = *reinterpret_cast<const floatx4 *>(betas + j0);
+                const floatx4 b1 = *reinterpret_cast<const floatx4 *>(betas + j0 + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x0[e] *= b0[e];
+                    x1[e] *= b1[e];
+                }
                 if ((j0 >> 4) > (i >> 4)) x0 = x1 = zero4();
                 *reinterpret_cast<uint4 *>(out + (size_t)i * C + j0) =
                     uint4{cvt2_bf16(x0[0], x0[1]), cvt2_bf16(x0[2], x0[3]), cvt2_bf16(x1[0], x1[1]),
