@@ -19,9 +19,9 @@
 //
 // Persistent workgroups of 4 waves walk the chunks with a stride of the
 // grid; the next chunk's K, Q, beta and g are loaded into registers while the
-// current one is solved, so the global-load latency stays hidden.  While
-// wave 0 runs the (sequential) forward substitution, waves 1..3 compute the
-// P tiles and write K^T.
+// current one is solved, so the global-load latency stays hidden.  Wave 0
+// inverts I + A alone (forward substitution, then the block rows: no
+// barriers) while waves 1..3 compute the P tiles and write K^T.
 #pragma once
 
 #include "chunk_kernels.h"
@@ -35,29 +35,28 @@ struct Prep1Shape {
     static constexpr int NKS = KD / 32;       // 32-wide k steps over the key dim
     static constexpr int LDK = KD + 8;        // Ks [C][KD] bf16
     static constexpr int LDA = C + 4;         // As, Ts [C][C] fp32
-    static constexpr int LDY = 17;            // merge scratch [16][17] fp32 per wave
     static constexpr int NKV = C * KD / 8;    // 16-byte vectors of K per chunk
     static constexpr int PK = (NKV + 255) / 256;
     static constexpr int al(int x) { return (x + 15) & ~15; }
     static constexpr int OFF_KS = 0;
     static constexpr int OFF_AS = OFF_KS + al(C * LDK * 2);
     static constexpr int OFF_TS = OFF_AS + al(C * LDA * 4);
-    static constexpr int OFF_Y = OFF_TS + al(C * LDA * 4);
-    static constexpr int OFF_G = OFF_Y + al(4 * 16 * LDY * 4);
+    static constexpr int OFF_G = OFF_TS + al(C * LDA * 4);
     static constexpr int BYTES = OFF_G + al(3 * C * 4);   // beta, G2, beta e^G
     static_assert(C % 32 == 0 && C <= 64 && KD % 32 == 0 && KD <= 256, "shape");
     static_assert(BYTES <= 80 * 1024, "two workgroups per CU");
-    // P row tiles during the substitution (waves 1..3; wave 0 substitutes):
-    // wave w takes rows prow0(w) and prow1(w) (-1: none), so that the
-    // 1 + 2 + ... + NTT tiles spread evenly.
-    static constexpr int prow0(int w) { return NTT == 4 ? (w == 1 ? 3 : w == 2 ? 2 : w == 3 ? 1 : -1) : (w == 1 ? 1 : w == 2 ? 0 : -1); }
+    // P row tiles while wave 0 inverts (waves 1..3; wave 3 also writes K^T):
+    // wave w takes rows prow0(w) and prow1(w) (-1: none).
+    static constexpr int prow0(int w) {
+        return NTT == 4 ? (w == 1 ? 3 : w == 2 ? 2 : w == 3 ? 1 : -1) : (w == 1 ? 1 : w == 2 ? 0 : -1);
+    }
     static constexpr int prow1(int w) { return NTT == 4 && w == 2 ? 0 : -1; }
 };
 
 template <int KD, int C>
 __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
     using S = Prep1Shape<KD, C>;
-    constexpr int NTT = S::NTT, NLOW = S::NLOW, NKS = S::NKS, LDK = S::LDK, LDA = S::LDA, LDY = S::LDY;
+    constexpr int NTT = S::NTT, NLOW = S::NLOW, NKS = S::NKS, LDK = S::LDK, LDA = S::LDA;
     constexpr int NKV = S::NKV, PK = S::PK;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::BYTES];
@@ -69,7 +68,6 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
 
     const int tid = threadIdx.x, l = tid & 63, c16 = l & 15, g = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    float *Ys = reinterpret_cast<float *>(smem + S::OFF_Y) + w * 16 * LDY;
     const int T = args.T, H = args.H;
     const int NT = (T + C - 1) / C;
     const int total = args.B * H * NT;
@@ -172,7 +170,8 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
         }
         __syncthreads();
 
-        // ---- diagonal blocks by forward substitution (wave 0); K^T out (others) ----
+        // ---- wave 0: T = (I + A)^-1 (diagonal blocks by forward substitution,
+        //      then the block rows, without barriers); waves 1..3: P, K^T ----
         if (w == 0) {
             const int ib = l >> 4, col = l & 15;
             if (ib < NTT) {
@@ -193,6 +192,28 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
                 float *Tc = Ts + (ib * 16) * LDA + ib * 16 + col;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) Tc[i * LDA] = x[i];
+            }
+            // block rows T_ij = -T_ii sum_{j<=m<i} A_im T_mj, by growing distance
+            // i - j; everything this wave reads it wrote itself (LDS is in order)
+#pragma unroll
+            for (int st = 1; st < NTT; ++st) {
+#pragma unroll
+                for (int jb = 0; jb + st < NTT; ++jb) {
+                    const int ib = jb + st;
+                    floatx4 y = zero4();
+#pragma unroll
+                    for (int m = jb; m < ib; ++m)
+                        mma_f32_bn(y, As + (ib * 16) * LDA + m * 16, LDA, Ts + (m * 16) * LDA + jb * 16, LDA, 16);
+                    // -T_ii Y with Y straight from the accumulator: lane (g, j) holds
+                    // Y[4g+e][j], fed as B[k][j] with k = 4g + s in step s, so the
+                    // A operand of step s is T_ii[row][4g + s]
+                    const floatx4 trow = *reinterpret_cast<const floatx4 *>(Ts + (ib * 16 + c16) * LDA + ib * 16 + 4 * g);
+                    floatx4 z = zero4();
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) z = __builtin_amdgcn_mfma_f32_16x16x4f32(trow[s4], y[s4], z, 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Ts[(ib * 16 + 4 * g + e) * LDA + jb * 16 + c16] = -z[e];
+                }
             }
         } else {
             // P row tiles of this wave (fragments to the work space)
@@ -224,7 +245,7 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
             // lane (g, j) of block (it, m): K^T row i = 16 it + j, stored chunk 4m + g =
             // tokens 32m + 4g + {0..3} and 32m + 16 + 4g + {0..3}, read transposed from Ks
             u16 *kout = reinterpret_cast<u16 *>(args.ktmat) + ((size_t)bh * NT + c) * KD * C;
-            for (int blk = w - 1; blk < (KD / 16) * (C / 32); blk += 3) {
+            for (int blk = w == 3 ? 0 : (KD / 16) * (C / 32); blk < (KD / 16) * (C / 32); ++blk) {
                 const int it = blk / (C / 32), m = blk % (C / 32);
                 const u16 *kp = Ks + (m * 32 + 4 * g + (c16 >> 2)) * LDK + it * 16 + 4 * (c16 & 3);
                 const uint2 lo = __builtin_bit_cast(uint2, ld_tr16(kp));
@@ -237,28 +258,6 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
         // registers are free: start loading the next chunk
         if (ci + (int)gridDim.x < total) prefetch(ci + gridDim.x);
         __syncthreads();
-
-        // ---- block rows: T_ij = -T_ii sum_{j<=m<i} A_im T_mj, one column block per wave ----
-#pragma unroll
-        for (int st = 1; st < NTT; ++st) {
-            const int jb = w, ib = w + st;
-            const bool act = ib < NTT;
-            if (act) {
-                floatx4 y = zero4();
-                for (int m = jb; m < ib; ++m)
-                    mma_f32_bn(y, As + (ib * 16) * LDA + m * 16, LDA, Ts + (m * 16) * LDA + jb * 16, LDA, 16);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Ys[(4 * g + e) * LDY + c16] = y[e];
-            }
-            __syncthreads();
-            if (act) {
-                floatx4 t2 = zero4();
-                mma_f32_bn(t2, Ts + (ib * 16) * LDA + ib * 16, LDA, Ys, LDY, 16);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Ts[(ib * 16 + 4 * g + e) * LDA + jb * 16 + c16] = -t2[e];
-            }
-            __syncthreads();
-        }
 
         // ---- W = T diag(beta e^G) K as W^T tiles K^T (T diag(beta e^G))^T ----
         {
