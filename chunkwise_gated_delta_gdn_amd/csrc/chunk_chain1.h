@@ -332,30 +332,34 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
         const int vi = ib - (NLB - 2 * C), vtok = max(vi, 0) >> 1, vcol = 8 * (max(vi, 0) & 1);
         // Rows past T are clamped to T-1 (and zeroed when committed); a chunk
         // index past the end is clamped to the last chunk (its staging then
-        // lands in a buffer no one reads).
-        u32x4 rk[PW], rt[PT], rw[PW], rv, rg;
-        auto prefetch = [&](int c) {
+        // lands in a buffer no one reads).  Two register sets: chunk c is
+        // loaded two iterations before it is committed.
+        struct Regs {
+            u32x4 rk[PW], rt[PT], rw[PW], rv, rg;
+        };
+        Regs ra, rb;
+        auto prefetch = [&](int c, Regs &r) {
             c = min(c, NT - 1);
             const int t0 = c * C;
             if constexpr (GA) {
 #pragma unroll
                 for (int q = 0; q < PW; ++q)
-                    rw[q] = reinterpret_cast<const u32x4 *>(wg + (size_t)c * C * KD)[ia + NLA * q];
+                    r.rw[q] = reinterpret_cast<const u32x4 *>(wg + (size_t)c * C * KD)[ia + NLA * q];
 #pragma unroll
                 for (int q = 0; q < PW; ++q)
-                    rk[q] = reinterpret_cast<const u32x4 *>(ktg + (size_t)c * KD * C)[ia + NLA * q];
+                    r.rk[q] = reinterpret_cast<const u32x4 *>(ktg + (size_t)c * KD * C)[ia + NLA * q];
             }
             if constexpr (GB) {
 #pragma unroll
                 for (int q = 0; q < PT; ++q)
-                    rt[q] = reinterpret_cast<const u32x4 *>(tg + (size_t)c * C * C)[ib + NLB * q];
+                    r.rt[q] = reinterpret_cast<const u32x4 *>(tg + (size_t)c * C * C)[ib + NLB * q];
                 const int t = min(t0 + vtok, tlast);
-                rv = *reinterpret_cast<const u32x4 *>(vg + (size_t)t * tokv + vcol);
+                r.rv = *reinterpret_cast<const u32x4 *>(vg + (size_t)t * tokv + vcol);
             }
             if constexpr (GATE)
-                rg = reinterpret_cast<const u32x4 *>(gtg + (size_t)c * (2 * C + 4))[min(l, NGV - 1)];
+                r.rg = reinterpret_cast<const u32x4 *>(gtg + (size_t)c * (2 * C + 4))[min(l, NGV - 1)];
         };
-        auto commit = [&](int c) {
+        auto commit = [&](int c, const Regs &r) {
             const int p = c & 1, t0 = c * C;
             u16 *ws = Ks(p), *kt = KsT(p), *tb = Tb(p), *bv = BVs(p);
             float *gp = gate(p);
@@ -363,25 +367,25 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
 #pragma unroll
                 for (int q = 0; q < PW; ++q) {  // W rows of tokens past T are zero
                     const int idx = ia + NLA * q;
-                    *reinterpret_cast<u32x4 *>(ws + (idx / (KD / 8)) * LDK + (idx % (KD / 8)) * 8) = rw[q];
+                    *reinterpret_cast<u32x4 *>(ws + (idx / (KD / 8)) * LDK + (idx % (KD / 8)) * 8) = r.rw[q];
                 }
 #pragma unroll
                 for (int q = 0; q < PW; ++q) {  // K^T, already swizzled (zero for tokens past T)
                     const int idx = ia + NLA * q;
-                    *reinterpret_cast<u32x4 *>(kt + (idx / (C / 8)) * LDKT + (idx % (C / 8)) * 8) = rk[q];
+                    *reinterpret_cast<u32x4 *>(kt + (idx / (C / 8)) * LDKT + (idx % (C / 8)) * 8) = r.rk[q];
                 }
             }
             if constexpr (GB) {
 #pragma unroll
                 for (int q = 0; q < PT; ++q) {
                     const int idx = ib + NLB * q;
-                    *reinterpret_cast<u32x4 *>(tb + (idx / (C / 8)) * LDT + (idx % (C / 8)) * 8) = rt[q];
+                    *reinterpret_cast<u32x4 *>(tb + (idx / (C / 8)) * LDT + (idx % (C / 8)) * 8) = r.rt[q];
                 }
                 if (vi >= 0)                    // V rows of tokens past T are zero
-                    *reinterpret_cast<u32x4 *>(bv + vtok * LDV + vcol) = t0 + vtok < T ? rv : u32x4{0u, 0u, 0u, 0u};
+                    *reinterpret_cast<u32x4 *>(bv + vtok * LDV + vcol) = t0 + vtok < T ? r.rv : u32x4{0u, 0u, 0u, 0u};
             }
             if constexpr (GATE) {               // the gate table
-                if (l < NGV) reinterpret_cast<u32x4 *>(gp)[l] = rg;
+                if (l < NGV) reinterpret_cast<u32x4 *>(gp)[l] = r.rg;
             }
         };
 
@@ -440,30 +444,36 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
         };
 
         // Iteration c (one barrier each): output of chunk c-1, operands of
-        // chunk c, commit of chunk c+1, prefetch of chunk c+2.
+        // chunk c, commit of chunk c+1 (register set (c+1) % 2), prefetch of
+        // chunk c+3 into the same set.
         if constexpr (LOAD) {
-            prefetch(0);
-            commit(0);
-            prefetch(1);
+            prefetch(0, ra);
+            prefetch(1, rb);
+            commit(0, ra);
+            prefetch(2, ra);
         }
         __syncthreads();
         if constexpr (TILE) load_qp(0);
         if constexpr (LOAD) {
-            commit(1);
-            prefetch(2);
+            commit(1, rb);
+            prefetch(3, rb);
         }
         __syncthreads();
-        for (int c = 1; c < NT; ++c) {
+        auto iter = [&](int c, Regs &r) {
             if constexpr (TILE) {
                 compute_out(c - 1);
                 load_qp(c);
             }
             if constexpr (LOAD) {
-                commit(c + 1);
-                prefetch(c + 2);
+                commit(c + 1, r);
+                prefetch(c + 3, r);
             }
             if constexpr (TILE) store_out(c - 1);
             __syncthreads();
+        };
+        for (int c = 1; c < NT; c += 2) {
+            iter(c, ra);
+            if (c + 1 < NT) iter(c + 1, rb);
         }
         if constexpr (TILE) {
             compute_out(NT - 1);
