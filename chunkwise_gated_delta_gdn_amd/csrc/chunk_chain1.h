@@ -28,13 +28,13 @@
 //   O^T = S_start^T Q^T e^G + V_new^T P^T (P, the causal intra-chunk scores,
 //   comes from the solve kernel as ready MFMA fragments; the transposed
 //   accumulator gives each lane 4 consecutive values of one token, one
-//   16-byte store), and the staging of the next chunks: a register prefetch
-//   one chunk ahead, then W, K^T, T diag(beta) and the gate table (copied as
-//   written by the prep kernel) and the V slice committed to LDS.
+//   16-byte store); staging waves copy the next chunk's W, K^T, T diag(beta)
+//   and gate table (as the prep kernel wrote them) and V slice straight into
+//   LDS with LDS-direct loads.
 //
 // One workgroup barrier per chunk.  Iteration c: the chain processes chunk c
-// and publishes its start state and V_new; the out waves write the output of
-// chunk c-1 and stage chunk c+1.
+// and publishes its start state and V_new; the other waves write the output
+// of chunk c-1 and stage chunk c+1.
 #pragma once
 
 #include <type_traits>
@@ -50,22 +50,25 @@ struct Chain1Shape {
     // Waves (they go to the four SIMDs of a CU in turn):
     //   C = 64: 0 the chain; 4 idle (it only takes part in the barriers, so
     //           the chain has its SIMD to itself); 1, 2, 3, 5 the output of
-    //           tiles 3, 2, 1, 0 and the staging of T, V and the gates; 6, 7
-    //           the staging of W and K^T.
-    //   C = 32: 0 the chain; 1, 2 the output of tiles 1, 0 and all staging.
+    //           tiles 3, 2, 1, 0; 6, 7 the staging.
+    //   C = 32: 0 the chain; 1, 2 the output of tiles 1, 0 and the staging.
     static constexpr int IDLE = NTT == 4 ? 4 : -1;
     static constexpr int NW = NTT == 4 ? 8 : 1 + NTT;
     static constexpr int NTHR = 64 * NW;
-    static constexpr int NLA = 128;           // threads staging W and K^T
-    static constexpr int NLB = 64 * NTT;      // threads staging T and V
+    static constexpr int NLW = 2;             // staging ("loader") waves
     static constexpr int NKS = KD / 32;       // 32-wide steps over the key dim
     static constexpr int NST = KD / 16;       // state row tiles
     static constexpr int NCS = C / 32;        // 32-wide steps over the tokens
-    static constexpr int SWM = C / 8 - 1;     // K^T chunk swizzle mask
-    static constexpr int LDK = KD + 8;        // Ws  [C][KD]   bf16, W (permuted k order)
-    static constexpr int LDKT = C + 8;        // KsT [KD][C]   bf16, permuted, 16-byte chunks swizzled
-    static constexpr int LDT = C + 8;         // Tb  [C][C]    bf16
-    static constexpr int LDV = BV + 8;        // Vs  [C][BV]   bf16, the V slice (row-major)
+    // Staging buffers are filled by LDS-direct loads (global_load_lds_dwordx4:
+    // lane i of a wave writes 16 bytes at base + 16 i), so their rows are
+    // unpadded; the 16-byte chunk j of row r sits at chunk j ^ (r & mask) to
+    // spread the state pass's row-wise reads over the banks.
+    static constexpr int WSW = (KD / 8 < 16 ? KD / 8 : 16) - 1;   // Ws swizzle mask
+    static constexpr int TSW = C / 8 - 1;     // KsT, Tb swizzle mask
+    static constexpr int LDK = KD;            // Ws  [C][KD]   bf16, W (permuted k order)
+    static constexpr int LDKT = C;            // KsT [KD][C]   bf16, K^T (permuted k order)
+    static constexpr int LDT = C;             // Tb  [C][C]    bf16, T diag(beta)
+    static constexpr int LDV = BV;            // Vs  [C][BV]   bf16, the V slice (row-major)
     static constexpr int LDSH = KD + 8;       // St  [2][BV][KD] bf16 hi, lo of S_start transposed
     static constexpr int LDVF = C + 4;        // Vn  [BV][C]   fp32, V_new transposed
     // gate table: e^G [C], e^{G_L-G} [C], e^{G_L}
@@ -78,18 +81,27 @@ struct Chain1Shape {
     static constexpr int SZ_GATE = al(NGATE * 4);
     static constexpr int SZ_ST = al(2 * BV * LDSH * 2);
     static constexpr int SZ_VN = al(BV * LDVF * 4);
-    // every buffer is double: index p = chunk & 1
+    // staging buffers are triple (index chunk % 3: staged two iterations
+    // ahead), St and Vn double (index chunk & 1)
     static constexpr int OFF_KS = 0;
-    static constexpr int OFF_KST = OFF_KS + 2 * SZ_KS;
-    static constexpr int OFF_TB = OFF_KST + 2 * SZ_KST;
-    static constexpr int OFF_BV = OFF_TB + 2 * SZ_TB;
-    static constexpr int OFF_GATE = OFF_BV + 2 * SZ_BV;
-    static constexpr int OFF_ST = OFF_GATE + 2 * SZ_GATE;
+    static constexpr int OFF_KST = OFF_KS + 3 * SZ_KS;
+    static constexpr int OFF_TB = OFF_KST + 3 * SZ_KST;
+    static constexpr int OFF_BV = OFF_TB + 3 * SZ_TB;
+    static constexpr int OFF_GATE = OFF_BV + 3 * SZ_BV;
+    static constexpr int OFF_ST = OFF_GATE + 3 * SZ_GATE;
     static constexpr int OFF_VN = OFF_ST + 2 * SZ_ST;
     static constexpr int BYTES = OFF_VN + 2 * SZ_VN;
     static_assert(C % 32 == 0 && C <= 64 && KD % 32 == 0, "32-wide MFMA steps");
     static_assert(BYTES <= 160 * 1024, "LDS budget of one workgroup exceeded");
+    static_assert(SZ_KS % 1024 == 0 && SZ_KST % 1024 == 0 && SZ_TB % 1024 == 0 && SZ_BV % 1024 == 0,
+                  "staging buffers are whole 1 KiB wave loads");
 };
+
+// LDS-direct 16-byte load: lane i writes at lds_base + 16 i (lds_base uniform).
+__device__ __forceinline__ void dma16(const void *src, void *lds_base) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 16, 0, 0);
+}
 
 // bf16 fragment of two accumulator tiles, in the permuted order (hi only).
 __device__ __forceinline__ bf16x8 frag_hi(const floatx4 &t0, const floatx4 &t1) {
@@ -127,7 +139,7 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
     using S = Chain1Shape<KD, C>;
     constexpr int BV = S::BV, NTT = S::NTT, NKS = S::NKS, NST = S::NST, NCS = S::NCS;
     constexpr int LDK = S::LDK, LDKT = S::LDKT, LDT = S::LDT, LDV = S::LDV, LDSH = S::LDSH, LDVF = S::LDVF;
-    constexpr int SWM = S::SWM;
+    constexpr int WSW = S::WSW, TSW = S::TSW;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::BYTES];
 
@@ -196,10 +208,10 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
             }
         }
         __syncthreads();
-        for (int c = 0; c < NT; ++c) {
-            const int p = c & 1;
-            const u16 *ws = Ks(p), *kt = KsT(p), *tb = Tb(p), *bv = BVs(p);
-            const float *gp = gate(p);
+        for (int c = 0, sq = 0; c < NT; ++c, sq = sq == 2 ? 0 : sq + 1) {
+            const int p = c & 1;                 // St, Vn; staging buffers: sq = c % 3
+            const u16 *ws = Ks(sq), *kt = KsT(sq), *tb = Tb(sq), *bv = BVs(sq);
+            const float *gp = gate(sq);
             // All LDS operands of W S and U first (nothing here depends on the
             // state), so their latency overlaps; the MFMAs below run over the
             // token tiles innermost, so consecutive MFMAs are independent.
@@ -207,7 +219,8 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
 #pragma unroll
             for (int m = 0; m < NKS; ++m)
 #pragma unroll
-                for (int tt = 0; tt < NTT; ++tt) wf[tt][m] = ld8(ws + (tt * 16 + c16) * LDK + m * 32 + 8 * g);
+                for (int tt = 0; tt < NTT; ++tt)
+                    wf[tt][m] = ld8(ws + (tt * 16 + c16) * LDK + ((((4 * m + g) ^ ((tt * 16 + c16) & WSW))) << 3));
 #pragma unroll
             for (int m = 0; m < NCS; ++m) {
                 // V rows 32m + 8g + {0..7}, column j = lane%16: transposed reads
@@ -217,7 +230,8 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
                 vf[m] = __builtin_bit_cast(bf16x8, uint4{v0.x, v0.y, v1.x, v1.y});
 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt)
-                    if (2 * m <= tt) tf[tt][m] = ld8(tb + (tt * 16 + c16) * LDT + m * 32 + 8 * g);
+                    if (2 * m <= tt)
+                        tf[tt][m] = ld8(tb + (tt * 16 + c16) * LDT + (((4 * m + g) ^ ((tt * 16 + c16) & TSW)) << 3));
             }
             bf16x8 sb[NKS];
 #pragma unroll
@@ -241,7 +255,7 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
             bf16x8 kf[NST][NCS];
 #pragma unroll
             for (int ti = 0; ti < NST; ++ti) {
-                const int xr = ((ti * 16 + c16) >> 3) & SWM;
+                const int xr = (ti * 16 + c16) & TSW;
 #pragma unroll
                 for (int m = 0; m < NCS; ++m) kf[ti][m] = ld8(kt + (ti * 16 + c16) * LDKT + (((4 * m + g) ^ xr) << 3));
             }
@@ -301,19 +315,16 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
     // outstanding loads is in order, and a load skipped on some path would
     // make the compiler wait for every load issued after the one it needs.
     //
-    // Roles: OW = token tile of the output (-1: none); group A (index LA,
-    // NLA threads): C*KD/8/NLA 16-byte vectors each of W and of K^T; group B
-    // (index LB, NLB threads): C*C/8/NLB 16-byte vectors of T diag(beta), and
-    // (the last 2C of them) the 16-byte pieces of the V slice; GATE: the gate
-    // table.
-    constexpr int NLA = S::NLA, NLB = S::NLB;
-    constexpr int NTV = C * C / 8;              // 16-byte vectors of T
-    constexpr int PT = NTV / NLB;
-    constexpr int NWV = C * KD / 8;             // 16-byte vectors of W (and of K^T)
-    constexpr int PW = NWV / NLA;
+    // Roles: OW = token tile of the output (-1: none); LI = staging index
+    // (-1: none).  Staging of chunk c+1 in iteration c: NDMA LDS-direct wave
+    // loads of 1 KiB (W, K^T, T diag(beta), the V slice, the gate table),
+    // load k on staging wave k % NLW, waited for before the barrier.
+    constexpr int NLW = S::NLW;
     constexpr int NLOW = NTT * (NTT + 1) / 2;
     constexpr int NGV = (2 * C + 4) / 4;        // 16-byte vectors of a gate table
-    static_assert(PT * NLB == NTV && PW * NLA == NWV && 2 * C <= NLB && NGV <= 64, "loader split");
+    constexpr int NDW = S::SZ_KS / 1024, NDK = S::SZ_KST / 1024, NDT = S::SZ_TB / 1024, NDV = S::SZ_BV / 1024;
+    constexpr int NDMA = NDW + NDK + NDT + NDV + 1;
+    static_assert(NGV <= 64 && S::SZ_GATE >= NGV * 16, "gate table: one partial wave load");
     const size_t tokq = (size_t)H * KD, tokv = (size_t)H * Dv;
     const u16 *ktg = reinterpret_cast<const u16 *>(args.ktmat) + (size_t)bh * NT * KD * C;
     const u16 *qg = reinterpret_cast<const u16 *>(args.q) + ((size_t)b * T * H + h) * KD;
@@ -322,71 +333,50 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
     const u16 *wg = reinterpret_cast<const u16 *>(args.wmat) + (size_t)bh * NT * C * KD;
     const float *gtg = reinterpret_cast<const float *>(args.gtab) + (size_t)bh * NT * (2 * C + 4);
 
-    auto out_wave = [&](auto owc, auto lac, auto lbc, auto gatec) {
-        constexpr int OW = decltype(owc)::value, LA = decltype(lac)::value, LB = decltype(lbc)::value;
-        constexpr bool TILE = OW >= 0, GA = LA >= 0, GB = LB >= 0, GATE = decltype(gatec)::value;
-        constexpr bool LOAD = GA || GB || GATE;
-        const int ia = (GA ? LA : 0) * 64 + l, ib = (GB ? LB : 0) * 64 + l;   // group thread indices
-        // the last 2C threads of group B (the lighter output tiles) stage V:
-        // token vi / 2, columns 8 (vi % 2) ..
-        const int vi = ib - (NLB - 2 * C), vtok = max(vi, 0) >> 1, vcol = 8 * (max(vi, 0) & 1);
-        // Rows past T are clamped to T-1 (and zeroed when committed); a chunk
-        // index past the end is clamped to the last chunk (its staging then
-        // lands in a buffer no one reads).  Two register sets: chunk c is
-        // loaded two iterations before it is committed.
-        struct Regs {
-            u32x4 rk[PW], rt[PT], rw[PW], rv, rg;
-        };
-        Regs ra, rb;
-        auto prefetch = [&](int c, Regs &r) {
+    auto out_wave = [&](auto owc, auto lic) {
+        constexpr int OW = decltype(owc)::value, LI = decltype(lic)::value;
+        constexpr bool TILE = OW >= 0, LOAD = LI >= 0;
+        // Stage chunk c (clamped to the last chunk; a past-the-end chunk lands in
+        // a buffer no one reads) into buffers c % 3.  Rows of the prep's
+        // outputs past T are zero; V rows past T are clamped to T-1 and only
+        // meet zero columns of T diag(beta).
+        auto stage = [&](int c) {
+            const int p = c % 3;
             c = min(c, NT - 1);
-            const int t0 = c * C;
-            if constexpr (GA) {
 #pragma unroll
-                for (int q = 0; q < PW; ++q)
-                    r.rw[q] = reinterpret_cast<const u32x4 *>(wg + (size_t)c * C * KD)[ia + NLA * q];
-#pragma unroll
-                for (int q = 0; q < PW; ++q)
-                    r.rk[q] = reinterpret_cast<const u32x4 *>(ktg + (size_t)c * KD * C)[ia + NLA * q];
+            for (int k = LI; k < NDMA; k += NLW) {
+                if (k < NDW) {                  // W: row r, stored chunk s holds chunk s ^ (r & WSW)
+                    const int pos = k * 64 + l, r = pos / (KD / 8), sc = pos % (KD / 8);
+                    dma16(wg + (size_t)c * C * KD + r * KD + ((sc ^ (r & WSW)) << 3),
+                          Ks(p) + k * 512);
+                } else if (k < NDW + NDK) {     // K^T: row i (key index)
+                    const int kk = k - NDW, pos = kk * 64 + l, r = pos / (C / 8), sc = pos % (C / 8);
+                    dma16(ktg + (size_t)c * KD * C + r * C + ((sc ^ (r & TSW)) << 3), KsT(p) + kk * 512);
+                } else if (k < NDW + NDK + NDT) {   // T diag(beta): row r (token)
+                    const int kk = k - NDW - NDK, pos = kk * 64 + l, r = pos / (C / 8), sc = pos % (C / 8);
+                    dma16(tg + (size_t)c * C * C + r * C + ((sc ^ (r & TSW)) << 3), Tb(p) + kk * 512);
+                } else if (k < NDW + NDK + NDT + NDV) {   // V slice: token pos / 2, half pos % 2
+                    const int kk = k - NDW - NDK - NDT, pos = kk * 64 + l;
+                    const int t = min(c * C + pos / 2, tlast);
+                    dma16(vg + (size_t)t * tokv + (pos & 1) * 8, BVs(p) + kk * 512);
+                } else {                        // gate table
+                    if (l < NGV) dma16(gtg + (size_t)c * (2 * C + 4) + l * 4, gate(p));
+                }
             }
-            if constexpr (GB) {
-#pragma unroll
-                for (int q = 0; q < PT; ++q)
-                    r.rt[q] = reinterpret_cast<const u32x4 *>(tg + (size_t)c * C * C)[ib + NLB * q];
-                const int t = min(t0 + vtok, tlast);
-                r.rv = *reinterpret_cast<const u32x4 *>(vg + (size_t)t * tokv + vcol);
-            }
-            if constexpr (GATE)
-                r.rg = reinterpret_cast<const u32x4 *>(gtg + (size_t)c * (2 * C + 4))[min(l, NGV - 1)];
         };
-        auto commit = [&](int c, const Regs &r) {
-            const int p = c & 1, t0 = c * C;
-            u16 *ws = Ks(p), *kt = KsT(p), *tb = Tb(p), *bv = BVs(p);
-            float *gp = gate(p);
-            if constexpr (GA) {
-#pragma unroll
-                for (int q = 0; q < PW; ++q) {  // W rows of tokens past T are zero
-                    const int idx = ia + NLA * q;
-                    *reinterpret_cast<u32x4 *>(ws + (idx / (KD / 8)) * LDK + (idx % (KD / 8)) * 8) = r.rw[q];
-                }
-#pragma unroll
-                for (int q = 0; q < PW; ++q) {  // K^T, already swizzled (zero for tokens past T)
-                    const int idx = ia + NLA * q;
-                    *reinterpret_cast<u32x4 *>(kt + (idx / (C / 8)) * LDKT + (idx % (C / 8)) * 8) = r.rk[q];
-                }
-            }
-            if constexpr (GB) {
-#pragma unroll
-                for (int q = 0; q < PT; ++q) {
-                    const int idx = ib + NLB * q;
-                    *reinterpret_cast<u32x4 *>(tb + (idx / (C / 8)) * LDT + (idx % (C / 8)) * 8) = r.rt[q];
-                }
-                if (vi >= 0)                    // V rows of tokens past T are zero
-                    *reinterpret_cast<u32x4 *>(bv + vtok * LDV + vcol) = t0 + vtok < T ? r.rv : u32x4{0u, 0u, 0u, 0u};
-            }
-            if constexpr (GATE) {               // the gate table
-                if (l < NGV) reinterpret_cast<u32x4 *>(gp)[l] = r.rg;
-            }
+        // Barrier of a staging wave: LDS operations done, at most the NMINE
+        // newest global loads (this iteration's staging) still outstanding, so
+        // every older one (the previous staging, this wave's output loads) has
+        // landed.  __syncthreads() would wait for all of them.
+        constexpr int NMINE = LOAD ? (NDMA - LI + NLW - 1) / NLW : 0;
+        static_assert(NMINE < 64, "6-bit vmcnt");
+        // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, lgkmcnt(0), expcnt at its maximum
+        constexpr int WAIT_IMM = (NMINE & 15) | ((NMINE >> 4) << 14) | 0x0070;
+        auto stage_barrier = [&]() {
+            asm volatile("" ::: "memory");      // keep memory operations on their side
+            __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
         };
 
         constexpr int TW = TILE ? OW : 0;
@@ -405,7 +395,7 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
             const uint4 *pc = pfg + (size_t)c * NLOW * 64;
 #pragma unroll
             for (int tj = 0; tj <= TW; ++tj) pf[tj] = __builtin_bit_cast(u32x4, pc[tj * 64]);
-            egt = gate(c & 1)[TW * 16 + c16];
+            egt = gate(c % 3)[TW * 16 + c16];
         };
         // O^T of chunk c: a1 = S_start^T Q^T, a2 = V_new^T P^T (buffers c & 1)
         auto compute_out = [&](int c) {
@@ -444,36 +434,32 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
         };
 
         // Iteration c (one barrier each): output of chunk c-1, operands of
-        // chunk c, commit of chunk c+1 (register set (c+1) % 2), prefetch of
-        // chunk c+3 into the same set.
+        // chunk c, staging of chunk c+2 (waited for one iteration later).
         if constexpr (LOAD) {
-            prefetch(0, ra);
-            prefetch(1, rb);
-            commit(0, ra);
-            prefetch(2, ra);
+            stage(0);
+            stage(1);
+            __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0)
         }
         __syncthreads();
         if constexpr (TILE) load_qp(0);
         if constexpr (LOAD) {
-            commit(1, rb);
-            prefetch(3, rb);
+            stage(2);
+            stage_barrier();
+        } else {
+            __syncthreads();
         }
-        __syncthreads();
-        auto iter = [&](int c, Regs &r) {
+        for (int c = 1; c < NT; ++c) {
             if constexpr (TILE) {
                 compute_out(c - 1);
                 load_qp(c);
+                store_out(c - 1);
             }
             if constexpr (LOAD) {
-                commit(c + 1, r);
-                prefetch(c + 3, r);
+                stage(c + 2);
+                stage_barrier();
+            } else {
+                __syncthreads();
             }
-            if constexpr (TILE) store_out(c - 1);
-            __syncthreads();
-        };
-        for (int c = 1; c < NT; c += 2) {
-            iter(c, ra);
-            if (c + 1 < NT) iter(c + 1, rb);
         }
         if constexpr (TILE) {
             compute_out(NT - 1);
@@ -487,22 +473,18 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
         return;
     }
     using std::integral_constant;
-    using std::false_type;
-    using std::true_type;
     using none = integral_constant<int, -1>;
     if constexpr (NTT == 4) {
-        if (w == 1) out_wave(integral_constant<int, 3>{}, none{}, integral_constant<int, 0>{}, false_type{});
-        if (w == 2) out_wave(integral_constant<int, 2>{}, none{}, integral_constant<int, 1>{}, false_type{});
-        if (w == 3) out_wave(integral_constant<int, 1>{}, none{}, integral_constant<int, 2>{}, true_type{});
-        if (w == 5) out_wave(integral_constant<int, 0>{}, none{}, integral_constant<int, 3>{}, false_type{});
-        if (w == 6) out_wave(none{}, integral_constant<int, 0>{}, none{}, false_type{});
-        if (w == 7) out_wave(none{}, integral_constant<int, 1>{}, none{}, false_type{});
+        if (w == 1) out_wave(integral_constant<int, 3>{}, none{});
+        if (w == 2) out_wave(integral_constant<int, 2>{}, none{});
+        if (w == 3) out_wave(integral_constant<int, 1>{}, none{});
+        if (w == 5) out_wave(integral_constant<int, 0>{}, none{});
+        if (w == 6) out_wave(none{}, integral_constant<int, 0>{});
+        if (w == 7) out_wave(none{}, integral_constant<int, 1>{});
     } else {
         static_assert(NTT == 2, "chunk of 32 or 64 tokens");
-        if (w == 1)
-            out_wave(integral_constant<int, 1>{}, integral_constant<int, 0>{}, integral_constant<int, 0>{}, true_type{});
-        if (w == 2)
-            out_wave(integral_constant<int, 0>{}, integral_constant<int, 1>{}, integral_constant<int, 1>{}, false_type{});
+        if (w == 1) out_wave(integral_constant<int, 1>{}, integral_constant<int, 0>{});
+        if (w == 2) out_wave(integral_constant<int, 0>{}, integral_constant<int, 1>{});
     }
 }
 

@@ -60,7 +60,7 @@ struct ChunkArgs {
     void *tmat;      // work space: T per chunk, [B*H][NT][NR][NR]
     void *pfrag;     // work space: intra-chunk P tiles as MFMA fragments (PFRAG shapes)
     void *wmat;      // work space: W = T diag(beta e^G) K per chunk, bf16 [C][KD] (PFRAG shapes)
-    void *ktmat;     // work space: K^T per chunk, bf16 [KD][C], 16-byte chunks swizzled (PFRAG shapes)
+    void *ktmat;     // work space: K^T per chunk, bf16 [KD][C], permuted k order (PFRAG shapes)
     void *gtab;      // work space: e^{G_t} [C], e^{G_L - G_t} [C], e^{G_L}, 0, 0, 0 per chunk, fp32 (PFRAG shapes)
     int B, T, H, Dv;
     int out_bf16;

@@ -11,7 +11,7 @@
 //           block rows T_ij = -T_ii sum_m A_im T_mj; stored as T diag(beta)
 //           (so the state pass forms U = T diag(beta) V from exact V) -> bf16
 //   W       T diag(beta e^G) K, rows in the permuted k order         -> bf16
-//   K^T     rows of C tokens, permuted k order, 16-byte chunks swizzled
+//   K^T     rows of C tokens, permuted k order
 //   P       [s<=t] (q_t . k_s) e^{G_t - G_s} of the lower 16x16 tiles, as
 //           hi/lo bf16 MFMA fragments (lane l: row t = 16 ti + l%16,
 //           columns s = 16 tj + 4 (l/16) + e)
@@ -251,8 +251,7 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
                 const uint2 lo = __builtin_bit_cast(uint2, ld_tr16(kp));
                 const uint2 hi = __builtin_bit_cast(uint2, ld_tr16(kp + 16 * LDK));
                 const int i = it * 16 + c16;
-                const int js = (4 * m + g) ^ ((i >> 3) & (C / 8 - 1));
-                *reinterpret_cast<uint4 *>(kout + i * C + js * 8) = uint4{lo.x, lo.y, hi.x, hi.y};
+                *reinterpret_cast<uint4 *>(kout + i * C + (4 * m + g) * 8) = uint4{lo.x, lo.y, hi.x, hi.y};
             }
         }
         // registers are free: start loading the next chunk
