@@ -1,40 +1,41 @@
 // Sequential state pass + output of the chunkwise gated delta rule, for bf16
 // inputs with one step per token (msj19 "gated_deltaproduct" test.py with
 // r = 1: gated_chunk_delta_rule_fwd_kernel_h and
-// gated_chunk_linear_attn_fwd_kernel_o; T = (I + A)^-1 comes from
-// chunk_solve_kernel in the work space).
+// gated_chunk_linear_attn_fwd_kernel_o; T diag(beta), the P tiles and the
+// gate tables come from chunk_prep1_kernel in the work space).
 //
 // One workgroup per (batch, head, 16-column slice of the value dimension),
 // 1 + C/16 waves, split by role outside the chunk loop (each role keeps only
 // its own registers live):
 //
 //   wave 0 ("chain") owns the (KD x 16) fp32 state slice in MFMA
-//   accumulators and runs the dependent part of every chunk in registers,
-//   in the page's WY form (u - w h):
-//       V_new = U - W S,  U = (T diag(beta)) V,  W = T diag(beta e^G) K;
-//       S <- e^{G_L} S + K^T diag(e^{G_L - G}) V_new.
-//   W comes from the solve kernel; U does not depend on S, so its MFMAs
-//   overlap those of W S.
+//   accumulators and runs the dependent part of every chunk in registers.
+//   The WY form's u - w h (U = T diag(beta) V, W = T diag(beta e^G) K) is
+//   taken as one product with T diag(beta) on the left:
+//       V_new = T diag(beta) (V - e^G K S),
+//       S <- e^{G_L} S + K^T diag(e^{G_L - G}) V_new,
+//   so only K itself is staged (no W), and the residual V - e^G K S, not
+//   two large terms, meets the rounding of T diag(beta).
 //   An MFMA accumulator tile (lane l holds rows 4*(l/16)+e, column l%16) is
 //   fed back as the B operand of the next product by reading the k index of
 //   a 32-wide MFMA step in the order {4g..4g+3, 16+4g..16+4g+3} (g = l/16)
-//   instead of 8g..8g+7; the A operand rows (W, K^T) are stored in that
-//   permuted order by the solve kernel, so each lane reads them as one
-//   16-byte piece and the sum over k is unchanged.  It publishes V_new
-//   (fp32) and the chunk-start state (hi + lo bf16) to LDS for the output
-//   waves.
+//   instead of 8g..8g+7; T diag(beta) is stored with its columns in that
+//   permuted order, and K^T fragments are read transposed from the K rows
+//   (ds_read_b64_tr_b16) with the token rows and key columns each lane
+//   needs.  It publishes V_new (fp32) and the chunk-start state (hi + lo
+//   bf16) to LDS for the output waves.
 //
 //   waves 1..C/16 ("out"), one 16-token tile each: the output, transposed,
 //   O^T = S_start^T Q^T e^G + V_new^T P^T (P, the causal intra-chunk scores,
-//   comes from the solve kernel as ready MFMA fragments; the transposed
+//   comes from the prep kernel as ready MFMA fragments; the transposed
 //   accumulator gives each lane 4 consecutive values of one token, one
-//   16-byte store); staging waves copy the next chunk's W, K^T, T diag(beta)
-//   and gate table (as the prep kernel wrote them) and V slice straight into
-//   LDS with LDS-direct loads.
+//   16-byte store); staging waves copy a later chunk's K rows and V slice
+//   (from the inputs) and T diag(beta) and gate table (from the prep kernel)
+//   straight into LDS with LDS-direct loads.
 //
 // One workgroup barrier per chunk.  Iteration c: the chain processes chunk c
 // and publishes its start state and V_new; the other waves write the output
-// of chunk c-1 and stage chunk c+1.
+// of chunk c-1 and stage chunk c+2.
 #pragma once
 
 #include <type_traits>
@@ -61,21 +62,19 @@ struct Chain1Shape {
     static constexpr int NCS = C / 32;        // 32-wide steps over the tokens
     // Staging buffers are filled by LDS-direct loads (global_load_lds_dwordx4:
     // lane i of a wave writes 16 bytes at base + 16 i), so their rows are
-    // unpadded; the 16-byte chunk j of row r sits at chunk j ^ (r & mask) to
-    // spread the state pass's row-wise reads over the banks.
-    static constexpr int WSW = (KD / 8 < 16 ? KD / 8 : 16) - 1;   // Ws swizzle mask
-    static constexpr int TSW = C / 8 - 1;     // KsT, Tb swizzle mask
-    static constexpr int LDK = KD;            // Ws  [C][KD]   bf16, W (permuted k order)
-    static constexpr int LDKT = C;            // KsT [KD][C]   bf16, K^T (permuted k order)
-    static constexpr int LDT = C;             // Tb  [C][C]    bf16, T diag(beta)
+    // unpadded; the 16-byte piece j of row r sits at piece j ^ swizzle(r) to
+    // spread the state pass's reads over the banks.
+    static constexpr int NKC = KD / 8;        // 16-byte pieces of a K row
+    static constexpr int TSW = C / 8 - 1;     // Tb swizzle mask
+    static constexpr int LDK = KD;            // Ks  [C][KD]   bf16, K rows (natural order)
+    static constexpr int LDT = C;             // Tb  [C][C]    bf16, T diag(beta) (permuted k order)
     static constexpr int LDV = BV;            // Vs  [C][BV]   bf16, the V slice (row-major)
     static constexpr int LDSH = KD + 8;       // St  [2][BV][KD] bf16 hi, lo of S_start transposed
     static constexpr int LDVF = C + 4;        // Vn  [BV][C]   fp32, V_new transposed
-    // gate table: e^G [C], e^{G_L-G} [C], e^{G_L}
-    static constexpr int NGATE = 2 * C + 4;
+    // gate table: e^G [C], e^{G_L-G} [C], e^{G_L} (+3), beta [C]
+    static constexpr int NGATE = gate_table_len<C>();
     static constexpr int al(int x) { return (x + 15) & ~15; }
     static constexpr int SZ_KS = al(C * LDK * 2);
-    static constexpr int SZ_KST = al(KD * LDKT * 2);
     static constexpr int SZ_TB = al(C * LDT * 2);
     static constexpr int SZ_BV = al(C * LDV * 2);
     static constexpr int SZ_GATE = al(NGATE * 4);
@@ -84,8 +83,7 @@ struct Chain1Shape {
     // staging buffers are triple (index chunk % 3: staged two iterations
     // ahead), St and Vn double (index chunk & 1)
     static constexpr int OFF_KS = 0;
-    static constexpr int OFF_KST = OFF_KS + 3 * SZ_KS;
-    static constexpr int OFF_TB = OFF_KST + 3 * SZ_KST;
+    static constexpr int OFF_TB = OFF_KS + 3 * SZ_KS;
     static constexpr int OFF_BV = OFF_TB + 3 * SZ_TB;
     static constexpr int OFF_GATE = OFF_BV + 3 * SZ_BV;
     static constexpr int OFF_ST = OFF_GATE + 3 * SZ_GATE;
@@ -93,9 +91,19 @@ struct Chain1Shape {
     static constexpr int BYTES = OFF_VN + 2 * SZ_VN;
     static_assert(C % 32 == 0 && C <= 64 && KD % 32 == 0, "32-wide MFMA steps");
     static_assert(BYTES <= 160 * 1024, "LDS budget of one workgroup exceeded");
-    static_assert(SZ_KS % 1024 == 0 && SZ_KST % 1024 == 0 && SZ_TB % 1024 == 0 && SZ_BV % 1024 == 0,
+    static_assert(SZ_KS % 1024 == 0 && SZ_TB % 1024 == 0 && SZ_BV % 1024 == 0,
                   "staging buffers are whole 1 KiB wave loads");
 };
+
+// Swizzle of K row r (token): the piece index is XORed with a permutation of
+// r's low four bits that keeps both read patterns free of bank conflicts (16
+// rows at one piece; 4 rows x 4 pieces for the transposed reads).
+template <int NKC>
+__device__ __forceinline__ int kswz(int r) {
+    if constexpr (NKC >= 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else if constexpr (NKC == 8) return ((r & 3) << 1) | ((r >> 2) & 1);
+    else return r & 3;
+}
 
 // LDS-direct 16-byte load: lane i writes at lds_base + 16 i (lds_base uniform).
 __device__ __forceinline__ void dma16(const void *src, void *lds_base) {
@@ -137,9 +145,9 @@ __device__ __forceinline__ floatx4 mfma16(shortx4 a, shortx4 b, floatx4 c) {
 template <int KD, int C>
 __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain1_kernel(ChunkArgs args) {
     using S = Chain1Shape<KD, C>;
-    constexpr int BV = S::BV, NTT = S::NTT, NKS = S::NKS, NST = S::NST, NCS = S::NCS;
-    constexpr int LDK = S::LDK, LDKT = S::LDKT, LDT = S::LDT, LDV = S::LDV, LDSH = S::LDSH, LDVF = S::LDVF;
-    constexpr int WSW = S::WSW, TSW = S::TSW;
+    constexpr int BV = S::BV, NTT = S::NTT, NKS = S::NKS, NST = S::NST, NCS = S::NCS, NKC = S::NKC;
+    constexpr int LDK = S::LDK, LDT = S::LDT, LDV = S::LDV, LDSH = S::LDSH, LDVF = S::LDVF;
+    constexpr int TSW = S::TSW;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::BYTES];
 
@@ -162,7 +170,6 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
     const int tlast = T > 0 ? T - 1 : 0;
 
     auto Ks = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_KS + p * S::SZ_KS); };
-    auto KsT = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_KST + p * S::SZ_KST); };
     auto Tb = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_TB + p * S::SZ_TB); };
     auto BVs = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_BV + p * S::SZ_BV); };
     auto gate = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_GATE + p * S::SZ_GATE); };
@@ -173,11 +180,13 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
         // =================================================================
         // chain wave
         // =================================================================
+        // State row tile ti = 2 mk + h, accumulator row 4 g + e holds key
+        // feature 32 mk + 8 g + 4 h + e: the bf16 fragment of tiles 2 mk and
+        // 2 mk + 1 is then features 32 mk + 8 g + {0..7} in natural order
+        // (the B operand of K S), and K^T fragments pick their rows to match.
         floatx4 Sreg[NST];
-        // S_start as hi + lo bf16, transposed to [j][i], for the output
-        // waves; hi[m] is the W S operand (the state rounded once).  A
-        // fragment holds rows {4g..4g+3} and {16+4g..16+4g+3} of 32-row
-        // block m: two 8-byte pieces each.
+        auto feat = [&](int ti, int e) { return (ti >> 1) * 32 + 8 * g + 4 * (ti & 1) + e; };
+        // S_start as hi + lo bf16, transposed to [j][i], for the output waves
         auto publish_state = [&](int p, const bf16x8 (&hi)[NKS]) {
             u16 *sh = St(p) + c16 * LDSH, *sl = sh + BV * LDSH;
 #pragma unroll
@@ -192,10 +201,8 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
                                 Sreg[2 * m + 1][1] - __builtin_bit_cast(float, h.z & 0xffff0000u));
                 o.w = cvt2_bf16(Sreg[2 * m + 1][2] - __builtin_bit_cast(float, h.w << 16),
                                 Sreg[2 * m + 1][3] - __builtin_bit_cast(float, h.w & 0xffff0000u));
-                *reinterpret_cast<uint2 *>(sh + m * 32 + 4 * g) = uint2{h.x, h.y};
-                *reinterpret_cast<uint2 *>(sh + m * 32 + 16 + 4 * g) = uint2{h.z, h.w};
-                *reinterpret_cast<uint2 *>(sl + m * 32 + 4 * g) = uint2{o.x, o.y};
-                *reinterpret_cast<uint2 *>(sl + m * 32 + 16 + 4 * g) = uint2{o.z, o.w};
+                *reinterpret_cast<uint4 *>(sh + m * 32 + 8 * g) = h;
+                *reinterpret_cast<uint4 *>(sl + m * 32 + 8 * g) = o;
             }
         };
 #pragma unroll
@@ -204,76 +211,104 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
             if (args.h0) {
                 const float *hp = args.h0 + ((size_t)bh * KD) * Dv + v0 + c16;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Sreg[ti][e] = hp[(size_t)(ti * 16 + 4 * g + e) * Dv];
+                for (int e = 0; e < 4; ++e) Sreg[ti][e] = hp[(size_t)feat(ti, e) * Dv];
             }
         }
         __syncthreads();
         for (int c = 0, sq = 0; c < NT; ++c, sq = sq == 2 ? 0 : sq + 1) {
             const int p = c & 1;                 // St, Vn; staging buffers: sq = c % 3
-            const u16 *ws = Ks(sq), *kt = KsT(sq), *tb = Tb(sq), *bv = BVs(sq);
+            const u16 *ks = Ks(sq), *tb = Tb(sq), *bv = BVs(sq);
             const float *gp = gate(sq);
-            // All LDS operands of W S and U first (nothing here depends on the
-            // state), so their latency overlaps; the MFMAs below run over the
-            // token tiles innermost, so consecutive MFMAs are independent.
-            bf16x8 wf[NTT][NKS], tf[NTT][NCS], vf[NCS];
+            // LDS operands of K S first (nothing here depends on the state), so
+            // their latency overlaps; the MFMAs run over the token tiles
+            // innermost, so consecutive MFMAs are independent.
+            bf16x8 kf[NTT][NKS], tf[NTT][NCS];
 #pragma unroll
             for (int m = 0; m < NKS; ++m)
 #pragma unroll
-                for (int tt = 0; tt < NTT; ++tt)
-                    wf[tt][m] = ld8(ws + (tt * 16 + c16) * LDK + ((((4 * m + g) ^ ((tt * 16 + c16) & WSW))) << 3));
+                for (int tt = 0; tt < NTT; ++tt) {
+                    const int r = tt * 16 + c16;
+                    kf[tt][m] = ld8(ks + r * LDK + (((4 * m + g) ^ kswz<NKC>(r)) << 3));
+                }
+            shortx4 vv[NTT];                     // V rows tt*16 + 4g + e, column c16
 #pragma unroll
-            for (int m = 0; m < NCS; ++m) {
-                // V rows 32m + 8g + {0..7}, column j = lane%16: transposed reads
-                const u16 *vp = bv + (m * 32 + 8 * g + (c16 >> 2)) * LDV + 4 * (c16 & 3);
-                const uint2 v0 = __builtin_bit_cast(uint2, ld_tr16(vp));
-                const uint2 v1 = __builtin_bit_cast(uint2, ld_tr16(vp + 4 * LDV));
-                vf[m] = __builtin_bit_cast(bf16x8, uint4{v0.x, v0.y, v1.x, v1.y});
+            for (int tt = 0; tt < NTT; ++tt) vv[tt] = ld_tr16(bv + (tt * 16 + 4 * g + (c16 >> 2)) * LDV + 4 * (c16 & 3));
+#pragma unroll
+            for (int m = 0; m < NCS; ++m)
 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt)
                     if (2 * m <= tt)
                         tf[tt][m] = ld8(tb + (tt * 16 + c16) * LDT + (((4 * m + g) ^ ((tt * 16 + c16) & TSW)) << 3));
-            }
             bf16x8 sb[NKS];
 #pragma unroll
             for (int m = 0; m < NKS; ++m) sb[m] = frag_hi(Sreg[2 * m], Sreg[2 * m + 1]);
             publish_state(p, sb);                // S_start of chunk c
-            // X = W S and U = (T diag(beta)) V (T is block lower triangular)
-            floatx4 x[NTT], u[NTT];
+            // Y = K S
+            floatx4 y[NTT];
 #pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) x[tt] = u[tt] = zero4();
+            for (int tt = 0; tt < NTT; ++tt) y[tt] = zero4();
 #pragma unroll
             for (int m = 0; m < NKS; ++m)
 #pragma unroll
-                for (int tt = 0; tt < NTT; ++tt) x[tt] = mfma32(wf[tt][m], sb[m], x[tt]);
-#pragma unroll
-            for (int m = 0; m < NCS; ++m) {
-#pragma unroll
-                for (int tt = 0; tt < NTT; ++tt)
-                    if (2 * m <= tt) u[tt] = mfma32(tf[tt][m], vf[m], u[tt]);
-            }
-            // operands of the state update, read while the MFMAs run
-            bf16x8 kf[NST][NCS];
+                for (int tt = 0; tt < NTT; ++tt) y[tt] = mfma32(kf[tt][m], sb[m], y[tt]);
+            // K^T fragments of the state update, read while the MFMAs run: lane
+            // (g, j) of tile ti gets feature feat(ti, j%4 .. ) from the pointers
+            // of lanes 4a + b (token row 32m + 4g + a, piece 4 mk + b, half h)
+            bf16x8 ka[NST][NCS];
 #pragma unroll
             for (int ti = 0; ti < NST; ++ti) {
-                const int xr = (ti * 16 + c16) & TSW;
+                const int pc = 4 * (ti >> 1) + (c16 & 3), hf = 4 * (ti & 1);
 #pragma unroll
-                for (int m = 0; m < NCS; ++m) kf[ti][m] = ld8(kt + (ti * 16 + c16) * LDKT + (((4 * m + g) ^ xr) << 3));
+                for (int m = 0; m < NCS; ++m) {
+                    const int r0 = m * 32 + 4 * g + (c16 >> 2), r1 = r0 + 16;
+                    const uint2 lo = __builtin_bit_cast(uint2, ld_tr16(ks + r0 * LDK + ((pc ^ kswz<NKC>(r0)) << 3) + hf));
+                    const uint2 hi = __builtin_bit_cast(uint2, ld_tr16(ks + r1 * LDK + ((pc ^ kswz<NKC>(r1)) << 3) + hf));
+                    ka[ti][m] = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
+                }
             }
-            floatx4 el[NTT];
+            floatx4 eg[NTT], el[NTT], bt[NTT];
 #pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) el[tt] = *reinterpret_cast<const floatx4 *>(gp + C + tt * 16 + 4 * g);
+            for (int tt = 0; tt < NTT; ++tt) {
+                eg[tt] = *reinterpret_cast<const floatx4 *>(gp + tt * 16 + 4 * g);
+                el[tt] = *reinterpret_cast<const floatx4 *>(gp + C + tt * 16 + 4 * g);
+                bt[tt] = *reinterpret_cast<const floatx4 *>(gp + 2 * C + 4 + tt * 16 + 4 * g);
+            }
             const float gL = gp[2 * C];
-            // V_new = U - X (published fp32 [j][s]); V~ = e^{G_L - G} V_new
+            // R = V - e^G Y; V_new = (T diag(beta)) R: its diagonal, beta, in fp32,
+            // the rest (block lower triangular) by MFMA on R as hi + lo
+            floatx4 rr[NTT];
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) {
+                const uint2 v2 = __builtin_bit_cast(uint2, vv[tt]);
+                const float vx[4] = {__builtin_bit_cast(float, v2.x << 16), __builtin_bit_cast(float, v2.x & 0xffff0000u),
+                                     __builtin_bit_cast(float, v2.y << 16), __builtin_bit_cast(float, v2.y & 0xffff0000u)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rr[tt][e] = vx[e] - eg[tt][e] * y[tt][e];
+            }
+            bf16x8 rh[NCS], rl[NCS];
+#pragma unroll
+            for (int m = 0; m < NCS; ++m) frag_split(rr[2 * m], rr[2 * m + 1], rh[m], rl[m]);
+            floatx4 vn[NTT];
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vn[tt][e] = bt[tt][e] * rr[tt][e];
+#pragma unroll
+            for (int m = 0; m < NCS; ++m)
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt)
+                    if (2 * m <= tt) {
+                        vn[tt] = mfma32(tf[tt][m], rh[m], vn[tt]);
+                        vn[tt] = mfma32(tf[tt][m], rl[m], vn[tt]);
+                    }
+            // V_new published fp32 [j][s]; V~ = e^{G_L - G} V_new
             float *vnp = Vn(p);
             floatx4 vt4[NTT];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
-                floatx4 vn;
+                *reinterpret_cast<floatx4 *>(vnp + c16 * LDVF + tt * 16 + 4 * g) = vn[tt];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) vn[e] = u[tt][e] - x[tt][e];
-                *reinterpret_cast<floatx4 *>(vnp + c16 * LDVF + tt * 16 + 4 * g) = vn;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vt4[tt][e] = el[tt][e] * vn[e];
+                for (int e = 0; e < 4; ++e) vt4[tt][e] = el[tt][e] * vn[tt][e];
             }
             bf16x8 vh[NCS], vl[NCS];
 #pragma unroll
@@ -285,9 +320,9 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
 #pragma unroll
             for (int m = 0; m < NCS; ++m) {
 #pragma unroll
-                for (int ti = 0; ti < NST; ++ti) ds[ti] = mfma32(kf[ti][m], vh[m], ds[ti]);
+                for (int ti = 0; ti < NST; ++ti) ds[ti] = mfma32(ka[ti][m], vh[m], ds[ti]);
 #pragma unroll
-                for (int ti = 0; ti < NST; ++ti) ds[ti] = mfma32(kf[ti][m], vl[m], ds[ti]);
+                for (int ti = 0; ti < NST; ++ti) ds[ti] = mfma32(ka[ti][m], vl[m], ds[ti]);
             }
 #pragma unroll
             for (int ti = 0; ti < NST; ++ti)
@@ -301,7 +336,7 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
             for (int ti = 0; ti < NST; ++ti) {
                 float *hp = args.hT + ((size_t)bh * KD) * Dv + v0 + c16;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) hp[(size_t)(ti * 16 + 4 * g + e) * Dv] = Sreg[ti][e];
+                for (int e = 0; e < 4; ++e) hp[(size_t)feat(ti, e) * Dv] = Sreg[ti][e];
             }
         }
         return;
@@ -316,51 +351,47 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
     // make the compiler wait for every load issued after the one it needs.
     //
     // Roles: OW = token tile of the output (-1: none); LI = staging index
-    // (-1: none).  Staging of chunk c+1 in iteration c: NDMA LDS-direct wave
-    // loads of 1 KiB (W, K^T, T diag(beta), the V slice, the gate table),
+    // (-1: none).  Staging of chunk c+2 in iteration c: NDMA LDS-direct wave
+    // loads of 1 KiB (K, T diag(beta), the V slice, the gate table),
     // load k on staging wave k % NLW, waited for before the barrier.
     constexpr int NLW = S::NLW;
     constexpr int NLOW = NTT * (NTT + 1) / 2;
-    constexpr int NGV = (2 * C + 4) / 4;        // 16-byte vectors of a gate table
-    constexpr int NDW = S::SZ_KS / 1024, NDK = S::SZ_KST / 1024, NDT = S::SZ_TB / 1024, NDV = S::SZ_BV / 1024;
-    constexpr int NDMA = NDW + NDK + NDT + NDV + 1;
+    constexpr int NGV = S::NGATE / 4;           // 16-byte vectors of a gate table
+    constexpr int NDK = S::SZ_KS / 1024, NDT = S::SZ_TB / 1024, NDV = S::SZ_BV / 1024;
+    constexpr int NDMA = NDK + NDT + NDV + 1;
     static_assert(NGV <= 64 && S::SZ_GATE >= NGV * 16, "gate table: one partial wave load");
     const size_t tokq = (size_t)H * KD, tokv = (size_t)H * Dv;
-    const u16 *ktg = reinterpret_cast<const u16 *>(args.ktmat) + (size_t)bh * NT * KD * C;
+    const u16 *kg = reinterpret_cast<const u16 *>(args.k) + ((size_t)b * T * H + h) * KD;
     const u16 *qg = reinterpret_cast<const u16 *>(args.q) + ((size_t)b * T * H + h) * KD;
     const u16 *vg = reinterpret_cast<const u16 *>(args.v) + ((size_t)b * T * H + h) * Dv + v0;
     const u16 *tg = reinterpret_cast<const u16 *>(args.tmat) + (size_t)bh * NT * C * C;
-    const u16 *wg = reinterpret_cast<const u16 *>(args.wmat) + (size_t)bh * NT * C * KD;
-    const float *gtg = reinterpret_cast<const float *>(args.gtab) + (size_t)bh * NT * (2 * C + 4);
+    const float *gtg = reinterpret_cast<const float *>(args.gtab) + (size_t)bh * NT * S::NGATE;
 
     auto out_wave = [&](auto owc, auto lic) {
         constexpr int OW = decltype(owc)::value, LI = decltype(lic)::value;
         constexpr bool TILE = OW >= 0, LOAD = LI >= 0;
         // Stage chunk c (clamped to the last chunk; a past-the-end chunk lands in
         // a buffer no one reads) into buffers c % 3.  Rows of the prep's
-        // outputs past T are zero; V rows past T are clamped to T-1 and only
-        // meet zero columns of T diag(beta).
+        // outputs past T are zero; K and V rows past T are clamped to T-1:
+        // they only meet zero columns of T diag(beta), and V_new is zero there.
         auto stage = [&](int c) {
             const int p = c % 3;
             c = min(c, NT - 1);
 #pragma unroll
             for (int k = LI; k < NDMA; k += NLW) {
-                if (k < NDW) {                  // W: row r, stored chunk s holds chunk s ^ (r & WSW)
-                    const int pos = k * 64 + l, r = pos / (KD / 8), sc = pos % (KD / 8);
-                    dma16(wg + (size_t)c * C * KD + r * KD + ((sc ^ (r & WSW)) << 3),
-                          Ks(p) + k * 512);
-                } else if (k < NDW + NDK) {     // K^T: row i (key index)
-                    const int kk = k - NDW, pos = kk * 64 + l, r = pos / (C / 8), sc = pos % (C / 8);
-                    dma16(ktg + (size_t)c * KD * C + r * C + ((sc ^ (r & TSW)) << 3), KsT(p) + kk * 512);
-                } else if (k < NDW + NDK + NDT) {   // T diag(beta): row r (token)
-                    const int kk = k - NDW - NDK, pos = kk * 64 + l, r = pos / (C / 8), sc = pos % (C / 8);
+                if (k < NDK) {                  // K: row r (token), stored piece j holds piece j ^ kswz(r)
+                    const int pos = k * 64 + l, r = pos / NKC, sc = pos % NKC;
+                    const int t = min(c * C + r, tlast);
+                    dma16(kg + (size_t)t * tokq + ((sc ^ kswz<NKC>(r)) << 3), Ks(p) + k * 512);
+                } else if (k < NDK + NDT) {     // T diag(beta): row r (token)
+                    const int kk = k - NDK, pos = kk * 64 + l, r = pos / (C / 8), sc = pos % (C / 8);
                     dma16(tg + (size_t)c * C * C + r * C + ((sc ^ (r & TSW)) << 3), Tb(p) + kk * 512);
-                } else if (k < NDW + NDK + NDT + NDV) {   // V slice: token pos / 2, half pos % 2
-                    const int kk = k - NDW - NDK - NDT, pos = kk * 64 + l;
+                } else if (k < NDK + NDT + NDV) {   // V slice: token pos / 2, half pos % 2
+                    const int kk = k - NDK - NDT, pos = kk * 64 + l;
                     const int t = min(c * C + pos / 2, tlast);
                     dma16(vg + (size_t)t * tokv + (pos & 1) * 8, BVs(p) + kk * 512);
                 } else {                        // gate table
-                    if (l < NGV) dma16(gtg + (size_t)c * (2 * C + 4) + l * 4, gate(p));
+                    if (l < NGV) dma16(gtg + (size_t)c * S::NGATE + l * 4, gate(p));
                 }
             }
         };

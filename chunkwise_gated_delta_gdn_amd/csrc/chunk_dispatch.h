@@ -33,13 +33,11 @@ inline int num_cus() {
 template <bool F32IN, int KD, int C, int R>
 hipError_t launch_chunk_fwd(const ChunkArgs &args, hipStream_t stream) {
     ChunkArgs a = args;
-    a.pfrag = a.wmat = a.ktmat = a.gtab = nullptr;
+    a.pfrag = a.gtab = nullptr;
     if (use_chain1<F32IN, KD, C, R>()) {
         char *ws = static_cast<char *>(a.tmat) + chunk_tmat_bytes<F32IN, KD, C, R>(a.B, a.T, a.H);
         a.pfrag = ws;
-        a.wmat = ws + chunk_pfrag_bytes<F32IN, KD, C, R>(a.B, a.T, a.H);
-        a.ktmat = static_cast<char *>(a.wmat) + (size_t)a.B * a.H * ((a.T + C - 1) / C) * C * KD * 2;
-        a.gtab = static_cast<char *>(a.ktmat) + (size_t)a.B * a.H * ((a.T + C - 1) / C) * C * KD * 2;
+        a.gtab = ws + chunk_pfrag_bytes<F32IN, KD, C, R>(a.B, a.T, a.H);
     }
     const int NT = (a.T + C - 1) / C;
     const int nbh = a.B * a.H;

@@ -59,8 +59,6 @@ struct ChunkArgs {
     void *o;
     void *tmat;      // work space: T per chunk, [B*H][NT][NR][NR]
     void *pfrag;     // work space: intra-chunk P tiles as MFMA fragments (PFRAG shapes)
-    void *wmat;      // work space: W = T diag(beta e^G) K per chunk, bf16 [C][KD] (PFRAG shapes)
-    void *ktmat;     // work space: K^T per chunk, bf16 [KD][C], permuted k order (PFRAG shapes)
     void *gtab;      // work space: e^{G_t} [C], e^{G_L - G_t} [C], e^{G_L}, 0, 0, 0 per chunk, fp32 (PFRAG shapes)
     int B, T, H, Dv;
     int out_bf16;
@@ -669,8 +667,13 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
     }
 }
 
-// Work space: T of every chunk, then (PFRAG shapes) the P fragments, W and
-// K^T of every chunk.
+// Per-chunk gate table of the PFRAG shapes (fp32): e^{G_t} [C], e^{G_L - G_t}
+// [C], e^{G_L}, 0, 0, 0, beta_t [C] (zero past the end of the sequence).
+template <int C>
+constexpr int gate_table_len() { return 3 * C + 4; }
+
+// Work space: T of every chunk, then (PFRAG shapes) the P fragments and the
+// gate tables of every chunk.
 template <bool F32IN, int KD, int C, int R>
 size_t chunk_tmat_bytes(int B, int T, int H) {
     using S = ChunkShape<F32IN, KD, C, R>;
@@ -687,10 +690,8 @@ template <bool F32IN, int KD, int C, int R>
 size_t chunk_workspace_bytes(int B, int T, int H) {
     using S = ChunkShape<F32IN, KD, C, R>;
     const size_t NT = (size_t)(T + C - 1) / C;
-    const size_t wbytes = S::PFRAG ? 2 * (size_t)B * H * NT * C * KD * 2 : 0;   // W and K^T
-    const size_t gbytes = S::PFRAG ? (size_t)B * H * NT * (2 * C + 4) * 4 : 0;  // gate tables
-    return chunk_tmat_bytes<F32IN, KD, C, R>(B, T, H) + chunk_pfrag_bytes<F32IN, KD, C, R>(B, T, H) + wbytes +
-           gbytes;
+    const size_t gbytes = S::PFRAG ? (size_t)B * H * NT * gate_table_len<C>() * 4 : 0;  // gate tables
+    return chunk_tmat_bytes<F32IN, KD, C, R>(B, T, H) + chunk_pfrag_bytes<F32IN, KD, C, R>(B, T, H) + gbytes;
 }
 
 }  // namespace gdn

@@ -2,26 +2,26 @@
 // one step per token): everything about a chunk that does not depend on the
 // state, computed in parallel over chunks (msj19 "gated_deltaproduct"
 // test.py with r = 1: gated_chunk_scaled_dot_kkt_fwd_kernel, solve_tril and
-// the block merges, gated_fwd_recompute_w_u_kernel, and the intra-chunk
-// scores of gated_chunk_linear_attn_fwd_kernel_o).  Per chunk of C tokens:
+// the block merges, and the intra-chunk scores of
+// gated_chunk_linear_attn_fwd_kernel_o).  Per chunk of C tokens:
 //
 //   G       chunk-local cumsum of the log-decay (kept in log2 units)
 //   A       [s<t] beta_t (k_t . k_s) e^{G_t - G_s}       (fp32, LDS)
 //   T       (I + A)^-1: 16x16 diagonal blocks by forward substitution, then
 //           block rows T_ij = -T_ii sum_m A_im T_mj; stored as T diag(beta)
-//           (so the state pass forms U = T diag(beta) V from exact V) -> bf16
-//   W       T diag(beta e^G) K, rows in the permuted k order         -> bf16
-//   K^T     rows of C tokens, permuted k order
+//           without its diagonal (the state pass forms V_new = T diag(beta)
+//           (V - e^G K S) from exact V and K and applies the diagonal, beta,
+//           in fp32), columns in the permuted k order              -> bf16
 //   P       [s<=t] (q_t . k_s) e^{G_t - G_s} of the lower 16x16 tiles, as
 //           hi/lo bf16 MFMA fragments (lane l: row t = 16 ti + l%16,
 //           columns s = 16 tj + 4 (l/16) + e)
-//   gates   e^{G_t}, e^{G_L - G_t}, e^{G_L}                           -> fp32
+//   gates   e^{G_t}, e^{G_L - G_t}, e^{G_L}, beta_t                   -> fp32
 //
 // Persistent workgroups of 4 waves walk the chunks with a stride of the
 // grid; the next chunk's K, Q, beta and g are loaded into registers while the
 // current one is solved, so the global-load latency stays hidden.  Wave 0
 // inverts I + A alone (forward substitution, then the block rows: no
-// barriers) while waves 1..3 compute the P tiles and write K^T.
+// barriers) while waves 1..3 compute the P tiles.
 #pragma once
 
 #include "chunk_kernels.h"
@@ -42,10 +42,10 @@ struct Prep1Shape {
     static constexpr int OFF_AS = OFF_KS + al(C * LDK * 2);
     static constexpr int OFF_TS = OFF_AS + al(C * LDA * 4);
     static constexpr int OFF_G = OFF_TS + al(C * LDA * 4);
-    static constexpr int BYTES = OFF_G + al(3 * C * 4);   // beta, G2, beta e^G
+    static constexpr int BYTES = OFF_G + al(2 * C * 4);   // beta, G2
     static_assert(C % 32 == 0 && C <= 64 && KD % 32 == 0 && KD <= 256, "shape");
     static_assert(BYTES <= 80 * 1024, "two workgroups per CU");
-    // P row tiles while wave 0 inverts (waves 1..3; wave 3 also writes K^T):
+    // P row tiles while wave 0 inverts (waves 1..3):
     // wave w takes rows prow0(w) and prow1(w) (-1: none).
     static constexpr int prow0(int w) {
         return NTT == 4 ? (w == 1 ? 3 : w == 2 ? 2 : w == 3 ? 1 : -1) : (w == 1 ? 1 : w == 2 ? 0 : -1);
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
     float *As = reinterpret_cast<float *>(smem + S::OFF_AS);
     float *Ts = reinterpret_cast<float *>(smem + S::OFF_TS);
     float *betas = reinterpret_cast<float *>(smem + S::OFF_G);
-    float *G2 = betas + C, *BEG = betas + 2 * C;
+    float *G2 = betas + C;
 
     const int tid = threadIdx.x, l = tid & 63, c16 = l & 15, g = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -136,11 +136,11 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
                 const float eg = fast_exp2(g2);
                 betas[l] = bt;
                 G2[l] = g2;
-                BEG[l] = bt * eg;
-                float *gt = reinterpret_cast<float *>(args.gtab) + ((size_t)bh * NT + c) * (2 * C + 4);
+                float *gt = reinterpret_cast<float *>(args.gtab) + ((size_t)bh * NT + c) * gate_table_len<C>();
                 gt[l] = eg;                          // e^{G_t}
                 gt[C + l] = fast_exp2(g2l - g2);     // e^{G_L - G_t}
                 if (l < 4) gt[2 * C + l] = l == 0 ? fast_exp2(g2l) : 0.f;   // e^{G_L}
+                gt[2 * C + 4 + l] = bt;              // beta_t
             }
         }
         __syncthreads();
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
         __syncthreads();
 
         // ---- wave 0: T = (I + A)^-1 (diagonal blocks by forward substitution,
-        //      then the block rows, without barriers); waves 1..3: P, K^T ----
+        //      then the block rows, without barriers); waves 1..3: P ----
         if (w == 0) {
             const int ib = l >> 4, col = l & 15;
             if (ib < NTT) {
@@ -242,91 +242,35 @@ __global__ __launch_bounds__(256) void chunk_prep1_kernel(ChunkArgs args) {
             };
             if (pr0 >= 0) p_row(pr0, qf);
             if (pr1 >= 0) p_row(pr1, qf1);
-            // lane (g, j) of block (it, m): K^T row i = 16 it + j, stored chunk 4m + g =
-            // tokens 32m + 4g + {0..3} and 32m + 16 + 4g + {0..3}, read transposed from Ks
-            u16 *kout = reinterpret_cast<u16 *>(args.ktmat) + ((size_t)bh * NT + c) * KD * C;
-            for (int blk = w == 3 ? 0 : (KD / 16) * (C / 32); blk < (KD / 16) * (C / 32); ++blk) {
-                const int it = blk / (C / 32), m = blk % (C / 32);
-                const u16 *kp = Ks + (m * 32 + 4 * g + (c16 >> 2)) * LDK + it * 16 + 4 * (c16 & 3);
-                const uint2 lo = __builtin_bit_cast(uint2, ld_tr16(kp));
-                const uint2 hi = __builtin_bit_cast(uint2, ld_tr16(kp + 16 * LDK));
-                const int i = it * 16 + c16;
-                *reinterpret_cast<uint4 *>(kout + i * C + (4 * m + g) * 8) = uint4{lo.x, lo.y, hi.x, hi.y};
-            }
         }
         // registers are free: start loading the next chunk
         if (ci + (int)gridDim.x < total) prefetch(ci + gridDim.x);
         __syncthreads();
 
-        // ---- W = T diag(beta e^G) K as W^T tiles K^T (T diag(beta e^G))^T ----
-        {
-            u16 *wout = reinterpret_cast<u16 *>(args.wmat) + ((size_t)bh * NT + c) * C * KD;
-            // B operands (T diag(beta e^G))^T, hi + lo, of every (tt, m) inside
-            // the block triangle: the same for all key tiles it of this wave
-            bf16x8 bh[NTT][C / 32], bl[NTT][C / 32];
-#pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) {
-                const int t = tt * 16 + c16;
-#pragma unroll
-                for (int m = 0; m < C / 32; ++m) {
-                    if (2 * m > tt) break;                      // T is block lower triangular
-                    const int s0 = m * 32 + 8 * g;
-                    const bool ok = (s0 >> 4) <= tt;
-                    const floatx4 x0 = *reinterpret_cast<const floatx4 *>(Ts + t * LDA + s0);
-                    const floatx4 x1 = *reinterpret_cast<const floatx4 *>(Ts + t * LDA + s0 + 4);
-                    const floatx4 b0 = *reinterpret_cast<const floatx4 *>(BEG + s0);
-                    const floatx4 b1 = *reinterpret_cast<const floatx4 *>(BEG + s0 + 4);
-                    uint4 hi, lo;
-                    split2_bf16(ok ? x0[0] * b0[0] : 0.f, ok ? x0[1] * b0[1] : 0.f, hi.x, lo.x);
-                    split2_bf16(ok ? x0[2] * b0[2] : 0.f, ok ? x0[3] * b0[3] : 0.f, hi.y, lo.y);
-                    split2_bf16(ok ? x1[0] * b1[0] : 0.f, ok ? x1[1] * b1[1] : 0.f, hi.z, lo.z);
-                    split2_bf16(ok ? x1[2] * b1[2] : 0.f, ok ? x1[3] * b1[3] : 0.f, hi.w, lo.w);
-                    bh[tt][m] = __builtin_bit_cast(bf16x8, hi);
-                    bl[tt][m] = __builtin_bit_cast(bf16x8, lo);
-                }
-            }
-            for (int it = w; it < KD / 16; it += 4) {
-                // K^T fragments of rows 16 it + j, k = 32 m + 8 g + {0..7}
-                bf16x8 ka[C / 32];
-#pragma unroll
-                for (int m = 0; m < C / 32; ++m) {
-                    const u16 *kp = Ks + (m * 32 + 8 * g + (c16 >> 2)) * LDK + it * 16 + 4 * (c16 & 3);
-                    const uint2 k0 = __builtin_bit_cast(uint2, ld_tr16(kp));
-                    const uint2 k1 = __builtin_bit_cast(uint2, ld_tr16(kp + 4 * LDK));
-                    ka[m] = __builtin_bit_cast(bf16x8, uint4{k0.x, k0.y, k1.x, k1.y});
-                }
-#pragma unroll
-                for (int tt = 0; tt < NTT; ++tt) {
-                    const int t = tt * 16 + c16;
-                    floatx4 acc = zero4();
-#pragma unroll
-                    for (int m = 0; m < C / 32; ++m) {
-                        if (2 * m > tt) break;
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], bh[tt][m], acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], bl[tt][m], acc, 0, 0, 0);
-                    }
-                    // lane: W[t][16 it + 4g + e], stored in the permuted order
-                    *reinterpret_cast<uint2 *>(wout + (size_t)t * KD + perm4_pos(it * 16 + 4 * g)) =
-                        uint2{cvt2_bf16(acc[0], acc[1]), cvt2_bf16(acc[2], acc[3])};
-                }
-            }
-        }
-        // ---- T diag(beta) (zero above the block diagonal), bf16 ----
+        // ---- T diag(beta) (zero above the block diagonal), bf16, columns in the
+        //      permuted order: 16-byte piece 4m + g of a row holds columns
+        //      32m + 4g + {0..3} and 32m + 16 + 4g + {0..3} ----
         {
             u16 *out = reinterpret_cast<u16 *>(args.tmat) + ((size_t)bh * NT + c) * C * C;
             for (int idx = tid; idx < C * C / 8; idx += 256) {
-                const int i = idx / (C / 8), j0 = (idx % (C / 8)) * 8;
+                const int i = idx / (C / 8), pc = idx % (C / 8), j0 = (pc >> 2) * 32 + 4 * (pc & 3), j1 = j0 + 16;
                 floatx4 x0 = *reinterpret_cast<const floatx4 *>(Ts + i * LDA + j0);
-                floatx4 x1 = *reinterpret_cast<const floatx4 *>(Ts + i * LDA + j0 + 4);
+                floatx4 x1 = *reinterpret_cast<const floatx4 *>(Ts + i * LDA + j1);
                 const floatx4 b0 = *reinterpret_cast<const floatx4 *>(betas + j0);
-                const floatx4 b1 = *reinterpret_cast<const floatx4 *>(betas + j0 + 4);
+                const floatx4 b1 = *reinterpret_cast<const floatx4 *>(betas + j1);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     x0[e] *= b0[e];
                     x1[e] *= b1[e];
                 }
-                if ((j0 >> 4) > (i >> 4)) x0 = x1 = zero4();
-                *reinterpret_cast<uint4 *>(out + (size_t)i * C + j0) =
+                if ((j0 >> 4) > (i >> 4)) x0 = zero4();
+                if ((j1 >> 4) > (i >> 4)) x1 = zero4();
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {       // the diagonal (beta) is applied in fp32 by the state pass
+                    if (j0 + e == i) x0[e] = 0.f;
+                    if (j1 + e == i) x1[e] = 0.f;
+                }
+                *reinterpret_cast<uint4 *>(out + (size_t)i * C + pc * 8) =
                     uint4{cvt2_bf16(x0[0], x0[1]), cvt2_bf16(x0[2], x0[3]), cvt2_bf16(x1[0], x1[1]),
                           cvt2_bf16(x1[2], x1[3])};
             }
