@@ -274,8 +274,9 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
                 bt[tt] = *reinterpret_cast<const floatx4 *>(gp + 2 * C + 4 + tt * 16 + 4 * g);
             }
             const float gL = gp[2 * C];
-            // R = V - e^G Y; V_new = (T diag(beta)) R: its diagonal, beta, in fp32,
-            // the rest (block lower triangular) by MFMA on R as hi + lo
+            // R = V - e^G Y; V_new = (T diag(beta)) R: its diagonal, beta, in fp32
+            // on R, the rest (block lower triangular, entries well below beta)
+            // by MFMA on R rounded to bf16
             floatx4 rr[NTT];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
@@ -285,9 +286,9 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
 #pragma unroll
                 for (int e = 0; e < 4; ++e) rr[tt][e] = vx[e] - eg[tt][e] * y[tt][e];
             }
-            bf16x8 rh[NCS], rl[NCS];
+            bf16x8 rh[NCS];
 #pragma unroll
-            for (int m = 0; m < NCS; ++m) frag_split(rr[2 * m], rr[2 * m + 1], rh[m], rl[m]);
+            for (int m = 0; m < NCS; ++m) rh[m] = frag_hi(rr[2 * m], rr[2 * m + 1]);
             floatx4 vn[NTT];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt)
@@ -297,10 +298,7 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
             for (int m = 0; m < NCS; ++m)
 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt)
-                    if (2 * m <= tt) {
-                        vn[tt] = mfma32(tf[tt][m], rh[m], vn[tt]);
-                        vn[tt] = mfma32(tf[tt][m], rl[m], vn[tt]);
-                    }
+                    if (2 * m <= tt) vn[tt] = mfma32(tf[tt][m], rh[m], vn[tt]);
             // V_new published fp32 [j][s]; V~ = e^{G_L - G} V_new
             float *vnp = Vn(p);
             floatx4 vt4[NTT];
