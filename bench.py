@@ -30,7 +30,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 KERNEL_SOURCES = ("chunkwise_gated_delta_gdn_amd/csrc/chunk_kernels.h",
-                  "chunkwise_gated_delta_gdn_amd/csrc/chunk_prep1.h",
+                  "chunkwise_gated_delta_gdn_amd/csrc/chunk_prep2.h",
                   "chunkwise_gated_delta_gdn_amd/csrc/chunk_chain1.h",
                   "chunkwise_gated_delta_gdn_amd/csrc/chunk_dispatch.h",
                   "chunkwise_gated_delta_gdn_amd/csrc/gdn_common.h")
@@ -205,7 +205,7 @@ def main():
         metric = "tokens/sec of chunkwise gated-delta fwd (B*T/s) at H=16, D=128"
         desc = (f"{args.workload}: B={wl['B']} H={wl['H']} T={wl['T']} Dk=Dv={wl['Dk']} chunk={wl['chunk']}, "
                 f"bf16 q/k/v, fp32 gates/state/output, " + ("h0~N(0,0.02^2)" if wl["h0_std"] else "h0=0"))
-        kernel = "gdn_chunk_fwd = chunk_prep1_kernel + chunk_chain1_kernel <KD=128, C=64>"
+        kernel = "gdn_chunk_fwd = chunk_prep2_kernel + chunk_chain1_kernel <KD=128, C=64>"
         traffic = measured_traffic(kernel_source_hash()) if args.workload == "gdn" else None
     elif args.workload == "deltaproduct":
         metric = "tokens/sec of chunkwise gated DeltaProduct fwd (B*T/s)"

@@ -2,7 +2,7 @@
 // inputs with one step per token (msj19 "gated_deltaproduct" test.py with
 // r = 1: gated_chunk_delta_rule_fwd_kernel_h and
 // gated_chunk_linear_attn_fwd_kernel_o; T diag(beta), the P tiles and the
-// gate tables come from chunk_prep1_kernel in the work space).
+// gate tables come from chunk_prep2_kernel in the work space).
 //
 // One workgroup per (batch, head, 16-column slice of the value dimension),
 // 1 + C/16 waves, split by role outside the chunk loop (each role keeps only
@@ -127,20 +127,7 @@ __device__ __forceinline__ void frag_split(const floatx4 &t0, const floatx4 &t1,
     hi = __builtin_bit_cast(bf16x8, h);
     lo = __builtin_bit_cast(bf16x8, o);
 }
-__device__ __forceinline__ void split4(const floatx4 &x, shortx4 &hi, shortx4 &lo) {
-    uint2 h, o;
-    split2_bf16(x[0], x[1], h.x, o.x);
-    split2_bf16(x[2], x[3], h.y, o.y);
-    hi = __builtin_bit_cast(shortx4, h);
-    lo = __builtin_bit_cast(shortx4, o);
-}
 
-__device__ __forceinline__ floatx4 mfma32(bf16x8 a, bf16x8 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx4 mfma16(shortx4 a, shortx4 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 
 template <int KD, int C>
 __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain1_kernel(ChunkArgs args) {

@@ -4,7 +4,7 @@
 
 #include "chunk_chain1.h"
 #include "chunk_kernels.h"
-#include "chunk_prep1.h"
+#include "chunk_prep2.h"
 
 namespace gdn {
 
@@ -44,10 +44,12 @@ hipError_t launch_chunk_fwd(const ChunkArgs &args, hipStream_t stream) {
     if (nbh == 0) return hipSuccess;
     if (NT > 0) {
         if constexpr (use_chain1<F32IN, KD, C, R>()) {
-            // persistent: two workgroups per CU, each walking chunks with the grid stride
+            // one wave per chunk, four per workgroup, at most two workgroups per
+            // CU resident; waves walk the chunks with the grid stride
             const int nchunks = nbh * NT;
-            const int grid = nchunks < 2 * num_cus() ? nchunks : 2 * num_cus();
-            hipLaunchKernelGGL((chunk_prep1_kernel<KD, C>), dim3(grid), dim3(256), 0, stream, a);
+            const int nwg = (nchunks + 3) / 4;
+            const int grid = nwg < 2 * num_cus() ? nwg : 2 * num_cus();
+            hipLaunchKernelGGL((chunk_prep2_kernel<KD, C>), dim3(grid), dim3(256), 0, stream, a);
         } else {
             hipLaunchKernelGGL((chunk_solve_kernel<F32IN, KD, C, R>), dim3(nbh * NT), dim3(256), 0, stream, a);
         }

@@ -119,8 +119,8 @@ struct ChunkShape {
     static constexpr int LDVT = C + PAD;       // Vn/Vt:   [R][BV][C]
     static constexpr int LDY = 17;             // merge scratch [16][17] fp32
     // bf16 inputs, one step per token, 32-multiple widths: these shapes run
-    // chunk_prep1_kernel + chunk_chain1_kernel, whose work space also holds
-    // the P fragments, W and K^T of every chunk.
+    // chunk_prep2_kernel + chunk_chain1_kernel, whose work space also holds
+    // the P fragments and gate tables of every chunk.
     static constexpr bool PFRAG = !F32IN && R == 1 && C % 32 == 0 && KD % 32 == 0;
     static constexpr int al(int x) { return (x + 15) & ~15; }
     static_assert(KD % R == 0, "key width must split into R sub-keys");

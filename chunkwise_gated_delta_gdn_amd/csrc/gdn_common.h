@@ -146,6 +146,23 @@ __device__ __forceinline__ void mma_f32(floatx4 &acc, const float *a, int lda, c
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[kk], pb[kk], acc, 0, 0, 0);
 }
 
+// hi and lo bf16 of 4 consecutive values (a 16-deep MFMA operand)
+__device__ __forceinline__ void split4(const floatx4 &x, shortx4 &hi, shortx4 &lo) {
+    uint2 h, o;
+    split2_bf16(x[0], x[1], h.x, o.x);
+    split2_bf16(x[2], x[3], h.y, o.y);
+    hi = __builtin_bit_cast(shortx4, h);
+    lo = __builtin_bit_cast(shortx4, o);
+}
+
+// 16x16 MFMA steps of 32 (bf16x8 operands) and 16 (4 x bf16) k values
+__device__ __forceinline__ floatx4 mfma32(bf16x8 a, bf16x8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(shortx4 a, shortx4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
 // acc += A * B with B stored row-major ([k][col], stride ldb).
 __device__ __forceinline__ void mma_f32_bn(floatx4 &acc, const float *a, int lda, const float *b, int ldb,
                                            int kdim) {
