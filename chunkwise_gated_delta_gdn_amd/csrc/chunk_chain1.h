@@ -69,7 +69,7 @@ struct Chain1Shape {
     static constexpr int LDK = KD;            // Ks  [C][KD]   bf16, K rows (natural order)
     static constexpr int LDT = C;             // Tb  [C][C]    bf16, T diag(beta) (permuted k order)
     static constexpr int LDV = BV;            // Vs  [C][BV]   bf16, the V slice (row-major)
-    static constexpr int LDSH = KD + 8;       // St  [2][BV][KD] bf16 hi, lo of S_start transposed
+    static constexpr int LDSF = KD + 4;       // St  [BV][KD]  fp32, S_start transposed
     static constexpr int LDVF = C + 4;        // Vn  [BV][C]   fp32, V_new transposed
     // gate table: e^G [C], e^{G_L-G} [C], e^{G_L} (+3), beta [C]
     static constexpr int NGATE = gate_table_len<C>();
@@ -78,7 +78,7 @@ struct Chain1Shape {
     static constexpr int SZ_TB = al(C * LDT * 2);
     static constexpr int SZ_BV = al(C * LDV * 2);
     static constexpr int SZ_GATE = al(NGATE * 4);
-    static constexpr int SZ_ST = al(2 * BV * LDSH * 2);
+    static constexpr int SZ_ST = al(BV * LDSF * 4);
     static constexpr int SZ_VN = al(BV * LDVF * 4);
     // staging buffers are triple (index chunk % 3: staged two iterations
     // ahead), St and Vn double (index chunk & 1)
@@ -133,7 +133,7 @@ template <int KD, int C>
 __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain1_kernel(ChunkArgs args) {
     using S = Chain1Shape<KD, C>;
     constexpr int BV = S::BV, NTT = S::NTT, NKS = S::NKS, NST = S::NST, NCS = S::NCS, NKC = S::NKC;
-    constexpr int LDK = S::LDK, LDT = S::LDT, LDV = S::LDV, LDSH = S::LDSH, LDVF = S::LDVF;
+    constexpr int LDK = S::LDK, LDT = S::LDT, LDV = S::LDV, LDSF = S::LDSF, LDVF = S::LDVF;
     constexpr int TSW = S::TSW;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::BYTES];
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
     auto Tb = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_TB + p * S::SZ_TB); };
     auto BVs = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_BV + p * S::SZ_BV); };
     auto gate = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_GATE + p * S::SZ_GATE); };
-    auto St = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_ST + p * S::SZ_ST); };
+    auto St = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_ST + p * S::SZ_ST); };
     auto Vn = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_VN + p * S::SZ_VN); };
 
     if (w == 0) {
@@ -173,24 +173,13 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
         // (the B operand of K S), and K^T fragments pick their rows to match.
         floatx4 Sreg[NST];
         auto feat = [&](int ti, int e) { return (ti >> 1) * 32 + 8 * g + 4 * (ti & 1) + e; };
-        // S_start as hi + lo bf16, transposed to [j][i], for the output waves
-        auto publish_state = [&](int p, const bf16x8 (&hi)[NKS]) {
-            u16 *sh = St(p) + c16 * LDSH, *sl = sh + BV * LDSH;
+        // S_start (fp32, transposed to [j][i]) for the output waves, which
+        // split their fragments into hi + lo bf16 themselves: the four rows
+        // of a tile are consecutive key features
+        auto publish_state = [&](int p) {
+            float *sf = St(p) + c16 * LDSF;
 #pragma unroll
-            for (int m = 0; m < NKS; ++m) {
-                const uint4 h = __builtin_bit_cast(uint4, hi[m]);
-                uint4 o;
-                o.x = cvt2_bf16(Sreg[2 * m][0] - __builtin_bit_cast(float, h.x << 16),
-                                Sreg[2 * m][1] - __builtin_bit_cast(float, h.x & 0xffff0000u));
-                o.y = cvt2_bf16(Sreg[2 * m][2] - __builtin_bit_cast(float, h.y << 16),
-                                Sreg[2 * m][3] - __builtin_bit_cast(float, h.y & 0xffff0000u));
-                o.z = cvt2_bf16(Sreg[2 * m + 1][0] - __builtin_bit_cast(float, h.z << 16),
-                                Sreg[2 * m + 1][1] - __builtin_bit_cast(float, h.z & 0xffff0000u));
-                o.w = cvt2_bf16(Sreg[2 * m + 1][2] - __builtin_bit_cast(float, h.w << 16),
-                                Sreg[2 * m + 1][3] - __builtin_bit_cast(float, h.w & 0xffff0000u));
-                *reinterpret_cast<uint4 *>(sh + m * 32 + 8 * g) = h;
-                *reinterpret_cast<uint4 *>(sl + m * 32 + 8 * g) = o;
-            }
+            for (int ti = 0; ti < NST; ++ti) *reinterpret_cast<floatx4 *>(sf + feat(ti, 0)) = Sreg[ti];
         };
 #pragma unroll
         for (int ti = 0; ti < NST; ++ti) {
@@ -226,10 +215,10 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
                 for (int tt = 0; tt < NTT; ++tt)
                     if (2 * m <= tt)
                         tf[tt][m] = ld8(tb + (tt * 16 + c16) * LDT + (((4 * m + g) ^ ((tt * 16 + c16) & TSW)) << 3));
+            publish_state(p);                    // S_start of chunk c
             bf16x8 sb[NKS];
 #pragma unroll
             for (int m = 0; m < NKS; ++m) sb[m] = frag_hi(Sreg[2 * m], Sreg[2 * m + 1]);
-            publish_state(p, sb);                // S_start of chunk c
             // Y = K S
             floatx4 y[NTT];
 #pragma unroll
@@ -415,13 +404,16 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
         };
         // O^T of chunk c: a1 = S_start^T Q^T, a2 = V_new^T P^T (buffers c & 1)
         auto compute_out = [&](int c) {
-            const u16 *sh = St(c & 1) + c16 * LDSH, *sl = sh + BV * LDSH;
+            const float *sf = St(c & 1) + c16 * LDSF;
             const float *vnp = Vn(c & 1);
             floatx4 a1 = zero4(), a2 = zero4();
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
-                a1 = mfma32(ld8(sh + m * 32 + 8 * g), qf[m], a1);
-                a1 = mfma32(ld8(sl + m * 32 + 8 * g), qf[m], a1);
+                bf16x8 sh, sl;
+                frag_split(*reinterpret_cast<const floatx4 *>(sf + m * 32 + 8 * g),
+                           *reinterpret_cast<const floatx4 *>(sf + m * 32 + 8 * g + 4), sh, sl);
+                a1 = mfma32(sh, qf[m], a1);
+                a1 = mfma32(sl, qf[m], a1);
             }
 #pragma unroll
             for (int tj = 0; tj <= TW; ++tj) {
