@@ -215,7 +215,6 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
                 for (int tt = 0; tt < NTT; ++tt)
                     if (2 * m <= tt)
                         tf[tt][m] = ld8(tb + (tt * 16 + c16) * LDT + (((4 * m + g) ^ ((tt * 16 + c16) & TSW)) << 3));
-            publish_state(p);                    // S_start of chunk c
             bf16x8 sb[NKS];
 #pragma unroll
             for (int m = 0; m < NKS; ++m) sb[m] = frag_hi(Sreg[2 * m], Sreg[2 * m + 1]);
@@ -298,6 +297,9 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
 #pragma unroll
                 for (int ti = 0; ti < NST; ++ti) ds[ti] = mfma32(ka[ti][m], vl[m], ds[ti]);
             }
+            // S_start of chunk c goes out while the state MFMAs run (its LDS
+            // writes then do not queue ahead of this chunk's operand reads)
+            publish_state(p);
 #pragma unroll
             for (int ti = 0; ti < NST; ++ti)
 #pragma unroll
