@@ -50,11 +50,12 @@ struct Chain1Shape {
     static constexpr int NTT = C / 16;        // token tiles
     // Waves (they go to the four SIMDs of a CU in turn):
     //   C = 64: 0 the chain; 4 idle (it only takes part in the barriers, so
-    //           the chain has its SIMD to itself); 1, 2, 3, 5 the output of
-    //           tiles 3, 2, 1, 0; 6, 7 the staging.
+    //           the chain has its SIMD to itself); 1, 2 the output of token
+    //           tiles {3, 0} and {2, 1} (equal score work; each reads the
+    //           start state once for its two tiles); 3, 5 the staging.
     //   C = 32: 0 the chain; 1, 2 the output of tiles 1, 0 and the staging.
     static constexpr int IDLE = NTT == 4 ? 4 : -1;
-    static constexpr int NW = NTT == 4 ? 8 : 1 + NTT;
+    static constexpr int NW = NTT == 4 ? 6 : 1 + NTT;
     static constexpr int NTHR = 64 * NW;
     static constexpr int NLW = 2;             // staging ("loader") waves
     static constexpr int NKS = KD / 32;       // 32-wide steps over the key dim
@@ -130,7 +131,7 @@ __device__ __forceinline__ void frag_split(const floatx4 &t0, const floatx4 &t1,
 
 
 template <int KD, int C>
-__global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain1_kernel(ChunkArgs args) {
+__global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kernel(ChunkArgs args) {
     using S = Chain1Shape<KD, C>;
     constexpr int BV = S::BV, NTT = S::NTT, NKS = S::NKS, NST = S::NST, NCS = S::NCS, NKC = S::NKC;
     constexpr int LDK = S::LDK, LDT = S::LDT, LDV = S::LDV, LDSF = S::LDSF, LDVF = S::LDVF;
@@ -326,8 +327,8 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
     // outstanding loads is in order, and a load skipped on some path would
     // make the compiler wait for every load issued after the one it needs.
     //
-    // Roles: OW = token tile of the output (-1: none); LI = staging index
-    // (-1: none).  Staging of chunk c+2 in iteration c: NDMA LDS-direct wave
+    // Roles: OA, OB = token tiles of the output (-1: none); LI = staging
+    // index (-1: none).  Staging of chunk c+2 in iteration c: NDMA LDS-direct wave
     // loads of 1 KiB (K, T diag(beta), the V slice, the gate table),
     // load k on staging wave k % NLW, waited for before the barrier.
     constexpr int NLW = S::NLW;
@@ -343,9 +344,9 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
     const u16 *tg = reinterpret_cast<const u16 *>(args.tmat) + (size_t)bh * NT * C * C;
     const float *gtg = reinterpret_cast<const float *>(args.gtab) + (size_t)bh * NT * S::NGATE;
 
-    auto out_wave = [&](auto owc, auto lic) {
-        constexpr int OW = decltype(owc)::value, LI = decltype(lic)::value;
-        constexpr bool TILE = OW >= 0, LOAD = LI >= 0;
+    auto out_wave = [&](auto owa, auto owb, auto lic) {
+        constexpr int OA = decltype(owa)::value, OB = decltype(owb)::value, LI = decltype(lic)::value;
+        constexpr bool TILE = OA >= 0, LOAD = LI >= 0;
         // Stage chunk c (clamped to the last chunk; a past-the-end chunk lands in
         // a buffer no one reads) into buffers c % 3.  Rows of the prep's
         // outputs past T are zero; K and V rows past T are clamped to T-1:
@@ -386,60 +387,77 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
             asm volatile("" ::: "memory");
         };
 
-        constexpr int TW = TILE ? OW : 0;
-        bf16x8 qf[NKS];                         // Q fragments (B operand, token = lane%16)
-        u32x4 pf[TW + 1];                       // P fragments of row tile OW: {hi01, hi23, lo01, lo23}
-        float egt = 0.f;                        // e^{G_t} of this lane's token
-        floatx4 ov = zero4();                   // output of the previous chunk
-        const uint4 *pfg = reinterpret_cast<const uint4 *>(args.pfrag) + (size_t)bh * NT * NLOW * 64 +
-                           (TW * (TW + 1) / 2) * 64 + l;
+        // token tiles of this wave: OA, and OB if any
+        constexpr int NTW = OB >= 0 ? 2 : 1;
+        constexpr int TW0 = OA >= 0 ? OA : 0, TW1 = OB >= 0 ? OB : 0;
+        constexpr int TWMAX = TW0 > TW1 ? TW0 : TW1;
+        auto tw = [](int i) { return i == 0 ? TW0 : TW1; };
+        bf16x8 qf[NTW][NKS];                    // Q fragments (B operand, token = lane%16)
+        u32x4 pf[NTW][NTT];                     // P fragments of each tile: {hi01, hi23, lo01, lo23}
+        float egt[NTW];                         // e^{G_t} of this lane's tokens
+        floatx4 ov[NTW];                        // outputs of the previous chunk
         // operands of chunk c's output, used one iteration later
         auto load_qp = [&](int c) {
-            const int t = min(c * C + TW * 16 + c16, tlast);   // rows past T are never stored
 #pragma unroll
-            for (int m = 0; m < NKS; ++m)
-                qf[m] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)t * tokq + m * 32 + 8 * g);
-            const uint4 *pc = pfg + (size_t)c * NLOW * 64;
+            for (int i = 0; i < NTW; ++i) {
+                const int t = min(c * C + tw(i) * 16 + c16, tlast);   // rows past T are never stored
 #pragma unroll
-            for (int tj = 0; tj <= TW; ++tj) pf[tj] = __builtin_bit_cast(u32x4, pc[tj * 64]);
-            egt = gate(c % 3)[TW * 16 + c16];
+                for (int m = 0; m < NKS; ++m)
+                    qf[i][m] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)t * tokq + m * 32 + 8 * g);
+                const uint4 *pc = reinterpret_cast<const uint4 *>(args.pfrag) + ((size_t)bh * NT + c) * NLOW * 64 +
+                                  (tw(i) * (tw(i) + 1) / 2) * 64 + l;
+#pragma unroll
+                for (int tj = 0; tj <= tw(i); ++tj) pf[i][tj] = __builtin_bit_cast(u32x4, pc[tj * 64]);
+                egt[i] = gate(c % 3)[tw(i) * 16 + c16];
+            }
         };
-        // O^T of chunk c: a1 = S_start^T Q^T, a2 = V_new^T P^T (buffers c & 1)
+        // O^T of chunk c: a1 = S_start^T Q^T, a2 = V_new^T P^T (buffers c & 1);
+        // the start state and V_new fragments are split once for both tiles
         auto compute_out = [&](int c) {
             const float *sf = St(c & 1) + c16 * LDSF;
             const float *vnp = Vn(c & 1);
-            floatx4 a1 = zero4(), a2 = zero4();
+            bf16x8 sh[NKS], sl[NKS];
 #pragma unroll
-            for (int m = 0; m < NKS; ++m) {
-                bf16x8 sh, sl;
+            for (int m = 0; m < NKS; ++m)
                 frag_split(*reinterpret_cast<const floatx4 *>(sf + m * 32 + 8 * g),
-                           *reinterpret_cast<const floatx4 *>(sf + m * 32 + 8 * g + 4), sh, sl);
-                a1 = mfma32(sh, qf[m], a1);
-                a1 = mfma32(sl, qf[m], a1);
-            }
+                           *reinterpret_cast<const floatx4 *>(sf + m * 32 + 8 * g + 4), sh[m], sl[m]);
+            shortx4 vh4[TWMAX + 1], vl4[TWMAX + 1];
 #pragma unroll
-            for (int tj = 0; tj <= TW; ++tj) {
-                shortx4 vh4, vl4;
-                split4(*reinterpret_cast<const floatx4 *>(vnp + c16 * LDVF + tj * 16 + 4 * g), vh4, vl4);
-                const shortx4 ph = __builtin_bit_cast(shortx4, uint2{pf[tj][0], pf[tj][1]});
-                const shortx4 pl = __builtin_bit_cast(shortx4, uint2{pf[tj][2], pf[tj][3]});
-                a2 = mfma16(vh4, ph, a2);
-                a2 = mfma16(vh4, pl, a2);
-                a2 = mfma16(vl4, ph, a2);
-            }
+            for (int tj = 0; tj <= TWMAX; ++tj)
+                split4(*reinterpret_cast<const floatx4 *>(vnp + c16 * LDVF + tj * 16 + 4 * g), vh4[tj], vl4[tj]);
             const float sc = args.scale;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ov[e] = sc * (egt * a1[e] + a2[e]);
+            for (int i = 0; i < NTW; ++i) {
+                floatx4 a1 = zero4(), a2 = zero4();
+#pragma unroll
+                for (int m = 0; m < NKS; ++m) {
+                    a1 = mfma32(sh[m], qf[i][m], a1);
+                    a1 = mfma32(sl[m], qf[i][m], a1);
+                }
+#pragma unroll
+                for (int tj = 0; tj <= tw(i); ++tj) {
+                    const shortx4 ph = __builtin_bit_cast(shortx4, uint2{pf[i][tj][0], pf[i][tj][1]});
+                    const shortx4 pl = __builtin_bit_cast(shortx4, uint2{pf[i][tj][2], pf[i][tj][3]});
+                    a2 = mfma16(vh4[tj], ph, a2);
+                    a2 = mfma16(vh4[tj], pl, a2);
+                    a2 = mfma16(vl4[tj], ph, a2);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ov[i][e] = sc * (egt[i] * a1[e] + a2[e]);
+            }
         };
         auto store_out = [&](int c) {
-            const int tt = c * C + TW * 16 + c16;
-            if (tt < T) {
-                const size_t off = (((size_t)b * T + tt) * H + h) * Dv + v0 + 4 * g;
-                if (args.out_bf16)
-                    *reinterpret_cast<uint2 *>(reinterpret_cast<u16 *>(args.o) + off) =
-                        uint2{cvt2_bf16(ov[0], ov[1]), cvt2_bf16(ov[2], ov[3])};
-                else
-                    *reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(args.o) + off) = ov;
+#pragma unroll
+            for (int i = 0; i < NTW; ++i) {
+                const int tt = c * C + tw(i) * 16 + c16;
+                if (tt < T) {
+                    const size_t off = (((size_t)b * T + tt) * H + h) * Dv + v0 + 4 * g;
+                    if (args.out_bf16)
+                        *reinterpret_cast<uint2 *>(reinterpret_cast<u16 *>(args.o) + off) =
+                            uint2{cvt2_bf16(ov[i][0], ov[i][1]), cvt2_bf16(ov[i][2], ov[i][3])};
+                    else
+                        *reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(args.o) + off) = ov[i];
+                }
             }
         };
 
@@ -485,16 +503,14 @@ __global__ __launch_bounds__(C == 64 ? 512 : (1 + C / 16) * 64) void chunk_chain
     using std::integral_constant;
     using none = integral_constant<int, -1>;
     if constexpr (NTT == 4) {
-        if (w == 1) out_wave(integral_constant<int, 3>{}, none{});
-        if (w == 2) out_wave(integral_constant<int, 2>{}, none{});
-        if (w == 3) out_wave(integral_constant<int, 1>{}, none{});
-        if (w == 5) out_wave(integral_constant<int, 0>{}, none{});
-        if (w == 6) out_wave(none{}, integral_constant<int, 0>{});
-        if (w == 7) out_wave(none{}, integral_constant<int, 1>{});
+        if (w == 1) out_wave(integral_constant<int, 3>{}, integral_constant<int, 0>{}, none{});
+        if (w == 2) out_wave(integral_constant<int, 2>{}, integral_constant<int, 1>{}, none{});
+        if (w == 3) out_wave(none{}, none{}, integral_constant<int, 0>{});
+        if (w == 5) out_wave(none{}, none{}, integral_constant<int, 1>{});
     } else {
         static_assert(NTT == 2, "chunk of 32 or 64 tokens");
-        if (w == 1) out_wave(integral_constant<int, 1>{}, integral_constant<int, 0>{});
-        if (w == 2) out_wave(integral_constant<int, 0>{}, integral_constant<int, 1>{});
+        if (w == 1) out_wave(integral_constant<int, 1>{}, none{}, integral_constant<int, 0>{});
+        if (w == 2) out_wave(integral_constant<int, 0>{}, none{}, integral_constant<int, 1>{});
     }
 }
 
