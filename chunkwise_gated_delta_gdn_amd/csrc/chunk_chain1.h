@@ -372,21 +372,6 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
                 }
             }
         };
-        // Barrier of a staging wave: LDS operations done, at most the NMINE
-        // newest global loads (this iteration's staging) still outstanding, so
-        // every older one (the previous staging, this wave's output loads) has
-        // landed.  __syncthreads() would wait for all of them.
-        constexpr int NMINE = LOAD ? (NDMA - LI + NLW - 1) / NLW : 0;
-        static_assert(NMINE < 64, "6-bit vmcnt");
-        // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, lgkmcnt(0), expcnt at its maximum
-        constexpr int WAIT_IMM = (NMINE & 15) | ((NMINE >> 4) << 14) | 0x0070;
-        auto stage_barrier = [&]() {
-            asm volatile("" ::: "memory");      // keep memory operations on their side
-            __builtin_amdgcn_s_waitcnt(WAIT_IMM);
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-        };
-
         // token tiles of this wave: OA, and OB if any
         constexpr int NTW = OB >= 0 ? 2 : 1;
         constexpr int TW0 = OA >= 0 ? OA : 0, TW1 = OB >= 0 ? OB : 0;
@@ -461,6 +446,30 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
             }
         };
 
+        // The workgroup barrier of an output or staging wave: its LDS
+        // operations done (the buffers it reads are rewritten next), but its
+        // newest global operations left in flight -- this iteration's staging
+        // (waited for at the next barrier), Q and P loads (used next
+        // iteration) and output stores.  __syncthreads() would wait for all of
+        // them.  The hardware counter of outstanding global operations is in
+        // order, so "at most N outstanding" completes everything older than
+        // the newest N; a staging wave's N counts only the operations it
+        // issues unconditionally after the previous staging (its Q and P
+        // loads, then this staging), so that staging is always complete.  An
+        // output-only wave stages nothing and waits for none of its own.
+        constexpr int NMINE = LOAD ? (NDMA - LI + NLW - 1) / NLW : 0;
+        constexpr int NQP = TILE ? NTW * NKS + (TW0 + 1) + (NTW > 1 ? TW1 + 1 : 0) : 0;
+        constexpr int NOWN = LOAD ? NMINE + NQP : 63;
+        static_assert(NOWN < 64, "6-bit vmcnt");
+        // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, lgkmcnt(0), expcnt at its maximum
+        constexpr int WAIT_IMM = (NOWN & 15) | ((NOWN >> 4) << 14) | 0x0070;
+        auto wave_barrier = [&]() {
+            asm volatile("" ::: "memory");      // keep memory operations on their side
+            __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+
         // Iteration c (one barrier each): output of chunk c-1, operands of
         // chunk c, staging of chunk c+2 (waited for one iteration later).
         if constexpr (LOAD) {
@@ -470,24 +479,16 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
         }
         __syncthreads();
         if constexpr (TILE) load_qp(0);
-        if constexpr (LOAD) {
-            stage(2);
-            stage_barrier();
-        } else {
-            __syncthreads();
-        }
+        if constexpr (LOAD) stage(2);
+        wave_barrier();
         for (int c = 1; c < NT; ++c) {
             if constexpr (TILE) {
                 compute_out(c - 1);
                 load_qp(c);
                 store_out(c - 1);
             }
-            if constexpr (LOAD) {
-                stage(c + 2);
-                stage_barrier();
-            } else {
-                __syncthreads();
-            }
+            if constexpr (LOAD) stage(c + 2);
+            wave_barrier();
         }
         if constexpr (TILE) {
             compute_out(NT - 1);
