@@ -2,8 +2,9 @@
 // and cam_prep_func, with the inverse RMS of _precompute_cam_inv_rms fused
 // in (the page computes it in separate torch reductions that re-read q and k).
 //
-// One wave per token.  The C = H*D channels of q, k and v are cut into
-// 8-element segments; lane l owns segments l, l+64, ... .  A segment lies in
+// One wave per token at a time (waves walk the tokens with a stride of the
+// grid).  The C = H*D channels of q, k and v are cut into 8-element
+// segments; lane l owns segments l, l+64, ... .  A segment lies in
 // one head and in one half of it (D/2 is a multiple of 8), so each lane works
 // either on two UCPE groups of 4 or on four RoPE pairs, in registers:
 //   1. load q, k, v segments (16-byte vector loads), sum q^2 and k^2, reduce
@@ -34,20 +35,6 @@ struct PrepArgs {
 };
 
 template <bool F32IN>
-__device__ __forceinline__ void load8(const void *base, size_t elem, float (&x)[8]) {
-    if constexpr (F32IN) {
-        const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + elem);
-        const float4 a = p[0], b = p[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    } else {
-        const U16x8 r = *reinterpret_cast<const U16x8 *>(reinterpret_cast<const u16 *>(base) + elem);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32(r.v[e]);
-    }
-}
-
-template <bool F32IN>
 __device__ __forceinline__ void store8(void *base, size_t elem, const float (&x)[8]) {
     if constexpr (F32IN) {
         float4 *p = reinterpret_cast<float4 *>(reinterpret_cast<float *>(base) + elem);
@@ -74,65 +61,149 @@ __device__ __forceinline__ float head_sum(float x) {     // over the D/8 lanes o
     return x;
 }
 
-// NSEG = segments per lane = H*D / 512 (rounded up); one wave per token.
+// A token's raw q, k or v segment (8 values) as loaded: bf16 in one 16-byte
+// vector, fp32 in two.
+template <bool F32IN>
+struct Raw8 {
+    uint4 w[F32IN ? 2 : 1];
+};
+template <bool F32IN>
+__device__ __forceinline__ Raw8<F32IN> load_raw8(const void *base, size_t elem) {
+    Raw8<F32IN> r;
+    if constexpr (F32IN) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(base) + elem);
+        r.w[0] = p[0];
+        r.w[1] = p[1];
+    } else {
+        r.w[0] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const u16 *>(base) + elem);
+    }
+    return r;
+}
+template <bool F32IN>
+__device__ __forceinline__ void unpack8(const Raw8<F32IN> &r, float (&x)[8]) {
+    if constexpr (F32IN) {
+        x[0] = __uint_as_float(r.w[0].x); x[1] = __uint_as_float(r.w[0].y);
+        x[2] = __uint_as_float(r.w[0].z); x[3] = __uint_as_float(r.w[0].w);
+        x[4] = __uint_as_float(r.w[1].x); x[5] = __uint_as_float(r.w[1].y);
+        x[6] = __uint_as_float(r.w[1].z); x[7] = __uint_as_float(r.w[1].w);
+    } else {
+        const unsigned u[4] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = __uint_as_float(u[e] << 16);
+            x[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+        }
+    }
+}
+__device__ __forceinline__ void load_f8(const float *p, float (&x)[8]) {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// NSEG = segments per lane = H*D / 512 (rounded up).  Each wave walks the
+// tokens with a stride of the grid: the RMSNorm weights of its channels stay
+// in registers, and the next token's q, k, v (and RoPE table row) are loaded
+// while the current one is processed.
 template <bool F32IN, bool F32OUT, int D, int NSEG>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const int l = threadIdx.x & 63;
-    const long tok = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const long ntok = (long)a.B * a.N;
+    const long stride = (long)gridDim.x * 4;
+    long tok = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (tok >= ntok) return;
-    const int b = (int)(tok / a.N), n = (int)(tok % a.N);
     const int H = a.H, C = H * D;
     const int nseg = C / 8;
-
-    float xq[NSEG][8], xk[NSEG][8], xv[NSEG][8];
-    float sq = 0.f, sk = 0.f;
-    const size_t tbase = (size_t)tok * 3 * C;
-#pragma unroll
-    for (int i = 0; i < NSEG; ++i) {
-        const int sg = l + 64 * i;
-        if (sg < nseg) {
-            load8<F32IN>(a.qkv, tbase + sg * 8, xq[i]);
-            load8<F32IN>(a.qkv, tbase + C + sg * 8, xk[i]);
-            load8<F32IN>(a.qkv, tbase + 2 * C + sg * 8, xv[i]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                sq += xq[i][e] * xq[i][e];
-                sk += xk[i][e] * xk[i][e];
-            }
-        }
-    }
-    sq = wave_sum(sq);
-    sk = wave_sum(sk);
-    const float inv_q = 1.f / sqrtf(sq / C + a.eps);
-    const float inv_k = 1.f / sqrtf(sk / C + a.eps);
-
-    // per-token projections (wave-uniform addresses)
-    float Pq[16], Pkv[16];
-    const float *pq = a.proj_q + tok * 16, *pkv = a.proj_kv + tok * 16;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        Pq[i] = pq[i];
-        Pkv[i] = pkv[i];
-    }
     constexpr int HALF = D / 2;
 
+    // this lane's segments: channel c0 = 8 sg, head sg*8 / D, offset d0 in the
+    // head (a segment never straddles a head or a half of it); inactive
+    // segments (C not a multiple of 512) point at segment 0 and store nothing
+    int hseg[NSEG], dseg[NSEG];
+    bool act[NSEG];
+    float wq[NSEG][8], wk[NSEG][8];
 #pragma unroll
     for (int i = 0; i < NSEG; ++i) {
         const int sg = l + 64 * i;
-        // every lane takes part in the head reductions below
-        const bool act = sg < nseg;
-        const int h = act ? (sg * 8) / D : 0, d0 = act ? (sg * 8) % D : 0;
-        float kpre = 0.f, kpost = 0.f;
-        float yq[8], yk[8], yv[8];
-        if (act) {
-            float qn[8], kn[8];
+        act[i] = sg < nseg;
+        const int c0 = act[i] ? sg * 8 : 0;
+        hseg[i] = c0 / D;
+        dseg[i] = c0 % D;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wq[i][e] = wk[i][e] = 1.f;
+        if (a.qw) load_f8(a.qw + c0, wq[i]);
+        if (a.kw) load_f8(a.kw + c0, wk[i]);
+    }
+    // RoPE lanes read 8 cos and 8 sin values of their token; UCPE lanes read
+    // the same row at offset 0 and ignore it
+    const int dr = dseg[0] >= HALF ? dseg[0] - HALF : 0;   // same offset in every segment of a lane
+    static_assert(NSEG == 1 || (512 % D) == 0, "a lane's segments share their offset in the head");
+
+    Raw8<F32IN> rq[NSEG], rk[NSEG], rv[NSEG];
+    float cv[8], sv[8];
+    auto load_token = [&](long t) {
+        const size_t tbase = (size_t)t * 3 * C;
+#pragma unroll
+        for (int i = 0; i < NSEG; ++i) {
+            const int c0 = act[i] ? (l + 64 * i) * 8 : 0;
+            rq[i] = load_raw8<F32IN>(a.qkv, tbase + c0);
+            rk[i] = load_raw8<F32IN>(a.qkv, tbase + C + c0);
+            rv[i] = load_raw8<F32IN>(a.qkv, tbase + 2 * C + c0);
+        }
+        const int n = (int)(t % a.N);
+        load_f8(a.cosv + (size_t)n * HALF + dr, cv);
+        load_f8(a.sinv + (size_t)n * HALF + dr, sv);
+    };
+    load_token(tok);
+    for (; tok < ntok; tok += stride) {
+        float xq[NSEG][8], xk[NSEG][8], xv[NSEG][8], cs[8], sn[8];
+#pragma unroll
+        for (int i = 0; i < NSEG; ++i) {
+            unpack8<F32IN>(rq[i], xq[i]);
+            unpack8<F32IN>(rk[i], xk[i]);
+            unpack8<F32IN>(rv[i], xv[i]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            cs[e] = cv[e];
+            sn[e] = sv[e];
+        }
+        const int b = (int)(tok / a.N), n = (int)(tok % a.N);
+        // per-token projections (wave-uniform addresses: scalar loads)
+        float Pq[16], Pkv[16];
+        const float *pq = a.proj_q + tok * 16, *pkv = a.proj_kv + tok * 16;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            Pq[i] = pq[i];
+            Pkv[i] = pkv[i];
+        }
+        // the next token's loads go out now (past the end: the last token again)
+        load_token(tok + stride < ntok ? tok + stride : ntok - 1);
+
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int i = 0; i < NSEG; ++i)
+            if (act[i]) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sq += xq[i][e] * xq[i][e];
+                    sk += xk[i][e] * xk[i][e];
+                }
+            }
+        sq = wave_sum(sq);
+        sk = wave_sum(sk);
+        const float inv_q = 1.f / sqrtf(sq / C + a.eps);
+        const float inv_k = 1.f / sqrtf(sk / C + a.eps);
+
+#pragma unroll
+        for (int i = 0; i < NSEG; ++i) {
+            const int h = hseg[i], d0 = dseg[i];
+            float kpre = 0.f, kpost = 0.f;
+            float qn[8], kn[8], yq[8], yk[8], yv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int c = h * D + d0 + e;
-                const float wq = a.qw ? a.qw[c] : 1.f, wk = a.kw ? a.kw[c] : 1.f;
-                const float vq = xq[i][e] * inv_q * wq;
-                const float vk = xk[i][e] * inv_k * wk;
+                const float vq = xq[i][e] * inv_q * wq[i][e];
+                const float vk = xk[i][e] * inv_k * wk[i][e];
                 qn[e] = vq > 0.f ? vq : 0.f;
                 kn[e] = (vk > 0.f ? vk : 0.f) * a.k_scale;
                 kpre += kn[e] * kn[e];
@@ -154,35 +225,30 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
                         yv[g * 4 + r] = av;
                     }
             } else {
-                const float *cs = a.cosv + (size_t)n * HALF + (d0 - HALF);
-                const float *sn = a.sinv + (size_t)n * HALF + (d0 - HALF);
-                float cv[8], sv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    cv[e] = cs[e];
-                    sv[e] = sn[e];
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    yq[e] = qn[e] * cv[e] + qn[e ^ 1] * sv[e];
-                    yk[e] = kn[e] * cv[e] + kn[e ^ 1] * sv[e];
-                    yv[e] = xv[i][e] * cv[e] + xv[i][e ^ 1] * sv[e];
+                    yq[e] = qn[e] * cs[e] + qn[e ^ 1] * sn[e];
+                    yk[e] = kn[e] * cs[e] + kn[e ^ 1] * sn[e];
+                    yv[e] = xv[i][e] * cs[e] + xv[i][e ^ 1] * sn[e];
                 }
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) kpost += yk[e] * yk[e];
-            const size_t o = (((size_t)b * H + h) * a.N + n) * D + d0;
-            store8<F32OUT>(a.qo, o, yq);
-            store8<F32OUT>(a.ko, o, yk);
-            store8<F32OUT>(a.vo, o, yv);
-        }
-        kpre = head_sum<D>(kpre);
-        kpost = head_sum<D>(kpost);
-        if (act && (d0 == 0)) {
-            const size_t so = ((size_t)b * H + h) * a.N + n;
-            a.pre[so] = kpre;
-            a.post[so] = kpost;
-            if (a.infl) a.infl[so] = fmaxf(kpost, 1e-12f) / fmaxf(kpre, 1e-12f);
+            if (act[i]) {
+                const size_t o = (((size_t)b * H + h) * a.N + n) * D + d0;
+                store8<F32OUT>(a.qo, o, yq);
+                store8<F32OUT>(a.ko, o, yk);
+                store8<F32OUT>(a.vo, o, yv);
+            }
+            // every lane takes part in the head reductions
+            kpre = head_sum<D>(act[i] ? kpre : 0.f);
+            kpost = head_sum<D>(act[i] ? kpost : 0.f);
+            if (act[i] && d0 == 0) {
+                const size_t so = ((size_t)b * H + h) * a.N + n;
+                a.pre[so] = kpre;
+                a.post[so] = kpost;
+                if (a.infl) a.infl[so] = fmaxf(kpost, 1e-12f) / fmaxf(kpre, 1e-12f);
+            }
         }
     }
 }
@@ -192,11 +258,15 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
     const long ntok = (long)a.B * a.N;
     const int C = a.H * D;
     const int nseg = C / 8;
-    const int blocks = (int)((ntok + 3) / 4);
-    if (nseg <= 64) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 1>), dim3(blocks), dim3(256), 0, s, a);
-    else if (nseg <= 128) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 2>), dim3(blocks), dim3(256), 0, s, a);
-    else if (nseg <= 256) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 4>), dim3(blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 8>), dim3(blocks), dim3(256), 0, s, a);
+    // about four tokens per wave: weights stay resident, loads overlap
+    long blocks = (ntok + 15) / 16;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 65535) blocks = 65535;
+    const dim3 grid((unsigned)blocks);
+    if (nseg <= 64) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 1>), grid, dim3(256), 0, s, a);
+    else if (nseg <= 128) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 2>), grid, dim3(256), 0, s, a);
+    else if (nseg <= 256) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 8>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -223,12 +293,12 @@ extern "C" int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_n
                     k_post_sq,
                 GDN_EINVAL, "%s: null tensor pointer", name);
     GDN_REQUIRE(gdn::aligned(qkv, 16) && gdn::aligned(q_out, 16) && gdn::aligned(k_out, 16) &&
-                    gdn::aligned(v_out, 16),
-                GDN_EINVAL, "%s: qkv and the q/k/v outputs must be 16-byte aligned", name);
-    GDN_REQUIRE(gdn::aligned(proj_q, 4) && gdn::aligned(proj_kv, 4) && gdn::aligned(rope_cos, 4) &&
-                    gdn::aligned(rope_sin, 4) && gdn::aligned(k_pre_sq, 4) && gdn::aligned(k_post_sq, 4) &&
-                    (!inflation_sq || gdn::aligned(inflation_sq, 4)) && (!q_norm_w || gdn::aligned(q_norm_w, 4)) &&
-                    (!k_norm_w || gdn::aligned(k_norm_w, 4)),
+                    gdn::aligned(v_out, 16) && gdn::aligned(rope_cos, 16) && gdn::aligned(rope_sin, 16) &&
+                    (!q_norm_w || gdn::aligned(q_norm_w, 16)) && (!k_norm_w || gdn::aligned(k_norm_w, 16)),
+                GDN_EINVAL, "%s: qkv, the q/k/v outputs, the norm weights and the RoPE tables must be 16-byte aligned",
+                name);
+    GDN_REQUIRE(gdn::aligned(proj_q, 4) && gdn::aligned(proj_kv, 4) && gdn::aligned(k_pre_sq, 4) &&
+                    gdn::aligned(k_post_sq, 4) && (!inflation_sq || gdn::aligned(inflation_sq, 4)),
                 GDN_EINVAL, "%s: float tensors must be 4-byte aligned", name);
     gdn::PrepArgs a;
     a.qkv = qkv;

@@ -177,7 +177,9 @@ size_t gdn_recurrent_fwd_workspace_bytes(int B, int H, int F, int S, int D, int 
  *                    dtype; GDN_DTYPE_F32 keeps the full fp32 result)
  *   k_pre_sq, k_post_sq (B, H, N)    float32
  *   inflation_sq     (B, H, N)       float32, nullable (not stored)
- * Supported: D in {16, 32, 64, 128}; H*D <= 4096.
+ * Supported: D in {16, 32, 64, 128}; H*D <= 4096.  qkv, the q/k/v outputs,
+ * the norm weights and the RoPE tables must be 16-byte aligned (they are
+ * read and written as 16-byte vectors); the other float tensors 4-byte.
  */
 int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_norm_w,
              const float *proj_q, const float *proj_kv,
