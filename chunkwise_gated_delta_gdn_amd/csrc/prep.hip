@@ -48,17 +48,34 @@ __device__ __forceinline__ void store8(void *base, size_t elem, const float (&x)
     }
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+// Sums over lane groups by DPP moves (VALU, no LDS round trip): within a
+// quad by quad permutations, within 8 and 16 lanes by the half-row and row
+// mirrors (after the smaller sums every lane of a group holds the group
+// total, so a mirrored partner from the other half gives the wider total).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int W>                                // W in {1, 2, 4, 8, 16}: consecutive lanes
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (W >= 2) x = dpp_add<0xB1>(x);     // quad_perm [1,0,3,2]
+    if constexpr (W >= 4) x = dpp_add<0x4E>(x);     // quad_perm [2,3,0,1]
+    if constexpr (W >= 8) x = dpp_add<0x141>(x);    // row_half_mirror
+    if constexpr (W >= 16) x = dpp_add<0x140>(x);   // row_mirror
     return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x = group_sum<16>(x);
+    const int xi = __builtin_bit_cast(int, x);
+    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16))) +
+           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48)));
 }
 
 template <int D>
 __device__ __forceinline__ float head_sum(float x) {     // over the D/8 lanes of one head
-#pragma unroll
-    for (int off = (D / 8) / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
+    return group_sum<D / 8>(x);
 }
 
 // A token's raw q, k or v segment (8 values) as loaded: bf16 in one 16-byte
