@@ -109,9 +109,10 @@ def _prepare(name, dev):
         h0 = None if d["h0"] is None else f32(d["h0"])
 
         def step():
-            return gdn.gdn_chunk_fwd(q, k, v, beta, g, 1.0, h0, chunk=wl["chunk"], out_dtype=torch.float32)
+            return gdn.gdn_chunk_fwd(q, k, v, beta, g, 1.0, h0, chunk=wl["chunk"], out_dtype=torch.bfloat16)
         B, T, H = wl["B"], wl["T"], wl["H"]
-        nbytes, flops = algorithmic_work(B, T, H, wl["Dk"], wl["Dv"], wl["chunk"], with_h0=h0 is not None)
+        nbytes, flops = algorithmic_work(B, T, H, wl["Dk"], wl["Dv"], wl["chunk"], out_bytes=2,
+                                         with_h0=h0 is not None)
         return d, step, B * T, nbytes, flops
     if wl["kind"] == "deltaproduct":
         q, k, v = bf(d["q"]), bf(d["k"]), bf(d["v"])
@@ -119,9 +120,10 @@ def _prepare(name, dev):
         K = wl["r"] * wl["dk"]
 
         def step():
-            return gdn.deltaproduct_chunk_fwd(q, k, v, beta, g, d["mask"], K ** -0.5, chunk=wl["chunk"])
+            return gdn.deltaproduct_chunk_fwd(q, k, v, beta, g, d["mask"], K ** -0.5, chunk=wl["chunk"],
+                                              out_dtype=torch.bfloat16)
         B, T, H, r, Dv = wl["B"], wl["T"], wl["H"], wl["r"], wl["Dv"]
-        nbytes = B * T * H * (2 * K + Dv) * 2 + B * T * H * (r + 1) * 4 + B * T * H * Dv * 4 + B * H * K * Dv * 4
+        nbytes = B * T * H * (2 * K + Dv) * 2 + B * T * H * (r + 1) * 4 + B * T * H * Dv * 2 + B * H * K * Dv * 4
         C, dk = wl["chunk"], wl["dk"]
         NR = C * r
         # per chunk: Gram r*C^2*dk, W/U NR^2*(K+Dv), state 2*NR*K*Dv, output 2*C*K*Dv + r*C^2*dk, all x2 FLOP
@@ -204,12 +206,12 @@ def main():
     if args.workload in ("gdn", "gdn_long"):
         metric = "tokens/sec of chunkwise gated-delta fwd (B*T/s) at H=16, D=128"
         desc = (f"{args.workload}: B={wl['B']} H={wl['H']} T={wl['T']} Dk=Dv={wl['Dk']} chunk={wl['chunk']}, "
-                f"bf16 q/k/v, fp32 gates/state/output, " + ("h0~N(0,0.02^2)" if wl["h0_std"] else "h0=0"))
+                f"bf16 q/k/v and output, fp32 gates and state, " + ("h0~N(0,0.02^2)" if wl["h0_std"] else "h0=0"))
         kernel = "gdn_chunk_fwd = chunk_prep2_kernel + chunk_chain1_kernel <KD=128, C=64>"
         traffic = measured_traffic(kernel_source_hash()) if args.workload == "gdn" else None
     elif args.workload == "deltaproduct":
         metric = "tokens/sec of chunkwise gated DeltaProduct fwd (B*T/s)"
-        desc = "deltaproduct: B=2 H=8 T=2048 K=2x128 Dv=128 chunk=32 r=2, bf16, lower-triangular step mask"
+        desc = "deltaproduct: B=2 H=8 T=2048 K=2x128 Dv=128 chunk=32 r=2, bf16 q/k/v and output, lower-triangular step mask"
         kernel = "deltaproduct_chunk_fwd = chunk_solve_kernel + chunk_chain_kernel <bf16, KD=256, C=32, R=2>"
         traffic = None
     else:
