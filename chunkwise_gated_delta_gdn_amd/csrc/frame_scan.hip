@@ -5,14 +5,16 @@
 // so the frame update is affine in S:
 //   S_f = P + sum_s beta_s k_s (v_s - P^T k_s)^T = (I - G_f) P + H_f,
 //   G_f = sum_{s in f} beta_s k_s k_s^T,   H_f = sum_{s in f} beta_s k_s v_s^T
-// (the matrix form of the page's _torch_cam_scan_single_chunk).  Three
-// kernels:
-//   frame_gram_kernel   parallel over (b, h, f, token range): partial G_f and
+// (the matrix form of the page's _torch_cam_scan_single_chunk).  Kernels:
+//   frame_gram_bf16_kernel / frame_gram_kernel (fp32 inputs)
+//                       parallel over (b, h, f, token range): partial G_f and
 //                       H_f from K^T diag(beta) K and K^T diag(beta) V (MFMA);
+//   frame_reduce_kernel sums the partials of the token ranges;
 //   frame_state_kernel  per (b, h, 16-column slice of S), sequential over
 //                       frames: S_f = e^{g_f} (S - G_f S) + H_f in fp32 (fp32
 //                       MFMA), stores S_f and the final state;
-//   frame_out_kernel    parallel over (b, h, f, 64-token tile):
+//   frame_out_bf16_kernel / frame_out_kernel (fp32 inputs, D = 16)
+//                       parallel over (b, h, f, token tile):
 //                       out_s = scale * S_f^T q_s.
 // Inputs q, k, v (B, H, N, D) as written by gdn_prep; out (B, H, N, D) fp32.
 #include <math.h>
@@ -27,13 +29,14 @@ struct FrameArgs {
     const void *q, *k, *v;
     const float *beta, *g, *h0;
     float *hT, *out;
-    float *part;     // [B*H*F][NSPLIT][2][D][D] partial G_f, H_f
-    float *sf;       // [B*H][F][D][D] state after each frame
+    float *part;     // [B*H*F][nsplit][2][D][D] partial G_f, H_f (= gh when nsplit is 1)
+    float *gh;       // [B*H*F][2][D][D] G_f, H_f
+    float *sf;       // [B*H][F][D][D] state after each frame, transposed ([column][row])
     int B, H, F, S, nsplit, spl;
     float scale;
 };
 
-constexpr int TS = 32;   // tokens per gram step
+constexpr int TS = 32;   // tokens per step of the fp32 gram kernel
 
 template <bool F32IN>
 struct OpT { typedef u16 type; };
@@ -145,13 +148,211 @@ __global__ __launch_bounds__(256) void frame_gram_kernel(FrameArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// sequential frame pass on a 16-column slice of the state
+// partial G_f and H_f for bf16 inputs.  G = K^T diag(beta) K and
+// H = K^T diag(beta) V contract over tokens, so both MFMA operands need 8
+// consecutive tokens of one feature per lane: the token rows are staged
+// row-major in LDS (64 tokens a step, two buffers) and read back transposed
+// with ds_read_b64_tr_b16.  A = K^T (exact bf16); B = beta (.) K or
+// beta (.) V, scaled in fp32 after the transposed read and split hi + lo.
+// Wave w owns whole column tiles ("jobs": matrix G or H, column tile tj);
+// every wave reads the A fragments of all row tiles.
+//
+// Loads run one round (SPW steps) ahead in two register sets.  Every load is
+// unconditional (rows past the range end read the range's last row, whose
+// beta is replaced by 0, so they add nothing) so that the wait before
+// staging a set counts only that set's loads.
+// ---------------------------------------------------------------------------
+constexpr int TSG = 64;      // tokens per staged step of the bf16 gram kernel
+// steps per round (register budget of the two sets)
+template <int D>
+constexpr int gram_steps() { return D == 128 ? 1 : 2; }
+constexpr int gram_round(int D) { return (D == 128 ? 1 : 2) * TSG; }
+
+template <int D>
+__global__ __launch_bounds__(256) void frame_gram_bf16_kernel(FrameArgs a) {
+    constexpr int NT1 = D / 16;                 // row tiles = column tiles of one matrix
+    constexpr int NJOB = 2 * NT1, JPW = (NJOB + 3) / 4;
+    // row stride: 4 rows of 32 bytes (one 16-lane transposed read) fall on
+    // distinct banks for 32 or 64 banks of 4 bytes
+    constexpr int LDR = D == 16 ? 16 : D + 16;
+    constexpr int SEGS = D / 8;                 // 16-byte pieces per token row
+    constexpr int PPT = 2 * TSG * SEGS / 256;   // pieces of k and v per thread per step
+    constexpr int SPW = gram_steps<D>(), RND = SPW * TSG;
+    static_assert(PPT * 256 == 2 * TSG * SEGS, "whole pieces per thread");
+    __shared__ __attribute__((aligned(16))) u16 Ks[2][TSG * LDR], Vs[2][TSG * LDR];
+    __shared__ __attribute__((aligned(16))) float Bs[2][TSG];
+    const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int unit = blockIdx.x / a.nsplit, sp = blockIdx.x % a.nsplit;
+    const size_t N = (size_t)a.F * a.S;
+    const int s_lo = sp * a.spl, s_hi = min(a.S, (sp + 1) * a.spl);
+    const int nrnd = (s_hi - s_lo + RND - 1) / RND;
+    const size_t row0 = (size_t)(unit / a.F) * N + (size_t)(unit % a.F) * a.S;   // frame start
+    const u16 *kin = reinterpret_cast<const u16 *>(a.k), *vin = reinterpret_cast<const u16 *>(a.v);
+
+    floatx4 acc[JPW][NT1];
+#pragma unroll
+    for (int jb = 0; jb < JPW; ++jb)
+#pragma unroll
+        for (int ti = 0; ti < NT1; ++ti) acc[jb][ti] = zero4();
+
+    struct Set {                                // native vectors keep the sets in registers
+        u32x4 x[SPW][PPT];
+        float b[SPW];
+    };
+    Set sa, sb;
+    auto gload = [&](Set &st, int rnd) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < SPW; ++u) {
+            const int s0 = s_lo + rnd * RND + u * TSG;
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                const int p = tid + 256 * i;
+                const int mat = p / (TSG * SEGS), rem = p % (TSG * SEGS), r = rem / SEGS, sg = rem % SEGS;
+                const int s = min(s0 + r, s_hi - 1);
+                st.x[u][i] = *reinterpret_cast<const u32x4 *>((mat ? vin : kin) + (row0 + s) * D + sg * 8);
+            }
+            const int s = s0 + (tid & (TSG - 1));
+            const float bt = a.beta[row0 + min(s, s_hi - 1)];
+            st.b[u] = s < s_hi ? bt : 0.f;
+        }
+    };
+    auto lstore = [&](const Set &st, int u, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = tid + 256 * i;
+            const int mat = p / (TSG * SEGS), rem = p % (TSG * SEGS), r = rem / SEGS, sg = rem % SEGS;
+            *reinterpret_cast<u32x4 *>((mat ? Vs[buf] : Ks[buf]) + r * LDR + sg * 8) = st.x[u][i];
+        }
+        if (tid < TSG) Bs[buf][tid] = st.b[u];
+    };
+    auto compute = [&](int buf) __attribute__((always_inline)) {
+        const u16 *ks = Ks[buf], *vs = Vs[buf];
+#pragma unroll
+        for (int kk = 0; kk < TSG / 32; ++kk) {
+            // lane (g, c16) receives tokens kk*32 + 8g + e (e < 8) of one column
+            const int ra = kk * 32 + 8 * g + (c16 >> 2), cq = 4 * (c16 & 3);
+            bf16x8 af[NT1];
+#pragma unroll
+            for (int ti = 0; ti < NT1; ++ti) {
+                const uint2 x0 = __builtin_bit_cast(uint2, ld_tr16(ks + ra * LDR + ti * 16 + cq));
+                const uint2 x1 = __builtin_bit_cast(uint2, ld_tr16(ks + (ra + 4) * LDR + ti * 16 + cq));
+                af[ti] = __builtin_bit_cast(bf16x8, uint4{x0.x, x0.y, x1.x, x1.y});
+            }
+            const float4 b0 = *reinterpret_cast<const float4 *>(&Bs[buf][kk * 32 + 8 * g]);
+            const float4 b1 = *reinterpret_cast<const float4 *>(&Bs[buf][kk * 32 + 8 * g + 4]);
+            const float bt[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int jb = 0; jb < JPW; ++jb) {
+                const int job = w + 4 * jb;
+                if (job < NJOB) {
+                    const int tj = job % NT1;
+                    const u16 *src = job < NT1 ? ks : vs;
+                    const uint2 x0 = __builtin_bit_cast(uint2, ld_tr16(src + ra * LDR + tj * 16 + cq));
+                    const uint2 x1 = __builtin_bit_cast(uint2, ld_tr16(src + (ra + 4) * LDR + tj * 16 + cq));
+                    const unsigned u[4] = {x0.x, x0.y, x1.x, x1.y};
+                    uint4 hi, lo;
+                    unsigned *ph = &hi.x, *pl = &lo.x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float y0 = __uint_as_float(u[e] << 16) * bt[2 * e];
+                        const float y1 = __uint_as_float(u[e] & 0xffff0000u) * bt[2 * e + 1];
+                        split2_bf16(y0, y1, ph[e], pl[e]);
+                    }
+                    const bf16x8 bh = __builtin_bit_cast(bf16x8, hi), bl = __builtin_bit_cast(bf16x8, lo);
+#pragma unroll
+                    for (int ti = 0; ti < NT1; ++ti) {
+                        acc[jb][ti] = mfma32(af[ti], bh, acc[jb][ti]);
+                        acc[jb][ti] = mfma32(af[ti], bl, acc[jb][ti]);
+                    }
+                }
+            }
+        }
+    };
+    // Step n is staged into buffer n & 1 and multiplied after one barrier;
+    // the barrier of step n also ends every read of the buffer that step n+1
+    // overwrites (read by step n-1).  Rounds come in pairs (set a, then set
+    // b at step offset SPW), so buffer parities are fixed at compile time.
+    // Round conditions are uniform over the workgroup.
+    auto consume = [&](const Set &st, int base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < SPW; ++u) {
+            lstore(st, u, (base + u) & 1);
+            lds_barrier();
+            compute((base + u) & 1);
+        }
+    };
+    gload(sa, 0);
+    for (int rnd = 0; rnd < nrnd; rnd += 2) {
+        gload(sb, min(rnd + 1, nrnd - 1));
+        consume(sa, 0);
+        gload(sa, min(rnd + 2, nrnd - 1));
+        if (rnd + 1 < nrnd) consume(sb, SPW);
+    }
+    lds_barrier();
+    float *dst = a.part + ((size_t)unit * a.nsplit + sp) * 2 * D * D;
+#pragma unroll
+    for (int jb = 0; jb < JPW; ++jb) {
+        const int job = w + 4 * jb;
+        if (job < NJOB) {
+            const int kind = job / NT1, tj = job % NT1;
+#pragma unroll
+            for (int ti = 0; ti < NT1; ++ti)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dst[(size_t)kind * D * D + (ti * 16 + 4 * g + e) * D + tj * 16 + c16] = acc[jb][ti][e];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// G_f, H_f = sum of the partials over token ranges (one float4 per thread)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void frame_reduce_kernel(FrameArgs a) {
+    constexpr size_t PU4 = 2 * D * D / 4;       // float4 per unit
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t units = (size_t)a.B * a.H * a.F;
+    if (idx >= units * PU4) return;
+    const size_t unit = idx / PU4, e = idx % PU4;
+    const float4 *p = reinterpret_cast<const float4 *>(a.part) + unit * a.nsplit * PU4 + e;
+    float4 s = p[0];
+    for (int sp = 1; sp < a.nsplit; ++sp) {
+        const float4 x = p[sp * PU4];
+        s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
+    }
+    reinterpret_cast<float4 *>(a.gh)[idx] = s;
+}
+
+// G_f (all of it) and the H_f slice of columns j0 .. j0+15 as float4 per
+// thread (row idx / 4 of H, columns j0 + 4 (idx % 4) ..).
+template <int D, int NG4, int NH4>
+__device__ __forceinline__ void state_fetch(const float *ghf, int j0, int tid, floatx4 (&gr)[NG4],
+                                            floatx4 (&hr)[NH4]) {
+    const floatx4 *gp = reinterpret_cast<const floatx4 *>(ghf);
+#pragma unroll
+    for (int i = 0; i < NG4; ++i) {
+        const int idx = tid + 256 * i;
+        if (idx < D * D / 4) gr[i] = gp[idx];
+    }
+#pragma unroll
+    for (int i = 0; i < NH4; ++i) {
+        const int idx = tid + 256 * i;
+        if (idx < D * 4) hr[i] = gp[(D * D + (idx >> 2) * D + j0) / 4 + (idx & 3)];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// sequential frame pass on a 16-column slice of the state.  G_{f+1} and the
+// H_{f+1} slice are loaded into registers while frame f is computed.  S_f is
+// stored transposed ([column][row]) for the output kernels.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
     constexpr int LDG = D + 4, LDS_ = 16 + 4;
     constexpr int NRT = D / 16, PERW = (NRT + 3) / 4;
-    __shared__ __attribute__((aligned(16))) float Gs[D * LDG], Sl[D * LDS_];
+    constexpr int NG4 = (D * D / 4 + 255) / 256, NH4 = (D * 4 + 255) / 256;   // float4 per thread
+    __shared__ __attribute__((aligned(16))) float Gs[D * LDG], Sl[D * LDS_], Hs[D * LDS_];
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ncb = D / 16;
@@ -167,19 +368,22 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
             for (int e = 0; e < 4; ++e)
                 S[n][e] = a.h0[((size_t)bh * D + ti * 16 + 4 * (l >> 4) + e) * D + j0 + (l & 15)];
     }
+    floatx4 gr[NG4], hr[NH4];    // native vectors: arrays of HIP float4 structs end up in scratch
+    state_fetch<D, NG4, NH4>(a.gh + (size_t)bh * a.F * 2 * D * D, j0, tid, gr, hr);
     for (int f = 0; f < a.F; ++f) {
         const size_t unit = (size_t)bh * a.F + f;
-        const float *pp = a.part + unit * a.nsplit * 2 * D * D;
-        // G_f (all of it) into LDS, summed over the token ranges
-        for (int idx = tid; idx < D * D / 4; idx += 256) {
-            float4 sum = {0.f, 0.f, 0.f, 0.f};
-            for (int sp = 0; sp < a.nsplit; ++sp) {
-                const float4 x = reinterpret_cast<const float4 *>(pp + (size_t)sp * 2 * D * D)[idx];
-                sum.x += x.x; sum.y += x.y; sum.z += x.z; sum.w += x.w;
+#pragma unroll
+        for (int i = 0; i < NG4; ++i) {
+            const int idx = tid + 256 * i;
+            if (idx < D * D / 4) {
+                const int r = (idx * 4) / D, c = (idx * 4) % D;
+                *reinterpret_cast<floatx4 *>(Gs + r * LDG + c) = gr[i];
             }
-            const int i = (idx * 4) / D, c = (idx * 4) % D;
-            float *gd = Gs + i * LDG + c;
-            gd[0] = sum.x; gd[1] = sum.y; gd[2] = sum.z; gd[3] = sum.w;
+        }
+#pragma unroll
+        for (int i = 0; i < NH4; ++i) {
+            const int idx = tid + 256 * i;
+            if (idx < D * 4) *reinterpret_cast<floatx4 *>(Hs + (idx >> 2) * LDS_ + 4 * (idx & 3)) = hr[i];
         }
         // current state slice into LDS as the B operand ([k][col])
 #pragma unroll
@@ -189,7 +393,8 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Sl[(ti * 16 + 4 * (l >> 4) + e) * LDS_ + (l & 15)] = S[n][e];
         }
-        __syncthreads();
+        lds_barrier();                  // the prefetch below stays in flight across barriers
+        if (f + 1 < a.F) state_fetch<D, NG4, NH4>(a.gh + ((size_t)bh * a.F + f + 1) * 2 * D * D, j0, tid, gr, hr);
         const float dec = expf(a.g[unit]);
 #pragma unroll
         for (int n = 0; n < PERW; ++n) {
@@ -197,23 +402,14 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
             if (ti < NRT) {
                 floatx4 gs = zero4();
                 mma_f32_bn(gs, Gs + ti * 16 * LDG, LDG, Sl, LDS_, D);
-                float hv[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = ti * 16 + 4 * (l >> 4) + e;
-                    float hsum = 0.f;
-                    for (int sp = 0; sp < a.nsplit; ++sp)
-                        hsum += pp[(size_t)sp * 2 * D * D + (size_t)D * D + i * D + j0 + (l & 15)];
-                    hv[e] = hsum;
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    S[n][e] = dec * (S[n][e] - gs[e]) + hv[e];
-                    a.sf[(unit * D + ti * 16 + 4 * (l >> 4) + e) * D + j0 + (l & 15)] = S[n][e];
-                }
+                for (int e = 0; e < 4; ++e)
+                    S[n][e] = dec * (S[n][e] - gs[e]) + Hs[(ti * 16 + 4 * (l >> 4) + e) * LDS_ + (l & 15)];
+                *reinterpret_cast<float4 *>(a.sf + (unit * D + j0 + (l & 15)) * D + ti * 16 + 4 * (l >> 4)) =
+                    float4{S[n][0], S[n][1], S[n][2], S[n][3]};
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
     if (a.hT) {
 #pragma unroll
@@ -229,6 +425,7 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
 
 // ---------------------------------------------------------------------------
 // out_s = scale * S_f^T q_s for a tile of up to 64 tokens of one frame
+// (general path: fp32 inputs, D = 16)
 // ---------------------------------------------------------------------------
 template <bool F32IN, int D>
 __global__ __launch_bounds__(256) void frame_out_kernel(FrameArgs a) {
@@ -246,12 +443,9 @@ __global__ __launch_bounds__(256) void frame_out_kernel(FrameArgs a) {
     const size_t row0 = (size_t)bh * N + (size_t)f * a.S + (size_t)tt * TT;
     const int nrows = min(TT, a.S - tt * TT);
 
-    // S_f transposed ([j][i]) as the B operand
+    // S_f transposed ([j][i], as stored) as the B operand
     const float *sf = a.sf + (size_t)unit * D * D;
-    for (int idx = tid; idx < D * D; idx += 256) {
-        const int i = idx / D, j = idx % D;
-        put_op<F32IN>(SH, SL, j * LDT + i, sf[idx]);
-    }
+    for (int idx = tid; idx < D * D; idx += 256) put_op<F32IN>(SH, SL, (idx / D) * LDT + idx % D, sf[idx]);
     constexpr int SEGS = D / 8;
     for (int idx = tid; idx < TT * SEGS; idx += 256) {
         const int r = idx / SEGS, i0 = (idx % SEGS) * 8;
@@ -290,32 +484,125 @@ __global__ __launch_bounds__(256) void frame_out_kernel(FrameArgs a) {
     }
 }
 
-int frame_nsplit(int B, int H, int F, int S) {
+// ---------------------------------------------------------------------------
+// out for bf16 inputs and D >= 32, computed transposed: out^T = S_f^T Q^T.
+// A = S_f^T (hi + lo bf16, staged once per workgroup in LDS from the stored
+// transpose), B = Q^T: lane (g, c16) needs 8 consecutive features of token
+// c16, one 16-byte load straight from the (token, D) rows.  The accumulator
+// gives each lane 4 consecutive outputs of one token: one 16-byte store.
+// A workgroup covers OUT_TOK tokens of one frame, each wave 64 of them.
+// ---------------------------------------------------------------------------
+constexpr int OUT_TOK = 256;
+
+template <int D>
+__global__ __launch_bounds__(256) void frame_out_bf16_kernel(FrameArgs a) {
+    constexpr int NT1 = D / 16, NK = D / 32, LDT = D + 8, SUB = 4;   // SUB tiles of 16 tokens per wave
+    static_assert(D >= 32, "32-deep k steps");
+    __shared__ __attribute__((aligned(16))) u16 SH[D * LDT], SL[D * LDT];
+    const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ntt = (a.S + OUT_TOK - 1) / OUT_TOK;
+    const int unit = blockIdx.x / ntt, tb = blockIdx.x % ntt;
+    const size_t N = (size_t)a.F * a.S;
+    const size_t row0 = (size_t)(unit / a.F) * N + (size_t)(unit % a.F) * a.S;
+    const int t0 = tb * OUT_TOK + w * (SUB * 16);          // this wave's first token in the frame
+    const u16 *qin = reinterpret_cast<const u16 *>(a.q);
+
+    // Q^T fragments of this wave's tokens go out first
+    bf16x8 bq[SUB][NK];
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+        const int t = t0 + u * 16 + c16;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            uint4 x = uint4{0u, 0u, 0u, 0u};
+            if (t < a.S) x = *reinterpret_cast<const uint4 *>(qin + (row0 + t) * D + kk * 32 + 8 * g);
+            bq[u][kk] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+    // S_f^T rows (output feature i, input features contiguous) split into LDS
+    const float4 *sf = reinterpret_cast<const float4 *>(a.sf + (size_t)unit * D * D);
+    for (int idx = tid; idx < D * D / 4; idx += 256) {
+        const float4 x = sf[idx];
+        const int r = (idx * 4) / D, c = (idx * 4) % D;
+        uint2 hi, lo;
+        split2_bf16(x.x, x.y, hi.x, lo.x);
+        split2_bf16(x.z, x.w, hi.y, lo.y);
+        *reinterpret_cast<uint2 *>(SH + r * LDT + c) = hi;
+        *reinterpret_cast<uint2 *>(SL + r * LDT + c) = lo;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ti = 0; ti < NT1; ++ti) {
+        bf16x8 ah[NK], al[NK];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            const int o = (ti * 16 + c16) * LDT + kk * 32 + 8 * g;
+            ah[kk] = ld8(SH + o);
+            al[kk] = ld8(SL + o);
+        }
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) {
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                acc = mfma32(ah[kk], bq[u][kk], acc);
+                acc = mfma32(al[kk], bq[u][kk], acc);
+            }
+            const int t = t0 + u * 16 + c16;
+            if (t < a.S)
+                *reinterpret_cast<float4 *>(a.out + (row0 + t) * D + ti * 16 + 4 * g) =
+                    float4{a.scale * acc[0], a.scale * acc[1], a.scale * acc[2], a.scale * acc[3]};
+        }
+    }
+}
+
+// Token ranges of the gram kernels: enough workgroups to fill the chip
+// (about three per compute unit), whole rounds of staged steps per range.
+int frame_nsplit(int B, int H, int F, int S, int D, int *spl_out) {
     const long units = (long)B * H * F;
-    const int maxsp = (S + TS - 1) / TS;
-    long want = units > 0 ? (512 + units - 1) / units : 1;
+    const int RND = gram_round(D);
+    const int maxsp = (S + RND - 1) / RND;
+    long want = units > 0 ? (768 + units - 1) / units : 1;
     if (want > maxsp) want = maxsp;
     if (want < 1) want = 1;
-    return (int)want;
+    const int per = (int)((S + want - 1) / want);
+    const int spl = (per + RND - 1) / RND * RND;
+    if (spl_out) *spl_out = spl;
+    return (S + spl - 1) / spl;
 }
 
 size_t frame_workspace(int B, int H, int F, int S, int D) {
-    const int ns = frame_nsplit(B, H, F, S);
+    const int ns = frame_nsplit(B, H, F, S, D, nullptr);
     const size_t units = (size_t)B * H * F;
-    return units * ns * 2 * D * D * sizeof(float) + units * D * D * sizeof(float);
+    // partials (only with more than one range), G_f and H_f, S_f
+    return (ns > 1 ? units * ns * 2 * D * D : 0) * sizeof(float) + units * 2 * D * D * sizeof(float) +
+           units * D * D * sizeof(float);
 }
 
 template <bool F32IN, int D>
 hipError_t launch_frame(FrameArgs a, hipStream_t s) {
     const int units = a.B * a.H * a.F;
-    hipLaunchKernelGGL((frame_gram_kernel<F32IN, D>), dim3(units * a.nsplit), dim3(256), 0, s, a);
+    if constexpr (F32IN) hipLaunchKernelGGL((frame_gram_kernel<true, D>), dim3(units * a.nsplit), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((frame_gram_bf16_kernel<D>), dim3(units * a.nsplit), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.nsplit > 1) {
+        const size_t n4 = (size_t)units * 2 * D * D / 4;
+        hipLaunchKernelGGL((frame_reduce_kernel<D>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((frame_state_kernel<D>), dim3(a.B * a.H * (D / 16)), dim3(256), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int ntt = (a.S + 63) / 64;
-    hipLaunchKernelGGL((frame_out_kernel<F32IN, D>), dim3(units * ntt), dim3(256), 0, s, a);
+    if constexpr (!F32IN && D >= 32) {
+        const int ntt = (a.S + OUT_TOK - 1) / OUT_TOK;
+        hipLaunchKernelGGL((frame_out_bf16_kernel<D>), dim3(units * ntt), dim3(256), 0, s, a);
+    } else {
+        const int ntt = (a.S + 63) / 64;
+        hipLaunchKernelGGL((frame_out_kernel<F32IN, D>), dim3(units * ntt), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -376,12 +663,13 @@ extern "C" int gdn_recurrent_fwd(const void *q, const void *k, const void *v, co
     a.H = H;
     a.F = F;
     a.S = S;
-    a.nsplit = gdn::frame_nsplit(B, H, F, S);
-    a.spl = ((S + a.nsplit - 1) / a.nsplit + gdn::TS - 1) / gdn::TS * gdn::TS;
+    a.nsplit = gdn::frame_nsplit(B, H, F, S, D, &a.spl);
     a.scale = scale;
     const size_t units = (size_t)B * H * F;
-    a.part = reinterpret_cast<float *>(workspace);
-    a.sf = a.part + units * a.nsplit * 2 * D * D;
+    float *ws = reinterpret_cast<float *>(workspace);
+    a.gh = ws;
+    a.sf = a.gh + units * 2 * D * D;
+    a.part = a.nsplit > 1 ? a.sf + units * D * D : a.gh;
     const bool f32 = dtype == GDN_DTYPE_F32;
     hipError_t e;
     switch (D) {

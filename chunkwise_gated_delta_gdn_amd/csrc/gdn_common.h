@@ -63,6 +63,18 @@ __device__ __forceinline__ shortx4 ld_tr16(const u16 *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p));
 }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations (lgkmcnt(0)) but leaves its global loads and stores in flight
+// (vmcnt and expcnt at their maxima), unlike __syncthreads(), which also
+// waits for every outstanding global operation.  The empty asm statements
+// keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);     // vmcnt(63) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
