@@ -33,6 +33,7 @@ struct FrameArgs {
     float *gh;       // [B*H*F][2][D][D] G_f, H_f
     float *sf;       // [B*H][F][D][D] state after each frame, transposed ([column][row])
     int B, H, F, S, nsplit, spl;
+    int reverse;     // anti-causal scan: frame f reads the state built from frames f+1 .. F-1
     float scale;
 };
 
@@ -369,21 +370,32 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
                 S[n][e] = a.h0[((size_t)bh * D + ti * 16 + 4 * (l >> 4) + e) * D + j0 + (l & 15)];
     }
     floatx4 gr[NG4], hr[NH4];    // native vectors: arrays of HIP float4 structs end up in scratch
-    state_fetch<D, NG4, NH4>(a.gh + (size_t)bh * a.F * 2 * D * D, j0, tid, gr, hr);
-    for (int f = 0; f < a.F; ++f) {
-        const size_t unit = (size_t)bh * a.F + f;
+    // Step i folds in the keys and values of frame kf and stores the state
+    // that frame of reads.  Forward: kf = of = i.  Reverse (the page's
+    // flip-and-shift: q flipped; k, v, beta flipped and shifted by one frame
+    // with zeros; the gates flipped and shifted with a gate of 1): step 0
+    // only stores the zero state for the last frame, step i >= 1 folds in
+    // frame F - i with its own gate and stores the state of frame F - 1 - i.
+    const bool rev = a.reverse != 0;
+    if ((rev ? 1 : 0) < a.F)
+        state_fetch<D, NG4, NH4>(a.gh + ((size_t)bh * a.F + (rev ? a.F - 1 : 0)) * 2 * D * D, j0, tid, gr, hr);
+    for (int i = 0; i < a.F; ++i) {
+        const bool upd = !rev || i > 0;          // uniform over the workgroup
+        const int kf = rev ? a.F - i : i, of = rev ? a.F - 1 - i : i;
+        if (upd) {
 #pragma unroll
-        for (int i = 0; i < NG4; ++i) {
-            const int idx = tid + 256 * i;
-            if (idx < D * D / 4) {
-                const int r = (idx * 4) / D, c = (idx * 4) % D;
-                *reinterpret_cast<floatx4 *>(Gs + r * LDG + c) = gr[i];
+            for (int j = 0; j < NG4; ++j) {
+                const int idx = tid + 256 * j;
+                if (idx < D * D / 4) {
+                    const int r = (idx * 4) / D, c = (idx * 4) % D;
+                    *reinterpret_cast<floatx4 *>(Gs + r * LDG + c) = gr[j];
+                }
             }
-        }
 #pragma unroll
-        for (int i = 0; i < NH4; ++i) {
-            const int idx = tid + 256 * i;
-            if (idx < D * 4) *reinterpret_cast<floatx4 *>(Hs + (idx >> 2) * LDS_ + 4 * (idx & 3)) = hr[i];
+            for (int j = 0; j < NH4; ++j) {
+                const int idx = tid + 256 * j;
+                if (idx < D * 4) *reinterpret_cast<floatx4 *>(Hs + (idx >> 2) * LDS_ + 4 * (idx & 3)) = hr[j];
+            }
         }
         // current state slice into LDS as the B operand ([k][col])
 #pragma unroll
@@ -394,17 +406,22 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
                 for (int e = 0; e < 4; ++e) Sl[(ti * 16 + 4 * (l >> 4) + e) * LDS_ + (l & 15)] = S[n][e];
         }
         lds_barrier();                  // the prefetch below stays in flight across barriers
-        if (f + 1 < a.F) state_fetch<D, NG4, NH4>(a.gh + ((size_t)bh * a.F + f + 1) * 2 * D * D, j0, tid, gr, hr);
-        const float dec = expf(a.g[unit]);
+        if (upd && i + 1 < a.F)
+            state_fetch<D, NG4, NH4>(a.gh + ((size_t)bh * a.F + (rev ? a.F - 1 - i : i + 1)) * 2 * D * D, j0, tid,
+                                     gr, hr);
+        const float dec = upd ? expf(a.g[(size_t)bh * a.F + kf]) : 1.f;
+        const size_t unit = (size_t)bh * a.F + of;
 #pragma unroll
         for (int n = 0; n < PERW; ++n) {
             const int ti = w + 4 * n;
             if (ti < NRT) {
-                floatx4 gs = zero4();
-                mma_f32_bn(gs, Gs + ti * 16 * LDG, LDG, Sl, LDS_, D);
+                if (upd) {
+                    floatx4 gs = zero4();
+                    mma_f32_bn(gs, Gs + ti * 16 * LDG, LDG, Sl, LDS_, D);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    S[n][e] = dec * (S[n][e] - gs[e]) + Hs[(ti * 16 + 4 * (l >> 4) + e) * LDS_ + (l & 15)];
+                    for (int e = 0; e < 4; ++e)
+                        S[n][e] = dec * (S[n][e] - gs[e]) + Hs[(ti * 16 + 4 * (l >> 4) + e) * LDS_ + (l & 15)];
+                }
                 *reinterpret_cast<float4 *>(a.sf + (unit * D + j0 + (l & 15)) * D + ti * 16 + 4 * (l >> 4)) =
                     float4{S[n][0], S[n][1], S[n][2], S[n][3]};
             }
@@ -617,7 +634,7 @@ extern "C" size_t gdn_recurrent_fwd_workspace_bytes(int B, int H, int F, int S, 
 
 extern "C" int gdn_recurrent_fwd(const void *q, const void *k, const void *v, const float *beta,
                                  const float *log_decay, float scale, const float *h0, float *hT, float *out,
-                                 int B, int H, int F, int S, int D, int dtype, void *workspace,
+                                 int B, int H, int F, int S, int D, int dtype, int reverse, void *workspace,
                                  size_t workspace_bytes, void *stream) {
     const char *name = "gdn_recurrent_fwd";
     GDN_REQUIRE(B >= 0 && H >= 0 && F >= 0, GDN_EINVAL, "%s: negative size (B=%d H=%d F=%d)", name, B, H, F);
@@ -626,6 +643,9 @@ extern "C" int gdn_recurrent_fwd(const void *q, const void *k, const void *v, co
     GDN_REQUIRE(D == 16 || D == 32 || D == 64 || D == 128, GDN_EUNSUPPORTED,
                 "%s: D=%d (supported: 16, 32, 64, 128)", name, D);
     GDN_REQUIRE(isfinite(scale), GDN_EINVAL, "%s: scale is not finite", name);
+    GDN_REQUIRE(reverse == 0 || reverse == 1, GDN_EINVAL, "%s: reverse=%d (0 or 1)", name, reverse);
+    GDN_REQUIRE(!reverse || (!h0 && !hT), GDN_EUNSUPPORTED,
+                "%s: the reverse scan takes no initial state and returns no final state", name);
     if ((long)B * H == 0) return GDN_OK;
     const bool work = (long)F > 0;
     if (work) {
@@ -665,6 +685,7 @@ extern "C" int gdn_recurrent_fwd(const void *q, const void *k, const void *v, co
     a.S = S;
     a.nsplit = gdn::frame_nsplit(B, H, F, S, D, &a.spl);
     a.scale = scale;
+    a.reverse = reverse;
     const size_t units = (size_t)B * H * F;
     float *ws = reinterpret_cast<float *>(workspace);
     a.gh = ws;

@@ -2,8 +2,8 @@
 // and cam_prep_func, with the inverse RMS of _precompute_cam_inv_rms fused
 // in (the page computes it in separate torch reductions that re-read q and k).
 //
-// One wave per token at a time (waves walk the tokens with a stride of the
-// grid).  The C = H*D channels of q, k and v are cut into 8-element
+// One wave per token at a time (workgroups walk blocks of consecutive
+// tokens with a stride of the grid).  The C = H*D channels of q, k and v are cut into 8-element
 // segments; lane l owns segments l, l+64, ... .  A segment lies in
 // one head and in one half of it (D/2 is a multiple of 8), so each lane works
 // either on two UCPE groups of 4 or on four RoPE pairs, in registers:
@@ -34,17 +34,24 @@ struct PrepArgs {
     int B, N, H;
 };
 
-template <bool F32IN>
+#ifndef GDN_PREP_NT
+#define GDN_PREP_NT 1
+#endif
+// 16-byte store of a q, k or v output piece; streaming (nontemporal: the
+// outputs are not read again by this kernel) unless GDN_PREP_NT is 0
+__device__ __forceinline__ void st16(void *p, u32x4 v) {
+    if constexpr (GDN_PREP_NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+    else *reinterpret_cast<u32x4 *>(p) = v;
+}
+template <bool F32OUT>
 __device__ __forceinline__ void store8(void *base, size_t elem, const float (&x)[8]) {
-    if constexpr (F32IN) {
-        float4 *p = reinterpret_cast<float4 *>(reinterpret_cast<float *>(base) + elem);
-        p[0] = float4{x[0], x[1], x[2], x[3]};
-        p[1] = float4{x[4], x[5], x[6], x[7]};
+    if constexpr (F32OUT) {
+        float *p = reinterpret_cast<float *>(base) + elem;
+        st16(p, u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])});
+        st16(p + 4, u32x4{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])});
     } else {
-        U16x8 r;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r.v[e] = bf16_bits(x[e]);
-        *reinterpret_cast<U16x8 *>(reinterpret_cast<u16 *>(base) + elem) = r;
+        st16(reinterpret_cast<u16 *>(base) + elem,
+             u32x4{cvt2_bf16(x[0], x[1]), cvt2_bf16(x[2], x[3]), cvt2_bf16(x[4], x[5]), cvt2_bf16(x[6], x[7])});
     }
 }
 
@@ -118,16 +125,26 @@ __device__ __forceinline__ void load_f8(const float *p, float (&x)[8]) {
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
-// NSEG = segments per lane = H*D / 512 (rounded up).  Each wave walks the
-// tokens with a stride of the grid: the RMSNorm weights of its channels stay
-// in registers, and the next token's q, k, v (and RoPE table row) are loaded
-// while the current one is processed.
+#ifndef GDN_PREP_TPB
+#define GDN_PREP_TPB 32
+#endif
+// NSEG = segments per lane = H*D / 512 (rounded up).  Workgroups take blocks
+// of TPB consecutive tokens with a stride of the grid, wave w tokens w, w+4,
+// ... of each block, so one workgroup writes TPB consecutive entries of
+// every per-head output row (whole 128-byte lines of the per-head scalars).
+// The RMSNorm weights of a wave's channels stay in registers, and its next
+// token's q, k, v (and RoPE table row) are loaded while the current one is
+// processed.
 template <bool F32IN, bool F32OUT, int D, int NSEG>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+    constexpr int TPB = GDN_PREP_TPB, TPW = TPB / 4;
+    static_assert(TPB % 4 == 0, "whole tokens per wave");
     const int l = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const long ntok = (long)a.B * a.N;
-    const long stride = (long)gridDim.x * 4;
-    long tok = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    long blk = blockIdx.x;
+    int jw = 0;                                  // this wave's token index inside the block
+    long tok = blk * TPB + w;
     if (tok >= ntok) return;
     const int H = a.H, C = H * D;
     const int nseg = C / 8;
@@ -172,7 +189,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         load_f8(a.sinv + (size_t)n * HALF + dr, sv);
     };
     load_token(tok);
-    for (; tok < ntok; tok += stride) {
+    while (tok < ntok) {
         float xq[NSEG][8], xk[NSEG][8], xv[NSEG][8], cs[8], sn[8];
 #pragma unroll
         for (int i = 0; i < NSEG; ++i) {
@@ -195,7 +212,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
             Pkv[i] = pkv[i];
         }
         // the next token's loads go out now (past the end: the last token again)
-        load_token(tok + stride < ntok ? tok + stride : ntok - 1);
+        long nblk = blk;
+        int njw = jw + 1;
+        if (njw == TPW) {
+            njw = 0;
+            nblk += gridDim.x;
+        }
+        const long next = nblk * TPB + w + 4 * njw;
+        load_token(next < ntok ? next : ntok - 1);
 
         float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -267,6 +291,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
                 if (a.infl) a.infl[so] = fmaxf(kpost, 1e-12f) / fmaxf(kpre, 1e-12f);
             }
         }
+        blk = nblk;
+        jw = njw;
+        tok = next;
     }
 }
 
@@ -275,8 +302,9 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
     const long ntok = (long)a.B * a.N;
     const int C = a.H * D;
     const int nseg = C / 8;
-    // about four tokens per wave: weights stay resident, loads overlap
-    long blocks = (ntok + 15) / 16;
+    // at least four tokens per wave: weights stay resident, loads overlap
+    const int per_wg = GDN_PREP_TPB > 16 ? GDN_PREP_TPB : 16;
+    long blocks = (ntok + per_wg - 1) / per_wg;
     if (blocks < 1) blocks = 1;
     if (blocks > 65535) blocks = 65535;
     const dim3 grid((unsigned)blocks);

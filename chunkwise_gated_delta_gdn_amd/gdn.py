@@ -54,7 +54,7 @@ def _load():
     lib.deltaproduct_chunk_fwd.restype = I
     lib.deltaproduct_chunk_fwd_workspace_bytes.argtypes = [I] * 8
     lib.deltaproduct_chunk_fwd_workspace_bytes.restype = Z
-    lib.gdn_recurrent_fwd.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, P, Z, P]
+    lib.gdn_recurrent_fwd.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, Z, P]
     lib.gdn_recurrent_fwd.restype = I
     lib.gdn_recurrent_fwd_workspace_bytes.argtypes = [I] * 6
     lib.gdn_recurrent_fwd_workspace_bytes.restype = Z
@@ -172,10 +172,14 @@ def deltaproduct_chunk_fwd(q, k, v, beta, log_decay, step_mask, scale=1.0, h0=No
     return o, hT
 
 
-def gdn_recurrent_fwd(q, k, v, beta, log_decay, scale=1.0, h0=None, output_final_state=True):
+def gdn_recurrent_fwd(q, k, v, beta, log_decay, scale=1.0, h0=None, output_final_state=True, reverse=False):
     """Camera-branch frame-synchronous numerator-only scan.  q,k,v (B,H,N,D);
     beta (B,H,N) fp32; log_decay (B,H,F) fp32 (one gate per frame, N = F*S);
-    h0 (B,H,D,D) fp32 or None.  Returns (out (B,H,N,D) fp32, hT or None)."""
+    h0 (B,H,D,D) fp32 or None.  Returns (out (B,H,N,D) fp32, hT or None).
+    reverse=True runs the anti-causal scan (frame f reads frames f+1..F-1);
+    it takes no h0 and returns no hT."""
+    if reverse:
+        output_final_state = False
     _dev(q, k, v, beta, log_decay, h0)
     _f32(beta, "beta"), _f32(log_decay, "log_decay"), _f32(h0, "h0")
     B, H, N, D = q.shape
@@ -195,8 +199,8 @@ def gdn_recurrent_fwd(q, k, v, beta, log_decay, scale=1.0, h0=None, output_final
     dt = _dtype_code(q.dtype)
     ws, nws = _workspace(_lib.gdn_recurrent_fwd_workspace_bytes(B, H, F, S, D, dt), q.device)
     rc = _lib.gdn_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_decay), float(scale),
-                                _ptr(h0), _ptr(hT), _ptr(out), B, H, F, S, D, dt, _ptr(ws), nws,
-                                _stream(q.device))
+                                _ptr(h0), _ptr(hT), _ptr(out), B, H, F, S, D, dt, int(bool(reverse)),
+                                _ptr(ws), nws, _stream(q.device))
     _check("gdn_recurrent_fwd", rc)
     return out, hT
 

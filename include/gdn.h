@@ -134,26 +134,38 @@ size_t deltaproduct_chunk_fwd_workspace_bytes(int B, int T, int H, int r, int dk
 
 /*
  * gdn_recurrent_fwd - camera-branch numerator-only scan ([cam]
- * _cam_scan_kernel, forward direction), frame-synchronous.
+ * _cam_scan_kernel, both directions; cam_scan_func), frame-synchronous.
  *
- * Tokens come in F frames of S tokens (N = F*S).  Per (b, h), with S = h0:
+ * Tokens come in F frames of S tokens (N = F*S).  Forward (reverse = 0),
+ * per (b, h), with S = h0:
  *   P = exp(g_f) S_{f-1};
  *   S_f = P + sum_{s in f} beta_s k_s (v_s - P^T k_s)^T
  *       (every token of the frame predicts from the same gated state P);
  *   out_s = scale * S_f^T q_s for s in f;    hT = S_F.
  * With S = 1 this is the token-level gated delta rule.
  *
+ * Reverse (reverse = 1; [cam] REVERSE branch of _cam_scan_kernel and the
+ * flip-and-shift reference of cam_scan_func): the forward scan run over
+ * frames F-1 .. 0 with k, v, beta shifted by one frame, so frame f reads the
+ * state R_f built from frames f+1 .. F-1 only:
+ *   R_{F-1} = 0;   R_f = (I - G_{f+1}) exp(g_{f+1}) R_{f+1} + H_{f+1},
+ *   G_j = sum_{s in j} beta_s k_s k_s^T,  H_j = sum_{s in j} beta_s k_s v_s^T;
+ *   out_s = scale * R_f^T q_s for s in f.
+ * The reverse scan takes no h0 and returns no hT (both must be NULL,
+ * GDN_EUNSUPPORTED otherwise), as on the page.
+ *
  *   q, k, v    (B, H, N, D)  dtype   (the layout gdn_prep writes)
  *   beta       (B, H, N)     float32
  *   log_decay  (B, H, F)     float32, one gate per frame
  *   h0, hT     (B, H, D, D)  float32, nullable
  *   out        (B, H, N, D)  float32
+ *   reverse    0 or 1
  * Supported: D in {16, 32, 64, 128}; F >= 1; S >= 1.
  */
 int gdn_recurrent_fwd(const void *q, const void *k, const void *v,
                       const float *beta, const float *log_decay, float scale,
                       const float *h0, float *hT, float *out,
-                      int B, int H, int F, int S, int D, int dtype,
+                      int B, int H, int F, int S, int D, int dtype, int reverse,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 size_t gdn_recurrent_fwd_workspace_bytes(int B, int H, int F, int S, int D, int dtype);

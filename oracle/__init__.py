@@ -17,6 +17,7 @@ receives; outputs are float64):
 * :func:`deltaproduct_recurrent`   - O2, gated DeltaProduct token by token.
 * :func:`cam_prep`                 - O3, camera-branch prep per token.
 * :func:`frame_scan`               - O4, frame-synchronous numerator-only scan.
+* :func:`frame_scan_reverse`       - O4 in the anti-causal direction.
 * :func:`invert_se3`               - closed-form rigid-transform inverse.
 """
 from __future__ import annotations
@@ -166,6 +167,39 @@ def frame_scan(q, k, v, beta, g, F, scale=1.0, h0=None, nthreads=0):
                                    float(scale), _ptr(h0), _ptr(out), _ptr(hT), int(nthreads))
     _check(rc, "frame_scan")
     return out, hT
+
+
+def _flip_and_shift(x, axis, pad):
+    """Reverse ``x`` along ``axis`` and move it one place later, filling the
+    first place with ``pad`` (the last element drops off) - the frame
+    re-indexing of [cam] ``_flip_and_shift``."""
+    xf = np.flip(x, axis=axis)
+    lead = np.full_like(np.take(xf, [0], axis=axis), pad)
+    return np.concatenate([lead, np.take(xf, np.arange(x.shape[axis] - 1), axis=axis)], axis=axis)
+
+
+def frame_scan_reverse(q, k, v, beta, g, F, scale=1.0, nthreads=0):
+    """O4, reverse direction, as [cam] defines it for ``cam_scan_func(...,
+    reverse=True)`` (its pure-torch reference): frames are reversed; q is only
+    flipped, k, v and beta are flipped and shifted by one frame with zeros,
+    the per-frame gates are flipped and shifted with a gate factor of 1
+    (log-decay 0); the forward scan O4 runs on that, and its output is
+    flipped back.  No initial or final state (the page rejects them).
+    Shapes as :func:`frame_scan`; returns out (B,H,N,D) float64."""
+    q, k, v, beta, g = map(_f32, (q, k, v, beta, g))
+    B, H, N, D = q.shape
+    assert N % F == 0
+    S = N // F
+    fr = lambda x: x.reshape(B, H, F, S, D)
+    q_b = np.flip(fr(q), axis=2)
+    k_b = _flip_and_shift(fr(k), 2, 0.0)
+    v_b = _flip_and_shift(fr(v), 2, 0.0)
+    beta_b = _flip_and_shift(beta.reshape(B, H, F, S), 2, 0.0)
+    g_b = _flip_and_shift(g, 2, 0.0)
+    flat = lambda x: np.ascontiguousarray(x.reshape(B, H, N, D))
+    out_b, _ = frame_scan(flat(q_b), flat(k_b), flat(v_b), np.ascontiguousarray(beta_b.reshape(B, H, N)),
+                          np.ascontiguousarray(g_b), F, scale, None, nthreads)
+    return np.ascontiguousarray(np.flip(out_b.reshape(B, H, F, S, D), axis=2).reshape(B, H, N, D))
 
 
 def invert_se3(P):

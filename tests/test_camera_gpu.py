@@ -210,3 +210,64 @@ def test_scan_split_resume_and_edges(gdn):
                         1.0, h0)
     assert out.shape == (B, H, 0, D)
     np.testing.assert_array_equal(hT, h0)
+
+
+# ---------------------------------------------------------------------------
+# reverse (anti-causal) scan
+# ---------------------------------------------------------------------------
+
+def _scan_rev_gpu(gdn, q, k, v, beta, g, dtype, scale=1.0):
+    import torch
+    out, hT = gdn.gdn_recurrent_fwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), to_dev(beta, "f32"),
+                                    to_dev(g, "f32"), scale, reverse=True)
+    torch.cuda.synchronize()
+    assert hT is None
+    return to_np(out)
+
+
+@pytest.mark.parametrize("case", [
+    # (B, H, F, S, D, dtype)
+    (1, 2, 3, 5, 16, "f32"),
+    (2, 2, 4, 33, 32, "f32"),
+    (1, 3, 5, 70, 64, "f32"),
+    (1, 2, 3, 40, 128, "f32"),
+    (1, 2, 1, 9, 32, "bf16"),
+    (1, 2, 3, 5, 16, "bf16"),
+    (2, 4, 6, 100, 64, "bf16"),
+    (1, 2, 3, 257, 128, "bf16"),
+], ids=lambda c: "B{}H{}F{}S{}D{}{}".format(*c))
+def test_scan_reverse_small(gdn, case):
+    B, H, F, S, D, dtype = case
+    _say(f"gdn_recurrent_fwd reverse small case {case}")
+    q, k, v, beta, g, _ = _scan_inputs(B, H, F, S, D, 700 + S + D, dtype)
+    out = _scan_rev_gpu(gdn, q, k, v, beta, g, dtype, 0.8)
+    oref = oracle.frame_scan_reverse(q, k, v, beta, g, F, 0.8)
+    assert np.all(out[:, :, (F - 1) * S:] == 0.0)                       # the last frame reads nothing
+    if F > 1:
+        eo = max_rel_err(out, oref)
+        _say(f"  {case}: max rel err out={eo:.2e}")
+        assert eo <= TOL[dtype], eo
+
+
+def test_scan_reverse_camera_workload(gdn):
+    _say("gdn_recurrent_fwd reverse, camera workload, full comparison")
+    d = synth.workload_inputs("camera")
+    pr = _prep_ref(d)
+    q, k, v = (synth.round_bf16(pr[n]) for n in ("q", "k", "v"))
+    out = _scan_rev_gpu(gdn, q, k, v, d["beta"], d["g"], "bf16")
+    oref = oracle.frame_scan_reverse(q, k, v, d["beta"], d["g"], d["F"], 1.0)
+    S, F = d["S"], d["F"]
+    per_frame = [max_rel_err(out[:, :, f * S:(f + 1) * S], oref[:, :, f * S:(f + 1) * S]) for f in range(F - 1)]
+    _say("  camera reverse: per frame " + " ".join(f"{e:.1e}" for e in per_frame))
+    assert max(per_frame) <= TOL["bf16"]
+    assert np.all(out[:, :, (F - 1) * S:] == 0.0)
+
+
+def test_scan_reverse_rejects_states(gdn):
+    import torch
+    q, k, v, beta, g, h0 = _scan_inputs(1, 1, 2, 4, 16, 5, "bf16", 0.1)
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.gdn_recurrent_fwd(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(beta, "f32"),
+                              to_dev(g, "f32"), 1.0, to_dev(h0, "f32"), reverse=True)
+    assert ei.value.code == -2                                          # GDN_EUNSUPPORTED
+    torch.cuda.synchronize()

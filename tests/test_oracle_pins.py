@@ -466,6 +466,86 @@ def test_frame_scan_split_and_resume():
 
 
 # --------------------------------------------------------------------------
+# O4 reverse ([cam] REVERSE branch / flip-and-shift reference of cam_scan_func)
+# --------------------------------------------------------------------------
+
+def _frame_GH(k, v, beta, F, S):
+    """G_j = sum beta k k^T, H_j = sum beta k v^T per frame, fp64 (one (b, h))."""
+    k, v, beta = (x.astype(np.float64) for x in (k, v, beta))
+    G = np.stack([(k[j * S:(j + 1) * S] * beta[j * S:(j + 1) * S, None]).T @ k[j * S:(j + 1) * S] for j in range(F)])
+    Hm = np.stack([(k[j * S:(j + 1) * S] * beta[j * S:(j + 1) * S, None]).T @ v[j * S:(j + 1) * S] for j in range(F)])
+    return G, Hm
+
+
+def test_frame_scan_reverse_is_the_unrolled_future_sum():
+    # R_f = sum_{j > f} (A_{f+1} ... A_{j-1}) H_j with A_m = e^{g_m} (I - G_m):
+    # only later frames enter, each frame's own gate applies to the state
+    # before that frame's keys and values are folded in.
+    B, H, F, S, D = 1, 2, 5, 3, 4
+    rng = _rng(31)
+    q, k, v = (_f32(rng.standard_normal((B, H, F * S, D)) * 0.6) for _ in range(3))
+    beta = _f32(rng.uniform(0, 1, (B, H, F * S)))
+    g = _f32(-rng.uniform(0.05, 1, (B, H, F)))
+    out = oracle.frame_scan_reverse(q, k, v, beta, g, F, 0.7)
+    for h in range(H):
+        G, Hm = _frame_GH(k[0, h], v[0, h], beta[0, h], F, S)
+        A = [np.exp(np.float64(g[0, h, m])) * (np.eye(D) - G[m]) for m in range(F)]
+        for f in range(F):
+            R = np.zeros((D, D))
+            P = np.eye(D)
+            for j in range(f + 1, F):
+                R += P @ Hm[j]
+                P = P @ A[j]
+            ref = 0.7 * q[0, h, f * S:(f + 1) * S].astype(np.float64) @ R
+            np.testing.assert_allclose(out[0, h, f * S:(f + 1) * S], ref, atol=1e-12)
+
+
+def test_frame_scan_reverse_edge_frames():
+    B, H, F, S, D = 1, 1, 4, 6, 8
+    rng = _rng(32)
+    q, k, v = (_f32(rng.standard_normal((B, H, F * S, D))) for _ in range(3))
+    beta = _f32(rng.uniform(0, 1, (B, H, F * S)))
+    g = _f32(-rng.uniform(0, 1, (B, H, F)))
+    out = oracle.frame_scan_reverse(q, k, v, beta, g, F, 1.0)
+    # the last frame has no future: exactly zero
+    assert np.all(out[0, 0, (F - 1) * S:] == 0.0)
+    # the frame before it sees only the last frame, from a zero state: plain
+    # linear attention onto that frame, sum_s beta_s (q . k_s) v_s
+    qf = q[0, 0, (F - 2) * S:(F - 1) * S].astype(np.float64)
+    kl, vl = (x[0, 0, (F - 1) * S:].astype(np.float64) for x in (k, v))
+    bl = beta[0, 0, (F - 1) * S:].astype(np.float64)
+    np.testing.assert_allclose(out[0, 0, (F - 2) * S:(F - 1) * S], (qf @ kl.T * bl) @ vl, atol=1e-12)
+    # one frame only: nothing to read
+    o1 = oracle.frame_scan_reverse(q[..., :S, :], k[..., :S, :], v[..., :S, :], beta[..., :S], g[..., :1], 1, 1.0)
+    assert np.all(o1 == 0.0)
+    # beta = 0: nothing is written, nothing is read
+    o0 = oracle.frame_scan_reverse(q, k, v, np.zeros_like(beta), g, F, 1.0)
+    assert np.all(o0 == 0.0)
+
+
+def test_frame_scan_reverse_mirrors_the_forward_scan():
+    # Reversing the frame order of the inputs turns the reverse scan into the
+    # forward scan with an exclusive read-out: frame f of the reverse scan of
+    # the reversed sequence reads the forward state after frame f - 1 of the
+    # original (gates shifted by one frame).
+    B, H, F, S, D = 1, 1, 5, 4, 6
+    rng = _rng(33)
+    q, k, v = (_f32(rng.standard_normal((B, H, F * S, D)) * 0.5) for _ in range(3))
+    beta = _f32(rng.uniform(0, 1, (B, H, F * S)))
+    g = _f32(-rng.uniform(0, 1, (B, H, F)))
+    rf = lambda x: np.ascontiguousarray(np.flip(x.reshape(B, H, F, S, -1), axis=2).reshape(x.shape))
+    out_r = oracle.frame_scan_reverse(rf(q), rf(k), rf(v), rf(beta[..., None])[..., 0], np.ascontiguousarray(g[..., ::-1]), F, 1.0)
+    out_r = rf(out_r)
+    # forward states S_f of the original order, in fp64 from G, H directly
+    G, Hm = _frame_GH(k[0, 0], v[0, 0], beta[0, 0], F, S)
+    St = np.zeros((D, D))
+    for f in range(F):
+        ref = q[0, 0, f * S:(f + 1) * S].astype(np.float64) @ St      # reads the state before frame f
+        np.testing.assert_allclose(out_r[0, 0, f * S:(f + 1) * S], ref, atol=1e-12)
+        St = np.exp(np.float64(g[0, 0, f])) * (np.eye(D) - G[f]) @ St + Hm[f]
+
+
+# --------------------------------------------------------------------------
 # A planted mistake must be caught: the pins are not vacuous.
 # --------------------------------------------------------------------------
 
