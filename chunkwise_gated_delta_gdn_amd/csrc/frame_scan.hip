@@ -155,8 +155,9 @@ __global__ __launch_bounds__(256) void frame_gram_kernel(FrameArgs a) {
 // row-major in LDS (64 tokens a step, two buffers) and read back transposed
 // with ds_read_b64_tr_b16.  A = K^T (exact bf16); B = beta (.) K or
 // beta (.) V, scaled in fp32 after the transposed read and split hi + lo.
-// Wave w owns whole column tiles ("jobs": matrix G or H, column tile tj);
-// every wave reads the A fragments of all row tiles.
+// Wave w owns whole column tiles ("jobs": matrix G or H, column tile tj;
+// eight waves at D >= 32, one job each at D = 64); every wave reads the A
+// fragments of all row tiles.
 //
 // Loads run one round (SPW steps) ahead in two register sets.  Every load is
 // unconditional (rows past the range end read the range's last row, whose
@@ -170,16 +171,20 @@ constexpr int gram_steps() { return D == 128 ? 1 : 2; }
 constexpr int gram_round(int D) { return (D == 128 ? 1 : 2) * TSG; }
 
 template <int D>
-__global__ __launch_bounds__(256) void frame_gram_bf16_kernel(FrameArgs a) {
+constexpr int gram_waves() { return D >= 32 ? 8 : 4; }
+
+template <int D>
+__global__ __launch_bounds__(512) void frame_gram_bf16_kernel(FrameArgs a) {
+    constexpr int NW = gram_waves<D>(), NTH = 64 * NW;   // waves, threads
     constexpr int NT1 = D / 16;                 // row tiles = column tiles of one matrix
-    constexpr int NJOB = 2 * NT1, JPW = (NJOB + 3) / 4;
+    constexpr int NJOB = 2 * NT1, JPW = (NJOB + NW - 1) / NW;
     // row stride: 4 rows of 32 bytes (one 16-lane transposed read) fall on
     // distinct banks for 32 or 64 banks of 4 bytes
     constexpr int LDR = D == 16 ? 16 : D + 16;
     constexpr int SEGS = D / 8;                 // 16-byte pieces per token row
-    constexpr int PPT = 2 * TSG * SEGS / 256;   // pieces of k and v per thread per step
+    constexpr int PPT = 2 * TSG * SEGS / NTH;   // pieces of k and v per thread per step
     constexpr int SPW = gram_steps<D>(), RND = SPW * TSG;
-    static_assert(PPT * 256 == 2 * TSG * SEGS, "whole pieces per thread");
+    static_assert(PPT * NTH == 2 * TSG * SEGS, "whole pieces per thread");
     __shared__ __attribute__((aligned(16))) u16 Ks[2][TSG * LDR], Vs[2][TSG * LDR];
     __shared__ __attribute__((aligned(16))) float Bs[2][TSG];
     const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(256) void frame_gram_bf16_kernel(FrameArgs a) {
             const int s0 = s_lo + rnd * RND + u * TSG;
 #pragma unroll
             for (int i = 0; i < PPT; ++i) {
-                const int p = tid + 256 * i;
+                const int p = tid + NTH * i;
                 const int mat = p / (TSG * SEGS), rem = p % (TSG * SEGS), r = rem / SEGS, sg = rem % SEGS;
                 const int s = min(s0 + r, s_hi - 1);
                 st.x[u][i] = *reinterpret_cast<const u32x4 *>((mat ? vin : kin) + (row0 + s) * D + sg * 8);
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(256) void frame_gram_bf16_kernel(FrameArgs a) {
     auto lstore = [&](const Set &st, int u, int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
-            const int p = tid + 256 * i;
+            const int p = tid + NTH * i;
             const int mat = p / (TSG * SEGS), rem = p % (TSG * SEGS), r = rem / SEGS, sg = rem % SEGS;
             *reinterpret_cast<u32x4 *>((mat ? Vs[buf] : Ks[buf]) + r * LDR + sg * 8) = st.x[u][i];
         }
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(256) void frame_gram_bf16_kernel(FrameArgs a) {
             const float bt[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
             for (int jb = 0; jb < JPW; ++jb) {
-                const int job = w + 4 * jb;
+                const int job = w + NW * jb;
                 if (job < NJOB) {
                     const int tj = job % NT1;
                     const u16 *src = job < NT1 ? ks : vs;
@@ -294,7 +299,7 @@ __global__ __launch_bounds__(256) void frame_gram_bf16_kernel(FrameArgs a) {
     float *dst = a.part + ((size_t)unit * a.nsplit + sp) * 2 * D * D;
 #pragma unroll
     for (int jb = 0; jb < JPW; ++jb) {
-        const int job = w + 4 * jb;
+        const int job = w + NW * jb;
         if (job < NJOB) {
             const int kind = job / NT1, tj = job % NT1;
 #pragma unroll
@@ -507,12 +512,13 @@ __global__ __launch_bounds__(256) void frame_out_kernel(FrameArgs a) {
 // transpose), B = Q^T: lane (g, c16) needs 8 consecutive features of token
 // c16, one 16-byte load straight from the (token, D) rows.  The accumulator
 // gives each lane 4 consecutive outputs of one token: one 16-byte store.
-// A workgroup covers OUT_TOK tokens of one frame, each wave 64 of them.
+// A workgroup (eight waves) covers 512 tokens of one frame, each wave 64 of
+// them, so S_f is staged once per 512 tokens.
 // ---------------------------------------------------------------------------
-constexpr int OUT_TOK = 256;
+constexpr int OUT_WAVES = 8, OUT_TOK = OUT_WAVES * 64;   // 64 tokens per wave
 
 template <int D>
-__global__ __launch_bounds__(256) void frame_out_bf16_kernel(FrameArgs a) {
+__global__ __launch_bounds__(64 * OUT_WAVES) void frame_out_bf16_kernel(FrameArgs a) {
     constexpr int NT1 = D / 16, NK = D / 32, LDT = D + 8, SUB = 4;   // SUB tiles of 16 tokens per wave
     static_assert(D >= 32, "32-deep k steps");
     __shared__ __attribute__((aligned(16))) u16 SH[D * LDT], SL[D * LDT];
@@ -539,7 +545,7 @@ __global__ __launch_bounds__(256) void frame_out_bf16_kernel(FrameArgs a) {
     }
     // S_f^T rows (output feature i, input features contiguous) split into LDS
     const float4 *sf = reinterpret_cast<const float4 *>(a.sf + (size_t)unit * D * D);
-    for (int idx = tid; idx < D * D / 4; idx += 256) {
+    for (int idx = tid; idx < D * D / 4; idx += 64 * OUT_WAVES) {
         const float4 x = sf[idx];
         const int r = (idx * 4) / D, c = (idx * 4) % D;
         uint2 hi, lo;
@@ -575,12 +581,12 @@ __global__ __launch_bounds__(256) void frame_out_bf16_kernel(FrameArgs a) {
 }
 
 // Token ranges of the gram kernels: enough workgroups to fill the chip
-// (about three per compute unit), whole rounds of staged steps per range.
+// (about two per compute unit), whole rounds of staged steps per range.
 int frame_nsplit(int B, int H, int F, int S, int D, int *spl_out) {
     const long units = (long)B * H * F;
     const int RND = gram_round(D);
     const int maxsp = (S + RND - 1) / RND;
-    long want = units > 0 ? (768 + units - 1) / units : 1;
+    long want = units > 0 ? (512 + units - 1) / units : 1;
     if (want > maxsp) want = maxsp;
     if (want < 1) want = 1;
     const int per = (int)((S + want - 1) / want);
@@ -601,7 +607,7 @@ template <bool F32IN, int D>
 hipError_t launch_frame(FrameArgs a, hipStream_t s) {
     const int units = a.B * a.H * a.F;
     if constexpr (F32IN) hipLaunchKernelGGL((frame_gram_kernel<true, D>), dim3(units * a.nsplit), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((frame_gram_bf16_kernel<D>), dim3(units * a.nsplit), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((frame_gram_bf16_kernel<D>), dim3(units * a.nsplit), dim3(64 * gram_waves<D>()), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.nsplit > 1) {
@@ -615,7 +621,7 @@ hipError_t launch_frame(FrameArgs a, hipStream_t s) {
     if (e != hipSuccess) return e;
     if constexpr (!F32IN && D >= 32) {
         const int ntt = (a.S + OUT_TOK - 1) / OUT_TOK;
-        hipLaunchKernelGGL((frame_out_bf16_kernel<D>), dim3(units * ntt), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((frame_out_bf16_kernel<D>), dim3(units * ntt), dim3(64 * OUT_WAVES), 0, s, a);
     } else {
         const int ntt = (a.S + 63) / 64;
         hipLaunchKernelGGL((frame_out_kernel<F32IN, D>), dim3(units * ntt), dim3(256), 0, s, a);
