@@ -84,3 +84,22 @@ def test_deltaproduct_rejects_bad_arguments(lib):
     assert call(m=None) == -1
     bad = (ctypes.c_float * 4)(1, 0, float("inf"), 1)
     assert call(m=bad) == -1
+
+
+def test_recurrent_rejects_bad_arguments(lib):
+    fake = ctypes.c_void_p(4096)
+
+    def call(reverse=0, h0=None, hT=None, D=64, S=4, dtype=1, ws=None, nws=0):
+        return lib.gdn_recurrent_fwd(fake, fake, fake, fake, fake, 1.0, h0, hT, fake,
+                                     1, 1, 2, S, D, dtype, reverse, ws, nws, None)
+    assert call(reverse=2) == -1
+    assert call(reverse=1, h0=fake) == -2                        # the reverse scan takes no state
+    assert b"reverse" in lib.gdn_last_error()
+    assert call(reverse=1, hT=fake) == -2
+    assert call(D=48) == -2
+    assert call(S=0) == -1
+    assert call(dtype=5) == -1
+    assert call() == -3                                          # no work space
+    need = lib.gdn_recurrent_fwd_workspace_bytes(1, 1, 2, 4, 64, 1)
+    assert need > 0
+    assert call(reverse=1) == -3
