@@ -99,7 +99,7 @@ def _prepare(name, dev):
     workload's hot path once through the C ABI."""
     import torch
     from chunkwise_gated_delta_gdn_amd import gdn, inputs
-    base = "camera" if name == "camera_reverse" else name    # same inputs, other scan direction
+    base = "camera" if name in ("camera_reverse", "camera_den") else name    # same inputs
     wl = inputs.WORKLOADS[base]
     d = inputs.workload_inputs(base)
     bf = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
@@ -137,14 +137,21 @@ def _prepare(name, dev):
     qkv = bf(d["qkv"])
     t = {n: f32(d[n]) for n in ("q_norm_w", "k_norm_w", "proj_q", "proj_kv", "rope_cos", "rope_sin", "beta", "g")}
 
+    with_den = name == "camera_den"
+
     def step():
         pr = gdn.gdn_prep(qkv, t["q_norm_w"], t["k_norm_w"], t["proj_q"], t["proj_kv"], t["rope_cos"],
                           t["rope_sin"], d["k_scale"], d["eps"])
-        return gdn.gdn_recurrent_fwd(pr["q"], pr["k"], pr["v"], t["beta"], t["g"], 1.0, reverse=reverse)
+        num = gdn.gdn_recurrent_fwd(pr["q"], pr["k"], pr["v"], t["beta"], t["g"], 1.0, reverse=reverse)
+        if with_den:        # normaliser stream on the prep's q and k (stand-ins for its own rows)
+            return num, gdn.gdn_recurrent_den_fwd(pr["q"], pr["k"], t["beta"], t["g"], 1.0)
+        return num
     B, F, S, H, D = wl["B"], wl["F"], wl["S"], wl["H"], wl["D"]
     N = F * S
     prep_bytes = B * N * 3 * H * D * 2 * 2 + B * N * 32 * 4 + N * D * 4 + B * H * N * 3 * 4
     scan_bytes = B * H * N * D * 2 * 3 + B * H * N * 4 + B * H * N * D * 4 + (0 if reverse else B * H * D * D * 4)
+    if with_den:            # q, k, beta read, den and zT written
+        scan_bytes += B * H * N * D * 2 * 2 + B * H * N * 4 + B * H * N * 4 + B * H * D * 4
     flops = B * H * N * 4 * D * D * 2
     return d, step, B * N, prep_bytes + scan_bytes, flops
 
@@ -168,7 +175,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="gdn", choices=("gdn", "gdn_long", "deltaproduct", "camera", "camera_reverse"),
+    ap.add_argument("--workload", default="gdn", choices=("gdn", "gdn_long", "deltaproduct", "camera", "camera_reverse", "camera_den"),
                     help="gdn is the headline workload; the others time the other operations")
     ap.add_argument("--copy-probe", action="store_true", help="run only the copy calibration kernel")
     args = ap.parse_args()
@@ -205,7 +212,7 @@ def main():
     kernel_ms = float(np.mean(kern_ms))
     achieved_gbs = nbytes / (kernel_ms * 1e-3) / 1e9
     from chunkwise_gated_delta_gdn_amd import inputs
-    wl = inputs.WORKLOADS["camera" if args.workload == "camera_reverse" else args.workload]
+    wl = inputs.WORKLOADS["camera" if args.workload in ("camera_reverse", "camera_den") else args.workload]
     if args.workload in ("gdn", "gdn_long"):
         metric = "tokens/sec of chunkwise gated-delta fwd (B*T/s) at H=16, D=128"
         desc = (f"{args.workload}: B={wl['B']} H={wl['H']} T={wl['T']} Dk=Dv={wl['Dk']} chunk={wl['chunk']}, "
@@ -221,7 +228,8 @@ def main():
         rev = args.workload == "camera_reverse"
         metric = "tokens/sec of camera prep + frame-synchronous scan (B*N/s)"
         desc = ("camera: B=1 F=8 S=30x52 H=16 D=64, bf16 prep output, fp32 scan output"
-                + (", reverse (anti-causal) scan" if rev else ""))
+                + (", reverse (anti-causal) scan" if rev else "")
+                + (", plus the normaliser stream on the prep's q and k" if args.workload == "camera_den" else ""))
         kernel = "gdn_prep + gdn_recurrent_fwd (prep_kernel, frame_gram/state/out kernels)"
         traffic = None
     rec = {

@@ -34,6 +34,8 @@ struct FrameArgs {
     float *sf;       // [B*H][F][D][D] state after each frame, transposed ([column][row])
     int B, H, F, S, nsplit, spl;
     int reverse;     // anti-causal scan: frame f reads the state built from frames f+1 .. F-1
+    int den;         // normaliser stream: unit values (v = 1), vector state z (h0/hT are z0/zT,
+                     // (B, H, D)), out is den (B, H, N)
     float scale;
 };
 
@@ -57,6 +59,15 @@ __device__ __forceinline__ void put_op(typename OpT<F32IN>::type *hi, typename O
     }
 }
 
+// Sum over aligned groups of W consecutive lanes (W a power of two <= 64);
+// every lane of a group receives the group total.
+template <int W>
+__device__ __forceinline__ float lane_group_sum(float x) {
+#pragma unroll
+    for (int off = 1; off < W; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
 template <bool F32IN>
 __device__ __forceinline__ void load8(const void *base, size_t elem, float (&x)[8]) {
     if constexpr (F32IN) {
@@ -74,7 +85,7 @@ __device__ __forceinline__ void load8(const void *base, size_t elem, float (&x)[
 // ---------------------------------------------------------------------------
 // partial G_f = K^T diag(beta) K and H_f = K^T diag(beta) V over one token range
 // ---------------------------------------------------------------------------
-template <bool F32IN, int D>
+template <bool F32IN, int D, bool VONES>
 __global__ __launch_bounds__(256) void frame_gram_kernel(FrameArgs a) {
     using Op = typename OpT<F32IN>::type;
     constexpr int PAD = F32IN ? 4 : 8, LD = TS + PAD;
@@ -102,7 +113,12 @@ __global__ __launch_bounds__(256) void frame_gram_kernel(FrameArgs a) {
             if (s0 + s < s_hi) {
                 const size_t row = row0 + s0 + s;
                 load8<F32IN>(a.k, row * D + i0, kx);
-                load8<F32IN>(a.v, row * D + i0, vx);
+                if constexpr (VONES) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vx[e] = 1.f;
+                } else {
+                    load8<F32IN>(a.v, row * D + i0, vx);
+                }
                 bt = a.beta[row];
             } else {
 #pragma unroll
@@ -173,7 +189,7 @@ constexpr int gram_round(int D) { return (D == 128 ? 1 : 2) * TSG; }
 template <int D>
 constexpr int gram_waves() { return D >= 32 ? 8 : 4; }
 
-template <int D>
+template <int D, bool VONES>
 __global__ __launch_bounds__(512) void frame_gram_bf16_kernel(FrameArgs a) {
     constexpr int NW = gram_waves<D>(), NTH = 64 * NW;   // waves, threads
     constexpr int NT1 = D / 16;                 // row tiles = column tiles of one matrix
@@ -216,7 +232,8 @@ __global__ __launch_bounds__(512) void frame_gram_bf16_kernel(FrameArgs a) {
                 const int p = tid + NTH * i;
                 const int mat = p / (TSG * SEGS), rem = p % (TSG * SEGS), r = rem / SEGS, sg = rem % SEGS;
                 const int s = min(s0 + r, s_hi - 1);
-                st.x[u][i] = *reinterpret_cast<const u32x4 *>((mat ? vin : kin) + (row0 + s) * D + sg * 8);
+                if (!VONES || !mat)            // unit values: no V rows
+                    st.x[u][i] = *reinterpret_cast<const u32x4 *>((mat ? vin : kin) + (row0 + s) * D + sg * 8);
             }
             const int s = s0 + (tid & (TSG - 1));
             const float bt = a.beta[row0 + min(s, s_hi - 1)];
@@ -228,7 +245,7 @@ __global__ __launch_bounds__(512) void frame_gram_bf16_kernel(FrameArgs a) {
         for (int i = 0; i < PPT; ++i) {
             const int p = tid + NTH * i;
             const int mat = p / (TSG * SEGS), rem = p % (TSG * SEGS), r = rem / SEGS, sg = rem % SEGS;
-            *reinterpret_cast<u32x4 *>((mat ? Vs[buf] : Ks[buf]) + r * LDR + sg * 8) = st.x[u][i];
+            if (!VONES || !mat) *reinterpret_cast<u32x4 *>((mat ? Vs[buf] : Ks[buf]) + r * LDR + sg * 8) = st.x[u][i];
         }
         if (tid < TSG) Bs[buf][tid] = st.b[u];
     };
@@ -254,8 +271,13 @@ __global__ __launch_bounds__(512) void frame_gram_bf16_kernel(FrameArgs a) {
                 if (job < NJOB) {
                     const int tj = job % NT1;
                     const u16 *src = job < NT1 ? ks : vs;
-                    const uint2 x0 = __builtin_bit_cast(uint2, ld_tr16(src + ra * LDR + tj * 16 + cq));
-                    const uint2 x1 = __builtin_bit_cast(uint2, ld_tr16(src + (ra + 4) * LDR + tj * 16 + cq));
+                    uint2 x0, x1;
+                    if (VONES && job >= NT1) {
+                        x0 = x1 = uint2{0x3F803F80u, 0x3F803F80u};      // bf16 ones
+                    } else {
+                        x0 = __builtin_bit_cast(uint2, ld_tr16(src + ra * LDR + tj * 16 + cq));
+                        x1 = __builtin_bit_cast(uint2, ld_tr16(src + (ra + 4) * LDR + tj * 16 + cq));
+                    }
                     const unsigned u[4] = {x0.x, x0.y, x1.x, x1.y};
                     uint4 hi, lo;
                     unsigned *ph = &hi.x, *pl = &lo.x;
@@ -361,7 +383,9 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
     __shared__ __attribute__((aligned(16))) float Gs[D * LDG], Sl[D * LDS_], Hs[D * LDS_];
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int ncb = D / 16;
+    // normaliser stream: one slice, whose 16 columns all carry z (the unit
+    // values make every column of H_f equal to b_f)
+    const int ncb = a.den ? 1 : D / 16;
     const int bh = blockIdx.x / ncb, cb = blockIdx.x % ncb, j0 = cb * 16;
 
     floatx4 S[PERW];
@@ -371,8 +395,10 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
         const int ti = w + 4 * n;
         if (ti < NRT && a.h0)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                S[n][e] = a.h0[((size_t)bh * D + ti * 16 + 4 * (l >> 4) + e) * D + j0 + (l & 15)];
+            for (int e = 0; e < 4; ++e) {
+                const int row = ti * 16 + 4 * (l >> 4) + e;
+                S[n][e] = a.den ? a.h0[(size_t)bh * D + row] : a.h0[((size_t)bh * D + row) * D + j0 + (l & 15)];
+            }
     }
     floatx4 gr[NG4], hr[NH4];    // native vectors: arrays of HIP float4 structs end up in scratch
     // Step i folds in the keys and values of frame kf and stores the state
@@ -439,8 +465,11 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
             const int ti = w + 4 * n;
             if (ti < NRT)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    a.hT[((size_t)bh * D + ti * 16 + 4 * (l >> 4) + e) * D + j0 + (l & 15)] = S[n][e];
+                for (int e = 0; e < 4; ++e) {
+                    const int row = ti * 16 + 4 * (l >> 4) + e;
+                    if (!a.den) a.hT[((size_t)bh * D + row) * D + j0 + (l & 15)] = S[n][e];
+                    else if ((l & 15) == 0) a.hT[(size_t)bh * D + row] = S[n][e];
+                }
         }
     }
 }
@@ -580,6 +609,50 @@ __global__ __launch_bounds__(64 * OUT_WAVES) void frame_out_bf16_kernel(FrameArg
     }
 }
 
+// ---------------------------------------------------------------------------
+// normaliser stream read-out: den_s = z_f . q_s, z_f = column 0 of S_f (the
+// first row of the stored transpose).  Each token's row is split over L
+// consecutive lanes (16-byte pieces, coalesced), partial dot products summed
+// over the L lanes by DPP; 256-thread workgroups walk 64/L tokens per wave
+// per step over one frame.
+// ---------------------------------------------------------------------------
+template <bool F32IN, int D>
+__global__ __launch_bounds__(256) void frame_den_kernel(FrameArgs a) {
+    constexpr int EPP = F32IN ? 4 : 8;            // elements per 16-byte piece
+    constexpr int L = D / EPP;                    // lanes per token
+    constexpr int TPW = 64 / L;                   // tokens per wave and step
+    static_assert(L >= 2 && L <= 64 && 64 % L == 0, "lanes per token");
+    __shared__ __attribute__((aligned(16))) float zs[D];
+    const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+    const int ntb = (a.S + 255) / 256;
+    const int unit = blockIdx.x / ntb, tb = blockIdx.x % ntb;
+    const size_t N = (size_t)a.F * a.S;
+    const size_t row0 = (size_t)(unit / a.F) * N + (size_t)(unit % a.F) * a.S;
+    if (tid < D) zs[tid] = a.sf[(size_t)unit * D * D + tid];
+    __syncthreads();
+    const int pc = l % L;                          // this lane's piece of the row
+    float z[EPP];
+#pragma unroll
+    for (int e = 0; e < EPP; ++e) z[e] = zs[pc * EPP + e];
+    for (int t = tb * 256 + w * TPW + l / L; t < min(a.S, tb * 256 + 256); t += 4 * TPW) {
+        float x[EPP];
+        const size_t off = (row0 + t) * D + pc * EPP;
+        if constexpr (F32IN) {
+            const float4 p0 = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + off);
+            x[0] = p0.x; x[1] = p0.y; x[2] = p0.z; x[3] = p0.w;
+        } else {
+            const U16x8 r = *reinterpret_cast<const U16x8 *>(reinterpret_cast<const u16 *>(a.q) + off);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32(r.v[e]);
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) acc += x[e] * z[e];
+        acc = lane_group_sum<L>(acc);
+        if (pc == 0) a.out[row0 + t] = a.scale * acc;
+    }
+}
+
 // Token ranges of the gram kernels: enough workgroups to fill the chip
 // (about two per compute unit), whole rounds of staged steps per range.
 int frame_nsplit(int B, int H, int F, int S, int D, int *spl_out) {
@@ -603,12 +676,21 @@ size_t frame_workspace(int B, int H, int F, int S, int D) {
            units * D * D * sizeof(float);
 }
 
+template <bool F32IN, int D, bool VONES>
+hipError_t launch_gram(const FrameArgs &a, hipStream_t s) {
+    const int units = a.B * a.H * a.F;
+    if constexpr (F32IN)
+        hipLaunchKernelGGL((frame_gram_kernel<true, D, VONES>), dim3(units * a.nsplit), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((frame_gram_bf16_kernel<D, VONES>), dim3(units * a.nsplit), dim3(64 * gram_waves<D>()),
+                           0, s, a);
+    return hipGetLastError();
+}
+
 template <bool F32IN, int D>
 hipError_t launch_frame(FrameArgs a, hipStream_t s) {
     const int units = a.B * a.H * a.F;
-    if constexpr (F32IN) hipLaunchKernelGGL((frame_gram_kernel<true, D>), dim3(units * a.nsplit), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((frame_gram_bf16_kernel<D>), dim3(units * a.nsplit), dim3(64 * gram_waves<D>()), 0, s, a);
-    hipError_t e = hipGetLastError();
+    hipError_t e = a.den ? launch_gram<F32IN, D, true>(a, s) : launch_gram<F32IN, D, false>(a, s);
     if (e != hipSuccess) return e;
     if (a.nsplit > 1) {
         const size_t n4 = (size_t)units * 2 * D * D / 4;
@@ -616,10 +698,12 @@ hipError_t launch_frame(FrameArgs a, hipStream_t s) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((frame_state_kernel<D>), dim3(a.B * a.H * (D / 16)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((frame_state_kernel<D>), dim3(a.B * a.H * (a.den ? 1 : D / 16)), dim3(256), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if constexpr (!F32IN && D >= 32) {
+    if (a.den) {
+        hipLaunchKernelGGL((frame_den_kernel<F32IN, D>), dim3(units * ((a.S + 255) / 256)), dim3(256), 0, s, a);
+    } else if constexpr (!F32IN && D >= 32) {
         const int ntt = (a.S + OUT_TOK - 1) / OUT_TOK;
         hipLaunchKernelGGL((frame_out_bf16_kernel<D>), dim3(units * ntt), dim3(64 * OUT_WAVES), 0, s, a);
     } else {
@@ -627,6 +711,78 @@ hipError_t launch_frame(FrameArgs a, hipStream_t s) {
         hipLaunchKernelGGL((frame_out_kernel<F32IN, D>), dim3(units * ntt), dim3(256), 0, s, a);
     }
     return hipGetLastError();
+}
+
+// Shared body of the two scan entry points (checks, work space carving, launch).
+int frame_entry(const char *name, const void *q, const void *k, const void *v, const float *beta,
+                const float *log_decay, float scale, const float *h0, float *hT, float *out, int B, int H, int F,
+                int S, int D, int dtype, int reverse, int den, void *workspace, size_t workspace_bytes,
+                void *stream) {
+    GDN_REQUIRE(B >= 0 && H >= 0 && F >= 0, GDN_EINVAL, "%s: negative size (B=%d H=%d F=%d)", name, B, H, F);
+    GDN_REQUIRE(S >= 1, GDN_EINVAL, "%s: S=%d (at least one token per frame)", name, S);
+    GDN_REQUIRE(dtype == GDN_DTYPE_F32 || dtype == GDN_DTYPE_BF16, GDN_EINVAL, "%s: unknown dtype %d", name, dtype);
+    GDN_REQUIRE(D == 16 || D == 32 || D == 64 || D == 128, GDN_EUNSUPPORTED,
+                "%s: D=%d (supported: 16, 32, 64, 128)", name, D);
+    GDN_REQUIRE(isfinite(scale), GDN_EINVAL, "%s: scale is not finite", name);
+    GDN_REQUIRE(reverse == 0 || reverse == 1, GDN_EINVAL, "%s: reverse=%d (0 or 1)", name, reverse);
+    GDN_REQUIRE(!reverse || (!h0 && !hT), GDN_EUNSUPPORTED,
+                "%s: the reverse scan takes no initial state and returns no final state", name);
+    if ((long)B * H == 0) return GDN_OK;
+    const bool work = (long)F > 0;
+    if (work) {
+        GDN_REQUIRE(q && k && (den || v) && beta && log_decay && out, GDN_EINVAL, "%s: null tensor pointer", name);
+        GDN_REQUIRE(gdn::aligned(q, 16) && gdn::aligned(k, 16) && (den || gdn::aligned(v, 16)) &&
+                        gdn::aligned(out, den ? 4 : 16),
+                    GDN_EINVAL, "%s: q, k, v must be 16-byte aligned, out %d-byte aligned", name, den ? 4 : 16);
+        GDN_REQUIRE(gdn::aligned(beta, 4) && gdn::aligned(log_decay, 4), GDN_EINVAL,
+                    "%s: beta and log_decay must be 4-byte aligned", name);
+    }
+    GDN_REQUIRE(!h0 || gdn::aligned(h0, 4), GDN_EINVAL, "%s: initial state misaligned", name);
+    GDN_REQUIRE(!hT || gdn::aligned(hT, 4), GDN_EINVAL, "%s: final state misaligned", name);
+    const size_t need = frame_workspace(B, H, F, S, D);
+    GDN_REQUIRE(workspace_bytes >= need, GDN_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", name,
+                workspace_bytes, need);
+    GDN_REQUIRE(need == 0 || (workspace && gdn::aligned(workspace, 16)), GDN_EINVAL,
+                "%s: workspace must be a 16-byte aligned device pointer", name);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!work) {
+        // no frames: the final state is the initial one
+        if (!hT) return GDN_OK;
+        const size_t bytes = (size_t)B * H * D * (den ? 1 : D) * sizeof(float);
+        hipError_t e = h0 ? hipMemcpyAsync(hT, h0, bytes, hipMemcpyDeviceToDevice, s) : hipMemsetAsync(hT, 0, bytes, s);
+        return check_hip(e, name);
+    }
+    FrameArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.g = log_decay;
+    a.h0 = h0;
+    a.hT = hT;
+    a.out = out;
+    a.B = B;
+    a.H = H;
+    a.F = F;
+    a.S = S;
+    a.nsplit = frame_nsplit(B, H, F, S, D, &a.spl);
+    a.scale = scale;
+    a.reverse = reverse;
+    a.den = den;
+    const size_t units = (size_t)B * H * F;
+    float *ws = reinterpret_cast<float *>(workspace);
+    a.gh = ws;
+    a.sf = a.gh + units * 2 * D * D;
+    a.part = a.nsplit > 1 ? a.sf + units * D * D : a.gh;
+    const bool f32 = dtype == GDN_DTYPE_F32;
+    hipError_t e;
+    switch (D) {
+        case 16: e = f32 ? launch_frame<true, 16>(a, s) : launch_frame<false, 16>(a, s); break;
+        case 32: e = f32 ? launch_frame<true, 32>(a, s) : launch_frame<false, 32>(a, s); break;
+        case 64: e = f32 ? launch_frame<true, 64>(a, s) : launch_frame<false, 64>(a, s); break;
+        default: e = f32 ? launch_frame<true, 128>(a, s) : launch_frame<false, 128>(a, s); break;
+    }
+    return check_hip(e, name);
 }
 
 }  // namespace
@@ -642,68 +798,18 @@ extern "C" int gdn_recurrent_fwd(const void *q, const void *k, const void *v, co
                                  const float *log_decay, float scale, const float *h0, float *hT, float *out,
                                  int B, int H, int F, int S, int D, int dtype, int reverse, void *workspace,
                                  size_t workspace_bytes, void *stream) {
-    const char *name = "gdn_recurrent_fwd";
-    GDN_REQUIRE(B >= 0 && H >= 0 && F >= 0, GDN_EINVAL, "%s: negative size (B=%d H=%d F=%d)", name, B, H, F);
-    GDN_REQUIRE(S >= 1, GDN_EINVAL, "%s: S=%d (at least one token per frame)", name, S);
-    GDN_REQUIRE(dtype == GDN_DTYPE_F32 || dtype == GDN_DTYPE_BF16, GDN_EINVAL, "%s: unknown dtype %d", name, dtype);
-    GDN_REQUIRE(D == 16 || D == 32 || D == 64 || D == 128, GDN_EUNSUPPORTED,
-                "%s: D=%d (supported: 16, 32, 64, 128)", name, D);
-    GDN_REQUIRE(isfinite(scale), GDN_EINVAL, "%s: scale is not finite", name);
-    GDN_REQUIRE(reverse == 0 || reverse == 1, GDN_EINVAL, "%s: reverse=%d (0 or 1)", name, reverse);
-    GDN_REQUIRE(!reverse || (!h0 && !hT), GDN_EUNSUPPORTED,
-                "%s: the reverse scan takes no initial state and returns no final state", name);
-    if ((long)B * H == 0) return GDN_OK;
-    const bool work = (long)F > 0;
-    if (work) {
-        GDN_REQUIRE(q && k && v && beta && log_decay && out, GDN_EINVAL, "%s: null tensor pointer", name);
-        GDN_REQUIRE(gdn::aligned(q, 16) && gdn::aligned(k, 16) && gdn::aligned(v, 16) && gdn::aligned(out, 16),
-                    GDN_EINVAL, "%s: q, k, v and out must be 16-byte aligned", name);
-        GDN_REQUIRE(gdn::aligned(beta, 4) && gdn::aligned(log_decay, 4), GDN_EINVAL,
-                    "%s: beta and log_decay must be 4-byte aligned", name);
-    }
-    GDN_REQUIRE(!h0 || gdn::aligned(h0, 4), GDN_EINVAL, "%s: h0 misaligned", name);
-    GDN_REQUIRE(!hT || gdn::aligned(hT, 4), GDN_EINVAL, "%s: hT misaligned", name);
-    const size_t need = gdn::frame_workspace(B, H, F, S, D);
-    GDN_REQUIRE(workspace_bytes >= need, GDN_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", name,
-                workspace_bytes, need);
-    GDN_REQUIRE(need == 0 || (workspace && gdn::aligned(workspace, 16)), GDN_EINVAL,
-                "%s: workspace must be a 16-byte aligned device pointer", name);
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (!work) {
-        // no frames: the final state is the initial one
-        if (!hT) return GDN_OK;
-        const size_t bytes = (size_t)B * H * D * D * sizeof(float);
-        hipError_t e = h0 ? hipMemcpyAsync(hT, h0, bytes, hipMemcpyDeviceToDevice, s) : hipMemsetAsync(hT, 0, bytes, s);
-        return gdn::check_hip(e, name);
-    }
-    gdn::FrameArgs a;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.beta = beta;
-    a.g = log_decay;
-    a.h0 = h0;
-    a.hT = hT;
-    a.out = out;
-    a.B = B;
-    a.H = H;
-    a.F = F;
-    a.S = S;
-    a.nsplit = gdn::frame_nsplit(B, H, F, S, D, &a.spl);
-    a.scale = scale;
-    a.reverse = reverse;
-    const size_t units = (size_t)B * H * F;
-    float *ws = reinterpret_cast<float *>(workspace);
-    a.gh = ws;
-    a.sf = a.gh + units * 2 * D * D;
-    a.part = a.nsplit > 1 ? a.sf + units * D * D : a.gh;
-    const bool f32 = dtype == GDN_DTYPE_F32;
-    hipError_t e;
-    switch (D) {
-        case 16: e = f32 ? gdn::launch_frame<true, 16>(a, s) : gdn::launch_frame<false, 16>(a, s); break;
-        case 32: e = f32 ? gdn::launch_frame<true, 32>(a, s) : gdn::launch_frame<false, 32>(a, s); break;
-        case 64: e = f32 ? gdn::launch_frame<true, 64>(a, s) : gdn::launch_frame<false, 64>(a, s); break;
-        default: e = f32 ? gdn::launch_frame<true, 128>(a, s) : gdn::launch_frame<false, 128>(a, s); break;
-    }
-    return gdn::check_hip(e, name);
+    return gdn::frame_entry("gdn_recurrent_fwd", q, k, v, beta, log_decay, scale, h0, hT, out, B, H, F, S, D,
+                            dtype, reverse, 0, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t gdn_recurrent_den_fwd_workspace_bytes(int B, int H, int F, int S, int D, int dtype) {
+    return gdn_recurrent_fwd_workspace_bytes(B, H, F, S, D, dtype);
+}
+
+extern "C" int gdn_recurrent_den_fwd(const void *q_den, const void *k_z, const float *beta, const float *log_decay,
+                                     float scale, const float *z0, float *zT, float *den, int B, int H, int F, int S,
+                                     int D, int dtype, int reverse, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+    return gdn::frame_entry("gdn_recurrent_den_fwd", q_den, k_z, nullptr, beta, log_decay, scale, z0, zT, den, B, H,
+                            F, S, D, dtype, reverse, 1, workspace, workspace_bytes, stream);
 }

@@ -25,6 +25,7 @@ EXPORTS = (
     "gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes",
     "deltaproduct_chunk_fwd", "deltaproduct_chunk_fwd_workspace_bytes",
     "gdn_recurrent_fwd", "gdn_recurrent_fwd_workspace_bytes",
+    "gdn_recurrent_den_fwd", "gdn_recurrent_den_fwd_workspace_bytes",
     "gdn_prep",
 )
 
@@ -58,6 +59,10 @@ def _load():
     lib.gdn_recurrent_fwd.restype = I
     lib.gdn_recurrent_fwd_workspace_bytes.argtypes = [I] * 6
     lib.gdn_recurrent_fwd_workspace_bytes.restype = Z
+    lib.gdn_recurrent_den_fwd.argtypes = [P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, Z, P]
+    lib.gdn_recurrent_den_fwd.restype = I
+    lib.gdn_recurrent_den_fwd_workspace_bytes.argtypes = [I] * 6
+    lib.gdn_recurrent_den_fwd_workspace_bytes.restype = Z
     lib.gdn_prep.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P, P, P, P, I, I, I, I, I, I, P]
     lib.gdn_prep.restype = I
     return lib
@@ -203,6 +208,41 @@ def gdn_recurrent_fwd(q, k, v, beta, log_decay, scale=1.0, h0=None, output_final
                                 _ptr(ws), nws, _stream(q.device))
     _check("gdn_recurrent_fwd", rc)
     return out, hT
+
+
+def gdn_recurrent_den_fwd(q_den, k_z, beta, log_decay, scale=1.0, z0=None, output_final_state=True,
+                          reverse=False):
+    """Normaliser stream of the frame scan.  q_den, k_z (B,H,N,D); beta (B,H,N)
+    fp32; log_decay (B,H,F) fp32; z0 (B,H,D) fp32 or None.  Returns
+    (den (B,H,N) fp32, zT (B,H,D) or None).  reverse=True runs the
+    anti-causal direction (no z0, no zT)."""
+    if reverse:
+        output_final_state = False
+    _dev(q_den, k_z, beta, log_decay, z0)
+    _f32(beta, "beta"), _f32(log_decay, "log_decay"), _f32(z0, "z0")
+    B, H, N, D = q_den.shape
+    F = log_decay.shape[-1]
+    if F == 0 and N == 0:
+        S = 1
+    elif F <= 0 or N % F:
+        raise ValueError("N must be a multiple of the number of frames")
+    else:
+        S = N // F
+    if k_z.shape != q_den.shape or k_z.dtype != q_den.dtype:
+        raise ValueError("q_den and k_z shapes or dtypes disagree")
+    if beta.shape != (B, H, N) or log_decay.shape != (B, H, F):
+        raise ValueError("beta must be (B,H,N) and log_decay (B,H,F)")
+    if z0 is not None and z0.shape != (B, H, D):
+        raise ValueError("z0 must be (B,H,D)")
+    den = torch.empty((B, H, N), dtype=torch.float32, device=q_den.device)
+    zT = torch.empty((B, H, D), dtype=torch.float32, device=q_den.device) if output_final_state else None
+    dt = _dtype_code(q_den.dtype)
+    ws, nws = _workspace(_lib.gdn_recurrent_den_fwd_workspace_bytes(B, H, F, S, D, dt), q_den.device)
+    rc = _lib.gdn_recurrent_den_fwd(_ptr(q_den), _ptr(k_z), _ptr(beta), _ptr(log_decay), float(scale), _ptr(z0),
+                                    _ptr(zT), _ptr(den), B, H, F, S, D, dt, int(bool(reverse)), _ptr(ws), nws,
+                                    _stream(q_den.device))
+    _check("gdn_recurrent_den_fwd", rc)
+    return den, zT
 
 
 def gdn_prep(qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_scale, norm_eps,

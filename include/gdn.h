@@ -1,11 +1,13 @@
 /*
  * gdn.h - C ABI of the MI355X (gfx950) gated delta rule forward library.
  *
- * Four operations, each a forward pass over device-resident tensors:
+ * Four operations (and the scan's normaliser stream), each a forward pass
+ * over device-resident tensors:
  *
  *   gdn_chunk_fwd           chunkwise gated delta rule (r = 1)
  *   deltaproduct_chunk_fwd  chunkwise gated DeltaProduct (r sub-keys per token)
  *   gdn_recurrent_fwd       camera-branch numerator-only scan, frame-synchronous
+ *   gdn_recurrent_den_fwd   its normaliser (denominator) stream
  *   gdn_prep                camera-branch per-token prep (RMSNorm over all
  *                           channels, ReLU, K-scale, UCPE 4x4, RoPE, ||k||^2)
  *
@@ -15,6 +17,7 @@
  *         gated_chunk_fwd_o_fn.
  *   [cam] Sana "fused_cam_gdn.py": cam_prep_func, _cam_prep_kernel,
  *         cam_scan_func, _cam_scan_kernel.
+ *   [cp]  Sana "fused_gdn_cp.py": module docstring (KV and Z recurrences).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -169,6 +172,37 @@ int gdn_recurrent_fwd(const void *q, const void *k, const void *v,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 size_t gdn_recurrent_fwd_workspace_bytes(int B, int H, int F, int S, int D, int dtype);
+
+/*
+ * gdn_recurrent_den_fwd - normaliser (denominator) stream of the camera
+ * branch ([cp] module docstring: the Z recurrence next to the KV state, its
+ * per-frame transition decay_f (I - P_z) and input B_z = sum of k beta).
+ * Per (b, h), frame-synchronous like gdn_recurrent_fwd, with a vector state
+ * z in R^D (z = z0 or 0):
+ *   z_f = exp(g_f) (I - P_f) z_{f-1} + b_f,
+ *   P_f = sum_{s in f} beta_s kz_s kz_s^T,   b_f = sum_{s in f} beta_s kz_s;
+ *   den_s = scale * qd_s . z_f   for s in f;   zT = z_F.
+ * This is gdn_recurrent_fwd with every value equal to 1, so z is any column
+ * of that scan's state.  reverse = 1 runs the anti-causal direction exactly
+ * as gdn_recurrent_fwd does (no z0, no zT).  The caller forms
+ * num / (den + eps) itself, as on the page.
+ *
+ *   q_den, k_z  (B, H, N, D)  dtype   (the read-out and key rows of the
+ *                                      stream; the page's Z keys carry no RoPE)
+ *   beta        (B, H, N)     float32
+ *   log_decay   (B, H, F)     float32, one gate per frame
+ *   z0, zT      (B, H, D)     float32, nullable
+ *   den         (B, H, N)     float32
+ * Supported: D in {16, 32, 64, 128}; F >= 1; S >= 1.  Work space:
+ * gdn_recurrent_den_fwd_workspace_bytes.
+ */
+int gdn_recurrent_den_fwd(const void *q_den, const void *k_z,
+                          const float *beta, const float *log_decay, float scale,
+                          const float *z0, float *zT, float *den,
+                          int B, int H, int F, int S, int D, int dtype, int reverse,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+size_t gdn_recurrent_den_fwd_workspace_bytes(int B, int H, int F, int S, int D, int dtype);
 
 /*
  * gdn_prep - camera-branch prep ([cam] cam_prep_func, _cam_prep_kernel),

@@ -18,6 +18,7 @@ receives; outputs are float64):
 * :func:`cam_prep`                 - O3, camera-branch prep per token.
 * :func:`frame_scan`               - O4, frame-synchronous numerator-only scan.
 * :func:`frame_scan_reverse`       - O4 in the anti-causal direction.
+* :func:`frame_den`                - the normaliser (Z) stream of O4.
 * :func:`invert_se3`               - closed-form rigid-transform inverse.
 """
 from __future__ import annotations
@@ -200,6 +201,25 @@ def frame_scan_reverse(q, k, v, beta, g, F, scale=1.0, nthreads=0):
     out_b, _ = frame_scan(flat(q_b), flat(k_b), flat(v_b), np.ascontiguousarray(beta_b.reshape(B, H, N)),
                           np.ascontiguousarray(g_b), F, scale, None, nthreads)
     return np.ascontiguousarray(np.flip(out_b.reshape(B, H, F, S, D), axis=2).reshape(B, H, N, D))
+
+
+def frame_den(q_den, k_z, beta, g, F, scale=1.0, z0=None, reverse=False, nthreads=0):
+    """Normaliser stream ([cp] module docstring: z_f = decay_f (I - P_z) z_{f-1}
+    + B_z with P_z = sum beta k k^T and B_z = sum beta k over the frame, read
+    out as den = q . z).  It is O4 with every value equal to 1: H_f = sum
+    beta_s k_s 1^T has B_z in every column, so each column of the O4 state is
+    z; den is column 0 of the O4 output.  q_den, k_z (B,H,N,D); z0 (B,H,D).
+    Returns (den (B,H,N), zT (B,H,D) or None for the reverse direction)."""
+    q_den, k_z, beta, g, z0 = map(_f32, (q_den, k_z, beta, g, z0))
+    B, H, N, D = q_den.shape
+    ones = np.ones((B, H, N, D), np.float32)
+    if reverse:
+        assert z0 is None
+        out = frame_scan_reverse(q_den, k_z, ones, beta, g, F, scale, nthreads)
+        return np.ascontiguousarray(out[..., 0]), None
+    h0 = None if z0 is None else np.ascontiguousarray(np.repeat(z0[..., :, None], D, axis=-1))
+    out, hT = frame_scan(q_den, k_z, ones, beta, g, F, scale, h0, nthreads)
+    return np.ascontiguousarray(out[..., 0]), np.ascontiguousarray(hT[..., :, 0])
 
 
 def invert_se3(P):

@@ -271,3 +271,71 @@ def test_scan_reverse_rejects_states(gdn):
                               to_dev(g, "f32"), 1.0, to_dev(h0, "f32"), reverse=True)
     assert ei.value.code == -2                                          # GDN_EUNSUPPORTED
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# normaliser (Z) stream
+# ---------------------------------------------------------------------------
+
+def _den_gpu(gdn, q, k, beta, g, dtype, scale=1.0, z0=None, reverse=False):
+    import torch
+    den, zT = gdn.gdn_recurrent_den_fwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(beta, "f32"), to_dev(g, "f32"),
+                                        scale, None if z0 is None else to_dev(z0, "f32"), reverse=reverse)
+    torch.cuda.synchronize()
+    return to_np(den), (None if zT is None else to_np(zT))
+
+
+@pytest.mark.parametrize("case", [
+    # (B, H, F, S, D, dtype, with z0, reverse)
+    (1, 2, 3, 5, 16, "f32", True, False),
+    (2, 2, 4, 33, 32, "f32", False, False),
+    (1, 3, 5, 70, 64, "f32", True, False),
+    (1, 2, 3, 40, 128, "f32", True, False),
+    (1, 2, 3, 5, 16, "bf16", True, False),
+    (2, 4, 6, 100, 64, "bf16", True, False),
+    (1, 2, 3, 257, 128, "bf16", False, False),
+    (1, 3, 5, 70, 64, "f32", False, True),
+    (2, 4, 6, 100, 64, "bf16", False, True),
+    (1, 2, 3, 257, 128, "bf16", False, True),
+], ids=lambda c: "B{}H{}F{}S{}D{}{}z{}r{}".format(*c))
+def test_den_small(gdn, case):
+    B, H, F, S, D, dtype, with_z0, rev = case
+    _say(f"gdn_recurrent_den_fwd small case {case}")
+    q, k, _, beta, g, _ = _scan_inputs(B, H, F, S, D, 800 + S + D, dtype)
+    z0 = np.random.default_rng(S).normal(0, 0.3, (B, H, D)).astype(np.float32) if with_z0 else None
+    den, zT = _den_gpu(gdn, q, k, beta, g, dtype, 0.9, z0, rev)
+    dref, zref = oracle.frame_den(q, k, beta, g, F, 0.9, z0, reverse=rev)
+    e = max_rel_err(den, dref)
+    _say(f"  {case}: max rel err den={e:.2e}")
+    assert e <= TOL[dtype], e
+    if not rev:
+        assert max_rel_err(zT, zref) <= TOL[dtype]
+    else:
+        assert zT is None and np.all(den[:, :, (F - 1) * S:] == 0.0)
+
+
+def test_den_camera_workload(gdn):
+    """The normaliser stream at the camera workload's size, with the prep's
+    q and k as its read-out and key rows (the workload defines no separate
+    normaliser rows)."""
+    _say("gdn_recurrent_den_fwd at the camera workload size")
+    d = synth.workload_inputs("camera")
+    pr = _prep_ref(d)
+    q, k = (synth.round_bf16(pr[n]) for n in ("q", "k"))
+    den, zT = _den_gpu(gdn, q, k, d["beta"], d["g"], "bf16")
+    dref, zref = oracle.frame_den(q, k, d["beta"], d["g"], d["F"], 1.0)
+    S = d["S"]
+    per_frame = [max_rel_err(den[:, :, f * S:(f + 1) * S], dref[:, :, f * S:(f + 1) * S]) for f in range(d["F"])]
+    _say("  camera den: per frame " + " ".join(f"{e:.1e}" for e in per_frame) + f" zT={max_rel_err(zT, zref):.1e}")
+    assert max(per_frame) <= TOL["bf16"] and max_rel_err(zT, zref) <= TOL["bf16"]
+
+
+def test_den_equals_unit_value_scan_on_gpu(gdn):
+    """GPU against GPU: the normaliser stream is the numerator scan with every
+    value equal to 1 (any output column)."""
+    B, H, F, S, D = 1, 2, 4, 50, 64
+    q, k, _, beta, g, _ = _scan_inputs(B, H, F, S, D, 77, "bf16")
+    ones = np.ones((B, H, F * S, D), np.float32)
+    out, _ = _scan_gpu(gdn, q, k, ones, beta, g, "bf16")
+    den, _ = _den_gpu(gdn, q, k, beta, g, "bf16")
+    assert max_rel_err(den, out[..., 5]) <= TOL["bf16"]

@@ -546,6 +546,56 @@ def test_frame_scan_reverse_mirrors_the_forward_scan():
 
 
 # --------------------------------------------------------------------------
+# normaliser (Z) stream ([cp] module docstring)
+# --------------------------------------------------------------------------
+
+def test_frame_den_follows_the_vector_recurrence():
+    # the page's Z recurrence written out for the vector state, in fp64
+    B, H, F, S, D = 1, 2, 4, 5, 6
+    rng = _rng(41)
+    q, k = (_f32(rng.standard_normal((B, H, F * S, D)) * 0.5) for _ in range(2))
+    beta = _f32(rng.uniform(0, 1, (B, H, F * S)))
+    g = _f32(-rng.uniform(0, 1, (B, H, F)))
+    z0 = _f32(rng.standard_normal((B, H, D)))
+    den, zT = oracle.frame_den(q, k, beta, g, F, 0.6, z0)
+    for h in range(H):
+        z = z0[0, h].astype(np.float64)
+        for f in range(F):
+            sl = slice(f * S, (f + 1) * S)
+            kf, bf = k[0, h, sl].astype(np.float64), beta[0, h, sl].astype(np.float64)
+            P = (kf * bf[:, None]).T @ kf
+            z = np.exp(np.float64(g[0, h, f])) * (np.eye(D) - P) @ z + kf.T @ bf
+            np.testing.assert_allclose(den[0, h, sl], 0.6 * q[0, h, sl].astype(np.float64) @ z, atol=1e-12)
+        np.testing.assert_allclose(zT[0, h], z, atol=1e-12)
+
+
+def test_frame_den_closed_forms():
+    B, H, F, S, D = 1, 1, 3, 7, 8
+    rng = _rng(42)
+    q, k = (_f32(rng.standard_normal((B, H, F * S, D))) for _ in range(2))
+    beta = _f32(rng.uniform(0, 1, (B, H, F * S)))
+    g = _f32(-rng.uniform(0, 1, (B, H, F)))
+    # one frame from zero: den = q . sum_s beta_s k_s
+    d1, _ = oracle.frame_den(q[..., :S, :], k[..., :S, :], beta[..., :S], g[..., :1], 1, 1.0)
+    ref = q[0, 0, :S].astype(np.float64) @ (k[0, 0, :S].astype(np.float64).T @ beta[0, 0, :S].astype(np.float64))
+    np.testing.assert_allclose(d1[0, 0], ref, atol=1e-12)
+    # beta = 0: the decayed initial state only
+    z0 = _f32(rng.standard_normal((B, H, D)))
+    d0, zT = oracle.frame_den(q, k, np.zeros_like(beta), g, F, 1.0, z0)
+    decay = np.exp(np.cumsum(g[0, 0].astype(np.float64)))
+    for f in range(F):
+        ref = decay[f] * (q[0, 0, f * S:(f + 1) * S].astype(np.float64) @ z0[0, 0].astype(np.float64))
+        np.testing.assert_allclose(d0[0, 0, f * S:(f + 1) * S], ref, atol=1e-12)
+    np.testing.assert_allclose(zT[0, 0], decay[-1] * z0[0, 0], atol=1e-12)
+    # reverse: the last frame reads nothing; the one before reads b of the last frame
+    dr, _ = oracle.frame_den(q, k, beta, g, F, 1.0, reverse=True)
+    assert np.all(dr[0, 0, (F - 1) * S:] == 0.0)
+    bl = k[0, 0, (F - 1) * S:].astype(np.float64).T @ beta[0, 0, (F - 1) * S:].astype(np.float64)
+    np.testing.assert_allclose(dr[0, 0, (F - 2) * S:(F - 1) * S], q[0, 0, (F - 2) * S:(F - 1) * S].astype(np.float64) @ bl,
+                               atol=1e-12)
+
+
+# --------------------------------------------------------------------------
 # A planted mistake must be caught: the pins are not vacuous.
 # --------------------------------------------------------------------------
 
