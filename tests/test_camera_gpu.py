@@ -339,3 +339,20 @@ def test_den_equals_unit_value_scan_on_gpu(gdn):
     out, _ = _scan_gpu(gdn, q, k, ones, beta, g, "bf16")
     den, _ = _den_gpu(gdn, q, k, beta, g, "bf16")
     assert max_rel_err(den, out[..., 5]) <= TOL["bf16"]
+
+
+def test_scan_long_token_ranges(gdn):
+    """Frames long enough that each gram workgroup walks several rounds of
+    staged token steps (an odd number here: 1500 tokens in ranges of 384),
+    forward, reverse and normaliser stream."""
+    B, H, F, S, D = 1, 16, 8, 1500, 64
+    _say(f"frame scan with long token ranges B{B} H{H} F{F} S{S} D{D}")
+    q, k, v, beta, g, h0 = _scan_inputs(B, H, F, S, D, 91, "bf16", 0.1)
+    out, hT = _scan_gpu(gdn, q, k, v, beta, g, "bf16", 1.0, h0)
+    oref, href = oracle.frame_scan(q, k, v, beta, g, F, 1.0, h0)
+    assert max_rel_err(out, oref) <= TOL["bf16"] and max_rel_err(hT, href) <= TOL["bf16"]
+    out_r = _scan_rev_gpu(gdn, q, k, v, beta, g, "bf16")
+    assert max_rel_err(out_r, oracle.frame_scan_reverse(q, k, v, beta, g, F, 1.0)) <= TOL["bf16"]
+    den, _ = _den_gpu(gdn, q, k, beta, g, "bf16")
+    dref, _ = oracle.frame_den(q, k, beta, g, F, 1.0)
+    assert max_rel_err(den, dref) <= TOL["bf16"]
