@@ -33,7 +33,10 @@
 //      O = scale (diag(e^G) Q S_start + sum_b P_b V_new_b)  -> HBM
 //      the global loads of the next chunks (register prefetch, LDS commit)
 //      and the chunk-local cumsum of the next chunk.
-//    Three workgroup barriers per chunk separate the phases.
+//    Three workgroup barriers per chunk separate the phases.  They hand over
+//    LDS only (no wave reads global memory that another wave writes), so
+//    they wait for LDS operations alone and leave the output stores and the
+//    prefetch loads in flight.
 //
 // V_new = T diag(beta) (V - diag(e^G) E S) is the page's u - w h with
 // w = T diag(beta e^G) E and u = T diag(beta) V, regrouped so that W is never
@@ -573,15 +576,18 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
                     store_op<F32IN>(PqH, PqL, (bb * C + t) * LDPQ + s, val);
                 }
             }
-            // Q S_start for the output tile of this wave
+        }
+        lds_barrier();
+        // ================= phase 2 =================
+        if (!chain) {
+            // Q S_start for the output tile of this wave (the output group is
+            // otherwise idle while the chain forms V_new)
             if (ow < NTT) {
                 a1[0] = zero4();
                 if constexpr (F32IN) mma_f32(a1[0], Qs + ow * 16 * LDK, LDK, StH, LDST, KD);
                 else mma_bf16_split(a1[0], Qs + ow * 16 * LDK, nullptr, LDK, StH, StL, LDST, KD);
             }
         }
-        __syncthreads();
-        // ================= phase 2 =================
         if (chain) {
             // V_new = T R, rows of virtual tile w
             if (w < NB) {
@@ -598,7 +604,7 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         // ================= phase 3 =================
         if (chain) {
             const float gL = gp[C * R + 3 * C];
@@ -615,8 +621,24 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
                         for (int kk = 0; kk < C; kk += 4)
                             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[kk * LDK], pb[kk], acc, 0, 0, 0);
                     } else {
-                        mma_bf16_at_split(acc, ks + ts * 16, LDK, VtH + bb * BV * LDVT, VtL + bb * BV * LDVT,
-                                          LDVT, C);
+                        if constexpr (C % 32 == 0) {
+                            // A = K_b^T: lane (g, j) takes column ts*16 + j of token rows
+                            // kk + 8g .. +7 with two transposed LDS reads
+                            const int l = lane_id(), g = l >> 4, c16 = l & 15;
+                            const u16 *bh = VtH + bb * BV * LDVT + c16 * LDVT, *bl = VtL + bb * BV * LDVT + c16 * LDVT;
+#pragma unroll
+                            for (int kk = 0; kk < C; kk += 32) {
+                                const u16 *pa = ks + (kk + 8 * g + (c16 >> 2)) * LDK + ts * 16 + 4 * (c16 & 3);
+                                const uint2 x0 = __builtin_bit_cast(uint2, ld_tr16(pa));
+                                const uint2 x1 = __builtin_bit_cast(uint2, ld_tr16(pa + 4 * LDK));
+                                const bf16x8 ah = __builtin_bit_cast(bf16x8, uint4{x0.x, x0.y, x1.x, x1.y});
+                                acc = mfma32(ah, ld8(bh + kk + 8 * g), acc);
+                                acc = mfma32(ah, ld8(bl + kk + 8 * g), acc);
+                            }
+                        } else {
+                            mma_bf16_at_split(acc, ks + ts * 16, LDK, VtH + bb * BV * LDVT, VtL + bb * BV * LDVT,
+                                              LDVT, C);
+                        }
                     }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) Sreg[n][e] = gL * Sreg[n][e] + acc[e];
@@ -624,6 +646,11 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
             }
             write_state_operand();
         } else {
+            // stage the next chunk first, so that its wait for the prefetched
+            // loads does not also wait for this chunk's output stores (the
+            // commit writes the other Ks/gate buffer and Qs, Vs, Tb, none of
+            // which the output below reads)
+            if (c + 1 < NT) commit(p ^ 1);
             // finish the output of chunk c
             if (ow < NTT) {
                 floatx4 a2 = zero4();
@@ -647,11 +674,10 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
                     }
                 }
             }
-            // stage the next chunk and start loading the one after
-            if (c + 1 < NT) commit(p ^ 1);
+            // start loading the chunk after the next
             if (c + 2 < NT) prefetch(c + 2);
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     if (chain && args.hT) {
