@@ -713,6 +713,12 @@ hipError_t launch_frame(FrameArgs a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// hT = h0 (or 0 without h0): the final state of a scan over no frames.
+__global__ __launch_bounds__(256) void state_copy_kernel(const float *h0, float *hT, size_t n) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) hT[i] = h0 ? h0[i] : 0.f;
+}
+
 // Shared body of the two scan entry points (checks, work space carving, launch).
 int frame_entry(const char *name, const void *q, const void *k, const void *v, const float *beta,
                 const float *log_decay, float scale, const float *h0, float *hT, float *out, int B, int H, int F,
@@ -748,9 +754,11 @@ int frame_entry(const char *name, const void *q, const void *k, const void *v, c
     if (!work) {
         // no frames: the final state is the initial one
         if (!hT) return GDN_OK;
-        const size_t bytes = (size_t)B * H * D * (den ? 1 : D) * sizeof(float);
-        hipError_t e = h0 ? hipMemcpyAsync(hT, h0, bytes, hipMemcpyDeviceToDevice, s) : hipMemsetAsync(hT, 0, bytes, s);
-        return check_hip(e, name);
+        // (a kernel rather than a memset or copy node, so that a captured
+        // graph holds kernels only)
+        const size_t n = (size_t)B * H * D * (den ? 1 : D);
+        hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, h0, hT, n);
+        return check_hip(hipGetLastError(), name);
     }
     FrameArgs a;
     a.q = q;

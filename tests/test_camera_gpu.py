@@ -210,6 +210,13 @@ def test_scan_split_resume_and_edges(gdn):
                         1.0, h0)
     assert out.shape == (B, H, 0, D)
     np.testing.assert_array_equal(hT, h0)
+    out, hT = _scan_gpu(gdn, z, z, z, np.zeros((B, H, 0), np.float32), np.zeros((B, H, 0), np.float32), "bf16")
+    assert np.all(hT == 0.0)
+    # the normaliser stream over no frames: zT = z0
+    z0 = np.random.default_rng(3).standard_normal((B, H, D)).astype(np.float32)
+    den, zT = _den_gpu(gdn, z, z, np.zeros((B, H, 0), np.float32), np.zeros((B, H, 0), np.float32), "bf16", 1.0, z0)
+    assert den.shape == (B, H, 0)
+    np.testing.assert_array_equal(zT, z0)
 
 
 # ---------------------------------------------------------------------------
