@@ -9,7 +9,8 @@
 //   frame_gram_bf16_kernel / frame_gram_kernel (fp32 inputs)
 //                       parallel over (b, h, f, token range): partial G_f and
 //                       H_f from K^T diag(beta) K and K^T diag(beta) V (MFMA);
-//   frame_reduce_kernel sums the partials of the token ranges;
+//   frame_reduce_kernel sums the partials of more than two token ranges (the
+//                       state pass adds two itself);
 //   frame_state_kernel  per (b, h, 16-column slice of S), sequential over
 //                       frames: S_f = e^{g_f} (S - G_f S) + H_f in fp32 (fp32
 //                       MFMA), stores S_f and the final state;
@@ -354,20 +355,37 @@ __global__ __launch_bounds__(256) void frame_reduce_kernel(FrameArgs a) {
 
 // G_f (all of it) and the H_f slice of columns j0 .. j0+15 as float4 per
 // thread (row idx / 4 of H, columns j0 + 4 (idx % 4) ..).
+// With two token ranges per frame the state pass adds the two partials
+// itself (no reduction kernel): both are loaded unconditionally (the second
+// pointer repeats the first with one range) and the second is added when
+// present.
 template <int D, int NG4, int NH4>
-__device__ __forceinline__ void state_fetch(const float *ghf, int j0, int tid, floatx4 (&gr)[NG4],
-                                            floatx4 (&hr)[NH4]) {
-    const floatx4 *gp = reinterpret_cast<const floatx4 *>(ghf);
+__device__ __forceinline__ void state_fetch(const float *p0, const float *p1, bool two, int j0, int tid,
+                                            floatx4 (&gr)[NG4], floatx4 (&hr)[NH4]) {
+    const floatx4 *g0 = reinterpret_cast<const floatx4 *>(p0), *g1 = reinterpret_cast<const floatx4 *>(p1);
+    floatx4 x0[NG4], x1[NG4], y0[NH4], y1[NH4];
 #pragma unroll
     for (int i = 0; i < NG4; ++i) {
         const int idx = tid + 256 * i;
-        if (idx < D * D / 4) gr[i] = gp[idx];
+        if (idx < D * D / 4) {
+            x0[i] = g0[idx];
+            x1[i] = g1[idx];
+        }
     }
 #pragma unroll
     for (int i = 0; i < NH4; ++i) {
         const int idx = tid + 256 * i;
-        if (idx < D * 4) hr[i] = gp[(D * D + (idx >> 2) * D + j0) / 4 + (idx & 3)];
+        if (idx < D * 4) {
+            const int o = (D * D + (idx >> 2) * D + j0) / 4 + (idx & 3);
+            y0[i] = g0[o];
+            y1[i] = g1[o];
+        }
     }
+    const float w1 = two ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 0; i < NG4; ++i) gr[i] = x0[i] + w1 * x1[i];
+#pragma unroll
+    for (int i = 0; i < NH4; ++i) hr[i] = y0[i] + w1 * y1[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -408,8 +426,17 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
     // only stores the zero state for the last frame, step i >= 1 folds in
     // frame F - i with its own gate and stores the state of frame F - 1 - i.
     const bool rev = a.reverse != 0;
+    // G_f and the H_f slice of frame f: the reduced sums, or (two ranges, no
+    // reduction kernel) the two partials added here
+    const bool two = a.nsplit == 2;
+    const float *src = two ? a.part : a.gh;
+    const int nsrc = two ? 2 : 1;
+    auto fetch = [&](int f) __attribute__((always_inline)) {
+        const float *p0 = src + ((size_t)bh * a.F + f) * nsrc * 2 * D * D;
+        state_fetch<D, NG4, NH4>(p0, p0 + (two ? 2 * D * D : 0), two, j0, tid, gr, hr);
+    };
     if ((rev ? 1 : 0) < a.F)
-        state_fetch<D, NG4, NH4>(a.gh + ((size_t)bh * a.F + (rev ? a.F - 1 : 0)) * 2 * D * D, j0, tid, gr, hr);
+        fetch(rev ? a.F - 1 : 0);
     for (int i = 0; i < a.F; ++i) {
         const bool upd = !rev || i > 0;          // uniform over the workgroup
         const int kf = rev ? a.F - i : i, of = rev ? a.F - 1 - i : i;
@@ -438,8 +465,7 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
         }
         lds_barrier();                  // the prefetch below stays in flight across barriers
         if (upd && i + 1 < a.F)
-            state_fetch<D, NG4, NH4>(a.gh + ((size_t)bh * a.F + (rev ? a.F - 1 - i : i + 1)) * 2 * D * D, j0, tid,
-                                     gr, hr);
+            fetch(rev ? a.F - 1 - i : i + 1);
         const float dec = upd ? expf(a.g[(size_t)bh * a.F + kf]) : 1.f;
         const size_t unit = (size_t)bh * a.F + of;
 #pragma unroll
@@ -653,13 +679,13 @@ __global__ __launch_bounds__(256) void frame_den_kernel(FrameArgs a) {
     }
 }
 
-// Token ranges of the gram kernels: enough workgroups to fill the chip
-// (about two per compute unit), whole rounds of staged steps per range.
+// Token ranges of the gram kernels: about one eight-wave workgroup per
+// compute unit, whole rounds of staged steps per range.
 int frame_nsplit(int B, int H, int F, int S, int D, int *spl_out) {
     const long units = (long)B * H * F;
     const int RND = gram_round(D);
     const int maxsp = (S + RND - 1) / RND;
-    long want = units > 0 ? (512 + units - 1) / units : 1;
+    long want = units > 0 ? (256 + units - 1) / units : 1;
     if (want > maxsp) want = maxsp;
     if (want < 1) want = 1;
     const int per = (int)((S + want - 1) / want);
@@ -692,7 +718,7 @@ hipError_t launch_frame(FrameArgs a, hipStream_t s) {
     const int units = a.B * a.H * a.F;
     hipError_t e = a.den ? launch_gram<F32IN, D, true>(a, s) : launch_gram<F32IN, D, false>(a, s);
     if (e != hipSuccess) return e;
-    if (a.nsplit > 1) {
+    if (a.nsplit > 2) {                        // two ranges: the state pass adds them
         const size_t n4 = (size_t)units * 2 * D * D / 4;
         hipLaunchKernelGGL((frame_reduce_kernel<D>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, a);
         e = hipGetLastError();
