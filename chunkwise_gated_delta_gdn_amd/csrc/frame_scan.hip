@@ -355,37 +355,40 @@ __global__ __launch_bounds__(256) void frame_reduce_kernel(FrameArgs a) {
 
 // G_f (all of it) and the H_f slice of columns j0 .. j0+15 as float4 per
 // thread (row idx / 4 of H, columns j0 + 4 (idx % 4) ..).
-// With two token ranges per frame the state pass adds the two partials
-// itself (no reduction kernel): both are loaded unconditionally (the second
-// pointer repeats the first with one range) and the second is added when
-// present.
+// The loads of one frame's operands: the gate, then G_f and the H_f slice
+// of columns j0 .. j0+15 as float4 per thread (H row idx / 4, columns
+// j0 + 4 (idx % 4) ..) from one or two token-range partials.  With two
+// ranges the state pass adds them itself (no reduction kernel) when it
+// stores them to LDS; both are loaded unconditionally (the second pointer
+// repeats the first with one range).  The gate goes out first: waiting for
+// it later does not wait for the operand loads behind it.
+template <int NG4, int NH4>
+struct FrameOps {
+    floatx4 g0[NG4], g1[NG4], h0[NH4], h1[NH4];
+    float gate;
+};
 template <int D, int NG4, int NH4>
-__device__ __forceinline__ void state_fetch(const float *p0, const float *p1, bool two, int j0, int tid,
-                                            floatx4 (&gr)[NG4], floatx4 (&hr)[NH4]) {
-    const floatx4 *g0 = reinterpret_cast<const floatx4 *>(p0), *g1 = reinterpret_cast<const floatx4 *>(p1);
-    floatx4 x0[NG4], x1[NG4], y0[NH4], y1[NH4];
+__device__ __forceinline__ void state_fetch(const float *gate, const float *p0, const float *p1, int j0, int tid,
+                                            FrameOps<NG4, NH4> &o) {
+    o.gate = *gate;
+    const floatx4 *q0 = reinterpret_cast<const floatx4 *>(p0), *q1 = reinterpret_cast<const floatx4 *>(p1);
 #pragma unroll
     for (int i = 0; i < NG4; ++i) {
         const int idx = tid + 256 * i;
-        if (idx < D * D / 4) {
-            x0[i] = g0[idx];
-            x1[i] = g1[idx];
+        if (NG4 * 256 == D * D / 4 || idx < D * D / 4) {
+            o.g0[i] = q0[idx];
+            o.g1[i] = q1[idx];
         }
     }
 #pragma unroll
     for (int i = 0; i < NH4; ++i) {
         const int idx = tid + 256 * i;
-        if (idx < D * 4) {
-            const int o = (D * D + (idx >> 2) * D + j0) / 4 + (idx & 3);
-            y0[i] = g0[o];
-            y1[i] = g1[o];
+        if (NH4 * 256 == D * 4 || idx < D * 4) {
+            const int off = (D * D + (idx >> 2) * D + j0) / 4 + (idx & 3);
+            o.h0[i] = q0[off];
+            o.h1[i] = q1[off];
         }
     }
-    const float w1 = two ? 1.f : 0.f;
-#pragma unroll
-    for (int i = 0; i < NG4; ++i) gr[i] = x0[i] + w1 * x1[i];
-#pragma unroll
-    for (int i = 0; i < NH4; ++i) hr[i] = y0[i] + w1 * y1[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -418,7 +421,11 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
                 S[n][e] = a.den ? a.h0[(size_t)bh * D + row] : a.h0[((size_t)bh * D + row) * D + j0 + (l & 15)];
             }
     }
-    floatx4 gr[NG4], hr[NH4];    // native vectors: arrays of HIP float4 structs end up in scratch
+    // the initial state is complete before the frame loop: otherwise the
+    // compiler treats the state registers as possibly pending in every
+    // iteration and waits for the operand prefetch before each update
+    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
+    FrameOps<NG4, NH4> ops;      // native vectors: arrays of HIP float4 structs end up in scratch
     // Step i folds in the keys and values of frame kf and stores the state
     // that frame of reads.  Forward: kf = of = i.  Reverse (the page's
     // flip-and-shift: q flipped; k, v, beta flipped and shifted by one frame
@@ -431,28 +438,30 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
     const bool two = a.nsplit == 2;
     const float *src = two ? a.part : a.gh;
     const int nsrc = two ? 2 : 1;
+    const float w1 = two ? 1.f : 0.f;
     auto fetch = [&](int f) __attribute__((always_inline)) {
         const float *p0 = src + ((size_t)bh * a.F + f) * nsrc * 2 * D * D;
-        state_fetch<D, NG4, NH4>(p0, p0 + (two ? 2 * D * D : 0), two, j0, tid, gr, hr);
+        state_fetch<D, NG4, NH4>(a.g + (size_t)bh * a.F + f, p0, p0 + (two ? 2 * D * D : 0), j0, tid, ops);
     };
     if ((rev ? 1 : 0) < a.F)
         fetch(rev ? a.F - 1 : 0);
     for (int i = 0; i < a.F; ++i) {
         const bool upd = !rev || i > 0;          // uniform over the workgroup
-        const int kf = rev ? a.F - i : i, of = rev ? a.F - 1 - i : i;
+        const int of = rev ? a.F - 1 - i : i;    // (operands: frame rev ? F - i : i, fetched ahead)
         if (upd) {
 #pragma unroll
             for (int j = 0; j < NG4; ++j) {
                 const int idx = tid + 256 * j;
                 if (idx < D * D / 4) {
                     const int r = (idx * 4) / D, c = (idx * 4) % D;
-                    *reinterpret_cast<floatx4 *>(Gs + r * LDG + c) = gr[j];
+                    *reinterpret_cast<floatx4 *>(Gs + r * LDG + c) = ops.g0[j] + w1 * ops.g1[j];
                 }
             }
 #pragma unroll
             for (int j = 0; j < NH4; ++j) {
                 const int idx = tid + 256 * j;
-                if (idx < D * 4) *reinterpret_cast<floatx4 *>(Hs + (idx >> 2) * LDS_ + 4 * (idx & 3)) = hr[j];
+                if (idx < D * 4)
+                    *reinterpret_cast<floatx4 *>(Hs + (idx >> 2) * LDS_ + 4 * (idx & 3)) = ops.h0[j] + w1 * ops.h1[j];
             }
         }
         // current state slice into LDS as the B operand ([k][col])
@@ -463,10 +472,10 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Sl[(ti * 16 + 4 * (l >> 4) + e) * LDS_ + (l & 15)] = S[n][e];
         }
+        const float dec = upd ? expf(ops.gate) : 1.f;   // this frame's gate, loaded with its operands
         lds_barrier();                  // the prefetch below stays in flight across barriers
         if (upd && i + 1 < a.F)
             fetch(rev ? a.F - 1 - i : i + 1);
-        const float dec = upd ? expf(a.g[(size_t)bh * a.F + kf]) : 1.f;
         const size_t unit = (size_t)bh * a.F + of;
 #pragma unroll
         for (int n = 0; n < PERW; ++n) {
