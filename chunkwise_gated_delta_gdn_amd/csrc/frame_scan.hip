@@ -169,8 +169,8 @@ __global__ __launch_bounds__(256) void frame_gram_kernel(FrameArgs a) {
 // partial G_f and H_f for bf16 inputs.  G = K^T diag(beta) K and
 // H = K^T diag(beta) V contract over tokens, so both MFMA operands need 8
 // consecutive tokens of one feature per lane: the token rows are staged
-// row-major in LDS (64 tokens a step, two buffers) and read back transposed
-// with ds_read_b64_tr_b16.  A = K^T (exact bf16); B = beta (.) K or
+// row-major in LDS (64 tokens a step, two buffers, 16-byte pieces
+// XOR-swizzled per row) and read back transposed with ds_read_b64_tr_b16.  A = K^T (exact bf16); B = beta (.) K or
 // beta (.) V, scaled in fp32 after the transposed read and split hi + lo.
 // Wave w owns whole column tiles ("jobs": matrix G or H, column tile tj;
 // eight waves at D >= 32, one job each at D = 64); every wave reads the A
@@ -195,9 +195,20 @@ __global__ __launch_bounds__(512) void frame_gram_bf16_kernel(FrameArgs a) {
     constexpr int NW = gram_waves<D>(), NTH = 64 * NW;   // waves, threads
     constexpr int NT1 = D / 16;                 // row tiles = column tiles of one matrix
     constexpr int NJOB = 2 * NT1, JPW = (NJOB + NW - 1) / NW;
-    // row stride: 4 rows of 32 bytes (one 16-lane transposed read) fall on
-    // distinct banks for 32 or 64 banks of 4 bytes
-    constexpr int LDR = D == 16 ? 16 : D + 16;
+    // Rows are unpadded; the 16-byte piece p of row r sits at p ^ swz(r), so
+    // that the 8 rows x 32 bytes that 32 lanes of a transposed read take
+    // (rows 8g + {0..3} of two lane groups) cover all 64 banks once.
+    constexpr int LDR = D;
+    auto swz = [](int r) __attribute__((always_inline)) {
+        if constexpr (D == 128) return 2 * ((r & 3) | (((r >> 3) & 1) << 2));
+        else if constexpr (D == 64) return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
+        else if constexpr (D == 32) return 2 * ((r >> 3) & 1);
+        else return 0;
+    };
+    // element offset of (row r, column c) in a staged buffer
+    auto at = [&](int r, int c) __attribute__((always_inline)) {
+        return r * LDR + ((((c >> 3) ^ swz(r))) << 3) + (c & 7);
+    };
     constexpr int SEGS = D / 8;                 // 16-byte pieces per token row
     constexpr int PPT = 2 * TSG * SEGS / NTH;   // pieces of k and v per thread per step
     constexpr int SPW = gram_steps<D>(), RND = SPW * TSG;
@@ -246,7 +257,7 @@ __global__ __launch_bounds__(512) void frame_gram_bf16_kernel(FrameArgs a) {
         for (int i = 0; i < PPT; ++i) {
             const int p = tid + NTH * i;
             const int mat = p / (TSG * SEGS), rem = p % (TSG * SEGS), r = rem / SEGS, sg = rem % SEGS;
-            if (!VONES || !mat) *reinterpret_cast<u32x4 *>((mat ? Vs[buf] : Ks[buf]) + r * LDR + sg * 8) = st.x[u][i];
+            if (!VONES || !mat) *reinterpret_cast<u32x4 *>((mat ? Vs[buf] : Ks[buf]) + at(r, sg * 8)) = st.x[u][i];
         }
         if (tid < TSG) Bs[buf][tid] = st.b[u];
     };
@@ -259,8 +270,8 @@ __global__ __launch_bounds__(512) void frame_gram_bf16_kernel(FrameArgs a) {
             bf16x8 af[NT1];
 #pragma unroll
             for (int ti = 0; ti < NT1; ++ti) {
-                const uint2 x0 = __builtin_bit_cast(uint2, ld_tr16(ks + ra * LDR + ti * 16 + cq));
-                const uint2 x1 = __builtin_bit_cast(uint2, ld_tr16(ks + (ra + 4) * LDR + ti * 16 + cq));
+                const uint2 x0 = __builtin_bit_cast(uint2, ld_tr16(ks + at(ra, ti * 16 + cq)));
+                const uint2 x1 = __builtin_bit_cast(uint2, ld_tr16(ks + at(ra + 4, ti * 16 + cq)));
                 af[ti] = __builtin_bit_cast(bf16x8, uint4{x0.x, x0.y, x1.x, x1.y});
             }
             const float4 b0 = *reinterpret_cast<const float4 *>(&Bs[buf][kk * 32 + 8 * g]);
@@ -276,8 +287,8 @@ __global__ __launch_bounds__(512) void frame_gram_bf16_kernel(FrameArgs a) {
                     if (VONES && job >= NT1) {
                         x0 = x1 = uint2{0x3F803F80u, 0x3F803F80u};      // bf16 ones
                     } else {
-                        x0 = __builtin_bit_cast(uint2, ld_tr16(src + ra * LDR + tj * 16 + cq));
-                        x1 = __builtin_bit_cast(uint2, ld_tr16(src + (ra + 4) * LDR + tj * 16 + cq));
+                        x0 = __builtin_bit_cast(uint2, ld_tr16(src + at(ra, tj * 16 + cq)));
+                        x1 = __builtin_bit_cast(uint2, ld_tr16(src + at(ra + 4, tj * 16 + cq)));
                     }
                     const unsigned u[4] = {x0.x, x0.y, x1.x, x1.y};
                     uint4 hi, lo;
