@@ -418,7 +418,11 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
     // normaliser stream: one slice, whose 16 columns all carry z (the unit
     // values make every column of H_f equal to b_f)
     const int ncb = a.den ? 1 : D / 16;
-    const int bh = blockIdx.x / ncb, cb = blockIdx.x % ncb, j0 = cb * 16;
+    // workgroups go round-robin over the 8 XCDs: block b runs on XCD b % 8,
+    // so the slices of one head, which all read its G_f, share an L2
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int bh = (slot / ncb) * 8 + xcd, cb = slot % ncb, j0 = cb * 16;
+    if (bh >= a.B * a.H) return;               // padding of the head count to 8
 
     floatx4 S[PERW];
 #pragma unroll
@@ -600,7 +604,11 @@ __global__ __launch_bounds__(64 * OUT_WAVES) void frame_out_bf16_kernel(FrameArg
     const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ntt = (a.S + OUT_TOK - 1) / OUT_TOK;
-    const int unit = blockIdx.x / ntt, tb = blockIdx.x % ntt;
+    // the token tiles of one (head, frame) read the same S_f: keep them on
+    // one XCD (block b runs on XCD b % 8) so that it is fetched into one L2
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int unit = (slot / ntt) * 8 + xcd, tb = slot % ntt;
+    if (unit >= a.B * a.H * a.F) return;        // padding of the unit count to 8
     const size_t N = (size_t)a.F * a.S;
     const size_t row0 = (size_t)(unit / a.F) * N + (size_t)(unit % a.F) * a.S;
     const int t0 = tb * OUT_TOK + w * (SUB * 16);          // this wave's first token in the frame
@@ -744,14 +752,14 @@ hipError_t launch_frame(FrameArgs a, hipStream_t s) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((frame_state_kernel<D>), dim3(a.B * a.H * (a.den ? 1 : D / 16)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((frame_state_kernel<D>), dim3((a.B * a.H + 7) / 8 * 8 * (a.den ? 1 : D / 16)), dim3(256), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.den) {
         hipLaunchKernelGGL((frame_den_kernel<F32IN, D>), dim3(units * ((a.S + 255) / 256)), dim3(256), 0, s, a);
     } else if constexpr (!F32IN && D >= 32) {
         const int ntt = (a.S + OUT_TOK - 1) / OUT_TOK;
-        hipLaunchKernelGGL((frame_out_bf16_kernel<D>), dim3(units * ntt), dim3(64 * OUT_WAVES), 0, s, a);
+        hipLaunchKernelGGL((frame_out_bf16_kernel<D>), dim3((units + 7) / 8 * 8 * ntt), dim3(64 * OUT_WAVES), 0, s, a);
     } else {
         const int ntt = (a.S + 63) / 64;
         hipLaunchKernelGGL((frame_out_kernel<F32IN, D>), dim3(units * ntt), dim3(256), 0, s, a);
