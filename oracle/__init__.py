@@ -19,6 +19,7 @@ receives; outputs are float64):
 * :func:`frame_scan`               - O4, frame-synchronous numerator-only scan.
 * :func:`frame_scan_reverse`       - O4 in the anti-causal direction.
 * :func:`frame_den`                - the normaliser (Z) stream of O4.
+* :func:`gdn_recurrent_bwd`        - O5, gradients of O1 (reverse mode).
 * :func:`invert_se3`               - closed-form rigid-transform inverse.
 """
 from __future__ import annotations
@@ -61,10 +62,12 @@ def _load():
     lib.oracle_deltaproduct_recurrent.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, D, P, P, P, I]
     lib.oracle_cam_prep.argtypes = [I, I, I, I, P, P, P, P, P, P, P, D, D, P, P, P, P, P, P, I]
     lib.oracle_frame_scan.argtypes = [I, I, I, I, I, P, P, P, P, P, D, P, P, P, I]
+    lib.oracle_gdn_recurrent_bwd.argtypes = [I, I, I, I, I, P, P, P, P, P, D, P, P, P,
+                                             P, P, P, P, P, P, I]
     lib.oracle_invert_se3.argtypes = [ctypes.c_long, P, P]
     lib.oracle_invert_se3.restype = None
     lib.oracle_max_threads.argtypes = []
-    for fn in (lib.oracle_gdn_recurrent, lib.oracle_deltaproduct_recurrent,
+    for fn in (lib.oracle_gdn_recurrent, lib.oracle_gdn_recurrent_bwd, lib.oracle_deltaproduct_recurrent,
                lib.oracle_cam_prep, lib.oracle_frame_scan, lib.oracle_max_threads):
         fn.restype = ctypes.c_int
     _lib = lib
@@ -108,6 +111,32 @@ def gdn_recurrent(q, k, v, beta, g, scale=1.0, h0=None, nthreads=0):
                                       int(nthreads))
     _check(rc, "gdn_recurrent")
     return o, hT
+
+
+def gdn_recurrent_bwd(q, k, v, beta, g, dout, scale=1.0, h0=None, dhT=None, nthreads=0):
+    """O5.  Gradients of :func:`gdn_recurrent`'s (o, hT) under the upstream
+    gradients dout (B,T,H,Dv) and dhT (B,H,Dk,Dv, or None = 0).  Returns
+    (dq, dk, dv, dbeta, dg, dh0) in float64 (dg is the gradient of the
+    log-decay g)."""
+    q, k, v, beta, g, dout, h0, dhT = map(_f32, (q, k, v, beta, g, dout, h0, dhT))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape[:3] == (B, T, H) and dout.shape == v.shape
+    assert beta.shape == (B, T, H) and g.shape == (B, T, H)
+    for st in (h0, dhT):
+        assert st is None or st.shape == (B, H, Dk, Dv)
+    dq = np.zeros((B, T, H, Dk), np.float64)
+    dk = np.zeros((B, T, H, Dk), np.float64)
+    dv = np.zeros((B, T, H, Dv), np.float64)
+    dbeta = np.zeros((B, T, H), np.float64)
+    dg = np.zeros((B, T, H), np.float64)
+    dh0 = np.zeros((B, H, Dk, Dv), np.float64)
+    rc = _load().oracle_gdn_recurrent_bwd(B, T, H, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                          _ptr(g), float(scale), _ptr(h0), _ptr(dout), _ptr(dhT),
+                                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dg),
+                                          _ptr(dh0), int(nthreads))
+    _check(rc, "gdn_recurrent_bwd")
+    return dq, dk, dv, dbeta, dg, dh0
 
 
 def deltaproduct_recurrent(q, k, v, beta, g, mask, scale=1.0, h0=None, nthreads=0):

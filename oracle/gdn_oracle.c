@@ -370,3 +370,135 @@ void oracle_invert_se3(long n, const double *in, double *out) {
         Y[15] = 1.0;
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* O5: gradients of O1 (reverse mode through its steps).                   */
+/*                                                                          */
+/* Given dL/do_t (dout) and dL/dS_T (dhT, or 0), the steps of O1 are        */
+/* walked from the last token back, each one's adjoint taken in turn:       */
+/*   read-out  o = scale S^T q     : dS += scale q do^T, dq = scale S do    */
+/*   correct   S = P + beta k r^T, r = v - p                                */
+/*                                 : dP = dS, dk = beta dS r,               */
+/*                                   dbeta = k^T dS r, dv = beta dS^T k,    */
+/*                                   dp = -dv                               */
+/*   predict   p = P^T k           : dP += k dp^T, dk += P dp               */
+/*   gate      P = exp(g) S_prev   : dS_prev = exp(g) dP, dg = <dP, P>      */
+/* and dh0 = dS_0.  S_prev of every token is recomputed forward from a     */
+/* state kept every 64 tokens (same steps as O1).  [dp] lists the chunk    */
+/* backward kernels of this rule; this is the gradient they compute,       */
+/* taken on the token recurrence.                                           */
+/* Layouts as O1; dout (B,T,H,Dv); dhT, dh0 (B,H,Dk,Dv); dq, dk (B,T,H,Dk); */
+/* dv (B,T,H,Dv); dbeta, dg (B,T,H).  dhT and h0 may be NULL; dh0 may be   */
+/* NULL (not stored).                                                       */
+/* ------------------------------------------------------------------------ */
+static void o1_step(int Dk, int Dv, double *S, double *p, const float *kt, const float *vt,
+                    double decay, double bt) {
+    for (int i = 0; i < Dk * Dv; ++i) S[i] *= decay;
+    for (int j = 0; j < Dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < Dk; ++i) acc += S[(size_t)i * Dv + j] * (double)kt[i];
+        p[j] = acc;
+    }
+    for (int i = 0; i < Dk; ++i) {
+        double ki = bt * (double)kt[i];
+        for (int j = 0; j < Dv; ++j) S[(size_t)i * Dv + j] += ki * ((double)vt[j] - p[j]);
+    }
+}
+
+int oracle_gdn_recurrent_bwd(int B, int T, int H, int Dk, int Dv,
+                             const float *q, const float *k, const float *v,
+                             const float *beta, const float *g, double scale,
+                             const float *h0, const float *dout, const float *dhT,
+                             double *dq, double *dk, double *dv, double *dbeta,
+                             double *dg, double *dh0, int nthreads) {
+    if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return -1;
+    set_threads(nthreads);
+    const int SEG = 64;
+    int nseg = (T + SEG - 1) / SEG;
+    int npairs = B * H;
+    size_t sz = (size_t)Dk * Dv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < npairs; ++bh) {
+        int b = bh / H, h = bh % H;
+        double *ck = (double *)malloc(sizeof(double) * sz * (size_t)(nseg > 0 ? nseg : 1));
+        double *st = (double *)malloc(sizeof(double) * sz * (SEG + 1));
+        double *S = (double *)calloc(sz, sizeof(double));
+        double *dS = (double *)calloc(sz, sizeof(double));
+        double *p = (double *)malloc(sizeof(double) * (size_t)Dv);
+        double *r = (double *)malloc(sizeof(double) * (size_t)Dv);
+        double *u = (double *)malloc(sizeof(double) * (size_t)Dv);
+        double *dp = (double *)malloc(sizeof(double) * (size_t)Dv);
+        if (h0)
+            for (size_t i = 0; i < sz; ++i) S[i] = (double)h0[(size_t)bh * sz + i];
+        /* forward: the state entering every segment */
+        for (int t = 0; t < T; ++t) {
+            size_t row = ((size_t)b * T + t) * H + h;
+            if (t % SEG == 0) memcpy(ck + (size_t)(t / SEG) * sz, S, sizeof(double) * sz);
+            o1_step(Dk, Dv, S, p, k + row * Dk, v + row * Dv, exp((double)g[row]), (double)beta[row]);
+        }
+        if (dhT)
+            for (size_t i = 0; i < sz; ++i) dS[i] = (double)dhT[(size_t)bh * sz + i];
+        for (int s = nseg - 1; s >= 0; --s) {
+            int t0 = s * SEG, t1 = t0 + SEG < T ? t0 + SEG : T;
+            /* st[i] = state before token t0 + i, st[t1 - t0] = after the last */
+            memcpy(st, ck + (size_t)s * sz, sizeof(double) * sz);
+            for (int t = t0; t < t1; ++t) {
+                size_t row = ((size_t)b * T + t) * H + h;
+                double *nx = st + (size_t)(t - t0 + 1) * sz;
+                memcpy(nx, st + (size_t)(t - t0) * sz, sizeof(double) * sz);
+                o1_step(Dk, Dv, nx, p, k + row * Dk, v + row * Dv, exp((double)g[row]), (double)beta[row]);
+            }
+            for (int t = t1 - 1; t >= t0; --t) {
+                size_t row = ((size_t)b * T + t) * H + h;
+                const float *qt = q + row * Dk, *kt = k + row * Dk, *vt = v + row * Dv;
+                const float *dot = dout + row * Dv;
+                const double *Sp = st + (size_t)(t - t0) * sz;       /* S_{t-1} */
+                const double *Sc = st + (size_t)(t - t0 + 1) * sz;   /* S_t */
+                double a = exp((double)g[row]), bt = (double)beta[row];
+                /* read-out */
+                for (int i = 0; i < Dk; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < Dv; ++j) {
+                        dS[(size_t)i * Dv + j] += scale * (double)qt[i] * (double)dot[j];
+                        acc += Sc[(size_t)i * Dv + j] * (double)dot[j];
+                    }
+                    dq[row * Dk + i] = scale * acc;
+                }
+                /* correct: p = (a S_prev)^T k, r = v - p, u = dS^T k */
+                double db = 0.0;
+                for (int j = 0; j < Dv; ++j) {
+                    double pa = 0.0, ua = 0.0;
+                    for (int i = 0; i < Dk; ++i) {
+                        pa += a * Sp[(size_t)i * Dv + j] * (double)kt[i];
+                        ua += dS[(size_t)i * Dv + j] * (double)kt[i];
+                    }
+                    p[j] = pa;
+                    r[j] = (double)vt[j] - pa;
+                    u[j] = ua;
+                    dv[row * Dv + j] = bt * ua;
+                    dp[j] = -bt * ua;
+                    db += ua * r[j];
+                }
+                dbeta[row] = db;
+                /* dk from the correction and the prediction; dP and dg */
+                double dgs = 0.0;
+                for (int i = 0; i < Dk; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < Dv; ++j) {
+                        double P = a * Sp[(size_t)i * Dv + j];
+                        double dP = dS[(size_t)i * Dv + j] + (double)kt[i] * dp[j];
+                        acc += bt * dS[(size_t)i * Dv + j] * r[j] + P * dp[j];
+                        dgs += dP * P;
+                        dS[(size_t)i * Dv + j] = a * dP;   /* gate: dS_prev */
+                    }
+                    dk[row * Dk + i] = acc;
+                }
+                dg[row] = dgs;
+            }
+        }
+        if (dh0)
+            for (size_t i = 0; i < sz; ++i) dh0[(size_t)bh * sz + i] = dS[i];
+        free(ck); free(st); free(S); free(dS); free(p); free(r); free(u); free(dp);
+    }
+    return 0;
+}
