@@ -116,11 +116,26 @@ def _prepare(name, dev):
     workload's hot path once through the C ABI."""
     import torch
     from chunkwise_gated_delta_gdn_amd import gdn, inputs
-    base = "camera" if name in ("camera_reverse", "camera_den") else name    # same inputs
+    base = {"camera_reverse": "camera", "camera_den": "camera", "gdn_bwd": "gdn"}.get(name, name)  # same inputs
     wl = inputs.WORKLOADS[base]
     d = inputs.workload_inputs(base)
     bf = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
     f32 = lambda x: torch.from_numpy(x).to(dev)
+    if name == "gdn_bwd":
+        # gradients of the gdn workload's forward under seeded upstream gradients
+        B, T, H, Dk, Dv = wl["B"], wl["T"], wl["H"], wl["Dk"], wl["Dv"]
+        up = inputs.gdn_upstream(B, T, H, Dk, Dv, 20265, "bf16")
+        q, k, v, dout = bf(d["q"]), bf(d["k"]), bf(d["v"]), bf(up["dout"])
+        beta, g = f32(d["beta"]), f32(d["g"])
+
+        def step():
+            return gdn.gdn_bwd(q, k, v, beta, g, dout, Dk ** -0.5)
+        # read q, k, v, dout (bf16), beta, g; write dq, dk, dv (fp32), dbeta, dg, dh0
+        nbytes = B * T * H * ((2 * Dk + 2 * Dv) * 2 + 8 + (2 * Dk + Dv) * 4 + 8) + B * H * Dk * Dv * 4
+        # per token and head: two forward recomputations (4 Dk Dv each) and the
+        # backward step (12 Dk Dv), FLOPs
+        flops = B * T * H * 20 * Dk * Dv
+        return d, step, B * T, nbytes, flops
     if wl["kind"] == "gdn":
         q, k, v = bf(d["q"]), bf(d["k"]), bf(d["v"])
         beta, g = f32(d["beta"]), f32(d["g"])
@@ -192,7 +207,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="gdn", choices=("gdn", "gdn_long", "deltaproduct", "camera", "camera_reverse", "camera_den"),
+    ap.add_argument("--workload", default="gdn", choices=("gdn", "gdn_long", "deltaproduct", "camera", "camera_reverse", "camera_den",
+                             "gdn_bwd"),
                     help="gdn is the headline workload; the others time the other operations")
     ap.add_argument("--copy-probe", action="store_true", help="run only the copy calibration kernel")
     args = ap.parse_args()
@@ -229,8 +245,15 @@ def main():
     kernel_ms = float(np.mean(kern_ms))
     achieved_gbs = nbytes / (kernel_ms * 1e-3) / 1e9
     from chunkwise_gated_delta_gdn_amd import inputs
-    wl = inputs.WORKLOADS["camera" if args.workload in ("camera_reverse", "camera_den") else args.workload]
-    if args.workload in ("gdn", "gdn_long"):
+    wl = inputs.WORKLOADS[{"camera_reverse": "camera", "camera_den": "camera",
+                           "gdn_bwd": "gdn"}.get(args.workload, args.workload)]
+    if args.workload == "gdn_bwd":
+        metric = "tokens/sec of gated-delta backward (B*T/s) at H=16, D=128"
+        desc = (f"gdn_bwd: gradients of the gdn workload (B={wl['B']} H={wl['H']} T={wl['T']} "
+                f"Dk=Dv={wl['Dk']}), bf16 q/k/v/dout, fp32 gradients, no dhT")
+        kernel = "gdn_bwd = bwd_scan_kernel<bf16, 128> + bwd_reduce_kernel<128>"
+        traffic = None
+    elif args.workload in ("gdn", "gdn_long"):
         metric = "tokens/sec of chunkwise gated-delta fwd (B*T/s) at H=16, D=128"
         desc = (f"{args.workload}: B={wl['B']} H={wl['H']} T={wl['T']} Dk=Dv={wl['Dk']} chunk={wl['chunk']}, "
                 f"bf16 q/k/v and output, fp32 gates and state, " + ("h0~N(0,0.02^2)" if wl["h0_std"] else "h0=0"))

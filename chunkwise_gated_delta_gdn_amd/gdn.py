@@ -27,6 +27,7 @@ EXPORTS = (
     "gdn_recurrent_fwd", "gdn_recurrent_fwd_workspace_bytes",
     "gdn_recurrent_den_fwd", "gdn_recurrent_den_fwd_workspace_bytes",
     "gdn_prep",
+    "gdn_bwd", "gdn_bwd_workspace_bytes",
 )
 
 
@@ -65,6 +66,10 @@ def _load():
     lib.gdn_recurrent_den_fwd_workspace_bytes.restype = Z
     lib.gdn_prep.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P, P, P, P, I, I, I, I, I, I, P]
     lib.gdn_prep.restype = I
+    lib.gdn_bwd.argtypes = [P, P, P, P, P, F, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, Z, P]
+    lib.gdn_bwd.restype = I
+    lib.gdn_bwd_workspace_bytes.argtypes = [I] * 5
+    lib.gdn_bwd_workspace_bytes.restype = Z
     return lib
 
 
@@ -275,3 +280,35 @@ def gdn_prep(qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_sca
                        _dtype_code(qkv.dtype), _dtype_code(out_dtype), _stream(dev))
     _check("gdn_prep", rc)
     return out
+
+
+def gdn_bwd(q, k, v, beta, log_decay, dout, scale=1.0, h0=None, dhT=None, need_dh0=True):
+    """Gradients of :func:`gdn_chunk_fwd`'s (o, hT).  q,k (B,T,H,Dk); v and
+    dout (B,T,H,Dv), all of one dtype; beta, log_decay (B,T,H) fp32; h0, dhT
+    (B,H,Dk,Dv) fp32 or None.  Returns (dq, dk, dv, dbeta, dlog_decay, dh0),
+    fp32 (dh0 None unless need_dh0)."""
+    _dev(q, k, v, beta, log_decay, dout, h0, dhT)
+    _f32(beta, "beta"), _f32(log_decay, "log_decay"), _f32(h0, "h0"), _f32(dhT, "dhT")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if (k.shape != q.shape or v.shape[:3] != (B, T, H) or dout.shape != v.shape
+            or k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype):
+        raise ValueError("q, k, v, dout shapes or dtypes disagree")
+    if beta.shape != (B, T, H) or log_decay.shape != (B, T, H):
+        raise ValueError("beta and log_decay must be (B, T, H)")
+    for name, st in (("h0", h0), ("dhT", dhT)):
+        if st is not None and st.shape != (B, H, Dk, Dv):
+            raise ValueError(f"{name} must be (B, H, Dk, Dv)")
+    dev = q.device
+    dq = torch.empty((B, T, H, Dk), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, T, H, Dk), dtype=torch.float32, device=dev)
+    dv = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    dbeta = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    dg = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    dh0 = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if need_dh0 else None
+    ws, nws = _workspace(_lib.gdn_bwd_workspace_bytes(B, T, H, Dk, Dv), dev)
+    rc = _lib.gdn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_decay), float(scale), _ptr(h0),
+                      _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dg),
+                      _ptr(dh0), B, T, H, Dk, Dv, _dtype_code(q.dtype), _ptr(ws), nws, _stream(dev))
+    _check("gdn_bwd", rc)
+    return dq, dk, dv, dbeta, dg, dh0

@@ -84,6 +84,16 @@ def gdn_inputs(B, T, H, Dk, Dv, seed, dtype="bf16", h0_std=0.0, decay_mean=2.0,
                 h0=None if h0 is None else h0.astype(np.float32))
 
 
+def gdn_upstream(B, T, H, Dk, Dv, seed, dtype="bf16", dhT_std=0.0):
+    """Upstream gradients for the backward: dout ~ N(0,1) (B,T,H,Dv) in
+    ``dtype``; dhT ~ N(0, dhT_std^2) (B,H,Dk,Dv) float32 when dhT_std > 0
+    (else None)."""
+    rng = np.random.default_rng(seed)
+    dout = rng.standard_normal((B, T, H, Dv))
+    dhT = rng.normal(0.0, dhT_std, (B, H, Dk, Dv)) if dhT_std > 0 else None
+    return dict(dout=cast(dout, dtype), dhT=None if dhT is None else dhT.astype(np.float32))
+
+
 def deltaproduct_inputs(B, T, H, r, dk, Dv, seed, dtype="bf16", h0_std=0.0, mask=None,
                         decay_mean=2.0, decay_std=0.5):
     """Draw order: q, k ~ N(0,1) (B,T,H,r*dk), each dk-wide sub-key

@@ -10,6 +10,7 @@
  *   gdn_recurrent_den_fwd   its normaliser (denominator) stream
  *   gdn_prep                camera-branch per-token prep (RMSNorm over all
  *                           channels, ReLU, K-scale, UCPE 4x4, RoPE, ||k||^2)
+ *   gdn_bwd                 gradients of gdn_chunk_fwd (q, k, v, beta, g, h0)
  *
  * Sources (web pages, cited by title and section):
  *   [dp]  msj19 "gated_deltaproduct" test.py: gated_chunk_scaled_dot_kkt_fwd,
@@ -234,6 +235,41 @@ int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_norm_w,
              void *q_out, void *k_out, void *v_out,
              float *k_pre_sq, float *k_post_sq, float *inflation_sq,
              int B, int N, int H, int D, int dtype, int out_dtype, void *stream);
+
+/*
+ * gdn_bwd - gradients of gdn_chunk_fwd's outputs (o, hT) ([dp] lists the
+ * chunk backward kernels of this rule: prepare_dv, dhu, dqkw, WY backward;
+ * this entry point computes the same gradients on the token recurrence).
+ *
+ * With the forward steps of one token, P = exp(g_t) S_{t-1}, p = P^T k_t,
+ * S_t = P + beta_t k_t (v_t - p)^T, o_t = scale S_t^T q_t, and dS = dL/dS_t
+ * (dhT, or 0, after the last token), the tokens are walked backwards:
+ *   dS += scale q_t do_t^T,  dq_t = scale S_t do_t,  r = v_t - p,
+ *   u = dS^T k_t,  dv_t = beta_t u,  dbeta_t = u . r,  dp = -beta_t u,
+ *   dk_t = beta_t dS r + P dp,  dP = dS + k_t dp^T,  dg_t = <dP, P>,
+ *   dS = exp(g_t) dP;   dh0 = dS after token 0.
+ * States are recomputed from copies kept every 32 tokens in the work space.
+ *
+ *   q, k            (B, T, H, Dk)  dtype
+ *   v, dout         (B, T, H, Dv)  dtype (dout = dL/do)
+ *   beta, log_decay (B, T, H)      float32
+ *   h0, dhT         (B, H, Dk, Dv) float32, nullable (zero)
+ *   dq, dk          (B, T, H, Dk)  float32
+ *   dv              (B, T, H, Dv)  float32
+ *   dbeta, dlog_decay (B, T, H)    float32 (dlog_decay = dL/dg)
+ *   dh0             (B, H, Dk, Dv) float32, nullable (not stored)
+ * Supported: Dk in {16, 32, 64, 128}; Dv a multiple of 16 up to 4096; any
+ * T >= 0.  q and k 16-byte aligned, the other tensors 4-byte.  The work
+ * space (gdn_bwd_workspace_bytes) holds the kept states and per-slice
+ * partial sums: about (2 Dk + 2) * Dv / 16 * 4 bytes per token and head.
+ */
+size_t gdn_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv);
+int gdn_bwd(const void *q, const void *k, const void *v,
+            const float *beta, const float *log_decay, float scale,
+            const float *h0, const void *dout, const float *dhT,
+            float *dq, float *dk, float *dv, float *dbeta, float *dlog_decay,
+            float *dh0, int B, int T, int H, int Dk, int Dv, int dtype,
+            void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
 
 
 def _chunk(lib, **kw):
@@ -103,3 +103,24 @@ def test_recurrent_rejects_bad_arguments(lib):
     need = lib.gdn_recurrent_fwd_workspace_bytes(1, 1, 2, 4, 64, 1)
     assert need > 0
     assert call(reverse=1) == -3
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    fake = ctypes.c_void_p(4096)        # aligned, never dereferenced: validation fails first
+
+    def call(Dk=64, Dv=64, T=8, dtype=1, q=fake, ws=None, nws=0, scale=1.0):
+        return lib.gdn_bwd(q, fake, fake, fake, fake, scale, None, fake, None, fake, fake, fake,
+                           fake, fake, None, 1, T, 2, Dk, Dv, dtype, ws, nws, None)
+    assert call(Dk=48) == -2
+    assert call(Dk=256) == -2
+    assert call(Dv=40) == -2
+    assert call(dtype=3) == -1
+    assert call(q=None) == -1                                    # null tensor
+    assert call(q=ctypes.c_void_p(4100)) == -1                   # q misaligned
+    assert call(scale=float("nan")) == -1
+    assert call() == -3                                          # no work space
+    need = lib.gdn_bwd_workspace_bytes(1, 8, 2, 64, 64)
+    assert need > 0
+    assert call(ws=None, nws=need) == -1                         # null work space
+    assert lib.gdn_bwd(None, None, None, None, None, 1.0, None, None, None, None, None, None,
+                       None, None, None, 0, 8, 2, 64, 64, 1, None, 0, None) == 0   # B = 0: nothing to do
