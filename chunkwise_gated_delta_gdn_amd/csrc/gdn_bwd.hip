@@ -15,11 +15,14 @@
 // Kernels:
 //   bwd_scan_kernel    one wave per (b, h, 16-column slice of the state).
 //                      Lane (row group rg = l / 16, column c = l % 16) holds
-//                      rows rg*Dk/4 .. of column c in registers.  A forward
-//                      sweep keeps the state entering every 32-token segment
+//                      rows rg*Dk/4 .. of column c in registers.  Tokens go
+//                      in 16-token segments whose k, q rows, v, dout slices
+//                      and gates are staged in LDS (the next segment's are
+//                      loaded into registers while one is computed).  A
+//                      forward sweep keeps the state entering every segment
 //                      in the work space; the reverse sweep recomputes each
-//                      segment's states into the work space and walks its
-//                      tokens backwards.  The columns of a slice are summed
+//                      segment's states into LDS and walks its tokens
+//                      backwards.  The columns of a slice are summed
 //                      in registers (reduce-scatter over the 16 column
 //                      lanes); dv and dh0 belong to one slice and are
 //                      written directly, dq, dk, dbeta and dg are per-slice
@@ -33,7 +36,7 @@
 namespace gdn {
 namespace {
 
-constexpr int BWD_SEG = 32;     // tokens between kept states
+constexpr int BWD_SEG = 16;     // tokens between kept states (one LDS-staged segment)
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -41,7 +44,7 @@ struct BwdArgs {
     const void *q, *k, *v, *dout;
     const float *beta, *g, *h0, *dhT;
     float *dq, *dk, *dv, *dbeta, *dg, *dh0;
-    float *ck, *st, *part;      // work space: kept states, segment states, partials
+    float *ck, *part;           // work space: kept states, partials
     int B, T, H, Dv, nvs;
     float scale;
 };
@@ -122,10 +125,42 @@ __device__ __forceinline__ float row_sum(float x) {
 }
 
 template <bool F32, int DK>
+struct BwdShape {
+    static constexpr int ES = F32 ? 4 : 2;                  // input element bytes
+    static constexpr int RPG = DK / 4;                      // state rows per lane
+    static constexpr int PPR = DK * ES / 16;                // 16-byte pieces of a k (or q) row
+    static constexpr int KP = BWD_SEG * PPR;                // ... of a segment's k rows
+    static constexpr int KPL = (KP + 63) / 64;              // ... per lane
+    static constexpr int VPR = 16 * ES / 16;                // pieces of a token's v (or dout) slice
+    static constexpr int VP = BWD_SEG * VPR;
+    // LDS (bytes): the states entering each token of the segment, fp32
+    // [token][row i][lane] (lane-contiguous: conflict-free); the segment's
+    // k and q rows, v and dout slices (input type), beta and g
+    static constexpr int OFF_ST = 0;
+    static constexpr int OFF_K = OFF_ST + BWD_SEG * DK * 16 * 4;
+    static constexpr int OFF_Q = OFF_K + BWD_SEG * DK * ES;
+    static constexpr int OFF_V = OFF_Q + BWD_SEG * DK * ES;
+    static constexpr int OFF_O = OFF_V + BWD_SEG * 16 * ES;
+    static constexpr int OFF_B = OFF_O + BWD_SEG * 16 * ES;
+    static constexpr int OFF_G = OFF_B + BWD_SEG * 4;
+    static constexpr int BYTES = OFF_G + BWD_SEG * 4;
+    static_assert(VP <= 64 && BWD_SEG <= 64, "one piece per lane");
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <bool F32, int DK>
 __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
-    constexpr int RPG = DK / 4;                        // rows per lane
+    using SH = BwdShape<F32, DK>;
+    constexpr int RPG = SH::RPG, KPL = SH::KPL, ES = SH::ES;
     constexpr int NOUT = RPG >= 16 ? RPG / 16 : 1;     // summed rows per lane
     constexpr int PW = 2 * DK + 2;                     // partial row: dq, dk, dbeta, dg
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SH::BYTES];
+    float *sst = reinterpret_cast<float *>(smem + SH::OFF_ST);
+    const unsigned char *ks = smem + SH::OFF_K, *qs = smem + SH::OFF_Q;
+    const unsigned char *vsl = smem + SH::OFF_V, *os = smem + SH::OFF_O;
+    const float *bs = reinterpret_cast<const float *>(smem + SH::OFF_B);
+    const float *gs = reinterpret_cast<const float *>(smem + SH::OFF_G);
+
     const int l = threadIdx.x, c = l & 15, rg = l >> 4;
     const int wv = blockIdx.x;                          // (b H + h) nvs + vs
     const int vs = wv % a.nvs, bh = wv / a.nvs, b = bh / a.H, h = bh % a.H;
@@ -133,18 +168,73 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
     const int T = a.T, H = a.H, Dv = a.Dv;
     const int nseg = (T + BWD_SEG - 1) / BWD_SEG;
     const size_t NROW = (size_t)a.B * T * H;
-    float *ck = a.ck + (size_t)wv * nseg * DK * 16;     // [nseg][DK][16]
-    float *st = a.st + (size_t)wv * BWD_SEG * DK * 16;  // [BWD_SEG][DK][16]
+    float *ck = a.ck + (size_t)wv * nseg * DK * 16;     // [nseg][RPG][64]
     auto row_of = [&](int t) { return ((size_t)b * T + t) * H + h; };
     auto state_at = [&](size_t i) { return ((size_t)bh * DK + r0 + i) * Dv + col; };
 
-    // one forward token step on this lane's rows of column c
-    auto fwd_step = [&](float (&X)[RPG], int t) __attribute__((always_inline)) {
-        const size_t row = row_of(t);
+    // the next segment's inputs (and kept state), loaded into registers while
+    // the current one is computed
+    struct Pre {
+        u32x4 k[KPL], q[KPL], v, o;
+        float b, g;
+        float x[RPG];
+    } pre;
+    auto prefetch = [&](int s, bool bwd) __attribute__((always_inline)) {
+        const int t0 = s * BWD_SEG;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+            const int idx = l + 64 * j, tt = idx / SH::PPR, t = t0 + tt;
+            pre.k[j] = pre.q[j] = u32x4{0u, 0u, 0u, 0u};
+            if (idx < SH::KP && t < T) {
+                const size_t off = row_of(t) * DK * ES + (idx % SH::PPR) * 16;
+                pre.k[j] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(a.k) + off);
+                if (bwd) pre.q[j] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(a.q) + off);
+            }
+        }
+        {
+            const int tt = l / SH::VPR, t = t0 + tt;
+            pre.v = pre.o = u32x4{0u, 0u, 0u, 0u};
+            if (l < SH::VP && t < T) {
+                const size_t off = (row_of(t) * Dv + vs * 16) * ES + (l % SH::VPR) * 16;
+                pre.v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(a.v) + off);
+                if (bwd) pre.o = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(a.dout) + off);
+            }
+        }
+        pre.b = pre.g = 0.f;
+        if (l < BWD_SEG && t0 + l < T) {
+            pre.b = a.beta[row_of(t0 + l)];
+            pre.g = a.g[row_of(t0 + l)];
+        }
+        if (bwd)
+#pragma unroll
+            for (int i = 0; i < RPG; ++i) pre.x[i] = ck[((size_t)s * RPG + i) * 64 + l];
+    };
+    auto commit = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+            const int idx = l + 64 * j;
+            if (idx < SH::KP) {
+                *reinterpret_cast<u32x4 *>(smem + SH::OFF_K + idx * 16) = pre.k[j];
+                *reinterpret_cast<u32x4 *>(smem + SH::OFF_Q + idx * 16) = pre.q[j];
+            }
+        }
+        if (l < SH::VP) {
+            *reinterpret_cast<u32x4 *>(smem + SH::OFF_V + l * 16) = pre.v;
+            *reinterpret_cast<u32x4 *>(smem + SH::OFF_O + l * 16) = pre.o;
+        }
+        if (l < BWD_SEG) {
+            reinterpret_cast<float *>(smem + SH::OFF_B)[l] = pre.b;
+            reinterpret_cast<float *>(smem + SH::OFF_G)[l] = pre.g;
+        }
+    };
+
+    // one forward token step (token tt of the staged segment) on this lane's
+    // rows of column c
+    auto fwd_step = [&](float (&X)[RPG], int tt) __attribute__((always_inline)) {
         float kr[RPG];
-        load_rows<F32, RPG>(a.k, row * DK + r0, kr);
-        const float vc = load1<F32>(a.v, row * Dv + col);
-        const float dec = expf(a.g[row]), bt = a.beta[row];
+        load_rows<F32, RPG>(ks, tt * DK + r0, kr);
+        const float vc = load1<F32>(vsl, tt * 16 + c);
+        const float dec = expf(gs[tt]), bt = bs[tt];
         float pl = 0.f;
 #pragma unroll
         for (int i = 0; i < RPG; ++i) pl += kr[i] * X[i];
@@ -156,41 +246,43 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
     float S[RPG];
 #pragma unroll
     for (int i = 0; i < RPG; ++i) S[i] = a.h0 ? a.h0[state_at(i)] : 0.f;
-    for (int t = 0; t < T; ++t) {
-        if (t % BWD_SEG == 0) {
-            float *cp = ck + (size_t)(t / BWD_SEG) * DK * 16;
+    // forward sweep: the state entering every segment is kept
+    if (nseg > 0) prefetch(0, false);
+    for (int s = 0; s < nseg; ++s) {
+        commit();
+        if (s + 1 < nseg) prefetch(s + 1, false);
 #pragma unroll
-            for (int i = 0; i < RPG; ++i) cp[(r0 + i) * 16 + c] = S[i];
-        }
-        fwd_step(S, t);
+        for (int i = 0; i < RPG; ++i) ck[((size_t)s * RPG + i) * 64 + l] = S[i];
+        const int len = min(BWD_SEG, T - s * BWD_SEG);
+        for (int tt = 0; tt < len; ++tt) fwd_step(S, tt);
     }
 
     float dS[RPG];
 #pragma unroll
     for (int i = 0; i < RPG; ++i) dS[i] = a.dhT ? a.dhT[state_at(i)] : 0.f;
-    // S holds S_t of the token being walked back (S_T first)
+    // reverse sweep; S holds S_t of the token being walked back (S_T first)
+    if (nseg > 0) prefetch(nseg - 1, true);
     for (int s = nseg - 1; s >= 0; --s) {
-        const int t0 = s * BWD_SEG, t1 = min(T, t0 + BWD_SEG);
+        commit();
         float X[RPG];
-        const float *cp = ck + (size_t)s * DK * 16;
 #pragma unroll
-        for (int i = 0; i < RPG; ++i) X[i] = cp[(r0 + i) * 16 + c];
-        for (int t = t0; t < t1; ++t) {
-            float *sp = st + (size_t)(t - t0) * DK * 16;
+        for (int i = 0; i < RPG; ++i) X[i] = pre.x[i];
+        if (s > 0) prefetch(s - 1, true);
+        const int t0 = s * BWD_SEG, len = min(BWD_SEG, T - t0);
+        for (int tt = 0; tt < len; ++tt) {
 #pragma unroll
-            for (int i = 0; i < RPG; ++i) sp[(r0 + i) * 16 + c] = X[i];
-            fwd_step(X, t);
+            for (int i = 0; i < RPG; ++i) sst[(tt * RPG + i) * 64 + l] = X[i];
+            fwd_step(X, tt);
         }
-        for (int t = t1 - 1; t >= t0; --t) {
-            const size_t row = row_of(t);
+        for (int tt = len - 1; tt >= 0; --tt) {
+            const size_t row = row_of(t0 + tt);
             float Sp[RPG], kr[RPG], qr[RPG], x[RPG];
-            const float *sp = st + (size_t)(t - t0) * DK * 16;
 #pragma unroll
-            for (int i = 0; i < RPG; ++i) Sp[i] = sp[(r0 + i) * 16 + c];
-            load_rows<F32, RPG>(a.k, row * DK + r0, kr);
-            load_rows<F32, RPG>(a.q, row * DK + r0, qr);
-            const float vc = load1<F32>(a.v, row * Dv + col), doc = load1<F32>(a.dout, row * Dv + col);
-            const float dec = expf(a.g[row]), bt = a.beta[row];
+            for (int i = 0; i < RPG; ++i) Sp[i] = sst[(tt * RPG + i) * 64 + l];
+            load_rows<F32, RPG>(ks, tt * DK + r0, kr);
+            load_rows<F32, RPG>(qs, tt * DK + r0, qr);
+            const float vc = load1<F32>(vsl, tt * 16 + c), doc = load1<F32>(os, tt * 16 + c);
+            const float dec = expf(gs[tt]), bt = bs[tt];
             float *pp = a.part + ((size_t)vs * NROW + row) * PW;
             // read-out
 #pragma unroll
@@ -269,7 +361,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
 size_t bwd_workspace(int B, int T, int H, int Dk, int Dv) {
     const size_t nvs = (size_t)Dv / 16, nw = (size_t)B * H * nvs;
     const size_t nseg = ((size_t)T + BWD_SEG - 1) / BWD_SEG;
-    const size_t fl = nw * nseg * Dk * 16 + nw * BWD_SEG * Dk * 16 + nvs * (size_t)B * T * H * (2 * Dk + 2);
+    const size_t fl = nw * nseg * Dk * 16 + nvs * (size_t)B * T * H * (2 * Dk + 2);
     return fl * sizeof(float);
 }
 
@@ -309,8 +401,8 @@ extern "C" int gdn_bwd(const void *q, const void *k, const void *v, const float 
     if (T > 0) {
         GDN_REQUIRE(q && k && v && beta && log_decay && dout && dq && dk && dv && dbeta && dlog_decay, GDN_EINVAL,
                     "%s: null tensor pointer", name);
-        GDN_REQUIRE(gdn::aligned(q, 16) && gdn::aligned(k, 16), GDN_EINVAL, "%s: q and k must be 16-byte aligned",
-                    name);
+        GDN_REQUIRE(gdn::aligned(q, 16) && gdn::aligned(k, 16) && gdn::aligned(v, 16) && gdn::aligned(dout, 16),
+                    GDN_EINVAL, "%s: q, k, v and dout must be 16-byte aligned", name);
         GDN_REQUIRE(gdn::aligned(v, 4) && gdn::aligned(dout, 4) && gdn::aligned(beta, 4) &&
                         gdn::aligned(log_decay, 4) && gdn::aligned(dq, 4) && gdn::aligned(dk, 4) &&
                         gdn::aligned(dv, 4) && gdn::aligned(dbeta, 4) && gdn::aligned(dlog_decay, 4),
@@ -350,8 +442,7 @@ extern "C" int gdn_bwd(const void *q, const void *k, const void *v, const float 
     const size_t nw = (size_t)B * H * a.nvs, nseg = ((size_t)T + gdn::BWD_SEG - 1) / gdn::BWD_SEG;
     float *ws = reinterpret_cast<float *>(workspace);
     a.ck = ws;
-    a.st = a.ck + nw * nseg * Dk * 16;
-    a.part = a.st + nw * gdn::BWD_SEG * Dk * 16;
+    a.part = a.ck + nw * nseg * Dk * 16;
     if (!dh0 && T == 0) return GDN_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool f32 = dtype == GDN_DTYPE_F32;
