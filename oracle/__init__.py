@@ -19,7 +19,7 @@ receives; outputs are float64):
 * :func:`frame_scan`               - O4, frame-synchronous numerator-only scan.
 * :func:`frame_scan_reverse`       - O4 in the anti-causal direction.
 * :func:`frame_den`                - the normaliser (Z) stream of O4.
-* :func:`gdn_recurrent_bwd`        - O5, gradients of O1 (reverse mode).
+* :func:`gdn_recurrent_bwd`        - O6, gradients of O1 (reverse mode).
 * :func:`invert_se3`               - closed-form rigid-transform inverse.
 """
 from __future__ import annotations
@@ -114,7 +114,7 @@ def gdn_recurrent(q, k, v, beta, g, scale=1.0, h0=None, nthreads=0):
 
 
 def gdn_recurrent_bwd(q, k, v, beta, g, dout, scale=1.0, h0=None, dhT=None, nthreads=0):
-    """O5.  Gradients of :func:`gdn_recurrent`'s (o, hT) under the upstream
+    """O6.  Gradients of :func:`gdn_recurrent`'s (o, hT) under the upstream
     gradients dout (B,T,H,Dv) and dhT (B,H,Dk,Dv, or None = 0).  Returns
     (dq, dk, dv, dbeta, dg, dh0) in float64 (dg is the gradient of the
     log-decay g)."""

@@ -372,7 +372,7 @@ void oracle_invert_se3(long n, const double *in, double *out) {
 }
 
 /* ------------------------------------------------------------------------ */
-/* O5: gradients of O1 (reverse mode through its steps).                   */
+/* O6: gradients of O1 (reverse mode through its steps).                   */
 /*                                                                          */
 /* Given dL/do_t (dout) and dL/dS_T (dhT, or 0), the steps of O1 are        */
 /* walked from the last token back, each one's adjoint taken in turn:       */

@@ -1,6 +1,6 @@
-"""Pins of the fp64 backward oracle (O5, gradients of the gated delta rule).
+"""Pins of the fp64 backward oracle (O6, gradients of the gated delta rule).
 
-O5 is checked against the forward oracle O1 (itself pinned in
+O6 is checked against the forward oracle O1 (itself pinned in
 ``test_oracle_pins.py``) by finite differences, and against closed forms of
 the special case beta = 0, where the rule is a gated linear read-out of h0.
 No GPU is needed.
