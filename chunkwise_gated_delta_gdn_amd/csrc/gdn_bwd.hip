@@ -13,9 +13,9 @@
 // and dh0 = dS after the first token.
 //
 // Kernels:
-//   bwd_scan_kernel    one wave per (b, h, 16-column slice of the state).
-//                      Lane (row group rg = l / 16, column c = l % 16) holds
-//                      rows rg*Dk/4 .. of column c in registers.  Tokens go
+//   bwd_scan_kernel    one wave per (b, h, 8-column slice of the state).
+//                      Lane (row group rg = l / 8, column c = l % 8) holds
+//                      rows rg*Dk/8 .. of column c in registers.  Tokens go
 //                      in 16-token segments whose k, q rows, v, dout slices
 //                      and gates are staged in LDS (the next segment's are
 //                      loaded into registers while one is computed).  A
@@ -23,7 +23,7 @@
 //                      in the work space; the reverse sweep recomputes each
 //                      segment's states into LDS and walks its tokens
 //                      backwards.  The columns of a slice are summed
-//                      in registers (reduce-scatter over the 16 column
+//                      in registers (reduce-scatter over the 8 column
 //                      lanes); dv and dh0 belong to one slice and are
 //                      written directly, dq, dk, dbeta and dg are per-slice
 //                      partial sums.
@@ -37,6 +37,7 @@ namespace gdn {
 namespace {
 
 constexpr int BWD_SEG = 16;     // tokens between kept states (one LDS-staged segment)
+constexpr int BWD_CW = 8;       // state columns per wave
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -49,11 +50,21 @@ struct BwdArgs {
     float scale;
 };
 
-// N consecutive elements at element offset `off` (16-byte pieces; 8 bytes
-// for four bf16).
+// N consecutive elements at element offset `off` (16-byte pieces; 8 or 4
+// bytes for four or two elements).
 template <bool F32, int N>
 __device__ __forceinline__ void load_rows(const void *p, size_t off, float (&x)[N]) {
-    if constexpr (F32) {
+    if constexpr (N == 2) {
+        if constexpr (F32) {
+            const floatx2 t = *reinterpret_cast<const floatx2 *>(reinterpret_cast<const float *>(p) + off);
+            x[0] = t[0];
+            x[1] = t[1];
+        } else {
+            const uint32_t t = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const u16 *>(p) + off);
+            x[0] = __builtin_bit_cast(float, t << 16);
+            x[1] = __builtin_bit_cast(float, t & 0xffff0000u);
+        }
+    } else if constexpr (F32) {
         const floatx4 *s = reinterpret_cast<const floatx4 *>(reinterpret_cast<const float *>(p) + off);
 #pragma unroll
         for (int i = 0; i < N / 4; ++i) {
@@ -89,11 +100,11 @@ __device__ __forceinline__ float load1(const void *p, size_t off) {
     else return bf16_to_f32(reinterpret_cast<const u16 *>(p)[off]);
 }
 
-// Sum of x over the 16 column lanes of a row group, scattered: at each
-// exchange (lane distance O = 8, 4, 2, 1) a lane keeps one half of its
+// Sum of x over the column lanes of a row group, scattered: at each
+// exchange (lane distance O = BWD_CW/2, ..., 2, 1) a lane keeps one half of its
 // window of rows and adds its partner's copy of that half.  At the end
-// x[0 .. max(N/16, 1) - 1] holds the sums of rows base + j of the window;
-// with N < 16 the last exchanges add single values, and lanes that differ
+// x[0 .. max(N/BWD_CW, 1) - 1] holds the sums of rows base + j of the window;
+// with N < BWD_CW the last exchanges add single values, and lanes that differ
 // only in those bits (`dup`) hold the same sums.
 template <int N, int O>
 __device__ __forceinline__ void col_reduce_scatter(float *x, int c, int &base, int &dup) {
@@ -117,34 +128,34 @@ __device__ __forceinline__ void col_reduce_scatter(float *x, int c, int &base, i
     }
 }
 
-// sum over the four row groups (lanes c, c + 16, c + 32, c + 48)
+// sum over the row groups (lanes c, c + BWD_CW, c + 2 BWD_CW, ...)
 __device__ __forceinline__ float row_sum(float x) {
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
+#pragma unroll
+    for (int o = BWD_CW; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
     return x;
 }
 
 template <bool F32, int DK>
 struct BwdShape {
     static constexpr int ES = F32 ? 4 : 2;                  // input element bytes
-    static constexpr int RPG = DK / 4;                      // state rows per lane
+    static constexpr int RPG = DK * BWD_CW / 64;            // state rows per lane
     static constexpr int PPR = DK * ES / 16;                // 16-byte pieces of a k (or q) row
     static constexpr int KP = BWD_SEG * PPR;                // ... of a segment's k rows
     static constexpr int KPL = (KP + 63) / 64;              // ... per lane
-    static constexpr int VPR = 16 * ES / 16;                // pieces of a token's v (or dout) slice
+    static constexpr int VPR = BWD_CW * ES / 16;            // pieces of a token's v (or dout) slice
     static constexpr int VP = BWD_SEG * VPR;
     // LDS (bytes): the states entering each token of the segment, fp32
     // [token][row i][lane] (lane-contiguous: conflict-free); the segment's
     // k and q rows, v and dout slices (input type), beta and g
     static constexpr int OFF_ST = 0;
-    static constexpr int OFF_K = OFF_ST + BWD_SEG * DK * 16 * 4;
+    static constexpr int OFF_K = OFF_ST + BWD_SEG * DK * BWD_CW * 4;
     static constexpr int OFF_Q = OFF_K + BWD_SEG * DK * ES;
     static constexpr int OFF_V = OFF_Q + BWD_SEG * DK * ES;
-    static constexpr int OFF_O = OFF_V + BWD_SEG * 16 * ES;
-    static constexpr int OFF_B = OFF_O + BWD_SEG * 16 * ES;
+    static constexpr int OFF_O = OFF_V + BWD_SEG * BWD_CW * ES;
+    static constexpr int OFF_B = OFF_O + BWD_SEG * BWD_CW * ES;
     static constexpr int OFF_G = OFF_B + BWD_SEG * 4;
     static constexpr int BYTES = OFF_G + BWD_SEG * 4;
-    static_assert(VP <= 64 && BWD_SEG <= 64, "one piece per lane");
+    static_assert(VP <= 64 && BWD_SEG <= 64 && VPR >= 1 && RPG >= 2, "one piece per lane");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -152,7 +163,7 @@ template <bool F32, int DK>
 __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
     using SH = BwdShape<F32, DK>;
     constexpr int RPG = SH::RPG, KPL = SH::KPL, ES = SH::ES;
-    constexpr int NOUT = RPG >= 16 ? RPG / 16 : 1;     // summed rows per lane
+    constexpr int NOUT = RPG >= BWD_CW ? RPG / BWD_CW : 1;   // summed rows per lane
     constexpr int PW = 2 * DK + 2;                     // partial row: dq, dk, dbeta, dg
     __shared__ __attribute__((aligned(16))) unsigned char smem[SH::BYTES];
     float *sst = reinterpret_cast<float *>(smem + SH::OFF_ST);
@@ -161,14 +172,14 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
     const float *bs = reinterpret_cast<const float *>(smem + SH::OFF_B);
     const float *gs = reinterpret_cast<const float *>(smem + SH::OFF_G);
 
-    const int l = threadIdx.x, c = l & 15, rg = l >> 4;
+    const int l = threadIdx.x, c = l % BWD_CW, rg = l / BWD_CW;
     const int wv = blockIdx.x;                          // (b H + h) nvs + vs
     const int vs = wv % a.nvs, bh = wv / a.nvs, b = bh / a.H, h = bh % a.H;
-    const int col = vs * 16 + c, r0 = rg * RPG;
+    const int col = vs * BWD_CW + c, r0 = rg * RPG;
     const int T = a.T, H = a.H, Dv = a.Dv;
     const int nseg = (T + BWD_SEG - 1) / BWD_SEG;
     const size_t NROW = (size_t)a.B * T * H;
-    float *ck = a.ck + (size_t)wv * nseg * DK * 16;     // [nseg][RPG][64]
+    float *ck = a.ck + (size_t)wv * nseg * DK * BWD_CW; // [nseg][RPG][64]
     auto row_of = [&](int t) { return ((size_t)b * T + t) * H + h; };
     auto state_at = [&](size_t i) { return ((size_t)bh * DK + r0 + i) * Dv + col; };
 
@@ -195,7 +206,7 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
             const int tt = l / SH::VPR, t = t0 + tt;
             pre.v = pre.o = u32x4{0u, 0u, 0u, 0u};
             if (l < SH::VP && t < T) {
-                const size_t off = (row_of(t) * Dv + vs * 16) * ES + (l % SH::VPR) * 16;
+                const size_t off = (row_of(t) * Dv + vs * BWD_CW) * ES + (l % SH::VPR) * 16;
                 pre.v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(a.v) + off);
                 if (bwd) pre.o = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(a.dout) + off);
             }
@@ -233,7 +244,7 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
     auto fwd_step = [&](float (&X)[RPG], int tt) __attribute__((always_inline)) {
         float kr[RPG];
         load_rows<F32, RPG>(ks, tt * DK + r0, kr);
-        const float vc = load1<F32>(vsl, tt * 16 + c);
+        const float vc = load1<F32>(vsl, tt * BWD_CW + c);
         const float dec = expf(gs[tt]), bt = bs[tt];
         float pl = 0.f;
 #pragma unroll
@@ -281,7 +292,7 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
             for (int i = 0; i < RPG; ++i) Sp[i] = sst[(tt * RPG + i) * 64 + l];
             load_rows<F32, RPG>(ks, tt * DK + r0, kr);
             load_rows<F32, RPG>(qs, tt * DK + r0, qr);
-            const float vc = load1<F32>(vsl, tt * 16 + c), doc = load1<F32>(os, tt * 16 + c);
+            const float vc = load1<F32>(vsl, tt * BWD_CW + c), doc = load1<F32>(os, tt * BWD_CW + c);
             const float dec = expf(gs[tt]), bt = bs[tt];
             float *pp = a.part + ((size_t)vs * NROW + row) * PW;
             // read-out
@@ -292,7 +303,7 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
             }
             {
                 int base = 0, dup = 0;
-                col_reduce_scatter<RPG, 8>(x, c, base, dup);
+                col_reduce_scatter<RPG, BWD_CW / 2>(x, c, base, dup);
                 if ((c & dup) == 0)
 #pragma unroll
                     for (int j = 0; j < NOUT; ++j) pp[r0 + base + j] = x[j];
@@ -308,7 +319,7 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
             if (rg == 0) a.dv[row * Dv + col] = bt * u;
             float db = u * r;
 #pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) db += __shfl_xor(db, o, 64);
+            for (int o = BWD_CW / 2; o >= 1; o >>= 1) db += __shfl_xor(db, o, 64);
             // dk, dg and the gate's adjoint
             float dgl = 0.f;
 #pragma unroll
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
             }
             {
                 int base = 0, dup = 0;
-                col_reduce_scatter<RPG, 8>(x, c, base, dup);
+                col_reduce_scatter<RPG, BWD_CW / 2>(x, c, base, dup);
                 if ((c & dup) == 0)
 #pragma unroll
                     for (int j = 0; j < NOUT; ++j) pp[DK + r0 + base + j] = x[j];
@@ -359,9 +370,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
 }
 
 size_t bwd_workspace(int B, int T, int H, int Dk, int Dv) {
-    const size_t nvs = (size_t)Dv / 16, nw = (size_t)B * H * nvs;
+    const size_t nvs = (size_t)Dv / BWD_CW, nw = (size_t)B * H * nvs;
     const size_t nseg = ((size_t)T + BWD_SEG - 1) / BWD_SEG;
-    const size_t fl = nw * nseg * Dk * 16 + nvs * (size_t)B * T * H * (2 * Dk + 2);
+    const size_t fl = nw * nseg * Dk * BWD_CW + nvs * (size_t)B * T * H * (2 * Dk + 2);
     return fl * sizeof(float);
 }
 
@@ -417,7 +428,8 @@ extern "C" int gdn_bwd(const void *q, const void *k, const void *v, const float 
                 workspace_bytes, need);
     GDN_REQUIRE(need == 0 || (workspace && gdn::aligned(workspace, 16)), GDN_EINVAL,
                 "%s: workspace must be a 16-byte aligned device pointer", name);
-    GDN_REQUIRE((size_t)B * H * (Dv / 16) < (1u << 31), GDN_EUNSUPPORTED, "%s: too many (b, h, slice) units", name);
+    GDN_REQUIRE((size_t)B * H * (Dv / gdn::BWD_CW) < (1u << 31), GDN_EUNSUPPORTED, "%s: too many (b, h, slice) units",
+                name);
     gdn::BwdArgs a;
     a.q = q;
     a.k = k;
@@ -437,12 +449,12 @@ extern "C" int gdn_bwd(const void *q, const void *k, const void *v, const float 
     a.T = T;
     a.H = H;
     a.Dv = Dv;
-    a.nvs = Dv / 16;
+    a.nvs = Dv / gdn::BWD_CW;
     a.scale = scale;
     const size_t nw = (size_t)B * H * a.nvs, nseg = ((size_t)T + gdn::BWD_SEG - 1) / gdn::BWD_SEG;
     float *ws = reinterpret_cast<float *>(workspace);
     a.ck = ws;
-    a.part = a.ck + nw * nseg * Dk * 16;
+    a.part = a.ck + nw * nseg * Dk * gdn::BWD_CW;
     if (!dh0 && T == 0) return GDN_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool f32 = dtype == GDN_DTYPE_F32;
