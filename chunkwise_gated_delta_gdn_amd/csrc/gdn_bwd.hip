@@ -13,17 +13,17 @@
 // and dh0 = dS after the first token.
 //
 // Kernels:
-//   bwd_scan_kernel    one wave per (b, h, 8-column slice of the state).
-//                      Lane (row group rg = l / 8, column c = l % 8) holds
-//                      rows rg*Dk/8 .. of column c in registers.  Tokens go
-//                      in 16-token segments whose k, q rows, v, dout slices
+//   bwd_scan_kernel    one wave per (b, h, 4-column slice of the state).
+//                      Lane (row group rg = l / 4, column c = l % 4) holds
+//                      rows rg*Dk/16 .. of column c in registers.  Tokens go
+//                      in 12-token segments whose k, q rows, v, dout slices
 //                      and gates are staged in LDS (the next segment's are
 //                      loaded into registers while one is computed).  A
 //                      forward sweep keeps the state entering every segment
 //                      in the work space; the reverse sweep recomputes each
 //                      segment's states into LDS and walks its tokens
 //                      backwards.  The columns of a slice are summed
-//                      in registers (reduce-scatter over the 8 column
+//                      in registers (reduce-scatter over the 4 column
 //                      lanes); dv and dh0 belong to one slice and are
 //                      written directly, dq, dk, dbeta and dg are per-slice
 //                      partial sums.
@@ -36,8 +36,8 @@
 namespace gdn {
 namespace {
 
-constexpr int BWD_SEG = 16;     // tokens between kept states (one LDS-staged segment)
-constexpr int BWD_CW = 8;       // state columns per wave
+constexpr int BWD_SEG = 12;     // tokens between kept states (one LDS-staged segment)
+constexpr int BWD_CW = 4;       // state columns per wave
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -50,11 +50,13 @@ struct BwdArgs {
     float scale;
 };
 
-// N consecutive elements at element offset `off` (16-byte pieces; 8 or 4
-// bytes for four or two elements).
+// N consecutive elements at element offset `off` (16-byte pieces; 8, 4 or
+// 2 bytes for fewer elements).
 template <bool F32, int N>
 __device__ __forceinline__ void load_rows(const void *p, size_t off, float (&x)[N]) {
-    if constexpr (N == 2) {
+    if constexpr (N == 1) {
+        x[0] = F32 ? reinterpret_cast<const float *>(p)[off] : bf16_to_f32(reinterpret_cast<const u16 *>(p)[off]);
+    } else if constexpr (N == 2) {
         if constexpr (F32) {
             const floatx2 t = *reinterpret_cast<const floatx2 *>(reinterpret_cast<const float *>(p) + off);
             x[0] = t[0];
@@ -142,7 +144,8 @@ struct BwdShape {
     static constexpr int PPR = DK * ES / 16;                // 16-byte pieces of a k (or q) row
     static constexpr int KP = BWD_SEG * PPR;                // ... of a segment's k rows
     static constexpr int KPL = (KP + 63) / 64;              // ... per lane
-    static constexpr int VPR = BWD_CW * ES / 16;            // pieces of a token's v (or dout) slice
+    static constexpr int VPB = BWD_CW * ES < 16 ? BWD_CW * ES : 16;   // bytes of a v (or dout) piece
+    static constexpr int VPR = BWD_CW * ES / VPB;           // pieces of a token's v (or dout) slice
     static constexpr int VP = BWD_SEG * VPR;
     // LDS (bytes): the states entering each token of the segment, fp32
     // [token][row i][lane] (lane-contiguous: conflict-free); the segment's
@@ -155,7 +158,8 @@ struct BwdShape {
     static constexpr int OFF_B = OFF_O + BWD_SEG * BWD_CW * ES;
     static constexpr int OFF_G = OFF_B + BWD_SEG * 4;
     static constexpr int BYTES = OFF_G + BWD_SEG * 4;
-    static_assert(VP <= 64 && BWD_SEG <= 64 && VPR >= 1 && RPG >= 2, "one piece per lane");
+    static_assert(VP <= 64 && BWD_SEG <= 64 && VPR >= 1 && RPG >= 1 && (VPB == 8 || VPB == 16),
+                  "one piece per lane");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -206,9 +210,20 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
             const int tt = l / SH::VPR, t = t0 + tt;
             pre.v = pre.o = u32x4{0u, 0u, 0u, 0u};
             if (l < SH::VP && t < T) {
-                const size_t off = (row_of(t) * Dv + vs * BWD_CW) * ES + (l % SH::VPR) * 16;
-                pre.v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(a.v) + off);
-                if (bwd) pre.o = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(a.dout) + off);
+                const size_t off = (row_of(t) * Dv + vs * BWD_CW) * ES + (l % SH::VPR) * SH::VPB;
+                if constexpr (SH::VPB == 16) {
+                    pre.v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(a.v) + off);
+                    if (bwd)
+                        pre.o = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(a.dout) + off);
+                } else {
+                    const u32x2 v2 = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const unsigned char *>(a.v) + off);
+                    pre.v = u32x4{v2[0], v2[1], 0u, 0u};
+                    if (bwd) {
+                        const u32x2 o2 =
+                            *reinterpret_cast<const u32x2 *>(reinterpret_cast<const unsigned char *>(a.dout) + off);
+                        pre.o = u32x4{o2[0], o2[1], 0u, 0u};
+                    }
+                }
             }
         }
         pre.b = pre.g = 0.f;
@@ -230,8 +245,13 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
             }
         }
         if (l < SH::VP) {
-            *reinterpret_cast<u32x4 *>(smem + SH::OFF_V + l * 16) = pre.v;
-            *reinterpret_cast<u32x4 *>(smem + SH::OFF_O + l * 16) = pre.o;
+            if constexpr (SH::VPB == 16) {
+                *reinterpret_cast<u32x4 *>(smem + SH::OFF_V + l * 16) = pre.v;
+                *reinterpret_cast<u32x4 *>(smem + SH::OFF_O + l * 16) = pre.o;
+            } else {
+                *reinterpret_cast<u32x2 *>(smem + SH::OFF_V + l * 8) = u32x2{pre.v[0], pre.v[1]};
+                *reinterpret_cast<u32x2 *>(smem + SH::OFF_O + l * 8) = u32x2{pre.o[0], pre.o[1]};
+            }
         }
         if (l < BWD_SEG) {
             reinterpret_cast<float *>(smem + SH::OFF_B)[l] = pre.b;
