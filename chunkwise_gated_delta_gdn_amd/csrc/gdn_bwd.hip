@@ -46,6 +46,7 @@ struct BwdArgs {
     const float *beta, *g, *h0, *dhT;
     float *dq, *dk, *dv, *dbeta, *dg, *dh0;
     float *ck, *part;           // work space: kept states, partials
+    size_t pstride;             // floats per slice of partials (a multiple of 4)
     int B, T, H, Dv, nvs;
     float scale;
 };
@@ -182,7 +183,6 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
     const int col = vs * BWD_CW + c, r0 = rg * RPG;
     const int T = a.T, H = a.H, Dv = a.Dv;
     const int nseg = (T + BWD_SEG - 1) / BWD_SEG;
-    const size_t NROW = (size_t)a.B * T * H;
     float *ck = a.ck + (size_t)wv * nseg * DK * BWD_CW; // [nseg][RPG][64]
     auto row_of = [&](int t) { return ((size_t)b * T + t) * H + h; };
     auto state_at = [&](size_t i) { return ((size_t)bh * DK + r0 + i) * Dv + col; };
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
             load_rows<F32, RPG>(qs, tt * DK + r0, qr);
             const float vc = load1<F32>(vsl, tt * BWD_CW + c), doc = load1<F32>(os, tt * BWD_CW + c);
             const float dec = expf(gs[tt]), bt = bs[tt];
-            float *pp = a.part + ((size_t)vs * NROW + row) * PW;
+            float *pp = a.part + (size_t)vs * a.pstride + row * PW;
             // read-out
 #pragma unroll
             for (int i = 0; i < RPG; ++i) {
@@ -372,27 +372,44 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
         for (int i = 0; i < RPG; ++i) a.dh0[state_at(i)] = dS[i];
 }
 
-// dq, dk, dbeta, dg: the per-slice partials summed in slice order
+// dq, dk, dbeta, dg: the per-slice partials summed in slice order, four
+// consecutive entries of the flat partial array per thread (16-byte loads;
+// the last thread takes a tail of fewer)
 template <int DK>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
     constexpr int PW = 2 * DK + 2;
-    const size_t NROW = (size_t)a.B * a.T * a.H;
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= NROW * PW) return;
-    const size_t row = i / PW;
-    const int e = (int)(i % PW);
-    float s = 0.f;
-    for (int vs = 0; vs < a.nvs; ++vs) s += a.part[(size_t)vs * NROW * PW + i];
-    if (e < DK) a.dq[row * DK + e] = s;
-    else if (e < 2 * DK) a.dk[row * DK + e - DK] = s;
-    else if (e == 2 * DK) a.dbeta[row] = s;
-    else a.dg[row] = s;
+    const size_t NROW = (size_t)a.B * a.T * a.H, n = NROW * PW;
+    const size_t i0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i0 >= n) return;
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    if (i0 + 4 <= n) {
+        for (int vs = 0; vs < a.nvs; ++vs) {
+            const floatx4 x = *reinterpret_cast<const floatx4 *>(a.part + (size_t)vs * a.pstride + i0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[e] += x[e];
+        }
+    } else {
+        for (int vs = 0; vs < a.nvs; ++vs)
+            for (size_t i = i0; i < n; ++i) s[i - i0] += a.part[(size_t)vs * a.pstride + i];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const size_t i = i0 + e;
+        if (i >= n) break;
+        const size_t row = i / PW;
+        const int c = (int)(i % PW);
+        if (c < DK) a.dq[row * DK + c] = s[e];
+        else if (c < 2 * DK) a.dk[row * DK + c - DK] = s[e];
+        else if (c == 2 * DK) a.dbeta[row] = s[e];
+        else a.dg[row] = s[e];
+    }
 }
 
 size_t bwd_workspace(int B, int T, int H, int Dk, int Dv) {
     const size_t nvs = (size_t)Dv / BWD_CW, nw = (size_t)B * H * nvs;
     const size_t nseg = ((size_t)T + BWD_SEG - 1) / BWD_SEG;
-    const size_t fl = nw * nseg * Dk * BWD_CW + nvs * (size_t)B * T * H * (2 * Dk + 2);
+    const size_t pstride = ((size_t)B * T * H * (2 * Dk + 2) + 3) & ~(size_t)3;
+    const size_t fl = nw * nseg * Dk * BWD_CW + nvs * pstride;
     return fl * sizeof(float);
 }
 
@@ -404,7 +421,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     const size_t n = (size_t)a.B * a.T * a.H * (2 * DK + 2);
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_reduce_kernel<DK>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_reduce_kernel<DK>), dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -475,6 +492,7 @@ extern "C" int gdn_bwd(const void *q, const void *k, const void *v, const float 
     float *ws = reinterpret_cast<float *>(workspace);
     a.ck = ws;
     a.part = a.ck + nw * nseg * Dk * gdn::BWD_CW;
+    a.pstride = ((size_t)B * T * H * (2 * Dk + 2) + 3) & ~(size_t)3;
     if (!dh0 && T == 0) return GDN_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool f32 = dtype == GDN_DTYPE_F32;
