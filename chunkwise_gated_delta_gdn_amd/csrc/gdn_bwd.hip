@@ -103,6 +103,22 @@ __device__ __forceinline__ float load1(const void *p, size_t off) {
     else return bf16_to_f32(reinterpret_cast<const u16 *>(p)[off]);
 }
 
+// Cross-lane moves inside a 16-lane row by DPP (VALU latency, no LDS
+// round trip): quad permutations [1,0,3,2] and [2,3,0,1] are the lane XORs
+// 1 and 2; row rotations by 4 and 8 keep a lane's index mod 4 (mod 8).
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_ROR4 = 0x124, DPP_ROR8 = 0x128;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+// x from lane l ^ O
+template <int O>
+__device__ __forceinline__ float xor_lane(float x) {
+    if constexpr (O == 1) return dpp<DPP_XOR1>(x);
+    else if constexpr (O == 2) return dpp<DPP_XOR2>(x);
+    else return __shfl_xor(x, O, 64);
+}
+
 // Sum of x over the column lanes of a row group, scattered: at each
 // exchange (lane distance O = BWD_CW/2, ..., 2, 1) a lane keeps one half of its
 // window of rows and adds its partner's copy of that half.  At the end
@@ -119,22 +135,36 @@ __device__ __forceinline__ void col_reduce_scatter(float *x, int c, int &base, i
             for (int j = 0; j < HALF; ++j) {
                 const float send = hi ? x[j] : x[HALF + j];
                 const float keep = hi ? x[HALF + j] : x[j];
-                x[j] = keep + __shfl_xor(send, O, 64);
+                x[j] = keep + xor_lane<O>(send);
             }
             base += hi ? HALF : 0;
             col_reduce_scatter<HALF, O / 2>(x, c, base, dup);
         } else {
-            x[0] += __shfl_xor(x[0], O, 64);
+            x[0] += xor_lane<O>(x[0]);
             dup |= O;
             col_reduce_scatter<1, O / 2>(x, c, base, dup);
         }
     }
 }
 
-// sum over the row groups (lanes c, c + BWD_CW, c + 2 BWD_CW, ...)
+// sum over the row groups (lanes c, c + BWD_CW, c + 2 BWD_CW, ...): by row
+// rotations inside each 16-lane row, then across the four rows
 __device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-    for (int o = BWD_CW; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+    static_assert(BWD_CW == 4 || BWD_CW == 8 || BWD_CW == 16, "column lanes");
+    if constexpr (BWD_CW == 4) x += dpp<DPP_ROR4>(x);
+    if constexpr (BWD_CW <= 8) x += dpp<DPP_ROR8>(x);
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+// sum over all 64 lanes
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp<DPP_XOR1>(x);
+    x += dpp<DPP_XOR2>(x);
+    x += dpp<DPP_ROR4>(x);
+    x += dpp<DPP_ROR8>(x);
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
     return x;
 }
 
@@ -339,7 +369,9 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
             if (rg == 0) a.dv[row * Dv + col] = bt * u;
             float db = u * r;
 #pragma unroll
-            for (int o = BWD_CW / 2; o >= 1; o >>= 1) db += __shfl_xor(db, o, 64);
+            for (int o = BWD_CW / 2; o >= 4; o >>= 1) db += __shfl_xor(db, o, 64);
+            db += dpp<DPP_XOR2>(db);
+            db += dpp<DPP_XOR1>(db);
             // dk, dg and the gate's adjoint
             float dgl = 0.f;
 #pragma unroll
@@ -357,8 +389,7 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
 #pragma unroll
                     for (int j = 0; j < NOUT; ++j) pp[DK + r0 + base + j] = x[j];
             }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) dgl += __shfl_xor(dgl, o, 64);
+            dgl = wave_sum(dgl);
             if (l == 0) {
                 pp[2 * DK] = db;
                 pp[2 * DK + 1] = dgl;
