@@ -37,11 +37,14 @@ KERNEL_SOURCES = ("chunkwise_gated_delta_gdn_amd/csrc/chunk_kernels.h",
 CAMERA_SOURCES = ("chunkwise_gated_delta_gdn_amd/csrc/prep.hip",
                   "chunkwise_gated_delta_gdn_amd/csrc/frame_scan.hip",
                   "chunkwise_gated_delta_gdn_amd/csrc/gdn_common.h")
+BWD_SOURCES = ("chunkwise_gated_delta_gdn_amd/csrc/gdn_bwd.hip",
+               "chunkwise_gated_delta_gdn_amd/csrc/gdn_common.h")
 # workload -> (rocprofv3 HBM counter record, kernel sources it was taken on)
 TRAFFIC = {
     "gdn": (os.path.join(ROOT, "profiles", "chunk_fwd_kernel_gdn_traffic.json"), KERNEL_SOURCES),
     "camera": (os.path.join(ROOT, "profiles", "camera_prep_scan_traffic.json"), CAMERA_SOURCES),
     "camera_den": (os.path.join(ROOT, "profiles", "camera_prep_scan_den_traffic.json"), CAMERA_SOURCES),
+    "gdn_bwd": (os.path.join(ROOT, "profiles", "gdn_bwd_traffic.json"), BWD_SOURCES),
 }
 
 
@@ -252,7 +255,7 @@ def main():
         desc = (f"gdn_bwd: gradients of the gdn workload (B={wl['B']} H={wl['H']} T={wl['T']} "
                 f"Dk=Dv={wl['Dk']}), bf16 q/k/v/dout, fp32 gradients, no dhT")
         kernel = "gdn_bwd = bwd_scan_kernel<bf16, 128> + bwd_reduce_kernel<128>"
-        traffic = None
+        traffic = measured_traffic(args.workload)
     elif args.workload in ("gdn", "gdn_long"):
         metric = "tokens/sec of chunkwise gated-delta fwd (B*T/s) at H=16, D=128"
         desc = (f"{args.workload}: B={wl['B']} H={wl['H']} T={wl['T']} Dk=Dv={wl['Dk']} chunk={wl['chunk']}, "
