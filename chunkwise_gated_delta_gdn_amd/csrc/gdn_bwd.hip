@@ -13,21 +13,23 @@
 // and dh0 = dS after the first token.
 //
 // Kernels:
-//   bwd_scan_kernel    one wave per (b, h, 4-column slice of the state).
-//                      Lane (row group rg = l / 4, column c = l % 4) holds
-//                      rows rg*Dk/16 .. of column c in registers.  Tokens go
-//                      in 12-token segments whose k, q rows, v, dout slices
-//                      and gates are staged in LDS (the next segment's are
-//                      loaded into registers while one is computed).  A
-//                      forward sweep keeps the state entering every segment
-//                      in the work space; the reverse sweep recomputes each
-//                      segment's states into LDS and walks its tokens
-//                      backwards.  The columns of a slice are summed
-//                      in registers (reduce-scatter over the 4 column
-//                      lanes); dv and dh0 belong to one slice and are
-//                      written directly, dq, dk, dbeta and dg are per-slice
-//                      partial sums.
-//   bwd_reduce_kernel  sums the partials over the slices.
+//   bwd_scan_kernel    one workgroup per (b, h, 16-column group of the
+//                      state), one wave per 4-column slice.  Lane (row group
+//                      rg = l / 4, column c = l % 4) holds rows rg*Dk/16 ..
+//                      of column c in registers.  Tokens go in 12-token
+//                      segments whose k, q rows, v, dout columns and gates
+//                      are staged in LDS once for the four waves (the next
+//                      segment's are loaded into registers while one is
+//                      computed).  A forward sweep keeps the state entering
+//                      every segment in the work space; the reverse sweep
+//                      recomputes each segment's states into LDS and walks
+//                      its tokens backwards.  The columns of a slice are
+//                      summed in registers (reduce-scatter over the 4 column
+//                      lanes), the four slices' rows in LDS at the end of a
+//                      segment; dv and dh0 belong to one column and are
+//                      written directly, dq, dk, dbeta and dg are
+//                      per-group partial sums.
+//   bwd_reduce_kernel  sums the partials over the groups.
 #include <math.h>
 
 #include "api_common.h"
@@ -38,6 +40,7 @@ namespace {
 
 constexpr int BWD_SEG = 12;     // tokens between kept states (one LDS-staged segment)
 constexpr int BWD_CW = 4;       // state columns per wave
+constexpr int BWD_WAVES = 4;    // waves per workgroup (their partials are added in LDS)
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -47,7 +50,7 @@ struct BwdArgs {
     float *dq, *dk, *dv, *dbeta, *dg, *dh0;
     float *ck, *part;           // work space: kept states, partials
     size_t pstride;             // floats per slice of partials (a multiple of 4)
-    int B, T, H, Dv, nvs;
+    int B, T, H, Dv, nvs;       // nvs: 16-column groups (one workgroup, one partial each)
     float scale;
 };
 
@@ -170,65 +173,72 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 template <bool F32, int DK>
 struct BwdShape {
+    static constexpr int NW = BWD_WAVES, GC = BWD_WAVES * BWD_CW;   // waves and columns per workgroup
+    static constexpr int NT = 64 * NW;                      // threads
     static constexpr int ES = F32 ? 4 : 2;                  // input element bytes
     static constexpr int RPG = DK * BWD_CW / 64;            // state rows per lane
+    static constexpr int PW = 2 * DK + 2;                   // partial row: dq, dk, dbeta, dg
     static constexpr int PPR = DK * ES / 16;                // 16-byte pieces of a k (or q) row
     static constexpr int KP = BWD_SEG * PPR;                // ... of a segment's k rows
-    static constexpr int KPL = (KP + 63) / 64;              // ... per lane
-    static constexpr int VPB = BWD_CW * ES < 16 ? BWD_CW * ES : 16;   // bytes of a v (or dout) piece
-    static constexpr int VPR = BWD_CW * ES / VPB;           // pieces of a token's v (or dout) slice
+    static constexpr int KPT = (KP + NT - 1) / NT;          // ... per thread
+    static constexpr int VPR = GC * ES / 16;                // pieces of a token's v (or dout) columns
     static constexpr int VP = BWD_SEG * VPR;
-    // LDS (bytes): the states entering each token of the segment, fp32
-    // [token][row i][lane] (lane-contiguous: conflict-free); the segment's
-    // k and q rows, v and dout slices (input type), beta and g
+    // LDS (bytes): per wave, the states entering each token of the segment,
+    // fp32 [token][row i][lane] (lane-contiguous: conflict-free); the
+    // segment's k and q rows, v and dout columns (input type), beta and g,
+    // shared by the waves; the waves' partial rows [token][wave][PW]
+    static constexpr int ST_W = BWD_SEG * DK * BWD_CW * 4;  // one wave's states
     static constexpr int OFF_ST = 0;
-    static constexpr int OFF_K = OFF_ST + BWD_SEG * DK * BWD_CW * 4;
+    static constexpr int OFF_K = OFF_ST + NW * ST_W;
     static constexpr int OFF_Q = OFF_K + BWD_SEG * DK * ES;
     static constexpr int OFF_V = OFF_Q + BWD_SEG * DK * ES;
-    static constexpr int OFF_O = OFF_V + BWD_SEG * BWD_CW * ES;
-    static constexpr int OFF_B = OFF_O + BWD_SEG * BWD_CW * ES;
+    static constexpr int OFF_O = OFF_V + BWD_SEG * GC * ES;
+    static constexpr int OFF_B = OFF_O + BWD_SEG * GC * ES;
     static constexpr int OFF_G = OFF_B + BWD_SEG * 4;
-    static constexpr int BYTES = OFF_G + BWD_SEG * 4;
-    static_assert(VP <= 64 && BWD_SEG <= 64 && VPR >= 1 && RPG >= 1 && (VPB == 8 || VPB == 16),
-                  "one piece per lane");
+    static constexpr int OFF_P = OFF_G + BWD_SEG * 4;
+    static constexpr int BYTES = OFF_P + BWD_SEG * NW * PW * 4;
+    static_assert(VP <= NT && BWD_SEG <= NT && VPR >= 1 && RPG >= 1, "staging pieces");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
 template <bool F32, int DK>
-__global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * BWD_WAVES) void bwd_scan_kernel(BwdArgs a) {
     using SH = BwdShape<F32, DK>;
-    constexpr int RPG = SH::RPG, KPL = SH::KPL, ES = SH::ES;
+    constexpr int RPG = SH::RPG, KPT = SH::KPT, ES = SH::ES, NW = SH::NW, GC = SH::GC, NT = SH::NT;
     constexpr int NOUT = RPG >= BWD_CW ? RPG / BWD_CW : 1;   // summed rows per lane
-    constexpr int PW = 2 * DK + 2;                     // partial row: dq, dk, dbeta, dg
+    constexpr int PW = SH::PW;
     __shared__ __attribute__((aligned(16))) unsigned char smem[SH::BYTES];
-    float *sst = reinterpret_cast<float *>(smem + SH::OFF_ST);
     const unsigned char *ks = smem + SH::OFF_K, *qs = smem + SH::OFF_Q;
     const unsigned char *vsl = smem + SH::OFF_V, *os = smem + SH::OFF_O;
     const float *bs = reinterpret_cast<const float *>(smem + SH::OFF_B);
     const float *gs = reinterpret_cast<const float *>(smem + SH::OFF_G);
+    float *pbuf = reinterpret_cast<float *>(smem + SH::OFF_P);
 
-    const int l = threadIdx.x, c = l % BWD_CW, rg = l / BWD_CW;
-    const int wv = blockIdx.x;                          // (b H + h) nvs + vs
-    const int vs = wv % a.nvs, bh = wv / a.nvs, b = bh / a.H, h = bh % a.H;
-    const int col = vs * BWD_CW + c, r0 = rg * RPG;
+    const int tid = threadIdx.x, l = tid & 63, c = l % BWD_CW, rg = l / BWD_CW;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = blockIdx.x;                         // (b H + h) ngrp + vg
+    const int vg = grp % a.nvs, bh = grp / a.nvs, b = bh / a.H, h = bh % a.H;
+    const int wcol = w * BWD_CW + c;                    // column within the group
+    const int col = vg * GC + wcol, r0 = rg * RPG;
     const int T = a.T, H = a.H, Dv = a.Dv;
     const int nseg = (T + BWD_SEG - 1) / BWD_SEG;
-    float *ck = a.ck + (size_t)wv * nseg * DK * BWD_CW; // [nseg][RPG][64]
+    float *sst = reinterpret_cast<float *>(smem + SH::OFF_ST + w * SH::ST_W);
+    float *ck = a.ck + ((size_t)grp * NW + w) * nseg * DK * BWD_CW;   // [nseg][RPG][64]
     auto row_of = [&](int t) { return ((size_t)b * T + t) * H + h; };
     auto state_at = [&](size_t i) { return ((size_t)bh * DK + r0 + i) * Dv + col; };
 
-    // the next segment's inputs (and kept state), loaded into registers while
-    // the current one is computed
+    // the next segment's inputs (and this wave's kept state), loaded into
+    // registers while the current one is computed
     struct Pre {
-        u32x4 k[KPL], q[KPL], v, o;
+        u32x4 k[KPT], q[KPT], v, o;
         float b, g;
         float x[RPG];
     } pre;
     auto prefetch = [&](int s, bool bwd) __attribute__((always_inline)) {
         const int t0 = s * BWD_SEG;
 #pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-            const int idx = l + 64 * j, tt = idx / SH::PPR, t = t0 + tt;
+        for (int j = 0; j < KPT; ++j) {
+            const int idx = tid + NT * j, tt = idx / SH::PPR, t = t0 + tt;
             pre.k[j] = pre.q[j] = u32x4{0u, 0u, 0u, 0u};
             if (idx < SH::KP && t < T) {
                 const size_t off = row_of(t) * DK * ES + (idx % SH::PPR) * 16;
@@ -237,29 +247,18 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
             }
         }
         {
-            const int tt = l / SH::VPR, t = t0 + tt;
+            const int tt = tid / SH::VPR, t = t0 + tt;
             pre.v = pre.o = u32x4{0u, 0u, 0u, 0u};
-            if (l < SH::VP && t < T) {
-                const size_t off = (row_of(t) * Dv + vs * BWD_CW) * ES + (l % SH::VPR) * SH::VPB;
-                if constexpr (SH::VPB == 16) {
-                    pre.v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(a.v) + off);
-                    if (bwd)
-                        pre.o = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(a.dout) + off);
-                } else {
-                    const u32x2 v2 = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const unsigned char *>(a.v) + off);
-                    pre.v = u32x4{v2[0], v2[1], 0u, 0u};
-                    if (bwd) {
-                        const u32x2 o2 =
-                            *reinterpret_cast<const u32x2 *>(reinterpret_cast<const unsigned char *>(a.dout) + off);
-                        pre.o = u32x4{o2[0], o2[1], 0u, 0u};
-                    }
-                }
+            if (tid < SH::VP && t < T) {
+                const size_t off = (row_of(t) * Dv + vg * GC) * ES + (tid % SH::VPR) * 16;
+                pre.v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(a.v) + off);
+                if (bwd) pre.o = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const unsigned char *>(a.dout) + off);
             }
         }
         pre.b = pre.g = 0.f;
-        if (l < BWD_SEG && t0 + l < T) {
-            pre.b = a.beta[row_of(t0 + l)];
-            pre.g = a.g[row_of(t0 + l)];
+        if (tid < BWD_SEG && t0 + tid < T) {
+            pre.b = a.beta[row_of(t0 + tid)];
+            pre.g = a.g[row_of(t0 + tid)];
         }
         if (bwd)
 #pragma unroll
@@ -267,34 +266,29 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
     };
     auto commit = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-            const int idx = l + 64 * j;
+        for (int j = 0; j < KPT; ++j) {
+            const int idx = tid + NT * j;
             if (idx < SH::KP) {
                 *reinterpret_cast<u32x4 *>(smem + SH::OFF_K + idx * 16) = pre.k[j];
                 *reinterpret_cast<u32x4 *>(smem + SH::OFF_Q + idx * 16) = pre.q[j];
             }
         }
-        if (l < SH::VP) {
-            if constexpr (SH::VPB == 16) {
-                *reinterpret_cast<u32x4 *>(smem + SH::OFF_V + l * 16) = pre.v;
-                *reinterpret_cast<u32x4 *>(smem + SH::OFF_O + l * 16) = pre.o;
-            } else {
-                *reinterpret_cast<u32x2 *>(smem + SH::OFF_V + l * 8) = u32x2{pre.v[0], pre.v[1]};
-                *reinterpret_cast<u32x2 *>(smem + SH::OFF_O + l * 8) = u32x2{pre.o[0], pre.o[1]};
-            }
+        if (tid < SH::VP) {
+            *reinterpret_cast<u32x4 *>(smem + SH::OFF_V + tid * 16) = pre.v;
+            *reinterpret_cast<u32x4 *>(smem + SH::OFF_O + tid * 16) = pre.o;
         }
-        if (l < BWD_SEG) {
-            reinterpret_cast<float *>(smem + SH::OFF_B)[l] = pre.b;
-            reinterpret_cast<float *>(smem + SH::OFF_G)[l] = pre.g;
+        if (tid < BWD_SEG) {
+            reinterpret_cast<float *>(smem + SH::OFF_B)[tid] = pre.b;
+            reinterpret_cast<float *>(smem + SH::OFF_G)[tid] = pre.g;
         }
     };
 
     // one forward token step (token tt of the staged segment) on this lane's
-    // rows of column c
+    // rows of its column
     auto fwd_step = [&](float (&X)[RPG], int tt) __attribute__((always_inline)) {
         float kr[RPG];
         load_rows<F32, RPG>(ks, tt * DK + r0, kr);
-        const float vc = load1<F32>(vsl, tt * BWD_CW + c);
+        const float vc = load1<F32>(vsl, tt * GC + wcol);
         const float dec = expf(gs[tt]), bt = bs[tt];
         float pl = 0.f;
 #pragma unroll
@@ -307,15 +301,19 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
     float S[RPG];
 #pragma unroll
     for (int i = 0; i < RPG; ++i) S[i] = a.h0 ? a.h0[state_at(i)] : 0.f;
-    // forward sweep: the state entering every segment is kept
+    // forward sweep: the state entering every segment is kept.  The segment
+    // loops run the same trip counts in every wave, so every barrier below
+    // is reached by the whole workgroup.
     if (nseg > 0) prefetch(0, false);
     for (int s = 0; s < nseg; ++s) {
         commit();
         if (s + 1 < nseg) prefetch(s + 1, false);
+        lds_barrier();                                  // the segment is staged
 #pragma unroll
         for (int i = 0; i < RPG; ++i) ck[((size_t)s * RPG + i) * 64 + l] = S[i];
         const int len = min(BWD_SEG, T - s * BWD_SEG);
         for (int tt = 0; tt < len; ++tt) fwd_step(S, tt);
+        lds_barrier();                                  // staging may be overwritten
     }
 
     float dS[RPG];
@@ -329,6 +327,7 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < RPG; ++i) X[i] = pre.x[i];
         if (s > 0) prefetch(s - 1, true);
+        lds_barrier();                                  // the segment is staged
         const int t0 = s * BWD_SEG, len = min(BWD_SEG, T - t0);
         for (int tt = 0; tt < len; ++tt) {
 #pragma unroll
@@ -336,15 +335,14 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
             fwd_step(X, tt);
         }
         for (int tt = len - 1; tt >= 0; --tt) {
-            const size_t row = row_of(t0 + tt);
             float Sp[RPG], kr[RPG], qr[RPG], x[RPG];
 #pragma unroll
             for (int i = 0; i < RPG; ++i) Sp[i] = sst[(tt * RPG + i) * 64 + l];
             load_rows<F32, RPG>(ks, tt * DK + r0, kr);
             load_rows<F32, RPG>(qs, tt * DK + r0, qr);
-            const float vc = load1<F32>(vsl, tt * BWD_CW + c), doc = load1<F32>(os, tt * BWD_CW + c);
+            const float vc = load1<F32>(vsl, tt * GC + wcol), doc = load1<F32>(os, tt * GC + wcol);
             const float dec = expf(gs[tt]), bt = bs[tt];
-            float *pp = a.part + (size_t)vs * a.pstride + row * PW;
+            float *pp = pbuf + (tt * NW + w) * PW;
             // read-out
 #pragma unroll
             for (int i = 0; i < RPG; ++i) {
@@ -366,7 +364,7 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
                 ul += kr[i] * dS[i];
             }
             const float r = vc - dec * row_sum(pl), u = row_sum(ul), dp = -bt * u;
-            if (rg == 0) a.dv[row * Dv + col] = bt * u;
+            if (rg == 0) a.dv[row_of(t0 + tt) * Dv + col] = bt * u;
             float db = u * r;
 #pragma unroll
             for (int o = BWD_CW / 2; o >= 4; o >>= 1) db += __shfl_xor(db, o, 64);
@@ -397,6 +395,17 @@ __global__ __launch_bounds__(64) void bwd_scan_kernel(BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < RPG; ++i) S[i] = Sp[i];
         }
+        lds_barrier();                                  // every wave's partial rows are in LDS
+        // the group's partial: the waves' rows added in wave order
+        float *gp = a.part + (size_t)vg * a.pstride;
+        for (int e = tid; e < len * PW; e += NT) {
+            const int tt = e / PW, j = e % PW;
+            float sum = 0.f;
+#pragma unroll
+            for (int v = 0; v < NW; ++v) sum += pbuf[(tt * NW + v) * PW + j];
+            gp[row_of(t0 + tt) * PW + j] = sum;
+        }
+        lds_barrier();                                  // staging and partial rows may be overwritten
     }
     if (a.dh0)
 #pragma unroll
@@ -437,17 +446,17 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
 }
 
 size_t bwd_workspace(int B, int T, int H, int Dk, int Dv) {
-    const size_t nvs = (size_t)Dv / BWD_CW, nw = (size_t)B * H * nvs;
+    const size_t ngrp = (size_t)Dv / (BWD_WAVES * BWD_CW), nw = (size_t)B * H * ngrp * BWD_WAVES;
     const size_t nseg = ((size_t)T + BWD_SEG - 1) / BWD_SEG;
     const size_t pstride = ((size_t)B * T * H * (2 * Dk + 2) + 3) & ~(size_t)3;
-    const size_t fl = nw * nseg * Dk * BWD_CW + nvs * pstride;
+    const size_t fl = nw * nseg * Dk * BWD_CW + ngrp * pstride;
     return fl * sizeof(float);
 }
 
 template <bool F32, int DK>
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
-    const unsigned nw = (unsigned)((size_t)a.B * a.H * a.nvs);
-    hipLaunchKernelGGL((bwd_scan_kernel<F32, DK>), dim3(nw), dim3(64), 0, s, a);
+    const unsigned ngrp = (unsigned)((size_t)a.B * a.H * a.nvs);
+    hipLaunchKernelGGL((bwd_scan_kernel<F32, DK>), dim3(ngrp), dim3(64 * BWD_WAVES), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t n = (size_t)a.B * a.T * a.H * (2 * DK + 2);
@@ -496,7 +505,7 @@ extern "C" int gdn_bwd(const void *q, const void *k, const void *v, const float 
                 workspace_bytes, need);
     GDN_REQUIRE(need == 0 || (workspace && gdn::aligned(workspace, 16)), GDN_EINVAL,
                 "%s: workspace must be a 16-byte aligned device pointer", name);
-    GDN_REQUIRE((size_t)B * H * (Dv / gdn::BWD_CW) < (1u << 31), GDN_EUNSUPPORTED, "%s: too many (b, h, slice) units",
+    GDN_REQUIRE((size_t)B * H * (Dv / 16) < (1u << 31), GDN_EUNSUPPORTED, "%s: too many (b, h, column group) units",
                 name);
     gdn::BwdArgs a;
     a.q = q;
@@ -517,9 +526,9 @@ extern "C" int gdn_bwd(const void *q, const void *k, const void *v, const float 
     a.T = T;
     a.H = H;
     a.Dv = Dv;
-    a.nvs = Dv / gdn::BWD_CW;
+    a.nvs = Dv / (gdn::BWD_WAVES * gdn::BWD_CW);       // 16-column groups
     a.scale = scale;
-    const size_t nw = (size_t)B * H * a.nvs, nseg = ((size_t)T + gdn::BWD_SEG - 1) / gdn::BWD_SEG;
+    const size_t nw = (size_t)B * H * a.nvs * gdn::BWD_WAVES, nseg = ((size_t)T + gdn::BWD_SEG - 1) / gdn::BWD_SEG;
     float *ws = reinterpret_cast<float *>(workspace);
     a.ck = ws;
     a.part = a.ck + nw * nseg * Dk * gdn::BWD_CW;
