@@ -261,7 +261,7 @@ int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_norm_w,
  * Supported: Dk in {16, 32, 64, 128}; Dv a multiple of 16 up to 4096; any
  * T >= 0.  q, k, v and dout 16-byte aligned, the other tensors 4-byte.  The work
  * space (gdn_bwd_workspace_bytes) holds the kept states and per-slice
- * partial sums: about (2 Dk + 2) * Dv / 4 * 4 bytes per token and head.
+ * partial sums: about (2 Dk + 2) * Dv / 16 * 4 bytes per token and head.
  */
 size_t gdn_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv);
 int gdn_bwd(const void *q, const void *k, const void *v,
