@@ -20,6 +20,7 @@ receives; outputs are float64):
 * :func:`frame_scan_reverse`       - O4 in the anti-causal direction.
 * :func:`frame_den`                - the normaliser (Z) stream of O4.
 * :func:`gdn_recurrent_bwd`        - O6, gradients of O1 (reverse mode).
+* :func:`frame_scan_bwd`           - O7, gradients of O4 (reverse mode).
 * :func:`invert_se3`               - closed-form rigid-transform inverse.
 """
 from __future__ import annotations
@@ -64,10 +65,13 @@ def _load():
     lib.oracle_frame_scan.argtypes = [I, I, I, I, I, P, P, P, P, P, D, P, P, P, I]
     lib.oracle_gdn_recurrent_bwd.argtypes = [I, I, I, I, I, P, P, P, P, P, D, P, P, P,
                                              P, P, P, P, P, P, I]
+    lib.oracle_frame_scan_bwd.argtypes = [I, I, I, I, I, P, P, P, P, P, D, P, P, P,
+                                          P, P, P, P, P, P, I]
     lib.oracle_invert_se3.argtypes = [ctypes.c_long, P, P]
     lib.oracle_invert_se3.restype = None
     lib.oracle_max_threads.argtypes = []
-    for fn in (lib.oracle_gdn_recurrent, lib.oracle_gdn_recurrent_bwd, lib.oracle_deltaproduct_recurrent,
+    for fn in (lib.oracle_gdn_recurrent, lib.oracle_gdn_recurrent_bwd, lib.oracle_frame_scan_bwd,
+               lib.oracle_deltaproduct_recurrent,
                lib.oracle_cam_prep, lib.oracle_frame_scan, lib.oracle_max_threads):
         fn.restype = ctypes.c_int
     _lib = lib
@@ -197,6 +201,26 @@ def frame_scan(q, k, v, beta, g, F, scale=1.0, h0=None, nthreads=0):
                                    float(scale), _ptr(h0), _ptr(out), _ptr(hT), int(nthreads))
     _check(rc, "frame_scan")
     return out, hT
+
+
+def frame_scan_bwd(q, k, v, beta, g, F, dout, scale=1.0, h0=None, dhT=None, nthreads=0):
+    """O7.  Gradients of :func:`frame_scan`'s (out, hT) under the upstream
+    gradients dout (B,H,N,D) and dhT (B,H,D,D, or None = 0).  Returns
+    (dq, dk, dv, dbeta (B,H,N), dg (B,H,F), dh0) in float64."""
+    q, k, v, beta, g, dout, h0, dhT = map(_f32, (q, k, v, beta, g, dout, h0, dhT))
+    B, H, N, D = q.shape
+    assert F > 0 and N % F == 0
+    S = N // F
+    assert beta.shape == (B, H, N) and g.shape == (B, H, F) and dout.shape == q.shape
+    dq, dk, dv = (np.zeros((B, H, N, D), np.float64) for _ in range(3))
+    dbeta = np.zeros((B, H, N), np.float64)
+    dg = np.zeros((B, H, F), np.float64)
+    dh0 = np.zeros((B, H, D, D), np.float64)
+    rc = _load().oracle_frame_scan_bwd(B, H, F, S, D, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                       float(scale), _ptr(h0), _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk),
+                                       _ptr(dv), _ptr(dbeta), _ptr(dg), _ptr(dh0), int(nthreads))
+    _check(rc, "frame_scan_bwd")
+    return dq, dk, dv, dbeta, dg, dh0
 
 
 def _flip_and_shift(x, axis, pad):

@@ -502,3 +502,123 @@ int oracle_gdn_recurrent_bwd(int B, int T, int H, int Dk, int Dv,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* O7: gradients of O4 (reverse mode through its frame steps).             */
+/*                                                                          */
+/* With the steps of frame f of O4, P = exp(g_f) S_{f-1},                   */
+/* S_f = P + sum_s beta_s k_s (v_s - P^T k_s)^T, o_s = scale S_f^T q_s, and  */
+/* dS = dL/dS_f (dhT, or 0, after the last frame), the frames are walked    */
+/* from the last back, each step's adjoint taken in turn:                   */
+/*   read-out  for s in f: dS += scale q_s do_s^T, dq_s = scale S_f do_s    */
+/*   correct   for s in f: r_s = v_s - P^T k_s, u_s = dS^T k_s,             */
+/*             dv_s = beta_s u_s, dbeta_s = u_s . r_s, dp_s = -beta_s u_s,  */
+/*             dk_s = beta_s dS r_s;  dP = dS                               */
+/*   predict   for s in f: dP += k_s dp_s^T, dk_s += P dp_s                 */
+/*   gate      dS_{f-1} = exp(g_f) dP, dg_f = <dP, P>                       */
+/* and dh0 = dS after frame 0.  Every state S_0 .. S_F is kept.  [cam]      */
+/* names the backward of this scan (_cam_scan_bwd_kernel); this is the      */
+/* gradient it computes.                                                    */
+/* Layouts as O4; dout (B,H,F*S,D); dhT, dh0 (B,H,D,D); dq, dk, dv          */
+/* (B,H,F*S,D); dbeta (B,H,F*S); dg (B,H,F).  h0, dhT, dh0 may be NULL.     */
+/* ------------------------------------------------------------------------ */
+int oracle_frame_scan_bwd(int B, int H, int F, int S, int D,
+                          const float *q, const float *k, const float *v,
+                          const float *beta, const float *g, double scale,
+                          const float *h0, const float *dout, const float *dhT,
+                          double *dq, double *dk, double *dv, double *dbeta,
+                          double *dg, double *dh0, int nthreads) {
+    if (B < 0 || H < 0 || F < 0 || S <= 0 || D <= 0) return -1;
+    set_threads(nthreads);
+    int npairs = B * H;
+    size_t N = (size_t)F * S, sz = (size_t)D * D;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < npairs; ++bh) {
+        double *st = (double *)calloc(sz * (size_t)(F + 1), sizeof(double));   /* S_0 .. S_F */
+        double *dS = (double *)calloc(sz, sizeof(double));
+        double *P = (double *)malloc(sizeof(double) * sz);
+        double *dP = (double *)malloc(sizeof(double) * sz);
+        double *r = (double *)malloc(sizeof(double) * (size_t)D);
+        double *u = (double *)malloc(sizeof(double) * (size_t)D);
+        if (h0)
+            for (size_t i = 0; i < sz; ++i) st[i] = (double)h0[(size_t)bh * sz + i];
+        /* forward: every frame's state */
+        for (int f = 0; f < F; ++f) {
+            const double *Sp = st + (size_t)f * sz;
+            double *Sn = st + (size_t)(f + 1) * sz;
+            double decay = exp((double)g[(size_t)bh * F + f]);
+            for (size_t i = 0; i < sz; ++i) Sn[i] = P[i] = decay * Sp[i];
+            for (int s = 0; s < S; ++s) {
+                size_t n = (size_t)bh * N + (size_t)f * S + s;
+                const float *ks = k + n * D, *vs = v + n * D;
+                double bs = (double)beta[n];
+                for (int j = 0; j < D; ++j) {
+                    double acc = 0.0;
+                    for (int i = 0; i < D; ++i) acc += P[(size_t)i * D + j] * (double)ks[i];
+                    r[j] = (double)vs[j] - acc;
+                }
+                for (int i = 0; i < D; ++i)
+                    for (int j = 0; j < D; ++j) Sn[(size_t)i * D + j] += bs * (double)ks[i] * r[j];
+            }
+        }
+        if (dhT)
+            for (size_t i = 0; i < sz; ++i) dS[i] = (double)dhT[(size_t)bh * sz + i];
+        for (int f = F - 1; f >= 0; --f) {
+            const double *Sp = st + (size_t)f * sz, *Sc = st + (size_t)(f + 1) * sz;
+            double decay = exp((double)g[(size_t)bh * F + f]);
+            for (size_t i = 0; i < sz; ++i) P[i] = decay * Sp[i];
+            /* read-out */
+            for (int s = 0; s < S; ++s) {
+                size_t n = (size_t)bh * N + (size_t)f * S + s;
+                const float *qs = q + n * D, *dos = dout + n * D;
+                for (int i = 0; i < D; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < D; ++j) {
+                        dS[(size_t)i * D + j] += scale * (double)qs[i] * (double)dos[j];
+                        acc += Sc[(size_t)i * D + j] * (double)dos[j];
+                    }
+                    dq[n * D + i] = scale * acc;
+                }
+            }
+            /* correct and predict, token by token (all read dS = dL/dS_f) */
+            for (size_t i = 0; i < sz; ++i) dP[i] = dS[i];
+            for (int s = 0; s < S; ++s) {
+                size_t n = (size_t)bh * N + (size_t)f * S + s;
+                const float *ks = k + n * D, *vs = v + n * D;
+                double bs = (double)beta[n], db = 0.0;
+                for (int j = 0; j < D; ++j) {
+                    double pa = 0.0, ua = 0.0;
+                    for (int i = 0; i < D; ++i) {
+                        pa += P[(size_t)i * D + j] * (double)ks[i];
+                        ua += dS[(size_t)i * D + j] * (double)ks[i];
+                    }
+                    r[j] = (double)vs[j] - pa;
+                    u[j] = ua;
+                    dv[n * D + j] = bs * ua;
+                    db += ua * r[j];
+                }
+                dbeta[n] = db;
+                for (int i = 0; i < D; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < D; ++j) {
+                        double dp = -bs * u[j];
+                        acc += bs * dS[(size_t)i * D + j] * r[j] + P[(size_t)i * D + j] * dp;
+                        dP[(size_t)i * D + j] += (double)ks[i] * dp;
+                    }
+                    dk[n * D + i] = acc;
+                }
+            }
+            /* gate */
+            double dgs = 0.0;
+            for (size_t i = 0; i < sz; ++i) {
+                dgs += dP[i] * P[i];
+                dS[i] = decay * dP[i];
+            }
+            dg[(size_t)bh * F + f] = dgs;
+        }
+        if (dh0)
+            for (size_t i = 0; i < sz; ++i) dh0[(size_t)bh * sz + i] = dS[i];
+        free(st); free(dS); free(P); free(dP); free(r); free(u);
+    }
+    return 0;
+}

@@ -129,3 +129,80 @@ def test_bwd_without_upstream_state_gradient():
     b = oracle.gdn_recurrent_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], up["dout"], 1.0, z0, z0)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+# ---------------------------------------------------------------------------
+# O7: gradients of the frame-synchronous scan (O4)
+# ---------------------------------------------------------------------------
+def _frame_case(seed, B, H, F, S, D, with_h0=True, with_dhT=True):
+    rng = np.random.default_rng(seed)
+    N = F * S
+    d = {
+        "q": _grid(rng, (B, H, N, D)),
+        "k": _grid(rng, (B, H, N, D), -0.5, 0.5),
+        "v": _grid(rng, (B, H, N, D)),
+        "beta": _grid(rng, (B, H, N), 0.05, 0.95),
+        "g": _grid(rng, (B, H, F), -0.6, -0.01),
+        "h0": _grid(rng, (B, H, D, D)) if with_h0 else None,
+    }
+    up = {"dout": _grid(rng, (B, H, N, D)),
+          "dhT": _grid(rng, (B, H, D, D)) if with_dhT else None}
+    return d, up
+
+
+def _frame_loss(d, up, F, scale):
+    out, hT = oracle.frame_scan(d["q"], d["k"], d["v"], d["beta"], d["g"], F, scale, d["h0"])
+    L = float(np.sum(out * up["dout"]))
+    if up["dhT"] is not None:
+        L += float(np.sum(hT * up["dhT"]))
+    return L
+
+
+def _frame_fd(d, up, F, scale, name, idx):
+    def central(h):
+        dp = {n: (None if x is None else x.copy()) for n, x in d.items()}
+        dm = {n: (None if x is None else x.copy()) for n, x in d.items()}
+        dp[name][idx] += h
+        dm[name][idx] -= h
+        return (_frame_loss(dp, up, F, scale) - _frame_loss(dm, up, F, scale)) / (2 * h)
+    h = 2.0 ** -8
+    return (4 * central(h / 2) - central(h)) / 3
+
+
+def test_frame_bwd_matches_finite_differences():
+    """Every gradient entry of O7 against central differences of O4: three
+    frames of four tokens, with h0 and dhT."""
+    B, H, F, S, D = 1, 2, 3, 4, 3
+    scale = 0.75
+    d, up = _frame_case(11, B, H, F, S, D)
+    grads = oracle.frame_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], F, up["dout"], scale,
+                                  d["h0"], up["dhT"])
+    for name, gr in zip(("q", "k", "v", "beta", "g", "h0"), grads):
+        for idx in np.ndindex(d[name].shape):
+            fd = _frame_fd(d, up, F, scale, name, idx)
+            assert abs(gr[idx] - fd) <= 1e-7 + 1e-6 * abs(fd), (name, idx, gr[idx], fd)
+
+
+def test_frame_bwd_one_token_per_frame_is_the_token_backward():
+    """With S = 1 the frame scan is the token recurrence (O1), so O7 equals
+    O6 once the (B,H,N,D) and (B,T,H,D) layouts are matched."""
+    B, H, T, D = 2, 3, 9, 4
+    d, up = _frame_case(12, B, H, T, 1, D)
+    f = oracle.frame_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], T, up["dout"], 0.5,
+                              d["h0"], up["dhT"])
+    tr = lambda x: np.ascontiguousarray(np.swapaxes(x, 1, 2))      # (B,H,T,...) <-> (B,T,H,...)
+    t = oracle.gdn_recurrent_bwd(tr(d["q"]), tr(d["k"]), tr(d["v"]), tr(d["beta"]), tr(d["g"]),
+                                 tr(up["dout"]), 0.5, d["h0"], up["dhT"])
+    for a, b in zip(f[:5], t[:5]):
+        np.testing.assert_allclose(a, tr(b), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(f[5], t[5], rtol=1e-12, atol=1e-14)
+
+
+def test_frame_bwd_without_upstream_state_gradient():
+    """dhT = None is the same as dhT = 0, and h0 = None the same as h0 = 0."""
+    d, up = _frame_case(13, 1, 2, 2, 5, 3, with_h0=False, with_dhT=False)
+    a = oracle.frame_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], 2, up["dout"], 1.0)
+    z0 = np.zeros((1, 2, 3, 3))
+    b = oracle.frame_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], 2, up["dout"], 1.0, z0, z0)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
