@@ -206,3 +206,47 @@ def test_frame_bwd_without_upstream_state_gradient():
     b = oracle.frame_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], 2, up["dout"], 1.0, z0, z0)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+def test_frame_bwd_matches_the_matrix_form():
+    """O7 against the frame-level matrix form of the same gradients (a
+    different algorithm): with G_f = sum_s beta_s k_s k_s^T,
+    A_f = scale Q_f^T dO_f, X_F-1 = dhT + A_F-1 and
+    X_f-1 = e^{g_f} (I - G_f) X_f + A_f-1, dh0 = e^{g_0} (I - G_0) X_0;
+    per token dq = scale S_f do, u = X_f^T k, r = v - P_f^T k, dv = beta u,
+    dbeta = u . r, dk = beta X_f r - beta P_f u; dg_f = <(I - G_f) X_f, P_f>."""
+    B, H, F, S, D = 1, 2, 4, 6, 5
+    scale = 0.6
+    d, up = _frame_case(14, B, H, F, S, D)
+    got = oracle.frame_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], F, up["dout"], scale,
+                                d["h0"], up["dhT"])
+    f64 = lambda x: np.asarray(x, np.float64)
+    for h in range(H):
+        q, k, v = (f64(d[n][0, h]).reshape(F, S, D) for n in ("q", "k", "v"))
+        beta = f64(d["beta"][0, h]).reshape(F, S)
+        g, do = f64(d["g"][0, h]), f64(up["dout"][0, h]).reshape(F, S, D)
+        I = np.eye(D)
+        # forward states with the frame matrices
+        G = [np.einsum("s,si,sj->ij", beta[f], k[f], k[f]) for f in range(F)]
+        Hm = [np.einsum("s,si,sj->ij", beta[f], k[f], v[f]) for f in range(F)]
+        Sst = [f64(d["h0"][0, h])]
+        for f in range(F):
+            Sst.append(np.exp(g[f]) * (I - G[f]) @ Sst[-1] + Hm[f])
+        A = [scale * q[f].T @ do[f] for f in range(F)]
+        X = [None] * F
+        X[F - 1] = f64(up["dhT"][0, h]) + A[F - 1]
+        for f in range(F - 1, 0, -1):
+            X[f - 1] = np.exp(g[f]) * (I - G[f]) @ X[f] + A[f - 1]
+        dh0 = np.exp(g[0]) * (I - G[0]) @ X[0]
+        for f in range(F):
+            P = np.exp(g[f]) * Sst[f]
+            U = k[f] @ X[f]                              # rows u_s = X_f^T k_s
+            R = v[f] - k[f] @ P                          # rows r_s = v_s - P^T k_s
+            sl = slice(f * S, (f + 1) * S)
+            np.testing.assert_allclose(got[0][0, h, sl], scale * do[f] @ Sst[f + 1].T, rtol=1e-11, atol=1e-13)
+            np.testing.assert_allclose(got[2][0, h, sl], beta[f][:, None] * U, rtol=1e-11, atol=1e-13)
+            np.testing.assert_allclose(got[3][0, h, sl], np.sum(U * R, axis=1), rtol=1e-11, atol=1e-13)
+            dk = beta[f][:, None] * (R @ X[f].T - U @ P.T)
+            np.testing.assert_allclose(got[1][0, h, sl], dk, rtol=1e-11, atol=1e-13)
+            np.testing.assert_allclose(got[4][0, h, f], np.sum(((I - G[f]) @ X[f]) * P), rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(got[5][0, h], dh0, rtol=1e-11, atol=1e-13)
