@@ -71,6 +71,8 @@ CASES = [
     (1, 100, 2, 32, 48, "bf16", 0.3, 0.5),
     (2, 150, 2, 64, 64, "bf16", 0.0, 0.5),
     (1, 77, 2, 128, 128, "bf16", 0.1, 0.0),
+    (1, 2000, 1, 64, 64, "bf16", 0.1, 0.3),    # 167 segments: error across a long walk back
+    (1, 1001, 1, 128, 16, "f32", 0.1, 0.3),
 ]
 
 
