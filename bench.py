@@ -1,7 +1,8 @@
 """Benchmark: chunkwise gated delta rule forward on one MI355X.
 
 One step = one gdn_chunk_fwd call over the "gdn" workload (B=2, H=16,
-T=4096, Dk=Dv=128, chunk 64, bf16 q/k/v, fp32 gates, fp32 state and output):
+T=4096, Dk=Dv=128, chunk 64, bf16 q/k/v, fp32 gates, fp32 state, bf16
+output o as the workload specifies; hT in fp32):
 chunk-local cumsum, the intra-chunk beta*K*K^T with decay mask, the (I+A)^-1
 solve, the WY form, the sequential inter-chunk state pass and the output
 product - the whole hot path, in two kernel launches (the parallel per-chunk
@@ -110,8 +111,56 @@ def cpu_baseline(d, B, T, H, budget_s=20.0):
     # tokens/s of the whole workload: B*T tokens need H heads of work
     value = reps * B * T * (nheads / H) / dt
     return {"value": value, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "host_cpu": host_cpu_model(), "nproc": os.cpu_count(),
             "sample": f"fp64 token recurrence on heads 0..{nheads - 1} of {H} (all B={B}, T={T}), "
                       f"{reps} run(s), {dt:.2f} s wall on {used} threads, scaled by {nheads}/{H}"}
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def measured_peaks(dev, reps=10):
+    """Achievable peaks on this device, measured next to the spec figures:
+    HBM bandwidth of a plain 1 GiB device-to-device copy (read + write
+    bytes over the time) and the bf16 rate of a large square matrix product
+    (the vendor GEMM), each the best of `reps` runs timed with HIP events."""
+    import torch
+    n = 256 * 1024 * 1024                           # 1 GiB of fp32 each way
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    m = 8192
+    a = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    b = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+    t_copy = best(lambda: dst.copy_(src))
+    t_mm = best(lambda: torch.mm(a, b))
+    out = {"hbm_copy_gbs": 2 * n * 4 / t_copy / 1e9, "bf16_gemm_tflops": 2 * m ** 3 / t_mm / 1e12,
+           "how": "1 GiB device copy (read+write bytes / time); 8192^3 bf16 torch.mm; best of "
+                  f"{reps}, HIP events"}
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 def _prepare(name, dev):
@@ -299,6 +348,11 @@ def main():
     if args.workload in ("gdn", "gdn_long"):
         rec["config"].update({"global_batch": wl["B"], "seq_len": wl["T"], "heads": wl["H"],
                               "head_dim": wl["Dk"], "chunk": wl["chunk"]})
+    mp = measured_peaks(dev)
+    r = rec["roofline"]
+    r["measured_peak"] = mp
+    r["frac_of_measured_hbm"] = achieved_gbs / mp["hbm_copy_gbs"]
+    r["mfma_frac_of_measured_gemm"] = r["mfma_tflops"] / mp["bf16_gemm_tflops"]
     if not args.no_cpu_baseline and args.workload == "gdn":
         rec["cpu_baseline"] = cpu_baseline(d, wl["B"], wl["T"], wl["H"])
     print(json.dumps(rec), flush=True)

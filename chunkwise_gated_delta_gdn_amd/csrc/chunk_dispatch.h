@@ -2,6 +2,8 @@
 // and step count, so they compile in parallel).
 #pragma once
 
+#include <atomic>
+
 #include "chunk_chain1.h"
 #include "chunk_kernels.h"
 #include "chunk_prep2.h"
@@ -16,17 +18,19 @@ constexpr bool use_chain1() {
     return ChunkShape<F32IN, KD, C, R>::PFRAG;
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device.  Cached per device ordinal in an
+// atomic (relaxed): concurrent first calls on one device each query the
+// attribute and store the same value, so the cache needs no lock.
 inline int num_cus() {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 // Launch both kernels of one instantiation on `stream`.

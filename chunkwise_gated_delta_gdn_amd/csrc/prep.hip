@@ -34,14 +34,10 @@ struct PrepArgs {
     int B, N, H;
 };
 
-#ifndef GDN_PREP_NT
-#define GDN_PREP_NT 1
-#endif
-// 16-byte store of a q, k or v output piece; streaming (nontemporal: the
-// outputs are not read again by this kernel) unless GDN_PREP_NT is 0
+// 16-byte streaming (nontemporal) store of a q, k or v output piece: the
+// outputs are not read again by this kernel
 __device__ __forceinline__ void st16(void *p, u32x4 v) {
-    if constexpr (GDN_PREP_NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-    else *reinterpret_cast<u32x4 *>(p) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 }
 template <bool F32OUT>
 __device__ __forceinline__ void store8(void *base, size_t elem, const float (&x)[8]) {
@@ -125,9 +121,8 @@ __device__ __forceinline__ void load_f8(const float *p, float (&x)[8]) {
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
-#ifndef GDN_PREP_TPB
-#define GDN_PREP_TPB 32
-#endif
+// tokens per block of consecutive tokens a workgroup takes
+constexpr int PREP_TPB = 32;
 // NSEG = segments per lane = H*D / 512 (rounded up).  Workgroups take blocks
 // of TPB consecutive tokens with a stride of the grid, wave w tokens w, w+4,
 // ... of each block, so one workgroup writes TPB consecutive entries of
@@ -137,7 +132,7 @@ __device__ __forceinline__ void load_f8(const float *p, float (&x)[8]) {
 // processed.
 template <bool F32IN, bool F32OUT, int D, int NSEG>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
-    constexpr int TPB = GDN_PREP_TPB, TPW = TPB / 4;
+    constexpr int TPB = PREP_TPB, TPW = TPB / 4;
     static_assert(TPB % 4 == 0, "whole tokens per wave");
     const int l = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -302,9 +297,8 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
     const long ntok = (long)a.B * a.N;
     const int C = a.H * D;
     const int nseg = C / 8;
-    // at least four tokens per wave: weights stay resident, loads overlap
-    const int per_wg = GDN_PREP_TPB > 16 ? GDN_PREP_TPB : 16;
-    long blocks = (ntok + per_wg - 1) / per_wg;
+    // blocks of PREP_TPB tokens, eight per wave: weights stay resident, loads overlap
+    long blocks = (ntok + PREP_TPB - 1) / PREP_TPB;
     if (blocks < 1) blocks = 1;
     if (blocks > 65535) blocks = 65535;
     const dim3 grid((unsigned)blocks);

@@ -38,7 +38,9 @@
  * - Ownership: all buffers belong to the caller.  The library keeps no
  *   pointer after the call returns, allocates no memory, and enqueues all
  *   work on `stream` (a hipStream_t passed as void*, NULL = default stream);
- *   the caller keeps buffers alive until that stream has finished.
+ *   the caller keeps buffers alive until that stream has finished.  Its only
+ *   process-wide state is a per-device cache of the compute-unit count
+ *   (atomic, set on first use) besides the thread-local error text.
  * - Work space: entry points that need scratch device memory take
  *   (workspace, workspace_bytes); the matching *_workspace_bytes() query
  *   returns the size needed (0 means workspace may be NULL).
@@ -260,8 +262,9 @@ int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_norm_w,
  *   dh0             (B, H, Dk, Dv) float32, nullable (not stored)
  * Supported: Dk in {16, 32, 64, 128}; Dv a multiple of 16 up to 4096; any
  * T >= 0.  q, k, v and dout 16-byte aligned, the other tensors 4-byte.  The work
- * space (gdn_bwd_workspace_bytes) holds the kept states and per-slice
- * partial sums: about (2 Dk + 2) * Dv / 16 * 4 bytes per token and head.
+ * space (gdn_bwd_workspace_bytes, the only authority on its size) holds the
+ * states kept every 12 tokens and the per-16-column partial sums: about
+ * (Dk Dv / 12 + (2 Dk + 2) Dv / 16) * 4 bytes per token and head.
  */
 size_t gdn_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv);
 int gdn_bwd(const void *q, const void *k, const void *v,

@@ -169,6 +169,50 @@ def test_scan_camera_workload(gdn):
     assert max(per_frame) <= TOL["bf16"]
 
 
+def test_camera_pipeline_end_to_end(gdn):
+    """The camera workload as the benchmark runs it: GPU gdn_prep (bf16
+    output) feeding GPU gdn_recurrent_fwd (forward and reverse) and
+    gdn_recurrent_den_fwd, against the oracle's prep rounded to bf16 feeding
+    the oracle's scans, frame by frame.  Where the GPU prep's fp32 value and
+    the exact one straddle a bf16 rounding boundary the two pipelines start
+    from inputs one ulp apart; the scan must not amplify that past the bar."""
+    import torch
+    _say("camera pipeline end to end: GPU prep -> GPU scan (forward, reverse, normaliser)")
+    d = synth.workload_inputs("camera")
+    pr = _prep_ref(d)
+    q, k, v = (synth.round_bf16(pr[n]) for n in ("q", "k", "v"))
+    t = {n: to_dev(d[n], "f32") for n in ("q_norm_w", "k_norm_w", "proj_q", "proj_kv", "rope_cos", "rope_sin",
+                                           "beta", "g")}
+    gp = gdn.gdn_prep(to_dev(d["qkv"], "bf16"), t["q_norm_w"], t["k_norm_w"], t["proj_q"], t["proj_kv"],
+                      t["rope_cos"], t["rope_sin"], d["k_scale"], d["eps"])
+    torch.cuda.synchronize()
+    flips = {n: float(np.mean(to_np(gp[n]) != x)) for n, x in (("q", q), ("k", k), ("v", v))}
+    _say("  prep elements one bf16 ulp off the rounded oracle: "
+         + " ".join(f"{n}={f:.1e}" for n, f in flips.items()))
+    F, S = d["F"], d["S"]
+
+    def per_frame(got, ref, nf):
+        return [max_rel_err(got[:, :, f * S:(f + 1) * S], ref[:, :, f * S:(f + 1) * S]) for f in range(nf)]
+
+    out, hT = gdn.gdn_recurrent_fwd(gp["q"], gp["k"], gp["v"], t["beta"], t["g"], 1.0)
+    out_r, _ = gdn.gdn_recurrent_fwd(gp["q"], gp["k"], gp["v"], t["beta"], t["g"], 1.0, reverse=True)
+    den, zT = gdn.gdn_recurrent_den_fwd(gp["q"], gp["k"], t["beta"], t["g"], 1.0)
+    torch.cuda.synchronize()
+    oref, href = oracle.frame_scan(q, k, v, d["beta"], d["g"], F, 1.0)
+    rref = oracle.frame_scan_reverse(q, k, v, d["beta"], d["g"], F, 1.0)
+    dref, zref = oracle.frame_den(q, k, d["beta"], d["g"], F, 1.0)
+    pf = per_frame(to_np(out), oref, F)
+    pr_ = per_frame(to_np(out_r), rref, F - 1)
+    pd = per_frame(to_np(den)[..., None], dref[..., None], F)
+    eh, ez = max_rel_err(to_np(hT), href), max_rel_err(to_np(zT), zref)
+    _say("  forward per frame " + " ".join(f"{e:.1e}" for e in pf) + f" hT={eh:.1e}")
+    _say("  reverse per frame " + " ".join(f"{e:.1e}" for e in pr_))
+    _say("  normaliser per frame " + " ".join(f"{e:.1e}" for e in pd) + f" zT={ez:.1e}")
+    assert max(pf) <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert max(pr_) <= TOL["bf16"] and np.all(to_np(out_r)[:, :, (F - 1) * S:] == 0.0)
+    assert max(pd) <= TOL["bf16"] and ez <= TOL["bf16"]
+
+
 def test_scan_one_token_per_frame_matches_chunk_path(gdn):
     """S = 1: the frame scan is the token-level gated delta rule; compare with
     gdn_chunk_fwd on the same inputs (GPU against GPU) and with the oracle."""

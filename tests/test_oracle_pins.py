@@ -263,6 +263,23 @@ def test_cam_prep_hand_worked_example():
         np.testing.assert_allclose(out[name][0, 0, 0], e[name], rtol=1e-12)
 
 
+def test_cam_prep_hand_worked_norm_weights():
+    """The per-channel RMSNorm weight path: weights indexed over all H*D
+    channels, applied before the ReLU and before the projection."""
+    fx = json.load(open(os.path.join(GOLDEN, "cam_prep_hand_weights_h2d8.json")))
+    i = fx["inputs"]
+    H, D = i["H"], i["D"]
+    qkv = _f32([i["q"], i["k"], i["v"]]).reshape(1, 1, 3, H, D)
+    out = oracle.cam_prep(qkv, _f32(i["q_norm_w"]), _f32(i["k_norm_w"]), _f32(i["proj_q"]).reshape(1, 1, 4, 4),
+                          _f32(i["proj_kv"]).reshape(1, 1, 4, 4), _f32(i["rope_cos"]).reshape(1, D // 2),
+                          _f32(i["rope_sin"]).reshape(1, D // 2), i["k_scale"], i["eps"])
+    e = fx["expected"]
+    for name in ("q", "k", "v"):
+        np.testing.assert_allclose(out[name][0, :, 0], e[name], atol=1e-12, err_msg=name)
+    for name in ("k_pre_sq", "k_post_sq", "inflation_sq"):
+        np.testing.assert_allclose(out[name][0, :, 0], e[name], rtol=1e-12, err_msg=name)
+
+
 def test_se3_inverse_round_trips():
     d = synth.camera_inputs(1, 2, 5, 1, 8, seed=12, dtype="f32")
     P = d["P"].astype(np.float64)
