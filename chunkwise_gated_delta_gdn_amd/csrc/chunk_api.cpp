@@ -2,10 +2,41 @@
 // dispatch to the chunk kernel instantiations).
 #include <math.h>
 
+#include <mutex>
+
 #include "api_common.h"
 #include "chunk_dispatch.h"
 
+// Scratch of gdn_chunk_fwd_noalloc: the work space of that entry point, one
+// copy per device, held from the library's first use on a device until the
+// process ends.  Host code never passes `scratch` itself to a kernel (on the
+// host it names a stand-in, not device memory): it passes the device address
+// hipGetSymbolAddress returned for the current device.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_dev[64];        // per device ordinal: device address of `scratch`
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void **out, const char *name) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return gdn::check_hip(e, name);
+    GDN_REQUIRE(dev >= 0 && dev < 64, GDN_EUNSUPPORTED, "%s: device ordinal %d (at most 63)", name, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return gdn::check_hip(e, name);
+        GDN_REQUIRE(p != nullptr, GDN_EHIP, "%s: no device address for the scratch array", name);
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return GDN_OK;
+}
 
 bool find_impl(int dtype, int r, int KD, int chunk, gdn::ChunkImpl *impl) {
     if (dtype == GDN_DTYPE_F32) return gdn::find_chunk_f32(KD, chunk, r, impl);
@@ -18,7 +49,7 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
                  const float *log_decay, const float *step_mask, int r, float scale,
                  const float *h0, float *hT, void *o, int B, int T, int H, int dk, int Dv,
                  int chunk, int dtype, int out_dtype, void *workspace, size_t workspace_bytes,
-                 void *stream, const char *name) {
+                 void *stream, const char *name, bool noalloc = false) {
     GDN_REQUIRE(B >= 0 && T >= 0 && H >= 0, GDN_EINVAL, "%s: negative size (B=%d T=%d H=%d)", name, B, T, H);
     GDN_REQUIRE(dtype == GDN_DTYPE_F32 || dtype == GDN_DTYPE_BF16, GDN_EINVAL, "%s: unknown dtype %d", name, dtype);
     GDN_REQUIRE(out_dtype == GDN_DTYPE_F32 || out_dtype == GDN_DTYPE_BF16, GDN_EINVAL,
@@ -54,6 +85,17 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
                 dtype == GDN_DTYPE_F32 ? "f32" : "bf16", r, KD, chunk);
     if ((size_t)B * H == 0) return GDN_OK;
     const size_t need = impl.workspace(B, T, H);
+    if (noalloc) {
+        GDN_REQUIRE(need <= GDN_NOALLOC_SCRATCH_BYTES, GDN_EWORKSPACE,
+                    "%s: this shape needs %zu bytes of scratch, the no-allocation entry point holds at most "
+                    "%zu (call gdn_chunk_fwd with a work space)", name, need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+        workspace = nullptr;
+        if (need > 0) {
+            const int rc = scratch_address(&workspace, name);
+            if (rc != GDN_OK) return rc;
+        }
+        workspace_bytes = GDN_NOALLOC_SCRATCH_BYTES;
+    }
     GDN_REQUIRE(workspace_bytes >= need, GDN_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", name,
                 workspace_bytes, need);
     GDN_REQUIRE(need == 0 || (workspace && gdn::aligned(workspace, 16)), GDN_EINVAL,
@@ -92,6 +134,14 @@ extern "C" int gdn_chunk_fwd(const void *q, const void *k, const void *v, const 
                              void *workspace, size_t workspace_bytes, void *stream) {
     return chunk_common(q, k, v, beta, log_decay, nullptr, 1, scale, h0, hT, o, B, T, H, Dk, Dv, chunk,
                         dtype, out_dtype, workspace, workspace_bytes, stream, "gdn_chunk_fwd");
+}
+
+extern "C" int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *beta,
+                                     const float *log_decay, float scale, const float *h0, float *hT, void *o,
+                                     int B, int T, int H, int Dk, int Dv, int chunk, int dtype, int out_dtype,
+                                     void *stream) {
+    return chunk_common(q, k, v, beta, log_decay, nullptr, 1, scale, h0, hT, o, B, T, H, Dk, Dv, chunk,
+                        dtype, out_dtype, nullptr, 0, stream, "gdn_chunk_fwd_noalloc", true);
 }
 
 extern "C" size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, int dtype) {

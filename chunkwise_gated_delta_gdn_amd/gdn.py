@@ -22,7 +22,7 @@ GDN_DTYPE_BF16 = 1
 # every symbol declared in include/gdn.h
 EXPORTS = (
     "gdn_last_error", "gdn_abi_version",
-    "gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes",
+    "gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_noalloc",
     "deltaproduct_chunk_fwd", "deltaproduct_chunk_fwd_workspace_bytes",
     "gdn_recurrent_fwd", "gdn_recurrent_fwd_workspace_bytes",
     "gdn_recurrent_den_fwd", "gdn_recurrent_den_fwd_workspace_bytes",
@@ -50,6 +50,8 @@ def _load():
     lib.gdn_abi_version.restype = I
     lib.gdn_chunk_fwd.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, I, P, Z, P]
     lib.gdn_chunk_fwd.restype = I
+    lib.gdn_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, I, P]
+    lib.gdn_chunk_fwd_noalloc.restype = I
     lib.gdn_chunk_fwd_workspace_bytes.argtypes = [I] * 7
     lib.gdn_chunk_fwd_workspace_bytes.restype = Z
     lib.deltaproduct_chunk_fwd.argtypes = [P, P, P, P, P, P, I, F, P, P, P, I, I, I, I, I, I, I, I, P, Z, P]
@@ -144,6 +146,36 @@ def gdn_chunk_fwd(q, k, v, beta, log_decay, scale=1.0, h0=None, output_final_sta
                             _ptr(h0), _ptr(hT), _ptr(o), B, T, H, Dk, Dv, int(chunk), dt,
                             _dtype_code(out_dtype), _ptr(ws), nws, _stream(q.device))
     _check("gdn_chunk_fwd", rc)
+    return o, hT
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, beta, log_decay, scale=1.0, h0=None, output_final_state=True,
+                          chunk=64, out_dtype=torch.float32, o=None, hT=None):
+    """:func:`gdn_chunk_fwd` on the library's own static scratch (no work-space
+    allocation).  ``o`` and ``hT`` may be passed in preallocated, so that the
+    call itself allocates nothing.  Calls that overlap on one device race."""
+    _dev(q, k, v, beta, log_decay, h0, o, hT)
+    _f32(beta, "beta"), _f32(log_decay, "log_decay"), _f32(h0, "h0"), _f32(hT, "hT")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != (B, T, H) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v shapes or dtypes disagree")
+    if beta.shape != (B, T, H) or log_decay.shape != (B, T, H):
+        raise ValueError("beta and log_decay must be (B, T, H)")
+    if h0 is not None and h0.shape != (B, H, Dk, Dv):
+        raise ValueError("h0 must be (B, H, Dk, Dv)")
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=out_dtype, device=q.device)
+    elif o.shape != (B, T, H, Dv):
+        raise ValueError("o must be (B, T, H, Dv)")
+    if hT is None and output_final_state:
+        hT = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    elif hT is not None and hT.shape != (B, H, Dk, Dv):
+        raise ValueError("hT must be (B, H, Dk, Dv)")
+    rc = _lib.gdn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_decay), float(scale),
+                                    _ptr(h0), _ptr(hT), _ptr(o), B, T, H, Dk, Dv, int(chunk),
+                                    _dtype_code(q.dtype), _dtype_code(o.dtype), _stream(q.device))
+    _check("gdn_chunk_fwd_noalloc", rc)
     return o, hT
 
 

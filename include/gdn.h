@@ -108,6 +108,31 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int ch
                                      int dtype);
 
 /*
+ * gdn_chunk_fwd_noalloc - gdn_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, meaning, kernels and
+ * results as gdn_chunk_fwd, without (workspace, workspace_bytes): the work
+ * space is a static device array of GDN_NOALLOC_SCRATCH_BYTES inside the
+ * library, one copy per device, looked up on the first call on a device and
+ * held until the process ends.  This entry point calls no hipMalloc,
+ * hipFree or allocating library routine.
+ * Limit: shapes whose gdn_chunk_fwd_workspace_bytes exceeds
+ * GDN_NOALLOC_SCRATCH_BYTES are rejected with GDN_EWORKSPACE (at Dk = 128,
+ * chunk 64, bf16: about 19.2 KB per chunk of one (b, h), i.e. B*H*ceil(T/64)
+ * up to 3490 chunks, e.g. B*H = 32 with T <= 6976).
+ * Every call on one device shares that device's array: calls that overlap
+ * on one device (on different streams, or from several threads without
+ * ordering) race and give wrong results; serialise them.  Nothing in the
+ * array needs to start at zero (each call writes every entry it reads).
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                          const float *beta, const float *log_decay, float scale,
+                          const float *h0, float *hT, void *o,
+                          int B, int T, int H, int Dk, int Dv, int chunk,
+                          int dtype, int out_dtype, void *stream);
+
+/*
  * deltaproduct_chunk_fwd - chunkwise gated DeltaProduct forward ([dp]).
  *
  * The key of width K = r*dk is split into r sub-keys k_{t,a}.  Step a of
