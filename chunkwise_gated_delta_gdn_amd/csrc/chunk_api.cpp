@@ -38,6 +38,16 @@ int scratch_address(void **out, const char *name) {
     return GDN_OK;
 }
 
+// Instantiated key width that runs a key of width r*dk: the width itself
+// for r = 2, else the next power of two (16 ... 256; the kernels read the
+// features past r*dk as zero and never store them).
+int padded_key_width(int r, int dk) {
+    if (r != 1) return r * dk;
+    int kd = 16;
+    while (kd < dk) kd *= 2;
+    return kd;
+}
+
 bool find_impl(int dtype, int r, int KD, int chunk, gdn::ChunkImpl *impl) {
     if (dtype == GDN_DTYPE_F32) return gdn::find_chunk_f32(KD, chunk, r, impl);
     if (r == 1) return gdn::find_chunk_bf16_r1(KD, chunk, impl);
@@ -55,8 +65,12 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
     GDN_REQUIRE(out_dtype == GDN_DTYPE_F32 || out_dtype == GDN_DTYPE_BF16, GDN_EINVAL,
                 "%s: unknown out_dtype %d", name, out_dtype);
     GDN_REQUIRE(r == 1 || r == 2, GDN_EUNSUPPORTED, "%s: r=%d (supported: 1, 2)", name, r);
-    GDN_REQUIRE(dk == 16 || dk == 32 || dk == 64 || dk == 128 || dk == 256, GDN_EUNSUPPORTED,
-                "%s: key width %d (supported: 16, 32, 64, 128, 256)", name, dk);
+    if (r == 1)
+        GDN_REQUIRE(dk > 0 && dk % 16 == 0 && dk <= 256, GDN_EUNSUPPORTED,
+                    "%s: key width %d (supported: multiples of 16 up to 256)", name, dk);
+    else
+        GDN_REQUIRE(dk == 16 || dk == 32 || dk == 64 || dk == 128, GDN_EUNSUPPORTED,
+                    "%s: sub-key width %d (supported: 16, 32, 64, 128)", name, dk);
     GDN_REQUIRE(r * dk <= 256, GDN_EUNSUPPORTED, "%s: total key width r*dk=%d exceeds 256", name, r * dk);
     GDN_REQUIRE(Dv > 0 && Dv % 16 == 0 && Dv <= 256, GDN_EUNSUPPORTED,
                 "%s: Dv=%d (must be a multiple of 16, at most 256)", name, Dv);
@@ -78,11 +92,11 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
     if (step_mask)
         for (int i = 0; i < r * r; ++i)
             GDN_REQUIRE(isfinite(step_mask[i]), GDN_EINVAL, "%s: step_mask[%d] is not finite", name, i);
-    const int KD = r * dk;
+    const int KD = padded_key_width(r, dk);
     gdn::ChunkImpl impl;
     GDN_REQUIRE(find_impl(dtype, r, KD, chunk, &impl), GDN_EUNSUPPORTED,
                 "%s: no kernel for dtype=%s r=%d key width=%d chunk=%d", name,
-                dtype == GDN_DTYPE_F32 ? "f32" : "bf16", r, KD, chunk);
+                dtype == GDN_DTYPE_F32 ? "f32" : "bf16", r, r * dk, chunk);
     if ((size_t)B * H == 0) return GDN_OK;
     const size_t need = impl.workspace(B, T, H);
     if (noalloc) {
@@ -115,6 +129,7 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
     a.T = T;
     a.H = H;
     a.Dv = Dv;
+    a.kw = r * dk;
     a.out_bf16 = out_dtype == GDN_DTYPE_BF16;
     a.scale = scale;
     for (int i = 0; i < 4; ++i) a.mask[i] = 0.f;
@@ -147,7 +162,9 @@ extern "C" int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v
 extern "C" size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, int dtype) {
     (void)Dv;
     gdn::ChunkImpl impl;
-    if (B < 0 || T < 0 || H < 0 || !find_impl(dtype, 1, Dk, chunk, &impl)) return 0;
+    if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dk % 16 || Dk > 256 ||
+        !find_impl(dtype, 1, padded_key_width(1, Dk), chunk, &impl))
+        return 0;
     return impl.workspace(B, T, H);
 }
 
@@ -156,8 +173,6 @@ extern "C" int deltaproduct_chunk_fwd(const void *q, const void *k, const void *
                                       const float *h0, float *hT, void *o, int B, int T, int H, int dk,
                                       int Dv, int chunk, int dtype, int out_dtype, void *workspace,
                                       size_t workspace_bytes, void *stream) {
-    if (dk > 128)
-        return gdn::set_error(GDN_EUNSUPPORTED, "deltaproduct_chunk_fwd: dk=%d (supported up to 128)", dk);
     return chunk_common(q, k, v, beta, log_decay, step_mask, r, scale, h0, hT, o, B, T, H, dk, Dv, chunk,
                         dtype, out_dtype, workspace, workspace_bytes, stream, "deltaproduct_chunk_fwd");
 }
@@ -166,6 +181,8 @@ extern "C" size_t deltaproduct_chunk_fwd_workspace_bytes(int B, int T, int H, in
                                                          int chunk, int dtype) {
     (void)Dv;
     gdn::ChunkImpl impl;
-    if (B < 0 || T < 0 || H < 0 || !find_impl(dtype, r, r * dk, chunk, &impl)) return 0;
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dk % 16 || r * dk > 256 ||
+        !find_impl(dtype, r, padded_key_width(r, dk), chunk, &impl))
+        return 0;
     return impl.workspace(B, T, H);
 }

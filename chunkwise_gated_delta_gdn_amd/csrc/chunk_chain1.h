@@ -106,6 +106,10 @@ __device__ __forceinline__ int kswz(int r) {
     else return r & 3;
 }
 
+// Sixteen zero bytes in global memory: the source of the LDS-direct loads of
+// K pieces past the key width (every lane of such a load writes its piece).
+static __device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};
+
 // LDS-direct 16-byte load: lane i writes at lds_base + 16 i (lds_base uniform).
 __device__ __forceinline__ void dma16(const void *src, void *lds_base) {
     typedef __attribute__((address_space(3))) void lds_void;
@@ -186,9 +190,10 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
         for (int ti = 0; ti < NST; ++ti) {
             Sreg[ti] = zero4();
             if (args.h0) {
-                const float *hp = args.h0 + ((size_t)bh * KD) * Dv + v0 + c16;
+                const float *hp = args.h0 + ((size_t)bh * args.kw) * Dv + v0 + c16;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Sreg[ti][e] = hp[(size_t)feat(ti, e) * Dv];
+                for (int e = 0; e < 4; ++e)
+                    if (feat(ti, e) < args.kw) Sreg[ti][e] = hp[(size_t)feat(ti, e) * Dv];
             }
         }
         __syncthreads();
@@ -311,9 +316,10 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
         if (args.hT) {
 #pragma unroll
             for (int ti = 0; ti < NST; ++ti) {
-                float *hp = args.hT + ((size_t)bh * KD) * Dv + v0 + c16;
+                float *hp = args.hT + ((size_t)bh * args.kw) * Dv + v0 + c16;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) hp[(size_t)feat(ti, e) * Dv] = Sreg[ti][e];
+                for (int e = 0; e < 4; ++e)
+                    if (feat(ti, e) < args.kw) hp[(size_t)feat(ti, e) * Dv] = Sreg[ti][e];
             }
         }
         return;
@@ -337,9 +343,10 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
     constexpr int NDK = S::SZ_KS / 1024, NDT = S::SZ_TB / 1024, NDV = S::SZ_BV / 1024;
     constexpr int NDMA = NDK + NDT + NDV + 1;
     static_assert(NGV <= 64 && S::SZ_GATE >= NGV * 16, "gate table: one partial wave load");
-    const size_t tokq = (size_t)H * KD, tokv = (size_t)H * Dv;
-    const u16 *kg = reinterpret_cast<const u16 *>(args.k) + ((size_t)b * T * H + h) * KD;
-    const u16 *qg = reinterpret_cast<const u16 *>(args.q) + ((size_t)b * T * H + h) * KD;
+    const int kw = args.kw;                     // key row width in HBM; pieces past it are zero
+    const size_t tokq = (size_t)H * kw, tokv = (size_t)H * Dv;
+    const u16 *kg = reinterpret_cast<const u16 *>(args.k) + ((size_t)b * T * H + h) * kw;
+    const u16 *qg = reinterpret_cast<const u16 *>(args.q) + ((size_t)b * T * H + h) * kw;
     const u16 *vg = reinterpret_cast<const u16 *>(args.v) + ((size_t)b * T * H + h) * Dv + v0;
     const u16 *tg = reinterpret_cast<const u16 *>(args.tmat) + (size_t)bh * NT * C * C;
     const float *gtg = reinterpret_cast<const float *>(args.gtab) + (size_t)bh * NT * S::NGATE;
@@ -358,8 +365,10 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
             for (int k = LI; k < NDMA; k += NLW) {
                 if (k < NDK) {                  // K: row r (token), stored piece j holds piece j ^ kswz(r)
                     const int pos = k * 64 + l, r = pos / NKC, sc = pos % NKC;
-                    const int t = min(c * C + r, tlast);
-                    dma16(kg + (size_t)t * tokq + ((sc ^ kswz<NKC>(r)) << 3), Ks(p) + k * 512);
+                    const int t = min(c * C + r, tlast), pc = sc ^ kswz<NKC>(r);
+                    dma16(pc * 8 < kw ? static_cast<const void *>(kg + (size_t)t * tokq + (pc << 3))
+                                      : static_cast<const void *>(&kZero16),
+                          Ks(p) + k * 512);
                 } else if (k < NDK + NDT) {     // T diag(beta): row r (token)
                     const int kk = k - NDK, pos = kk * 64 + l, r = pos / (C / 8), sc = pos % (C / 8);
                     dma16(tg + (size_t)c * C * C + r * C + ((sc ^ (r & TSW)) << 3), Tb(p) + kk * 512);
@@ -387,8 +396,11 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
             for (int i = 0; i < NTW; ++i) {
                 const int t = min(c * C + tw(i) * 16 + c16, tlast);   // rows past T are never stored
 #pragma unroll
-                for (int m = 0; m < NKS; ++m)
-                    qf[i][m] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)t * tokq + m * 32 + 8 * g);
+                for (int m = 0; m < NKS; ++m) {
+                    const bool pad = m * 32 + 8 * g >= kw;   // loaded anyway (counted loads), then zeroed
+                    qf[i][m] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)t * tokq + (pad ? 0 : m * 32 + 8 * g));
+                    if (pad) qf[i][m] = bf16x8{};
+                }
                 const uint4 *pc = reinterpret_cast<const uint4 *>(args.pfrag) + ((size_t)bh * NT + c) * NLOW * 64 +
                                   (tw(i) * (tw(i) + 1) / 2) * 64 + l;
 #pragma unroll

@@ -9,10 +9,12 @@ bool find_chunk_f32(int KD, int C, int R, ChunkImpl *out) {
         GDN_CASE(true, 32, 16, 1) GDN_CASE(true, 32, 32, 1) GDN_CASE(true, 32, 64, 1)
         GDN_CASE(true, 64, 16, 1) GDN_CASE(true, 64, 32, 1) GDN_CASE(true, 64, 64, 1)
         GDN_CASE(true, 128, 16, 1) GDN_CASE(true, 128, 32, 1)
+        GDN_CASE(true, 256, 16, 1) GDN_CASE(true, 256, 32, 1)
     } else if (R == 2) {
         GDN_CASE(true, 32, 16, 2) GDN_CASE(true, 32, 32, 2)
         GDN_CASE(true, 64, 16, 2) GDN_CASE(true, 64, 32, 2)
         GDN_CASE(true, 128, 16, 2) GDN_CASE(true, 128, 32, 2)
+        GDN_CASE(true, 256, 16, 2) GDN_CASE(true, 256, 32, 2)
     }
     return false;
 }

@@ -64,6 +64,7 @@ struct ChunkArgs {
     void *pfrag;     // work space: intra-chunk P tiles as MFMA fragments (PFRAG shapes)
     void *gtab;      // work space: e^{G_t} [C], e^{G_L - G_t} [C], e^{G_L}, 0, 0, 0 per chunk, fp32 (PFRAG shapes)
     int B, T, H, Dv;
+    int kw;          // key row width in HBM (q, k, h0, hT rows); KD >= kw, features past kw are zero
     int out_bf16;
     float scale;
     float mask[4];   // R x R step mask, row-major
@@ -177,10 +178,10 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(ChunkArgs args) {
     for (int idx = tid; idx < C * NV; idx += 256) {
         const int t = idx / NV, cv = idx % NV, tt = t0 + t;
         U16x8 raw;
-        if (tt < T) {
+        if (tt < T && cv * VEC < args.kw) {
             const size_t row = ((size_t)b * T + tt) * H + h;
             raw = *reinterpret_cast<const U16x8 *>(reinterpret_cast<const unsigned char *>(args.k) +
-                                                   (row * KD + cv * VEC) * S::ESZ);
+                                                   (row * args.kw + cv * VEC) * S::ESZ);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) raw.v[e] = 0;
@@ -373,15 +374,18 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
     U16x8 rkq[PKQ], rv[PV], rt[PT];
     float rbeta = 0.f, rg = 0.f;
     // Per-slot source offsets (bytes) at chunk 0; chunk c adds c*C token rows.
-    const size_t tok_bytes_qk = (size_t)H * KD * S::ESZ, tok_bytes_v = (size_t)H * Dv * S::ESZ;
+    const int kw = args.kw;
+    const size_t tok_bytes_qk = (size_t)H * kw * S::ESZ, tok_bytes_v = (size_t)H * Dv * S::ESZ;
     size_t kq_off[PKQ], v_off[PV];
     int kq_t[PKQ], v_t[PV];
+    bool kq_pad[PKQ];                             // a feature vector past kw: zero
 #pragma unroll
     for (int p = 0; p < PKQ; ++p) {
         const int idx = otid + 256 * p;
         const int rem = idx % (C * NV);
         kq_t[p] = rem / NV;
-        kq_off[p] = (((size_t)b * T + kq_t[p]) * H + h) * KD * S::ESZ + (size_t)(rem % NV) * 16;
+        kq_pad[p] = (rem % NV) * VEC >= kw;
+        kq_off[p] = (((size_t)b * T + kq_t[p]) * H + h) * kw * S::ESZ + (kq_pad[p] ? 0 : (size_t)(rem % NV) * 16);
     }
 #pragma unroll
     for (int p = 0; p < PV; ++p) {
@@ -400,7 +404,7 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
             const int idx = otid + 256 * p;
             if (idx < NKQ) {
                 const unsigned char *src = (idx < C * NV ? kbase : qbase) + kq_off[p] + (size_t)t0 * tok_bytes_qk;
-                if (full || t0 + kq_t[p] < T) {
+                if ((full || t0 + kq_t[p] < T) && !kq_pad[p]) {
                     rkq[p] = *reinterpret_cast<const U16x8 *>(src);
                 } else {
 #pragma unroll
@@ -511,9 +515,12 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
             Sreg[n] = zero4();
             const int ts = w + 4 * n;
             if (ts < NST && args.h0) {
-                const float *hp = args.h0 + ((size_t)bh * KD) * Dv + v0 + (l & 15);
+                const float *hp = args.h0 + ((size_t)bh * args.kw) * Dv + v0 + (l & 15);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Sreg[n][e] = hp[(size_t)(ts * 16 + 4 * (l >> 4) + e) * Dv];
+                for (int e = 0; e < 4; ++e) {
+                    const int row = ts * 16 + 4 * (l >> 4) + e;
+                    Sreg[n][e] = row < args.kw ? hp[(size_t)row * Dv] : 0.f;
+                }
             }
         }
         write_state_operand();
@@ -685,9 +692,12 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
         for (int n = 0; n < NSTW; ++n) {
             const int ts = w + 4 * n;
             if (ts < NST) {
-                float *hp = args.hT + ((size_t)bh * KD) * Dv + v0 + (l & 15);
+                float *hp = args.hT + ((size_t)bh * args.kw) * Dv + v0 + (l & 15);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) hp[(size_t)(ts * 16 + 4 * (l >> 4) + e) * Dv] = Sreg[n][e];
+                for (int e = 0; e < 4; ++e) {
+                    const int row = ts * 16 + 4 * (l >> 4) + e;
+                    if (row < args.kw) hp[(size_t)row * Dv] = Sreg[n][e];
+                }
             }
         }
     }

@@ -73,16 +73,20 @@ __global__ __launch_bounds__(256) void chunk_prep2_kernel(ChunkArgs args) {
 
         // ---- K and Q rows as MFMA fragments: lane (g, j) of (tt, m) holds
         //      row 16 tt + j, key features 32m + 8g + {0..7}; zero past T ----
+        // (features past the key width kw <= KD read as zero)
+        const int kw = args.kw;
         bf16x8 kf[NTT][NKS], qf[NTT][NKS];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
             const int t = t0 + tt * 16 + c16;
-            const size_t off = (row0 + (size_t)min(t, T - 1) * H) * KD + 8 * g;
+            const size_t off = (row0 + (size_t)min(t, T - 1) * H) * kw;
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
-                kf[tt][m] = *reinterpret_cast<const bf16x8 *>(kg + off + m * 32);
-                qf[tt][m] = *reinterpret_cast<const bf16x8 *>(qg + off + m * 32);
-                if (t >= T) kf[tt][m] = qf[tt][m] = bf16x8{};
+                const int f = m * 32 + 8 * g;
+                const bool pad = f >= kw;
+                kf[tt][m] = *reinterpret_cast<const bf16x8 *>(kg + off + (pad ? 0 : f));
+                qf[tt][m] = *reinterpret_cast<const bf16x8 *>(qg + off + (pad ? 0 : f));
+                if (t >= T || pad) kf[tt][m] = qf[tt][m] = bf16x8{};
             }
         }
 

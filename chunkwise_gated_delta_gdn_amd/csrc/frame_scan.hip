@@ -34,6 +34,8 @@ struct FrameArgs {
     float *gh;       // [B*H*F][2][D][D] G_f, H_f
     float *sf;       // [B*H][F][D][D] state after each frame, transposed ([column][row])
     int B, H, F, S, nsplit, spl;
+    int dd;          // head width in HBM (q, k, v, out rows; h0, hT); the kernels' D >= dd,
+                     // features past dd read as zero and are never stored
     int reverse;     // anti-causal scan: frame f reads the state built from frames f+1 .. F-1
     int den;         // normaliser stream: unit values (v = 1), vector state z (h0/hT are z0/zT,
                      // (B, H, D)), out is den (B, H, N)
@@ -111,14 +113,14 @@ __global__ __launch_bounds__(256) void frame_gram_kernel(FrameArgs a) {
             const int s = idx / SEGS, i0 = (idx % SEGS) * 8;
             float kx[8], vx[8];
             float bt = 0.f;
-            if (s0 + s < s_hi) {
+            if (s0 + s < s_hi && i0 < a.dd) {
                 const size_t row = row0 + s0 + s;
-                load8<F32IN>(a.k, row * D + i0, kx);
+                load8<F32IN>(a.k, row * a.dd + i0, kx);
                 if constexpr (VONES) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) vx[e] = 1.f;
                 } else {
-                    load8<F32IN>(a.v, row * D + i0, vx);
+                    load8<F32IN>(a.v, row * a.dd + i0, vx);
                 }
                 bt = a.beta[row];
             } else {
@@ -244,8 +246,14 @@ __global__ __launch_bounds__(512) void frame_gram_bf16_kernel(FrameArgs a) {
                 const int p = tid + NTH * i;
                 const int mat = p / (TSG * SEGS), rem = p % (TSG * SEGS), r = rem / SEGS, sg = rem % SEGS;
                 const int s = min(s0 + r, s_hi - 1);
-                if (!VONES || !mat)            // unit values: no V rows
-                    st.x[u][i] = *reinterpret_cast<const u32x4 *>((mat ? vin : kin) + (row0 + s) * D + sg * 8);
+                if (!VONES || !mat) {          // unit values: no V rows
+                    // pieces past dd: loaded from the row start (the loads stay
+                    // unconditional), then zeroed
+                    const bool pad = sg * 8 >= a.dd;
+                    st.x[u][i] = *reinterpret_cast<const u32x4 *>((mat ? vin : kin) + (row0 + s) * a.dd +
+                                                                  (pad ? 0 : sg * 8));
+                    if (pad) st.x[u][i] = u32x4{0u, 0u, 0u, 0u};
+                }
             }
             const int s = s0 + (tid & (TSG - 1));
             const float bt = a.beta[row0 + min(s, s_hi - 1)];
@@ -432,8 +440,9 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
         if (ti < NRT && a.h0)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int row = ti * 16 + 4 * (l >> 4) + e;
-                S[n][e] = a.den ? a.h0[(size_t)bh * D + row] : a.h0[((size_t)bh * D + row) * D + j0 + (l & 15)];
+                const int row = ti * 16 + 4 * (l >> 4) + e, col = j0 + (l & 15);
+                if (row < a.dd && (a.den || col < a.dd))
+                    S[n][e] = a.den ? a.h0[(size_t)bh * a.dd + row] : a.h0[((size_t)bh * a.dd + row) * a.dd + col];
             }
     }
     // the initial state is complete before the frame loop: otherwise the
@@ -516,9 +525,13 @@ __global__ __launch_bounds__(256) void frame_state_kernel(FrameArgs a) {
             if (ti < NRT)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int row = ti * 16 + 4 * (l >> 4) + e;
-                    if (!a.den) a.hT[((size_t)bh * D + row) * D + j0 + (l & 15)] = S[n][e];
-                    else if ((l & 15) == 0) a.hT[(size_t)bh * D + row] = S[n][e];
+                    const int row = ti * 16 + 4 * (l >> 4) + e, col = j0 + (l & 15);
+                    if (row >= a.dd) continue;
+                    if (!a.den) {
+                        if (col < a.dd) a.hT[((size_t)bh * a.dd + row) * a.dd + col] = S[n][e];
+                    } else if ((l & 15) == 0) {
+                        a.hT[(size_t)bh * a.dd + row] = S[n][e];
+                    }
                 }
         }
     }
@@ -551,9 +564,9 @@ __global__ __launch_bounds__(256) void frame_out_kernel(FrameArgs a) {
     for (int idx = tid; idx < TT * SEGS; idx += 256) {
         const int r = idx / SEGS, i0 = (idx % SEGS) * 8;
         U16x8 raw[F32IN ? 2 : 1];
-        if (r < nrows) {
+        if (r < nrows && i0 < a.dd) {
             const unsigned char *src = reinterpret_cast<const unsigned char *>(a.q) +
-                                       ((row0 + r) * D + i0) * (F32IN ? 4 : 2);
+                                       ((row0 + r) * a.dd + i0) * (F32IN ? 4 : 2);
             raw[0] = reinterpret_cast<const U16x8 *>(src)[0];
             if constexpr (F32IN) raw[1] = reinterpret_cast<const U16x8 *>(src)[1];
         } else {
@@ -579,7 +592,7 @@ __global__ __launch_bounds__(256) void frame_out_kernel(FrameArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = ti * 16 + 4 * (l >> 4) + e;
-                if (r < nrows) a.out[(row0 + r) * D + tj * 16 + (l & 15)] = a.scale * acc[e];
+                if (r < nrows && tj * 16 < a.dd) a.out[(row0 + r) * a.dd + tj * 16 + (l & 15)] = a.scale * acc[e];
             }
         }
     }
@@ -622,7 +635,8 @@ __global__ __launch_bounds__(64 * OUT_WAVES) void frame_out_bf16_kernel(FrameArg
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
             uint4 x = uint4{0u, 0u, 0u, 0u};
-            if (t < a.S) x = *reinterpret_cast<const uint4 *>(qin + (row0 + t) * D + kk * 32 + 8 * g);
+            if (t < a.S && kk * 32 + 8 * g < a.dd)
+                x = *reinterpret_cast<const uint4 *>(qin + (row0 + t) * a.dd + kk * 32 + 8 * g);
             bq[u][kk] = __builtin_bit_cast(bf16x8, x);
         }
     }
@@ -656,8 +670,8 @@ __global__ __launch_bounds__(64 * OUT_WAVES) void frame_out_bf16_kernel(FrameArg
                 acc = mfma32(al[kk], bq[u][kk], acc);
             }
             const int t = t0 + u * 16 + c16;
-            if (t < a.S)
-                *reinterpret_cast<float4 *>(a.out + (row0 + t) * D + ti * 16 + 4 * g) =
+            if (t < a.S && ti * 16 < a.dd)
+                *reinterpret_cast<float4 *>(a.out + (row0 + t) * a.dd + ti * 16 + 4 * g) =
                     float4{a.scale * acc[0], a.scale * acc[1], a.scale * acc[2], a.scale * acc[3]};
         }
     }
@@ -690,7 +704,8 @@ __global__ __launch_bounds__(256) void frame_den_kernel(FrameArgs a) {
     for (int e = 0; e < EPP; ++e) z[e] = zs[pc * EPP + e];
     for (int t = tb * 256 + w * TPW + l / L; t < min(a.S, tb * 256 + 256); t += 4 * TPW) {
         float x[EPP];
-        const size_t off = (row0 + t) * D + pc * EPP;
+        const bool pad = pc * EPP >= a.dd;       // loaded from the row start, then zeroed
+        const size_t off = (row0 + t) * a.dd + (pad ? 0 : pc * EPP);
         if constexpr (F32IN) {
             const float4 p0 = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + off);
             x[0] = p0.x; x[1] = p0.y; x[2] = p0.z; x[3] = p0.w;
@@ -702,6 +717,7 @@ __global__ __launch_bounds__(256) void frame_den_kernel(FrameArgs a) {
         float acc = 0.f;
 #pragma unroll
         for (int e = 0; e < EPP; ++e) acc += x[e] * z[e];
+        if (pad) acc = 0.f;
         acc = lane_group_sum<L>(acc);
         if (pc == 0) a.out[row0 + t] = a.scale * acc;
     }
@@ -773,16 +789,26 @@ __global__ __launch_bounds__(256) void state_copy_kernel(const float *h0, float 
     if (i < n) hT[i] = h0 ? h0[i] : 0.f;
 }
 
+// Kernel head width that runs heads of width dd: the next power of two
+// (16 ... 128; the kernels read the features past dd as zero and never store
+// them), or 0 when dd is not a multiple of 16 up to 128.
+int padded_head_width(int dd) {
+    if (dd <= 0 || dd % 16 || dd > 128) return 0;
+    int D = 16;
+    while (D < dd) D *= 2;
+    return D;
+}
+
 // Shared body of the two scan entry points (checks, work space carving, launch).
 int frame_entry(const char *name, const void *q, const void *k, const void *v, const float *beta,
                 const float *log_decay, float scale, const float *h0, float *hT, float *out, int B, int H, int F,
-                int S, int D, int dtype, int reverse, int den, void *workspace, size_t workspace_bytes,
+                int S, int dd, int dtype, int reverse, int den, void *workspace, size_t workspace_bytes,
                 void *stream) {
     GDN_REQUIRE(B >= 0 && H >= 0 && F >= 0, GDN_EINVAL, "%s: negative size (B=%d H=%d F=%d)", name, B, H, F);
     GDN_REQUIRE(S >= 1, GDN_EINVAL, "%s: S=%d (at least one token per frame)", name, S);
     GDN_REQUIRE(dtype == GDN_DTYPE_F32 || dtype == GDN_DTYPE_BF16, GDN_EINVAL, "%s: unknown dtype %d", name, dtype);
-    GDN_REQUIRE(D == 16 || D == 32 || D == 64 || D == 128, GDN_EUNSUPPORTED,
-                "%s: D=%d (supported: 16, 32, 64, 128)", name, D);
+    const int D = padded_head_width(dd);
+    GDN_REQUIRE(D > 0, GDN_EUNSUPPORTED, "%s: D=%d (supported: multiples of 16 up to 128)", name, dd);
     GDN_REQUIRE(isfinite(scale), GDN_EINVAL, "%s: scale is not finite", name);
     GDN_REQUIRE(reverse == 0 || reverse == 1, GDN_EINVAL, "%s: reverse=%d (0 or 1)", name, reverse);
     GDN_REQUIRE(!reverse || (!h0 && !hT), GDN_EUNSUPPORTED,
@@ -810,7 +836,7 @@ int frame_entry(const char *name, const void *q, const void *k, const void *v, c
         if (!hT) return GDN_OK;
         // (a kernel rather than a memset or copy node, so that a captured
         // graph holds kernels only)
-        const size_t n = (size_t)B * H * D * (den ? 1 : D);
+        const size_t n = (size_t)B * H * dd * (den ? 1 : dd);
         hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, h0, hT, n);
         return check_hip(hipGetLastError(), name);
     }
@@ -828,6 +854,7 @@ int frame_entry(const char *name, const void *q, const void *k, const void *v, c
     a.F = F;
     a.S = S;
     a.nsplit = frame_nsplit(B, H, F, S, D, &a.spl);
+    a.dd = dd;
     a.scale = scale;
     a.reverse = reverse;
     a.den = den;
@@ -852,8 +879,9 @@ int frame_entry(const char *name, const void *q, const void *k, const void *v, c
 
 extern "C" size_t gdn_recurrent_fwd_workspace_bytes(int B, int H, int F, int S, int D, int dtype) {
     (void)dtype;
-    if (B < 0 || H < 0 || F < 0 || S <= 0 || D <= 0) return 0;
-    return gdn::frame_workspace(B, H, F, S, D);
+    const int KD = gdn::padded_head_width(D);
+    if (B < 0 || H < 0 || F < 0 || S <= 0 || KD == 0) return 0;
+    return gdn::frame_workspace(B, H, F, S, KD);
 }
 
 extern "C" int gdn_recurrent_fwd(const void *q, const void *k, const void *v, const float *beta,

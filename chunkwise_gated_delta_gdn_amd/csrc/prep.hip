@@ -31,7 +31,7 @@ struct PrepArgs {
     float k_scale, eps;
     void *qo, *ko, *vo;
     float *pre, *post, *infl;
-    int B, N, H;
+    int B, N, H, D;
 };
 
 // 16-byte streaming (nontemporal) store of a q, k or v output piece: the
@@ -76,11 +76,6 @@ __device__ __forceinline__ float wave_sum(float x) {
             __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48)));
 }
 
-template <int D>
-__device__ __forceinline__ float head_sum(float x) {     // over the D/8 lanes of one head
-    return group_sum<D / 8>(x);
-}
-
 // A token's raw q, k or v segment (8 values) as loaded: bf16 in one 16-byte
 // vector, fp32 in two.
 template <bool F32IN>
@@ -123,17 +118,23 @@ __device__ __forceinline__ void load_f8(const float *p, float (&x)[8]) {
 
 // tokens per block of consecutive tokens a workgroup takes
 constexpr int PREP_TPB = 32;
-// NSEG = segments per lane = H*D / 512 (rounded up).  Workgroups take blocks
-// of TPB consecutive tokens with a stride of the grid, wave w tokens w, w+4,
-// ... of each block, so one workgroup writes TPB consecutive entries of
-// every per-head output row (whole 128-byte lines of the per-head scalars).
-// The RMSNorm weights of a wave's channels stay in registers, and its next
+// Lanes per head: LPH = D/8 rounded up to a power of two (the lanes past D/8
+// of each head idle), 64/LPH heads per wave step, NSEG = ceil(H / (64/LPH))
+// heads per lane.  Lane l holds the 8-channel segment at offset 8 (l % LPH)
+// of heads (l / LPH) + i (64/LPH), so its segments share one offset in the
+// head (one RoPE table row piece) and a head's lanes are LPH consecutive
+// lanes (sums over a head by DPP).  Workgroups take blocks of TPB
+// consecutive tokens with a stride of the grid, wave w tokens w, w+4, ...
+// of each block, so one workgroup writes TPB consecutive entries of every
+// per-head output row (whole 128-byte lines of the per-head scalars).  The
+// RMSNorm weights of a wave's channels stay in registers, and its next
 // token's q, k, v (and RoPE table row) are loaded while the current one is
 // processed.
-template <bool F32IN, bool F32OUT, int D, int NSEG>
+template <bool F32IN, bool F32OUT, int LPH, int NSEG>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
-    constexpr int TPB = PREP_TPB, TPW = TPB / 4;
+    constexpr int TPB = PREP_TPB, TPW = TPB / 4, HPS = 64 / LPH;
     static_assert(TPB % 4 == 0, "whole tokens per wave");
+    static_assert(LPH >= 2 && LPH <= 16 && (LPH & (LPH - 1)) == 0, "lanes per head");
     const int l = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const long ntok = (long)a.B * a.N;
@@ -141,23 +142,22 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     int jw = 0;                                  // this wave's token index inside the block
     long tok = blk * TPB + w;
     if (tok >= ntok) return;
-    const int H = a.H, C = H * D;
-    const int nseg = C / 8;
-    constexpr int HALF = D / 2;
+    const int H = a.H, D = a.D, C = H * D;
+    const int HALF = D / 2;
+    const int d0 = 8 * (l % LPH);                // this lane's offset in each of its heads
+    const bool lane_ok = d0 < D;
 
-    // this lane's segments: channel c0 = 8 sg, head sg*8 / D, offset d0 in the
-    // head (a segment never straddles a head or a half of it); inactive
-    // segments (C not a multiple of 512) point at segment 0 and store nothing
-    int hseg[NSEG], dseg[NSEG];
+    // this lane's segments: head hseg[i], channel c0 = hseg[i] * D + d0 (a
+    // segment never straddles a half of a head: D/2 is a multiple of 8);
+    // inactive segments point at channel 0 and store nothing
+    int hseg[NSEG];
     bool act[NSEG];
     float wq[NSEG][8], wk[NSEG][8];
 #pragma unroll
     for (int i = 0; i < NSEG; ++i) {
-        const int sg = l + 64 * i;
-        act[i] = sg < nseg;
-        const int c0 = act[i] ? sg * 8 : 0;
-        hseg[i] = c0 / D;
-        dseg[i] = c0 % D;
+        hseg[i] = i * HPS + l / LPH;
+        act[i] = lane_ok && hseg[i] < H;
+        const int c0 = act[i] ? hseg[i] * D + d0 : 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) wq[i][e] = wk[i][e] = 1.f;
         if (a.qw) load_f8(a.qw + c0, wq[i]);
@@ -165,8 +165,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     }
     // RoPE lanes read 8 cos and 8 sin values of their token; UCPE lanes read
     // the same row at offset 0 and ignore it
-    const int dr = dseg[0] >= HALF ? dseg[0] - HALF : 0;   // same offset in every segment of a lane
-    static_assert(NSEG == 1 || (512 % D) == 0, "a lane's segments share their offset in the head");
+    const int dr = lane_ok && d0 >= HALF ? d0 - HALF : 0;
 
     Raw8<F32IN> rq[NSEG], rk[NSEG], rv[NSEG];
     float cv[8], sv[8];
@@ -174,7 +173,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         const size_t tbase = (size_t)t * 3 * C;
 #pragma unroll
         for (int i = 0; i < NSEG; ++i) {
-            const int c0 = act[i] ? (l + 64 * i) * 8 : 0;
+            const int c0 = act[i] ? hseg[i] * D + d0 : 0;
             rq[i] = load_raw8<F32IN>(a.qkv, tbase + c0);
             rk[i] = load_raw8<F32IN>(a.qkv, tbase + C + c0);
             rv[i] = load_raw8<F32IN>(a.qkv, tbase + 2 * C + c0);
@@ -233,7 +232,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 
 #pragma unroll
         for (int i = 0; i < NSEG; ++i) {
-            const int h = hseg[i], d0 = dseg[i];
+            const int h = hseg[i];
             float kpre = 0.f, kpost = 0.f;
             float qn[8], kn[8], yq[8], yk[8], yv[8];
 #pragma unroll
@@ -277,8 +276,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
                 store8<F32OUT>(a.vo, o, yv);
             }
             // every lane takes part in the head reductions
-            kpre = head_sum<D>(act[i] ? kpre : 0.f);
-            kpost = head_sum<D>(act[i] ? kpost : 0.f);
+            kpre = group_sum<LPH>(act[i] ? kpre : 0.f);
+            kpost = group_sum<LPH>(act[i] ? kpost : 0.f);
             if (act[i] && d0 == 0) {
                 const size_t so = ((size_t)b * H + h) * a.N + n;
                 a.pre[so] = kpre;
@@ -292,20 +291,19 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     }
 }
 
-template <bool F32IN, bool F32OUT, int D>
+template <bool F32IN, bool F32OUT, int LPH>
 hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
     const long ntok = (long)a.B * a.N;
-    const int C = a.H * D;
-    const int nseg = C / 8;
+    const int nseg = (a.H + 64 / LPH - 1) / (64 / LPH);      // heads per lane
     // blocks of PREP_TPB tokens, eight per wave: weights stay resident, loads overlap
     long blocks = (ntok + PREP_TPB - 1) / PREP_TPB;
     if (blocks < 1) blocks = 1;
     if (blocks > 65535) blocks = 65535;
     const dim3 grid((unsigned)blocks);
-    if (nseg <= 64) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 1>), grid, dim3(256), 0, s, a);
-    else if (nseg <= 128) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 2>), grid, dim3(256), 0, s, a);
-    else if (nseg <= 256) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 4>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, D, 8>), grid, dim3(256), 0, s, a);
+    if (nseg <= 1) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, LPH, 1>), grid, dim3(256), 0, s, a);
+    else if (nseg <= 2) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, LPH, 2>), grid, dim3(256), 0, s, a);
+    else if (nseg <= 4) hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, LPH, 4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((prep_kernel<F32IN, F32OUT, LPH, 8>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -322,9 +320,12 @@ extern "C" int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_n
     GDN_REQUIRE(dtype == GDN_DTYPE_F32 || dtype == GDN_DTYPE_BF16, GDN_EINVAL, "%s: unknown dtype %d", name, dtype);
     GDN_REQUIRE(out_dtype == GDN_DTYPE_F32 || out_dtype == GDN_DTYPE_BF16, GDN_EINVAL, "%s: unknown out_dtype %d",
                 name, out_dtype);
-    GDN_REQUIRE(D == 16 || D == 32 || D == 64 || D == 128, GDN_EUNSUPPORTED,
-                "%s: D=%d (supported: 16, 32, 64, 128)", name, D);
-    GDN_REQUIRE((long)H * D <= 4096, GDN_EUNSUPPORTED, "%s: H*D=%d exceeds 4096", name, H * D);
+    GDN_REQUIRE(D > 0 && D % 16 == 0 && D <= 128, GDN_EUNSUPPORTED,
+                "%s: D=%d (supported: multiples of 16 up to 128)", name, D);
+    int lph = 2;                                 // lanes per head: D/8 rounded up to a power of two
+    while (lph < D / 8) lph *= 2;
+    GDN_REQUIRE((long)H * 8 * lph <= 4096, GDN_EUNSUPPORTED,
+                "%s: H=%d heads of D=%d (at most 4096 / %d heads)", name, H, D, 8 * lph);
     GDN_REQUIRE(isfinite(k_scale) && isfinite(norm_eps) && norm_eps >= 0.f, GDN_EINVAL,
                 "%s: k_scale and norm_eps must be finite, norm_eps >= 0", name);
     if ((long)B * N * H == 0) return GDN_OK;
@@ -358,6 +359,7 @@ extern "C" int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_n
     a.B = B;
     a.N = N;
     a.H = H;
+    a.D = D;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     const int sel = (dtype == GDN_DTYPE_F32 ? 2 : 0) + (out_dtype == GDN_DTYPE_F32 ? 1 : 0);
@@ -368,11 +370,11 @@ extern "C" int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_n
         case 2: e = gdn::launch_prep<true, false, DD>(a, s); break;                \
         default: e = gdn::launch_prep<true, true, DD>(a, s); break;                \
     }
-    switch (D) {
-        case 16: GDN_PREP_D(16) break;
-        case 32: GDN_PREP_D(32) break;
-        case 64: GDN_PREP_D(64) break;
-        default: GDN_PREP_D(128) break;
+    switch (lph) {
+        case 2: GDN_PREP_D(2) break;
+        case 4: GDN_PREP_D(4) break;
+        case 8: GDN_PREP_D(8) break;
+        default: GDN_PREP_D(16) break;
     }
 #undef GDN_PREP_D
     return gdn::check_hip(e, name);

@@ -93,9 +93,13 @@ int gdn_abi_version(void);
  *   log_decay (B, T, H)      float32, g_t (gate exp(g_t); normally <= 0)
  *   h0, hT    (B, H, Dk, Dv) float32, nullable
  *   o         (B, T, H, Dv)  out_dtype
- * Supported: Dk, Dv in {16, 32, 64, 128, 256} with Dk <= 256 and Dv a
- * multiple of 16; chunk in {16, 32, 64}; any T >= 0 (a last chunk shorter
- * than `chunk` is handled).  16-byte aligned tensor pointers.
+ * Supported: Dk and Dv multiples of 16 with Dv <= 256 and
+ *   bf16 inputs:  Dk <= 256 at chunk 16 or 32, Dk <= 128 at chunk 64;
+ *   fp32 inputs:  Dk <= 256 at chunk 16 or 32, Dk <= 64 at chunk 64;
+ * any T >= 0 (a last chunk shorter than `chunk` is handled).  A Dk that is
+ * not a power of two runs the next power of two's kernels with the extra
+ * features read as zero (e.g. Dk = 112 as 128).  16-byte aligned tensor
+ * pointers.  Other combinations return GDN_EUNSUPPORTED.
  */
 int gdn_chunk_fwd(const void *q, const void *k, const void *v,
                   const float *beta, const float *log_decay, float scale,
@@ -149,8 +153,9 @@ int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
  *   step_mask  (r, r)          float32 HOST array, row-major M[a][b]
  *   h0, hT     (B, H, r*dk, Dv) float32, nullable
  *   o          (B, T, H, Dv)   out_dtype
- * Supported: r in {1, 2}; dk in {16, 32, 64, 128}; r*dk <= 256; Dv a
- * multiple of 16 up to 256; chunk*r <= 64 with chunk in {16, 32, 64}.
+ * Supported: r = 1 as gdn_chunk_fwd; r = 2 with dk in {16, 32, 64, 128}
+ * and chunk in {16, 32} (bf16 and fp32 inputs); Dv a multiple of 16 up to
+ * 256.  Other combinations return GDN_EUNSUPPORTED.
  */
 int deltaproduct_chunk_fwd(const void *q, const void *k, const void *v,
                            const float *beta, const float *log_decay,
@@ -191,7 +196,9 @@ size_t deltaproduct_chunk_fwd_workspace_bytes(int B, int T, int H, int r, int dk
  *   h0, hT     (B, H, D, D)  float32, nullable
  *   out        (B, H, N, D)  float32
  *   reverse    0 or 1
- * Supported: D in {16, 32, 64, 128}; F >= 1; S >= 1.
+ * Supported: D a multiple of 16 up to 128 (a D that is not a power of two
+ * runs the next power of two's kernels with the extra features read as
+ * zero); F >= 0; S >= 1.
  */
 int gdn_recurrent_fwd(const void *q, const void *k, const void *v,
                       const float *beta, const float *log_decay, float scale,
@@ -221,7 +228,7 @@ size_t gdn_recurrent_fwd_workspace_bytes(int B, int H, int F, int S, int D, int 
  *   log_decay   (B, H, F)     float32, one gate per frame
  *   z0, zT      (B, H, D)     float32, nullable
  *   den         (B, H, N)     float32
- * Supported: D in {16, 32, 64, 128}; F >= 1; S >= 1.  Work space:
+ * Supported: D a multiple of 16 up to 128; F >= 0; S >= 1.  Work space:
  * gdn_recurrent_den_fwd_workspace_bytes.
  */
 int gdn_recurrent_den_fwd(const void *q_den, const void *k_z,
@@ -251,7 +258,8 @@ size_t gdn_recurrent_den_fwd_workspace_bytes(int B, int H, int F, int S, int D, 
  *                    dtype; GDN_DTYPE_F32 keeps the full fp32 result)
  *   k_pre_sq, k_post_sq (B, H, N)    float32
  *   inflation_sq     (B, H, N)       float32, nullable (not stored)
- * Supported: D in {16, 32, 64, 128}; H*D <= 4096.  qkv, the q/k/v outputs,
+ * Supported: D a multiple of 16 up to 128; H * D' <= 4096 with D' the
+ * smallest power of two >= D (e.g. H <= 32 at D = 112).  qkv, the q/k/v outputs,
  * the norm weights and the RoPE tables must be 16-byte aligned (they are
  * read and written as 16-byte vectors); the other float tensors 4-byte.
  */

@@ -58,7 +58,8 @@ def test_chunk_rejects_bad_arguments_without_launching(lib):
     assert _chunk(lib, B=-1) == -1
     assert _chunk(lib) == -1                                     # null pointers
     assert b"null" in lib.gdn_last_error()
-    assert _chunk(lib, Dk=48) == -2                              # unsupported key width
+    assert _chunk(lib, Dk=40) == -2                              # unsupported key width
+    assert _chunk(lib, Dk=272) == -2
     assert _chunk(lib, Dv=24) == -2
     assert _chunk(lib, chunk=128) == -2
     assert _chunk(lib, dtype=7) == -1
@@ -96,7 +97,8 @@ def test_recurrent_rejects_bad_arguments(lib):
     assert call(reverse=1, h0=fake) == -2                        # the reverse scan takes no state
     assert b"reverse" in lib.gdn_last_error()
     assert call(reverse=1, hT=fake) == -2
-    assert call(D=48) == -2
+    assert call(D=40) == -2
+    assert call(D=144) == -2
     assert call(S=0) == -1
     assert call(dtype=5) == -1
     assert call() == -3                                          # no work space
@@ -124,3 +126,80 @@ def test_bwd_rejects_bad_arguments(lib):
     assert call(ws=None, nws=need) == -1                         # null work space
     assert lib.gdn_bwd(None, None, None, None, None, 1.0, None, None, None, None, None, None,
                        None, None, None, 0, 8, 2, 64, 64, 1, None, 0, None) == 0   # B = 0: nothing to do
+
+
+# ---------------------------------------------------------------------------
+# Every combination include/gdn.h declares supported has a kernel, and the
+# rest are refused: probed without launching (fake, aligned pointers and no
+# work space: a supported shape stops at the work-space check, -3; an
+# unsupported one at the shape check, -2).
+# ---------------------------------------------------------------------------
+
+def _chunk_declared(dtype, Dk, chunk):
+    if Dk % 16 or not 16 <= Dk <= 256:
+        return False
+    if chunk in (16, 32):
+        return True
+    return Dk <= (128 if dtype == 1 else 64)
+
+
+@pytest.mark.parametrize("dtype", [0, 1], ids=["f32", "bf16"])
+def test_chunk_declared_combinations_have_kernels(lib, dtype):
+    fake = ctypes.c_void_p(4096)
+    for chunk in (16, 32, 64):
+        for Dk in range(16, 288, 16):
+            for Dv in (16, 112, 256):
+                rc = lib.gdn_chunk_fwd(fake, fake, fake, fake, fake, 1.0, None, None, fake, 1, 8, 1, Dk, Dv,
+                                       chunk, dtype, 0, None, 0, None)
+                want = -3 if _chunk_declared(dtype, Dk, chunk) else -2
+                assert rc == want, (dtype, Dk, Dv, chunk, rc, lib.gdn_last_error())
+                need = lib.gdn_chunk_fwd_workspace_bytes(1, 8, 1, Dk, Dv, chunk, dtype)
+                assert (need > 0) == (want == -3)
+        assert lib.gdn_chunk_fwd(fake, fake, fake, fake, fake, 1.0, None, None, fake, 1, 8, 1, 64, 272, chunk,
+                                 dtype, 0, None, 0, None) == -2               # Dv past 256
+
+
+@pytest.mark.parametrize("dtype", [0, 1], ids=["f32", "bf16"])
+def test_deltaproduct_declared_combinations_have_kernels(lib, dtype):
+    fake = ctypes.c_void_p(4096)
+    mask = (ctypes.c_float * 4)(1, 0, 1, 1)
+    for dk in (16, 32, 48, 64, 128, 256):
+        for chunk in (16, 32, 64):
+            rc = lib.deltaproduct_chunk_fwd(fake, fake, fake, fake, fake, mask, 2, 1.0, None, None, fake,
+                                            1, 8, 1, dk, 64, chunk, dtype, 0, None, 0, None)
+            want = -3 if dk in (16, 32, 64, 128) and chunk in (16, 32) else -2
+            assert rc == want, (dtype, dk, chunk, rc, lib.gdn_last_error())
+    one = (ctypes.c_float * 1)(1.0)
+    for dk in (16, 48, 112, 256):                                      # r = 1: as gdn_chunk_fwd
+        rc = lib.deltaproduct_chunk_fwd(fake, fake, fake, fake, fake, one, 1, 1.0, None, None, fake,
+                                        1, 8, 1, dk, 64, 32, dtype, 0, None, 0, None)
+        assert rc == -3, (dk, rc)
+
+
+@pytest.mark.parametrize("den", [0, 1], ids=["scan", "normaliser"])
+def test_recurrent_declared_head_widths_have_kernels(lib, den):
+    fake = ctypes.c_void_p(4096)
+    for dtype in (0, 1):
+        for D in range(16, 160, 16):
+            if den:
+                rc = lib.gdn_recurrent_den_fwd(fake, fake, fake, fake, 1.0, None, None, fake, 1, 1, 2, 4, D,
+                                               dtype, 0, None, 0, None)
+            else:
+                rc = lib.gdn_recurrent_fwd(fake, fake, fake, fake, fake, 1.0, None, None, fake, 1, 1, 2, 4, D,
+                                           dtype, 0, None, 0, None)
+            assert rc == (-3 if D <= 128 else -2), (dtype, D, rc)
+            assert (lib.gdn_recurrent_fwd_workspace_bytes(1, 1, 2, 4, D, dtype) > 0) == (D <= 128)
+
+
+def test_prep_declared_head_widths(lib):
+    fake = ctypes.c_void_p(4096)
+
+    def call(D, H=2, eps=-1.0, dtype=1):
+        # a negative eps is refused after the shape checks: -1 for a declared shape
+        return lib.gdn_prep(fake, None, None, fake, fake, fake, fake, 1.0, eps, fake, fake, fake, fake, fake,
+                            None, 1, 4, H, D, dtype, dtype, None)
+    for D in range(16, 160, 16):
+        assert call(D) == (-1 if D <= 128 else -2), D
+    assert call(40) == -2
+    assert call(112, H=32) == -1 and call(112, H=33) == -2             # H * 128 <= 4096
+    assert call(64, H=64) == -1 and call(64, H=65) == -2

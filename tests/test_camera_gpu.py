@@ -66,6 +66,12 @@ def _check_prep(got, ref, dtype, out_bf16, what):
     (1, 2, 7, 2, 16, "bf16"),
     (2, 3, 40, 16, 64, "bf16"),
     (1, 2, 30, 32, 128, "bf16"),
+    # head widths that are multiples of 16 but not powers of two
+    (1, 2, 9, 3, 48, "f32"),
+    (1, 2, 20, 16, 112, "bf16"),
+    (2, 1, 17, 5, 80, "bf16"),
+    (1, 3, 11, 32, 112, "bf16"),
+    (1, 2, 13, 7, 96, "f32"),
 ], ids=lambda c: "B{}F{}S{}H{}D{}{}".format(*c))
 def test_prep_small(gdn, case):
     import torch
@@ -139,6 +145,11 @@ def _scan_inputs(B, H, F, S, D, seed, dtype, h0_std=0.0):
     (1, 2, 3, 5, 16, "bf16", 0.3),
     (2, 4, 6, 100, 64, "bf16", 0.1),
     (1, 2, 3, 257, 128, "bf16", 0.1),
+    (1, 2, 3, 40, 112, "f32", 0.1),
+    (1, 3, 4, 70, 48, "f32", 0.2),
+    (2, 2, 3, 100, 112, "bf16", 0.1),
+    (1, 2, 5, 33, 80, "bf16", 0.2),
+    (1, 2, 3, 130, 96, "bf16", 0.1),
 ], ids=lambda c: "B{}H{}F{}S{}D{}{}h{}".format(*c))
 def test_scan_small(gdn, case):
     B, H, F, S, D, dtype, h0s = case
@@ -211,6 +222,29 @@ def test_camera_pipeline_end_to_end(gdn):
     assert max(pf) <= TOL["bf16"] and eh <= TOL["bf16"]
     assert max(pr_) <= TOL["bf16"] and np.all(to_np(out_r)[:, :, (F - 1) * S:] == 0.0)
     assert max(pd) <= TOL["bf16"] and ez <= TOL["bf16"]
+
+
+def test_camera_pipeline_head_dim_112(gdn):
+    """GPU prep (bf16 output) feeding the GPU scan at D = 112: B=1, 4 frames of
+    200 tokens, H=8, C = 896; against the oracle's prep rounded to bf16 feeding
+    the oracle's scan."""
+    import torch
+    _say("camera pipeline at D=112: GPU prep -> GPU scan")
+    d = synth.camera_inputs(1, 4, 200, 8, 112, seed=20267, dtype="bf16")
+    pr = _prep_ref(d)
+    t = {n: to_dev(d[n], "f32") for n in ("q_norm_w", "k_norm_w", "proj_q", "proj_kv", "rope_cos", "rope_sin",
+                                           "beta", "g")}
+    gp = gdn.gdn_prep(to_dev(d["qkv"], "bf16"), t["q_norm_w"], t["k_norm_w"], t["proj_q"], t["proj_kv"],
+                      t["rope_cos"], t["rope_sin"], d["k_scale"], d["eps"])
+    torch.cuda.synchronize()
+    _check_prep({n: to_np(x) for n, x in gp.items()}, pr, "bf16", True, "D=112 prep")
+    q, k, v = (synth.round_bf16(pr[n]) for n in ("q", "k", "v"))
+    out, hT = gdn.gdn_recurrent_fwd(gp["q"], gp["k"], gp["v"], t["beta"], t["g"], 1.0)
+    torch.cuda.synchronize()
+    oref, href = oracle.frame_scan(q, k, v, d["beta"], d["g"], d["F"], 1.0)
+    eo, eh = max_rel_err(to_np(out), oref), max_rel_err(to_np(hT), href)
+    _say(f"  D=112 scan on the GPU prep: out={eo:.2e} hT={eh:.2e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
 
 
 def test_scan_one_token_per_frame_matches_chunk_path(gdn):
@@ -286,6 +320,8 @@ def _scan_rev_gpu(gdn, q, k, v, beta, g, dtype, scale=1.0):
     (1, 2, 3, 5, 16, "bf16"),
     (2, 4, 6, 100, 64, "bf16"),
     (1, 2, 3, 257, 128, "bf16"),
+    (1, 2, 4, 60, 112, "bf16"),
+    (1, 3, 3, 25, 48, "f32"),
 ], ids=lambda c: "B{}H{}F{}S{}D{}{}".format(*c))
 def test_scan_reverse_small(gdn, case):
     B, H, F, S, D, dtype = case
@@ -348,6 +384,9 @@ def _den_gpu(gdn, q, k, beta, g, dtype, scale=1.0, z0=None, reverse=False):
     (1, 3, 5, 70, 64, "f32", False, True),
     (2, 4, 6, 100, 64, "bf16", False, True),
     (1, 2, 3, 257, 128, "bf16", False, True),
+    (1, 2, 4, 90, 112, "bf16", True, False),
+    (1, 2, 3, 50, 80, "f32", True, False),
+    (1, 2, 4, 90, 112, "bf16", False, True),
 ], ids=lambda c: "B{}H{}F{}S{}D{}{}z{}r{}".format(*c))
 def test_den_small(gdn, case):
     B, H, F, S, D, dtype, with_z0, rev = case

@@ -63,6 +63,14 @@ SMALL = [
     (1, 129, 2, 128, 256, 32, "bf16", 0.05),
     (1, 95, 2, 256, 64, 32, "bf16", 0.05),
     (1, 33, 1, 256, 128, 16, "bf16", 0.05),
+    # key and value widths that are multiples of 16 but not powers of two
+    # (run on the next power of two's kernels, the extra features zero)
+    (1, 150, 2, 112, 112, 64, "bf16", 0.1),
+    (2, 77, 2, 48, 80, 32, "bf16", 0.2),
+    (1, 100, 2, 176, 48, 32, "bf16", 0.05),
+    (1, 90, 2, 80, 112, 16, "f32", 0.2),
+    (1, 70, 2, 112, 32, 32, "f32", 0.1),
+    (1, 40, 1, 240, 16, 16, "f32", 0.05),
 ]
 
 
@@ -127,6 +135,17 @@ def test_gdn_chunk_long_workload(gdn):
     _check(o, hT, oref, href, "bf16", "gdn_long all heads")
     per_head = [max_rel_err(o[:, :, h], oref[:, :, h]) for h in range(o.shape[2])]
     _say("  per head: " + " ".join(f"{e:.1e}" for e in per_head))
+
+
+def test_gdn_chunk_head_dim_112(gdn):
+    """D = 112 (the width of the pages' reference model) at a workload-like
+    size: B=1 H=8 T=2048 Dk=Dv=112 chunk 64 bf16, h0 ~ N(0, 0.02^2), every
+    output element."""
+    _say("gdn_chunk_fwd D=112 B=1 H=8 T=2048 chunk 64, full comparison")
+    d = synth.gdn_inputs(1, 2048, 8, 112, 112, seed=20266, dtype="bf16", h0_std=0.02)
+    o, hT = _run_gdn(gdn, d, "bf16", 64)
+    oref, href = oracle.gdn_recurrent(d["q"], d["k"], d["v"], d["beta"], d["g"], 1.0, d["h0"])
+    _check(o, hT, oref, href, "bf16", "D=112")
 
 
 def test_gdn_chunk_split_resume_on_gpu(gdn):
