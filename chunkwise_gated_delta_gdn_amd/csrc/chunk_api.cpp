@@ -98,7 +98,7 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
                 "%s: no kernel for dtype=%s r=%d key width=%d chunk=%d", name,
                 dtype == GDN_DTYPE_F32 ? "f32" : "bf16", r, r * dk, chunk);
     if ((size_t)B * H == 0) return GDN_OK;
-    const size_t need = impl.workspace(B, T, H);
+    const size_t need = impl.workspace(B, T, H, Dv);
     if (noalloc) {
         GDN_REQUIRE(need <= GDN_NOALLOC_SCRATCH_BYTES, GDN_EWORKSPACE,
                     "%s: this shape needs %zu bytes of scratch, the no-allocation entry point holds at most "
@@ -160,12 +160,11 @@ extern "C" int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v
 }
 
 extern "C" size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, int dtype) {
-    (void)Dv;
     gdn::ChunkImpl impl;
-    if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dk % 16 || Dk > 256 ||
+    if (B < 0 || T < 0 || H < 0 || Dv <= 0 || Dk <= 0 || Dk % 16 || Dk > 256 ||
         !find_impl(dtype, 1, padded_key_width(1, Dk), chunk, &impl))
         return 0;
-    return impl.workspace(B, T, H);
+    return impl.workspace(B, T, H, Dv);
 }
 
 extern "C" int deltaproduct_chunk_fwd(const void *q, const void *k, const void *v, const float *beta,
@@ -179,10 +178,9 @@ extern "C" int deltaproduct_chunk_fwd(const void *q, const void *k, const void *
 
 extern "C" size_t deltaproduct_chunk_fwd_workspace_bytes(int B, int T, int H, int r, int dk, int Dv,
                                                          int chunk, int dtype) {
-    (void)Dv;
     gdn::ChunkImpl impl;
-    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dk % 16 || r * dk > 256 ||
+    if (B < 0 || T < 0 || H < 0 || Dv <= 0 || dk <= 0 || dk % 16 || r * dk > 256 ||
         !find_impl(dtype, r, padded_key_width(r, dk), chunk, &impl))
         return 0;
-    return impl.workspace(B, T, H);
+    return impl.workspace(B, T, H, Dv);
 }

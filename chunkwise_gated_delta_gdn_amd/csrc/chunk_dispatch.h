@@ -7,6 +7,7 @@
 #include "chunk_chain1.h"
 #include "chunk_kernels.h"
 #include "chunk_prep2.h"
+#include "chunk_seg.h"
 
 namespace gdn {
 
@@ -33,7 +34,79 @@ inline int num_cus() {
     return n;
 }
 
-// Launch both kernels of one instantiation on `stream`.
+// bf16 inputs, one step per token, 64-token chunks and key widths up to 128
+// run the segment pass (chunk_seg.h) after the prep.
+template <bool F32IN, int KD, int C, int R>
+constexpr bool use_seg() {
+    return !F32IN && R == 1 && C == 64 && KD % 32 == 0 && KD <= 128;
+}
+
+// Choice between the two state passes for the segment-pass shapes, and the
+// segment count: a model of a 256-CU device with per-chunk-step times
+// measured on MI355X (B=2 H=16 T=4096 and B=1 H=16 T=65536, Dk = Dv = 128):
+//   chunk_chain1_kernel   one workgroup per (b, h, 16 columns), one per CU,
+//                         1.3 us per chunk step;
+//   segment pass          summaries 3.3 us per chunk step (one workgroup per
+//                         CU), compose 4 us per segment, output 6.7 us per
+//                         chunk step (one workgroup per CU), each workgroup
+//                         covering 128 columns.
+// Returns 0 for chunk_chain1_kernel, else the segment count P (1 = the
+// output pass over all chunks).  A fixed model (not the queried device), so
+// the work space does not depend on the device it is queried on.
+inline int seg_count(int nbh, int NT, int Dv, int KD) {
+    constexpr int SLOTS = 256, MIN_LS = 4;
+    constexpr double T_CHAIN = 1.3, T_SUM = 3.3, T_COMP = 4.0, T_OUT = 6.7;
+    const int ncgv = (Dv + 127) / 128, ncga = (KD + 127) / 128;
+    auto rounds = [&](long wgs) { return (double)((wgs + SLOTS - 1) / SLOTS); };
+    double best = rounds((long)nbh * (Dv / 16)) * NT * T_CHAIN;
+    int bestP = 0;
+    const double t1 = rounds((long)nbh * ncgv) * NT * T_OUT;
+    if (t1 < best) {
+        best = t1;
+        bestP = 1;
+    }
+    for (int P = 3; P <= NT / MIN_LS && P <= 256; ++P) {
+        const int LS = (NT + P - 1) / P, Pe = (NT + LS - 1) / LS;
+        if (Pe < 3) continue;
+        const long sum_wgs = (long)nbh * ncgv + (long)nbh * (Pe - 2) * (ncgv + ncga);
+        const double t = rounds(sum_wgs) * LS * T_SUM + (Pe - 2) * T_COMP + rounds((long)nbh * Pe * ncgv) * LS * T_OUT;
+        if (t < best) {
+            best = t;
+            bestP = Pe;
+        }
+    }
+    return bestP;
+}
+
+template <int KD>
+hipError_t launch_seg(const ChunkArgs &a, char *seg_ws, hipStream_t stream) {
+    const int NT = (a.T + 63) / 64, nbh = a.B * a.H;
+    SegArgs sa;
+    sa.a = a;
+    sa.P = seg_count(nbh, NT, a.Dv, KD);
+    sa.LS = (NT + sa.P - 1) / sa.P;
+    sa.P = (NT + sa.LS - 1) / sa.LS;
+    sa.amat = reinterpret_cast<float *>(seg_ws);
+    sa.bmat = sa.amat + (size_t)nbh * sa.P * KD * KD;
+    const int ncgv = (a.Dv + 127) / 128, ncga = (KD + 127) / 128;
+    if (sa.P > 1) {
+        sa.nseg_units = nbh + nbh * (sa.P - 2);
+        const int grid = (sa.nseg_units + 7) / 8 * 8 * (ncgv + ncga);
+        hipLaunchKernelGGL((chunk_seg_kernel<KD, false>), dim3(grid), dim3(SegShape<KD>::NTHR), 0, stream, sa);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (sa.P > 2) {
+            hipLaunchKernelGGL((seg_compose_kernel<KD>), dim3(nbh * ((a.Dv + 31) / 32)), dim3(256), 0, stream, sa);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    sa.nseg_units = 0;
+    hipLaunchKernelGGL((chunk_seg_kernel<KD, true>), dim3(nbh * sa.P * ncgv), dim3(SegShape<KD>::NTHR), 0, stream, sa);
+    return hipGetLastError();
+}
+
+// Launch the kernels of one instantiation on `stream`.
 template <bool F32IN, int KD, int C, int R>
 hipError_t launch_chunk_fwd(const ChunkArgs &args, hipStream_t stream) {
     ChunkArgs a = args;
@@ -60,6 +133,12 @@ hipError_t launch_chunk_fwd(const ChunkArgs &args, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if constexpr (use_seg<F32IN, KD, C, R>()) {
+        if (NT > 0 && seg_count(nbh, NT, a.Dv, KD) > 0) {
+            char *seg_ws = static_cast<char *>(a.tmat) + chunk_workspace_bytes<F32IN, KD, C, R>(a.B, a.T, a.H);
+            return launch_seg<KD>(a, seg_ws, stream);
+        }
+    }
     const int nvb = a.Dv / 16;
     const int grid = ((nbh + 7) / 8) * 8 * nvb;
     if constexpr (use_chain1<F32IN, KD, C, R>()) {
@@ -70,9 +149,25 @@ hipError_t launch_chunk_fwd(const ChunkArgs &args, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Work space of one instantiation: the prep's, and the segment pass's.
+template <bool F32IN, int KD, int C, int R>
+size_t chunk_fwd_workspace_bytes(int B, int T, int H, int Dv) {
+    size_t n = chunk_workspace_bytes<F32IN, KD, C, R>(B, T, H);
+    if constexpr (use_seg<F32IN, KD, C, R>()) {
+        const int NT = (T + C - 1) / C;
+        int P = NT > 0 ? seg_count(B * H, NT, Dv, KD) : 0;
+        if (P > 0) {
+            const int LS = (NT + P - 1) / P;
+            P = (NT + LS - 1) / LS;
+            n += seg_workspace_bytes<KD>(B, H, Dv, P);
+        }
+    }
+    return n;
+}
+
 struct ChunkImpl {
     hipError_t (*launch)(const ChunkArgs &, hipStream_t);
-    size_t (*workspace)(int B, int T, int H);
+    size_t (*workspace)(int B, int T, int H, int Dv);
 };
 
 // Each returns false when (KD, C) has no instantiation for that input type
@@ -86,6 +181,6 @@ bool find_chunk_f32(int KD, int C, int R, ChunkImpl *out);
 #define GDN_CASE(F32, KD_, C_, R_)                                   \
     if (KD == KD_ && C == C_) {                                      \
         out->launch = launch_chunk_fwd<F32, KD_, C_, R_>;            \
-        out->workspace = chunk_workspace_bytes<F32, KD_, C_, R_>;    \
+        out->workspace = chunk_fwd_workspace_bytes<F32, KD_, C_, R_>; \
         return true;                                                 \
     }

@@ -85,7 +85,11 @@ int gdn_abi_version(void);
  * cumsum of g, the strictly-lower intra-chunk matrix
  * A[t,s] = beta_t (k_t . k_s) exp(G_t - G_s), T = (I + A)^-1 from 16x16
  * diagonal blocks and exact block merges, the WY form, the sequential
- * inter-chunk state pass and the output product.
+ * inter-chunk state pass and the output product.  For long sequences over
+ * few heads (bf16, chunk 64, Dk <= 128) the state pass runs segment-parallel:
+ * per-segment transitions and states from zero, composed, then each segment
+ * from its true start ([cp] module docstring); the work space then also
+ * holds one Dk x (Dk + Dv) fp32 pair per segment.
  *
  *   q, k      (B, T, H, Dk)  dtype
  *   v         (B, T, H, Dv)  dtype
@@ -121,15 +125,15 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int ch
  * held until the process ends.  This entry point calls no hipMalloc,
  * hipFree or allocating library routine.
  * Limit: shapes whose gdn_chunk_fwd_workspace_bytes exceeds
- * GDN_NOALLOC_SCRATCH_BYTES are rejected with GDN_EWORKSPACE (at Dk = 128,
- * chunk 64, bf16: about 19.2 KB per chunk of one (b, h), i.e. B*H*ceil(T/64)
- * up to 3490 chunks, e.g. B*H = 32 with T <= 6976).
+ * GDN_NOALLOC_SCRATCH_BYTES are rejected with GDN_EWORKSPACE (B=2 H=16
+ * T=4096 Dk=Dv=128 chunk 64 bf16 needs 73 MB and runs; B=1 H=16 T=65536
+ * needs over 300 MB and is rejected).
  * Every call on one device shares that device's array: calls that overlap
  * on one device (on different streams, or from several threads without
  * ordering) race and give wrong results; serialise them.  Nothing in the
  * array needs to start at zero (each call writes every entry it reads).
  */
-#define GDN_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+#define GDN_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
 int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
                           const float *beta, const float *log_decay, float scale,
                           const float *h0, float *hT, void *o,

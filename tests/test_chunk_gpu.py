@@ -84,6 +84,32 @@ def test_gdn_chunk_small(gdn, case):
     _check(o, hT, oref, href, dtype, str(case))
 
 
+# Long sequences over few heads, where the dispatch takes the segment-parallel
+# state pass (segment summaries, their composition, then the output pass per
+# segment; 24-29 segments here): key widths 32...128 (112 padded), value
+# widths 64...256 (two 128-column groups at 256), ragged last chunk and
+# segment, nonzero initial state.
+SEG = [
+    # (B, T, H, Dk, Dv, h0_std)
+    (1, 16384, 2, 128, 128, 0.02),
+    (1, 16384, 1, 112, 256, 0.05),
+    (1, 12288, 2, 64, 80, 0.1),
+    (1, 16384, 1, 32, 64, 0.1),
+    (1, 20000, 1, 128, 112, 0.05),
+    (1, 16384, 1, 48, 128, 0.1),
+]
+
+
+@pytest.mark.parametrize("case", SEG, ids=lambda c: "B{}T{}H{}K{}V{}h{}".format(*c))
+def test_gdn_chunk_segment_pass(gdn, case):
+    B, T, H, Dk, Dv, h0s = case
+    _say(f"gdn_chunk_fwd segment pass {case}")
+    d = synth.gdn_inputs(B, T, H, Dk, Dv, seed=3000 + T + Dk + Dv, dtype="bf16", h0_std=h0s)
+    o, hT = _run_gdn(gdn, d, "bf16", 64)
+    oref, href = oracle.gdn_recurrent(d["q"], d["k"], d["v"], d["beta"], d["g"], 1.0, d["h0"])
+    _check(o, hT, oref, href, "bf16", str(case))
+
+
 def test_gdn_chunk_tiny_workload(gdn):
     """The tiny fp32 workload exactly: B=1 H=2 T=64 D=16 chunk 16."""
     _say("gdn_chunk_fwd gdn_tiny workload")

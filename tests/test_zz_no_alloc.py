@@ -14,7 +14,7 @@ from tests._helpers import TOL, max_rel_err, to_dev, to_np
 pytestmark = pytest.mark.gpu
 
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
-NOALLOC_MAX = 64 * 1024 * 1024
+NOALLOC_MAX = 128 * 1024 * 1024
 
 
 @pytest.fixture(scope="module")
