@@ -314,7 +314,8 @@ def main():
     elif args.workload == "deltaproduct":
         metric = "tokens/sec of chunkwise gated DeltaProduct fwd (B*T/s)"
         desc = "deltaproduct: B=2 H=8 T=2048 K=2x128 Dv=128 chunk=32 r=2, bf16 q/k/v and output, lower-triangular step mask"
-        kernel = "deltaproduct_chunk_fwd = chunk_solve_kernel + chunk_chain_kernel <bf16, KD=256, C=32, R=2>"
+        kernel = ("deltaproduct_chunk_fwd = chunk_prep2_kernel (both sub-keys) + chunk_chain1_kernel<128, 64, 1> "
+                  "+ chunk_chain1_kernel<128, 64, 2> (two passes, lower unitriangular step mask)")
         traffic = None
     else:
         rev = args.workload == "camera_reverse"

@@ -48,6 +48,16 @@ int padded_key_width(int r, int dk) {
     return kd;
 }
 
+// Work space of a DeltaProduct call: enough for the general path and for
+// the two-pass one (the query does not see the step mask).
+size_t dp2_workspace(int dk, int B, int T, int H, int Dv, const gdn::ChunkImpl &general) {
+    gdn::ChunkImpl dp2;
+    const size_t g = general.workspace(B, T, H, Dv);
+    if (!gdn::find_dp2(dk, &dp2)) return g;
+    const size_t f = dp2.workspace(B, T, H, Dv);
+    return f > g ? f : g;
+}
+
 bool find_impl(int dtype, int r, int KD, int chunk, gdn::ChunkImpl *impl) {
     if (dtype == GDN_DTYPE_F32) return gdn::find_chunk_f32(KD, chunk, r, impl);
     if (r == 1) return gdn::find_chunk_bf16_r1(KD, chunk, impl);
@@ -97,8 +107,13 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
     GDN_REQUIRE(find_impl(dtype, r, KD, chunk, &impl), GDN_EUNSUPPORTED,
                 "%s: no kernel for dtype=%s r=%d key width=%d chunk=%d", name,
                 dtype == GDN_DTYPE_F32 ? "f32" : "bf16", r, r * dk, chunk);
+    // two steps with a lower unitriangular mask (bf16): two passes of the
+    // single-chain kernels (the work-space query covers both paths)
+    gdn::ChunkImpl dp2;
+    const bool use_dp2 = r == 2 && T > 0 && dtype == GDN_DTYPE_BF16 && step_mask[0] == 1.f &&
+                         step_mask[1] == 0.f && step_mask[3] == 1.f && gdn::find_dp2(dk, &dp2);
     if ((size_t)B * H == 0) return GDN_OK;
-    const size_t need = impl.workspace(B, T, H, Dv);
+    const size_t need = use_dp2 ? dp2_workspace(dk, B, T, H, Dv, impl) : impl.workspace(B, T, H, Dv);
     if (noalloc) {
         GDN_REQUIRE(need <= GDN_NOALLOC_SCRATCH_BYTES, GDN_EWORKSPACE,
                     "%s: this shape needs %zu bytes of scratch, the no-allocation entry point holds at most "
@@ -130,6 +145,19 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
     a.H = H;
     a.Dv = Dv;
     a.kw = r * dk;
+    a.kst = r * dk;
+    a.koff = 0;
+    a.bst = 1;
+    a.boff = 0;
+    a.hrows = r * dk;
+    a.hoff = 0;
+    a.atil = nullptr;
+    a.vout = nullptr;
+    a.vin = nullptr;
+    a.oprev = nullptr;
+    a.mcoef = r == 2 ? step_mask[2] : 0.f;
+    a.nsub = 1;
+    a.subws = 0;
     a.out_bf16 = out_dtype == GDN_DTYPE_BF16;
     a.scale = scale;
     for (int i = 0; i < 4; ++i) a.mask[i] = 0.f;
@@ -138,7 +166,7 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
     } else {
         for (int i = 0; i < r * r; ++i) a.mask[i] = step_mask[i];
     }
-    return gdn::check_hip(impl.launch(a, reinterpret_cast<hipStream_t>(stream)), name);
+    return gdn::check_hip((use_dp2 ? dp2 : impl).launch(a, reinterpret_cast<hipStream_t>(stream)), name);
 }
 
 }  // namespace
@@ -182,5 +210,6 @@ extern "C" size_t deltaproduct_chunk_fwd_workspace_bytes(int B, int T, int H, in
     if (B < 0 || T < 0 || H < 0 || Dv <= 0 || dk <= 0 || dk % 16 || r * dk > 256 ||
         !find_impl(dtype, r, padded_key_width(r, dk), chunk, &impl))
         return 0;
+    if (r == 2 && dtype == GDN_DTYPE_BF16) return dp2_workspace(dk, B, T, H, Dv, impl);
     return impl.workspace(B, T, H, Dv);
 }

@@ -36,6 +36,18 @@
 // One workgroup barrier per chunk.  Iteration c: the chain processes chunk c
 // and publishes its start state and V_new; the other waves write the output
 // of chunk c-1 and stage chunk c+2.
+//
+// DPM selects a pass of the gated DeltaProduct with a lower unitriangular
+// 2 x 2 step mask [[1, 0], [m, 1]] (two sub-keys): the first row block of the
+// state is then a gated delta rule on (k_0, v, beta_0) and the second one on
+// (k_1, v', beta_1) with v'_t = v_t - m p_t, p_t the first block's prediction
+// at token t (the product of the page's erase key with the gated state).
+//   DPM = 1: the pass on sub-key 0; also forms the per-token errors
+//            e = R - A~ V_new (A~ the decay-masked gram without beta, from the
+//            prep; V_new = beta e) and writes v' = (1 - m) v + m e (fp32);
+//            its output goes to an fp32 buffer;
+//   DPM = 2: the pass on sub-key 1 with v' (fp32, read by the chain wave) as
+//            the values; its output adds the first pass's.
 #pragma once
 
 #include <type_traits>
@@ -58,6 +70,7 @@ struct Chain1Shape {
     static constexpr int NW = NTT == 4 ? 6 : 1 + NTT;
     static constexpr int NTHR = 64 * NW;
     static constexpr int NLW = 2;             // staging ("loader") waves
+    static constexpr int NLOW = NTT * (NTT + 1) / 2;
     static constexpr int NKS = KD / 32;       // 32-wide steps over the key dim
     static constexpr int NST = KD / 16;       // state row tiles
     static constexpr int NCS = C / 32;        // 32-wide steps over the tokens
@@ -89,9 +102,13 @@ struct Chain1Shape {
     static constexpr int OFF_GATE = OFF_BV + 3 * SZ_BV;
     static constexpr int OFF_ST = OFF_GATE + 3 * SZ_GATE;
     static constexpr int OFF_VN = OFF_ST + 2 * SZ_ST;
-    static constexpr int BYTES = OFF_VN + 2 * SZ_VN;
+    static constexpr int SZ_AT = NLOW * 1024;                     // A~ fragments (DeltaProduct first pass)
+    static constexpr int OFF_AT = OFF_VN + 2 * SZ_VN;
+    static constexpr int BYTES = OFF_AT + 3 * SZ_AT;
+    static constexpr int BYTES_PLAIN = OFF_AT;
     static_assert(C % 32 == 0 && C <= 64 && KD % 32 == 0, "32-wide MFMA steps");
-    static_assert(BYTES <= 160 * 1024, "LDS budget of one workgroup exceeded");
+    static_assert(BYTES <= 160 * 1024 || KD > 128, "LDS budget of one workgroup exceeded");
+    static_assert(BYTES_PLAIN <= 160 * 1024, "LDS budget of one workgroup exceeded");
     static_assert(SZ_KS % 1024 == 0 && SZ_TB % 1024 == 0 && SZ_BV % 1024 == 0,
                   "staging buffers are whole 1 KiB wave loads");
 };
@@ -134,14 +151,15 @@ __device__ __forceinline__ void frag_split(const floatx4 &t0, const floatx4 &t1,
 }
 
 
-template <int KD, int C>
+template <int KD, int C, int DPM = 0>
 __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kernel(ChunkArgs args) {
     using S = Chain1Shape<KD, C>;
+    static_assert(DPM == 0 || C == 64, "DeltaProduct passes run 64-token chunks");
     constexpr int BV = S::BV, NTT = S::NTT, NKS = S::NKS, NST = S::NST, NCS = S::NCS, NKC = S::NKC;
     constexpr int LDK = S::LDK, LDT = S::LDT, LDV = S::LDV, LDSF = S::LDSF, LDVF = S::LDVF;
     constexpr int TSW = S::TSW;
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[S::BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[DPM == 1 ? S::BYTES : S::BYTES_PLAIN];
 
     const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -167,6 +185,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
     auto gate = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_GATE + p * S::SZ_GATE); };
     auto St = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_ST + p * S::SZ_ST); };
     auto Vn = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_VN + p * S::SZ_VN); };
+    auto At = [&](int p) { return reinterpret_cast<const uint4 *>(smem + S::OFF_AT + p * S::SZ_AT); };
 
     if (w == 0) {
         // =================================================================
@@ -190,12 +209,26 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
         for (int ti = 0; ti < NST; ++ti) {
             Sreg[ti] = zero4();
             if (args.h0) {
-                const float *hp = args.h0 + ((size_t)bh * args.kw) * Dv + v0 + c16;
+                const float *hp = args.h0 + ((size_t)bh * args.hrows + args.hoff) * Dv + v0 + c16;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     if (feat(ti, e) < args.kw) Sreg[ti][e] = hp[(size_t)feat(ti, e) * Dv];
             }
         }
+        // DPM 2: this lane's values v' (rows tt*16 + 4g + e, column c16) of
+        // the next chunk, loaded one iteration ahead
+        floatx4 vpre[NTT];
+        auto load_vin = [&](int c) {
+            const float *vp = args.vin + (((size_t)b * T) * H + h) * Dv + v0 + c16;
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = min(c * C + tt * 16 + 4 * g + e, tlast);
+                    vpre[tt][e] = vp[(size_t)t * H * Dv];
+                }
+        };
+        if constexpr (DPM == 2) load_vin(0);
         __syncthreads();
         for (int c = 0, sq = 0; c < NT; ++c, sq = sq == 2 ? 0 : sq + 1) {
             const int p = c & 1;                 // St, Vn; staging buffers: sq = c % 3
@@ -213,8 +246,15 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
                     kf[tt][m] = ld8(ks + r * LDK + (((4 * m + g) ^ kswz<NKC>(r)) << 3));
                 }
             shortx4 vv[NTT];                     // V rows tt*16 + 4g + e, column c16
+            floatx4 vcur[NTT];                   // DPM 2: v' of this chunk
+            if constexpr (DPM == 2) {
 #pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) vv[tt] = ld_tr16(bv + (tt * 16 + 4 * g + (c16 >> 2)) * LDV + 4 * (c16 & 3));
+                for (int tt = 0; tt < NTT; ++tt) vcur[tt] = vpre[tt];
+                if (c + 1 < NT) load_vin(c + 1);
+            } else {
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt) vv[tt] = ld_tr16(bv + (tt * 16 + 4 * g + (c16 >> 2)) * LDV + 4 * (c16 & 3));
+            }
 #pragma unroll
             for (int m = 0; m < NCS; ++m)
 #pragma unroll
@@ -258,14 +298,18 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
             // R = V - e^G Y; V_new = (T diag(beta)) R: its diagonal, beta, in fp32
             // on R, the rest (block lower triangular, entries well below beta)
             // by MFMA on R rounded to bf16
-            floatx4 rr[NTT];
+            floatx4 rr[NTT], vin4[NTT];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
-                const uint2 v2 = __builtin_bit_cast(uint2, vv[tt]);
-                const float vx[4] = {__builtin_bit_cast(float, v2.x << 16), __builtin_bit_cast(float, v2.x & 0xffff0000u),
-                                     __builtin_bit_cast(float, v2.y << 16), __builtin_bit_cast(float, v2.y & 0xffff0000u)};
+                if constexpr (DPM == 2) {
+                    vin4[tt] = vcur[tt];
+                } else {
+                    const uint2 v2 = __builtin_bit_cast(uint2, vv[tt]);
+                    vin4[tt] = floatx4{__builtin_bit_cast(float, v2.x << 16), __builtin_bit_cast(float, v2.x & 0xffff0000u),
+                                       __builtin_bit_cast(float, v2.y << 16), __builtin_bit_cast(float, v2.y & 0xffff0000u)};
+                }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) rr[tt][e] = vx[e] - eg[tt][e] * y[tt][e];
+                for (int e = 0; e < 4; ++e) rr[tt][e] = vin4[tt][e] - eg[tt][e] * y[tt][e];
             }
             bf16x8 rh[NCS];
 #pragma unroll
@@ -306,17 +350,50 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
             // S_start of chunk c goes out while the state MFMAs run (its LDS
             // writes then do not queue ahead of this chunk's operand reads)
             publish_state(p);
+            if constexpr (DPM == 1) {
+                // (issued after the state update's MFMAs: off the chain's path)
+                // per-token errors e = R - A~ V_new and v' = (1 - m) v + m e;
+                // A~ tile (tt, tj) is the A operand (rows t), V_new tile tj the B
+                // operand (its accumulator layout), both as hi + lo
+                shortx4 nh[NTT], nl[NTT];
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt) split4(vn[tt], nh[tt], nl[tt]);
+                const uint4 *at = At(sq);
+                const float mc = args.mcoef;
+                float *vo = args.vout + (((size_t)b * T) * H + h) * Dv + v0 + c16;
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt) {
+                    floatx4 acc = zero4();
+#pragma unroll
+                    for (int tj = 0; tj <= tt; ++tj) {
+                        const u32x4 af = __builtin_bit_cast(u32x4, at[(tt * (tt + 1) / 2 + tj) * 64 + l]);
+                        const shortx4 ah = __builtin_bit_cast(shortx4, uint2{af[0], af[1]});
+                        const shortx4 al = __builtin_bit_cast(shortx4, uint2{af[2], af[3]});
+                        acc = mfma16(ah, nh[tj], acc);
+                        acc = mfma16(ah, nl[tj], acc);
+                        acc = mfma16(al, nh[tj], acc);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = c * C + tt * 16 + 4 * g + e;
+                        const float ee = rr[tt][e] - acc[e];
+                        if (t < T) vo[(size_t)t * H * Dv] = (1.f - mc) * vin4[tt][e] + mc * ee;
+                    }
+                }
+            }
 #pragma unroll
             for (int ti = 0; ti < NST; ++ti)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Sreg[ti][e] = gL * Sreg[ti][e] + ds[ti][e];
-            __syncthreads();
+            // LDS operations only: the chain wave's own global loads (v' of the
+            // next chunk) and stores (v') stay in flight across the barrier
+            lds_barrier();
         }
         __syncthreads();                       // matches the out waves' drain step
         if (args.hT) {
 #pragma unroll
             for (int ti = 0; ti < NST; ++ti) {
-                float *hp = args.hT + ((size_t)bh * args.kw) * Dv + v0 + c16;
+                float *hp = args.hT + ((size_t)bh * args.hrows + args.hoff) * Dv + v0 + c16;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     if (feat(ti, e) < args.kw) hp[(size_t)feat(ti, e) * Dv] = Sreg[ti][e];
@@ -340,13 +417,14 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
     constexpr int NLW = S::NLW;
     constexpr int NLOW = NTT * (NTT + 1) / 2;
     constexpr int NGV = S::NGATE / 4;           // 16-byte vectors of a gate table
-    constexpr int NDK = S::SZ_KS / 1024, NDT = S::SZ_TB / 1024, NDV = S::SZ_BV / 1024;
-    constexpr int NDMA = NDK + NDT + NDV + 1;
+    constexpr int NDK = S::SZ_KS / 1024, NDT = S::SZ_TB / 1024, NDV = DPM == 2 ? 0 : S::SZ_BV / 1024;
+    constexpr int NDA = DPM == 1 ? S::SZ_AT / 1024 : 0;            // A~ fragments
+    constexpr int NDMA = NDK + NDT + NDV + 1 + NDA;
     static_assert(NGV <= 64 && S::SZ_GATE >= NGV * 16, "gate table: one partial wave load");
-    const int kw = args.kw;                     // key row width in HBM; pieces past it are zero
-    const size_t tokq = (size_t)H * kw, tokv = (size_t)H * Dv;
-    const u16 *kg = reinterpret_cast<const u16 *>(args.k) + ((size_t)b * T * H + h) * kw;
-    const u16 *qg = reinterpret_cast<const u16 *>(args.q) + ((size_t)b * T * H + h) * kw;
+    const int kw = args.kw;                     // key width; pieces past it are zero
+    const size_t tokq = (size_t)H * args.kst, tokv = (size_t)H * Dv;
+    const u16 *kg = reinterpret_cast<const u16 *>(args.k) + ((size_t)b * T * H + h) * args.kst + args.koff;
+    const u16 *qg = reinterpret_cast<const u16 *>(args.q) + ((size_t)b * T * H + h) * args.kst + args.koff;
     const u16 *vg = reinterpret_cast<const u16 *>(args.v) + ((size_t)b * T * H + h) * Dv + v0;
     const u16 *tg = reinterpret_cast<const u16 *>(args.tmat) + (size_t)bh * NT * C * C;
     const float *gtg = reinterpret_cast<const float *>(args.gtab) + (size_t)bh * NT * S::NGATE;
@@ -376,8 +454,12 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
                     const int kk = k - NDK - NDT, pos = kk * 64 + l;
                     const int t = min(c * C + pos / 2, tlast);
                     dma16(vg + (size_t)t * tokv + (pos & 1) * 8, BVs(p) + kk * 512);
-                } else {                        // gate table
+                } else if (k == NDK + NDT + NDV) {  // gate table
                     if (l < NGV) dma16(gtg + (size_t)c * S::NGATE + l * 4, gate(p));
+                } else {                            // A~ fragments (DeltaProduct first pass)
+                    const int kk = k - NDK - NDT - NDV - 1;
+                    dma16(reinterpret_cast<const uint4 *>(args.atil) + ((size_t)bh * NT + c) * NLOW * 64 + kk * 64 + l,
+                          smem + S::OFF_AT + p * S::SZ_AT + kk * 1024);
                 }
             }
         };
@@ -390,22 +472,31 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
         u32x4 pf[NTW][NTT];                     // P fragments of each tile: {hi01, hi23, lo01, lo23}
         float egt[NTW];                         // e^{G_t} of this lane's tokens
         floatx4 ov[NTW];                        // outputs of the previous chunk
+        floatx4 op[NTW];                        // DPM 2: the first pass's output of those tokens
         // operands of chunk c's output, used one iteration later
         auto load_qp = [&](int c) {
 #pragma unroll
             for (int i = 0; i < NTW; ++i) {
                 const int t = min(c * C + tw(i) * 16 + c16, tlast);   // rows past T are never stored
+                if (kw == KD) {                 // (wave-uniform) no padded key features
 #pragma unroll
-                for (int m = 0; m < NKS; ++m) {
-                    const bool pad = m * 32 + 8 * g >= kw;   // loaded anyway (counted loads), then zeroed
-                    qf[i][m] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)t * tokq + (pad ? 0 : m * 32 + 8 * g));
-                    if (pad) qf[i][m] = bf16x8{};
+                    for (int m = 0; m < NKS; ++m)
+                        qf[i][m] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)t * tokq + m * 32 + 8 * g);
+                } else {
+#pragma unroll
+                    for (int m = 0; m < NKS; ++m) {
+                        const bool pad = m * 32 + 8 * g >= kw;   // loaded anyway (counted loads), then zeroed
+                        qf[i][m] = *reinterpret_cast<const bf16x8 *>(qg + (size_t)t * tokq + (pad ? 0 : m * 32 + 8 * g));
+                        if (pad) qf[i][m] = bf16x8{};
+                    }
                 }
                 const uint4 *pc = reinterpret_cast<const uint4 *>(args.pfrag) + ((size_t)bh * NT + c) * NLOW * 64 +
                                   (tw(i) * (tw(i) + 1) / 2) * 64 + l;
 #pragma unroll
                 for (int tj = 0; tj <= tw(i); ++tj) pf[i][tj] = __builtin_bit_cast(u32x4, pc[tj * 64]);
                 egt[i] = gate(c % 3)[tw(i) * 16 + c16];
+                if constexpr (DPM == 2)
+                    op[i] = *reinterpret_cast<const floatx4 *>(args.oprev + (((size_t)b * T + t) * H + h) * Dv + v0 + 4 * g);
             }
         };
         // O^T of chunk c: a1 = S_start^T Q^T, a2 = V_new^T P^T (buffers c & 1);
@@ -440,7 +531,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
                     a2 = mfma16(vl4[tj], ph, a2);
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ov[i][e] = sc * (egt[i] * a1[e] + a2[e]);
+                for (int e = 0; e < 4; ++e) ov[i][e] = sc * (egt[i] * a1[e] + a2[e]) + (DPM == 2 ? op[i][e] : 0.f);
             }
         };
         auto store_out = [&](int c) {

@@ -165,6 +165,76 @@ size_t chunk_fwd_workspace_bytes(int B, int T, int H, int Dv) {
     return n;
 }
 
+// Gated DeltaProduct, two sub-keys of width KD, lower unitriangular step
+// mask [[1, 0], [m, 1]], bf16: two passes of the single-chain kernels with
+// 64-token chunks (chunk_chain1.h, DPM), the first on sub-key 0 (also
+// writing v' and its output in fp32), the second on sub-key 1 with v' as
+// the values.  Work space: the prep's (shared by the passes), the A~
+// fragments, v' and the first output.
+template <int KD>
+size_t dp2_workspace_bytes(int B, int T, int H, int Dv) {
+    constexpr int C = 64;
+    const size_t prep = 2 * ((chunk_workspace_bytes<false, KD, C, 1>(B, T, H) + 255) & ~(size_t)255);
+    const size_t at = chunk_pfrag_bytes<false, KD, C, 1>(B, T, H);
+    const size_t vo = ((size_t)B * T * H * Dv * 4 + 255) & ~(size_t)255;
+    return prep + at + 2 * vo;
+}
+
+template <int KD>
+hipError_t launch_dp2(const ChunkArgs &args, hipStream_t stream) {
+    constexpr int C = 64;
+    ChunkArgs a = args;
+    const int NT = (a.T + C - 1) / C, nbh = a.B * a.H;
+    if (nbh == 0 || NT == 0) return launch_chunk_fwd<false, KD, C, 1>(a, stream);   // hT = h0 only
+    char *ws = static_cast<char *>(a.tmat);
+    const size_t subws = (chunk_workspace_bytes<false, KD, C, 1>(a.B, a.T, a.H) + 255) & ~(size_t)255;
+    a.pfrag = ws + chunk_tmat_bytes<false, KD, C, 1>(a.B, a.T, a.H);
+    a.gtab = static_cast<char *>(a.pfrag) + chunk_pfrag_bytes<false, KD, C, 1>(a.B, a.T, a.H);
+    char *at = ws + 2 * subws;
+    const size_t vo = ((size_t)a.B * a.T * a.H * a.Dv * 4 + 255) & ~(size_t)255;
+    float *vprime = reinterpret_cast<float *>(at + chunk_pfrag_bytes<false, KD, C, 1>(a.B, a.T, a.H));
+    float *o0 = reinterpret_cast<float *>(reinterpret_cast<char *>(vprime) + vo);
+    const int nchunks = 2 * nbh * NT, nwg = (nchunks + 3) / 4;     // both sub-keys
+    const int pgrid = nwg < 2 * num_cus() ? nwg : 2 * num_cus();
+    const int cgrid = ((nbh + 7) / 8) * 8 * (a.Dv / 16);
+    const int ktot = 2 * KD;
+    a.kw = KD;
+    a.kst = ktot;
+    a.bst = 2;
+    a.hrows = ktot;
+    // pass 1: sub-key 0
+    ChunkArgs p1 = a;
+    p1.koff = 0;
+    p1.boff = 0;
+    p1.hoff = 0;
+    p1.atil = at;
+    p1.vout = vprime;
+    p1.o = o0;
+    p1.out_bf16 = 0;
+    // the prep of both sub-keys in one launch (sub-key 1's work space subws on)
+    ChunkArgs pp = p1;
+    pp.nsub = 2;
+    pp.subws = subws;
+    hipLaunchKernelGGL((chunk_prep2_kernel<KD, C>), dim3(pgrid), dim3(256), 0, stream, pp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_chain1_kernel<KD, C, 1>), dim3(cgrid), dim3(Chain1Shape<KD, C>::NTHR), 0, stream, p1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // pass 2: sub-key 1, values v', output added
+    ChunkArgs p2 = a;
+    p2.koff = KD;
+    p2.boff = 1;
+    p2.hoff = KD;
+    p2.atil = nullptr;
+    p2.vin = vprime;
+    p2.oprev = o0;
+    p2.tmat = ws + subws;
+    p2.pfrag = static_cast<char *>(a.pfrag) + subws;
+    p2.gtab = static_cast<char *>(a.gtab) + subws;
+    hipLaunchKernelGGL((chunk_chain1_kernel<KD, C, 2>), dim3(cgrid), dim3(Chain1Shape<KD, C>::NTHR), 0, stream, p2);
+    return hipGetLastError();
+}
+
 struct ChunkImpl {
     hipError_t (*launch)(const ChunkArgs &, hipStream_t);
     size_t (*workspace)(int B, int T, int H, int Dv);
@@ -175,6 +245,8 @@ struct ChunkImpl {
 bool find_chunk_bf16_r1(int KD, int C, ChunkImpl *out);
 bool find_chunk_bf16_r2(int KD, int C, ChunkImpl *out);
 bool find_chunk_f32(int KD, int C, int R, ChunkImpl *out);
+// the two-pass DeltaProduct path for sub-keys of width dk (bf16)
+bool find_dp2(int dk, ChunkImpl *out);
 
 }  // namespace gdn
 

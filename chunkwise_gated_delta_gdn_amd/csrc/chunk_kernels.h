@@ -64,7 +64,21 @@ struct ChunkArgs {
     void *pfrag;     // work space: intra-chunk P tiles as MFMA fragments (PFRAG shapes)
     void *gtab;      // work space: e^{G_t} [C], e^{G_L - G_t} [C], e^{G_L}, 0, 0, 0 per chunk, fp32 (PFRAG shapes)
     int B, T, H, Dv;
-    int kw;          // key row width in HBM (q, k, h0, hT rows); KD >= kw, features past kw are zero
+    int kw;          // key width (q, k, h0, hT rows); KD >= kw, features past kw are zero
+    int kst, koff;   // q, k: elements per (token, head) row and first column of this key (kst = kw, koff = 0
+                     // except for a DeltaProduct sub-key pass)
+    int bst, boff;   // beta[((b T + t) H + h) bst + boff] (1, 0 except for a DeltaProduct sub-key pass)
+    int hrows, hoff; // h0, hT: (B, H, hrows, Dv), this key's rows start at row hoff (kw, 0 ...)
+    // DeltaProduct sub-key passes of the single-chain kernels:
+    void *atil;      // prep: [s<t] (k_t . k_s) e^{G_t - G_s} as hi/lo fragments (P's layout), or null
+    float *vout;     // first pass: v' = (1 - m) v + m e written here, fp32 (B, T, H, Dv)
+    const float *vin;    // second pass: the values v' (fp32), in place of v
+    const float *oprev;  // second pass: the first pass's output (fp32), added to this pass's
+    float mcoef;     // m = step_mask[1][0]
+    int nsub;        // prep: sub-keys prepared in one launch (1, or 2 for a DeltaProduct call:
+                     // sub-key 1 at column koff + kw, beta offset boff + 1, its work space after
+                     // sub-key 0's (subws bytes on), no A~)
+    size_t subws;
     int out_bf16;
     float scale;
     float mask[4];   // R x R step mask, row-major
@@ -181,7 +195,7 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(ChunkArgs args) {
         if (tt < T && cv * VEC < args.kw) {
             const size_t row = ((size_t)b * T + tt) * H + h;
             raw = *reinterpret_cast<const U16x8 *>(reinterpret_cast<const unsigned char *>(args.k) +
-                                                   (row * args.kw + cv * VEC) * S::ESZ);
+                                                   (row * args.kst + args.koff + cv * VEC) * S::ESZ);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) raw.v[e] = 0;
@@ -375,7 +389,7 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
     float rbeta = 0.f, rg = 0.f;
     // Per-slot source offsets (bytes) at chunk 0; chunk c adds c*C token rows.
     const int kw = args.kw;
-    const size_t tok_bytes_qk = (size_t)H * kw * S::ESZ, tok_bytes_v = (size_t)H * Dv * S::ESZ;
+    const size_t tok_bytes_qk = (size_t)H * args.kst * S::ESZ, tok_bytes_v = (size_t)H * Dv * S::ESZ;
     size_t kq_off[PKQ], v_off[PV];
     int kq_t[PKQ], v_t[PV];
     bool kq_pad[PKQ];                             // a feature vector past kw: zero
@@ -385,7 +399,8 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
         const int rem = idx % (C * NV);
         kq_t[p] = rem / NV;
         kq_pad[p] = (rem % NV) * VEC >= kw;
-        kq_off[p] = (((size_t)b * T + kq_t[p]) * H + h) * kw * S::ESZ + (kq_pad[p] ? 0 : (size_t)(rem % NV) * 16);
+        kq_off[p] = ((((size_t)b * T + kq_t[p]) * H + h) * args.kst + args.koff) * S::ESZ +
+                    (kq_pad[p] ? 0 : (size_t)(rem % NV) * 16);
     }
 #pragma unroll
     for (int p = 0; p < PV; ++p) {
@@ -515,7 +530,7 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
             Sreg[n] = zero4();
             const int ts = w + 4 * n;
             if (ts < NST && args.h0) {
-                const float *hp = args.h0 + ((size_t)bh * args.kw) * Dv + v0 + (l & 15);
+                const float *hp = args.h0 + ((size_t)bh * args.hrows + args.hoff) * Dv + v0 + (l & 15);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int row = ts * 16 + 4 * (l >> 4) + e;
@@ -692,7 +707,7 @@ __global__ __launch_bounds__(512) void chunk_chain_kernel(ChunkArgs args) {
         for (int n = 0; n < NSTW; ++n) {
             const int ts = w + 4 * n;
             if (ts < NST) {
-                float *hp = args.hT + ((size_t)bh * args.kw) * Dv + v0 + (l & 15);
+                float *hp = args.hT + ((size_t)bh * args.hrows + args.hoff) * Dv + v0 + (l & 15);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int row = ts * 16 + 4 * (l >> 4) + e;

@@ -63,13 +63,19 @@ __global__ __launch_bounds__(256) void chunk_prep2_kernel(ChunkArgs args) {
 
     const int T = args.T, H = args.H;
     const int NT = (T + C - 1) / C;
-    const int total = args.B * H * NT;
+    const int per_sub = args.B * H * NT, total = per_sub * args.nsub;
     const u16 *kg = reinterpret_cast<const u16 *>(args.k);
     const u16 *qg = reinterpret_cast<const u16 *>(args.q);
 
-    for (int ci = blockIdx.x * S::NWAVE + w; ci < total; ci += gridDim.x * S::NWAVE) {
+    for (int cs = blockIdx.x * S::NWAVE + w; cs < total; cs += gridDim.x * S::NWAVE) {
+        // work item cs: sub-key sub = cs / per_sub, chunk ci of it
+        const int sub = cs / per_sub, ci = cs - sub * per_sub;
         const int bh = ci / NT, c = ci % NT, b = bh / H, h = bh % H, t0 = c * C;
         const size_t row0 = (size_t)b * T * H + h;
+        const int koff = args.koff + sub * args.kw, boff = args.boff + sub;
+        char *const wsa = static_cast<char *>(args.tmat) + sub * args.subws;   // this sub-key's work space
+        void *const pfrag = static_cast<char *>(args.pfrag) + sub * args.subws;
+        void *const gtab = static_cast<char *>(args.gtab) + sub * args.subws;
 
         // ---- K and Q rows as MFMA fragments: lane (g, j) of (tt, m) holds
         //      row 16 tt + j, key features 32m + 8g + {0..7}; zero past T ----
@@ -79,14 +85,24 @@ __global__ __launch_bounds__(256) void chunk_prep2_kernel(ChunkArgs args) {
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
             const int t = t0 + tt * 16 + c16;
-            const size_t off = (row0 + (size_t)min(t, T - 1) * H) * kw;
+            const size_t off = (row0 + (size_t)min(t, T - 1) * H) * args.kst + koff;
+            if (kw == KD) {                     // (wave-uniform) no padded key features
 #pragma unroll
-            for (int m = 0; m < NKS; ++m) {
-                const int f = m * 32 + 8 * g;
-                const bool pad = f >= kw;
-                kf[tt][m] = *reinterpret_cast<const bf16x8 *>(kg + off + (pad ? 0 : f));
-                qf[tt][m] = *reinterpret_cast<const bf16x8 *>(qg + off + (pad ? 0 : f));
-                if (t >= T || pad) kf[tt][m] = qf[tt][m] = bf16x8{};
+                for (int m = 0; m < NKS; ++m) {
+                    const int f = m * 32 + 8 * g;
+                    kf[tt][m] = *reinterpret_cast<const bf16x8 *>(kg + off + f);
+                    qf[tt][m] = *reinterpret_cast<const bf16x8 *>(qg + off + f);
+                    if (t >= T) kf[tt][m] = qf[tt][m] = bf16x8{};
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < NKS; ++m) {
+                    const int f = m * 32 + 8 * g;
+                    const bool pad = f >= kw;
+                    kf[tt][m] = *reinterpret_cast<const bf16x8 *>(kg + off + (pad ? 0 : f));
+                    qf[tt][m] = *reinterpret_cast<const bf16x8 *>(qg + off + (pad ? 0 : f));
+                    if (t >= T || pad) kf[tt][m] = qf[tt][m] = bf16x8{};
+                }
             }
         }
 
@@ -95,7 +111,7 @@ __global__ __launch_bounds__(256) void chunk_prep2_kernel(ChunkArgs args) {
             const int t = t0 + l;
             const bool ok = l < C && t < T;
             float gs = ok ? args.g[row0 + (size_t)t * H] : 0.f;
-            const float bt = ok ? args.beta[row0 + (size_t)t * H] : 0.f;
+            const float bt = ok ? args.beta[(row0 + (size_t)t * H) * args.bst + boff] : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(gs, off, 64);
@@ -106,7 +122,7 @@ __global__ __launch_bounds__(256) void chunk_prep2_kernel(ChunkArgs args) {
             if (l < C) {
                 G2[l] = g2;
                 betas[l] = bt;
-                float *gt = reinterpret_cast<float *>(args.gtab) + (size_t)ci * gate_table_len<C>();
+                float *gt = reinterpret_cast<float *>(gtab) + (size_t)ci * gate_table_len<C>();
                 gt[l] = fast_exp2(g2);               // e^{G_t}
                 gt[C + l] = fast_exp2(g2l - g2);     // e^{G_L - G_t}
                 if (l < 4) gt[2 * C + l] = l == 0 ? fast_exp2(g2l) : 0.f;   // e^{G_L}
@@ -116,7 +132,10 @@ __global__ __launch_bounds__(256) void chunk_prep2_kernel(ChunkArgs args) {
         lds_fence();
 
         // ---- A: tile (tt, ss <= tt); lane (g, j) gets row t = 16 tt + j and
-        //      columns s = 16 ss + 4g + e (one 16-byte store) ----
+        //      columns s = 16 ss + 4g + e (one 16-byte store).  With atil,
+        //      A without beta (the decay-masked gram) also goes out as hi/lo
+        //      MFMA fragments in P's layout ----
+        uint4 *adst = args.atil && sub == 0 ? reinterpret_cast<uint4 *>(args.atil) + (size_t)ci * NLOW * 64 + l : nullptr;
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
             const int t = tt * 16 + c16;
@@ -127,19 +146,26 @@ __global__ __launch_bounds__(256) void chunk_prep2_kernel(ChunkArgs args) {
 #pragma unroll
                 for (int m = 0; m < NKS; ++m) acc = mfma32(kf[ss][m], kf[tt][m], acc);
                 const floatx4 g2s = *reinterpret_cast<const floatx4 *>(G2 + ss * 16 + 4 * g);
-                floatx4 a;
+                floatx4 a, at;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int s = ss * 16 + 4 * g + e;
-                    a[e] = s < t ? btt * acc[e] * fast_exp2(fminf(g2t - g2s[e], 0.f)) : 0.f;
+                    at[e] = s < t ? acc[e] * fast_exp2(fminf(g2t - g2s[e], 0.f)) : 0.f;
+                    a[e] = btt * at[e];
                 }
                 *reinterpret_cast<floatx4 *>(As + t * LDA + ss * 16 + 4 * g) = a;
+                if (adst) {
+                    uint4 f;
+                    split2_bf16(at[0], at[1], f.x, f.z);
+                    split2_bf16(at[2], at[3], f.y, f.w);
+                    adst[(tt * (tt + 1) / 2 + ss) * 64] = f;
+                }
             }
         }
 
         // ---- P tiles (ti, tj <= ti), fragments to the work space ----
         {
-            uint4 *dst = reinterpret_cast<uint4 *>(args.pfrag) + (size_t)ci * NLOW * 64 + l;
+            uint4 *dst = reinterpret_cast<uint4 *>(pfrag) + (size_t)ci * NLOW * 64 + l;
 #pragma unroll
             for (int ti = 0; ti < NTT; ++ti) {
                 const float g2t = G2[ti * 16 + c16];
@@ -253,7 +279,7 @@ __global__ __launch_bounds__(256) void chunk_prep2_kernel(ChunkArgs args) {
         // ---- T diag(beta) without its diagonal, zero above the block
         //      diagonal, bf16, columns in the permuted order ----
         {
-            u16 *out = reinterpret_cast<u16 *>(args.tmat) + (size_t)ci * C * C;
+            u16 *out = reinterpret_cast<u16 *>(wsa) + (size_t)ci * C * C;
 #pragma unroll
             for (int k = 0; k < C * C / 8 / 64; ++k) {
                 const int idx = k * 64 + l;

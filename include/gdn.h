@@ -148,7 +148,10 @@ int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
  * erases along e_{t,a} = sum_b M[a][b] k_{t,b} (placed in row block b).
  * Per token: P = exp(g_t) S; p_a = P^T e_{t,a} for all a from the same P;
  * S = P + sum_a beta_{t,a} E_a k_{t,a} (v_t - p_a)^T; o_t = scale S^T q_t.
- * With r = 1 and M = [[1]] this is gdn_chunk_fwd.
+ * With r = 1 and M = [[1]] this is gdn_chunk_fwd.  For r = 2 with a lower
+ * unitriangular mask [[1, 0], [m, 1]] and bf16 inputs the row blocks are two
+ * chained gated delta rules (block 1's values are v - m times block 0's
+ * prediction) and run as two passes of 64-token chunks, whatever `chunk`.
  *
  *   q, k       (B, T, H, r*dk) dtype
  *   v          (B, T, H, Dv)   dtype

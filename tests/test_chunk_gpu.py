@@ -228,6 +228,12 @@ DP_SMALL = [
     (2, 100, 2, 2, 64, 64, 32, "bf16", "rand"),
     (1, 130, 2, 2, 128, 128, 32, "bf16", "tril"),
     (1, 77, 2, 1, 128, 64, 64, "bf16", "one"),
+    # lower unitriangular masks [[1, 0], [m, 1]] in bf16 run as two passes of
+    # the single-chain kernels: m = 1, 0.5, 0 (M = I), several chunks, ragged
+    (1, 300, 2, 2, 128, 128, 32, "bf16", "tril"),
+    (2, 200, 3, 2, 64, 48, 16, "bf16", "half"),
+    (1, 150, 2, 2, 32, 64, 32, "bf16", "eye"),
+    (1, 1000, 1, 2, 128, 80, 32, "bf16", "half"),
 ]
 
 
@@ -238,7 +244,8 @@ def test_deltaproduct_small(gdn, case):
     _say(f"deltaproduct_chunk_fwd small case {case}")
     rng = np.random.default_rng(T + dk)
     mask = {"tril": np.tril(np.ones((r, r))), "rand": np.tril(rng.uniform(-1, 1, (r, r))),
-            "one": np.ones((1, 1))}[mk].astype(np.float32)
+            "one": np.ones((1, 1)), "half": np.array([[1.0, 0.0], [0.5, 1.0]]),
+            "eye": np.eye(2)}[mk].astype(np.float32)
     d = synth.deltaproduct_inputs(B, T, H, r, dk, Dv, seed=2000 + T, dtype=dtype, h0_std=0.1, mask=mask)
     q, k, v = (to_dev(d[n], dtype) for n in ("q", "k", "v"))
     o, hT = gdn.deltaproduct_chunk_fwd(q, k, v, to_dev(d["beta"], "f32"), to_dev(d["g"], "f32"), mask,
