@@ -160,6 +160,8 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
     a.subws = 0;
     a.out_bf16 = out_dtype == GDN_DTYPE_BF16;
     a.scale = scale;
+    a.tmatT = nullptr;
+    a.sst = a.rst = nullptr;
     for (int i = 0; i < 4; ++i) a.mask[i] = 0.f;
     if (r == 1) {
         a.mask[0] = step_mask ? step_mask[0] : 1.f;

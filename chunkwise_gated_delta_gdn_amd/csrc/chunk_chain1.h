@@ -48,6 +48,10 @@
 //            its output goes to an fp32 buffer;
 //   DPM = 2: the pass on sub-key 1 with v' (fp32, read by the chain wave) as
 //            the values; its output adds the first pass's.
+//
+// DPM = 3 is the state pass of the backward: no output; the chain wave
+// writes every chunk's start state S (row-major, fp32) and its residual
+// R = V - e^G K S (this lane's 16 values, accumulator order) instead.
 #pragma once
 
 #include <type_traits>
@@ -154,7 +158,7 @@ __device__ __forceinline__ void frag_split(const floatx4 &t0, const floatx4 &t1,
 template <int KD, int C, int DPM = 0>
 __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kernel(ChunkArgs args) {
     using S = Chain1Shape<KD, C>;
-    static_assert(DPM == 0 || C == 64, "DeltaProduct passes run 64-token chunks");
+    static_assert(DPM == 0 || C == 64, "DeltaProduct and backward passes run 64-token chunks");
     constexpr int BV = S::BV, NTT = S::NTT, NKS = S::NKS, NST = S::NST, NCS = S::NCS, NKC = S::NKC;
     constexpr int LDK = S::LDK, LDT = S::LDT, LDV = S::LDV, LDSF = S::LDSF, LDVF = S::LDVF;
     constexpr int TSW = S::TSW;
@@ -233,6 +237,13 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
         for (int c = 0, sq = 0; c < NT; ++c, sq = sq == 2 ? 0 : sq + 1) {
             const int p = c & 1;                 // St, Vn; staging buffers: sq = c % 3
             const u16 *ks = Ks(sq), *tb = Tb(sq), *bv = BVs(sq);
+            if constexpr (DPM == 3) {            // the chunk-start state, row-major
+                float *sp = args.sst + ((size_t)bh * NT + c) * args.kw * Dv + v0 + c16;
+#pragma unroll
+                for (int ti = 0; ti < NST; ++ti)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sp[(size_t)feat(ti, e) * Dv] = Sreg[ti][e];
+            }
             const float *gp = gate(sq);
             // LDS operands of K S first (nothing here depends on the state), so
             // their latency overlaps; the MFMAs run over the token tiles
@@ -311,6 +322,11 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
 #pragma unroll
                 for (int e = 0; e < 4; ++e) rr[tt][e] = vin4[tt][e] - eg[tt][e] * y[tt][e];
             }
+            if constexpr (DPM == 3) {
+                floatx4 *rp = reinterpret_cast<floatx4 *>(args.rst) + (((size_t)bh * NT + c) * nvb + vb) * 64 * NTT + l * NTT;
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt) rp[tt] = rr[tt];
+            }
             bf16x8 rh[NCS];
 #pragma unroll
             for (int m = 0; m < NCS; ++m) rh[m] = frag_hi(rr[2 * m], rr[2 * m + 1]);
@@ -329,7 +345,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
             floatx4 vt4[NTT];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
-                *reinterpret_cast<floatx4 *>(vnp + c16 * LDVF + tt * 16 + 4 * g) = vn[tt];
+                if constexpr (DPM != 3) *reinterpret_cast<floatx4 *>(vnp + c16 * LDVF + tt * 16 + 4 * g) = vn[tt];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vt4[tt][e] = el[tt][e] * vn[tt][e];
             }
@@ -349,7 +365,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
             }
             // S_start of chunk c goes out while the state MFMAs run (its LDS
             // writes then do not queue ahead of this chunk's operand reads)
-            publish_state(p);
+            if constexpr (DPM != 3) publish_state(p);
             if constexpr (DPM == 1) {
                 // (issued after the state update's MFMAs: off the chain's path)
                 // per-token errors e = R - A~ V_new and v' = (1 - m) v + m e;
@@ -606,7 +622,11 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
     }
     using std::integral_constant;
     using none = integral_constant<int, -1>;
-    if constexpr (NTT == 4) {
+    if constexpr (DPM == 3) {                   // no output: waves 1 and 2 take part in the barriers only
+        if (w == 1 || w == 2) out_wave(none{}, none{}, none{});
+        if (w == 3) out_wave(none{}, none{}, integral_constant<int, 0>{});
+        if (w == 5) out_wave(none{}, none{}, integral_constant<int, 1>{});
+    } else if constexpr (NTT == 4) {
         if (w == 1) out_wave(integral_constant<int, 3>{}, integral_constant<int, 0>{}, none{});
         if (w == 2) out_wave(integral_constant<int, 2>{}, integral_constant<int, 1>{}, none{});
         if (w == 3) out_wave(none{}, none{}, integral_constant<int, 0>{});

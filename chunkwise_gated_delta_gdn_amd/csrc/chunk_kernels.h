@@ -82,6 +82,10 @@ struct ChunkArgs {
     int out_bf16;
     float scale;
     float mask[4];   // R x R step mask, row-major
+    // backward of the single-step bf16 path (64-token chunks):
+    void *tmatT;     // prep: T^T without its diagonal (unscaled), rows s, columns t in the permuted k order
+    float *sst;      // state pass: chunk-start state per chunk, (B*H, NT, Dk, Dv) fp32
+    float *rst;      // state pass: R = V - e^G K S per chunk, (B*H, NT, Dv/16, 64 lanes, 16) fp32
 };
 
 constexpr float LOG2E = 1.4426950408889634f;

@@ -20,6 +20,11 @@
 //           columns s = 16 tj + 4 (l/16) + e)
 //   gates   e^{G_t}, e^{G_L - G_t}, e^{G_L}, beta_t                   -> fp32
 //
+// BWD (the backward of the rule) writes, in place of P, the same scores as
+// the A operand of P^T (lane l: row s = 16 tj + l%16, columns t = 16 ti +
+// 4 (l/16) + e), and also T^T without its diagonal, unscaled, rows s and
+// columns t in the permuted k order (tmatT).
+//
 // A wave needs no other wave: K and Q come straight from global memory as
 // MFMA fragments (the gram matrix K K^T and the scores K Q^T take both
 // operands from the same row fragments), A and T live in the wave's own LDS
@@ -50,7 +55,7 @@ struct Prep2Shape {
 // keeps one wave's LDS operations in order)
 __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
 
-template <int KD, int C>
+template <int KD, int C, bool BWD = false>
 __global__ __launch_bounds__(256) void chunk_prep2_kernel(ChunkArgs args) {
     using S = Prep2Shape<KD, C>;
     constexpr int NTT = S::NTT, NLOW = S::NLOW, NKS = S::NKS, LDA = S::LDA;
@@ -172,14 +177,27 @@ __global__ __launch_bounds__(256) void chunk_prep2_kernel(ChunkArgs args) {
 #pragma unroll
                 for (int tj = 0; tj <= ti; ++tj) {
                     floatx4 acc = zero4();
-#pragma unroll
-                    for (int m = 0; m < NKS; ++m) acc = mfma32(kf[tj][m], qf[ti][m], acc);
-                    const floatx4 g2s = *reinterpret_cast<const floatx4 *>(G2 + tj * 16 + 4 * g);
                     float pv[4];
+                    if constexpr (BWD) {
+                        // Q rows as the A operand: lane (g, j) gets rows t = 16 ti + 4g + e, column s = 16 tj + j
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s = tj * 16 + 4 * g + e;
-                        pv[e] = s <= ti * 16 + c16 ? acc[e] * fast_exp2(fminf(g2t - g2s[e], 0.f)) : 0.f;
+                        for (int m = 0; m < NKS; ++m) acc = mfma32(qf[ti][m], kf[tj][m], acc);
+                        const floatx4 g2r = *reinterpret_cast<const floatx4 *>(G2 + ti * 16 + 4 * g);
+                        const float g2c = G2[tj * 16 + c16];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int t = ti * 16 + 4 * g + e;
+                            pv[e] = tj * 16 + c16 <= t ? acc[e] * fast_exp2(fminf(g2r[e] - g2c, 0.f)) : 0.f;
+                        }
+                    } else {
+#pragma unroll
+                        for (int m = 0; m < NKS; ++m) acc = mfma32(kf[tj][m], qf[ti][m], acc);
+                        const floatx4 g2s = *reinterpret_cast<const floatx4 *>(G2 + tj * 16 + 4 * g);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int s = tj * 16 + 4 * g + e;
+                            pv[e] = s <= ti * 16 + c16 ? acc[e] * fast_exp2(fminf(g2t - g2s[e], 0.f)) : 0.f;
+                        }
                     }
                     uint4 f;
                     split2_bf16(pv[0], pv[1], f.x, f.z);
@@ -294,6 +312,26 @@ __global__ __launch_bounds__(256) void chunk_prep2_kernel(ChunkArgs args) {
                     x1[e] = (j1 >> 4) > (i >> 4) || j1 + e == i ? 0.f : x1[e] * b1[e];
                 }
                 *reinterpret_cast<uint4 *>(out + (size_t)i * C + pc * 8) =
+                    uint4{cvt2_bf16(x0[0], x0[1]), cvt2_bf16(x0[2], x0[3]), cvt2_bf16(x1[0], x1[1]),
+                          cvt2_bf16(x1[2], x1[3])};
+            }
+        }
+        if constexpr (BWD) {
+            // T^T without its diagonal, unscaled: row s holds T[t][s] for t > s (T's
+            // strictly lower part, read down the columns of the LDS copy), columns in
+            // the permuted order
+            u16 *out = reinterpret_cast<u16 *>(args.tmatT) + (size_t)ci * C * C;
+#pragma unroll
+            for (int k = 0; k < C * C / 8 / 64; ++k) {
+                const int idx = k * 64 + l;
+                const int s = idx / (C / 8), pc = idx % (C / 8), j0 = (pc >> 2) * 32 + 4 * (pc & 3), j1 = j0 + 16;
+                float x0[4], x1[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x0[e] = j0 + e > s ? As[(j0 + e) * LDA + s] : 0.f;
+                    x1[e] = j1 + e > s ? As[(j1 + e) * LDA + s] : 0.f;
+                }
+                *reinterpret_cast<uint4 *>(out + (size_t)s * C + pc * 8) =
                     uint4{cvt2_bf16(x0[0], x0[1]), cvt2_bf16(x0[2], x0[3]), cvt2_bf16(x1[0], x1[1]),
                           cvt2_bf16(x1[2], x1[3])};
             }

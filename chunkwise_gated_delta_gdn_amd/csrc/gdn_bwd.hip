@@ -482,8 +482,19 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
 }  // namespace
 }  // namespace gdn
 
-extern "C" size_t gdn_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
+namespace gdn {
+// chunk_bwd.hip: the chunkwise MFMA path
+bool chunk_bwd_eligible(int T, int Dk, int Dv, int dtype);
+size_t chunk_bwd_workspace(int B, int T, int H, int Dk, int Dv);
+hipError_t chunk_bwd_launch(const void *q, const void *k, const void *v, const float *beta, const float *g,
+                            float scale, const float *h0, const void *dout, const float *dhT, float *dq, float *dk,
+                            float *dv, float *dbeta, float *dg, float *dh0, int B, int T, int H, int Dk, int Dv,
+                            void *workspace, hipStream_t s);
+}  // namespace gdn
+
+extern "C" size_t gdn_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int dtype) {
     if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return 0;
+    if (gdn::chunk_bwd_eligible(T, Dk, Dv, dtype)) return gdn::chunk_bwd_workspace(B, T, H, Dk, Dv);
     return gdn::bwd_workspace(B, T, H, Dk, Dv);
 }
 
@@ -514,13 +525,21 @@ extern "C" int gdn_bwd(const void *q, const void *k, const void *v, const float 
     }
     GDN_REQUIRE((!h0 || gdn::aligned(h0, 4)) && (!dhT || gdn::aligned(dhT, 4)) && (!dh0 || gdn::aligned(dh0, 4)),
                 GDN_EINVAL, "%s: misaligned state pointer", name);
-    const size_t need = gdn::bwd_workspace(B, T, H, Dk, Dv);
+    const bool chunked = gdn::chunk_bwd_eligible(T, Dk, Dv, dtype);
+    const size_t need = chunked ? gdn::chunk_bwd_workspace(B, T, H, Dk, Dv) : gdn::bwd_workspace(B, T, H, Dk, Dv);
     GDN_REQUIRE(workspace_bytes >= need, GDN_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", name,
                 workspace_bytes, need);
     GDN_REQUIRE(need == 0 || (workspace && gdn::aligned(workspace, 16)), GDN_EINVAL,
                 "%s: workspace must be a 16-byte aligned device pointer", name);
     GDN_REQUIRE((size_t)B * H * (Dv / 16) < (1u << 31), GDN_EUNSUPPORTED, "%s: too many (b, h, column group) units",
                 name);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (chunked) {
+        GDN_REQUIRE((size_t)B * H * ((T + 63) / 64) < (1u << 31), GDN_EUNSUPPORTED, "%s: too many chunks", name);
+        return gdn::check_hip(gdn::chunk_bwd_launch(q, k, v, beta, log_decay, scale, h0, dout, dhT, dq, dk, dv,
+                                                    dbeta, dlog_decay, dh0, B, T, H, Dk, Dv, workspace, s),
+                              name);
+    }
     gdn::BwdArgs a;
     a.q = q;
     a.k = k;
@@ -548,7 +567,6 @@ extern "C" int gdn_bwd(const void *q, const void *k, const void *v, const float 
     a.part = a.ck + nw * nseg * Dk * gdn::BWD_CW;
     a.pstride = ((size_t)B * T * H * (2 * Dk + 2) + 3) & ~(size_t)3;
     if (!dh0 && T == 0) return GDN_OK;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool f32 = dtype == GDN_DTYPE_F32;
     hipError_t e;
     switch (Dk) {

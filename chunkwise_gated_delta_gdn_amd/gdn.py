@@ -70,7 +70,7 @@ def _load():
     lib.gdn_prep.restype = I
     lib.gdn_bwd.argtypes = [P, P, P, P, P, F, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, Z, P]
     lib.gdn_bwd.restype = I
-    lib.gdn_bwd_workspace_bytes.argtypes = [I] * 5
+    lib.gdn_bwd_workspace_bytes.argtypes = [I] * 6
     lib.gdn_bwd_workspace_bytes.restype = Z
     return lib
 
@@ -338,7 +338,7 @@ def gdn_bwd(q, k, v, beta, log_decay, dout, scale=1.0, h0=None, dhT=None, need_d
     dbeta = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     dg = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     dh0 = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if need_dh0 else None
-    ws, nws = _workspace(_lib.gdn_bwd_workspace_bytes(B, T, H, Dk, Dv), dev)
+    ws, nws = _workspace(_lib.gdn_bwd_workspace_bytes(B, T, H, Dk, Dv, _dtype_code(q.dtype)), dev)
     rc = _lib.gdn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_decay), float(scale), _ptr(h0),
                       _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dg),
                       _ptr(dh0), B, T, H, Dk, Dv, _dtype_code(q.dtype), _ptr(ws), nws, _stream(dev))

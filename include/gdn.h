@@ -280,17 +280,25 @@ int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_norm_w,
 
 /*
  * gdn_bwd - gradients of gdn_chunk_fwd's outputs (o, hT) ([dp] lists the
- * chunk backward kernels of this rule: prepare_dv, dhu, dqkw, WY backward;
- * this entry point computes the same gradients on the token recurrence).
+ * chunk backward kernels of this rule: prepare_dv, dhu, dqkw, WY backward).
  *
- * With the forward steps of one token, P = exp(g_t) S_{t-1}, p = P^T k_t,
- * S_t = P + beta_t k_t (v_t - p)^T, o_t = scale S_t^T q_t, and dS = dL/dS_t
- * (dhT, or 0, after the last token), the tokens are walked backwards:
+ * bf16 inputs with Dk in {32, 64, 128} and Dv a multiple of 32 up to 128
+ * (and T > 0) take the chunkwise path, 64-token chunks on MFMA: the chunk
+ * prep (T = (I + A)^-1, its transpose, the transposed causal scores), the
+ * forward state pass keeping every chunk's start state S and residual
+ * R = V - e^G K S, the reverse pass over the chunks,
+ *   dVn = scale Pm^T dO + diag(e^{G_L - G}) K dS',  dX = T^T dVn,
+ *   dS = e^{G_L} dS' + scale Q^T diag(e^G) dO - K^T diag(e^G beta) dX,
+ * (dS' = dhT, or 0, after the last chunk; dh0 = dS before the first), and
+ * the per-chunk gradients of q, k, v, beta and g from S, dS', R and dX.
+ * Every other shape walks the token recurrence backwards: with
+ * P = exp(g_t) S_{t-1}, p = P^T k_t, S_t = P + beta_t k_t (v_t - p)^T,
+ * o_t = scale S_t^T q_t and dS = dL/dS_t,
  *   dS += scale q_t do_t^T,  dq_t = scale S_t do_t,  r = v_t - p,
  *   u = dS^T k_t,  dv_t = beta_t u,  dbeta_t = u . r,  dp = -beta_t u,
  *   dk_t = beta_t dS r + P dp,  dP = dS + k_t dp^T,  dg_t = <dP, P>,
- *   dS = exp(g_t) dP;   dh0 = dS after token 0.
- * States are recomputed from copies kept every 12 tokens in the work space.
+ *   dS = exp(g_t) dP;   dh0 = dS after token 0,
+ * with states recomputed from copies kept every 12 tokens.
  *
  *   q, k            (B, T, H, Dk)  dtype
  *   v, dout         (B, T, H, Dv)  dtype (dout = dL/do)
@@ -301,12 +309,15 @@ int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_norm_w,
  *   dbeta, dlog_decay (B, T, H)    float32 (dlog_decay = dL/dg)
  *   dh0             (B, H, Dk, Dv) float32, nullable (not stored)
  * Supported: Dk in {16, 32, 64, 128}; Dv a multiple of 16 up to 4096; any
- * T >= 0.  q, k, v and dout 16-byte aligned, the other tensors 4-byte.  The work
- * space (gdn_bwd_workspace_bytes, the only authority on its size) holds the
- * states kept every 12 tokens and the per-16-column partial sums: about
+ * T >= 0.  q, k, v and dout 16-byte aligned, the other tensors 4-byte.  The
+ * work space depends on the path, hence on dtype; gdn_bwd_workspace_bytes
+ * is the only authority on its size.  Chunkwise path: per 64-token chunk
+ * and head, T and T^T (16 KiB), the scores (10 KiB), the gate table, S and
+ * dS' (2 Dk Dv * 4 bytes), R and dX (2 * 64 Dv * 4 bytes).  Token path:
+ * the states kept every 12 tokens and per-16-column partial sums, about
  * (Dk Dv / 12 + (2 Dk + 2) Dv / 16) * 4 bytes per token and head.
  */
-size_t gdn_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv);
+size_t gdn_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int dtype);
 int gdn_bwd(const void *q, const void *k, const void *v,
             const float *beta, const float *log_decay, float scale,
             const float *h0, const void *dout, const float *dhT,

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.gdn_abi_version() == 3
+    assert lib.gdn_abi_version() == 4
 
 
 def _chunk(lib, **kw):
@@ -121,7 +121,7 @@ def test_bwd_rejects_bad_arguments(lib):
     assert call(q=ctypes.c_void_p(4100)) == -1                   # q misaligned
     assert call(scale=float("nan")) == -1
     assert call() == -3                                          # no work space
-    need = lib.gdn_bwd_workspace_bytes(1, 8, 2, 64, 64)
+    need = lib.gdn_bwd_workspace_bytes(1, 8, 2, 64, 64, 1)
     assert need > 0
     assert call(ws=None, nws=need) == -1                         # null work space
     assert lib.gdn_bwd(None, None, None, None, None, 1.0, None, None, None, None, None, None,
