@@ -52,9 +52,13 @@ struct BwdChunkArgs {
 //   0  the chain: dS' (KD x 16, fp32) in MFMA accumulators, chunks walked
 //      from the last to the first;
 //   4  idle (the chain's SIMD partner; barriers only);
-//   1  E = scale Q^T diag(gamma) dO of the chunk after next in walk order
-//      (published to LDS in the chain's accumulator order);
-//   2  dV0 = scale Pm^T dO of that chunk (published likewise);
+//   1, 2  E = scale Q^T diag(gamma) dO of the next chunk in walk order,
+//      half of the state rows each (published to LDS in the chain's
+//      accumulator order), and the copy of dS' the chain leaves in that
+//      buffer, to the work space;
+//      Wave 2 also forms dV0 = scale Pm^T dO of that chunk (Pm^T
+//      fragments, hi/lo, straight from the prep into registers one step
+//      ahead; published like E);
 //   3, 5 staging: ring A (K rows, T^T, gate table) two steps before the
 //      chain uses it, ring B (Q rows, dO slice, gate table) two steps
 //      before the helpers use it, by LDS-direct loads.
@@ -170,14 +174,6 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
             const int sq = ring(c), p = c & 1;
             const u16 *ks = Ks(sq), *tt_ = Tt(sq);
             const float *gp = gA(sq);
-            // dS' of this chunk (the gradient of the state leaving it), row-major
-            {
-                float *sp = ba.dsst + ((size_t)bh * NT + c) * KD * Dv + v0 + c16;
-#pragma unroll
-                for (int ti = 0; ti < NST; ++ti)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sp[(size_t)feat(ti, e) * Dv] = Sreg[ti][e];
-            }
             bf16x8 kf[NTT][NKS];
 #pragma unroll
             for (int m = 0; m < NKS; ++m)
@@ -207,7 +203,7 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
                 for (int st = 0; st < NTT; ++st)
                     if (2 * m + 1 >= st)
                         tf[st][m] = ld8(tt_ + (st * 16 + c16) * LDT + (((4 * m + g) ^ ((st * 16 + c16) & TSW)) << 3));
-            floatx4 eg[NTT], el[NTT], bt[NTT], dv0[NTT], ep[NST];
+            floatx4 eg[NTT], el[NTT], bt[NTT], dv0[NTT];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
                 eg[tt] = *reinterpret_cast<const floatx4 *>(gp + tt * 16 + 4 * g);
@@ -215,8 +211,7 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
                 bt[tt] = *reinterpret_cast<const floatx4 *>(gp + 2 * C + 4 + tt * 16 + 4 * g);
                 dv0[tt] = Dp(p)[tt * 64 + l];
             }
-#pragma unroll
-            for (int ti = 0; ti < NST; ++ti) ep[ti] = Ep(p)[ti * 64 + l];
+
             const float gL = gp[2 * C];
             // dVn = dV0 + lambda o X1; dX = dVn + T_off^T dVn (dVn rounded once)
             floatx4 dvn[NTT];
@@ -244,9 +239,15 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
             bf16x8 zh[NCS], zl[NCS];
 #pragma unroll
             for (int m = 0; m < NCS; ++m) frag_split(z[2 * m], z[2 * m + 1], zh[m], zl[m]);
+            // E initialises the update's accumulators; dS' of this chunk (the
+            // gradient of the state leaving it) goes over it, and waves 1 and 2
+            // write it to the work space next step
             floatx4 ds[NST];
 #pragma unroll
-            for (int ti = 0; ti < NST; ++ti) ds[ti] = ep[ti];
+            for (int ti = 0; ti < NST; ++ti) {
+                ds[ti] = Ep(p)[ti * 64 + l];
+                Ep(p)[ti * 64 + l] = Sreg[ti];
+            }
 #pragma unroll
             for (int m = 0; m < NCS; ++m) {
 #pragma unroll
@@ -284,24 +285,59 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
     }
 
     const float scale = args.scale;
-    if (w == 1) {
+    if (w == 1 || w == 2) {
         // ================================================================
-        // E = scale Q^T diag(gamma) dO, in the chain's accumulator order
+        // waves 1 and 2: E = scale Q^T diag(gamma) dO of the next chunk in
+        // walk order, state row tiles [0, NST/2) and [NST/2, NST) (published
+        // in the chain's accumulator order over the dS' copy the chain left
+        // in that buffer one step earlier, which each wave first writes to
+        // the work space for its own tiles)
         // ================================================================
+        const int th0 = (w - 1) * (NST / 2);
+        // the dS' copy of chunk cd, this wave's tiles, as 16-byte pieces of its
+        // rows: lane l takes state row 4 (l/16) + e of tile ti ... i.e. copy
+        // row rr = l/4 (accumulator row 4 g' + e' of the tile) and value
+        // columns 4 (l%4) .. +3, gathered from the four lanes holding them
+        auto store_ds = [&](int cd) {
+            const int rr = l >> 2, q = l & 3, gq = rr >> 2, eq = rr & 3;
+            const float *ep = reinterpret_cast<const float *>(Ep(cd & 1));
+            float *sp = ba.dsst + ((size_t)bh * NT + cd) * KD * Dv + v0 + 4 * q;
+#pragma unroll
+            for (int i = 0; i < NST / 2; ++i) {
+                const int ti = th0 + i;
+                floatx4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = ep[(ti * 64 + gq * 16 + 4 * q + e) * 4 + eq];
+                const int f = (ti >> 1) * 32 + 8 * gq + 4 * (ti & 1) + eq;
+                *reinterpret_cast<floatx4 *>(sp + (size_t)f * Dv) = x;
+            }
+        };
+        u32x4 pf[NLOW];
+        auto load_pf = [&](int c) {
+            c = c < 0 ? 0 : c;                  // (past the first chunk: loaded again, unused)
+            const uint4 *pc = reinterpret_cast<const uint4 *>(args.pfrag) + ((size_t)bh * NT + c) * NLOW * 64 + l;
+#pragma unroll
+            for (int i = 0; i < NLOW; ++i) pf[i] = __builtin_bit_cast(u32x4, pc[i * 64]);
+        };
+        if (w == 2) load_pf(NT - 1);
         __syncthreads();
         for (int s = 0; s <= NT; ++s) {
             const int c = NT - 1 - s;
+            if (s >= 2) store_ds(c + 2);
             if (c >= 0) {
                 const int sq = ring(c), p = c & 1;
                 const u16 *dos = dOs(sq);
                 const float *gp = gB(sq);
-                bf16x8 qa[NST][NCS];
-                kt_frags<KD>(Qs(sq), qa);
+                shortx4 vv[NTT];
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt)
+                    vv[tt] = ld_tr16(dos + (tt * 16 + 4 * g + (c16 >> 2)) * LDV + 4 * (c16 & 3));
+                // E tiles of this wave: Q^T fragments (the chain's row order) times
+                // gamma dO (hi + lo)
                 floatx4 gd[NTT];
 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt) {
-                    const uint2 v2 = __builtin_bit_cast(
-                        uint2, ld_tr16(dos + (tt * 16 + 4 * g + (c16 >> 2)) * LDV + 4 * (c16 & 3)));
+                    const uint2 v2 = __builtin_bit_cast(uint2, vv[tt]);
                     const floatx4 e4 = *reinterpret_cast<const floatx4 *>(gp + tt * 16 + 4 * g);
                     gd[tt] = floatx4{scale * e4[0] * __builtin_bit_cast(float, v2.x << 16),
                                      scale * e4[1] * __builtin_bit_cast(float, v2.x & 0xffff0000u),
@@ -311,66 +347,45 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
                 bf16x8 gh[NCS], gl[NCS];
 #pragma unroll
                 for (int m = 0; m < NCS; ++m) frag_split(gd[2 * m], gd[2 * m + 1], gh[m], gl[m]);
-                floatx4 ev[NST];
+                const u16 *qs = Qs(sq);
+#pragma unroll 1
+                for (int i = 0; i < NST / 2; ++i) {
+                    const int ti = th0 + i;
+                    const int pc = 4 * (ti >> 1) + (c16 & 3), hf = 4 * (ti & 1);
+                    floatx4 ev = zero4();
 #pragma unroll
-                for (int ti = 0; ti < NST; ++ti) ev[ti] = zero4();
-#pragma unroll
-                for (int m = 0; m < NCS; ++m) {
-#pragma unroll
-                    for (int ti = 0; ti < NST; ++ti) ev[ti] = mfma32(qa[ti][m], gh[m], ev[ti]);
-#pragma unroll
-                    for (int ti = 0; ti < NST; ++ti) ev[ti] = mfma32(qa[ti][m], gl[m], ev[ti]);
-                }
-#pragma unroll
-                for (int ti = 0; ti < NST; ++ti) Ep(p)[ti * 64 + l] = ev[ti];
-            }
-            lds_barrier();
-        }
-        __syncthreads();
-        return;
-    }
-
-    if (w == 2) {
-        // ================================================================
-        // dV0 = scale Pm^T dO; Pm^T fragments (hi/lo) straight from the prep
-        // into registers one step ahead
-        // ================================================================
-        u32x4 pf[NLOW];
-        auto load_pf = [&](int c) {
-            const uint4 *pc = reinterpret_cast<const uint4 *>(args.pfrag) + ((size_t)bh * NT + c) * NLOW * 64 + l;
-#pragma unroll
-            for (int i = 0; i < NLOW; ++i) pf[i] = __builtin_bit_cast(u32x4, pc[i * 64]);
-        };
-        load_pf(NT - 1);
-        __syncthreads();
-        for (int s = 0; s <= NT; ++s) {
-            const int c = NT - 1 - s;
-            if (c >= 0) {
-                const int sq = ring(c), p = c & 1;
-                const u16 *dos = dOs(sq);
-                shortx4 vv[NTT];
-#pragma unroll
-                for (int tt = 0; tt < NTT; ++tt)
-                    vv[tt] = ld_tr16(dos + (tt * 16 + 4 * g + (c16 >> 2)) * LDV + 4 * (c16 & 3));
-#pragma unroll
-                for (int st = 0; st < NTT; ++st) {
-                    floatx4 acc = zero4();
-#pragma unroll
-                    for (int tt = st; tt < NTT; ++tt) {
-                        const u32x4 f = pf[tt * (tt + 1) / 2 + st];
-                        const shortx4 ah = __builtin_bit_cast(shortx4, uint2{f[0], f[1]});
-                        const shortx4 al = __builtin_bit_cast(shortx4, uint2{f[2], f[3]});
-                        acc = mfma16(ah, vv[tt], acc);
-                        acc = mfma16(al, vv[tt], acc);
+                    for (int m = 0; m < NCS; ++m) {
+                        const int r0 = m * 32 + 4 * g + (c16 >> 2), r1 = r0 + 16;
+                        const uint2 lo = __builtin_bit_cast(uint2, ld_tr16(qs + r0 * LDK + ((pc ^ kswz<NKC>(r0)) << 3) + hf));
+                        const uint2 hi = __builtin_bit_cast(uint2, ld_tr16(qs + r1 * LDK + ((pc ^ kswz<NKC>(r1)) << 3) + hf));
+                        const bf16x8 qa = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
+                        ev = mfma32(qa, gh[m], ev);
+                        ev = mfma32(qa, gl[m], ev);
                     }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] *= scale;
-                    Dp(p)[st * 64 + l] = acc;
+                    Ep(p)[ti * 64 + l] = ev;
                 }
-                if (c > 0) load_pf(c - 1);
+                if (w == 2) {                   // dV0 = scale Pm^T dO
+#pragma unroll
+                    for (int st = 0; st < NTT; ++st) {
+                        floatx4 acc = zero4();
+#pragma unroll
+                        for (int tt = st; tt < NTT; ++tt) {
+                            const u32x4 f = pf[tt * (tt + 1) / 2 + st];
+                            const shortx4 ah = __builtin_bit_cast(shortx4, uint2{f[0], f[1]});
+                            const shortx4 al = __builtin_bit_cast(shortx4, uint2{f[2], f[3]});
+                            acc = mfma16(ah, vv[tt], acc);
+                            acc = mfma16(al, vv[tt], acc);
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[e] *= scale;
+                        Dp(p)[st * 64 + l] = acc;
+                    }
+                    load_pf(c - 1);
+                }
             }
             lds_barrier();
         }
+        store_ds(0);                            // published at the last step
         __syncthreads();
         return;
     }
@@ -428,7 +443,7 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
                 }
             }
         };
-        // loads this wave issues per step: after the barrier wait, at most these
+        // loads this wave issues per step: after the barrier wait at most these
         // (this step's) are outstanding, so the previous step's are complete
         constexpr int NMINE = (NDMA - LI + 1) / 2;
         static_assert(NMINE < 64, "6-bit vmcnt");
@@ -456,8 +471,10 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
 // ---------------------------------------------------------------------------
 // Per-chunk gradients.  One workgroup of eight waves per (batch, head,
 // chunk), in phases separated by barriers:
-//   0  K and Q rows of the chunk staged in LDS (LDS-direct, zero past T),
-//      the gates (cumsum in log2 units) and beta;
+//   0  K, Q and dO rows of the chunk staged in LDS (LDS-direct, zero past
+//      T), the gates (cumsum in log2 units) and beta; every wave also issues
+//      its loads of phases 1 and 3 (R, dX, T' fragments; S, dS' fragments),
+//      so all of the chunk's HBM reads are in flight together;
 //   1  wave w < Dv/16 owns value columns 16w..16w+15: Vn = beta R + T' R
 //      (T' = T diag(beta) without its diagonal, R hi + lo), dV = beta dX,
 //      dbeta's first sum; Vn and dX go to LDS as hi/lo bf16 rows;
@@ -482,7 +499,8 @@ struct BGradShape {
     static constexpr int OFF_VH = 2 * SZ_KC, OFF_VL = OFF_VH + SZ_V, OFF_XH = OFF_VL + SZ_V, OFF_XL = OFF_XH + SZ_V;
     static constexpr int OFF_M1H = OFF_XL + SZ_V, OFF_M1L = OFF_M1H + SZ_M, OFF_M2H = OFF_M1L + SZ_M,
                          OFF_M2L = OFF_M2H + SZ_M;
-    static constexpr int OFF_G2 = OFF_M2L + SZ_M;      // G (log2 units) [C]
+    static constexpr int OFF_DO = OFF_M2L + SZ_M;      // dO rows, bf16, swizzled pieces
+    static constexpr int OFF_G2 = OFF_DO + SZ_V;       // G (log2 units) [C]
     static constexpr int OFF_BT = OFF_G2 + C * 4;      // beta [C]
     static constexpr int OFF_ZERO = OFF_BT + C * 4;    // cleared in phase 0:
     static constexpr int OFF_DB2 = OFF_ZERO;           //   [4][C] dbeta, second sum, by column tile
@@ -575,19 +593,63 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
     const size_t rowk0 = ((size_t)b * T * H + h) * KD, rowv0 = ((size_t)b * T * H + h) * Dv;
     const u16 *og = reinterpret_cast<const u16 *>(ba.dout) + rowv0;
 
+    u16 *dOc = reinterpret_cast<u16 *>(smem + S::OFF_DO);
     // ---- phase 0 ----
+    // LDS-direct loads of K, Q, dO first, then this wave's register loads;
+    // the wait below (at most NREG outstanding) then covers the LDS-direct ones
+    constexpr int NREG = 2 * NTT + 6 + 16;      // R, dX; T' fragments; S, dS' fragments
+    floatx4 rr[NTT], xr[NTT];
+    bf16x8 tf[NTT][2];
+    floatx4 sf[4][2], df[4][2];
+    const int f0 = 16 * w;
     {
-        constexpr int NDK = S::SZ_KC / 1024;
+        constexpr int NDK = S::SZ_KC / 1024, NDO = S::SZ_V / 1024;
         const u16 *kg = reinterpret_cast<const u16 *>(args.k) + rowk0;
         const u16 *qg = reinterpret_cast<const u16 *>(args.q) + rowk0;
 #pragma unroll
-        for (int k = w; k < 2 * NDK; k += S::NW) {
-            const int kk = k % NDK, pos = kk * 64 + l, r = pos / NKC, sc = pos % NKC;
-            const int t = t0 + r, pc = sc ^ kswz<NKC>(r);
-            const u16 *src = (k < NDK ? kg : qg) + (size_t)t * tokk + (pc << 3);
-            dma16(t < T ? static_cast<const void *>(src) : static_cast<const void *>(&kZero16),
-                  (k < NDK ? Kc : Qc) + kk * 512);
+        for (int k = w; k < 2 * NDK + NDO; k += S::NW) {
+            if (k < 2 * NDK) {
+                const int kk = k % NDK, pos = kk * 64 + l, r = pos / NKC, sc = pos % NKC;
+                const int t = t0 + r, pc = sc ^ kswz<NKC>(r);
+                const u16 *src = (k < NDK ? kg : qg) + (size_t)t * tokk + (pc << 3);
+                dma16(t < T ? static_cast<const void *>(src) : static_cast<const void *>(&kZero16),
+                      (k < NDK ? Kc : Qc) + kk * 512);
+            } else {
+                const int kk = k - 2 * NDK, pos = kk * 64 + l, r = pos / NPV, sc = pos % NPV;
+                const int t = t0 + r, pc = sc ^ kswz<NPV>(r);
+                dma16(t < T && pc * 8 < Dv ? static_cast<const void *>(og + (size_t)t * tokv + (pc << 3))
+                                           : static_cast<const void *>(&kZero16),
+                      dOc + kk * 512);
+            }
         }
+        asm volatile("" ::: "memory");
+        // phase 1 operands (value slice w; a valid slice for waves past the last)
+        const int ws = w < nvs ? w : 0;
+        const size_t so = ((((size_t)bh * NT + c) * nvs + ws) * 64 + l) * NTT;
+        const floatx4 *rp = reinterpret_cast<const floatx4 *>(args.rst) + so;
+        const floatx4 *xp = reinterpret_cast<const floatx4 *>(ba.dxst) + so;
+        const u16 *tg = reinterpret_cast<const u16 *>(args.tmat) + ((size_t)bh * NT + c) * C * C;
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) {
+            rr[tt] = rp[tt];
+            xr[tt] = xp[tt];
+        }
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                if (2 * m <= tt) tf[tt][m] = ld8(tg + (tt * 16 + c16) * C + (4 * m + g) * 8);
+        // phase 3 operands: S and dS' as B operands (lane (g, j): row f0 + j,
+        // value columns 32 mv + 8 g .. +7)
+        const size_t sbase = (((size_t)bh * NT + c) * KD + (w < nfs ? f0 : 0) + c16) * Dv + 8 * g;
+#pragma unroll
+        for (int mv = 0; mv < 4; ++mv)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const size_t o = sbase + (mv < nmv ? 32 * mv + 4 * hh : 0);
+                sf[mv][hh] = *reinterpret_cast<const floatx4 *>(args.sst + o);
+                df[mv][hh] = *reinterpret_cast<const floatx4 *>(ba.dsst + o);
+            }
         // M1, M2 (all four arrays, 32 KiB) and the per-tile partial slots cleared
         {
             uint4 *z = reinterpret_cast<uint4 *>(smem + S::OFF_M1H);
@@ -608,42 +670,18 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
             G2[l] = gs * LOG2E;
             Bt[l] = ok ? args.beta[gi] : 0.f;
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): the staging is in LDS
-        __syncthreads();
-    }
-    // S and dS' fragments of phase 3 (B operands: lane (g, j) holds row f0 + j,
-    // value columns 32 mv + 8 g .. +7), loaded now so their latency overlaps
-    // phases 1 and 2
-    floatx4 sf[4][2], df[4][2];
-    const int f0 = 16 * w;
-    if (w < nfs) {
-        const size_t so = (((size_t)bh * NT + c) * KD + f0 + c16) * Dv + 8 * g;
-#pragma unroll
-        for (int mv = 0; mv < 4; ++mv)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const size_t o = so + (mv < nmv ? 32 * mv + 4 * hh : 0);
-                sf[mv][hh] = *reinterpret_cast<const floatx4 *>(args.sst + o);
-                df[mv][hh] = *reinterpret_cast<const floatx4 *>(ba.dsst + o);
-            }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((NREG & 15) | ((NREG >> 4) << 14) | 0x0070);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     }
 
     // ---- phase 1: value slice w ----
     if (w < nvs) {
         const int v0 = 16 * w;
-        const size_t so = ((((size_t)bh * NT + c) * nvs + w) * 64 + l) * NTT;
-        const floatx4 *rp = reinterpret_cast<const floatx4 *>(args.rst) + so;
-        const floatx4 *xp = reinterpret_cast<const floatx4 *>(ba.dxst) + so;
-        const u16 *tg = reinterpret_cast<const u16 *>(args.tmat) + ((size_t)bh * NT + c) * C * C;
-        floatx4 rr[NTT], xr[NTT], bt[NTT];
-        bf16x8 tf[NTT][2];
+        floatx4 bt[NTT];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
-            rr[tt] = rp[tt];
-            xr[tt] = xp[tt];
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-                if (2 * m <= tt) tf[tt][m] = ld8(tg + (tt * 16 + c16) * C + (4 * m + g) * 8);
             bt[tt] = *reinterpret_cast<const floatx4 *>(Bt + tt * 16 + 4 * g);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -692,14 +730,11 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
         const int ra = ti * 16 + c16, rb = tj * 16 + c16;   // this lane's A and B operand rows
         floatx4 x = zero4(), y = zero4();
         if (kind == 0) {
-            // x = dO Vn^T (dO rows from global, zero past T), y = Q K^T
-            const int t = t0 + ra;
-            const u16 *op = og + (size_t)(t < T ? t : 0) * tokv + 8 * g;
+            // x = dO Vn^T, y = Q K^T
 #pragma unroll
             for (int mv = 0; mv < 4; ++mv)
                 if (mv < nmv) {
-                    bf16x8 oa = ld8(op + 32 * mv);
-                    if (t >= T) oa = bf16x8{};
+                    const bf16x8 oa = row_frag<NPV>(dOc, ra, 32 * mv);
                     x = mfma32(oa, row_frag<NPV>(Vh, rb, 32 * mv), x);
                     x = mfma32(oa, row_frag<NPV>(Vl, rb, 32 * mv), x);
                 }
@@ -774,6 +809,13 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
         for (int off = 1; off < 64; off <<= 1) sdot += __shfl_xor(sdot, off, 64);
         if (l == 0) ss[w] = sdot;
         const float g2L = G2[C - 1];
+        // K and Q as B operands (k = token, n = feature f0 + j), both 32-token steps
+        bf16x8 kb[2], qb[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            kb[m] = tr_frag<NKC>(Kc, 32 * m + 8 * g, f0);
+            qb[m] = tr_frag<NKC>(Qc, 32 * m + 8 * g, f0);
+        }
         float *dqp = ba.dq + rowk0 + f0 + c16;
         float *dkp = ba.dk + rowk0 + f0 + c16;
 #pragma unroll
@@ -781,43 +823,34 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
             const int ra = tt * 16 + c16;       // this lane's A operand row
             // dQ: a = dO S^T, bq = M1 K
             floatx4 a = zero4(), bq = zero4();
-            {
-                const int t = t0 + ra;
-                const u16 *op = og + (size_t)(t < T ? t : 0) * tokv + 8 * g;
 #pragma unroll
-                for (int mv = 0; mv < 4; ++mv)
-                    if (mv < nmv) {
-                        bf16x8 oa = ld8(op + 32 * mv);
-                        if (t >= T) oa = bf16x8{};
-                        a = mfma32(oa, sh[mv], a);
-                        a = mfma32(oa, sl[mv], a);
-                    }
-            }
+            for (int mv = 0; mv < 4; ++mv)
+                if (mv < nmv) {
+                    const bf16x8 oa = row_frag<NPV>(dOc, ra, 32 * mv);
+                    a = mfma32(oa, sh[mv], a);
+                    a = mfma32(oa, sl[mv], a);
+                }
 #pragma unroll
             for (int m = 0; m < 2; ++m)
                 if (m <= tt / 2) {
-                    const bf16x8 kb = tr_frag<NKC>(Kc, 32 * m + 8 * g, f0);
-                    bq = mfma32(row_frag<NPM>(M1h, ra, 32 * m), kb, bq);
-                    bq = mfma32(row_frag<NPM>(M1l, ra, 32 * m), kb, bq);
+                    bq = mfma32(row_frag<NPM>(M1h, ra, 32 * m), kb[m], bq);
+                    bq = mfma32(row_frag<NPM>(M1l, ra, 32 * m), kb[m], bq);
                 }
             // dK: c1 = M1^T Q + M2^T K + M2 K, d1 = dX S^T, d2 = Vn dS'^T
             floatx4 c1 = zero4(), d1 = zero4(), d2 = zero4();
 #pragma unroll
             for (int m = 0; m < 2; ++m)
                 if (m >= tt / 2) {
-                    const bf16x8 qb = tr_frag<NKC>(Qc, 32 * m + 8 * g, f0);
-                    const bf16x8 kb = tr_frag<NKC>(Kc, 32 * m + 8 * g, f0);
-                    c1 = mfma32(tr_frag<NPM>(M1h, 32 * m + 8 * g, tt * 16), qb, c1);
-                    c1 = mfma32(tr_frag<NPM>(M1l, 32 * m + 8 * g, tt * 16), qb, c1);
-                    c1 = mfma32(tr_frag<NPM>(M2h, 32 * m + 8 * g, tt * 16), kb, c1);
-                    c1 = mfma32(tr_frag<NPM>(M2l, 32 * m + 8 * g, tt * 16), kb, c1);
+                    c1 = mfma32(tr_frag<NPM>(M1h, 32 * m + 8 * g, tt * 16), qb[m], c1);
+                    c1 = mfma32(tr_frag<NPM>(M1l, 32 * m + 8 * g, tt * 16), qb[m], c1);
+                    c1 = mfma32(tr_frag<NPM>(M2h, 32 * m + 8 * g, tt * 16), kb[m], c1);
+                    c1 = mfma32(tr_frag<NPM>(M2l, 32 * m + 8 * g, tt * 16), kb[m], c1);
                 }
 #pragma unroll
             for (int m = 0; m < 2; ++m)
                 if (m <= tt / 2) {
-                    const bf16x8 kb = tr_frag<NKC>(Kc, 32 * m + 8 * g, f0);
-                    c1 = mfma32(row_frag<NPM>(M2h, ra, 32 * m), kb, c1);
-                    c1 = mfma32(row_frag<NPM>(M2l, ra, 32 * m), kb, c1);
+                    c1 = mfma32(row_frag<NPM>(M2h, ra, 32 * m), kb[m], c1);
+                    c1 = mfma32(row_frag<NPM>(M2l, ra, 32 * m), kb[m], c1);
                 }
 #pragma unroll
             for (int mv = 0; mv < 4; ++mv)

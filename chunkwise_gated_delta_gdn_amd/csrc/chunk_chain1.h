@@ -49,9 +49,10 @@
 //   DPM = 2: the pass on sub-key 1 with v' (fp32, read by the chain wave) as
 //            the values; its output adds the first pass's.
 //
-// DPM = 3 is the state pass of the backward: no output; the chain wave
-// writes every chunk's start state S (row-major, fp32) and its residual
-// R = V - e^G K S (this lane's 16 values, accumulator order) instead.
+// DPM = 3 is the state pass of the backward: no output; every chunk's start
+// state S goes out row-major (fp32; waves 1 and 2 copy the published state,
+// half of the key rows each) and the chain wave writes the residual
+// R = V - e^G K S (this lane's 16 values, accumulator order).
 #pragma once
 
 #include <type_traits>
@@ -237,13 +238,6 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
         for (int c = 0, sq = 0; c < NT; ++c, sq = sq == 2 ? 0 : sq + 1) {
             const int p = c & 1;                 // St, Vn; staging buffers: sq = c % 3
             const u16 *ks = Ks(sq), *tb = Tb(sq), *bv = BVs(sq);
-            if constexpr (DPM == 3) {            // the chunk-start state, row-major
-                float *sp = args.sst + ((size_t)bh * NT + c) * args.kw * Dv + v0 + c16;
-#pragma unroll
-                for (int ti = 0; ti < NST; ++ti)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sp[(size_t)feat(ti, e) * Dv] = Sreg[ti][e];
-            }
             const float *gp = gate(sq);
             // LDS operands of K S first (nothing here depends on the state), so
             // their latency overlaps; the MFMAs run over the token tiles
@@ -365,7 +359,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
             }
             // S_start of chunk c goes out while the state MFMAs run (its LDS
             // writes then do not queue ahead of this chunk's operand reads)
-            if constexpr (DPM != 3) publish_state(p);
+            publish_state(p);
             if constexpr (DPM == 1) {
                 // (issued after the state update's MFMAs: off the chain's path)
                 // per-token errors e = R - A~ V_new and v' = (1 - m) v + m e;
@@ -622,8 +616,34 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
     }
     using std::integral_constant;
     using none = integral_constant<int, -1>;
-    if constexpr (DPM == 3) {                   // no output: waves 1 and 2 take part in the barriers only
-        if (w == 1 || w == 2) out_wave(none{}, none{}, none{});
+    if constexpr (DPM == 3) {
+        // no output: waves 1 and 2 write the published chunk-start states of
+        // the previous iteration to the work space, row-major, key rows
+        // [0, KD/2) and [KD/2, KD): lane l takes row 16 i + l/4, value columns
+        // 4 (l%4) .. +3 (one 16-byte store)
+        if (w == 1 || w == 2) {
+            const int f0 = (w - 1) * (KD / 2);
+            auto store_state = [&](int c) {
+                const float *sf = St(c & 1);
+#pragma unroll
+                for (int i = 0; i < KD / 32; ++i) {
+                    const int f = f0 + 16 * i + (l >> 2), v4 = 4 * (l & 3);
+                    floatx4 x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = sf[(v4 + e) * LDSF + f];
+                    if (f < kw)
+                        *reinterpret_cast<floatx4 *>(args.sst + (((size_t)bh * NT + c) * kw + f) * args.Dv + v0 + v4) = x;
+                }
+            };
+            __syncthreads();
+            lds_barrier();
+            for (int c = 1; c < NT; ++c) {
+                store_state(c - 1);
+                lds_barrier();
+            }
+            store_state(NT - 1);
+            __syncthreads();
+        }
         if (w == 3) out_wave(none{}, none{}, integral_constant<int, 0>{});
         if (w == 5) out_wave(none{}, none{}, integral_constant<int, 1>{});
     } else if constexpr (NTT == 4) {
