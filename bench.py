@@ -39,6 +39,10 @@ CAMERA_SOURCES = ("chunkwise_gated_delta_gdn_amd/csrc/prep.hip",
                   "chunkwise_gated_delta_gdn_amd/csrc/frame_scan.hip",
                   "chunkwise_gated_delta_gdn_amd/csrc/gdn_common.h")
 BWD_SOURCES = ("chunkwise_gated_delta_gdn_amd/csrc/gdn_bwd.hip",
+               "chunkwise_gated_delta_gdn_amd/csrc/chunk_bwd.h",
+               "chunkwise_gated_delta_gdn_amd/csrc/chunk_bwd.hip",
+               "chunkwise_gated_delta_gdn_amd/csrc/chunk_chain1.h",
+               "chunkwise_gated_delta_gdn_amd/csrc/chunk_prep2.h",
                "chunkwise_gated_delta_gdn_amd/csrc/gdn_common.h")
 # workload -> (rocprofv3 HBM counter record, kernel sources it was taken on)
 TRAFFIC = {
@@ -168,7 +172,8 @@ def _prepare(name, dev):
     workload's hot path once through the C ABI."""
     import torch
     from chunkwise_gated_delta_gdn_amd import gdn, inputs
-    base = {"camera_reverse": "camera", "camera_den": "camera", "gdn_bwd": "gdn"}.get(name, name)  # same inputs
+    base = {"camera_reverse": "camera", "camera_den": "camera", "camera_bwd": "camera",
+            "gdn_bwd": "gdn"}.get(name, name)  # same inputs
     wl = inputs.WORKLOADS[base]
     d = inputs.workload_inputs(base)
     bf = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
@@ -215,6 +220,27 @@ def _prepare(name, dev):
         per_chunk = 2 * (r * C * C * dk * 2 + NR * NR * (K + Dv) + 2 * NR * K * Dv + C * K * Dv) + 2 * NR ** 3 / 3
         flops = B * H * (T // C) * per_chunk
         return d, step, B * T, nbytes, flops
+    if name == "camera_bwd":
+        # gradients of the camera scan (forward direction) on the GPU prep's
+        # outputs (formed once, outside the timed steps) under seeded dout
+        import numpy as np
+        t = {n: f32(d[n]) for n in ("q_norm_w", "k_norm_w", "proj_q", "proj_kv", "rope_cos", "rope_sin",
+                                    "beta", "g")}
+        pr = gdn.gdn_prep(bf(d["qkv"]), t["q_norm_w"], t["k_norm_w"], t["proj_q"], t["proj_kv"], t["rope_cos"],
+                          t["rope_sin"], d["k_scale"], d["eps"])
+        rng = np.random.default_rng(20263 + 7)
+        dout = bf(inputs.cast(rng.standard_normal(tuple(pr["q"].shape)), "bf16"))
+
+        def step():
+            return gdn.gdn_recurrent_bwd(pr["q"], pr["k"], pr["v"], t["beta"], t["g"], dout, wl["F"], 1.0)
+        B, F, S, H, D = wl["B"], wl["F"], wl["S"], wl["H"], wl["D"]
+        N = F * S
+        # read q, k, v, dout (bf16), beta, g; write dq, dk, dv (fp32), dbeta, dg, dh0
+        nbytes = B * H * N * (4 * D * 2 + 4 + 3 * D * 4 + 4) + B * H * F * 8 + B * H * D * D * 4
+        # per token: the forward's G and H (4 D^2), A (2 D^2), u and r (4 D^2),
+        # dk (4 D^2), dq (2 D^2)
+        flops = B * H * N * 16 * D * D
+        return d, step, B * N, nbytes, flops
     # camera: prep, then the frame-synchronous scan on its outputs (the
     # anti-causal direction for camera_reverse)
     reverse = name == "camera_reverse"
@@ -260,7 +286,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="gdn", choices=("gdn", "gdn_long", "deltaproduct", "camera", "camera_reverse", "camera_den",
-                             "gdn_bwd"),
+                             "gdn_bwd", "camera_bwd"),
                     help="gdn is the headline workload; the others time the other operations")
     ap.add_argument("--copy-probe", action="store_true", help="run only the copy calibration kernel")
     args = ap.parse_args()
@@ -297,14 +323,22 @@ def main():
     kernel_ms = float(np.mean(kern_ms))
     achieved_gbs = nbytes / (kernel_ms * 1e-3) / 1e9
     from chunkwise_gated_delta_gdn_amd import inputs
-    wl = inputs.WORKLOADS[{"camera_reverse": "camera", "camera_den": "camera",
+    wl = inputs.WORKLOADS[{"camera_reverse": "camera", "camera_den": "camera", "camera_bwd": "camera",
                            "gdn_bwd": "gdn"}.get(args.workload, args.workload)]
     if args.workload == "gdn_bwd":
         metric = "tokens/sec of gated-delta backward (B*T/s) at H=16, D=128"
         desc = (f"gdn_bwd: gradients of the gdn workload (B={wl['B']} H={wl['H']} T={wl['T']} "
                 f"Dk=Dv={wl['Dk']}), bf16 q/k/v/dout, fp32 gradients, no dhT")
-        kernel = "gdn_bwd = bwd_scan_kernel<bf16, 128> + bwd_reduce_kernel<128>"
+        kernel = ("gdn_bwd = chunk_prep2_kernel<128, 64, bwd> + chunk_chain1_kernel<128, 64, 3> (forward states) "
+                  "+ chunk_bchain_kernel<128> (reverse state pass) + chunk_bgrad_kernel<128> (per-chunk gradients)")
         traffic = measured_traffic(args.workload)
+    elif args.workload == "camera_bwd":
+        metric = "tokens/sec of camera scan backward (B*N/s)"
+        desc = ("camera_bwd: gradients of the camera workload's scan (B=1 F=8 S=30x52 H=16 D=64) on the GPU "
+                "prep's bf16 outputs, bf16 dout, fp32 gradients, no dhT")
+        kernel = ("gdn_recurrent_bwd = frame_gram_bf16_kernel (G, H; A) + frame_reduce_kernel + frame_state_kernel "
+                  "+ frame_bstate_kernel + frame_bgrad_kernel")
+        traffic = None
     elif args.workload in ("gdn", "gdn_long"):
         metric = "tokens/sec of chunkwise gated-delta fwd (B*T/s) at H=16, D=128"
         desc = (f"{args.workload}: B={wl['B']} H={wl['H']} T={wl['T']} Dk=Dv={wl['Dk']} chunk={wl['chunk']}, "

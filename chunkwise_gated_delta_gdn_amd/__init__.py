@@ -7,7 +7,8 @@ seeded synthetic input generator.  The binding functions are re-exported
 here on first use.
 """
 
-_BINDING = ("gdn_chunk_fwd", "deltaproduct_chunk_fwd", "gdn_recurrent_fwd", "gdn_prep")
+_BINDING = ("gdn_chunk_fwd", "deltaproduct_chunk_fwd", "gdn_recurrent_fwd", "gdn_recurrent_den_fwd", "gdn_prep",
+            "gdn_bwd", "gdn_recurrent_bwd")
 
 
 def __getattr__(name):

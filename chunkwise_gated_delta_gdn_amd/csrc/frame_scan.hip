@@ -192,11 +192,14 @@ constexpr int gram_round(int D) { return (D == 128 ? 1 : 2) * TSG; }
 template <int D>
 constexpr int gram_waves() { return D >= 32 ? 8 : 4; }
 
-template <int D, bool VONES>
+// CROSS (the scan's backward): only the second product, with the constant
+// weight `scale` for beta: K^T V * scale (called with q for k and dout for v:
+// A_f = scale Q_f^T dO_f), one D x D matrix per partial.
+template <int D, bool VONES, bool CROSS = false>
 __global__ __launch_bounds__(512) void frame_gram_bf16_kernel(FrameArgs a) {
     constexpr int NW = gram_waves<D>(), NTH = 64 * NW;   // waves, threads
     constexpr int NT1 = D / 16;                 // row tiles = column tiles of one matrix
-    constexpr int NJOB = 2 * NT1, JPW = (NJOB + NW - 1) / NW;
+    constexpr int NJOB = (CROSS ? 1 : 2) * NT1, JPW = (NJOB + NW - 1) / NW;
     // Rows are unpadded; the 16-byte piece p of row r sits at p ^ swz(r), so
     // that the 8 rows x 32 bytes that 32 lanes of a transposed read take
     // (rows 8g + {0..3} of two lane groups) cover all 64 banks once.
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(512) void frame_gram_bf16_kernel(FrameArgs a) {
                 }
             }
             const int s = s0 + (tid & (TSG - 1));
-            const float bt = a.beta[row0 + min(s, s_hi - 1)];
+            const float bt = CROSS ? a.scale : a.beta[row0 + min(s, s_hi - 1)];
             st.b[u] = s < s_hi ? bt : 0.f;
         }
     };
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(512) void frame_gram_bf16_kernel(FrameArgs a) {
                 const int job = w + NW * jb;
                 if (job < NJOB) {
                     const int tj = job % NT1;
-                    const u16 *src = job < NT1 ? ks : vs;
+                    const u16 *src = job < NT1 && !CROSS ? ks : vs;
                     uint2 x0, x1;
                     if (VONES && job >= NT1) {
                         x0 = x1 = uint2{0x3F803F80u, 0x3F803F80u};      // bf16 ones
@@ -338,12 +341,12 @@ __global__ __launch_bounds__(512) void frame_gram_bf16_kernel(FrameArgs a) {
         if (rnd + 1 < nrnd) consume(sb, SPW);
     }
     lds_barrier();
-    float *dst = a.part + ((size_t)unit * a.nsplit + sp) * 2 * D * D;
+    float *dst = a.part + ((size_t)unit * a.nsplit + sp) * (CROSS ? 1 : 2) * D * D;
 #pragma unroll
     for (int jb = 0; jb < JPW; ++jb) {
         const int job = w + NW * jb;
         if (job < NJOB) {
-            const int kind = job / NT1, tj = job % NT1;
+            const int kind = CROSS ? 0 : job / NT1, tj = job % NT1;
 #pragma unroll
             for (int ti = 0; ti < NT1; ++ti)
 #pragma unroll
@@ -874,6 +877,440 @@ int frame_entry(const char *name, const void *q, const void *k, const void *v, c
     return check_hip(e, name);
 }
 
+// ===========================================================================
+// Backward of the frame-synchronous scan (reverse mode through the frame
+// steps).  With S_f = (I - G_f) P_f + H_f, P_f = e^{g_f} S_{f-1} and
+// out_s = scale S_f^T q_s (s in frame f), let X_f = dL/dS_f including the
+// read-out of frame f: X_f = dS_f + A_f with A_f = scale Q_f^T dO_f and dS_f
+// the gradient carried back from frame f + 1 (dhT after the last frame).
+// Every token of frame f predicts from P_f, so the prediction terms of the
+// frame sum to G_f X_f, and
+//   X_{f-1} = e^{g_f} (I - G_f) X_f + A_{f-1},   dh0 = e^{g_0} (I - G_0) X_0,
+//   dg_f = <(I - G_f) X_f, P_f>,
+// and per token s of frame f, with u_s = X_f^T k_s and r_s = v_s - P_f^T k_s:
+//   dq_s = scale S_f do_s,  dv_s = beta_s u_s,  dbeta_s = u_s . r_s,
+//   dk_s = beta_s (X_f r_s - P_f u_s).
+// Kernels: the forward's gram and state passes (G_f, S_f), the gram kernel
+// in CROSS mode (A_f), frame_bstate_kernel (X_f, dg partials, dh0) and
+// frame_bgrad_kernel (token gradients, dg).
+// ===========================================================================
+struct FrameBwdArgs {
+    FrameArgs a;             // q, k, v, beta, g, h0, scale; gh (G_f), sf (S_f), nsplit, spl
+    const void *dout;        // (B, H, N, D) as q
+    const float *dhT;        // (B, H, D, D) or null
+    const float *apart;      // [B*H*F][nsplit][D][D] partial A_f
+    float *xf;               // [B*H][F][D][D] X_f, transposed ([column][row])
+    float *dgp;              // [B*H][F][D/16] gate gradient by state column slice
+    float *dq, *dk, *dv, *dbeta, *dg, *dh0;
+};
+
+// X_f backwards over the frames, per (b, h, 16-column slice of X), fp32 MFMA
+// (the frame state pass's form).  Stores every X_f (transposed, as the
+// forward stores S_f), the slice's share of dg_f, and dh0.
+template <int D>
+__global__ __launch_bounds__(256) void frame_bstate_kernel(FrameBwdArgs ba) {
+    constexpr int LDG = D + 4, LDS_ = 16 + 4;
+    constexpr int NRT = D / 16, PERW = (NRT + 3) / 4;
+    __shared__ __attribute__((aligned(16))) float Gs[D * LDG], Xl[D * LDS_];
+    __shared__ float red[4];
+    const FrameArgs &a = ba.a;
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    constexpr int ncb = D / 16;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int bh = (slot / ncb) * 8 + xcd, cb = slot % ncb, j0 = cb * 16;
+    if (bh >= a.B * a.H) return;
+    const int col = j0 + (l & 15);
+    auto row_of = [&](int ti, int e) { return ti * 16 + 4 * (l >> 4) + e; };
+
+    floatx4 X[PERW];
+#pragma unroll
+    for (int n = 0; n < PERW; ++n) {
+        X[n] = zero4();
+        const int ti = w + 4 * n;
+        if (ti < NRT && ba.dhT)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) X[n][e] = ba.dhT[((size_t)bh * D + row_of(ti, e)) * D + col];
+    }
+    for (int f = a.F - 1; f >= 0; --f) {
+        const size_t unit = (size_t)bh * a.F + f;
+        // G_f into LDS; X += A_f (sum of the token-range partials)
+        const floatx4 *gsrc = reinterpret_cast<const floatx4 *>(a.gh + unit * 2 * D * D);
+        for (int idx = tid; idx < D * D / 4; idx += 256) {
+            const int r = (idx * 4) / D, c = (idx * 4) % D;
+            *reinterpret_cast<floatx4 *>(Gs + r * LDG + c) = gsrc[idx];
+        }
+#pragma unroll
+        for (int n = 0; n < PERW; ++n) {
+            const int ti = w + 4 * n;
+            if (ti < NRT)
+                for (int sp = 0; sp < a.nsplit; ++sp) {
+                    const float *ap = ba.apart + (unit * a.nsplit + sp) * D * D;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) X[n][e] += ap[row_of(ti, e) * D + col];
+                }
+        }
+        // X_f out (transposed) and into LDS as the B operand
+#pragma unroll
+        for (int n = 0; n < PERW; ++n) {
+            const int ti = w + 4 * n;
+            if (ti < NRT) {
+                *reinterpret_cast<float4 *>(ba.xf + (unit * D + col) * D + ti * 16 + 4 * (l >> 4)) =
+                    float4{X[n][0], X[n][1], X[n][2], X[n][3]};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Xl[row_of(ti, e) * LDS_ + (l & 15)] = X[n][e];
+            }
+        }
+        __syncthreads();
+        const float dec = expf(a.g[unit]);
+        // P_f = e^{g_f} S_{f-1}: the stored S_{f-1} (transposed), or h0 for f = 0
+        float part = 0.f;
+#pragma unroll
+        for (int n = 0; n < PERW; ++n) {
+            const int ti = w + 4 * n;
+            if (ti < NRT) {
+                floatx4 gx = zero4();
+                mma_f32_bn(gx, Gs + ti * 16 * LDG, LDG, Xl, LDS_, D);
+                floatx4 pv = zero4();
+                if (f > 0) {
+                    const float4 x = *reinterpret_cast<const float4 *>(a.sf + ((unit - 1) * D + col) * D + ti * 16 +
+                                                                       4 * (l >> 4));
+                    pv = floatx4{x.x, x.y, x.z, x.w};
+                } else if (a.h0) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pv[e] = a.h0[((size_t)bh * D + row_of(ti, e)) * D + col];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float y = X[n][e] - gx[e];
+                    part += y * pv[e];
+                    X[n][e] = dec * y;
+                }
+            }
+        }
+        // dg_f share of this slice: dec * sum (I - G_f) X_f o S_{f-1}
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) part += __shfl_xor(part, off, 64);
+        if (l == 0) red[w] = part;
+        __syncthreads();
+        if (tid == 0) ba.dgp[unit * ncb + cb] = dec * (((red[0] + red[1]) + red[2]) + red[3]);
+    }
+    if (ba.dh0) {
+#pragma unroll
+        for (int n = 0; n < PERW; ++n) {
+            const int ti = w + 4 * n;
+            if (ti < NRT)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ba.dh0[((size_t)bh * D + row_of(ti, e)) * D + col] = X[n][e];
+        }
+    }
+}
+
+// Token gradients of one frame, 512 tokens per workgroup (8 waves x 4 tiles
+// of 16), bf16 inputs, D >= 32.  Products are taken transposed so each lane
+// holds 4 consecutive features of one token (16-byte stores):
+//   u^T = X_f^T K^T,  r^T = V^T - P_f^T K^T           (A: X^T, P^T rows)
+//   dk^T = beta (X_f r^T - P_f u^T)                    (A: X, P rows, read
+//                                                      transposed; B: r^T, u^T
+//                                                      from the accumulators,
+//                                                      permuted k order)
+//   dq^T = scale S_f dO^T                              (A: S rows, read transposed)
+// X^T, P^T (then S^T) are staged in LDS as hi/lo bf16 from the stored
+// transposes.  The workgroup of each frame's first block also adds the dg
+// shares of the state slices.
+constexpr int BG_WAVES = 8, BG_TOK = BG_WAVES * 64;
+
+template <int D>
+__global__ __launch_bounds__(64 * BG_WAVES) void frame_bgrad_kernel(FrameBwdArgs ba) {
+    constexpr int NT1 = D / 16, NK = D / 32, LDT = D + 8, SUB = 4;
+    static_assert(D >= 32, "32-deep k steps");
+    __shared__ __attribute__((aligned(16))) u16 AH[D * LDT], AL[D * LDT], BH[D * LDT], BL[D * LDT];
+    const FrameArgs &a = ba.a;
+    const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ntt = (a.S + BG_TOK - 1) / BG_TOK;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int unit = (slot / ntt) * 8 + xcd, tb = slot % ntt;
+    if (unit >= a.B * a.H * a.F) return;
+    const int bh = unit / a.F, f = unit % a.F;
+    const size_t N = (size_t)a.F * a.S;
+    const size_t row0 = (size_t)bh * N + (size_t)f * a.S;
+    const int t0 = tb * BG_TOK + w * (SUB * 16);
+    const u16 *kin = reinterpret_cast<const u16 *>(a.k), *vin = reinterpret_cast<const u16 *>(a.v);
+    const u16 *oin = reinterpret_cast<const u16 *>(ba.dout);
+    const float dec = expf(a.g[unit]);
+    if (tb == 0 && tid == 0) {
+        float s = 0.f;
+        for (int cb = 0; cb < NT1; ++cb) s += ba.dgp[(size_t)unit * NT1 + cb];
+        ba.dg[unit] = s;
+    }
+    // stage a transposed D x D matrix (src[r][c], r = column of the state)
+    // times `mul` as hi/lo bf16 rows
+    auto stage = [&](u16 *hi, u16 *lo, const float *src, float mul) {
+        const float4 *p = reinterpret_cast<const float4 *>(src);
+        for (int idx = tid; idx < D * D / 4; idx += 64 * BG_WAVES) {
+            const float4 x = p[idx];
+            const int r = (idx * 4) / D, c = (idx * 4) % D;
+            uint2 h, o;
+            split2_bf16(mul * x.x, mul * x.y, h.x, o.x);
+            split2_bf16(mul * x.z, mul * x.w, h.y, o.y);
+            *reinterpret_cast<uint2 *>(hi + r * LDT + c) = h;
+            *reinterpret_cast<uint2 *>(lo + r * LDT + c) = o;
+        }
+    };
+    stage(AH, AL, ba.xf + (size_t)unit * D * D, 1.f);            // X_f^T
+    if (f > 0) {
+        stage(BH, BL, a.sf + (size_t)(unit - 1) * D * D, dec);   // P_f^T = e^{g_f} S_{f-1}^T
+    } else {
+        for (int idx = tid; idx < D * D; idx += 64 * BG_WAVES) {
+            const int r = idx / D, c = idx % D;                  // P^T[r][c] = e^{g} h0[c][r]
+            const float x = a.h0 ? dec * a.h0[((size_t)bh * D + c) * D + r] : 0.f;
+            u16 h, o;
+            split_bf16(x, h, o);
+            BH[r * LDT + c] = h;
+            BL[r * LDT + c] = o;
+        }
+    }
+    // B operand fragments of this wave's tokens (lane (g, c16): token c16 of
+    // tile u, features 32 kk + 8 g .. +7): k, and dO in the dq phase
+    auto row_frag8 = [&](const u16 *in, int t, int kk) {
+        uint4 x = uint4{0u, 0u, 0u, 0u};
+        if (t < a.S) x = *reinterpret_cast<const uint4 *>(in + (row0 + t) * D + kk * 32 + 8 * g);
+        return __builtin_bit_cast(bf16x8, x);
+    };
+    __syncthreads();
+    // A operand of rows i of a matrix M whose transpose is staged (M^T[j][i]):
+    // lane (g, c16) gets M[i0 + c16][j] for j = r0 .. r0+3 and r1 .. r1+3
+    auto tr_a = [&](const u16 *mt, int r0, int r1, int i0) {
+        const uint2 x0 = __builtin_bit_cast(uint2, ld_tr16(mt + (r0 + (c16 >> 2)) * LDT + i0 + 4 * (c16 & 3)));
+        const uint2 x1 = __builtin_bit_cast(uint2, ld_tr16(mt + (r1 + (c16 >> 2)) * LDT + i0 + 4 * (c16 & 3)));
+        return __builtin_bit_cast(bf16x8, uint4{x0.x, x0.y, x1.x, x1.y});
+    };
+#pragma unroll 1
+    for (int u = 0; u < SUB; ++u) {
+        // (the staged operands are read again for every tile: a compiler fence
+        // keeps their loads from being hoisted out of the loop into registers)
+        asm volatile("" ::: "memory");
+        const int t = t0 + u * 16 + c16;        // this lane's token (B operand column)
+        bf16x8 bk[NK];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) bk[kk] = row_frag8(kin, t, kk);
+        const float bt = t < a.S ? a.beta[row0 + t] : 0.f;
+        // u^T and r^T tiles (rows j = jt*16 + 4g + e, column token c16)
+        floatx4 ut[NT1], rt[NT1];
+#pragma unroll
+        for (int jt = 0; jt < NT1; ++jt) {
+            floatx4 ua = zero4(), pa = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const int o = (jt * 16 + c16) * LDT + kk * 32 + 8 * g;
+                ua = mfma32(ld8(AH + o), bk[kk], ua);
+                ua = mfma32(ld8(AL + o), bk[kk], ua);
+                pa = mfma32(ld8(BH + o), bk[kk], pa);
+                pa = mfma32(ld8(BL + o), bk[kk], pa);
+            }
+            uint2 vr = uint2{0u, 0u};
+            if (t < a.S) vr = *reinterpret_cast<const uint2 *>(vin + (row0 + t) * D + jt * 16 + 4 * g);
+            const floatx4 vv = floatx4{__builtin_bit_cast(float, vr.x << 16), __builtin_bit_cast(float, vr.x & 0xffff0000u),
+                                       __builtin_bit_cast(float, vr.y << 16), __builtin_bit_cast(float, vr.y & 0xffff0000u)};
+            ut[jt] = ua;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rt[jt][e] = vv[e] - pa[e];
+        }
+        // dv = beta u, dbeta = u . r
+        float db = 0.f;
+#pragma unroll
+        for (int jt = 0; jt < NT1; ++jt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) db += ut[jt][e] * rt[jt][e];
+            if (t < a.S)
+                *reinterpret_cast<float4 *>(ba.dv + (row0 + t) * D + jt * 16 + 4 * g) =
+                    float4{bt * ut[jt][0], bt * ut[jt][1], bt * ut[jt][2], bt * ut[jt][3]};
+        }
+        db += __shfl_xor(db, 16, 64);
+        db += __shfl_xor(db, 32, 64);
+        if (g == 0 && t < a.S) ba.dbeta[row0 + t] = db;
+        // dk^T = beta (X r^T - P u^T): r^T, u^T as B operands (hi + lo), k = j in
+        // the permuted order of two accumulator tiles
+        bf16x8 rh[NK], rl[NK], uh[NK], ul[NK];
+#pragma unroll
+        for (int m = 0; m < NK; ++m) {
+            frag_split(rt[2 * m], rt[2 * m + 1], rh[m], rl[m]);
+            frag_split(ut[2 * m], ut[2 * m + 1], uh[m], ul[m]);
+        }
+#pragma unroll
+        for (int it = 0; it < NT1; ++it) {
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int m = 0; m < NK; ++m) {
+                const int r0 = m * 32 + 4 * g, r1 = r0 + 16;
+                const bf16x8 xh = tr_a(AH, r0, r1, it * 16), xl = tr_a(AL, r0, r1, it * 16);
+                acc = mfma32(xh, rh[m], acc);
+                acc = mfma32(xh, rl[m], acc);
+                acc = mfma32(xl, rh[m], acc);
+                const bf16x8 ph = tr_a(BH, r0, r1, it * 16), pl = tr_a(BL, r0, r1, it * 16);
+                floatx4 nacc = zero4();
+                nacc = mfma32(ph, uh[m], nacc);
+                nacc = mfma32(ph, ul[m], nacc);
+                nacc = mfma32(pl, uh[m], nacc);
+                acc -= nacc;
+            }
+            if (t < a.S)
+                *reinterpret_cast<float4 *>(ba.dk + (row0 + t) * D + it * 16 + 4 * g) =
+                    float4{bt * acc[0], bt * acc[1], bt * acc[2], bt * acc[3]};
+        }
+    }
+    // dq^T = scale S_f dO^T: S_f^T staged over X^T
+    __syncthreads();
+    stage(AH, AL, a.sf + (size_t)unit * D * D, 1.f);
+    __syncthreads();
+#pragma unroll 1
+    for (int u = 0; u < SUB; ++u) {
+        asm volatile("" ::: "memory");
+        const int t = t0 + u * 16 + c16;
+        bf16x8 bo[NK];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) bo[kk] = row_frag8(oin, t, kk);
+#pragma unroll
+        for (int it = 0; it < NT1; ++it) {
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const int r0 = kk * 32 + 8 * g;
+                acc = mfma32(tr_a(AH, r0, r0 + 4, it * 16), bo[kk], acc);
+                acc = mfma32(tr_a(AL, r0, r0 + 4, it * 16), bo[kk], acc);
+            }
+            if (t < a.S)
+                *reinterpret_cast<float4 *>(ba.dq + (row0 + t) * D + it * 16 + 4 * g) =
+                    float4{a.scale * acc[0], a.scale * acc[1], a.scale * acc[2], a.scale * acc[3]};
+        }
+    }
+}
+
+// Work space of the backward: the forward's (partials, G_f and H_f, S_f),
+// then the partial A_f, X_f, and the dg shares.
+size_t frame_bwd_workspace(int B, int H, int F, int S, int D) {
+    const int ns = frame_nsplit(B, H, F, S, D, nullptr);
+    const size_t units = (size_t)B * H * F;
+    return (units * ns * 2 * D * D + units * 2 * D * D + units * D * D + units * ns * D * D + units * D * D +
+            units * (D / 16)) * sizeof(float);
+}
+
+template <int D>
+hipError_t launch_frame_bwd(FrameBwdArgs ba, hipStream_t s) {
+    FrameArgs &a = ba.a;
+    const int units = a.B * a.H * a.F;
+    // forward: G_f, H_f (summed over the token ranges) and S_f
+    hipError_t e = launch_gram<false, D, false>(a, s);
+    if (e != hipSuccess) return e;
+    if (a.nsplit > 1) {
+        const size_t n4 = (size_t)units * 2 * D * D / 4;
+        hipLaunchKernelGGL((frame_reduce_kernel<D>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    FrameArgs fa = a;
+    fa.nsplit = 1;                              // G_f, H_f reduced
+    fa.part = fa.gh;
+    hipLaunchKernelGGL((frame_state_kernel<D>), dim3((a.B * a.H + 7) / 8 * 8 * (D / 16)), dim3(256), 0, s, fa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // A_f = scale Q_f^T dO_f (partials)
+    FrameArgs ca = a;
+    ca.k = a.q;
+    ca.v = ba.dout;
+    ca.part = const_cast<float *>(ba.apart);
+    hipLaunchKernelGGL((frame_gram_bf16_kernel<D, false, true>), dim3(units * a.nsplit), dim3(64 * gram_waves<D>()),
+                       0, s, ca);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((frame_bstate_kernel<D>), dim3((a.B * a.H + 7) / 8 * 8 * (D / 16)), dim3(256), 0, s, ba);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int ntt = (a.S + BG_TOK - 1) / BG_TOK;
+    hipLaunchKernelGGL((frame_bgrad_kernel<D>), dim3((units + 7) / 8 * 8 * ntt), dim3(64 * BG_WAVES), 0, s, ba);
+    return hipGetLastError();
+}
+
+int frame_bwd_entry(const void *q, const void *k, const void *v, const float *beta, const float *log_decay,
+                    float scale, const float *h0, const void *dout, const float *dhT, float *dq, float *dk, float *dv,
+                    float *dbeta, float *dlog_decay, float *dh0, int B, int H, int F, int S, int D, int dtype,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    const char *name = "gdn_recurrent_bwd";
+    GDN_REQUIRE(B >= 0 && H >= 0 && F >= 0, GDN_EINVAL, "%s: negative size (B=%d H=%d F=%d)", name, B, H, F);
+    GDN_REQUIRE(S >= 1, GDN_EINVAL, "%s: S=%d (at least one token per frame)", name, S);
+    GDN_REQUIRE(dtype == GDN_DTYPE_F32 || dtype == GDN_DTYPE_BF16, GDN_EINVAL, "%s: unknown dtype %d", name, dtype);
+    GDN_REQUIRE(dtype == GDN_DTYPE_BF16, GDN_EUNSUPPORTED, "%s: bf16 inputs only", name);
+    GDN_REQUIRE(D == 32 || D == 64 || D == 128, GDN_EUNSUPPORTED, "%s: D=%d (supported: 32, 64, 128)", name, D);
+    GDN_REQUIRE(isfinite(scale), GDN_EINVAL, "%s: scale is not finite", name);
+    if ((long)B * H == 0) return GDN_OK;
+    const bool work = F > 0;
+    if (work) {
+        GDN_REQUIRE(q && k && v && beta && log_decay && dout && dq && dk && dv && dbeta && dlog_decay, GDN_EINVAL,
+                    "%s: null tensor pointer", name);
+        GDN_REQUIRE(gdn::aligned(q, 16) && gdn::aligned(k, 16) && gdn::aligned(v, 16) && gdn::aligned(dout, 16) &&
+                        gdn::aligned(dq, 16) && gdn::aligned(dk, 16) && gdn::aligned(dv, 16),
+                    GDN_EINVAL, "%s: q, k, v, dout, dq, dk, dv must be 16-byte aligned", name);
+        GDN_REQUIRE(gdn::aligned(beta, 4) && gdn::aligned(log_decay, 4) && gdn::aligned(dbeta, 4) &&
+                        gdn::aligned(dlog_decay, 4),
+                    GDN_EINVAL, "%s: misaligned gate pointer", name);
+    }
+    GDN_REQUIRE((!h0 || gdn::aligned(h0, 4)) && (!dhT || gdn::aligned(dhT, 4)) && (!dh0 || gdn::aligned(dh0, 4)),
+                GDN_EINVAL, "%s: misaligned state pointer", name);
+    const size_t need = frame_bwd_workspace(B, H, F, S, D);
+    GDN_REQUIRE(workspace_bytes >= need, GDN_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", name,
+                workspace_bytes, need);
+    GDN_REQUIRE(need == 0 || (workspace && gdn::aligned(workspace, 16)), GDN_EINVAL,
+                "%s: workspace must be a 16-byte aligned device pointer", name);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!work) {                                // no frames: dh0 = dhT (or 0)
+        if (!dh0) return GDN_OK;
+        const size_t n = (size_t)B * H * D * D;
+        hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dhT, dh0, n);
+        return check_hip(hipGetLastError(), name);
+    }
+    FrameBwdArgs ba;
+    FrameArgs &a = ba.a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.g = log_decay;
+    a.h0 = h0;
+    a.hT = nullptr;
+    a.out = nullptr;
+    a.B = B;
+    a.H = H;
+    a.F = F;
+    a.S = S;
+    a.nsplit = frame_nsplit(B, H, F, S, D, &a.spl);
+    a.dd = D;
+    a.scale = scale;
+    a.reverse = 0;
+    a.den = 0;
+    const size_t units = (size_t)B * H * F;
+    float *ws = reinterpret_cast<float *>(workspace);
+    a.part = ws;
+    a.gh = a.part + units * a.nsplit * 2 * D * D;
+    a.sf = a.gh + units * 2 * D * D;
+    float *ap = a.sf + units * D * D;
+    ba.apart = ap;
+    ba.xf = ap + units * a.nsplit * D * D;
+    ba.dgp = ba.xf + units * D * D;
+    if (a.nsplit == 1) a.part = a.gh;            // one range: the gram kernel writes G_f, H_f directly
+    ba.dout = dout;
+    ba.dhT = dhT;
+    ba.dq = dq;
+    ba.dk = dk;
+    ba.dv = dv;
+    ba.dbeta = dbeta;
+    ba.dg = dlog_decay;
+    ba.dh0 = dh0;
+    hipError_t e;
+    switch (D) {
+        case 32: e = launch_frame_bwd<32>(ba, s); break;
+        case 64: e = launch_frame_bwd<64>(ba, s); break;
+        default: e = launch_frame_bwd<128>(ba, s); break;
+    }
+    return check_hip(e, name);
+}
+
 }  // namespace
 }  // namespace gdn
 
@@ -902,4 +1339,19 @@ extern "C" int gdn_recurrent_den_fwd(const void *q_den, const void *k_z, const f
                                      void *stream) {
     return gdn::frame_entry("gdn_recurrent_den_fwd", q_den, k_z, nullptr, beta, log_decay, scale, z0, zT, den, B, H,
                             F, S, D, dtype, reverse, 1, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t gdn_recurrent_bwd_workspace_bytes(int B, int H, int F, int S, int D, int dtype) {
+    (void)dtype;
+    if (B < 0 || H < 0 || F < 0 || S <= 0 || (D != 32 && D != 64 && D != 128)) return 0;
+    return gdn::frame_bwd_workspace(B, H, F, S, D);
+}
+
+extern "C" int gdn_recurrent_bwd(const void *q, const void *k, const void *v, const float *beta,
+                                 const float *log_decay, float scale, const float *h0, const void *dout,
+                                 const float *dhT, float *dq, float *dk, float *dv, float *dbeta, float *dlog_decay,
+                                 float *dh0, int B, int H, int F, int S, int D, int dtype, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    return gdn::frame_bwd_entry(q, k, v, beta, log_decay, scale, h0, dout, dhT, dq, dk, dv, dbeta, dlog_decay, dh0,
+                                B, H, F, S, D, dtype, workspace, workspace_bytes, stream);
 }

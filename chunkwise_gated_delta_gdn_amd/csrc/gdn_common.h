@@ -175,6 +175,23 @@ __device__ __forceinline__ floatx4 mfma16(shortx4 a, shortx4 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// bf16 fragment of two accumulator tiles, in the permuted order (hi only).
+__device__ __forceinline__ bf16x8 frag_hi(const floatx4 &t0, const floatx4 &t1) {
+    return __builtin_bit_cast(bf16x8, uint4{cvt2_bf16(t0[0], t0[1]), cvt2_bf16(t0[2], t0[3]),
+                                            cvt2_bf16(t1[0], t1[1]), cvt2_bf16(t1[2], t1[3])});
+}
+// hi and lo fragments of two accumulator tiles (permuted order), or of 8
+// consecutive values (natural order).
+__device__ __forceinline__ void frag_split(const floatx4 &t0, const floatx4 &t1, bf16x8 &hi, bf16x8 &lo) {
+    uint4 h, o;
+    split2_bf16(t0[0], t0[1], h.x, o.x);
+    split2_bf16(t0[2], t0[3], h.y, o.y);
+    split2_bf16(t1[0], t1[1], h.z, o.z);
+    split2_bf16(t1[2], t1[3], h.w, o.w);
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, o);
+}
+
 // acc += A * B with B stored row-major ([k][col], stride ldb).
 __device__ __forceinline__ void mma_f32_bn(floatx4 &acc, const float *a, int lda, const float *b, int ldb,
                                            int kdim) {

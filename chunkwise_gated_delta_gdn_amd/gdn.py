@@ -28,6 +28,7 @@ EXPORTS = (
     "gdn_recurrent_den_fwd", "gdn_recurrent_den_fwd_workspace_bytes",
     "gdn_prep",
     "gdn_bwd", "gdn_bwd_workspace_bytes",
+    "gdn_recurrent_bwd", "gdn_recurrent_bwd_workspace_bytes",
 )
 
 
@@ -72,6 +73,10 @@ def _load():
     lib.gdn_bwd.restype = I
     lib.gdn_bwd_workspace_bytes.argtypes = [I] * 6
     lib.gdn_bwd_workspace_bytes.restype = Z
+    lib.gdn_recurrent_bwd.argtypes = [P, P, P, P, P, F, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, Z, P]
+    lib.gdn_recurrent_bwd.restype = I
+    lib.gdn_recurrent_bwd_workspace_bytes.argtypes = [I] * 6
+    lib.gdn_recurrent_bwd_workspace_bytes.restype = Z
     return lib
 
 
@@ -343,4 +348,37 @@ def gdn_bwd(q, k, v, beta, log_decay, dout, scale=1.0, h0=None, dhT=None, need_d
                       _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dg),
                       _ptr(dh0), B, T, H, Dk, Dv, _dtype_code(q.dtype), _ptr(ws), nws, _stream(dev))
     _check("gdn_bwd", rc)
+    return dq, dk, dv, dbeta, dg, dh0
+
+
+def gdn_recurrent_bwd(q, k, v, beta, log_decay, dout, frames, scale=1.0, h0=None, dhT=None, need_dh0=True):
+    """Gradients of :func:`gdn_recurrent_fwd`'s (out, hT), forward direction.
+    q, k, v, dout (B,H,N,D) of one dtype; beta (B,H,N) and log_decay
+    (B,H,F) fp32; h0, dhT (B,H,D,D) fp32 or None.  Returns (dq, dk, dv,
+    dbeta, dlog_decay, dh0), fp32 (dh0 None unless need_dh0)."""
+    _dev(q, k, v, beta, log_decay, dout, h0, dhT)
+    _f32(beta, "beta"), _f32(log_decay, "log_decay"), _f32(h0, "h0"), _f32(dhT, "dhT")
+    B, H, N, D = q.shape
+    F = int(frames)
+    if F <= 0 or N % F:
+        raise ValueError("frames must divide N")
+    if (k.shape != q.shape or v.shape != q.shape or dout.shape != q.shape
+            or k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype):
+        raise ValueError("q, k, v, dout shapes or dtypes disagree")
+    if beta.shape != (B, H, N) or log_decay.shape != (B, H, F):
+        raise ValueError("beta must be (B, H, N) and log_decay (B, H, F)")
+    for name, st in (("h0", h0), ("dhT", dhT)):
+        if st is not None and st.shape != (B, H, D, D):
+            raise ValueError(f"{name} must be (B, H, D, D)")
+    dev = q.device
+    dq, dk, dv = (torch.empty((B, H, N, D), dtype=torch.float32, device=dev) for _ in range(3))
+    dbeta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dg = torch.empty((B, H, F), dtype=torch.float32, device=dev)
+    dh0 = torch.empty((B, H, D, D), dtype=torch.float32, device=dev) if need_dh0 else None
+    dt = _dtype_code(q.dtype)
+    ws, nws = _workspace(_lib.gdn_recurrent_bwd_workspace_bytes(B, H, F, N // F, D, dt), dev)
+    rc = _lib.gdn_recurrent_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_decay), float(scale), _ptr(h0),
+                                _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dg),
+                                _ptr(dh0), B, H, F, N // F, D, dt, _ptr(ws), nws, _stream(dev))
+    _check("gdn_recurrent_bwd", rc)
     return dq, dk, dv, dbeta, dg, dh0

@@ -11,6 +11,7 @@
  *   gdn_prep                camera-branch per-token prep (RMSNorm over all
  *                           channels, ReLU, K-scale, UCPE 4x4, RoPE, ||k||^2)
  *   gdn_bwd                 gradients of gdn_chunk_fwd (q, k, v, beta, g, h0)
+ *   gdn_recurrent_bwd       gradients of gdn_recurrent_fwd (forward direction)
  *
  * Sources (web pages, cited by title and section):
  *   [dp]  msj19 "gated_deltaproduct" test.py: gated_chunk_scaled_dot_kkt_fwd,
@@ -214,6 +215,42 @@ int gdn_recurrent_fwd(const void *q, const void *k, const void *v,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 size_t gdn_recurrent_fwd_workspace_bytes(int B, int H, int F, int S, int D, int dtype);
+
+/*
+ * gdn_recurrent_bwd - gradients of gdn_recurrent_fwd's outputs (out, hT) in
+ * the forward direction ([cam] _cam_scan_bwd_kernel, the backward of
+ * cam_scan_func), frame-synchronous like the forward.
+ *
+ * With P_f = exp(g_f) S_{f-1}, G_f = sum_{s in f} beta_s k_s k_s^T and
+ * X_f = dL/dS_f including frame f's read-out (A_f = scale Q_f^T dO_f),
+ * walked from the last frame back (X_{F-1} = dhT + A_{F-1}):
+ *   X_{f-1} = exp(g_f) (I - G_f) X_f + A_{f-1},  dh0 = exp(g_0)(I - G_0) X_0,
+ *   dlog_decay_f = <(I - G_f) X_f, P_f>,
+ * and per token s of frame f, u_s = X_f^T k_s, r_s = v_s - P_f^T k_s:
+ *   dq_s = scale S_f dout_s,  dv_s = beta_s u_s,  dbeta_s = u_s . r_s,
+ *   dk_s = beta_s (X_f r_s - P_f u_s).
+ *
+ *   q, k, v, dout   (B, H, N, D)  dtype (dout = dL/dout)
+ *   beta            (B, H, N)     float32
+ *   log_decay       (B, H, F)     float32
+ *   h0, dhT         (B, H, D, D)  float32, nullable (zero)
+ *   dq, dk, dv      (B, H, N, D)  float32
+ *   dbeta           (B, H, N)     float32
+ *   dlog_decay      (B, H, F)     float32
+ *   dh0             (B, H, D, D)  float32, nullable (not stored)
+ * Supported: bf16 inputs; D in {32, 64, 128}; F >= 0; S >= 1.  q, k, v,
+ * dout, dq, dk, dv 16-byte aligned, the other tensors 4-byte.  The work
+ * space (gdn_recurrent_bwd_workspace_bytes) holds the forward's per-frame
+ * G_f, H_f and S_f, the partial A_f and every X_f.
+ */
+int gdn_recurrent_bwd(const void *q, const void *k, const void *v,
+                      const float *beta, const float *log_decay, float scale,
+                      const float *h0, const void *dout, const float *dhT,
+                      float *dq, float *dk, float *dv, float *dbeta, float *dlog_decay,
+                      float *dh0, int B, int H, int F, int S, int D, int dtype,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+size_t gdn_recurrent_bwd_workspace_bytes(int B, int H, int F, int S, int D, int dtype);
 
 /*
  * gdn_recurrent_den_fwd - normaliser (denominator) stream of the camera
