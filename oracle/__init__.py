@@ -21,6 +21,7 @@ receives; outputs are float64):
 * :func:`frame_den`                - the normaliser (Z) stream of O4.
 * :func:`gdn_recurrent_bwd`        - O6, gradients of O1 (reverse mode).
 * :func:`frame_scan_bwd`           - O7, gradients of O4 (reverse mode).
+* :func:`cam_prep_bwd`             - O8, gradients of O3 (reverse mode).
 * :func:`invert_se3`               - closed-form rigid-transform inverse.
 """
 from __future__ import annotations
@@ -67,12 +68,14 @@ def _load():
                                              P, P, P, P, P, P, I]
     lib.oracle_frame_scan_bwd.argtypes = [I, I, I, I, I, P, P, P, P, P, D, P, P, P,
                                           P, P, P, P, P, P, I]
+    lib.oracle_cam_prep_bwd.argtypes = [I, I, I, I, P, P, P, P, P, P, P, D, D, P, P, P, P, P, P, P, P, P,
+                                        P, P, I]
     lib.oracle_invert_se3.argtypes = [ctypes.c_long, P, P]
     lib.oracle_invert_se3.restype = None
     lib.oracle_max_threads.argtypes = []
     for fn in (lib.oracle_gdn_recurrent, lib.oracle_gdn_recurrent_bwd, lib.oracle_frame_scan_bwd,
                lib.oracle_deltaproduct_recurrent,
-               lib.oracle_cam_prep, lib.oracle_frame_scan, lib.oracle_max_threads):
+               lib.oracle_cam_prep, lib.oracle_cam_prep_bwd, lib.oracle_frame_scan, lib.oracle_max_threads):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -184,6 +187,29 @@ def cam_prep(qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin,
                                  _ptr(out["v"]), _ptr(out["k_pre_sq"]), _ptr(out["k_post_sq"]),
                                  _ptr(out["inflation_sq"]), int(nthreads))
     _check(rc, "cam_prep")
+    return out
+
+
+def cam_prep_bwd(qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_scale, eps,
+                 dq, dk, dv, dpre=None, dpost=None, dinfl=None, nthreads=0):
+    """O8.  Gradients of :func:`cam_prep` under the upstream gradients dq,
+    dk, dv (B,H,N,D) of its q, k, v outputs and, each optional, dpre, dpost,
+    dinfl (B,H,N) of k_pre_sq, k_post_sq, inflation_sq.  Returns a dict of
+    float64 arrays: dqkv (B,N,3,H,D), dq_norm_w and dk_norm_w (H*D),
+    dproj_q and dproj_kv (B,N,4,4)."""
+    qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, dq, dk, dv, dpre, dpost, dinfl = map(
+        _f32, (qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, dq, dk, dv, dpre, dpost, dinfl))
+    B, N, three, H, D = qkv.shape
+    assert three == 3 and dq.shape == (B, H, N, D) and dk.shape == dq.shape and dv.shape == dq.shape
+    out = {"dqkv": np.zeros((B, N, 3, H, D), np.float64),
+           "dq_norm_w": np.zeros(H * D, np.float64), "dk_norm_w": np.zeros(H * D, np.float64),
+           "dproj_q": np.zeros((B, N, 4, 4), np.float64), "dproj_kv": np.zeros((B, N, 4, 4), np.float64)}
+    rc = _load().oracle_cam_prep_bwd(B, N, H, D, _ptr(qkv), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(proj_q),
+                                     _ptr(proj_kv), _ptr(rope_cos), _ptr(rope_sin), float(k_scale), float(eps),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dpre), _ptr(dpost), _ptr(dinfl),
+                                     _ptr(out["dqkv"]), _ptr(out["dq_norm_w"]), _ptr(out["dk_norm_w"]),
+                                     _ptr(out["dproj_q"]), _ptr(out["dproj_kv"]), int(nthreads))
+    _check(rc, "cam_prep_bwd")
     return out
 
 

@@ -281,6 +281,150 @@ int oracle_cam_prep(int B, int N, int H, int D, const float *qkv,
 }
 
 /* ------------------------------------------------------------------------ */
+/* O8: backward of O3 ([cam] _cam_prep_bwd_kernel and                      */
+/* _cam_prep_bwd_dispatch): reverse mode through the prep steps of one      */
+/* token, last step first.  Upstream gradients: gq, gk, gv of the outputs   */
+/* q, k, v (B,H,N,D) and, each nullable, gpre, gpost, ginfl of k_pre_sq,    */
+/* k_post_sq and inflation_sq (B,H,N).  Per head:                           */
+/*   inflation = max(post, 1e-12) / max(pre, 1e-12) sends                   */
+/*     ginfl / max(pre, 1e-12) to post (if post > 1e-12) and                */
+/*     -ginfl max(post, 1e-12) / pre^2 to pre (if pre > 1e-12);             */
+/*   post = ||k_out||^2 sends 2 k_out gpost to k_out; pre = ||k~||^2 sends  */
+/*     2 k~ gpre to k~;                                                     */
+/*   RoPE half: y[r] = x[r] c[r] + x[r^1] s[r] gives                        */
+/*     gx[r] = gy[r] c[r] + gy[r^1] s[r^1];                                 */
+/*   UCPE half: y_g = P x_g gives gx_g = P^T gy_g and dP += gy_g x_g^T       */
+/*     (summed over groups and heads; proj_q from q, proj_kv from k and v); */
+/*   k~ = relu(a) k_scale, q~ = relu(a), a = x inv_rms w: ga = gx k_scale   */
+/*     (or gx) where a > 0, else 0;                                         */
+/*   RMSNorm over the token's C channels: dw_c += ga_c x_c inv_rms (summed  */
+/*     over tokens) and gx_c = inv_rms w_c ga_c                             */
+/*       - inv_rms^3 / C x_c sum_c' ga_c' w_c' x_c';                        */
+/*   v skips norm, relu and scale: gv_raw = gx.                             */
+/* Outputs: dqkv (B,N,3,H,D); dq_w, dk_w (H*D); dproj_q, dproj_kv (B,N,4,4).*/
+/* ------------------------------------------------------------------------ */
+static void prep_head_bwd(int D, const double *gy, const double *xin, const float *P, const float *cs,
+                          const float *sn, double *gx, double *dP) {
+    int half = D / 2;
+    for (int grp = 0; grp < half / 4; ++grp)
+        for (int j = 0; j < 4; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < 4; ++i) {
+                acc += (double)P[i * 4 + j] * gy[grp * 4 + i];
+                dP[i * 4 + j] += gy[grp * 4 + i] * xin[grp * 4 + j];
+            }
+            gx[grp * 4 + j] = acc;
+        }
+    for (int rr = 0; rr < half; ++rr)
+        gx[half + rr] = gy[half + rr] * (double)cs[rr] + gy[half + (rr ^ 1)] * (double)sn[rr ^ 1];
+}
+
+int oracle_cam_prep_bwd(int B, int N, int H, int D, const float *qkv,
+                        const float *q_norm_w, const float *k_norm_w,
+                        const float *proj_q, const float *proj_kv,
+                        const float *rope_cos, const float *rope_sin,
+                        double k_scale, double eps,
+                        const float *gq, const float *gk, const float *gv,
+                        const float *gpre, const float *gpost, const float *ginfl,
+                        double *dqkv, double *dq_w, double *dk_w,
+                        double *dproj_q, double *dproj_kv, int nthreads) {
+    if (B < 0 || N < 0 || H <= 0 || D <= 0 || D > 512 || (D % 8) != 0) return -1;
+    set_threads(nthreads);
+    int C = H * D, half = D / 2;
+    long ntok = (long)B * N;
+    int nt = omp_get_max_threads();
+    double *wpart = (double *)calloc((size_t)nt * 2 * C, sizeof(double));   /* per-thread dq_w, dk_w */
+#pragma omp parallel
+    {
+        double *myw = wpart + (size_t)omp_get_thread_num() * 2 * C;
+        double *gaq = (double *)malloc(sizeof(double) * C), *gak = (double *)malloc(sizeof(double) * C);
+#pragma omp for schedule(static)
+        for (long bn = 0; bn < ntok; ++bn) {
+            int b = (int)(bn / N), n = (int)(bn % N);
+            const float *tok = qkv + (size_t)bn * 3 * C;
+            const float *xq = tok, *xk = tok + C, *xv = tok + 2 * C;
+            double sq = 0.0, sk = 0.0;
+            for (int c = 0; c < C; ++c) {
+                sq += (double)xq[c] * (double)xq[c];
+                sk += (double)xk[c] * (double)xk[c];
+            }
+            double inv_q = 1.0 / sqrt(sq / C + eps);
+            double inv_k = 1.0 / sqrt(sk / C + eps);
+            const float *Pq = proj_q + (size_t)bn * 16, *Pkv = proj_kv + (size_t)bn * 16;
+            const float *cs = rope_cos + (size_t)n * half, *sn = rope_sin + (size_t)n * half;
+            double *dPq = dproj_q + (size_t)bn * 16, *dPkv = dproj_kv + (size_t)bn * 16;
+            for (int i = 0; i < 16; ++i) dPq[i] = dPkv[i] = 0.0;
+            double *out_q = dqkv + (size_t)bn * 3 * C, *out_k = out_q + C, *out_v = out_k + C;
+            double xin[512], yo[512], gy[512], gx[512];
+            for (int h = 0; h < H; ++h) {
+                size_t obase = (((size_t)b * H + h) * N + n) * D;
+                size_t sbase = ((size_t)b * H + h) * N + n;
+                const float *wq = q_norm_w ? q_norm_w + h * D : NULL, *wk = k_norm_w ? k_norm_w + h * D : NULL;
+                /* q */
+                prep_head(D, xq + h * D, inv_q, wq, 1, 1.0, Pq, cs, sn, xin, yo);
+                for (int d = 0; d < D; ++d) gy[d] = (double)gq[obase + d];
+                prep_head_bwd(D, gy, xin, Pq, cs, sn, gx, dPq);
+                for (int d = 0; d < D; ++d) {
+                    double a = (double)xq[h * D + d] * inv_q * (wq ? (double)wq[d] : 1.0);
+                    gaq[h * D + d] = a > 0.0 ? gx[d] : 0.0;
+                }
+                /* k, with the norm outputs */
+                prep_head(D, xk + h * D, inv_k, wk, 1, k_scale, Pkv, cs, sn, xin, yo);
+                double pre = 0.0, post = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    pre += xin[d] * xin[d];
+                    post += yo[d] * yo[d];
+                }
+                double gpo = gpost ? (double)gpost[sbase] : 0.0, gpr = gpre ? (double)gpre[sbase] : 0.0;
+                if (ginfl) {
+                    double gi = (double)ginfl[sbase];
+                    if (post > 1e-12) gpo += gi / (pre > 1e-12 ? pre : 1e-12);
+                    if (pre > 1e-12) gpr -= gi * (post > 1e-12 ? post : 1e-12) / (pre * pre);
+                }
+                for (int d = 0; d < D; ++d) gy[d] = (double)gk[obase + d] + 2.0 * yo[d] * gpo;
+                prep_head_bwd(D, gy, xin, Pkv, cs, sn, gx, dPkv);
+                for (int d = 0; d < D; ++d) {
+                    gx[d] += 2.0 * xin[d] * gpr;
+                    double a = (double)xk[h * D + d] * inv_k * (wk ? (double)wk[d] : 1.0);
+                    gak[h * D + d] = a > 0.0 ? gx[d] * k_scale : 0.0;
+                }
+                /* v */
+                prep_head(D, xv + h * D, 0.0, NULL, 0, 1.0, Pkv, cs, sn, xin, yo);
+                for (int d = 0; d < D; ++d) gy[d] = (double)gv[obase + d];
+                prep_head_bwd(D, gy, xin, Pkv, cs, sn, gx, dPkv);
+                for (int d = 0; d < D; ++d) out_v[h * D + d] = gx[d];
+            }
+            /* RMSNorm backward over all C channels, and the weight gradients */
+            double s_q = 0.0, s_k = 0.0;
+            for (int c = 0; c < C; ++c) {
+                s_q += gaq[c] * (q_norm_w ? (double)q_norm_w[c] : 1.0) * (double)xq[c];
+                s_k += gak[c] * (k_norm_w ? (double)k_norm_w[c] : 1.0) * (double)xk[c];
+            }
+            for (int c = 0; c < C; ++c) {
+                double w_q = q_norm_w ? (double)q_norm_w[c] : 1.0, w_k = k_norm_w ? (double)k_norm_w[c] : 1.0;
+                out_q[c] = inv_q * w_q * gaq[c] - inv_q * inv_q * inv_q / C * (double)xq[c] * s_q;
+                out_k[c] = inv_k * w_k * gak[c] - inv_k * inv_k * inv_k / C * (double)xk[c] * s_k;
+                myw[c] += gaq[c] * (double)xq[c] * inv_q;
+                myw[C + c] += gak[c] * (double)xk[c] * inv_k;
+            }
+        }
+        free(gaq);
+        free(gak);
+    }
+    for (int c = 0; c < C; ++c) {
+        double a = 0.0, b2 = 0.0;
+        for (int t = 0; t < nt; ++t) {
+            a += wpart[(size_t)t * 2 * C + c];
+            b2 += wpart[(size_t)t * 2 * C + C + c];
+        }
+        dq_w[c] = a;
+        dk_w[c] = b2;
+    }
+    free(wpart);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* O4: camera-branch numerator-only scan, frame-synchronous ([cam]          */
 /* _cam_scan_kernel, forward direction).                                    */
 /*                                                                          */
