@@ -231,16 +231,25 @@ def _prepare(name, dev):
         rng = np.random.default_rng(20263 + 7)
         dout = bf(inputs.cast(rng.standard_normal(tuple(pr["q"].shape)), "bf16"))
 
+        qkv = bf(d["qkv"])
+
         def step():
-            return gdn.gdn_recurrent_bwd(pr["q"], pr["k"], pr["v"], t["beta"], t["g"], dout, wl["F"], 1.0)
+            # the scan's backward, then the prep's backward on its gradients
+            sg = gdn.gdn_recurrent_bwd(pr["q"], pr["k"], pr["v"], t["beta"], t["g"], dout, wl["F"], 1.0)
+            return gdn.gdn_prep_bwd(qkv, t["q_norm_w"], t["k_norm_w"], t["proj_q"], t["proj_kv"], t["rope_cos"],
+                                    t["rope_sin"], d["k_scale"], d["eps"], sg[0], sg[1], sg[2])
         B, F, S, H, D = wl["B"], wl["F"], wl["S"], wl["H"], wl["D"]
         N = F * S
-        # read q, k, v, dout (bf16), beta, g; write dq, dk, dv (fp32), dbeta, dg, dh0
-        nbytes = B * H * N * (4 * D * 2 + 4 + 3 * D * 4 + 4) + B * H * F * 8 + B * H * D * D * 4
+        # scan backward: read q, k, v, dout (bf16), beta, g; write dq, dk, dv
+        # (fp32), dbeta, dg, dh0.  Prep backward: read qkv (bf16), the three
+        # fp32 gradients, projections, tables; write dqkv (fp32), projection
+        # and weight gradients
+        scan_bytes = B * H * N * (4 * D * 2 + 4 + 3 * D * 4 + 4) + B * H * F * 8 + B * H * D * D * 4
+        prep_bytes = B * N * 3 * H * D * (2 + 4 + 4) + B * N * 32 * 4 * 2 + N * D * 4 + 2 * H * D * 4
         # per token: the forward's G and H (4 D^2), A (2 D^2), u and r (4 D^2),
         # dk (4 D^2), dq (2 D^2)
         flops = B * H * N * 16 * D * D
-        return d, step, B * N, nbytes, flops
+        return d, step, B * N, scan_bytes + prep_bytes, flops
     # camera: prep, then the frame-synchronous scan on its outputs (the
     # anti-causal direction for camera_reverse)
     reverse = name == "camera_reverse"
@@ -333,11 +342,12 @@ def main():
                   "+ chunk_bchain_kernel<128> (reverse state pass) + chunk_bgrad_kernel<128> (per-chunk gradients)")
         traffic = measured_traffic(args.workload)
     elif args.workload == "camera_bwd":
-        metric = "tokens/sec of camera scan backward (B*N/s)"
-        desc = ("camera_bwd: gradients of the camera workload's scan (B=1 F=8 S=30x52 H=16 D=64) on the GPU "
-                "prep's bf16 outputs, bf16 dout, fp32 gradients, no dhT")
-        kernel = ("gdn_recurrent_bwd = frame_gram_bf16_kernel (G, H; A) + frame_reduce_kernel + frame_state_kernel "
-                  "+ frame_bstate_kernel + frame_bgrad_kernel")
+        metric = "tokens/sec of camera scan + prep backward (B*N/s)"
+        desc = ("camera_bwd: gradients of the camera workload (B=1 F=8 S=30x52 H=16 D=64): the scan's on the "
+                "GPU prep's bf16 outputs under bf16 dout, then the prep's on those fp32 gradients (qkv, norm "
+                "weights, projections)")
+        kernel = ("gdn_recurrent_bwd (frame_gram_bf16_kernel for G, H and A, frame_reduce_kernel, frame_state_kernel, "
+                  "frame_bstate_kernel, frame_bgrad_kernel) + gdn_prep_bwd (prep_bwd_kernel, prep_bwd_reduce_kernel)")
         traffic = None
     elif args.workload in ("gdn", "gdn_long"):
         metric = "tokens/sec of chunkwise gated-delta fwd (B*T/s) at H=16, D=128"

@@ -307,6 +307,318 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ===========================================================================
+// Backward of the prep ([cam] _cam_prep_bwd_kernel and
+// _cam_prep_bwd_dispatch): reverse mode through the steps above, with the
+// forward's values recomputed per token (same lane layout and token walk as
+// prep_kernel).  Per token:
+//   1. the forward again: inv_rms_q, inv_rms_k (wave sums), q~, k~, v and, on
+//      k, the outputs and their norms (sums over a head's lanes);
+//   2. the norm outputs' gradients: inflation = max(post, 1e-12) /
+//      max(pre, 1e-12) sends ginf / max(pre, 1e-12) to post (post > 1e-12)
+//      and -ginf max(post, 1e-12) / pre^2 to pre (pre > 1e-12); post sends
+//      2 k_out gpost to k_out, pre sends 2 k~ gpre to k~;
+//   3. RoPE^T on the second half, gx[d] = gy[d] cos[d] + gy[d^1] sin[d^1];
+//      UCPE^T on the first half, gx_g = P^T gy_g, and dP += gy_g x_g^T;
+//   4. the ReLU mask (and K-scale on k) gives ga; the RMSNorm backward over
+//      all C channels, gx_c = inv w_c ga_c - inv^3 / C x_c sum_c' ga_c' w_c' x_c'
+//      (one more wave sum per stream); dw_c += ga_c x_c inv in registers;
+//   5. dqkv (fp32) out; the projection gradients summed over the wave;
+// every wave writes its dw partial sums at the end, and prep_bwd_reduce_kernel
+// adds them in a fixed order.
+// ===========================================================================
+struct PrepBwdArgs {
+    PrepArgs a;                   // forward inputs (qkv, weights, proj, tables, k_scale, eps, sizes)
+    const void *gq, *gk, *gv;     // upstream gradients of q, k, v (B, H, N, D), gdtype
+    const float *gpre, *gpost, *ginf;   // of k_pre_sq, k_post_sq, inflation_sq (B, H, N), nullable
+    float *dqkv;                  // (B, N, 3, H, D)
+    float *dpq, *dpkv;            // (B, N, 4, 4), nullable
+    float *wpart;                 // [waves][2][C] partial weight gradients, or null
+    float *dqw, *dkw;             // (C), nullable
+    int nwaves;
+};
+
+template <bool F32IN, bool F32G, int LPH, int NSEG>
+__global__ __launch_bounds__(256) void prep_bwd_kernel(PrepBwdArgs ba) {
+    const PrepArgs &a = ba.a;
+    constexpr int TPB = PREP_TPB, TPW = TPB / 4, HPS = 64 / LPH;
+    const int l = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long ntok = (long)a.B * a.N;
+    long blk = blockIdx.x;
+    int jw = 0;
+    long tok = blk * TPB + w;
+    const int H = a.H, D = a.D, C = H * D;
+    const int HALF = D / 2;
+    const int d0 = 8 * (l % LPH);
+    const bool lane_ok = d0 < D;
+    int hseg[NSEG];
+    bool act[NSEG];
+    float wq[NSEG][8], wk[NSEG][8], dwq[NSEG][8], dwk[NSEG][8];
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) {
+        hseg[i] = i * HPS + l / LPH;
+        act[i] = lane_ok && hseg[i] < H;
+        const int c0 = act[i] ? hseg[i] * D + d0 : 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            wq[i][e] = wk[i][e] = 1.f;
+            dwq[i][e] = dwk[i][e] = 0.f;
+        }
+        if (a.qw) load_f8(a.qw + c0, wq[i]);
+        if (a.kw) load_f8(a.kw + c0, wk[i]);
+    }
+    const int dr = lane_ok && d0 >= HALF ? d0 - HALF : 0;
+    const bool rope = d0 >= HALF;
+    const float ks = a.k_scale;
+    while (tok < ntok) {
+        const int b = (int)(tok / a.N), n = (int)(tok % a.N);
+        const size_t tbase = (size_t)tok * 3 * C;
+        float xq[NSEG][8], xk[NSEG][8], xv[NSEG][8], cs[8], sn[8];
+#pragma unroll
+        for (int i = 0; i < NSEG; ++i) {
+            const int c0 = act[i] ? hseg[i] * D + d0 : 0;
+            unpack8<F32IN>(load_raw8<F32IN>(a.qkv, tbase + c0), xq[i]);
+            unpack8<F32IN>(load_raw8<F32IN>(a.qkv, tbase + C + c0), xk[i]);
+            unpack8<F32IN>(load_raw8<F32IN>(a.qkv, tbase + 2 * C + c0), xv[i]);
+        }
+        load_f8(a.cosv + (size_t)n * HALF + dr, cs);
+        load_f8(a.sinv + (size_t)n * HALF + dr, sn);
+        float Pq[16], Pkv[16];
+        const float *pq = a.proj_q + tok * 16, *pkv = a.proj_kv + tok * 16;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            Pq[i] = pq[i];
+            Pkv[i] = pkv[i];
+        }
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int i = 0; i < NSEG; ++i)
+            if (act[i])
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sq += xq[i][e] * xq[i][e];
+                    sk += xk[i][e] * xk[i][e];
+                }
+        sq = wave_sum(sq);
+        sk = wave_sum(sk);
+        const float inv_q = 1.f / sqrtf(sq / C + a.eps);
+        const float inv_k = 1.f / sqrtf(sk / C + a.eps);
+        float gaq[NSEG][8], gak[NSEG][8];
+        float dPq[16], dPkv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dPq[i] = dPkv[i] = 0.f;
+        float rq = 0.f, rk = 0.f;                // sums of ga w x for the RMSNorm backward
+#pragma unroll
+        for (int i = 0; i < NSEG; ++i) {
+            const int h = hseg[i];
+            // (an inactive segment reads the head row's start: lanes past D/8 of a
+            // head would read past the end of the last row)
+            const size_t o = (((size_t)b * H + (act[i] ? h : 0)) * a.N + n) * D + (act[i] ? d0 : 0);
+            float gyq[8], gyk[8], gyv[8];
+            unpack8<F32G>(load_raw8<F32G>(ba.gq, o), gyq);
+            unpack8<F32G>(load_raw8<F32G>(ba.gk, o), gyk);
+            unpack8<F32G>(load_raw8<F32G>(ba.gv, o), gyv);
+            const size_t so = ((size_t)b * H + (act[i] ? h : 0)) * a.N + n;
+            float qa[8], qn[8], ka[8], kn[8], yk[8];
+            float kpre = 0.f, kpost = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                qa[e] = xq[i][e] * inv_q * wq[i][e];
+                qn[e] = qa[e] > 0.f ? qa[e] : 0.f;
+                ka[e] = xk[i][e] * inv_k * wk[i][e];
+                kn[e] = (ka[e] > 0.f ? ka[e] : 0.f) * ks;
+                kpre += kn[e] * kn[e];
+            }
+            if (!rope) {
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float acc = 0.f;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) acc += Pkv[r * 4 + c] * kn[g * 4 + c];
+                        yk[g * 4 + r] = acc;
+                    }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) yk[e] = kn[e] * cs[e] + kn[e ^ 1] * sn[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kpost += yk[e] * yk[e];
+            kpre = group_sum<LPH>(act[i] ? kpre : 0.f);
+            kpost = group_sum<LPH>(act[i] ? kpost : 0.f);
+            float gpo = ba.gpost ? ba.gpost[so] : 0.f, gpr = ba.gpre ? ba.gpre[so] : 0.f;
+            if (ba.ginf) {
+                const float gi = ba.ginf[so];
+                if (kpost > 1e-12f) gpo += gi / fmaxf(kpre, 1e-12f);
+                if (kpre > 1e-12f) gpr -= gi * fmaxf(kpost, 1e-12f) / (kpre * kpre);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gyk[e] += 2.f * yk[e] * gpo;
+            // RoPE^T or UCPE^T (with the projection gradients)
+            float gxq[8], gxk[8], gxv[8];
+            if (!rope) {
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        float aq = 0.f, ak = 0.f, av = 0.f;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            aq += Pq[r * 4 + c] * gyq[g * 4 + r];
+                            ak += Pkv[r * 4 + c] * gyk[g * 4 + r];
+                            av += Pkv[r * 4 + c] * gyv[g * 4 + r];
+                            if (act[i]) {
+                                dPq[r * 4 + c] += gyq[g * 4 + r] * qn[g * 4 + c];
+                                dPkv[r * 4 + c] += gyk[g * 4 + r] * kn[g * 4 + c] + gyv[g * 4 + r] * xv[i][g * 4 + c];
+                            }
+                        }
+                        gxq[g * 4 + c] = aq;
+                        gxk[g * 4 + c] = ak;
+                        gxv[g * 4 + c] = av;
+                    }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    gxq[e] = gyq[e] * cs[e] + gyq[e ^ 1] * sn[e ^ 1];
+                    gxk[e] = gyk[e] * cs[e] + gyk[e ^ 1] * sn[e ^ 1];
+                    gxv[e] = gyv[e] * cs[e] + gyv[e ^ 1] * sn[e ^ 1];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                gxk[e] += 2.f * kn[e] * gpr;
+                gaq[i][e] = qa[e] > 0.f ? gxq[e] : 0.f;
+                gak[i][e] = ka[e] > 0.f ? gxk[e] * ks : 0.f;
+            }
+            if (act[i]) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    rq += gaq[i][e] * wq[i][e] * xq[i][e];
+                    rk += gak[i][e] * wk[i][e] * xk[i][e];
+                    dwq[i][e] += gaq[i][e] * xq[i][e] * inv_q;
+                    dwk[i][e] += gak[i][e] * xk[i][e] * inv_k;
+                }
+                float *dv = ba.dqkv + tbase + 2 * C + hseg[i] * D + d0;
+                *reinterpret_cast<float4 *>(dv) = float4{gxv[0], gxv[1], gxv[2], gxv[3]};
+                *reinterpret_cast<float4 *>(dv + 4) = float4{gxv[4], gxv[5], gxv[6], gxv[7]};
+            }
+        }
+        rq = wave_sum(rq);
+        rk = wave_sum(rk);
+        const float cq = inv_q * inv_q * inv_q / C * rq, ck = inv_k * inv_k * inv_k / C * rk;
+#pragma unroll
+        for (int i = 0; i < NSEG; ++i)
+            if (act[i]) {
+                float gq8[8], gk8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    gq8[e] = inv_q * wq[i][e] * gaq[i][e] - cq * xq[i][e];
+                    gk8[e] = inv_k * wk[i][e] * gak[i][e] - ck * xk[i][e];
+                }
+                float *dq = ba.dqkv + tbase + hseg[i] * D + d0, *dk = dq + C;
+                *reinterpret_cast<float4 *>(dq) = float4{gq8[0], gq8[1], gq8[2], gq8[3]};
+                *reinterpret_cast<float4 *>(dq + 4) = float4{gq8[4], gq8[5], gq8[6], gq8[7]};
+                *reinterpret_cast<float4 *>(dk) = float4{gk8[0], gk8[1], gk8[2], gk8[3]};
+                *reinterpret_cast<float4 *>(dk + 4) = float4{gk8[4], gk8[5], gk8[6], gk8[7]};
+            }
+        if (ba.dpq) {
+            // projection gradients: sums over the wave, lane i < 16 writes entry i
+            // of proj_q's, lanes 16..31 of proj_kv's
+            float mine = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float sq_ = wave_sum(dPq[i]), skv = wave_sum(dPkv[i]);
+                if (l == i) mine = sq_;
+                if (l == 16 + i) mine = skv;
+            }
+            if (l < 16) ba.dpq[tok * 16 + l] = mine;
+            else if (l < 32) ba.dpkv[tok * 16 + l - 16] = mine;
+        }
+        // the next token of this wave
+        int njw = jw + 1;
+        if (njw == TPW) {
+            njw = 0;
+            blk += gridDim.x;
+        }
+        jw = njw;
+        tok = blk * TPB + w + 4 * jw;
+    }
+    if (ba.wpart) {
+        float *wp = ba.wpart + (size_t)(blockIdx.x * 4 + w) * 2 * C;
+#pragma unroll
+        for (int i = 0; i < NSEG; ++i)
+            if (act[i]) {
+                const int c0 = hseg[i] * D + d0;
+                *reinterpret_cast<float4 *>(wp + c0) = float4{dwq[i][0], dwq[i][1], dwq[i][2], dwq[i][3]};
+                *reinterpret_cast<float4 *>(wp + c0 + 4) = float4{dwq[i][4], dwq[i][5], dwq[i][6], dwq[i][7]};
+                *reinterpret_cast<float4 *>(wp + C + c0) = float4{dwk[i][0], dwk[i][1], dwk[i][2], dwk[i][3]};
+                *reinterpret_cast<float4 *>(wp + C + c0 + 4) = float4{dwk[i][4], dwk[i][5], dwk[i][6], dwk[i][7]};
+            }
+    }
+}
+
+// dq_norm_w, dk_norm_w: the waves' partial sums, 64 channels per workgroup
+// of 16 waves; wave j adds partials j, j + 16, ... (four interleaved
+// accumulators), then the 16 wave totals are added in wave order.
+constexpr int PRB_WAVES = 16;
+__global__ __launch_bounds__(64 * PRB_WAVES) void prep_bwd_reduce_kernel(PrepBwdArgs ba) {
+    __shared__ float tot[PRB_WAVES][64];
+    const int C = ba.a.H * ba.a.D;
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + l;
+    const bool ok = c < 2 * C;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    int wv = w;
+    if (ok) {
+        const float *p = ba.wpart + c;
+        const size_t st = (size_t)2 * C * PRB_WAVES;
+        for (; wv + 3 * PRB_WAVES < ba.nwaves; wv += 4 * PRB_WAVES) {
+            s0 += p[(size_t)wv * 2 * C];
+            s1 += p[(size_t)wv * 2 * C + st];
+            s2 += p[(size_t)wv * 2 * C + 2 * st];
+            s3 += p[(size_t)wv * 2 * C + 3 * st];
+        }
+        for (; wv < ba.nwaves; wv += PRB_WAVES) s0 += p[(size_t)wv * 2 * C];
+    }
+    tot[w][l] = (s0 + s1) + (s2 + s3);
+    __syncthreads();
+    if (w == 0 && ok) {
+        float s = 0.f;
+        for (int i = 0; i < PRB_WAVES; ++i) s += tot[i][l];
+        if (c < C) {
+            if (ba.dqw) ba.dqw[c] = s;
+        } else if (ba.dkw) {
+            ba.dkw[c - C] = s;
+        }
+    }
+}
+
+long prep_bwd_grid(long ntok) {
+    long blocks = (ntok + PREP_TPB - 1) / PREP_TPB;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 65535) blocks = 65535;
+    return blocks;
+}
+
+template <bool F32IN, bool F32G, int LPH>
+hipError_t launch_prep_bwd(const PrepBwdArgs &ba, hipStream_t s) {
+    const PrepArgs &a = ba.a;
+    const long ntok = (long)a.B * a.N;
+    const int nseg = (a.H + 64 / LPH - 1) / (64 / LPH);
+    const dim3 grid((unsigned)prep_bwd_grid(ntok));
+    if (nseg <= 1) hipLaunchKernelGGL((prep_bwd_kernel<F32IN, F32G, LPH, 1>), grid, dim3(256), 0, s, ba);
+    else if (nseg <= 2) hipLaunchKernelGGL((prep_bwd_kernel<F32IN, F32G, LPH, 2>), grid, dim3(256), 0, s, ba);
+    else if (nseg <= 4) hipLaunchKernelGGL((prep_bwd_kernel<F32IN, F32G, LPH, 4>), grid, dim3(256), 0, s, ba);
+    else hipLaunchKernelGGL((prep_bwd_kernel<F32IN, F32G, LPH, 8>), grid, dim3(256), 0, s, ba);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !ba.wpart) return e;
+    const int C = a.H * a.D;
+    hipLaunchKernelGGL(prep_bwd_reduce_kernel, dim3((2 * C + 63) / 64), dim3(64 * PRB_WAVES), 0, s, ba);
+    return hipGetLastError();
+}
+
 }  // namespace
 }  // namespace gdn
 
@@ -377,5 +689,104 @@ extern "C" int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_n
         default: GDN_PREP_D(16) break;
     }
 #undef GDN_PREP_D
+    return gdn::check_hip(e, name);
+}
+
+extern "C" size_t gdn_prep_bwd_workspace_bytes(int B, int N, int H, int D) {
+    if (B < 0 || N < 0 || H <= 0 || D <= 0) return 0;
+    return (size_t)gdn::prep_bwd_grid((long)B * N) * 4 * 2 * H * D * sizeof(float);
+}
+
+extern "C" int gdn_prep_bwd(const void *qkv, const float *q_norm_w, const float *k_norm_w, const float *proj_q,
+                            const float *proj_kv, const float *rope_cos, const float *rope_sin, float k_scale,
+                            float norm_eps, const void *dq_out, const void *dk_out, const void *dv_out,
+                            const float *dk_pre_sq, const float *dk_post_sq, const float *dinflation_sq,
+                            float *dqkv, float *dq_norm_w, float *dk_norm_w, float *dproj_q, float *dproj_kv,
+                            int B, int N, int H, int D, int dtype, int grad_dtype, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    const char *name = "gdn_prep_bwd";
+    GDN_REQUIRE(B >= 0 && N >= 0 && H >= 0, GDN_EINVAL, "%s: negative size (B=%d N=%d H=%d)", name, B, N, H);
+    GDN_REQUIRE(dtype == GDN_DTYPE_F32 || dtype == GDN_DTYPE_BF16, GDN_EINVAL, "%s: unknown dtype %d", name, dtype);
+    GDN_REQUIRE(grad_dtype == GDN_DTYPE_F32 || grad_dtype == GDN_DTYPE_BF16, GDN_EINVAL,
+                "%s: unknown grad_dtype %d", name, grad_dtype);
+    GDN_REQUIRE(D > 0 && D % 16 == 0 && D <= 128, GDN_EUNSUPPORTED,
+                "%s: D=%d (supported: multiples of 16 up to 128)", name, D);
+    int lph = 2;
+    while (lph < D / 8) lph *= 2;
+    GDN_REQUIRE((long)H * 8 * lph <= 4096, GDN_EUNSUPPORTED,
+                "%s: H=%d heads of D=%d (at most 4096 / %d heads)", name, H, D, 8 * lph);
+    GDN_REQUIRE(isfinite(k_scale) && isfinite(norm_eps) && norm_eps >= 0.f, GDN_EINVAL,
+                "%s: k_scale and norm_eps must be finite, norm_eps >= 0", name);
+    GDN_REQUIRE(!dproj_q == !dproj_kv, GDN_EINVAL, "%s: dproj_q and dproj_kv are both given or both NULL", name);
+    const bool wgrad = dq_norm_w || dk_norm_w;
+    const size_t need = wgrad ? gdn_prep_bwd_workspace_bytes(B, N, H, D) : 0;
+    GDN_REQUIRE(workspace_bytes >= need, GDN_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", name,
+                workspace_bytes, need);
+    GDN_REQUIRE(need == 0 || (workspace && gdn::aligned(workspace, 16)), GDN_EINVAL,
+                "%s: workspace must be a 16-byte aligned device pointer", name);
+    if ((long)H == 0) return GDN_OK;
+    const bool any = (long)B * N > 0;
+    if (any) {
+        GDN_REQUIRE(qkv && proj_q && proj_kv && rope_cos && rope_sin && dq_out && dk_out && dv_out && dqkv,
+                    GDN_EINVAL, "%s: null tensor pointer", name);
+        GDN_REQUIRE(gdn::aligned(qkv, 16) && gdn::aligned(dq_out, 16) && gdn::aligned(dk_out, 16) &&
+                        gdn::aligned(dv_out, 16) && gdn::aligned(dqkv, 16) && gdn::aligned(rope_cos, 16) &&
+                        gdn::aligned(rope_sin, 16) && (!q_norm_w || gdn::aligned(q_norm_w, 16)) &&
+                        (!k_norm_w || gdn::aligned(k_norm_w, 16)),
+                    GDN_EINVAL, "%s: qkv, the gradients, dqkv, the weights and the RoPE tables must be 16-byte aligned",
+                    name);
+    }
+    GDN_REQUIRE(gdn::aligned(proj_q, 4) && gdn::aligned(proj_kv, 4) && (!dk_pre_sq || gdn::aligned(dk_pre_sq, 4)) &&
+                    (!dk_post_sq || gdn::aligned(dk_post_sq, 4)) && (!dinflation_sq || gdn::aligned(dinflation_sq, 4)) &&
+                    (!dproj_q || (gdn::aligned(dproj_q, 4) && gdn::aligned(dproj_kv, 4))) &&
+                    (!dq_norm_w || gdn::aligned(dq_norm_w, 4)) && (!dk_norm_w || gdn::aligned(dk_norm_w, 4)),
+                GDN_EINVAL, "%s: float tensors must be 4-byte aligned", name);
+    gdn::PrepBwdArgs ba;
+    gdn::PrepArgs &a = ba.a;
+    a.qkv = qkv;
+    a.qw = q_norm_w;
+    a.kw = k_norm_w;
+    a.proj_q = proj_q;
+    a.proj_kv = proj_kv;
+    a.cosv = rope_cos;
+    a.sinv = rope_sin;
+    a.k_scale = k_scale;
+    a.eps = norm_eps;
+    a.qo = a.ko = a.vo = nullptr;
+    a.pre = a.post = a.infl = nullptr;
+    a.B = B;
+    a.N = N;
+    a.H = H;
+    a.D = D;
+    ba.gq = dq_out;
+    ba.gk = dk_out;
+    ba.gv = dv_out;
+    ba.gpre = dk_pre_sq;
+    ba.gpost = dk_post_sq;
+    ba.ginf = dinflation_sq;
+    ba.dqkv = dqkv;
+    ba.dpq = dproj_q;
+    ba.dpkv = dproj_kv;
+    ba.wpart = wgrad ? reinterpret_cast<float *>(workspace) : nullptr;
+    ba.dqw = dq_norm_w;
+    ba.dkw = dk_norm_w;
+    ba.nwaves = (int)gdn::prep_bwd_grid((long)B * N) * 4;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    const int sel = (dtype == GDN_DTYPE_F32 ? 2 : 0) + (grad_dtype == GDN_DTYPE_F32 ? 1 : 0);
+#define GDN_PREPB_D(DD)                                                            \
+    switch (sel) {                                                                 \
+        case 0: e = gdn::launch_prep_bwd<false, false, DD>(ba, s); break;          \
+        case 1: e = gdn::launch_prep_bwd<false, true, DD>(ba, s); break;           \
+        case 2: e = gdn::launch_prep_bwd<true, false, DD>(ba, s); break;           \
+        default: e = gdn::launch_prep_bwd<true, true, DD>(ba, s); break;           \
+    }
+    switch (lph) {
+        case 2: GDN_PREPB_D(2) break;
+        case 4: GDN_PREPB_D(4) break;
+        case 8: GDN_PREPB_D(8) break;
+        default: GDN_PREPB_D(16) break;
+    }
+#undef GDN_PREPB_D
     return gdn::check_hip(e, name);
 }

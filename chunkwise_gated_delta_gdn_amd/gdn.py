@@ -29,6 +29,7 @@ EXPORTS = (
     "gdn_prep",
     "gdn_bwd", "gdn_bwd_workspace_bytes",
     "gdn_recurrent_bwd", "gdn_recurrent_bwd_workspace_bytes",
+    "gdn_prep_bwd", "gdn_prep_bwd_workspace_bytes",
 )
 
 
@@ -77,6 +78,11 @@ def _load():
     lib.gdn_recurrent_bwd.restype = I
     lib.gdn_recurrent_bwd_workspace_bytes.argtypes = [I] * 6
     lib.gdn_recurrent_bwd_workspace_bytes.restype = Z
+    lib.gdn_prep_bwd.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I,
+                                 P, Z, P]
+    lib.gdn_prep_bwd.restype = I
+    lib.gdn_prep_bwd_workspace_bytes.argtypes = [I] * 4
+    lib.gdn_prep_bwd_workspace_bytes.restype = Z
     return lib
 
 
@@ -382,3 +388,42 @@ def gdn_recurrent_bwd(q, k, v, beta, log_decay, dout, frames, scale=1.0, h0=None
                                 _ptr(dh0), B, H, F, N // F, D, dt, _ptr(ws), nws, _stream(dev))
     _check("gdn_recurrent_bwd", rc)
     return dq, dk, dv, dbeta, dg, dh0
+
+
+def gdn_prep_bwd(qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, k_scale, norm_eps,
+                 dq, dk, dv, dk_pre_sq=None, dk_post_sq=None, dinflation_sq=None, weight_grads=True,
+                 proj_grads=True):
+    """Gradients of :func:`gdn_prep`.  Forward arguments as there; dq, dk, dv
+    (B,H,N,D) gradients of its q, k, v outputs (bf16 or fp32, one dtype);
+    dk_pre_sq, dk_post_sq, dinflation_sq (B,H,N) fp32 or None.  Returns a
+    dict: dqkv (B,N,3,H,D) fp32, dq_norm_w and dk_norm_w (H*D) (None unless
+    weight_grads), dproj_q and dproj_kv (B,N,4,4) (None unless proj_grads)."""
+    _dev(qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin, dq, dk, dv, dk_pre_sq, dk_post_sq,
+         dinflation_sq)
+    for name, t in (("q_norm_w", q_norm_w), ("k_norm_w", k_norm_w), ("proj_q", proj_q), ("proj_kv", proj_kv),
+                    ("rope_cos", rope_cos), ("rope_sin", rope_sin), ("dk_pre_sq", dk_pre_sq),
+                    ("dk_post_sq", dk_post_sq), ("dinflation_sq", dinflation_sq)):
+        _f32(t, name)
+    B, N, three, H, D = qkv.shape
+    if three != 3:
+        raise ValueError("qkv must be (B, N, 3, H, D)")
+    if dq.shape != (B, H, N, D) or dk.shape != dq.shape or dv.shape != dq.shape:
+        raise ValueError("dq, dk, dv must be (B, H, N, D)")
+    if dk.dtype != dq.dtype or dv.dtype != dq.dtype:
+        raise ValueError("dq, dk, dv must share one dtype")
+    dev = qkv.device
+    out = {"dqkv": torch.empty((B, N, 3, H, D), dtype=torch.float32, device=dev)}
+    out["dq_norm_w"] = torch.empty(H * D, dtype=torch.float32, device=dev) if weight_grads else None
+    out["dk_norm_w"] = torch.empty(H * D, dtype=torch.float32, device=dev) if weight_grads else None
+    out["dproj_q"] = torch.empty((B, N, 4, 4), dtype=torch.float32, device=dev) if proj_grads else None
+    out["dproj_kv"] = torch.empty((B, N, 4, 4), dtype=torch.float32, device=dev) if proj_grads else None
+    nws = _lib.gdn_prep_bwd_workspace_bytes(B, N, H, D) if weight_grads else 0
+    ws, nws = _workspace(nws, dev)
+    rc = _lib.gdn_prep_bwd(_ptr(qkv), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(proj_q), _ptr(proj_kv),
+                           _ptr(rope_cos), _ptr(rope_sin), float(k_scale), float(norm_eps), _ptr(dq), _ptr(dk),
+                           _ptr(dv), _ptr(dk_pre_sq), _ptr(dk_post_sq), _ptr(dinflation_sq), _ptr(out["dqkv"]),
+                           _ptr(out["dq_norm_w"]), _ptr(out["dk_norm_w"]), _ptr(out["dproj_q"]),
+                           _ptr(out["dproj_kv"]), B, N, H, D, _dtype_code(qkv.dtype), _dtype_code(dq.dtype),
+                           _ptr(ws), nws, _stream(dev))
+    _check("gdn_prep_bwd", rc)
+    return out

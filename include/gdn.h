@@ -10,6 +10,7 @@
  *   gdn_recurrent_den_fwd   its normaliser (denominator) stream
  *   gdn_prep                camera-branch per-token prep (RMSNorm over all
  *                           channels, ReLU, K-scale, UCPE 4x4, RoPE, ||k||^2)
+ *   gdn_prep_bwd            gradients of gdn_prep (qkv, norm weights, projections)
  *   gdn_bwd                 gradients of gdn_chunk_fwd (q, k, v, beta, g, h0)
  *   gdn_recurrent_bwd       gradients of gdn_recurrent_fwd (forward direction)
  *
@@ -314,6 +315,40 @@ int gdn_prep(const void *qkv, const float *q_norm_w, const float *k_norm_w,
              void *q_out, void *k_out, void *v_out,
              float *k_pre_sq, float *k_post_sq, float *inflation_sq,
              int B, int N, int H, int D, int dtype, int out_dtype, void *stream);
+
+/*
+ * gdn_prep_bwd - gradients of gdn_prep ([cam] _cam_prep_bwd_kernel and
+ * _cam_prep_bwd_dispatch, including the RMSNorm backward the page leaves
+ * to torch).  Reverse mode through the prep's steps, with the forward's
+ * values recomputed per token: the norm outputs send
+ * 2 k_out (dk_post_sq + [post > 1e-12] dinflation_sq / max(pre, 1e-12)) to
+ * k_out and 2 k~ (dk_pre_sq - [pre > 1e-12] dinflation_sq max(post, 1e-12)
+ * / pre^2) to k~; RoPE^T on the second half (gx[d] = gy[d] cos[d] +
+ * gy[d^1] sin[d^1]); UCPE^T on the first (gx_g = P^T gy_g, dP += gy_g x_g^T
+ * over groups and heads); the ReLU mask and K-scale; the RMSNorm backward
+ * over all C channels (gx_c = inv w_c ga_c - inv^3/C x_c sum ga w x, and
+ * dw_c = sum over tokens of ga_c x_c inv).
+ *
+ *   qkv, weights, proj, tables, k_scale, norm_eps: as gdn_prep (dtype)
+ *   dq_out, dk_out, dv_out  (B, H, N, D)  grad_dtype (dL/d of the outputs)
+ *   dk_pre_sq, dk_post_sq, dinflation_sq  (B, H, N) float32, nullable (zero)
+ *   dqkv                    (B, N, 3, H, D) float32
+ *   dq_norm_w, dk_norm_w    (H*D) float32, nullable (not formed)
+ *   dproj_q, dproj_kv       (B, N, 4, 4) float32, both or neither nullable
+ * Supported: as gdn_prep.  The work space (gdn_prep_bwd_workspace_bytes,
+ * needed only for the weight gradients) holds one partial sum of the
+ * weight gradients per wave; they are added in a fixed order.
+ */
+int gdn_prep_bwd(const void *qkv, const float *q_norm_w, const float *k_norm_w,
+                 const float *proj_q, const float *proj_kv,
+                 const float *rope_cos, const float *rope_sin, float k_scale, float norm_eps,
+                 const void *dq_out, const void *dk_out, const void *dv_out,
+                 const float *dk_pre_sq, const float *dk_post_sq, const float *dinflation_sq,
+                 float *dqkv, float *dq_norm_w, float *dk_norm_w, float *dproj_q, float *dproj_kv,
+                 int B, int N, int H, int D, int dtype, int grad_dtype,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+size_t gdn_prep_bwd_workspace_bytes(int B, int N, int H, int D);
 
 /*
  * gdn_bwd - gradients of gdn_chunk_fwd's outputs (o, hT) ([dp] lists the
