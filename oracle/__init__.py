@@ -22,6 +22,7 @@ receives; outputs are float64):
 * :func:`gdn_recurrent_bwd`        - O6, gradients of O1 (reverse mode).
 * :func:`frame_scan_bwd`           - O7, gradients of O4 (reverse mode).
 * :func:`cam_prep_bwd`             - O8, gradients of O3 (reverse mode).
+* :func:`deltaproduct_bwd`         - O9, gradients of O2 (reverse mode).
 * :func:`invert_se3`               - closed-form rigid-transform inverse.
 """
 from __future__ import annotations
@@ -70,12 +71,14 @@ def _load():
                                           P, P, P, P, P, P, I]
     lib.oracle_cam_prep_bwd.argtypes = [I, I, I, I, P, P, P, P, P, P, P, D, D, P, P, P, P, P, P, P, P, P,
                                         P, P, I]
+    lib.oracle_deltaproduct_bwd.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, D, P, P, P, P, P, P, P, P, P, I]
     lib.oracle_invert_se3.argtypes = [ctypes.c_long, P, P]
     lib.oracle_invert_se3.restype = None
     lib.oracle_max_threads.argtypes = []
     for fn in (lib.oracle_gdn_recurrent, lib.oracle_gdn_recurrent_bwd, lib.oracle_frame_scan_bwd,
                lib.oracle_deltaproduct_recurrent,
-               lib.oracle_cam_prep, lib.oracle_cam_prep_bwd, lib.oracle_frame_scan, lib.oracle_max_threads):
+               lib.oracle_cam_prep, lib.oracle_cam_prep_bwd, lib.oracle_deltaproduct_bwd, lib.oracle_frame_scan,
+               lib.oracle_max_threads):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -165,6 +168,29 @@ def deltaproduct_recurrent(q, k, v, beta, g, mask, scale=1.0, h0=None, nthreads=
                                                _ptr(h0), _ptr(o), _ptr(hT), int(nthreads))
     _check(rc, "deltaproduct_recurrent")
     return o, hT
+
+
+def deltaproduct_bwd(q, k, v, beta, g, mask, dout, scale=1.0, h0=None, dhT=None, nthreads=0):
+    """O9.  Gradients of :func:`deltaproduct_recurrent`'s (o, hT) under dout
+    (B,T,H,Dv) and dhT (B,H,r*dk,Dv, or None).  Returns (dq, dk, dv, dbeta
+    (B,T,H,r), dg (B,T,H), dh0) in float64."""
+    q, k, v, beta, g, dout, h0, dhT = map(_f32, (q, k, v, beta, g, dout, h0, dhT))
+    mask = np.ascontiguousarray(mask, np.float64)
+    B, T, H, K = q.shape
+    r = mask.shape[0]
+    assert mask.shape == (r, r) and K % r == 0 and beta.shape == (B, T, H, r)
+    Dv = v.shape[-1]
+    dq = np.zeros((B, T, H, K), np.float64)
+    dk = np.zeros((B, T, H, K), np.float64)
+    dv = np.zeros((B, T, H, Dv), np.float64)
+    dbeta = np.zeros((B, T, H, r), np.float64)
+    dg = np.zeros((B, T, H), np.float64)
+    dh0 = np.zeros((B, H, K, Dv), np.float64)
+    rc = _load().oracle_deltaproduct_bwd(B, T, H, r, K // r, Dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                         _ptr(mask), float(scale), _ptr(h0), _ptr(dout), _ptr(dhT), _ptr(dq),
+                                         _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dg), _ptr(dh0), int(nthreads))
+    _check(rc, "deltaproduct_bwd")
+    return dq, dk, dv, dbeta, dg, dh0
 
 
 def cam_prep(qkv, q_norm_w, k_norm_w, proj_q, proj_kv, rope_cos, rope_sin,

@@ -766,3 +766,166 @@ int oracle_frame_scan_bwd(int B, int H, int F, int S, int D,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* O9: backward of O2 (gated DeltaProduct), reverse mode through the token  */
+/* steps of O2, last token first.  With w_a = E_a k_{t,a} (write key),      */
+/* e_a = sum_b M[a][b] E_b k_{t,b} (erase key), P = exp(g_t) S_{t-1},       */
+/* p_a = P^T e_a, r_a = v_t - p_a, S_t = P + sum_a beta_a w_a r_a^T and     */
+/* o_t = scale S_t^T q_t, each token's adjoint, given dS = dL/dS_t:          */
+/*   read-out : dS += scale q do^T,  dq = scale S_t do                      */
+/*   correct  : u_a = dS^T w_a,  dbeta_a = u_a . r_a,  dv += beta_a u_a,    */
+/*              dp_a = -beta_a u_a,  dw_a = beta_a dS r_a,  dP = dS         */
+/*   predict  : dP += sum_a e_a dp_a^T,  de_a = P dp_a                      */
+/*   keys     : dk_{t,a} = E_a^T dw_a + sum_c M[c][a] E_a^T de_c            */
+/*   gate     : dg = <dP, P>,  dS_{t-1} = exp(g_t) dP                        */
+/* and dh0 = dS_0.  States are recomputed from one kept every 64 tokens.    */
+/* Layouts as O2; dout (B,T,H,Dv); dhT, dh0 (B,H,r*dk,Dv); dq, dk           */
+/* (B,T,H,r*dk); dv (B,T,H,Dv); dbeta (B,T,H,r); dg (B,T,H).                */
+/* ------------------------------------------------------------------------ */
+static void o2_step(int r, int dk, int Dv, double *S, double *pa, double *e, const float *kt, const float *vt,
+                    const float *bt, const double *mask, double decay) {
+    int K = r * dk;
+    for (int i = 0; i < K * Dv; ++i) S[i] *= decay;
+    for (int a = 0; a < r; ++a) {
+        for (int bb = 0; bb < r; ++bb)
+            for (int c = 0; c < dk; ++c) e[bb * dk + c] = mask[a * r + bb] * (double)kt[bb * dk + c];
+        for (int j = 0; j < Dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < K; ++i) acc += S[(size_t)i * Dv + j] * e[i];
+            pa[(size_t)a * Dv + j] = acc;
+        }
+    }
+    for (int a = 0; a < r; ++a)
+        for (int c = 0; c < dk; ++c) {
+            int i = a * dk + c;
+            double ki = (double)bt[a] * (double)kt[i];
+            for (int j = 0; j < Dv; ++j) S[(size_t)i * Dv + j] += ki * ((double)vt[j] - pa[(size_t)a * Dv + j]);
+        }
+}
+
+int oracle_deltaproduct_bwd(int B, int T, int H, int r, int dk, int Dv,
+                            const float *q, const float *k, const float *v,
+                            const float *beta, const float *g, const double *mask, double scale,
+                            const float *h0, const float *dout, const float *dhT,
+                            double *dq, double *dkk, double *dv, double *dbeta,
+                            double *dg, double *dh0, int nthreads) {
+    if (B < 0 || T < 0 || H < 0 || r <= 0 || r > 8 || dk <= 0 || Dv <= 0) return -1;
+    set_threads(nthreads);
+    const int SEG = 64;
+    int K = r * dk;
+    int nseg = (T + SEG - 1) / SEG;
+    int npairs = B * H;
+    size_t sz = (size_t)K * Dv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < npairs; ++bh) {
+        int b = bh / H, h = bh % H;
+        double *ck = (double *)malloc(sizeof(double) * sz * (size_t)(nseg > 0 ? nseg : 1));
+        double *st = (double *)malloc(sizeof(double) * sz * (SEG + 1));
+        double *S = (double *)calloc(sz, sizeof(double));
+        double *dS = (double *)calloc(sz, sizeof(double));
+        double *dP = (double *)malloc(sizeof(double) * sz);
+        double *pa = (double *)malloc(sizeof(double) * (size_t)r * Dv);
+        double *ra = (double *)malloc(sizeof(double) * (size_t)r * Dv);
+        double *ua = (double *)malloc(sizeof(double) * (size_t)r * Dv);
+        double *e = (double *)malloc(sizeof(double) * (size_t)r * K);   /* erase key of each step */
+        double *de = (double *)malloc(sizeof(double) * (size_t)K);
+        if (h0)
+            for (size_t i = 0; i < sz; ++i) S[i] = (double)h0[(size_t)bh * sz + i];
+        for (int t = 0; t < T; ++t) {
+            size_t row = ((size_t)b * T + t) * H + h;
+            if (t % SEG == 0) memcpy(ck + (size_t)(t / SEG) * sz, S, sizeof(double) * sz);
+            o2_step(r, dk, Dv, S, pa, e, k + row * K, v + row * Dv, beta + row * r, mask, exp((double)g[row]));
+        }
+        if (dhT)
+            for (size_t i = 0; i < sz; ++i) dS[i] = (double)dhT[(size_t)bh * sz + i];
+        for (int s = nseg - 1; s >= 0; --s) {
+            int t0 = s * SEG, t1 = t0 + SEG < T ? t0 + SEG : T;
+            memcpy(st, ck + (size_t)s * sz, sizeof(double) * sz);
+            for (int t = t0; t < t1; ++t) {
+                size_t row = ((size_t)b * T + t) * H + h;
+                double *nx = st + (size_t)(t - t0 + 1) * sz;
+                memcpy(nx, st + (size_t)(t - t0) * sz, sizeof(double) * sz);
+                o2_step(r, dk, Dv, nx, pa, e, k + row * K, v + row * Dv, beta + row * r, mask, exp((double)g[row]));
+            }
+            for (int t = t1 - 1; t >= t0; --t) {
+                size_t row = ((size_t)b * T + t) * H + h;
+                const float *qt = q + row * K, *kt = k + row * K, *vt = v + row * Dv, *bt = beta + row * r;
+                const float *dot = dout + row * Dv;
+                const double *Sp = st + (size_t)(t - t0) * sz;       /* S_{t-1} */
+                const double *Sc = st + (size_t)(t - t0 + 1) * sz;   /* S_t */
+                double a = exp((double)g[row]);
+                /* read-out */
+                for (int i = 0; i < K; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < Dv; ++j) {
+                        dS[(size_t)i * Dv + j] += scale * (double)qt[i] * (double)dot[j];
+                        acc += Sc[(size_t)i * Dv + j] * (double)dot[j];
+                    }
+                    dq[row * K + i] = scale * acc;
+                }
+                /* erase keys, predictions p_a = (a S_prev)^T e_a, residuals, u_a = dS^T w_a */
+                for (int st_ = 0; st_ < r; ++st_)
+                    for (int bb = 0; bb < r; ++bb)
+                        for (int c = 0; c < dk; ++c)
+                            e[(size_t)st_ * K + bb * dk + c] = mask[st_ * r + bb] * (double)kt[bb * dk + c];
+                for (int j = 0; j < Dv; ++j) dv[row * Dv + j] = 0.0;
+                for (int st_ = 0; st_ < r; ++st_) {
+                    double db = 0.0, bs = (double)bt[st_];
+                    for (int j = 0; j < Dv; ++j) {
+                        double p = 0.0, u = 0.0;
+                        for (int i = 0; i < K; ++i) p += a * Sp[(size_t)i * Dv + j] * e[(size_t)st_ * K + i];
+                        for (int c = 0; c < dk; ++c)
+                            u += dS[(size_t)(st_ * dk + c) * Dv + j] * (double)kt[st_ * dk + c];
+                        pa[(size_t)st_ * Dv + j] = p;
+                        ra[(size_t)st_ * Dv + j] = (double)vt[j] - p;
+                        ua[(size_t)st_ * Dv + j] = u;
+                        dv[row * Dv + j] += bs * u;
+                        db += u * ((double)vt[j] - p);
+                    }
+                    dbeta[row * r + st_] = db;
+                }
+                /* dP = dS + sum_a e_a dp_a^T (dp_a = -beta_a u_a); dg; write-key and erase-key gradients */
+                double dgs = 0.0;
+                for (size_t i = 0; i < sz; ++i) dP[i] = dS[i];
+                for (int st_ = 0; st_ < r; ++st_) {
+                    double bs = (double)bt[st_];
+                    for (int i = 0; i < K; ++i) {
+                        double ei = e[(size_t)st_ * K + i];
+                        if (ei == 0.0) continue;
+                        for (int j = 0; j < Dv; ++j) dP[(size_t)i * Dv + j] += ei * (-bs * ua[(size_t)st_ * Dv + j]);
+                    }
+                }
+                for (int i = 0; i < K; ++i) dkk[row * K + i] = 0.0;
+                for (int st_ = 0; st_ < r; ++st_) {
+                    double bs = (double)bt[st_];
+                    /* dw_a = beta_a dS r_a on row block a */
+                    for (int c = 0; c < dk; ++c) {
+                        int i = st_ * dk + c;
+                        double acc = 0.0;
+                        for (int j = 0; j < Dv; ++j) acc += dS[(size_t)i * Dv + j] * ra[(size_t)st_ * Dv + j];
+                        dkk[row * K + i] += bs * acc;
+                    }
+                    /* de_a = P dp_a, sent to the sub-keys through the mask */
+                    for (int i = 0; i < K; ++i) {
+                        double acc = 0.0;
+                        for (int j = 0; j < Dv; ++j) acc += a * Sp[(size_t)i * Dv + j] * (-bs * ua[(size_t)st_ * Dv + j]);
+                        de[i] = acc;
+                    }
+                    for (int bb = 0; bb < r; ++bb)
+                        for (int c = 0; c < dk; ++c) dkk[row * K + bb * dk + c] += mask[st_ * r + bb] * de[bb * dk + c];
+                }
+                for (size_t i = 0; i < sz; ++i) {
+                    dgs += dP[i] * a * Sp[i];
+                    dS[i] = a * dP[i];
+                }
+                dg[row] = dgs;
+            }
+        }
+        if (dh0)
+            for (size_t i = 0; i < sz; ++i) dh0[(size_t)bh * sz + i] = dS[i];
+        free(ck); free(st); free(S); free(dS); free(dP); free(pa); free(ra); free(ua); free(e); free(de);
+    }
+    return 0;
+}
+
