@@ -8,7 +8,7 @@ here on first use.
 """
 
 _BINDING = ("gdn_chunk_fwd", "deltaproduct_chunk_fwd", "gdn_recurrent_fwd", "gdn_recurrent_den_fwd", "gdn_prep",
-            "gdn_bwd", "gdn_recurrent_bwd", "gdn_prep_bwd")
+            "gdn_bwd", "gdn_recurrent_bwd", "gdn_prep_bwd", "deltaproduct_bwd")
 
 
 def __getattr__(name):

@@ -24,4 +24,4 @@ int check_hip(hipError_t e, const char *what) {
 
 extern "C" const char *gdn_last_error(void) { return gdn::g_err; }
 
-extern "C" int gdn_abi_version(void) { return 4; }
+extern "C" int gdn_abi_version(void) { return 5; }

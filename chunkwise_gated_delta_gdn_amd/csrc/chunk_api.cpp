@@ -161,6 +161,7 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
     a.out_bf16 = out_dtype == GDN_DTYPE_BF16;
     a.scale = scale;
     a.tmatT = nullptr;
+    a.atilT = nullptr;
     a.sst = a.rst = nullptr;
     for (int i = 0; i < 4; ++i) a.mask[i] = 0.f;
     if (r == 1) {

@@ -31,6 +31,18 @@
 // The forward's chunk-start states S and residuals R come from the forward
 // state pass (chunk_chain1_kernel<KD, 64, 3>); T, T^T and the transposed
 // scores from chunk_prep2_kernel<KD, 64, true>.
+//
+// DPE: the first pass of the DeltaProduct backward (sub-key 0 of a 2 x 2
+// lower unitriangular step mask [[1, 0], [m, 1]]).  Its errors
+// e = R - A~ Vn (A~ = strict_lower((K K^T) o Gam)) feed the second pass
+// through v' = (1 - m) v + m e, so the second pass's gradient of v' brings
+// dE = m dv'.  Then dV0 gains -A~^T dE, the state recurrence -K^T diag(gamma)
+// dE, and with dR = diag(beta) dX + dE (the total gradient of R):
+//   dV = dR + (1 - m) dv' (+ m dv' through dE: dV = diag(beta) dX + dv'),
+//   dB = strict_lower(-dR Vn^T) the gradient of the gram K K^T o Gam, taking
+//   the place of diag(beta) dA (M2 = dB o Gam, W = M1 o (Q K^T) + dB o A~),
+//   dK_R = -diag(gamma) dR S^T,  dbeta_t = sum_v dX (R - A~ Vn) = sum_v dX e,
+// and dg adds the second pass's.
 #pragma once
 
 #include "chunk_chain1.h"
@@ -44,6 +56,7 @@ struct BwdChunkArgs {
     float *dq, *dk, *dv, *dbeta, *dg, *dh0;
     float *dsst;             // gradient of the state leaving each chunk, (B*H, NT, Dk, Dv) fp32
     float *dxst;             // dX per chunk, (B*H, NT, Dv/16, 64 lanes, 16) fp32, accumulator order
+    const float *dvprev;     // DeltaProduct first pass: the second pass's gradient of v', (B, T, H, Dv)
 };
 
 // ---------------------------------------------------------------------------
@@ -115,7 +128,7 @@ __device__ __forceinline__ void kt_frags(const u16 *ks, bf16x8 (&ka)[KD / 16][2]
     }
 }
 
-template <int KD>
+template <int KD, bool DPE = false>
 __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(BwdChunkArgs ba) {
     using S = BChainShape<KD>;
     constexpr int C = S::C, BV = S::BV, NTT = S::NTT, NKS = S::NKS, NST = S::NST, NCS = S::NCS, NKC = S::NKC;
@@ -163,7 +176,7 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
         for (int ti = 0; ti < NST; ++ti) {
             Sreg[ti] = zero4();
             if (ba.dhT) {
-                const float *hp = ba.dhT + (size_t)bh * KD * Dv + v0 + c16;
+                const float *hp = ba.dhT + ((size_t)bh * args.hrows + args.hoff) * Dv + v0 + c16;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Sreg[ti][e] = hp[(size_t)feat(ti, e) * Dv];
             }
@@ -172,6 +185,7 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
         lds_barrier();                          // step 0: the helpers' first chunk
         for (int c = NT - 1; c >= 0; --c) {
             const int sq = ring(c), p = c & 1;
+
             const u16 *ks = Ks(sq), *tt_ = Tt(sq);
             const float *gp = gA(sq);
             bf16x8 kf[NTT][NKS];
@@ -182,17 +196,19 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
                     const int r = tt * 16 + c16;
                     kf[tt][m] = ld8(ks + r * LDK + (((4 * m + g) ^ kswz<NKC>(r)) << 3));
                 }
-            bf16x8 sb[NKS];
-#pragma unroll
-            for (int m = 0; m < NKS; ++m) sb[m] = frag_hi(Sreg[2 * m], Sreg[2 * m + 1]);
-            // X1 = K dS'
+            // X1 = K dS' (dS' as hi + lo bf16)
             floatx4 x1[NTT];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) x1[tt] = zero4();
 #pragma unroll
-            for (int m = 0; m < NKS; ++m)
+            for (int m = 0; m < NKS; ++m) {
+                bf16x8 sh, sl;
+                frag_split(Sreg[2 * m], Sreg[2 * m + 1], sh, sl);
 #pragma unroll
-                for (int tt = 0; tt < NTT; ++tt) x1[tt] = mfma32(kf[tt][m], sb[m], x1[tt]);
+                for (int tt = 0; tt < NTT; ++tt) x1[tt] = mfma32(kf[tt][m], sh, x1[tt]);
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt) x1[tt] = mfma32(kf[tt][m], sl, x1[tt]);
+            }
             bf16x8 ka[NST][NCS];
             kt_frags<KD>(ks, ka);
             // T^T fragments: row tile st, 32-token step m (t > s only: 2m + 1 >= st)
@@ -230,12 +246,33 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
 #pragma unroll
                 for (int st = 0; st < NTT; ++st)
                     if (2 * m + 1 >= st) dx[st] = mfma32(tf[st][m], dvh[m], dx[st]);
-            // Z = -gamma beta dX (hi + lo); dS = Lambda dS' + E + K^T Z
+            // DPE: dE = m dv' of this chunk (rows tt*16 + 4g + e, column v0 + c16,
+            // zero past T), used for Z
+            floatx4 dE[NTT];
+            if constexpr (DPE) {
+                const float *dp = ba.dvprev + ((size_t)b * T * H + h) * Dv + v0 + c16;
+                const float mc = args.mcoef;
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = c * C + tt * 16 + 4 * g + e;
+                        const float x = dp[(size_t)min(t, tlast) * H * Dv];
+                        dE[tt][e] = t <= tlast ? mc * x : 0.f;
+                    }
+            }
+            // Z = -gamma beta dX (DPE: -gamma (beta dX + dE)), hi + lo;
+            // dS = Lambda dS' + E + K^T Z
             floatx4 z[NTT];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) z[tt][e] = -(eg[tt][e] * bt[tt][e]) * dx[tt][e];
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (DPE)
+                        z[tt][e] = -eg[tt][e] * (bt[tt][e] * dx[tt][e] + dE[tt][e]);
+                    else
+                        z[tt][e] = -(eg[tt][e] * bt[tt][e]) * dx[tt][e];
+                }
             bf16x8 zh[NCS], zl[NCS];
 #pragma unroll
             for (int m = 0; m < NCS; ++m) frag_split(z[2 * m], z[2 * m + 1], zh[m], zl[m]);
@@ -275,7 +312,7 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
         }
         __syncthreads();
         if (ba.dh0) {
-            float *hp = ba.dh0 + (size_t)bh * KD * Dv + v0 + c16;
+            float *hp = ba.dh0 + ((size_t)bh * args.hrows + args.hoff) * Dv + v0 + c16;
 #pragma unroll
             for (int ti = 0; ti < NST; ++ti)
 #pragma unroll
@@ -312,14 +349,38 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
                 *reinterpret_cast<floatx4 *>(sp + (size_t)f * Dv) = x;
             }
         };
-        u32x4 pf[NLOW];
+        u32x4 pf[NLOW], af[NLOW];
         auto load_pf = [&](int c) {
             c = c < 0 ? 0 : c;                  // (past the first chunk: loaded again, unused)
             const uint4 *pc = reinterpret_cast<const uint4 *>(args.pfrag) + ((size_t)bh * NT + c) * NLOW * 64 + l;
 #pragma unroll
             for (int i = 0; i < NLOW; ++i) pf[i] = __builtin_bit_cast(u32x4, pc[i * 64]);
+            if constexpr (DPE) {                // A~^T fragments, the same layout
+                const uint4 *ac = reinterpret_cast<const uint4 *>(args.atilT) + ((size_t)bh * NT + c) * NLOW * 64 + l;
+#pragma unroll
+                for (int i = 0; i < NLOW; ++i) af[i] = __builtin_bit_cast(u32x4, ac[i * 64]);
+            }
         };
-        if (w == 2) load_pf(NT - 1);
+        // DPE: dE = m dv' of a chunk, this lane's rows tt*16 + 4g + e, column
+        // v0 + c16 (zero past T), loaded one step ahead
+        floatx4 dep[NTT];
+        auto load_de = [&](int c) {
+            c = c < 0 ? 0 : c;
+            const float *dp = ba.dvprev + ((size_t)b * T * H + h) * Dv + v0 + c16;
+            const float mc = args.mcoef;
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = c * C + tt * 16 + 4 * g + e;
+                    const float x = dp[(size_t)min(t, tlast) * H * Dv];
+                    dep[tt][e] = t <= tlast ? mc * x : 0.f;
+                }
+        };
+        if (w == 2) {
+            load_pf(NT - 1);
+            if constexpr (DPE) load_de(NT - 1);
+        }
         __syncthreads();
         for (int s = 0; s <= NT; ++s) {
             const int c = NT - 1 - s;
@@ -347,6 +408,14 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
                 bf16x8 gh[NCS], gl[NCS];
 #pragma unroll
                 for (int m = 0; m < NCS; ++m) frag_split(gd[2 * m], gd[2 * m + 1], gh[m], gl[m]);
+                floatx4 dcur[NTT];              // DPE: dE of this chunk
+                if constexpr (DPE) {
+                    if (w == 2) {
+#pragma unroll
+                        for (int tt = 0; tt < NTT; ++tt) dcur[tt] = dep[tt];
+                        load_de(c - 1);
+                    }
+                }
                 const u16 *qs = Qs(sq);
 #pragma unroll 1
                 for (int i = 0; i < NST / 2; ++i) {
@@ -364,10 +433,15 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
                     }
                     Ep(p)[ti * 64 + l] = ev;
                 }
-                if (w == 2) {                   // dV0 = scale Pm^T dO
+                if (w == 2) {                   // dV0 = scale Pm^T dO (DPE: - A~^T dE)
+                    shortx4 dh4[NTT], dl4[NTT];
+                    if constexpr (DPE) {
+#pragma unroll
+                        for (int tt = 0; tt < NTT; ++tt) split4(dcur[tt], dh4[tt], dl4[tt]);
+                    }
 #pragma unroll
                     for (int st = 0; st < NTT; ++st) {
-                        floatx4 acc = zero4();
+                        floatx4 acc = zero4(), acc2 = zero4();
 #pragma unroll
                         for (int tt = st; tt < NTT; ++tt) {
                             const u32x4 f = pf[tt * (tt + 1) / 2 + st];
@@ -375,9 +449,17 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
                             const shortx4 al = __builtin_bit_cast(shortx4, uint2{f[2], f[3]});
                             acc = mfma16(ah, vv[tt], acc);
                             acc = mfma16(al, vv[tt], acc);
+                            if constexpr (DPE) {
+                                const u32x4 fa = af[tt * (tt + 1) / 2 + st];
+                                const shortx4 bh_ = __builtin_bit_cast(shortx4, uint2{fa[0], fa[1]});
+                                const shortx4 bl_ = __builtin_bit_cast(shortx4, uint2{fa[2], fa[3]});
+                                acc2 = mfma16(bh_, dh4[tt], acc2);
+                                acc2 = mfma16(bh_, dl4[tt], acc2);
+                                acc2 = mfma16(bl_, dh4[tt], acc2);
+                            }
                         }
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[e] *= scale;
+                        for (int e = 0; e < 4; ++e) acc[e] = scale * acc[e] - acc2[e];
                         Dp(p)[st * 64 + l] = acc;
                     }
                     load_pf(c - 1);
@@ -397,9 +479,9 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
     constexpr int NGV = NGATE / 4;
     constexpr int NA = NDK + NDT + 1, NB = NDK + NDO + 1, NDMA = NA + NB;
     static_assert(NGV <= 64 && S::SZ_GA >= NGV * 16, "gate table: one partial wave load");
-    const size_t tokq = (size_t)H * KD, tokv = (size_t)H * Dv;
-    const u16 *kg = reinterpret_cast<const u16 *>(args.k) + ((size_t)b * T * H + h) * KD;
-    const u16 *qg = reinterpret_cast<const u16 *>(args.q) + ((size_t)b * T * H + h) * KD;
+    const size_t tokq = (size_t)H * args.kst, tokv = (size_t)H * Dv;
+    const u16 *kg = reinterpret_cast<const u16 *>(args.k) + ((size_t)b * T * H + h) * args.kst + args.koff;
+    const u16 *qg = reinterpret_cast<const u16 *>(args.q) + ((size_t)b * T * H + h) * args.kst + args.koff;
     const u16 *og = reinterpret_cast<const u16 *>(ba.dout) + ((size_t)b * T * H + h) * Dv + v0;
     const u16 *tg = reinterpret_cast<const u16 *>(args.tmatT) + (size_t)bh * NT * C * C;
     const float *gtg = reinterpret_cast<const float *>(args.gtab) + (size_t)bh * NT * NGATE;
@@ -560,7 +642,7 @@ __device__ __forceinline__ float sum16(float v) {
 // hi and lo bf16 of one value
 __device__ __forceinline__ void split1(float x, u16 &hi, u16 &lo) { split_bf16(x, hi, lo); }
 
-template <int KD>
+template <int KD, bool DPE = false>
 __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdChunkArgs ba) {
     using S = BGradShape<KD>;
     constexpr int C = S::C, NTT = S::NTT, NKS = S::NKS, NKC = S::NKC, DVM = S::DVM;
@@ -589,12 +671,30 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
     float *db1 = reinterpret_cast<float *>(smem + S::OFF_DB1), *g3 = reinterpret_cast<float *>(smem + S::OFF_G3);
     float *gS = reinterpret_cast<float *>(smem + S::OFF_GS), *ss = reinterpret_cast<float *>(smem + S::OFF_SS);
 
-    const size_t tokk = (size_t)H * KD, tokv = (size_t)H * Dv;
-    const size_t rowk0 = ((size_t)b * T * H + h) * KD, rowv0 = ((size_t)b * T * H + h) * Dv;
+    const size_t tokk = (size_t)H * args.kst, tokv = (size_t)H * Dv;
+    const size_t rowk0 = ((size_t)b * T * H + h) * args.kst + args.koff, rowv0 = ((size_t)b * T * H + h) * Dv;
     const u16 *og = reinterpret_cast<const u16 *>(ba.dout) + rowv0;
 
     u16 *dOc = reinterpret_cast<u16 *>(smem + S::OFF_DO);
+    constexpr int NLOW = NTT * (NTT + 1) / 2;
     // ---- phase 0 ----
+    // DPE: the second pass's v' gradient of this wave's value slice (rows
+    // tt*16 + 4g + e, column 16 w + c16) and the A~ fragments, loaded before
+    // everything else (the wait below then covers them)
+    floatx4 dvr[NTT];
+    u32x4 atf[NLOW];
+    if constexpr (DPE) {
+        const int ws = w < nvs ? w : 0;
+        const float *dp = ba.dvprev + rowv0 + 16 * ws + c16;
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dvr[tt][e] = dp[(size_t)min(t0 + tt * 16 + 4 * g + e, T - 1) * tokv];
+        const uint4 *ap = reinterpret_cast<const uint4 *>(args.atil) + ((size_t)bh * NT + c) * NLOW * 64 + l;
+#pragma unroll
+        for (int i = 0; i < NLOW; ++i) atf[i] = __builtin_bit_cast(u32x4, ap[i * 64]);
+        asm volatile("" ::: "memory");
+    }
     // LDS-direct loads of K, Q, dO first, then this wave's register loads;
     // the wait below (at most NREG outstanding) then covers the LDS-direct ones
     constexpr int NREG = 2 * NTT + 6 + 16;      // R, dX; T' fragments; S, dS' fragments
@@ -668,7 +768,7 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
                 if (l >= off) gs += y;
             }
             G2[l] = gs * LOG2E;
-            Bt[l] = ok ? args.beta[gi] : 0.f;
+            Bt[l] = ok ? args.beta[gi * args.bst + args.boff] : 0.f;
         }
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt((NREG & 15) | ((NREG >> 4) << 14) | 0x0070);
@@ -687,6 +787,13 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
             for (int e = 0; e < 4; ++e)
                 if (t0 + tt * 16 + 4 * g + e >= T) rr[tt][e] = xr[tt][e] = 0.f;
         }
+        if constexpr (DPE) {
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (t0 + tt * 16 + 4 * g + e >= T) dvr[tt][e] = 0.f;
+        }
         bf16x8 rh[2], rl[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) frag_split(rr[2 * m], rr[2 * m + 1], rh[m], rl[m]);
@@ -702,21 +809,54 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
                     vn[tt] = mfma32(tf[tt][m], rl[m], vn[tt]);
                 }
         }
+        // DPE: e = R - A~ Vn for dbeta (A~ tiles as A operands, Vn tiles as B
+        // operands in their accumulator layout, both hi + lo)
+        floatx4 ev[NTT];
+        if constexpr (DPE) {
+            shortx4 nh[NTT], nl[NTT];
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) split4(vn[tt], nh[tt], nl[tt]);
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) {
+                floatx4 u = zero4();
+#pragma unroll
+                for (int ss = 0; ss <= tt; ++ss) {
+                    const u32x4 f = atf[tt * (tt + 1) / 2 + ss];
+                    const shortx4 ah = __builtin_bit_cast(shortx4, uint2{f[0], f[1]});
+                    const shortx4 al = __builtin_bit_cast(shortx4, uint2{f[2], f[3]});
+                    u = mfma16(ah, nh[ss], u);
+                    u = mfma16(ah, nl[ss], u);
+                    u = mfma16(al, nh[ss], u);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ev[tt][e] = rr[tt][e] - u[e];
+            }
+        }
+        const float mc = args.mcoef;
         float *dvp = ba.dv + rowv0 + v0 + c16;
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = tt * 16 + 4 * g + e, t = t0 + r;
-                if (t < T) dvp[(size_t)t * tokv] = bt[tt][e] * xr[tt][e];
-                const float pb = sum16(xr[tt][e] * rr[tt][e]);
+                const float bx = bt[tt][e] * xr[tt][e];
+                // dV = beta dX (DPE: + dv'); the X rows hold dX (DPE: dR = beta dX + m dv')
+                float xs = xr[tt][e], pb;
+                if constexpr (DPE) {
+                    if (t < T) dvp[(size_t)t * tokv] = bx + dvr[tt][e];
+                    xs = bx + mc * dvr[tt][e];
+                    pb = sum16(xr[tt][e] * ev[tt][e]);
+                } else {
+                    if (t < T) dvp[(size_t)t * tokv] = bx;
+                    pb = sum16(xr[tt][e] * rr[tt][e]);
+                }
                 if (c16 == 0) db1[w * C + r] = pb;
                 u16 hi, lo;
                 const int at = swz_at<NPV>(r, v0 + c16);
                 split1(vn[tt][e], hi, lo);
                 Vh[at] = hi;
                 Vl[at] = lo;
-                split1(xr[tt][e], hi, lo);
+                split1(xs, hi, lo);
                 Xh[at] = hi;
                 Xl[at] = lo;
             }
@@ -767,7 +907,8 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
                 mval = s <= t ? scale * x[e] * gam : 0.f;
                 wv[e] = mval * y[e];
             } else {
-                const float da = s < t ? -x[e] : 0.f, bg = s < t ? y[e] * gam : 0.f, btt = Bt[t];
+                // DPE: x = dR Vn^T, and da is dB (beta already in dR)
+                const float da = s < t ? -x[e] : 0.f, bg = s < t ? y[e] * gam : 0.f, btt = DPE ? 1.f : Bt[t];
                 wv[e] = da * btt * bg;
                 mval = btt * da * gam;
                 dbv = da * bg;
@@ -778,7 +919,7 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
             (kind == 0 ? M1h : M2h)[at] = hi;
             (kind == 0 ? M1l : M2l)[at] = lo;
             const float rs = sum16(wv[e]);
-            if (kind == 1) {
+            if (!DPE && kind == 1) {
                 const float rb2 = sum16(dbv);
                 if (c16 == 0) db2[tj * C + t] = rb2;
             }
@@ -872,7 +1013,7 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
                 const int r = tt * 16 + 4 * g + e, t = t0 + r;
                 const float g2 = G2[r], gam = fast_exp2(g2), lam = fast_exp2(g2L - g2), btt = Bt[r];
                 const float qd = scale * gam * a[e];          // dQ_dir
-                const float kr = -gam * btt * d1[e];          // dK_R
+                const float kr = -gam * (DPE ? 1.f : btt) * d1[e];   // dK_R
                 const float ks_ = lam * d2[e];                // dK_S'
                 if (t < T) {
                     dqp[(size_t)t * tokk] = qd + bq[e];
@@ -896,7 +1037,7 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
         for (int i = 0; i < nvs; ++i) db += db1[i * C + r];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            db += db2[i * C + r];
+            if constexpr (!DPE) db += db2[i * C + r];
             dG += gr1[i * C + r] - gc1[i * C + r] + gr2[i * C + r] - gc2[i * C + r];
         }
         float sst = 0.f;
@@ -918,8 +1059,8 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
         }
         if (t < T) {
             const size_t gi = ((size_t)b * T + t) * H + h;
-            ba.dbeta[gi] = db;
-            ba.dg[gi] = dG;
+            ba.dbeta[gi * args.bst + args.boff] = db;
+            ba.dg[gi] = DPE ? ba.dg[gi] + dG : dG;   // DPE: the second pass's share is there
         }
     }
 }

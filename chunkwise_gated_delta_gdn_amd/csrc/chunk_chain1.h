@@ -52,7 +52,10 @@
 // DPM = 3 is the state pass of the backward: no output; every chunk's start
 // state S goes out row-major (fp32; waves 1 and 2 copy the published state,
 // half of the key rows each) and the chain wave writes the residual
-// R = V - e^G K S (this lane's 16 values, accumulator order).
+// R = V - e^G K S (this lane's 16 values, accumulator order).  The
+// DeltaProduct backward has two more such passes: DPM = 5 on sub-key 0,
+// which also writes v' as DPM = 1 does, and DPM = 4 on sub-key 1, which
+// reads v' as DPM = 2 does.
 #pragma once
 
 #include <type_traits>
@@ -142,11 +145,14 @@ template <int KD, int C, int DPM = 0>
 __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kernel(ChunkArgs args) {
     using S = Chain1Shape<KD, C>;
     static_assert(DPM == 0 || C == 64, "DeltaProduct and backward passes run 64-token chunks");
+    constexpr bool VIN = DPM == 2 || DPM == 4;  // values v' (fp32, read by the chain wave)
+    constexpr bool ERR = DPM == 1 || DPM == 5;  // per-token errors and v' out
+    constexpr bool BST = DPM >= 3;              // backward state pass: states and R out, no output
     constexpr int BV = S::BV, NTT = S::NTT, NKS = S::NKS, NST = S::NST, NCS = S::NCS, NKC = S::NKC;
     constexpr int LDK = S::LDK, LDT = S::LDT, LDV = S::LDV, LDSF = S::LDSF, LDVF = S::LDVF;
     constexpr int TSW = S::TSW;
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[DPM == 1 ? S::BYTES : S::BYTES_PLAIN];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[ERR ? S::BYTES : S::BYTES_PLAIN];
 
     const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -202,7 +208,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
                     if (feat(ti, e) < args.kw) Sreg[ti][e] = hp[(size_t)feat(ti, e) * Dv];
             }
         }
-        // DPM 2: this lane's values v' (rows tt*16 + 4g + e, column c16) of
+        // VIN: this lane's values v' (rows tt*16 + 4g + e, column c16) of
         // the next chunk, loaded one iteration ahead
         floatx4 vpre[NTT];
         auto load_vin = [&](int c) {
@@ -215,7 +221,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
                     vpre[tt][e] = vp[(size_t)t * H * Dv];
                 }
         };
-        if constexpr (DPM == 2) load_vin(0);
+        if constexpr (VIN) load_vin(0);
         __syncthreads();
         for (int c = 0, sq = 0; c < NT; ++c, sq = sq == 2 ? 0 : sq + 1) {
             const int p = c & 1;                 // St, Vn; staging buffers: sq = c % 3
@@ -233,8 +239,8 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
                     kf[tt][m] = ld8(ks + r * LDK + (((4 * m + g) ^ kswz<NKC>(r)) << 3));
                 }
             shortx4 vv[NTT];                     // V rows tt*16 + 4g + e, column c16
-            floatx4 vcur[NTT];                   // DPM 2: v' of this chunk
-            if constexpr (DPM == 2) {
+            floatx4 vcur[NTT];                   // VIN: v' of this chunk
+            if constexpr (VIN) {
 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt) vcur[tt] = vpre[tt];
                 if (c + 1 < NT) load_vin(c + 1);
@@ -288,7 +294,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
             floatx4 rr[NTT], vin4[NTT];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
-                if constexpr (DPM == 2) {
+                if constexpr (VIN) {
                     vin4[tt] = vcur[tt];
                 } else {
                     const uint2 v2 = __builtin_bit_cast(uint2, vv[tt]);
@@ -298,7 +304,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
 #pragma unroll
                 for (int e = 0; e < 4; ++e) rr[tt][e] = vin4[tt][e] - eg[tt][e] * y[tt][e];
             }
-            if constexpr (DPM == 3) {
+            if constexpr (BST) {
                 floatx4 *rp = reinterpret_cast<floatx4 *>(args.rst) + (((size_t)bh * NT + c) * nvb + vb) * 64 * NTT + l * NTT;
 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt) rp[tt] = rr[tt];
@@ -321,7 +327,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
             floatx4 vt4[NTT];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
-                if constexpr (DPM != 3) *reinterpret_cast<floatx4 *>(vnp + c16 * LDVF + tt * 16 + 4 * g) = vn[tt];
+                if constexpr (!BST) *reinterpret_cast<floatx4 *>(vnp + c16 * LDVF + tt * 16 + 4 * g) = vn[tt];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vt4[tt][e] = el[tt][e] * vn[tt][e];
             }
@@ -342,7 +348,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
             // S_start of chunk c goes out while the state MFMAs run (its LDS
             // writes then do not queue ahead of this chunk's operand reads)
             publish_state(p);
-            if constexpr (DPM == 1) {
+            if constexpr (ERR) {
                 // (issued after the state update's MFMAs: off the chain's path)
                 // per-token errors e = R - A~ V_new and v' = (1 - m) v + m e;
                 // A~ tile (tt, tj) is the A operand (rows t), V_new tile tj the B
@@ -409,8 +415,8 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
     constexpr int NLW = S::NLW;
     constexpr int NLOW = NTT * (NTT + 1) / 2;
     constexpr int NGV = S::NGATE / 4;           // 16-byte vectors of a gate table
-    constexpr int NDK = S::SZ_KS / 1024, NDT = S::SZ_TB / 1024, NDV = DPM == 2 ? 0 : S::SZ_BV / 1024;
-    constexpr int NDA = DPM == 1 ? S::SZ_AT / 1024 : 0;            // A~ fragments
+    constexpr int NDK = S::SZ_KS / 1024, NDT = S::SZ_TB / 1024, NDV = VIN ? 0 : S::SZ_BV / 1024;
+    constexpr int NDA = ERR ? S::SZ_AT / 1024 : 0;            // A~ fragments
     constexpr int NDMA = NDK + NDT + NDV + 1 + NDA;
     static_assert(NGV <= 64 && S::SZ_GATE >= NGV * 16, "gate table: one partial wave load");
     const int kw = args.kw;                     // key width; pieces past it are zero
@@ -598,7 +604,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
     }
     using std::integral_constant;
     using none = integral_constant<int, -1>;
-    if constexpr (DPM == 3) {
+    if constexpr (BST) {
         // no output: waves 1 and 2 write the published chunk-start states of
         // the previous iteration to the work space, row-major, key rows
         // [0, KD/2) and [KD/2, KD): lane l takes row 16 i + l/4, value columns

@@ -84,6 +84,7 @@ struct ChunkArgs {
     float mask[4];   // R x R step mask, row-major
     // backward of the single-step bf16 path (64-token chunks):
     void *tmatT;     // prep: T^T without its diagonal (unscaled), rows s, columns t in the permuted k order
+    void *atilT;     // prep (backward, sub-key 0 with atil): A~ as hi/lo fragments in the transposed-score layout
     float *sst;      // state pass: chunk-start state per chunk, (B*H, NT, Dk, Dv) fp32
     float *rst;      // state pass: R = V - e^G K S per chunk, (B*H, NT, Dv/16, 64 lanes, 16) fp32
 };

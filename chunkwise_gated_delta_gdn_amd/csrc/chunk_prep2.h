@@ -23,7 +23,8 @@
 // BWD (the backward of the rule) writes, in place of P, the same scores as
 // the A operand of P^T (lane l: row s = 16 tj + l%16, columns t = 16 ti +
 // 4 (l/16) + e), and also T^T without its diagonal, unscaled, rows s and
-// columns t in the permuted k order (tmatT).
+// columns t in the permuted k order (tmatT); with atil and atilT also A~ in
+// that transposed layout (for the DeltaProduct backward's error gradient).
 //
 // A wave needs no other wave: K and Q come straight from global memory as
 // MFMA fragments (the gram matrix K K^T and the scores K Q^T take both
@@ -56,7 +57,7 @@ struct Prep2Shape {
 __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
 
 template <int KD, int C, bool BWD = false>
-__global__ __launch_bounds__(256) void chunk_prep2_kernel(ChunkArgs args) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void chunk_prep2_kernel(ChunkArgs args) {
     using S = Prep2Shape<KD, C>;
     constexpr int NTT = S::NTT, NLOW = S::NLOW, NKS = S::NKS, LDA = S::LDA;
 
@@ -206,6 +207,33 @@ __global__ __launch_bounds__(256) void chunk_prep2_kernel(ChunkArgs args) {
                 }
             }
         }
+        if constexpr (BWD) {
+            // A~ again as the A operand of its transpose (tile (tt, ss), lane (g, j):
+            // rows t = 16 tt + 4g + e, column s = 16 ss + j), after the scores so that
+            // the Q fragments are no longer held
+            if (adst && args.atilT) {
+                uint4 *tdst = reinterpret_cast<uint4 *>(args.atilT) + (size_t)ci * NLOW * 64 + l;
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt) {
+                    const floatx4 g2r = *reinterpret_cast<const floatx4 *>(G2 + tt * 16 + 4 * g);
+#pragma unroll
+                    for (int ss = 0; ss <= tt; ++ss) {
+                        floatx4 tr = zero4();
+#pragma unroll
+                        for (int m = 0; m < NKS; ++m) tr = mfma32(kf[tt][m], kf[ss][m], tr);
+                        const float g2c = G2[ss * 16 + c16];
+                        float tv[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            tv[e] = ss * 16 + c16 < tt * 16 + 4 * g + e ? tr[e] * fast_exp2(fminf(g2r[e] - g2c, 0.f)) : 0.f;
+                        uint4 ft;
+                        split2_bf16(tv[0], tv[1], ft.x, ft.z);
+                        split2_bf16(tv[2], tv[3], ft.y, ft.w);
+                        tdst[(tt * (tt + 1) / 2 + ss) * 64] = ft;
+                    }
+                }
+            }
+        }
         lds_fence();
 
         // ---- T = (I + A)^-1: diagonal blocks by forward substitution (lane
@@ -320,7 +348,7 @@ __global__ __launch_bounds__(256) void chunk_prep2_kernel(ChunkArgs args) {
             // T^T without its diagonal, unscaled: row s holds T[t][s] for t > s (T's
             // strictly lower part, read down the columns of the LDS copy), columns in
             // the permuted order
-            u16 *out = reinterpret_cast<u16 *>(args.tmatT) + (size_t)ci * C * C;
+            u16 *out = reinterpret_cast<u16 *>(static_cast<char *>(args.tmatT) + sub * args.subws) + (size_t)ci * C * C;
 #pragma unroll
             for (int k = 0; k < C * C / 8 / 64; ++k) {
                 const int idx = k * 64 + l;

@@ -30,6 +30,7 @@ EXPORTS = (
     "gdn_bwd", "gdn_bwd_workspace_bytes",
     "gdn_recurrent_bwd", "gdn_recurrent_bwd_workspace_bytes",
     "gdn_prep_bwd", "gdn_prep_bwd_workspace_bytes",
+    "deltaproduct_bwd", "deltaproduct_bwd_workspace_bytes",
 )
 
 
@@ -83,6 +84,10 @@ def _load():
     lib.gdn_prep_bwd.restype = I
     lib.gdn_prep_bwd_workspace_bytes.argtypes = [I] * 4
     lib.gdn_prep_bwd_workspace_bytes.restype = Z
+    lib.deltaproduct_bwd.argtypes = [P, P, P, P, P, P, I, F, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, Z, P]
+    lib.deltaproduct_bwd.restype = I
+    lib.deltaproduct_bwd_workspace_bytes.argtypes = [I] * 7
+    lib.deltaproduct_bwd_workspace_bytes.restype = Z
     return lib
 
 
@@ -354,6 +359,49 @@ def gdn_bwd(q, k, v, beta, log_decay, dout, scale=1.0, h0=None, dhT=None, need_d
                       _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dg),
                       _ptr(dh0), B, T, H, Dk, Dv, _dtype_code(q.dtype), _ptr(ws), nws, _stream(dev))
     _check("gdn_bwd", rc)
+    return dq, dk, dv, dbeta, dg, dh0
+
+
+def deltaproduct_bwd(q, k, v, beta, log_decay, step_mask, dout, scale=1.0, h0=None, dhT=None, need_dh0=True):
+    """Gradients of :func:`deltaproduct_chunk_fwd`'s (o, hT) for r = 2 with a
+    lower unitriangular step mask [[1, 0], [m, 1]] (bf16).  q,k (B,T,H,2*dk);
+    v and dout (B,T,H,Dv); beta (B,T,H,2) and log_decay (B,T,H) fp32; h0, dhT
+    (B,H,2*dk,Dv) fp32 or None.  Returns (dq, dk, dv, dbeta, dlog_decay, dh0),
+    fp32 (dh0 None unless need_dh0)."""
+    _dev(q, k, v, beta, log_decay, dout, h0, dhT)
+    _f32(beta, "beta"), _f32(log_decay, "log_decay"), _f32(h0, "h0"), _f32(dhT, "dhT")
+    import numpy as np
+    m = np.ascontiguousarray(np.asarray(step_mask, dtype=np.float32))
+    r = m.shape[0]
+    if m.shape != (r, r):
+        raise ValueError("step_mask must be square")
+    B, T, H, K = q.shape
+    Dv = v.shape[-1]
+    if K % r:
+        raise ValueError("key width must be a multiple of r")
+    dk_ = K // r
+    if (k.shape != q.shape or v.shape[:3] != (B, T, H) or dout.shape != v.shape
+            or k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype):
+        raise ValueError("q, k, v, dout shapes or dtypes disagree")
+    if beta.shape != (B, T, H, r) or log_decay.shape != (B, T, H):
+        raise ValueError("beta must be (B,T,H,r) and log_decay (B,T,H)")
+    for name, st in (("h0", h0), ("dhT", dhT)):
+        if st is not None and st.shape != (B, H, K, Dv):
+            raise ValueError(f"{name} must be (B, H, r*dk, Dv)")
+    dev = q.device
+    dq = torch.empty((B, T, H, K), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, T, H, K), dtype=torch.float32, device=dev)
+    dv = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    dbeta = torch.empty((B, T, H, r), dtype=torch.float32, device=dev)
+    dg = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    dh0 = torch.empty((B, H, K, Dv), dtype=torch.float32, device=dev) if need_dh0 else None
+    dt = _dtype_code(q.dtype)
+    ws, nws = _workspace(_lib.deltaproduct_bwd_workspace_bytes(B, T, H, r, dk_, Dv, dt), dev)
+    rc = _lib.deltaproduct_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_decay),
+                               m.ctypes.data_as(ctypes.c_void_p), r, float(scale), _ptr(h0), _ptr(dout),
+                               _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dg), _ptr(dh0),
+                               B, T, H, dk_, Dv, dt, _ptr(ws), nws, _stream(dev))
+    _check("deltaproduct_bwd", rc)
     return dq, dk, dv, dbeta, dg, dh0
 
 

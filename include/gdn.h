@@ -12,6 +12,8 @@
  *                           channels, ReLU, K-scale, UCPE 4x4, RoPE, ||k||^2)
  *   gdn_prep_bwd            gradients of gdn_prep (qkv, norm weights, projections)
  *   gdn_bwd                 gradients of gdn_chunk_fwd (q, k, v, beta, g, h0)
+ *   deltaproduct_bwd        gradients of deltaproduct_chunk_fwd (r = 2, lower
+ *                           unitriangular step mask)
  *   gdn_recurrent_bwd       gradients of gdn_recurrent_fwd (forward direction)
  *
  * Sources (web pages, cited by title and section):
@@ -26,7 +28,7 @@
  * ---------------------------------------
  * - Pointers named as tensors are DEVICE pointers to dense row-major arrays
  *   with the shapes given below (last index fastest).  The only host pointer
- *   is `step_mask` of deltaproduct_chunk_fwd.
+ *   is `step_mask` of deltaproduct_chunk_fwd and deltaproduct_bwd.
  * - `dtype` selects the element type of the q/k/v (and qkv) inputs:
  *   GDN_DTYPE_F32 or GDN_DTYPE_BF16.  Gates (beta, log_decay), states
  *   (h0, hT) and the prep's projection and RoPE tables are always float32.
@@ -396,6 +398,53 @@ int gdn_bwd(const void *q, const void *k, const void *v,
             float *dq, float *dk, float *dv, float *dbeta, float *dlog_decay,
             float *dh0, int B, int T, int H, int Dk, int Dv, int dtype,
             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * deltaproduct_bwd - gradients of deltaproduct_chunk_fwd's outputs (o, hT)
+ * for r = 2 with a lower unitriangular step mask M = [[1, 0], [m, 1]] ([dp]:
+ * the forward's chunk kernels with two steps per token; the backward is
+ * that forward's reverse mode).
+ *
+ * With that mask the state's row block 0 is a gated delta rule on
+ * (q_0, k_0, v, beta_0) and row block 1 one on (q_1, k_1, v', beta_1), with
+ * v'_t = (1 - m) v_t + m e_t and e_t = v_t minus block 0's prediction at
+ * token t (its per-token error, the same for every chunk size), both under
+ * the one gate g.  The gradients come from two chunkwise backward passes
+ * (64-token chunks, MFMA) as in gdn_bwd: block 1's, whose v gradient is
+ * that of v' (dv'), then block 0's with the error gradient dE = m dv'
+ * (through e = R - A~ Vn: dVn gains -A~^T dE, the state recurrence
+ * -K^T diag(e^G) dE, the gram gradient -(beta dX + dE) Vn^T), giving
+ *   dv = beta_0 dX_0 + dv',  dg = dg_0 + dg_1,
+ * dq, dk, dbeta and dh0 per sub-key block.
+ *
+ *   q, k            (B, T, H, 2*dk) dtype (sub-key a in columns a*dk ..)
+ *   v, dout         (B, T, H, Dv)   dtype (dout = dL/do)
+ *   beta            (B, T, H, 2)    float32
+ *   log_decay       (B, T, H)       float32
+ *   step_mask       (2, 2)          float32 HOST array, row-major
+ *   h0, dhT         (B, H, 2*dk, Dv) float32, nullable (zero)
+ *   dq, dk          (B, T, H, 2*dk) float32
+ *   dv              (B, T, H, Dv)   float32
+ *   dbeta           (B, T, H, 2)    float32
+ *   dlog_decay      (B, T, H)       float32
+ *   dh0             (B, H, 2*dk, Dv) float32, nullable (not stored)
+ * Supported: bf16 inputs, r = 2, M[0][0] = M[1][1] = 1 and M[0][1] = 0,
+ * dk in {32, 64, 128}, Dv a multiple of 32 from 32 to 128, any T >= 0
+ * (T = 0 gives dh0 = dhT).  Other masks, types and widths return
+ * GDN_EUNSUPPORTED.  q, k, v, dout, dq, dk, dv 16-byte aligned; h0, dhT,
+ * dh0 16-byte; the other tensors 4-byte; workspace 256-byte aligned.  The
+ * work space (deltaproduct_bwd_workspace_bytes, 0 for an unsupported
+ * shape) holds gdn_bwd's chunkwise regions for each sub-key, A~ in two
+ * fragment layouts and v' (B*T*H*Dv floats).
+ */
+size_t deltaproduct_bwd_workspace_bytes(int B, int T, int H, int r, int dk, int Dv, int dtype);
+int deltaproduct_bwd(const void *q, const void *k, const void *v,
+                     const float *beta, const float *log_decay,
+                     const float *step_mask, int r, float scale,
+                     const float *h0, const void *dout, const float *dhT,
+                     float *dq, float *dk, float *dv, float *dbeta, float *dlog_decay,
+                     float *dh0, int B, int T, int H, int sub_dk, int Dv, int dtype,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }
