@@ -167,13 +167,17 @@ def measured_peaks(dev, reps=10):
     return out
 
 
+# workloads that time another operation on a named workload's inputs
+BASE = {"camera_reverse": "camera", "camera_den": "camera", "camera_bwd": "camera", "gdn_bwd": "gdn",
+        "deltaproduct_bwd": "deltaproduct"}
+
+
 def _prepare(name, dev):
     """Inputs of a workload on the GPU and a step() closure that runs the
     workload's hot path once through the C ABI."""
     import torch
     from chunkwise_gated_delta_gdn_amd import gdn, inputs
-    base = {"camera_reverse": "camera", "camera_den": "camera", "camera_bwd": "camera",
-            "gdn_bwd": "gdn"}.get(name, name)  # same inputs
+    base = BASE.get(name, name)  # same inputs
     wl = inputs.WORKLOADS[base]
     d = inputs.workload_inputs(base)
     bf = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
@@ -192,6 +196,24 @@ def _prepare(name, dev):
         # per token and head: two forward recomputations (4 Dk Dv each) and the
         # backward step (12 Dk Dv), FLOPs
         flops = B * T * H * 20 * Dk * Dv
+        return d, step, B * T, nbytes, flops
+    if name == "deltaproduct_bwd":
+        # gradients of the DeltaProduct workload's forward under seeded dout
+        B, T, H, r, dk, Dv = wl["B"], wl["T"], wl["H"], wl["r"], wl["dk"], wl["Dv"]
+        K = r * dk
+        up = inputs.gdn_upstream(B, T, H, K, Dv, 20266, "bf16")
+        q, k, v, dout = bf(d["q"]), bf(d["k"]), bf(d["v"]), bf(up["dout"])
+        beta, g = f32(d["beta"]), f32(d["g"])
+
+        def step():
+            return gdn.deltaproduct_bwd(q, k, v, beta, g, d["mask"], dout, K ** -0.5)
+        # read q, k (K), v, dout (Dv), bf16, beta (r), g; write dq, dk, dv (fp32),
+        # dbeta (r), dg, dh0
+        nbytes = (B * T * H * ((2 * K + 2 * Dv) * 2 + (r + 1) * 4 + (2 * K + Dv) * 4 + (r + 1) * 4)
+                  + B * H * K * Dv * 4)
+        # per token and head, per sub-key: two forward recomputations (4 dk Dv
+        # each) and the backward step (12 dk Dv)
+        flops = B * T * H * 20 * K * Dv
         return d, step, B * T, nbytes, flops
     if wl["kind"] == "gdn":
         q, k, v = bf(d["q"]), bf(d["k"]), bf(d["v"])
@@ -295,7 +317,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="gdn", choices=("gdn", "gdn_long", "deltaproduct", "camera", "camera_reverse", "camera_den",
-                             "gdn_bwd", "camera_bwd"),
+                             "gdn_bwd", "camera_bwd", "deltaproduct_bwd"),
                     help="gdn is the headline workload; the others time the other operations")
     ap.add_argument("--copy-probe", action="store_true", help="run only the copy calibration kernel")
     args = ap.parse_args()
@@ -332,8 +354,7 @@ def main():
     kernel_ms = float(np.mean(kern_ms))
     achieved_gbs = nbytes / (kernel_ms * 1e-3) / 1e9
     from chunkwise_gated_delta_gdn_amd import inputs
-    wl = inputs.WORKLOADS[{"camera_reverse": "camera", "camera_den": "camera", "camera_bwd": "camera",
-                           "gdn_bwd": "gdn"}.get(args.workload, args.workload)]
+    wl = inputs.WORKLOADS[BASE.get(args.workload, args.workload)]
     if args.workload == "gdn_bwd":
         metric = "tokens/sec of gated-delta backward (B*T/s) at H=16, D=128"
         desc = (f"gdn_bwd: gradients of the gdn workload (B={wl['B']} H={wl['H']} T={wl['T']} "
@@ -341,6 +362,14 @@ def main():
         kernel = ("gdn_bwd = chunk_prep2_kernel<128, 64, bwd> + chunk_chain1_kernel<128, 64, 3> (forward states) "
                   "+ chunk_bchain_kernel<128> (reverse state pass) + chunk_bgrad_kernel<128> (per-chunk gradients)")
         traffic = measured_traffic(args.workload)
+    elif args.workload == "deltaproduct_bwd":
+        metric = "tokens/sec of gated DeltaProduct backward (B*T/s)"
+        desc = ("deltaproduct_bwd: gradients of the deltaproduct workload (B=2 H=8 T=2048 K=2x128 Dv=128 r=2, "
+                "lower-triangular step mask), bf16 q/k/v/dout, fp32 gradients, no dhT")
+        kernel = ("deltaproduct_bwd = chunk_prep2_kernel<128, 64, bwd> (both sub-keys) + chunk_chain1_kernel<128, 64, 5> "
+                  "and <128, 64, 4> (forward states, v') + chunk_bchain_kernel<128> and chunk_bgrad_kernel<128> "
+                  "(sub-key 1), then their error-gradient forms <128, true> (sub-key 0)")
+        traffic = None
     elif args.workload == "camera_bwd":
         metric = "tokens/sec of camera scan + prep backward (B*N/s)"
         desc = ("camera_bwd: gradients of the camera workload (B=1 F=8 S=30x52 H=16 D=64): the scan's on the "

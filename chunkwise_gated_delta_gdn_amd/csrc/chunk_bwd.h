@@ -78,7 +78,7 @@ struct BwdChunkArgs {
 // Step s = 0 .. NT: the chain processes chunk NT - s (s >= 1), the helpers
 // chunk NT - 1 - s; one workgroup barrier per step.
 // ---------------------------------------------------------------------------
-template <int KD>
+template <int KD, bool DPE = false>
 struct BChainShape {
     static constexpr int C = 64, BV = 16, NTT = 4, NCS = 2;
     static constexpr int NKS = KD / 32, NST = KD / 16, NKC = KD / 8;
@@ -90,6 +90,7 @@ struct BChainShape {
     static constexpr int SZ_KS = al(C * LDK * 2);
     static constexpr int SZ_TT = al(C * LDT * 2);
     static constexpr int SZ_GA = al(NGATE * 4);
+    static constexpr int SZ_GB = al(C * 4);           // ring B holds e^G only
     static constexpr int SZ_DO = al(C * LDV * 2);
     static constexpr int SZ_EP = 64 * NST * 16;
     static constexpr int SZ_DP = 64 * NTT * 16;
@@ -98,10 +99,14 @@ struct BChainShape {
     static constexpr int OFF_GA = OFF_TT + 3 * SZ_TT;
     static constexpr int OFF_QS = OFF_GA + 3 * SZ_GA;
     static constexpr int OFF_DO = OFF_QS + 3 * SZ_KS;
-    static constexpr int OFF_GB = OFF_DO + 3 * SZ_DO;
-    static constexpr int OFF_EP = OFF_GB + 3 * SZ_GA;
+    // DPE: the dO slice goes to registers straight from global memory (no
+    // ring), which leaves room for dE (three buffers, index chunk % 3)
+    static constexpr int NDOB = DPE ? 0 : 3;
+    static constexpr int OFF_GB = OFF_DO + NDOB * SZ_DO;
+    static constexpr int OFF_EP = OFF_GB + 3 * SZ_GB;
     static constexpr int OFF_DP = OFF_EP + 2 * SZ_EP;
-    static constexpr int BYTES = OFF_DP + 2 * SZ_DP;
+    static constexpr int OFF_DE = OFF_DP + 2 * SZ_DP;
+    static constexpr int BYTES = OFF_DE + (DPE ? 3 * SZ_DP : 0);
     static_assert(KD % 32 == 0 && KD <= 128, "key width");
     static_assert(BYTES <= 160 * 1024, "LDS budget of one workgroup exceeded");
     static_assert(SZ_KS % 1024 == 0 && SZ_TT % 1024 == 0 && SZ_DO % 1024 == 0, "whole 1 KiB wave loads");
@@ -130,7 +135,7 @@ __device__ __forceinline__ void kt_frags(const u16 *ks, bf16x8 (&ka)[KD / 16][2]
 
 template <int KD, bool DPE = false>
 __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(BwdChunkArgs ba) {
-    using S = BChainShape<KD>;
+    using S = BChainShape<KD, DPE>;
     constexpr int C = S::C, BV = S::BV, NTT = S::NTT, NKS = S::NKS, NST = S::NST, NCS = S::NCS, NKC = S::NKC;
     constexpr int LDK = S::LDK, LDT = S::LDT, LDV = S::LDV, TSW = S::TSW, NGATE = S::NGATE;
     constexpr int NLOW = NTT * (NTT + 1) / 2;
@@ -160,9 +165,10 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
     auto gA = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_GA + p * S::SZ_GA); };
     auto Qs = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_QS + p * S::SZ_KS); };
     auto dOs = [&](int p) { return reinterpret_cast<u16 *>(smem + S::OFF_DO + p * S::SZ_DO); };
-    auto gB = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_GB + p * S::SZ_GA); };
+    auto gB = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_GB + p * S::SZ_GB); };
     auto Ep = [&](int p) { return reinterpret_cast<floatx4 *>(smem + S::OFF_EP + p * S::SZ_EP); };
     auto Dp = [&](int p) { return reinterpret_cast<floatx4 *>(smem + S::OFF_DP + p * S::SZ_DP); };
+    auto De = [&](int p) { return reinterpret_cast<floatx4 *>(smem + S::OFF_DE + p * S::SZ_DP); };
     auto ring = [](int c) { return ((c % 3) + 3) % 3; };
 
     if (w == 0) {
@@ -246,20 +252,12 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
 #pragma unroll
                 for (int st = 0; st < NTT; ++st)
                     if (2 * m + 1 >= st) dx[st] = mfma32(tf[st][m], dvh[m], dx[st]);
-            // DPE: dE = m dv' of this chunk (rows tt*16 + 4g + e, column v0 + c16,
-            // zero past T), used for Z
+            // DPE: dE = m dv' of this chunk (accumulator layout, zero past T),
+            // published by wave 1 two steps earlier
             floatx4 dE[NTT];
             if constexpr (DPE) {
-                const float *dp = ba.dvprev + ((size_t)b * T * H + h) * Dv + v0 + c16;
-                const float mc = args.mcoef;
 #pragma unroll
-                for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = c * C + tt * 16 + 4 * g + e;
-                        const float x = dp[(size_t)min(t, tlast) * H * Dv];
-                        dE[tt][e] = t <= tlast ? mc * x : 0.f;
-                    }
+                for (int tt = 0; tt < NTT; ++tt) dE[tt] = De(sq)[tt * 64 + l];
             }
             // Z = -gamma beta dX (DPE: -gamma (beta dX + dE)), hi + lo;
             // dS = Lambda dS' + E + K^T Z
@@ -349,37 +347,65 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
                 *reinterpret_cast<floatx4 *>(sp + (size_t)f * Dv) = x;
             }
         };
+        // wave 2: fragments of a chunk's transposed scores (and with DPE of
+        // A~^T, the same layout), loaded one step ahead
         u32x4 pf[NLOW], af[NLOW];
         auto load_pf = [&](int c) {
             c = c < 0 ? 0 : c;                  // (past the first chunk: loaded again, unused)
             const uint4 *pc = reinterpret_cast<const uint4 *>(args.pfrag) + ((size_t)bh * NT + c) * NLOW * 64 + l;
 #pragma unroll
             for (int i = 0; i < NLOW; ++i) pf[i] = __builtin_bit_cast(u32x4, pc[i * 64]);
-            if constexpr (DPE) {                // A~^T fragments, the same layout
+            if constexpr (DPE) {
                 const uint4 *ac = reinterpret_cast<const uint4 *>(args.atilT) + ((size_t)bh * NT + c) * NLOW * 64 + l;
 #pragma unroll
                 for (int i = 0; i < NLOW; ++i) af[i] = __builtin_bit_cast(u32x4, ac[i * 64]);
             }
         };
-        // DPE: dE = m dv' of a chunk, this lane's rows tt*16 + 4g + e, column
-        // v0 + c16 (zero past T), loaded one step ahead
+        // DPE, wave 1: dv' of a chunk, this lane's rows tt*16 + 4g + e
+        // (clamped to T - 1), column v0 + c16, loaded one step before it is
+        // published as dE = m dv' (rows past T zero) in De(chunk % 3), a step
+        // before wave 2 and two before the chain use it (the loads are kept
+        // as they are until then, so that nothing waits for them earlier)
         floatx4 dep[NTT];
         auto load_de = [&](int c) {
             c = c < 0 ? 0 : c;
             const float *dp = ba.dvprev + ((size_t)b * T * H + h) * Dv + v0 + c16;
-            const float mc = args.mcoef;
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = c * C + tt * 16 + 4 * g + e;
-                    const float x = dp[(size_t)min(t, tlast) * H * Dv];
-                    dep[tt][e] = t <= tlast ? mc * x : 0.f;
-                }
+                for (int e = 0; e < 4; ++e) dep[tt][e] = dp[(size_t)min(c * C + tt * 16 + 4 * g + e, tlast) * H * Dv];
         };
-        if (w == 2) {
-            load_pf(NT - 1);
-            if constexpr (DPE) load_de(NT - 1);
+        // DPE: the dO slice of a chunk (rows tt*16 + 4g + e clamped to T - 1,
+        // column v0 + c16), loaded one step ahead as it is (rows past T zeroed
+        // where it is used), each value into a register of its own (loads into
+        // halves of one register would wait for each other)
+        unsigned int opre[NTT][4];
+        auto load_do = [&](int c) {
+            c = c < 0 ? 0 : c;
+            const u16 *op = reinterpret_cast<const u16 *>(ba.dout) + ((size_t)b * T * H + h) * Dv + v0 + c16;
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) opre[tt][e] = op[(size_t)min(c * C + tt * 16 + 4 * g + e, tlast) * H * Dv];
+        };
+        auto publish_de = [&](int c) {
+            const float mc = args.mcoef;
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) {
+                floatx4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = c * C + tt * 16 + 4 * g + e <= tlast ? mc * dep[tt][e] : 0.f;
+                De(ring(c))[tt * 64 + l] = x;
+            }
+        };
+        if (w == 2) load_pf(NT - 1);
+        if constexpr (DPE) {
+            if (w == 1) {
+                load_de(NT - 1);
+                publish_de(NT - 1);             // (waits for those loads: once)
+                load_de(NT - 2);
+            }
+            load_do(NT - 1);
         }
         __syncthreads();
         for (int s = 0; s <= NT; ++s) {
@@ -387,12 +413,23 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
             if (s >= 2) store_ds(c + 2);
             if (c >= 0) {
                 const int sq = ring(c), p = c & 1;
-                const u16 *dos = dOs(sq);
                 const float *gp = gB(sq);
                 shortx4 vv[NTT];
+                if constexpr (DPE) {
 #pragma unroll
-                for (int tt = 0; tt < NTT; ++tt)
-                    vv[tt] = ld_tr16(dos + (tt * 16 + 4 * g + (c16 >> 2)) * LDV + 4 * (c16 & 3));
+                    for (int tt = 0; tt < NTT; ++tt) {
+                        unsigned int x[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = c * C + tt * 16 + 4 * g + e <= tlast ? opre[tt][e] : 0u;
+                        vv[tt] = __builtin_bit_cast(shortx4, uint2{x[0] | (x[1] << 16), x[2] | (x[3] << 16)});
+                    }
+                    load_do(c - 1);
+                } else {
+                    const u16 *dos = dOs(sq);
+#pragma unroll
+                    for (int tt = 0; tt < NTT; ++tt)
+                        vv[tt] = ld_tr16(dos + (tt * 16 + 4 * g + (c16 >> 2)) * LDV + 4 * (c16 & 3));
+                }
                 // E tiles of this wave: Q^T fragments (the chain's row order) times
                 // gamma dO (hi + lo)
                 floatx4 gd[NTT];
@@ -408,14 +445,6 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
                 bf16x8 gh[NCS], gl[NCS];
 #pragma unroll
                 for (int m = 0; m < NCS; ++m) frag_split(gd[2 * m], gd[2 * m + 1], gh[m], gl[m]);
-                floatx4 dcur[NTT];              // DPE: dE of this chunk
-                if constexpr (DPE) {
-                    if (w == 2) {
-#pragma unroll
-                        for (int tt = 0; tt < NTT; ++tt) dcur[tt] = dep[tt];
-                        load_de(c - 1);
-                    }
-                }
                 const u16 *qs = Qs(sq);
 #pragma unroll 1
                 for (int i = 0; i < NST / 2; ++i) {
@@ -433,11 +462,11 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
                     }
                     Ep(p)[ti * 64 + l] = ev;
                 }
-                if (w == 2) {                   // dV0 = scale Pm^T dO (DPE: - A~^T dE)
+                if (w == 2) {                   // dV0 = scale Pm^T dO (DPE: - A~^T dE, hi + lo)
                     shortx4 dh4[NTT], dl4[NTT];
                     if constexpr (DPE) {
 #pragma unroll
-                        for (int tt = 0; tt < NTT; ++tt) split4(dcur[tt], dh4[tt], dl4[tt]);
+                        for (int tt = 0; tt < NTT; ++tt) split4(De(sq)[tt * 64 + l], dh4[tt], dl4[tt]);
                     }
 #pragma unroll
                     for (int st = 0; st < NTT; ++st) {
@@ -464,6 +493,12 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
                     }
                     load_pf(c - 1);
                 }
+                if constexpr (DPE) {
+                    if (w == 1 && c >= 1) {     // dE of the next chunk
+                        publish_de(c - 1);
+                        load_de(c - 2);
+                    }
+                }
             }
             lds_barrier();
         }
@@ -475,7 +510,7 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
     // ====================================================================
     // staging waves (3 and 5)
     // ====================================================================
-    constexpr int NDK = S::SZ_KS / 1024, NDT = S::SZ_TT / 1024, NDO = S::SZ_DO / 1024;
+    constexpr int NDK = S::SZ_KS / 1024, NDT = S::SZ_TT / 1024, NDO = DPE ? 0 : S::SZ_DO / 1024;
     constexpr int NGV = NGATE / 4;
     constexpr int NA = NDK + NDT + 1, NB = NDK + NDO + 1, NDMA = NA + NB;
     static_assert(NGV <= 64 && S::SZ_GA >= NGV * 16, "gate table: one partial wave load");
@@ -521,7 +556,7 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
                                      : static_cast<const void *>(&kZero16),
                           dOs(pb) + kk * 512);
                 } else {
-                    if (l < NGV) dma16(gtg + (size_t)cb * NGATE + l * 4, gB(pb));
+                    if (l < C / 4) dma16(gtg + (size_t)cb * NGATE + l * 4, gB(pb));   // e^G
                 }
             }
         };
