@@ -45,7 +45,10 @@
 //   DPM = 1: the pass on sub-key 0; also forms the per-token errors
 //            e = R - A~ V_new (A~ the decay-masked gram without beta, from the
 //            prep; V_new = beta e) and writes v' = (1 - m) v + m e (fp32);
-//            its output goes to an fp32 buffer;
+//            its output goes to an fp32 buffer.  The chain wave publishes
+//            W = (1 - m) v + m R next to V_new, and the output waves form
+//            v' = W - m A~ V_new for their token tiles a step later, with
+//            the A~ fragments loaded from global memory like P's;
 //   DPM = 2: the pass on sub-key 1 with v' (fp32, read by the chain wave) as
 //            the values; its output adds the first pass's.
 //
@@ -110,10 +113,9 @@ struct Chain1Shape {
     static constexpr int OFF_GATE = OFF_BV + 3 * SZ_BV;
     static constexpr int OFF_ST = OFF_GATE + 3 * SZ_GATE;
     static constexpr int OFF_VN = OFF_ST + 2 * SZ_ST;
-    static constexpr int SZ_AT = NLOW * 1024;                     // A~ fragments (DeltaProduct first pass)
-    static constexpr int OFF_AT = OFF_VN + 2 * SZ_VN;
-    static constexpr int BYTES = OFF_AT + 3 * SZ_AT;
-    static constexpr int BYTES_PLAIN = OFF_AT;
+    static constexpr int OFF_WT = OFF_VN + 2 * SZ_VN;             // W = (1 - m) v + m R (DeltaProduct first pass)
+    static constexpr int BYTES = OFF_WT + 2 * SZ_VN;
+    static constexpr int BYTES_PLAIN = OFF_WT;
     static_assert(C % 32 == 0 && C <= 64 && KD % 32 == 0, "32-wide MFMA steps");
     static_assert(BYTES <= 160 * 1024 || KD > 128, "LDS budget of one workgroup exceeded");
     static_assert(BYTES_PLAIN <= 160 * 1024, "LDS budget of one workgroup exceeded");
@@ -178,7 +180,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
     auto gate = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_GATE + p * S::SZ_GATE); };
     auto St = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_ST + p * S::SZ_ST); };
     auto Vn = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_VN + p * S::SZ_VN); };
-    auto At = [&](int p) { return reinterpret_cast<const uint4 *>(smem + S::OFF_AT + p * S::SZ_AT); };
+    auto Wt = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_WT + p * S::SZ_VN); };
 
     if (w == 0) {
         // =================================================================
@@ -327,7 +329,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
             floatx4 vt4[NTT];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
-                if constexpr (!BST) *reinterpret_cast<floatx4 *>(vnp + c16 * LDVF + tt * 16 + 4 * g) = vn[tt];
+                if constexpr (!BST || ERR) *reinterpret_cast<floatx4 *>(vnp + c16 * LDVF + tt * 16 + 4 * g) = vn[tt];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vt4[tt][e] = el[tt][e] * vn[tt][e];
             }
@@ -349,34 +351,16 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
             // writes then do not queue ahead of this chunk's operand reads)
             publish_state(p);
             if constexpr (ERR) {
-                // (issued after the state update's MFMAs: off the chain's path)
-                // per-token errors e = R - A~ V_new and v' = (1 - m) v + m e;
-                // A~ tile (tt, tj) is the A operand (rows t), V_new tile tj the B
-                // operand (its accumulator layout), both as hi + lo
-                shortx4 nh[NTT], nl[NTT];
-#pragma unroll
-                for (int tt = 0; tt < NTT; ++tt) split4(vn[tt], nh[tt], nl[tt]);
-                const uint4 *at = At(sq);
+                // W = (1 - m) v + m R, published like V_new ([j][s]); the waves
+                // that read V_new a step later form v' = W - m A~ V_new
                 const float mc = args.mcoef;
-                float *vo = args.vout + (((size_t)b * T) * H + h) * Dv + v0 + c16;
+                float *wp = Wt(p) + c16 * LDVF + 4 * g;
 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt) {
-                    floatx4 acc = zero4();
+                    floatx4 w4;
 #pragma unroll
-                    for (int tj = 0; tj <= tt; ++tj) {
-                        const u32x4 af = __builtin_bit_cast(u32x4, at[(tt * (tt + 1) / 2 + tj) * 64 + l]);
-                        const shortx4 ah = __builtin_bit_cast(shortx4, uint2{af[0], af[1]});
-                        const shortx4 al = __builtin_bit_cast(shortx4, uint2{af[2], af[3]});
-                        acc = mfma16(ah, nh[tj], acc);
-                        acc = mfma16(ah, nl[tj], acc);
-                        acc = mfma16(al, nh[tj], acc);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = c * C + tt * 16 + 4 * g + e;
-                        const float ee = rr[tt][e] - acc[e];
-                        if (t < T) vo[(size_t)t * H * Dv] = (1.f - mc) * vin4[tt][e] + mc * ee;
-                    }
+                    for (int e = 0; e < 4; ++e) w4[e] = (1.f - mc) * vin4[tt][e] + mc * rr[tt][e];
+                    *reinterpret_cast<floatx4 *>(wp + tt * 16) = w4;
                 }
             }
 #pragma unroll
@@ -384,7 +368,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Sreg[ti][e] = gL * Sreg[ti][e] + ds[ti][e];
             // LDS operations only: the chain wave's own global loads (v' of the
-            // next chunk) and stores (v') stay in flight across the barrier
+            // next chunk) stay in flight across the barrier
             lds_barrier();
         }
         __syncthreads();                       // matches the out waves' drain step
@@ -416,8 +400,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
     constexpr int NLOW = NTT * (NTT + 1) / 2;
     constexpr int NGV = S::NGATE / 4;           // 16-byte vectors of a gate table
     constexpr int NDK = S::SZ_KS / 1024, NDT = S::SZ_TB / 1024, NDV = VIN ? 0 : S::SZ_BV / 1024;
-    constexpr int NDA = ERR ? S::SZ_AT / 1024 : 0;            // A~ fragments
-    constexpr int NDMA = NDK + NDT + NDV + 1 + NDA;
+    constexpr int NDMA = NDK + NDT + NDV + 1;
     static_assert(NGV <= 64 && S::SZ_GATE >= NGV * 16, "gate table: one partial wave load");
     const int kw = args.kw;                     // key width; pieces past it are zero
     const size_t tokq = (size_t)H * args.kst, tokv = (size_t)H * Dv;
@@ -452,12 +435,8 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
                     const int kk = k - NDK - NDT, pos = kk * 64 + l;
                     const int t = min(c * C + pos / 2, tlast);
                     dma16(vg + (size_t)t * tokv + (pos & 1) * 8, BVs(p) + kk * 512);
-                } else if (k == NDK + NDT + NDV) {  // gate table
+                } else {                            // gate table
                     if (l < NGV) dma16(gtg + (size_t)c * S::NGATE + l * 4, gate(p));
-                } else {                            // A~ fragments (DeltaProduct first pass)
-                    const int kk = k - NDK - NDT - NDV - 1;
-                    dma16(reinterpret_cast<const uint4 *>(args.atil) + ((size_t)bh * NT + c) * NLOW * 64 + kk * 64 + l,
-                          smem + S::OFF_AT + p * S::SZ_AT + kk * 1024);
                 }
             }
         };
@@ -471,6 +450,8 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
         float egt[NTW];                         // e^{G_t} of this lane's tokens
         floatx4 ov[NTW];                        // outputs of the previous chunk
         floatx4 op[NTW];                        // DPM 2: the first pass's output of those tokens
+        u32x4 af[NTW][NTT];                     // ERR: A~ fragments of each tile (P's layout)
+        floatx4 vq[NTW];                        // ERR: v' of the previous chunk (4 columns of one token)
         // operands of chunk c's output, used one iteration later
         auto load_qp = [&](int c) {
 #pragma unroll
@@ -493,6 +474,12 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
 #pragma unroll
                 for (int tj = 0; tj <= tw(i); ++tj) pf[i][tj] = __builtin_bit_cast(u32x4, pc[tj * 64]);
                 egt[i] = gate(c % 3)[tw(i) * 16 + c16];
+                if constexpr (ERR) {
+                    const uint4 *ac = reinterpret_cast<const uint4 *>(args.atil) + ((size_t)bh * NT + c) * NLOW * 64 +
+                                      (tw(i) * (tw(i) + 1) / 2) * 64 + l;
+#pragma unroll
+                    for (int tj = 0; tj <= tw(i); ++tj) af[i][tj] = __builtin_bit_cast(u32x4, ac[tj * 64]);
+                }
                 if constexpr (DPM == 2)
                     op[i] = *reinterpret_cast<const floatx4 *>(args.oprev + (((size_t)b * T + t) * H + h) * Dv + v0 + 4 * g);
             }
@@ -530,6 +517,22 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ov[i][e] = sc * (egt[i] * a1[e] + a2[e]) + (DPM == 2 ? op[i][e] : 0.f);
+                if constexpr (ERR) {
+                    // v'^T = W^T - m V_new^T A~^T (A~ in P's layout, hi + lo)
+                    floatx4 a3 = zero4();
+#pragma unroll
+                    for (int tj = 0; tj <= tw(i); ++tj) {
+                        const shortx4 ah = __builtin_bit_cast(shortx4, uint2{af[i][tj][0], af[i][tj][1]});
+                        const shortx4 al = __builtin_bit_cast(shortx4, uint2{af[i][tj][2], af[i][tj][3]});
+                        a3 = mfma16(vh4[tj], ah, a3);
+                        a3 = mfma16(vh4[tj], al, a3);
+                        a3 = mfma16(vl4[tj], ah, a3);
+                    }
+                    const float *wt = Wt(c & 1) + tw(i) * 16 + c16;
+                    const float mc = args.mcoef;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vq[i][e] = wt[(4 * g + e) * LDVF] - mc * a3[e];
+                }
             }
         };
         auto store_out = [&](int c) {
@@ -543,6 +546,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
                             uint2{cvt2_bf16(ov[i][0], ov[i][1]), cvt2_bf16(ov[i][2], ov[i][3])};
                     else
                         *reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(args.o) + off) = ov[i];
+                    if constexpr (ERR) *reinterpret_cast<floatx4 *>(args.vout + off) = vq[i];
                 }
             }
         };
@@ -559,7 +563,8 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
         // loads, then this staging), so that staging is always complete.  An
         // output-only wave stages nothing and waits for none of its own.
         constexpr int NMINE = LOAD ? (NDMA - LI + NLW - 1) / NLW : 0;
-        constexpr int NQP = TILE ? NTW * NKS + (TW0 + 1) + (NTW > 1 ? TW1 + 1 : 0) : 0;
+        constexpr int NPF = (TW0 + 1) + (NTW > 1 ? TW1 + 1 : 0);   // P (and A~) fragment loads
+        constexpr int NQP = TILE ? NTW * NKS + NPF * (ERR ? 2 : 1) : 0;
         constexpr int NOWN = LOAD ? NMINE + NQP : 63;
         static_assert(NOWN < 64, "6-bit vmcnt");
         // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, lgkmcnt(0), expcnt at its maximum
@@ -623,14 +628,75 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
                         *reinterpret_cast<floatx4 *>(args.sst + (((size_t)bh * NT + c) * kw + f) * args.Dv + v0 + v4) = x;
                 }
             };
-            __syncthreads();
-            lds_barrier();
-            for (int c = 1; c < NT; ++c) {
-                store_state(c - 1);
+            // DPM 5: v' of the previous chunk for token tiles {3, 0} (wave 1)
+            // or {2, 1} (wave 2), as the output waves of DPM 1 form it
+            auto err_wave = [&](auto owa, auto owb) {
+                constexpr int TA = decltype(owa)::value, TB = decltype(owb)::value;
+                constexpr int TM = TA > TB ? TA : TB;
+                auto twi = [](int i) { return i == 0 ? TA : TB; };
+                u32x4 af[2][NTT];
+                auto load_af = [&](int c) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const uint4 *ac = reinterpret_cast<const uint4 *>(args.atil) + ((size_t)bh * NT + c) * NLOW * 64 +
+                                          (twi(i) * (twi(i) + 1) / 2) * 64 + l;
+#pragma unroll
+                        for (int tj = 0; tj <= twi(i); ++tj) af[i][tj] = __builtin_bit_cast(u32x4, ac[tj * 64]);
+                    }
+                };
+                auto err = [&](int c) {
+                    const float *vnp = Vn(c & 1);
+                    shortx4 vh4[TM + 1], vl4[TM + 1];
+#pragma unroll
+                    for (int tj = 0; tj <= TM; ++tj)
+                        split4(*reinterpret_cast<const floatx4 *>(vnp + c16 * LDVF + tj * 16 + 4 * g), vh4[tj], vl4[tj]);
+                    const float mc = args.mcoef;
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        floatx4 a3 = zero4();
+#pragma unroll
+                        for (int tj = 0; tj <= twi(i); ++tj) {
+                            const shortx4 ah = __builtin_bit_cast(shortx4, uint2{af[i][tj][0], af[i][tj][1]});
+                            const shortx4 al = __builtin_bit_cast(shortx4, uint2{af[i][tj][2], af[i][tj][3]});
+                            a3 = mfma16(vh4[tj], ah, a3);
+                            a3 = mfma16(vh4[tj], al, a3);
+                            a3 = mfma16(vl4[tj], ah, a3);
+                        }
+                        const float *wt = Wt(c & 1) + twi(i) * 16 + c16;
+                        floatx4 x;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = wt[(4 * g + e) * LDVF] - mc * a3[e];
+                        const int t = c * C + twi(i) * 16 + c16;
+                        if (t < T)
+                            *reinterpret_cast<floatx4 *>(args.vout + (((size_t)b * T + t) * H + h) * Dv + v0 + 4 * g) = x;
+                    }
+                };
+                load_af(0);
+                __syncthreads();
                 lds_barrier();
+                for (int c = 1; c < NT; ++c) {
+                    store_state(c - 1);
+                    err(c - 1);
+                    load_af(c);
+                    lds_barrier();
+                }
+                store_state(NT - 1);
+                err(NT - 1);
+                __syncthreads();
+            };
+            if constexpr (ERR) {
+                if (w == 1) err_wave(integral_constant<int, 3>{}, integral_constant<int, 0>{});
+                else err_wave(integral_constant<int, 2>{}, integral_constant<int, 1>{});
+            } else {
+                __syncthreads();
+                lds_barrier();
+                for (int c = 1; c < NT; ++c) {
+                    store_state(c - 1);
+                    lds_barrier();
+                }
+                store_state(NT - 1);
+                __syncthreads();
             }
-            store_state(NT - 1);
-            __syncthreads();
         }
         if (w == 3) out_wave(none{}, none{}, integral_constant<int, 0>{});
         if (w == 5) out_wave(none{}, none{}, integral_constant<int, 1>{});
