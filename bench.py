@@ -50,6 +50,9 @@ TRAFFIC = {
     "camera": (os.path.join(ROOT, "profiles", "camera_prep_scan_traffic.json"), CAMERA_SOURCES),
     "camera_den": (os.path.join(ROOT, "profiles", "camera_prep_scan_den_traffic.json"), CAMERA_SOURCES),
     "gdn_bwd": (os.path.join(ROOT, "profiles", "gdn_bwd_traffic.json"), BWD_SOURCES),
+    "deltaproduct": (os.path.join(ROOT, "profiles", "deltaproduct_traffic.json"), KERNEL_SOURCES),
+    "deltaproduct_bwd": (os.path.join(ROOT, "profiles", "deltaproduct_bwd_traffic.json"), BWD_SOURCES),
+    "camera_bwd": (os.path.join(ROOT, "profiles", "camera_bwd_traffic.json"), CAMERA_SOURCES),
 }
 
 
@@ -369,7 +372,7 @@ def main():
         kernel = ("deltaproduct_bwd = chunk_prep2_kernel<128, 64, bwd> (both sub-keys) + chunk_chain1_kernel<128, 64, 5> "
                   "and <128, 64, 4> (forward states, v') + chunk_bchain_kernel<128> and chunk_bgrad_kernel<128> "
                   "(sub-key 1), then their error-gradient forms <128, true> (sub-key 0)")
-        traffic = None
+        traffic = measured_traffic(args.workload)
     elif args.workload == "camera_bwd":
         metric = "tokens/sec of camera scan + prep backward (B*N/s)"
         desc = ("camera_bwd: gradients of the camera workload (B=1 F=8 S=30x52 H=16 D=64): the scan's on the "
@@ -377,7 +380,7 @@ def main():
                 "weights, projections)")
         kernel = ("gdn_recurrent_bwd (frame_gram_bf16_kernel for G, H and A, frame_reduce_kernel, frame_state_kernel, "
                   "frame_bstate_kernel, frame_bgrad_kernel) + gdn_prep_bwd (prep_bwd_kernel, prep_bwd_reduce_kernel)")
-        traffic = None
+        traffic = measured_traffic(args.workload)
     elif args.workload in ("gdn", "gdn_long"):
         metric = "tokens/sec of chunkwise gated-delta fwd (B*T/s) at H=16, D=128"
         desc = (f"{args.workload}: B={wl['B']} H={wl['H']} T={wl['T']} Dk=Dv={wl['Dk']} chunk={wl['chunk']}, "
@@ -389,7 +392,7 @@ def main():
         desc = "deltaproduct: B=2 H=8 T=2048 K=2x128 Dv=128 chunk=32 r=2, bf16 q/k/v and output, lower-triangular step mask"
         kernel = ("deltaproduct_chunk_fwd = chunk_prep2_kernel (both sub-keys) + chunk_chain1_kernel<128, 64, 1> "
                   "+ chunk_chain1_kernel<128, 64, 2> (two passes, lower unitriangular step mask)")
-        traffic = None
+        traffic = measured_traffic(args.workload)
     else:
         rev = args.workload == "camera_reverse"
         metric = "tokens/sec of camera prep + frame-synchronous scan (B*N/s)"
