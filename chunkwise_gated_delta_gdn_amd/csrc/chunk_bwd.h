@@ -598,9 +598,10 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
 //   2  the 10 lower 16x16 tiles of M1 (with Q K^T) and of dA, M2 (with
 //      K K^T), one job per (tile, kind) over the waves; M1 and M2 go to
 //      LDS as hi/lo bf16, row and column sums of W to per-tile slots;
-//   3  wave w < Dk/16 owns key features 16w..16w+15: dQ and dK, and their
-//      row products with q and k for the gate gradient; S and dS' come
-//      straight from the work space as B operands (k = value column);
+//   3  wave w < Dk/16 owns key features 16w..16w+15: dQ and dK (products
+//      taken transposed, so each lane stores 4 features of one token), and
+//      their row products with q and k for the gate gradient; S and dS'
+//      come straight from the work space as A operands (k = value column);
 //   4  wave 0: dbeta and dg of the chunk (fixed-order sums, reverse
 //      cumsum).
 // ---------------------------------------------------------------------------
@@ -656,15 +657,6 @@ __device__ __forceinline__ bf16x8 tr_frag(const u16 *base, int r0, int c0) {
     const uint2 lo = __builtin_bit_cast(uint2, ld_tr16(base + swz_at<NPC>(ra, col)));
     const uint2 hi = __builtin_bit_cast(uint2, ld_tr16(base + swz_at<NPC>(ra + 4, col)));
     return __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
-}
-// Accumulator-layout values: lane (g, j) gets X[r0 + e][c0 + j] for e < 4
-// (r0 per lane group), as floats.
-template <int NPC>
-__device__ __forceinline__ floatx4 acc_vals(const u16 *base, int r0, int c0) {
-    const int c16 = lane_id() & 15;
-    const uint2 v = __builtin_bit_cast(uint2, ld_tr16(base + swz_at<NPC>(r0 + (c16 >> 2), c0 + 4 * (c16 & 3))));
-    return floatx4{__builtin_bit_cast(float, v.x << 16), __builtin_bit_cast(float, v.x & 0xffff0000u),
-                   __builtin_bit_cast(float, v.y << 16), __builtin_bit_cast(float, v.y & 0xffff0000u)};
 }
 // Sum over the 16 lanes of a lane group (the columns of an accumulator tile).
 __device__ __forceinline__ float sum16(float v) {
@@ -992,74 +984,89 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
             kb[m] = tr_frag<NKC>(Kc, 32 * m + 8 * g, f0);
             qb[m] = tr_frag<NKC>(Qc, 32 * m + 8 * g, f0);
         }
-        float *dqp = ba.dq + rowk0 + f0 + c16;
-        float *dkp = ba.dk + rowk0 + f0 + c16;
+        // Every product is taken transposed (operands swapped): lane (g, j) then
+        // holds features f0 + 4g + e of token 16 tt + j, one 16-byte store each
+        float *dqp = ba.dq + rowk0 + f0 + 4 * g;
+        float *dkp = ba.dk + rowk0 + f0 + 4 * g;
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
-            const int ra = tt * 16 + c16;       // this lane's A operand row
-            // dQ: a = dO S^T, bq = M1 K
+            const int ra = tt * 16 + c16;       // this lane's token row of the row fragments
+            // dQ^T: a = S dO^T, bq = K^T M1^T
             floatx4 a = zero4(), bq = zero4();
 #pragma unroll
             for (int mv = 0; mv < 4; ++mv)
                 if (mv < nmv) {
                     const bf16x8 oa = row_frag<NPV>(dOc, ra, 32 * mv);
-                    a = mfma32(oa, sh[mv], a);
-                    a = mfma32(oa, sl[mv], a);
+                    a = mfma32(sh[mv], oa, a);
+                    a = mfma32(sl[mv], oa, a);
                 }
 #pragma unroll
             for (int m = 0; m < 2; ++m)
                 if (m <= tt / 2) {
-                    bq = mfma32(row_frag<NPM>(M1h, ra, 32 * m), kb[m], bq);
-                    bq = mfma32(row_frag<NPM>(M1l, ra, 32 * m), kb[m], bq);
+                    bq = mfma32(kb[m], row_frag<NPM>(M1h, ra, 32 * m), bq);
+                    bq = mfma32(kb[m], row_frag<NPM>(M1l, ra, 32 * m), bq);
                 }
-            // dK: c1 = M1^T Q + M2^T K + M2 K, d1 = dX S^T, d2 = Vn dS'^T
+            // dK^T: c1 = Q^T M1 + K^T M2 + K^T M2^T, d1 = S dX^T, d2 = dS' Vn^T
             floatx4 c1 = zero4(), d1 = zero4(), d2 = zero4();
 #pragma unroll
             for (int m = 0; m < 2; ++m)
                 if (m >= tt / 2) {
-                    c1 = mfma32(tr_frag<NPM>(M1h, 32 * m + 8 * g, tt * 16), qb[m], c1);
-                    c1 = mfma32(tr_frag<NPM>(M1l, 32 * m + 8 * g, tt * 16), qb[m], c1);
-                    c1 = mfma32(tr_frag<NPM>(M2h, 32 * m + 8 * g, tt * 16), kb[m], c1);
-                    c1 = mfma32(tr_frag<NPM>(M2l, 32 * m + 8 * g, tt * 16), kb[m], c1);
+                    c1 = mfma32(qb[m], tr_frag<NPM>(M1h, 32 * m + 8 * g, tt * 16), c1);
+                    c1 = mfma32(qb[m], tr_frag<NPM>(M1l, 32 * m + 8 * g, tt * 16), c1);
+                    c1 = mfma32(kb[m], tr_frag<NPM>(M2h, 32 * m + 8 * g, tt * 16), c1);
+                    c1 = mfma32(kb[m], tr_frag<NPM>(M2l, 32 * m + 8 * g, tt * 16), c1);
                 }
 #pragma unroll
             for (int m = 0; m < 2; ++m)
                 if (m <= tt / 2) {
-                    c1 = mfma32(row_frag<NPM>(M2h, ra, 32 * m), kb[m], c1);
-                    c1 = mfma32(row_frag<NPM>(M2l, ra, 32 * m), kb[m], c1);
+                    c1 = mfma32(kb[m], row_frag<NPM>(M2h, ra, 32 * m), c1);
+                    c1 = mfma32(kb[m], row_frag<NPM>(M2l, ra, 32 * m), c1);
                 }
 #pragma unroll
             for (int mv = 0; mv < 4; ++mv)
                 if (mv < nmv) {
                     const bf16x8 xh = row_frag<NPV>(Xh, ra, 32 * mv), xl = row_frag<NPV>(Xl, ra, 32 * mv);
-                    d1 = mfma32(xh, sh[mv], d1);
-                    d1 = mfma32(xh, sl[mv], d1);
-                    d1 = mfma32(xl, sh[mv], d1);
+                    d1 = mfma32(sh[mv], xh, d1);
+                    d1 = mfma32(sl[mv], xh, d1);
+                    d1 = mfma32(sh[mv], xl, d1);
                     const bf16x8 vh = row_frag<NPV>(Vh, ra, 32 * mv), vl = row_frag<NPV>(Vl, ra, 32 * mv);
-                    d2 = mfma32(vh, dh[mv], d2);
-                    d2 = mfma32(vh, dl[mv], d2);
-                    d2 = mfma32(vl, dh[mv], d2);
+                    d2 = mfma32(dh[mv], vh, d2);
+                    d2 = mfma32(dl[mv], vh, d2);
+                    d2 = mfma32(dh[mv], vl, d2);
                 }
-            // accumulator rows r = 16 tt + 4g + e, feature f0 + j
-            const floatx4 qv = acc_vals<NKC>(Qc, tt * 16 + 4 * g, f0);
-            const floatx4 kv = acc_vals<NKC>(Kc, tt * 16 + 4 * g, f0);
+            // token r = 16 tt + j, features f0 + 4g + e
+            const int r = tt * 16 + c16, t = t0 + r;
+            const uint2 q2 = *reinterpret_cast<const uint2 *>(Qc + swz_at<NKC>(r, f0 + 4 * g));
+            const uint2 k2 = *reinterpret_cast<const uint2 *>(Kc + swz_at<NKC>(r, f0 + 4 * g));
+            const floatx4 qv{__builtin_bit_cast(float, q2.x << 16), __builtin_bit_cast(float, q2.x & 0xffff0000u),
+                             __builtin_bit_cast(float, q2.y << 16), __builtin_bit_cast(float, q2.y & 0xffff0000u)};
+            const floatx4 kv{__builtin_bit_cast(float, k2.x << 16), __builtin_bit_cast(float, k2.x & 0xffff0000u),
+                             __builtin_bit_cast(float, k2.y << 16), __builtin_bit_cast(float, k2.y & 0xffff0000u)};
+            const float g2 = G2[r], gam = fast_exp2(g2), lam = fast_exp2(g2L - g2), btt = Bt[r];
+            floatx4 dqo, dko;
+            float p3 = 0.f, ps = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = tt * 16 + 4 * g + e, t = t0 + r;
-                const float g2 = G2[r], gam = fast_exp2(g2), lam = fast_exp2(g2L - g2), btt = Bt[r];
-                const float qd = scale * gam * a[e];          // dQ_dir
+                const float qd = scale * gam * a[e];                  // dQ_dir
                 const float kr = -gam * (DPE ? 1.f : btt) * d1[e];   // dK_R
-                const float ks_ = lam * d2[e];                // dK_S'
-                if (t < T) {
-                    dqp[(size_t)t * tokk] = qd + bq[e];
-                    dkp[(size_t)t * tokk] = c1[e] + kr + ks_;
-                }
-                const float p3 = sum16(qd * qv[e] + kr * kv[e]);
-                const float ps = sum16(ks_ * kv[e]);
-                if (c16 == 0) {
-                    g3[w * C + r] = p3;
-                    gS[w * C + r] = ps;
-                }
+                const float ks_ = lam * d2[e];                        // dK_S'
+                dqo[e] = qd + bq[e];
+                dko[e] = c1[e] + kr + ks_;
+                p3 += qd * qv[e] + kr * kv[e];
+                ps += ks_ * kv[e];
+            }
+            if (t < T) {
+                *reinterpret_cast<floatx4 *>(dqp + (size_t)t * tokk) = dqo;
+                *reinterpret_cast<floatx4 *>(dkp + (size_t)t * tokk) = dko;
+            }
+            // sums over the slice's 16 features: the lane's 4, then the 4 lane groups
+            p3 += __shfl_xor(p3, 16, 64);
+            p3 += __shfl_xor(p3, 32, 64);
+            ps += __shfl_xor(ps, 16, 64);
+            ps += __shfl_xor(ps, 32, 64);
+            if (g == 0) {
+                g3[w * C + r] = p3;
+                gS[w * C + r] = ps;
             }
         }
     }

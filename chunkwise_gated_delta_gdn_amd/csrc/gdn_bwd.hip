@@ -514,8 +514,9 @@ extern "C" int gdn_bwd(const void *q, const void *k, const void *v, const float 
     if (T > 0) {
         GDN_REQUIRE(q && k && v && beta && log_decay && dout && dq && dk && dv && dbeta && dlog_decay, GDN_EINVAL,
                     "%s: null tensor pointer", name);
-        GDN_REQUIRE(gdn::aligned(q, 16) && gdn::aligned(k, 16) && gdn::aligned(v, 16) && gdn::aligned(dout, 16),
-                    GDN_EINVAL, "%s: q, k, v and dout must be 16-byte aligned", name);
+        GDN_REQUIRE(gdn::aligned(q, 16) && gdn::aligned(k, 16) && gdn::aligned(v, 16) && gdn::aligned(dout, 16) &&
+                        gdn::aligned(dq, 16) && gdn::aligned(dk, 16),
+                    GDN_EINVAL, "%s: q, k, v, dout, dq and dk must be 16-byte aligned", name);
         GDN_REQUIRE(gdn::aligned(v, 4) && gdn::aligned(dout, 4) && gdn::aligned(beta, 4) &&
                         gdn::aligned(log_decay, 4) && gdn::aligned(dq, 4) && gdn::aligned(dk, 4) &&
                         gdn::aligned(dv, 4) && gdn::aligned(dbeta, 4) && gdn::aligned(dlog_decay, 4),

@@ -383,7 +383,8 @@ size_t gdn_prep_bwd_workspace_bytes(int B, int N, int H, int D);
  *   dbeta, dlog_decay (B, T, H)    float32 (dlog_decay = dL/dg)
  *   dh0             (B, H, Dk, Dv) float32, nullable (not stored)
  * Supported: Dk in {16, 32, 64, 128}; Dv a multiple of 16 up to 4096; any
- * T >= 0.  q, k, v and dout 16-byte aligned, the other tensors 4-byte.  The
+ * T >= 0.  q, k, v, dout, dq and dk 16-byte aligned, the other tensors
+ * 4-byte.  The
  * work space depends on the path, hence on dtype; gdn_bwd_workspace_bytes
  * is the only authority on its size.  Chunkwise path: per 64-token chunk
  * and head, T and T^T (16 KiB), the scores (10 KiB), the gate table, S and
