@@ -681,8 +681,6 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int T = args.T, H = args.H, Dv = args.Dv;
     const int NT = (T + C - 1) / C;
-    const int bh = blockIdx.x / NT, c = blockIdx.x % NT;
-    const int b = bh / H, h = bh % H, t0 = c * C;
     const int nvs = Dv / 16, nmv = Dv / 32, nfs = KD / 16;
     const float scale = args.scale;
 
@@ -699,59 +697,23 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
     float *gS = reinterpret_cast<float *>(smem + S::OFF_GS), *ss = reinterpret_cast<float *>(smem + S::OFF_SS);
 
     const size_t tokk = (size_t)H * args.kst, tokv = (size_t)H * Dv;
-    const size_t rowk0 = ((size_t)b * T * H + h) * args.kst + args.koff, rowv0 = ((size_t)b * T * H + h) * Dv;
-    const u16 *og = reinterpret_cast<const u16 *>(ba.dout) + rowv0;
-
     u16 *dOc = reinterpret_cast<u16 *>(smem + S::OFF_DO);
     constexpr int NLOW = NTT * (NTT + 1) / 2;
-    // ---- phase 0 ----
-    // DPE: the second pass's v' gradient of this wave's value slice (rows
-    // tt*16 + 4g + e, column 16 w + c16) and the A~ fragments, loaded before
-    // everything else (the wait below then covers them)
-    floatx4 dvr[NTT];
-    u32x4 atf[NLOW];
-    if constexpr (DPE) {
-        const int ws = w < nvs ? w : 0;
-        const float *dp = ba.dvprev + rowv0 + 16 * ws + c16;
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dvr[tt][e] = dp[(size_t)min(t0 + tt * 16 + 4 * g + e, T - 1) * tokv];
-        const uint4 *ap = reinterpret_cast<const uint4 *>(args.atil) + ((size_t)bh * NT + c) * NLOW * 64 + l;
-#pragma unroll
-        for (int i = 0; i < NLOW; ++i) atf[i] = __builtin_bit_cast(u32x4, ap[i * 64]);
-        asm volatile("" ::: "memory");
-    }
-    // LDS-direct loads of K, Q, dO first, then this wave's register loads;
-    // the wait below (at most NREG outstanding) then covers the LDS-direct ones
-    constexpr int NREG = 2 * NTT + 6 + 16;      // R, dX; T' fragments; S, dS' fragments
+    const int f0 = 16 * w;
+    const int ws = w < nvs ? w : 0;             // a valid value slice for waves past the last
+
+    // One chunk per workgroup (job = blockIdx.x).  Its phase-3 operands (S and
+    // dS', half of its bytes) are loaded after the LDS-direct loads and not
+    // waited for until phase 3, so their latency hides behind phases 1 and 2.
+    // (A persistent form, walking chunks with the next chunk's operands in
+    // flight, needs more registers than two waves per SIMD have.)
     floatx4 rr[NTT], xr[NTT];
     bf16x8 tf[NTT][2];
+    floatx4 dvr[NTT];
+    u32x4 atf[NLOW];
     floatx4 sf[4][2], df[4][2];
-    const int f0 = 16 * w;
-    {
-        constexpr int NDK = S::SZ_KC / 1024, NDO = S::SZ_V / 1024;
-        const u16 *kg = reinterpret_cast<const u16 *>(args.k) + rowk0;
-        const u16 *qg = reinterpret_cast<const u16 *>(args.q) + rowk0;
-#pragma unroll
-        for (int k = w; k < 2 * NDK + NDO; k += S::NW) {
-            if (k < 2 * NDK) {
-                const int kk = k % NDK, pos = kk * 64 + l, r = pos / NKC, sc = pos % NKC;
-                const int t = t0 + r, pc = sc ^ kswz<NKC>(r);
-                const u16 *src = (k < NDK ? kg : qg) + (size_t)t * tokk + (pc << 3);
-                dma16(t < T ? static_cast<const void *>(src) : static_cast<const void *>(&kZero16),
-                      (k < NDK ? Kc : Qc) + kk * 512);
-            } else {
-                const int kk = k - 2 * NDK, pos = kk * 64 + l, r = pos / NPV, sc = pos % NPV;
-                const int t = t0 + r, pc = sc ^ kswz<NPV>(r);
-                dma16(t < T && pc * 8 < Dv ? static_cast<const void *>(og + (size_t)t * tokv + (pc << 3))
-                                           : static_cast<const void *>(&kZero16),
-                      dOc + kk * 512);
-            }
-        }
-        asm volatile("" ::: "memory");
-        // phase 1 operands (value slice w; a valid slice for waves past the last)
-        const int ws = w < nvs ? w : 0;
+    auto load_p1 = [&](int job) {
+        const int bh = job / NT, c = job % NT, b = bh / H, h = bh % H, t0 = c * C;
         const size_t so = ((((size_t)bh * NT + c) * nvs + ws) * 64 + l) * NTT;
         const floatx4 *rp = reinterpret_cast<const floatx4 *>(args.rst) + so;
         const floatx4 *xp = reinterpret_cast<const floatx4 *>(ba.dxst) + so;
@@ -766,8 +728,24 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
 #pragma unroll
             for (int m = 0; m < 2; ++m)
                 if (2 * m <= tt) tf[tt][m] = ld8(tg + (tt * 16 + c16) * C + (4 * m + g) * 8);
-        // phase 3 operands: S and dS' as B operands (lane (g, j): row f0 + j,
-        // value columns 32 mv + 8 g .. +7)
+        if constexpr (DPE) {
+            // the second pass's v' gradient of this wave's value slice (rows
+            // tt*16 + 4g + e, column 16 ws + c16) and the A~ fragments
+            const float *dp = ba.dvprev + ((size_t)b * T * H + h) * Dv + 16 * ws + c16;
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dvr[tt][e] = dp[(size_t)min(t0 + tt * 16 + 4 * g + e, T - 1) * tokv];
+            const uint4 *ap = reinterpret_cast<const uint4 *>(args.atil) + ((size_t)bh * NT + c) * NLOW * 64 + l;
+#pragma unroll
+            for (int i = 0; i < NLOW; ++i) atf[i] = __builtin_bit_cast(u32x4, ap[i * 64]);
+        }
+    };
+    // S and dS' as phase 3's A operands (lane (g, j): row f0 + j, value
+    // columns 32 mv + 8 g .. +7): NP3 loads
+    constexpr int NP3 = 16;
+    auto load_p3 = [&](int job) {
+        const int bh = job / NT, c = job % NT;
         const size_t sbase = (((size_t)bh * NT + c) * KD + (w < nfs ? f0 : 0) + c16) * Dv + 8 * g;
 #pragma unroll
         for (int mv = 0; mv < 4; ++mv)
@@ -777,332 +755,368 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
                 sf[mv][hh] = *reinterpret_cast<const floatx4 *>(args.sst + o);
                 df[mv][hh] = *reinterpret_cast<const floatx4 *>(ba.dsst + o);
             }
-        // M1, M2 (all four arrays, 32 KiB) and the per-tile partial slots cleared
+    };
+    {
+        const int job = blockIdx.x;
+        const int bh = job / NT, c = job % NT;
+        const int b = bh / H, h = bh % H, t0 = c * C;
+        const size_t rowk0 = ((size_t)b * T * H + h) * args.kst + args.koff, rowv0 = ((size_t)b * T * H + h) * Dv;
+        const u16 *og = reinterpret_cast<const u16 *>(ba.dout) + rowv0;
+        // ---- phase 0 ----
+        // phase 1's operands, the LDS-direct loads of K, Q and dO, then this
+        // wave's S and dS' loads; the wait below (at most NP3 outstanding)
+        // covers the LDS-direct loads and everything issued before them
+        load_p1(job);
+        asm volatile("" ::: "memory");
         {
-            uint4 *z = reinterpret_cast<uint4 *>(smem + S::OFF_M1H);
-            for (int i = tid; i < 4 * S::SZ_M / 16; i += S::NTHR) z[i] = uint4{0u, 0u, 0u, 0u};
-            float *zf = reinterpret_cast<float *>(smem + S::OFF_ZERO);
-            for (int i = tid; i < (S::OFF_ZEND - S::OFF_ZERO) / 4; i += S::NTHR) zf[i] = 0.f;
-        }
-        if (w == S::NW - 1) {
-            const int t = t0 + l;
-            const bool ok = t < T;
-            const size_t gi = ((size_t)b * T + (ok ? t : 0)) * H + h;
-            float gs = ok ? args.g[gi] : 0.f;
+            constexpr int NDK = S::SZ_KC / 1024, NDO = S::SZ_V / 1024;
+            const u16 *kg = reinterpret_cast<const u16 *>(args.k) + rowk0;
+            const u16 *qg = reinterpret_cast<const u16 *>(args.q) + rowk0;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(gs, off, 64);
-                if (l >= off) gs += y;
+            for (int k = w; k < 2 * NDK + NDO; k += S::NW) {
+                if (k < 2 * NDK) {
+                    const int kk = k % NDK, pos = kk * 64 + l, r = pos / NKC, sc = pos % NKC;
+                    const int t = t0 + r, pc = sc ^ kswz<NKC>(r);
+                    const u16 *src = (k < NDK ? kg : qg) + (size_t)t * tokk + (pc << 3);
+                    dma16(t < T ? static_cast<const void *>(src) : static_cast<const void *>(&kZero16),
+                          (k < NDK ? Kc : Qc) + kk * 512);
+                } else {
+                    const int kk = k - 2 * NDK, pos = kk * 64 + l, r = pos / NPV, sc = pos % NPV;
+                    const int t = t0 + r, pc = sc ^ kswz<NPV>(r);
+                    dma16(t < T && pc * 8 < Dv ? static_cast<const void *>(og + (size_t)t * tokv + (pc << 3))
+                                               : static_cast<const void *>(&kZero16),
+                          dOc + kk * 512);
+                }
             }
-            G2[l] = gs * LOG2E;
-            Bt[l] = ok ? args.beta[gi * args.bst + args.boff] : 0.f;
+            asm volatile("" ::: "memory");
+            load_p3(job);
+            // M1, M2 (all four arrays, 32 KiB) and the per-tile partial slots cleared
+            {
+                uint4 *z = reinterpret_cast<uint4 *>(smem + S::OFF_M1H);
+                for (int i = tid; i < 4 * S::SZ_M / 16; i += S::NTHR) z[i] = uint4{0u, 0u, 0u, 0u};
+                float *zf = reinterpret_cast<float *>(smem + S::OFF_ZERO);
+                for (int i = tid; i < (S::OFF_ZEND - S::OFF_ZERO) / 4; i += S::NTHR) zf[i] = 0.f;
+            }
+            if (w == S::NW - 1) {
+                const int t = t0 + l;
+                const bool ok = t < T;
+                const size_t gi = ((size_t)b * T + (ok ? t : 0)) * H + h;
+                float gs = ok ? args.g[gi] : 0.f;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float y = __shfl_up(gs, off, 64);
+                    if (l >= off) gs += y;
+                }
+                G2[l] = gs * LOG2E;
+                Bt[l] = ok ? args.beta[gi * args.bst + args.boff] : 0.f;
+            }
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt((NP3 & 15) | ((NP3 >> 4) << 14) | 0x0070);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
         }
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt((NREG & 15) | ((NREG >> 4) << 14) | 0x0070);
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-    }
 
-    // ---- phase 1: value slice w ----
-    if (w < nvs) {
-        const int v0 = 16 * w;
-        floatx4 bt[NTT];
+        // ---- phase 1: value slice w ----
+        if (w < nvs) {
+            const int v0 = 16 * w;
+            floatx4 bt[NTT];
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-            bt[tt] = *reinterpret_cast<const floatx4 *>(Bt + tt * 16 + 4 * g);
+            for (int tt = 0; tt < NTT; ++tt) {
+                bt[tt] = *reinterpret_cast<const floatx4 *>(Bt + tt * 16 + 4 * g);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (t0 + tt * 16 + 4 * g + e >= T) rr[tt][e] = xr[tt][e] = 0.f;
-        }
-        if constexpr (DPE) {
+                for (int e = 0; e < 4; ++e)
+                    if (t0 + tt * 16 + 4 * g + e >= T) rr[tt][e] = xr[tt][e] = 0.f;
+            }
+            if constexpr (DPE) {
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (t0 + tt * 16 + 4 * g + e >= T) dvr[tt][e] = 0.f;
+            }
+            bf16x8 rh[2], rl[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) frag_split(rr[2 * m], rr[2 * m + 1], rh[m], rl[m]);
+            floatx4 vn[NTT];
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vn[tt][e] = bt[tt][e] * rr[tt][e];
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    if (2 * m <= tt) {
+                        vn[tt] = mfma32(tf[tt][m], rh[m], vn[tt]);
+                        vn[tt] = mfma32(tf[tt][m], rl[m], vn[tt]);
+                    }
+            }
+            // DPE: e = R - A~ Vn for dbeta (A~ tiles as A operands, Vn tiles as B
+            // operands in their accumulator layout, both hi + lo)
+            floatx4 ev[NTT];
+            if constexpr (DPE) {
+                shortx4 nh[NTT], nl[NTT];
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt) split4(vn[tt], nh[tt], nl[tt]);
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt) {
+                    floatx4 u = zero4();
+#pragma unroll
+                    for (int ss = 0; ss <= tt; ++ss) {
+                        const u32x4 f = atf[tt * (tt + 1) / 2 + ss];
+                        const shortx4 ah = __builtin_bit_cast(shortx4, uint2{f[0], f[1]});
+                        const shortx4 al = __builtin_bit_cast(shortx4, uint2{f[2], f[3]});
+                        u = mfma16(ah, nh[ss], u);
+                        u = mfma16(ah, nl[ss], u);
+                        u = mfma16(al, nh[ss], u);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ev[tt][e] = rr[tt][e] - u[e];
+                }
+            }
+            const float mc = args.mcoef;
+            float *dvp = ba.dv + rowv0 + v0 + c16;
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (t0 + tt * 16 + 4 * g + e >= T) dvr[tt][e] = 0.f;
-        }
-        bf16x8 rh[2], rl[2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) frag_split(rr[2 * m], rr[2 * m + 1], rh[m], rl[m]);
-        floatx4 vn[NTT];
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vn[tt][e] = bt[tt][e] * rr[tt][e];
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-                if (2 * m <= tt) {
-                    vn[tt] = mfma32(tf[tt][m], rh[m], vn[tt]);
-                    vn[tt] = mfma32(tf[tt][m], rl[m], vn[tt]);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = tt * 16 + 4 * g + e, t = t0 + r;
+                    const float bx = bt[tt][e] * xr[tt][e];
+                    // dV = beta dX (DPE: + dv'); the X rows hold dX (DPE: dR = beta dX + m dv')
+                    float xs = xr[tt][e], pb;
+                    if constexpr (DPE) {
+                        if (t < T) dvp[(size_t)t * tokv] = bx + dvr[tt][e];
+                        xs = bx + mc * dvr[tt][e];
+                        pb = sum16(xr[tt][e] * ev[tt][e]);
+                    } else {
+                        if (t < T) dvp[(size_t)t * tokv] = bx;
+                        pb = sum16(xr[tt][e] * rr[tt][e]);
+                    }
+                    if (c16 == 0) db1[w * C + r] = pb;
+                    u16 hi, lo;
+                    const int at = swz_at<NPV>(r, v0 + c16);
+                    split1(vn[tt][e], hi, lo);
+                    Vh[at] = hi;
+                    Vl[at] = lo;
+                    split1(xs, hi, lo);
+                    Xh[at] = hi;
+                    Xl[at] = lo;
                 }
         }
-        // DPE: e = R - A~ Vn for dbeta (A~ tiles as A operands, Vn tiles as B
-        // operands in their accumulator layout, both hi + lo)
-        floatx4 ev[NTT];
-        if constexpr (DPE) {
-            shortx4 nh[NTT], nl[NTT];
+        lds_barrier();
+
+        // ---- phase 2: lower tiles of M1 (kind 0) and of dA, M2 (kind 1) ----
+        for (int job = w; job < 20; job += S::NW) {
+            const int kind = job / 10, idx = job % 10;
+            const int ti = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0, tj = idx - ti * (ti + 1) / 2;
+            const int ra = ti * 16 + c16, rb = tj * 16 + c16;   // this lane's A and B operand rows
+            floatx4 x = zero4(), y = zero4();
+            if (kind == 0) {
+                // x = dO Vn^T, y = Q K^T
 #pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) split4(vn[tt], nh[tt], nl[tt]);
+                for (int mv = 0; mv < 4; ++mv)
+                    if (mv < nmv) {
+                        const bf16x8 oa = row_frag<NPV>(dOc, ra, 32 * mv);
+                        x = mfma32(oa, row_frag<NPV>(Vh, rb, 32 * mv), x);
+                        x = mfma32(oa, row_frag<NPV>(Vl, rb, 32 * mv), x);
+                    }
+#pragma unroll
+                for (int m = 0; m < NKS; ++m) y = mfma32(row_frag<NKC>(Qc, ra, 32 * m), row_frag<NKC>(Kc, rb, 32 * m), y);
+            } else {
+                // x = dX Vn^T (both hi + lo), y = K K^T
+#pragma unroll
+                for (int mv = 0; mv < 4; ++mv)
+                    if (mv < nmv) {
+                        const bf16x8 ah = row_frag<NPV>(Xh, ra, 32 * mv), al = row_frag<NPV>(Xl, ra, 32 * mv);
+                        const bf16x8 bh_ = row_frag<NPV>(Vh, rb, 32 * mv), bl = row_frag<NPV>(Vl, rb, 32 * mv);
+                        x = mfma32(ah, bh_, x);
+                        x = mfma32(ah, bl, x);
+                        x = mfma32(al, bh_, x);
+                    }
+#pragma unroll
+                for (int m = 0; m < NKS; ++m) y = mfma32(row_frag<NKC>(Kc, ra, 32 * m), row_frag<NKC>(Kc, rb, 32 * m), y);
+            }
+            // accumulator: lane (g, j) holds rows t = 16 ti + 4g + e, column s = 16 tj + j
+            const int s = tj * 16 + c16;
+            const float g2s = G2[s];
+            float wv[4], csum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = ti * 16 + 4 * g + e;
+                const float gam = fast_exp2(fminf(G2[t] - g2s, 0.f));
+                float mval, dbv = 0.f;
+                if (kind == 0) {
+                    mval = s <= t ? scale * x[e] * gam : 0.f;
+                    wv[e] = mval * y[e];
+                } else {
+                    // DPE: x = dR Vn^T, and da is dB (beta already in dR)
+                    const float da = s < t ? -x[e] : 0.f, bg = s < t ? y[e] * gam : 0.f, btt = DPE ? 1.f : Bt[t];
+                    wv[e] = da * btt * bg;
+                    mval = btt * da * gam;
+                    dbv = da * bg;
+                }
+                u16 hi, lo;
+                split1(mval, hi, lo);
+                const int at = swz_at<NPM>(t, s);
+                (kind == 0 ? M1h : M2h)[at] = hi;
+                (kind == 0 ? M1l : M2l)[at] = lo;
+                const float rs = sum16(wv[e]);
+                if (!DPE && kind == 1) {
+                    const float rb2 = sum16(dbv);
+                    if (c16 == 0) db2[tj * C + t] = rb2;
+                }
+                if (c16 == 0) (kind == 0 ? gr1 : gr2)[tj * C + t] = rs;
+                csum += wv[e];
+            }
+            csum += __shfl_xor(csum, 16, 64);
+            csum += __shfl_xor(csum, 32, 64);
+            if (g == 0) (kind == 0 ? gc1 : gc2)[ti * C + s] = csum;
+        }
+        lds_barrier();
+
+        // ---- phase 3: key features f0 .. f0 + 15 ----
+        if (w < nfs) {
+            bf16x8 sh[4], sl[4], dh[4], dl[4];
+            float sdot = 0.f;
+#pragma unroll
+            for (int mv = 0; mv < 4; ++mv) {
+                frag_split(sf[mv][0], sf[mv][1], sh[mv], sl[mv]);
+                frag_split(df[mv][0], df[mv][1], dh[mv], dl[mv]);
+                if (mv < nmv)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sdot += sf[mv][hh][e] * df[mv][hh][e];
+            }
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) sdot += __shfl_xor(sdot, off, 64);
+            if (l == 0) ss[w] = sdot;
+            const float g2L = G2[C - 1];
+            // K and Q as B operands (k = token, n = feature f0 + j), both 32-token steps
+            bf16x8 kb[2], qb[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                kb[m] = tr_frag<NKC>(Kc, 32 * m + 8 * g, f0);
+                qb[m] = tr_frag<NKC>(Qc, 32 * m + 8 * g, f0);
+            }
+            // Every product is taken transposed (operands swapped): lane (g, j) then
+            // holds features f0 + 4g + e of token 16 tt + j, one 16-byte store each
+            float *dqp = ba.dq + rowk0 + f0 + 4 * g;
+            float *dkp = ba.dk + rowk0 + f0 + 4 * g;
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
-                floatx4 u = zero4();
+                const int ra = tt * 16 + c16;       // this lane's token row of the row fragments
+                // dQ^T: a = S dO^T, bq = K^T M1^T
+                floatx4 a = zero4(), bq = zero4();
 #pragma unroll
-                for (int ss = 0; ss <= tt; ++ss) {
-                    const u32x4 f = atf[tt * (tt + 1) / 2 + ss];
-                    const shortx4 ah = __builtin_bit_cast(shortx4, uint2{f[0], f[1]});
-                    const shortx4 al = __builtin_bit_cast(shortx4, uint2{f[2], f[3]});
-                    u = mfma16(ah, nh[ss], u);
-                    u = mfma16(ah, nl[ss], u);
-                    u = mfma16(al, nh[ss], u);
+                for (int mv = 0; mv < 4; ++mv)
+                    if (mv < nmv) {
+                        const bf16x8 oa = row_frag<NPV>(dOc, ra, 32 * mv);
+                        a = mfma32(sh[mv], oa, a);
+                        a = mfma32(sl[mv], oa, a);
+                    }
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    if (m <= tt / 2) {
+                        bq = mfma32(kb[m], row_frag<NPM>(M1h, ra, 32 * m), bq);
+                        bq = mfma32(kb[m], row_frag<NPM>(M1l, ra, 32 * m), bq);
+                    }
+                // dK^T: c1 = Q^T M1 + K^T M2 + K^T M2^T, d1 = S dX^T, d2 = dS' Vn^T
+                floatx4 c1 = zero4(), d1 = zero4(), d2 = zero4();
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    if (m >= tt / 2) {
+                        c1 = mfma32(qb[m], tr_frag<NPM>(M1h, 32 * m + 8 * g, tt * 16), c1);
+                        c1 = mfma32(qb[m], tr_frag<NPM>(M1l, 32 * m + 8 * g, tt * 16), c1);
+                        c1 = mfma32(kb[m], tr_frag<NPM>(M2h, 32 * m + 8 * g, tt * 16), c1);
+                        c1 = mfma32(kb[m], tr_frag<NPM>(M2l, 32 * m + 8 * g, tt * 16), c1);
+                    }
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    if (m <= tt / 2) {
+                        c1 = mfma32(kb[m], row_frag<NPM>(M2h, ra, 32 * m), c1);
+                        c1 = mfma32(kb[m], row_frag<NPM>(M2l, ra, 32 * m), c1);
+                    }
+#pragma unroll
+                for (int mv = 0; mv < 4; ++mv)
+                    if (mv < nmv) {
+                        const bf16x8 xh = row_frag<NPV>(Xh, ra, 32 * mv), xl = row_frag<NPV>(Xl, ra, 32 * mv);
+                        d1 = mfma32(sh[mv], xh, d1);
+                        d1 = mfma32(sl[mv], xh, d1);
+                        d1 = mfma32(sh[mv], xl, d1);
+                        const bf16x8 vh = row_frag<NPV>(Vh, ra, 32 * mv), vl = row_frag<NPV>(Vl, ra, 32 * mv);
+                        d2 = mfma32(dh[mv], vh, d2);
+                        d2 = mfma32(dl[mv], vh, d2);
+                        d2 = mfma32(dh[mv], vl, d2);
+                    }
+                // token r = 16 tt + j, features f0 + 4g + e
+                const int r = tt * 16 + c16, t = t0 + r;
+                const uint2 q2 = *reinterpret_cast<const uint2 *>(Qc + swz_at<NKC>(r, f0 + 4 * g));
+                const uint2 k2 = *reinterpret_cast<const uint2 *>(Kc + swz_at<NKC>(r, f0 + 4 * g));
+                const floatx4 qv{__builtin_bit_cast(float, q2.x << 16), __builtin_bit_cast(float, q2.x & 0xffff0000u),
+                                 __builtin_bit_cast(float, q2.y << 16), __builtin_bit_cast(float, q2.y & 0xffff0000u)};
+                const floatx4 kv{__builtin_bit_cast(float, k2.x << 16), __builtin_bit_cast(float, k2.x & 0xffff0000u),
+                                 __builtin_bit_cast(float, k2.y << 16), __builtin_bit_cast(float, k2.y & 0xffff0000u)};
+                const float g2 = G2[r], gam = fast_exp2(g2), lam = fast_exp2(g2L - g2), btt = Bt[r];
+                floatx4 dqo, dko;
+                float p3 = 0.f, ps = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float qd = scale * gam * a[e];                  // dQ_dir
+                    const float kr = -gam * (DPE ? 1.f : btt) * d1[e];   // dK_R
+                    const float ks_ = lam * d2[e];                        // dK_S'
+                    dqo[e] = qd + bq[e];
+                    dko[e] = c1[e] + kr + ks_;
+                    p3 += qd * qv[e] + kr * kv[e];
+                    ps += ks_ * kv[e];
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ev[tt][e] = rr[tt][e] - u[e];
+                if (t < T) {
+                    *reinterpret_cast<floatx4 *>(dqp + (size_t)t * tokk) = dqo;
+                    *reinterpret_cast<floatx4 *>(dkp + (size_t)t * tokk) = dko;
+                }
+                // sums over the slice's 16 features: the lane's 4, then the 4 lane groups
+                p3 += __shfl_xor(p3, 16, 64);
+                p3 += __shfl_xor(p3, 32, 64);
+                ps += __shfl_xor(ps, 16, 64);
+                ps += __shfl_xor(ps, 32, 64);
+                if (g == 0) {
+                    g3[w * C + r] = p3;
+                    gS[w * C + r] = ps;
+                }
             }
         }
-        const float mc = args.mcoef;
-        float *dvp = ba.dv + rowv0 + v0 + c16;
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = tt * 16 + 4 * g + e, t = t0 + r;
-                const float bx = bt[tt][e] * xr[tt][e];
-                // dV = beta dX (DPE: + dv'); the X rows hold dX (DPE: dR = beta dX + m dv')
-                float xs = xr[tt][e], pb;
-                if constexpr (DPE) {
-                    if (t < T) dvp[(size_t)t * tokv] = bx + dvr[tt][e];
-                    xs = bx + mc * dvr[tt][e];
-                    pb = sum16(xr[tt][e] * ev[tt][e]);
-                } else {
-                    if (t < T) dvp[(size_t)t * tokv] = bx;
-                    pb = sum16(xr[tt][e] * rr[tt][e]);
-                }
-                if (c16 == 0) db1[w * C + r] = pb;
-                u16 hi, lo;
-                const int at = swz_at<NPV>(r, v0 + c16);
-                split1(vn[tt][e], hi, lo);
-                Vh[at] = hi;
-                Vl[at] = lo;
-                split1(xs, hi, lo);
-                Xh[at] = hi;
-                Xl[at] = lo;
-            }
-    }
-    lds_barrier();
+        lds_barrier();
 
-    // ---- phase 2: lower tiles of M1 (kind 0) and of dA, M2 (kind 1) ----
-    for (int job = w; job < 20; job += S::NW) {
-        const int kind = job / 10, idx = job % 10;
-        const int ti = idx >= 6 ? 3 : idx >= 3 ? 2 : idx >= 1 ? 1 : 0, tj = idx - ti * (ti + 1) / 2;
-        const int ra = ti * 16 + c16, rb = tj * 16 + c16;   // this lane's A and B operand rows
-        floatx4 x = zero4(), y = zero4();
-        if (kind == 0) {
-            // x = dO Vn^T, y = Q K^T
+        // ---- phase 4: dbeta, dg ----
+        if (w == 0) {
+            const int r = l, t = t0 + r;
+            float db = 0.f, dG = 0.f, gsum = 0.f;
+            for (int i = 0; i < nvs; ++i) db += db1[i * C + r];
 #pragma unroll
-            for (int mv = 0; mv < 4; ++mv)
-                if (mv < nmv) {
-                    const bf16x8 oa = row_frag<NPV>(dOc, ra, 32 * mv);
-                    x = mfma32(oa, row_frag<NPV>(Vh, rb, 32 * mv), x);
-                    x = mfma32(oa, row_frag<NPV>(Vl, rb, 32 * mv), x);
-                }
-#pragma unroll
-            for (int m = 0; m < NKS; ++m) y = mfma32(row_frag<NKC>(Qc, ra, 32 * m), row_frag<NKC>(Kc, rb, 32 * m), y);
-        } else {
-            // x = dX Vn^T (both hi + lo), y = K K^T
-#pragma unroll
-            for (int mv = 0; mv < 4; ++mv)
-                if (mv < nmv) {
-                    const bf16x8 ah = row_frag<NPV>(Xh, ra, 32 * mv), al = row_frag<NPV>(Xl, ra, 32 * mv);
-                    const bf16x8 bh_ = row_frag<NPV>(Vh, rb, 32 * mv), bl = row_frag<NPV>(Vl, rb, 32 * mv);
-                    x = mfma32(ah, bh_, x);
-                    x = mfma32(ah, bl, x);
-                    x = mfma32(al, bh_, x);
-                }
-#pragma unroll
-            for (int m = 0; m < NKS; ++m) y = mfma32(row_frag<NKC>(Kc, ra, 32 * m), row_frag<NKC>(Kc, rb, 32 * m), y);
-        }
-        // accumulator: lane (g, j) holds rows t = 16 ti + 4g + e, column s = 16 tj + j
-        const int s = tj * 16 + c16;
-        const float g2s = G2[s];
-        float wv[4], csum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = ti * 16 + 4 * g + e;
-            const float gam = fast_exp2(fminf(G2[t] - g2s, 0.f));
-            float mval, dbv = 0.f;
-            if (kind == 0) {
-                mval = s <= t ? scale * x[e] * gam : 0.f;
-                wv[e] = mval * y[e];
-            } else {
-                // DPE: x = dR Vn^T, and da is dB (beta already in dR)
-                const float da = s < t ? -x[e] : 0.f, bg = s < t ? y[e] * gam : 0.f, btt = DPE ? 1.f : Bt[t];
-                wv[e] = da * btt * bg;
-                mval = btt * da * gam;
-                dbv = da * bg;
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (!DPE) db += db2[i * C + r];
+                dG += gr1[i * C + r] - gc1[i * C + r] + gr2[i * C + r] - gc2[i * C + r];
             }
-            u16 hi, lo;
-            split1(mval, hi, lo);
-            const int at = swz_at<NPM>(t, s);
-            (kind == 0 ? M1h : M2h)[at] = hi;
-            (kind == 0 ? M1l : M2l)[at] = lo;
-            const float rs = sum16(wv[e]);
-            if (!DPE && kind == 1) {
-                const float rb2 = sum16(dbv);
-                if (c16 == 0) db2[tj * C + t] = rb2;
+            float sst = 0.f;
+            for (int i = 0; i < nfs; ++i) {
+                dG += g3[i * C + r];
+                gsum += gS[i * C + r];
+                sst += ss[i];
             }
-            if (c16 == 0) (kind == 0 ? gr1 : gr2)[tj * C + t] = rs;
-            csum += wv[e];
-        }
-        csum += __shfl_xor(csum, 16, 64);
-        csum += __shfl_xor(csum, 32, 64);
-        if (g == 0) (kind == 0 ? gc1 : gc2)[ti * C + s] = csum;
-    }
-    lds_barrier();
-
-    // ---- phase 3: key features f0 .. f0 + 15 ----
-    if (w < nfs) {
-        bf16x8 sh[4], sl[4], dh[4], dl[4];
-        float sdot = 0.f;
+            dG -= gsum;
+            float tot = gsum;
 #pragma unroll
-        for (int mv = 0; mv < 4; ++mv) {
-            frag_split(sf[mv][0], sf[mv][1], sh[mv], sl[mv]);
-            frag_split(df[mv][0], df[mv][1], dh[mv], dl[mv]);
-            if (mv < nmv)
+            for (int off = 1; off < 64; off <<= 1) tot += __shfl_xor(tot, off, 64);
+            if (r == C - 1) dG += tot + fast_exp2(G2[C - 1]) * sst;
+            // dg_t = sum over t' >= t of dG_t'
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sdot += sf[mv][hh][e] * df[mv][hh][e];
-        }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) sdot += __shfl_xor(sdot, off, 64);
-        if (l == 0) ss[w] = sdot;
-        const float g2L = G2[C - 1];
-        // K and Q as B operands (k = token, n = feature f0 + j), both 32-token steps
-        bf16x8 kb[2], qb[2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            kb[m] = tr_frag<NKC>(Kc, 32 * m + 8 * g, f0);
-            qb[m] = tr_frag<NKC>(Qc, 32 * m + 8 * g, f0);
-        }
-        // Every product is taken transposed (operands swapped): lane (g, j) then
-        // holds features f0 + 4g + e of token 16 tt + j, one 16-byte store each
-        float *dqp = ba.dq + rowk0 + f0 + 4 * g;
-        float *dkp = ba.dk + rowk0 + f0 + 4 * g;
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-            const int ra = tt * 16 + c16;       // this lane's token row of the row fragments
-            // dQ^T: a = S dO^T, bq = K^T M1^T
-            floatx4 a = zero4(), bq = zero4();
-#pragma unroll
-            for (int mv = 0; mv < 4; ++mv)
-                if (mv < nmv) {
-                    const bf16x8 oa = row_frag<NPV>(dOc, ra, 32 * mv);
-                    a = mfma32(sh[mv], oa, a);
-                    a = mfma32(sl[mv], oa, a);
-                }
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-                if (m <= tt / 2) {
-                    bq = mfma32(kb[m], row_frag<NPM>(M1h, ra, 32 * m), bq);
-                    bq = mfma32(kb[m], row_frag<NPM>(M1l, ra, 32 * m), bq);
-                }
-            // dK^T: c1 = Q^T M1 + K^T M2 + K^T M2^T, d1 = S dX^T, d2 = dS' Vn^T
-            floatx4 c1 = zero4(), d1 = zero4(), d2 = zero4();
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-                if (m >= tt / 2) {
-                    c1 = mfma32(qb[m], tr_frag<NPM>(M1h, 32 * m + 8 * g, tt * 16), c1);
-                    c1 = mfma32(qb[m], tr_frag<NPM>(M1l, 32 * m + 8 * g, tt * 16), c1);
-                    c1 = mfma32(kb[m], tr_frag<NPM>(M2h, 32 * m + 8 * g, tt * 16), c1);
-                    c1 = mfma32(kb[m], tr_frag<NPM>(M2l, 32 * m + 8 * g, tt * 16), c1);
-                }
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-                if (m <= tt / 2) {
-                    c1 = mfma32(kb[m], row_frag<NPM>(M2h, ra, 32 * m), c1);
-                    c1 = mfma32(kb[m], row_frag<NPM>(M2l, ra, 32 * m), c1);
-                }
-#pragma unroll
-            for (int mv = 0; mv < 4; ++mv)
-                if (mv < nmv) {
-                    const bf16x8 xh = row_frag<NPV>(Xh, ra, 32 * mv), xl = row_frag<NPV>(Xl, ra, 32 * mv);
-                    d1 = mfma32(sh[mv], xh, d1);
-                    d1 = mfma32(sl[mv], xh, d1);
-                    d1 = mfma32(sh[mv], xl, d1);
-                    const bf16x8 vh = row_frag<NPV>(Vh, ra, 32 * mv), vl = row_frag<NPV>(Vl, ra, 32 * mv);
-                    d2 = mfma32(dh[mv], vh, d2);
-                    d2 = mfma32(dl[mv], vh, d2);
-                    d2 = mfma32(dh[mv], vl, d2);
-                }
-            // token r = 16 tt + j, features f0 + 4g + e
-            const int r = tt * 16 + c16, t = t0 + r;
-            const uint2 q2 = *reinterpret_cast<const uint2 *>(Qc + swz_at<NKC>(r, f0 + 4 * g));
-            const uint2 k2 = *reinterpret_cast<const uint2 *>(Kc + swz_at<NKC>(r, f0 + 4 * g));
-            const floatx4 qv{__builtin_bit_cast(float, q2.x << 16), __builtin_bit_cast(float, q2.x & 0xffff0000u),
-                             __builtin_bit_cast(float, q2.y << 16), __builtin_bit_cast(float, q2.y & 0xffff0000u)};
-            const floatx4 kv{__builtin_bit_cast(float, k2.x << 16), __builtin_bit_cast(float, k2.x & 0xffff0000u),
-                             __builtin_bit_cast(float, k2.y << 16), __builtin_bit_cast(float, k2.y & 0xffff0000u)};
-            const float g2 = G2[r], gam = fast_exp2(g2), lam = fast_exp2(g2L - g2), btt = Bt[r];
-            floatx4 dqo, dko;
-            float p3 = 0.f, ps = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float qd = scale * gam * a[e];                  // dQ_dir
-                const float kr = -gam * (DPE ? 1.f : btt) * d1[e];   // dK_R
-                const float ks_ = lam * d2[e];                        // dK_S'
-                dqo[e] = qd + bq[e];
-                dko[e] = c1[e] + kr + ks_;
-                p3 += qd * qv[e] + kr * kv[e];
-                ps += ks_ * kv[e];
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_down(dG, off, 64);
+                if (r + off < 64) dG += y;
             }
             if (t < T) {
-                *reinterpret_cast<floatx4 *>(dqp + (size_t)t * tokk) = dqo;
-                *reinterpret_cast<floatx4 *>(dkp + (size_t)t * tokk) = dko;
+                const size_t gi = ((size_t)b * T + t) * H + h;
+                ba.dbeta[gi * args.bst + args.boff] = db;
+                ba.dg[gi] = DPE ? ba.dg[gi] + dG : dG;   // DPE: the second pass's share is there
             }
-            // sums over the slice's 16 features: the lane's 4, then the 4 lane groups
-            p3 += __shfl_xor(p3, 16, 64);
-            p3 += __shfl_xor(p3, 32, 64);
-            ps += __shfl_xor(ps, 16, 64);
-            ps += __shfl_xor(ps, 32, 64);
-            if (g == 0) {
-                g3[w * C + r] = p3;
-                gS[w * C + r] = ps;
-            }
-        }
-    }
-    lds_barrier();
-
-    // ---- phase 4: dbeta, dg ----
-    if (w == 0) {
-        const int r = l, t = t0 + r;
-        float db = 0.f, dG = 0.f, gsum = 0.f;
-        for (int i = 0; i < nvs; ++i) db += db1[i * C + r];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (!DPE) db += db2[i * C + r];
-            dG += gr1[i * C + r] - gc1[i * C + r] + gr2[i * C + r] - gc2[i * C + r];
-        }
-        float sst = 0.f;
-        for (int i = 0; i < nfs; ++i) {
-            dG += g3[i * C + r];
-            gsum += gS[i * C + r];
-            sst += ss[i];
-        }
-        dG -= gsum;
-        float tot = gsum;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) tot += __shfl_xor(tot, off, 64);
-        if (r == C - 1) dG += tot + fast_exp2(G2[C - 1]) * sst;
-        // dg_t = sum over t' >= t of dG_t'
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_down(dG, off, 64);
-            if (r + off < 64) dG += y;
-        }
-        if (t < T) {
-            const size_t gi = ((size_t)b * T + t) * H + h;
-            ba.dbeta[gi * args.bst + args.boff] = db;
-            ba.dg[gi] = DPE ? ba.dg[gi] + dG : dG;   // DPE: the second pass's share is there
         }
     }
 }
