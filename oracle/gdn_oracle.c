@@ -48,6 +48,14 @@ int oracle_max_threads(void) {
 #endif
 }
 
+static int thread_num(void) {
+#ifdef _OPENMP
+    return omp_get_thread_num();
+#else
+    return 0;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* O1: gated delta rule, token by token.                                    */
 /*                                                                          */
@@ -332,11 +340,11 @@ int oracle_cam_prep_bwd(int B, int N, int H, int D, const float *qkv,
     set_threads(nthreads);
     int C = H * D, half = D / 2;
     long ntok = (long)B * N;
-    int nt = omp_get_max_threads();
+    int nt = oracle_max_threads();
     double *wpart = (double *)calloc((size_t)nt * 2 * C, sizeof(double));   /* per-thread dq_w, dk_w */
 #pragma omp parallel
     {
-        double *myw = wpart + (size_t)omp_get_thread_num() * 2 * C;
+        double *myw = wpart + (size_t)thread_num() * 2 * C;
         double *gaq = (double *)malloc(sizeof(double) * C), *gak = (double *)malloc(sizeof(double) * C);
 #pragma omp for schedule(static)
         for (long bn = 0; bn < ntok; ++bn) {
