@@ -67,20 +67,26 @@
 
 namespace gdn {
 
-template <int KD, int C>
+// DUAL (C = 64, the forward only): the configuration for more chains than
+// compute units, two workgroups per CU -- four waves, two staging buffers
+// (about 78.5 KB of LDS at KD = 128).
+template <int KD, int C, bool DUAL = false>
 struct Chain1Shape {
     static constexpr int BV = 16;
     static constexpr int NTT = C / 16;        // token tiles
+    static_assert(!DUAL || NTT == 4, "the two-workgroup configuration runs 64-token chunks");
     // Waves (they go to the four SIMDs of a CU in turn):
     //   C = 64: 0 the chain; 4 idle (it only takes part in the barriers, so
     //           the chain has its SIMD to itself); 1, 2 the output of token
     //           tiles {3, 0} and {2, 1} (equal score work; each reads the
     //           start state once for its two tiles); 3, 5 the staging.
+    //   C = 64, DUAL: 0 the chain; 1, 2 the output as above; 3 the staging.
     //   C = 32: 0 the chain; 1, 2 the output of tiles 1, 0 and the staging.
-    static constexpr int IDLE = NTT == 4 ? 4 : -1;
-    static constexpr int NW = NTT == 4 ? 6 : 1 + NTT;
+    static constexpr int IDLE = NTT == 4 && !DUAL ? 4 : -1;
+    static constexpr int NW = NTT == 4 ? (DUAL ? 4 : 6) : 1 + NTT;
     static constexpr int NTHR = 64 * NW;
-    static constexpr int NLW = 2;             // staging ("loader") waves
+    static constexpr int NLW = DUAL ? 1 : 2;  // staging ("loader") waves
+    static constexpr int NB = DUAL ? 2 : 3;   // staging buffers
     static constexpr int NLOW = NTT * (NTT + 1) / 2;
     static constexpr int NKS = KD / 32;       // 32-wide steps over the key dim
     static constexpr int NST = KD / 16;       // state row tiles
@@ -108,10 +114,10 @@ struct Chain1Shape {
     // staging buffers are triple (index chunk % 3: staged two iterations
     // ahead), St and Vn double (index chunk & 1)
     static constexpr int OFF_KS = 0;
-    static constexpr int OFF_TB = OFF_KS + 3 * SZ_KS;
-    static constexpr int OFF_BV = OFF_TB + 3 * SZ_TB;
-    static constexpr int OFF_GATE = OFF_BV + 3 * SZ_BV;
-    static constexpr int OFF_ST = OFF_GATE + 3 * SZ_GATE;
+    static constexpr int OFF_TB = OFF_KS + NB * SZ_KS;
+    static constexpr int OFF_BV = OFF_TB + NB * SZ_TB;
+    static constexpr int OFF_GATE = OFF_BV + NB * SZ_BV;
+    static constexpr int OFF_ST = OFF_GATE + NB * SZ_GATE;
     static constexpr int OFF_VN = OFF_ST + 2 * SZ_ST;
     static constexpr int OFF_WT = OFF_VN + 2 * SZ_VN;             // W = (1 - m) v + m R (DeltaProduct first pass)
     static constexpr int BYTES = OFF_WT + 2 * SZ_VN;
@@ -143,10 +149,13 @@ __device__ __forceinline__ void dma16(const void *src, void *lds_base) {
     __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 16, 0, 0);
 }
 
-template <int KD, int C, int DPM = 0>
-__global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kernel(ChunkArgs args) {
-    using S = Chain1Shape<KD, C>;
+template <int KD, int C, int DPM = 0, bool DUAL = false>
+__global__ __launch_bounds__((Chain1Shape<KD, C, DUAL>::NTHR)) __attribute__((amdgpu_waves_per_eu(DUAL ? 2 : 1)))
+void chunk_chain1_kernel(ChunkArgs args) {
+    using S = Chain1Shape<KD, C, DUAL>;
     static_assert(DPM == 0 || C == 64, "DeltaProduct and backward passes run 64-token chunks");
+    static_assert(!DUAL || DPM == 0, "the two-workgroup configuration is the forward's");
+    static_assert(!DUAL || S::BYTES_PLAIN <= 80 * 1024, "two workgroups per CU");
     constexpr bool VIN = DPM == 2 || DPM == 4;  // values v' (fp32, read by the chain wave)
     constexpr bool ERR = DPM == 1 || DPM == 5;  // per-token errors and v' out
     constexpr bool BST = DPM >= 3;              // backward state pass: states and R out, no output
@@ -225,8 +234,8 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
         };
         if constexpr (VIN) load_vin(0);
         __syncthreads();
-        for (int c = 0, sq = 0; c < NT; ++c, sq = sq == 2 ? 0 : sq + 1) {
-            const int p = c & 1;                 // St, Vn; staging buffers: sq = c % 3
+        for (int c = 0, sq = 0; c < NT; ++c, sq = sq == S::NB - 1 ? 0 : sq + 1) {
+            const int p = c & 1;                 // St, Vn; staging buffers: sq = c % NB
             const u16 *ks = Ks(sq), *tb = Tb(sq), *bv = BVs(sq);
             const float *gp = gate(sq);
             // LDS operands of K S first (nothing here depends on the state), so
@@ -414,11 +423,11 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
         constexpr int OA = decltype(owa)::value, OB = decltype(owb)::value, LI = decltype(lic)::value;
         constexpr bool TILE = OA >= 0, LOAD = LI >= 0;
         // Stage chunk c (clamped to the last chunk; a past-the-end chunk lands in
-        // a buffer no one reads) into buffers c % 3.  Rows of the prep's
+        // a buffer no one reads) into buffers c % NB.  Rows of the prep's
         // outputs past T are zero; K and V rows past T are clamped to T-1:
         // they only meet zero columns of T diag(beta), and V_new is zero there.
         auto stage = [&](int c) {
-            const int p = c % 3;
+            const int p = c % S::NB;
             c = min(c, NT - 1);
 #pragma unroll
             for (int k = LI; k < NDMA; k += NLW) {
@@ -473,7 +482,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
                                   (tw(i) * (tw(i) + 1) / 2) * 64 + l;
 #pragma unroll
                 for (int tj = 0; tj <= tw(i); ++tj) pf[i][tj] = __builtin_bit_cast(u32x4, pc[tj * 64]);
-                egt[i] = gate(c % 3)[tw(i) * 16 + c16];
+                egt[i] = gate(c % S::NB)[tw(i) * 16 + c16];
                 if constexpr (ERR) {
                     const uint4 *ac = reinterpret_cast<const uint4 *>(args.atil) + ((size_t)bh * NT + c) * NLOW * 64 +
                                       (tw(i) * (tw(i) + 1) / 2) * 64 + l;
@@ -565,7 +574,8 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
         constexpr int NMINE = LOAD ? (NDMA - LI + NLW - 1) / NLW : 0;
         constexpr int NPF = (TW0 + 1) + (NTW > 1 ? TW1 + 1 : 0);   // P (and A~) fragment loads
         constexpr int NQP = TILE ? NTW * NKS + NPF * (ERR ? 2 : 1) : 0;
-        constexpr int NOWN = LOAD ? NMINE + NQP : 63;
+        // (two staging buffers: the staging of this iteration completes at its barrier)
+        constexpr int NOWN = LOAD ? (S::NB == 2 ? 0 : NMINE + NQP) : 63;
         static_assert(NOWN < 64, "6-bit vmcnt");
         // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, lgkmcnt(0), expcnt at its maximum
         constexpr int WAIT_IMM = (NOWN & 15) | ((NOWN >> 4) << 14) | 0x0070;
@@ -577,15 +587,15 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
         };
 
         // Iteration c (one barrier each): output of chunk c-1, operands of
-        // chunk c, staging of chunk c+2 (waited for one iteration later).
+        // chunk c, staging of chunk c+NB-1 (waited for NB-2 iterations later:
+        // one with three buffers, at its own barrier with two).
         if constexpr (LOAD) {
-            stage(0);
-            stage(1);
+            for (int j = 0; j < S::NB - 1; ++j) stage(j);
             __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0)
         }
         __syncthreads();
         if constexpr (TILE) load_qp(0);
-        if constexpr (LOAD) stage(2);
+        if constexpr (LOAD) stage(S::NB - 1);
         wave_barrier();
         for (int c = 1; c < NT; ++c) {
             if constexpr (TILE) {
@@ -593,7 +603,7 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
                 load_qp(c);
                 store_out(c - 1);
             }
-            if constexpr (LOAD) stage(c + 2);
+            if constexpr (LOAD) stage(c + S::NB - 1);
             wave_barrier();
         }
         if constexpr (TILE) {
@@ -704,7 +714,8 @@ __global__ __launch_bounds__((Chain1Shape<KD, C>::NTHR)) void chunk_chain1_kerne
         if (w == 1) out_wave(integral_constant<int, 3>{}, integral_constant<int, 0>{}, none{});
         if (w == 2) out_wave(integral_constant<int, 2>{}, integral_constant<int, 1>{}, none{});
         if (w == 3) out_wave(none{}, none{}, integral_constant<int, 0>{});
-        if (w == 5) out_wave(none{}, none{}, integral_constant<int, 1>{});
+        if constexpr (!DUAL)
+            if (w == 5) out_wave(none{}, none{}, integral_constant<int, 1>{});
     } else {
         static_assert(NTT == 2, "chunk of 32 or 64 tokens");
         if (w == 1) out_wave(integral_constant<int, 1>{}, none{}, integral_constant<int, 0>{});

@@ -142,6 +142,15 @@ hipError_t launch_chunk_fwd(const ChunkArgs &args, hipStream_t stream) {
     const int nvb = a.Dv / 16;
     const int grid = ((nbh + 7) / 8) * 8 * nvb;
     if constexpr (use_chain1<F32IN, KD, C, R>()) {
+        // more chains than compute units: the two-workgroups-per-CU
+        // configuration runs them in one round instead of two or more
+        if constexpr (C == 64) {
+            if (grid > num_cus()) {
+                hipLaunchKernelGGL((chunk_chain1_kernel<KD, C, 0, true>), dim3(grid), dim3(Chain1Shape<KD, C, true>::NTHR),
+                                   0, stream, a);
+                return hipGetLastError();
+            }
+        }
         hipLaunchKernelGGL((chunk_chain1_kernel<KD, C>), dim3(grid), dim3(Chain1Shape<KD, C>::NTHR), 0, stream, a);
     } else {
         hipLaunchKernelGGL((chunk_chain_kernel<F32IN, KD, C, R>), dim3(grid), dim3(512), 0, stream, a);

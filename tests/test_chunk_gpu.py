@@ -84,6 +84,43 @@ def test_gdn_chunk_small(gdn, case):
     _check(o, hT, oref, href, dtype, str(case))
 
 
+# More (batch, head, 16-column slice) chains than compute units: the state
+# pass runs in its two-workgroups-per-CU configuration (four waves, two
+# staging buffers).  Key widths 32...128 (112 padded), value widths 48...128,
+# ragged last chunks, one-token and one-chunk sequences, nonzero initial
+# state, fp32 and bf16 output.
+DUAL = [
+    # (B, T, H, Dk, Dv, h0_std, out)
+    (4, 300, 16, 128, 128, 0.05, "bf16"),
+    (2, 200, 40, 64, 64, 0.1, "f32"),
+    (3, 130, 32, 32, 128, 0.2, "bf16"),
+    (2, 257, 48, 112, 48, 0.1, "f32"),
+    (4, 1, 16, 128, 128, 0.1, "f32"),
+    (4, 64, 16, 128, 128, 0.1, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", DUAL, ids=lambda c: "B{}T{}H{}K{}V{}h{}{}".format(*c))
+def test_gdn_chunk_two_workgroups_per_cu(gdn, case):
+    import torch
+    B, T, H, Dk, Dv, h0s, out = case
+    _say(f"gdn_chunk_fwd two workgroups per CU {case}")
+    d = synth.gdn_inputs(B, T, H, Dk, Dv, seed=5000 + T + Dk + Dv + H, dtype="bf16", h0_std=h0s)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    o, hT = _run_gdn(gdn, d, "bf16", 64, scale=Dk ** -0.5, out_dtype=od)
+    oref, href = oracle.gdn_recurrent(d["q"], d["k"], d["v"], d["beta"], d["g"], Dk ** -0.5, d["h0"])
+    if out == "bf16":
+        bar = _bf16_out_bar(o, oref, TOL["bf16"])
+        err = np.abs(o.astype(np.float64) - oref)
+        _say(f"  o: max err / bar {np.max(err / bar):.3f}")
+        assert np.all(err <= bar)
+        eh = max_rel_err(hT, href)
+        _say(f"  hT: max rel err {eh:.3e}")
+        assert eh <= TOL["bf16"]
+    else:
+        _check(o, hT, oref, href, "bf16", str(case))
+
+
 # Long sequences over few heads, where the dispatch takes the segment-parallel
 # state pass (segment summaries, their composition, then the output pass per
 # segment; 24-29 segments here): key widths 32...128 (112 padded), value
