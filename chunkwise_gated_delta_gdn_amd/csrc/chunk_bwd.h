@@ -658,13 +658,19 @@ __device__ __forceinline__ bf16x8 tr_frag(const u16 *base, int r0, int c0) {
     const uint2 hi = __builtin_bit_cast(uint2, ld_tr16(base + swz_at<NPC>(ra + 4, col)));
     return __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
 }
-// Sum over the 16 lanes of a lane group (the columns of an accumulator tile).
+// Sum over the 16 lanes of a lane group (the columns of an accumulator tile)
+// by DPP moves, VALU only: pairs and quads by quad permutations, then 8 and 16
+// lanes by the half-row and row mirrors (each lane of a group already holds
+// the group's total, so the mirrored partner brings the other half's).
+template <int CTRL>
+__device__ __forceinline__ float dpp_plus(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float sum16(float v) {
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    v += __shfl_xor(v, 8, 64);
-    return v;
+    v = dpp_plus<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v = dpp_plus<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v = dpp_plus<0x141>(v);   // row_half_mirror
+    return dpp_plus<0x140>(v);  // row_mirror
 }
 // hi and lo bf16 of one value
 __device__ __forceinline__ void split1(float x, u16 &hi, u16 &lo) { split_bf16(x, hi, lo); }
@@ -742,8 +748,7 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
         }
     };
     // S and dS' as phase 3's A operands (lane (g, j): row f0 + j, value
-    // columns 32 mv + 8 g .. +7): NP3 loads
-    constexpr int NP3 = 16;
+    // columns 32 mv + 8 g .. +7)
     auto load_p3 = [&](int job) {
         const int bh = job / NT, c = job % NT;
         const size_t sbase = (((size_t)bh * NT + c) * KD + (w < nfs ? f0 : 0) + c16) * Dv + 8 * g;
@@ -763,9 +768,8 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
         const size_t rowk0 = ((size_t)b * T * H + h) * args.kst + args.koff, rowv0 = ((size_t)b * T * H + h) * Dv;
         const u16 *og = reinterpret_cast<const u16 *>(ba.dout) + rowv0;
         // ---- phase 0 ----
-        // phase 1's operands, the LDS-direct loads of K, Q and dO, then this
-        // wave's S and dS' loads; the wait below (at most NP3 outstanding)
-        // covers the LDS-direct loads and everything issued before them
+        // phase 1's operands and the LDS-direct loads of K, Q and dO, all
+        // waited for before the barrier; this wave's S and dS' loads follow it
         load_p1(job);
         asm volatile("" ::: "memory");
         {
@@ -789,7 +793,6 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
                 }
             }
             asm volatile("" ::: "memory");
-            load_p3(job);
             // M1, M2 (all four arrays, 32 KiB) and the per-tile partial slots cleared
             {
                 uint4 *z = reinterpret_cast<uint4 *>(smem + S::OFF_M1H);
@@ -811,9 +814,12 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
                 Bt[l] = ok ? args.beta[gi * args.bst + args.boff] : 0.f;
             }
             asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_waitcnt((NP3 & 15) | ((NP3 >> 4) << 14) | 0x0070);
+            __builtin_amdgcn_s_waitcnt(0x0070);
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
+            // S and dS' (half of the chunk's bytes) after the wait: issued
+            // earlier they share the memory path with the loads phase 1 needs
+            load_p3(job);
         }
 
         // ---- phase 1: value slice w ----
