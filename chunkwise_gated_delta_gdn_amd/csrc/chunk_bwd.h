@@ -708,11 +708,14 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
     const int f0 = 16 * w;
     const int ws = w < nvs ? w : 0;             // a valid value slice for waves past the last
 
-    // One chunk per workgroup (job = blockIdx.x).  Its phase-3 operands (S and
-    // dS', half of its bytes) are loaded after the LDS-direct loads and not
-    // waited for until phase 3, so their latency hides behind phases 1 and 2.
-    // (A persistent form, walking chunks with the next chunk's operands in
-    // flight, needs more registers than two waves per SIMD have.)
+    // One chunk per workgroup (job = blockIdx.x).  Loads in three steps, each
+    // behind the work that does not need it: phase 1's register operands
+    // (waited for in phase 0); K, Q and dO rows into LDS (LDS-direct, issued
+    // after phase 0, needed from phase 2); S and dS' (NP3 loads, issued after
+    // phase 1, needed in phase 3).  (A persistent form, walking chunks with
+    // the next chunk's operands in flight, needs more registers than two
+    // waves per SIMD have: the loop keeps its lane address arithmetic live
+    // and spills.)
     floatx4 rr[NTT], xr[NTT];
     bf16x8 tf[NTT][2];
     floatx4 dvr[NTT];
@@ -748,7 +751,8 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
         }
     };
     // S and dS' as phase 3's A operands (lane (g, j): row f0 + j, value
-    // columns 32 mv + 8 g .. +7)
+    // columns 32 mv + 8 g .. +7): NP3 loads
+    constexpr int NP3 = 16;
     auto load_p3 = [&](int job) {
         const int bh = job / NT, c = job % NT;
         const size_t sbase = (((size_t)bh * NT + c) * KD + (w < nfs ? f0 : 0) + c16) * Dv + 8 * g;
@@ -768,30 +772,13 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
         const size_t rowk0 = ((size_t)b * T * H + h) * args.kst + args.koff, rowv0 = ((size_t)b * T * H + h) * Dv;
         const u16 *og = reinterpret_cast<const u16 *>(ba.dout) + rowv0;
         // ---- phase 0 ----
-        // phase 1's operands and the LDS-direct loads of K, Q and dO, all
-        // waited for before the barrier; this wave's S and dS' loads follow it
+        // phase 1's operands, waited for before the barrier
         load_p1(job);
         asm volatile("" ::: "memory");
         {
             constexpr int NDK = S::SZ_KC / 1024, NDO = S::SZ_V / 1024;
             const u16 *kg = reinterpret_cast<const u16 *>(args.k) + rowk0;
             const u16 *qg = reinterpret_cast<const u16 *>(args.q) + rowk0;
-#pragma unroll
-            for (int k = w; k < 2 * NDK + NDO; k += S::NW) {
-                if (k < 2 * NDK) {
-                    const int kk = k % NDK, pos = kk * 64 + l, r = pos / NKC, sc = pos % NKC;
-                    const int t = t0 + r, pc = sc ^ kswz<NKC>(r);
-                    const u16 *src = (k < NDK ? kg : qg) + (size_t)t * tokk + (pc << 3);
-                    dma16(t < T ? static_cast<const void *>(src) : static_cast<const void *>(&kZero16),
-                          (k < NDK ? Kc : Qc) + kk * 512);
-                } else {
-                    const int kk = k - 2 * NDK, pos = kk * 64 + l, r = pos / NPV, sc = pos % NPV;
-                    const int t = t0 + r, pc = sc ^ kswz<NPV>(r);
-                    dma16(t < T && pc * 8 < Dv ? static_cast<const void *>(og + (size_t)t * tokv + (pc << 3))
-                                               : static_cast<const void *>(&kZero16),
-                          dOc + kk * 512);
-                }
-            }
             asm volatile("" ::: "memory");
             // M1, M2 (all four arrays, 32 KiB) and the per-tile partial slots cleared
             {
@@ -817,9 +804,23 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
             __builtin_amdgcn_s_waitcnt(0x0070);
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            // S and dS' (half of the chunk's bytes) after the wait: issued
-            // earlier they share the memory path with the loads phase 1 needs
-            load_p3(job);
+            // K, Q and dO rows, in flight through phase 1
+#pragma unroll
+            for (int k = w; k < 2 * NDK + NDO; k += S::NW) {
+                if (k < 2 * NDK) {
+                    const int kk = k % NDK, pos = kk * 64 + l, r = pos / NKC, sc = pos % NKC;
+                    const int t = t0 + r, pc = sc ^ kswz<NKC>(r);
+                    const u16 *src = (k < NDK ? kg : qg) + (size_t)t * tokk + (pc << 3);
+                    dma16(t < T ? static_cast<const void *>(src) : static_cast<const void *>(&kZero16),
+                          (k < NDK ? Kc : Qc) + kk * 512);
+                } else {
+                    const int kk = k - 2 * NDK, pos = kk * 64 + l, r = pos / NPV, sc = pos % NPV;
+                    const int t = t0 + r, pc = sc ^ kswz<NPV>(r);
+                    dma16(t < T && pc * 8 < Dv ? static_cast<const void *>(og + (size_t)t * tokv + (pc << 3))
+                                               : static_cast<const void *>(&kZero16),
+                          dOc + kk * 512);
+                }
+            }
         }
 
         // ---- phase 1: value slice w ----
@@ -907,7 +908,14 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
                     Xl[at] = lo;
                 }
         }
-        lds_barrier();
+        // S and dS' in flight through phase 2; the wait (at most NP3
+        // outstanding, loads complete in issue order) covers the K, Q, dO rows
+        asm volatile("" ::: "memory");
+        load_p3(job);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((NP3 & 15) | ((NP3 >> 4) << 14) | 0x0070);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
 
         // ---- phase 2: lower tiles of M1 (kind 0) and of dA, M2 (kind 1) ----
         for (int job = w; job < 20; job += S::NW) {
