@@ -980,8 +980,7 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
                 if (c16 == 0) (kind == 0 ? gr1 : gr2)[tj * C + t] = rs;
                 csum += wv[e];
             }
-            csum += __shfl_xor(csum, 16, 64);
-            csum += __shfl_xor(csum, 32, 64);
+            csum = add_xor32(add_xor16(csum));
             if (g == 0) (kind == 0 ? gc1 : gc2)[ti * C + s] = csum;
         }
         lds_barrier();
@@ -1000,8 +999,7 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
 #pragma unroll
                         for (int e = 0; e < 4; ++e) sdot += sf[mv][hh][e] * df[mv][hh][e];
             }
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) sdot += __shfl_xor(sdot, off, 64);
+            sdot = add_xor32(add_xor16(sum16(sdot)));
             if (l == 0) ss[w] = sdot;
             const float g2L = G2[C - 1];
             // K and Q as B operands (k = token, n = feature f0 + j), both 32-token steps
@@ -1087,10 +1085,8 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
                     *reinterpret_cast<floatx4 *>(dkp + (size_t)t * tokk) = dko;
                 }
                 // sums over the slice's 16 features: the lane's 4, then the 4 lane groups
-                p3 += __shfl_xor(p3, 16, 64);
-                p3 += __shfl_xor(p3, 32, 64);
-                ps += __shfl_xor(ps, 16, 64);
-                ps += __shfl_xor(ps, 32, 64);
+                p3 = add_xor32(add_xor16(p3));
+                ps = add_xor32(add_xor16(ps));
                 if (g == 0) {
                     g3[w * C + r] = p3;
                     gS[w * C + r] = ps;
@@ -1117,8 +1113,7 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
             }
             dG -= gsum;
             float tot = gsum;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) tot += __shfl_xor(tot, off, 64);
+            tot = add_xor32(add_xor16(sum16(tot)));
             if (r == C - 1) dG += tot + fast_exp2(G2[C - 1]) * sst;
             // dg_t = sum over t' >= t of dG_t'
 #pragma unroll

@@ -63,6 +63,24 @@ __device__ __forceinline__ shortx4 ld_tr16(const u16 *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p));
 }
 
+// x + (x from lane l ^ 16), x + (x from lane l ^ 32), in registers: gfx950's
+// permlane swaps exchange 16-lane rows 0 <-> 1 and 2 <-> 3 (the 32-lane
+// halves) between their two operands; with both operands x, every lane ends
+// up with its own value in one result and its partner's in the other.  (The
+// two results are copied out to plain variables before use.)
+__device__ __forceinline__ float add_xor16(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned a0 = r[0], a1 = r[1];
+    return __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned a0 = r[0], a1 = r[1];
+    return __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1);
+}
+
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
 // operations (lgkmcnt(0)) but leaves its global loads and stores in flight
 // (vmcnt and expcnt at their maxima), unlike __syncthreads(), which also
