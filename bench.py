@@ -316,8 +316,8 @@ def copy_probe(dev, mib=512, reps=5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="gdn", choices=("gdn", "gdn_long", "deltaproduct", "camera", "camera_reverse", "camera_den",
                              "gdn_bwd", "camera_bwd", "deltaproduct_bwd"),
