@@ -711,8 +711,8 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
     // One chunk per workgroup (job = blockIdx.x).  Loads in three steps, each
     // behind the work that does not need it: phase 1's register operands
     // (waited for in phase 0); K, Q and dO rows into LDS (LDS-direct, issued
-    // after phase 0, needed from phase 2); S and dS' (NP3 loads, issued after
-    // phase 1, needed in phase 3).  (A persistent form, walking chunks with
+    // right after them, needed from phase 2); S and dS' (NP3 loads, issued
+    // after phase 1, needed in phase 3).  (A persistent form, walking chunks with
     // the next chunk's operands in flight, needs more registers than two
     // waves per SIMD have: the loop keeps its lane address arithmetic live
     // and spills.)
@@ -721,6 +721,7 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
     floatx4 dvr[NTT];
     u32x4 atf[NLOW];
     floatx4 sf[4][2], df[4][2];
+    float graw = 0.f, braw = 0.f;               // wave NW - 1: g and beta of token t0 + l
     auto load_p1 = [&](int job) {
         const int bh = job / NT, c = job % NT, b = bh / H, h = bh % H, t0 = c * C;
         const size_t so = ((((size_t)bh * NT + c) * nvs + ws) * 64 + l) * NTT;
@@ -737,6 +738,13 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
 #pragma unroll
             for (int m = 0; m < 2; ++m)
                 if (2 * m <= tt) tf[tt][m] = ld8(tg + (tt * 16 + c16) * C + (4 * m + g) * 8);
+        if (w == S::NW - 1) {
+            const int t = t0 + l;
+            const bool ok = t < T;
+            const size_t gi = ((size_t)b * T + (ok ? t : 0)) * H + h;
+            graw = ok ? args.g[gi] : 0.f;
+            braw = ok ? args.beta[gi * args.bst + args.boff] : 0.f;
+        }
         if constexpr (DPE) {
             // the second pass's v' gradient of this wave's value slice (rows
             // tt*16 + 4g + e, column 16 ws + c16) and the A~ fragments
@@ -779,32 +787,10 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
             constexpr int NDK = S::SZ_KC / 1024, NDO = S::SZ_V / 1024;
             const u16 *kg = reinterpret_cast<const u16 *>(args.k) + rowk0;
             const u16 *qg = reinterpret_cast<const u16 *>(args.q) + rowk0;
-            asm volatile("" ::: "memory");
-            // M1, M2 (all four arrays, 32 KiB) and the per-tile partial slots cleared
-            {
-                uint4 *z = reinterpret_cast<uint4 *>(smem + S::OFF_M1H);
-                for (int i = tid; i < 4 * S::SZ_M / 16; i += S::NTHR) z[i] = uint4{0u, 0u, 0u, 0u};
-                float *zf = reinterpret_cast<float *>(smem + S::OFF_ZERO);
-                for (int i = tid; i < (S::OFF_ZEND - S::OFF_ZERO) / 4; i += S::NTHR) zf[i] = 0.f;
-            }
-            if (w == S::NW - 1) {
-                const int t = t0 + l;
-                const bool ok = t < T;
-                const size_t gi = ((size_t)b * T + (ok ? t : 0)) * H + h;
-                float gs = ok ? args.g[gi] : 0.f;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float y = __shfl_up(gs, off, 64);
-                    if (l >= off) gs += y;
-                }
-                G2[l] = gs * LOG2E;
-                Bt[l] = ok ? args.beta[gi * args.bst + args.boff] : 0.f;
-            }
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_waitcnt(0x0070);
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            // K, Q and dO rows, in flight through phase 1
+            // K, Q and dO rows (NDW LDS-direct loads per wave), in flight
+            // through the rest of phase 0 and phase 1
+            constexpr int NDW = (2 * NDK + NDO) / S::NW;
+            static_assert((2 * NDK + NDO) % S::NW == 0, "as many LDS-direct loads on every wave");
 #pragma unroll
             for (int k = w; k < 2 * NDK + NDO; k += S::NW) {
                 if (k < 2 * NDK) {
@@ -821,6 +807,29 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
                           dOc + kk * 512);
                 }
             }
+            asm volatile("" ::: "memory");
+            // M1, M2 (all four arrays, 32 KiB) and the per-tile partial slots cleared
+            {
+                uint4 *z = reinterpret_cast<uint4 *>(smem + S::OFF_M1H);
+                for (int i = tid; i < 4 * S::SZ_M / 16; i += S::NTHR) z[i] = uint4{0u, 0u, 0u, 0u};
+                float *zf = reinterpret_cast<float *>(smem + S::OFF_ZERO);
+                for (int i = tid; i < (S::OFF_ZEND - S::OFF_ZERO) / 4; i += S::NTHR) zf[i] = 0.f;
+            }
+            if (w == S::NW - 1) {
+                float gs = graw;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float y = __shfl_up(gs, off, 64);
+                    if (l >= off) gs += y;
+                }
+                G2[l] = gs * LOG2E;
+                Bt[l] = braw;
+            }
+            // phase 1's operands (older than the LDS-direct loads) complete
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt((NDW & 15) | ((NDW >> 4) << 14) | 0x0070);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
         }
 
         // ---- phase 1: value slice w ----
