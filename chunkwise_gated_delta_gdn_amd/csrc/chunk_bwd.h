@@ -528,32 +528,39 @@ __global__ __launch_bounds__(BChainShape<KD>::NTHR) void chunk_bchain_kernel(Bwd
         // slice, gates).  A chunk before the first lands in a buffer no one
         // reads (its data clamped to chunk 0).  K rows past T are clamped (they
         // meet zero beta); Q and dO rows past T are zero.
+        // Addresses: a per-call base of the chunk (scalar) plus a 32-bit
+        // per-lane offset (row < 64 times a row stride below 2^24: a 24-bit
+        // multiply), so that a load costs a few VALU operations rather than
+        // 64-bit multiplies (these waves' issue time is a large part of a step)
+        const unsigned tokq_u = (unsigned)tokq, tokv_u = (unsigned)tokv;
         auto stage = [&](int ca, int cb) {
             const int pa = ring(ca), pb = ring(cb);
             ca = ca < 0 ? 0 : ca;
             cb = cb < 0 ? 0 : cb;
+            const int rla = tlast - ca * C, rlb = tlast - cb * C;   // last valid row of each chunk
+            const u16 *kc = kg + (size_t)ca * C * tokq, *qc = qg + (size_t)cb * C * tokq;
+            const u16 *tc = tg + (size_t)ca * C * C, *oc = og + (size_t)cb * C * tokv;
 #pragma unroll
             for (int k = LI; k < NDMA; k += 2) {
                 if (k < NDK) {
                     const int pos = k * 64 + l, r = pos / NKC, sc = pos % NKC;
-                    const int t = min(ca * C + r, tlast), pc = sc ^ kswz<NKC>(r);
-                    dma16(kg + (size_t)t * tokq + (pc << 3), Ks(pa) + k * 512);
+                    const int pc = sc ^ kswz<NKC>(r);
+                    dma16(kc + (__umul24(min(r, rla), tokq_u) + (unsigned)(pc << 3)), Ks(pa) + k * 512);
                 } else if (k < NDK + NDT) {
                     const int kk = k - NDK, pos = kk * 64 + l, r = pos / (C / 8), sc = pos % (C / 8);
-                    dma16(tg + (size_t)ca * C * C + r * C + ((sc ^ (r & TSW)) << 3), Tt(pa) + kk * 512);
+                    dma16(tc + (unsigned)(r * C + ((sc ^ (r & TSW)) << 3)), Tt(pa) + kk * 512);
                 } else if (k == NDK + NDT) {
                     if (l < NGV) dma16(gtg + (size_t)ca * NGATE + l * 4, gA(pa));
                 } else if (k < NA + NDK) {
                     const int kk = k - NA, pos = kk * 64 + l, r = pos / NKC, sc = pos % NKC;
-                    const int t = cb * C + r, pc = sc ^ kswz<NKC>(r);
-                    dma16(t <= tlast ? static_cast<const void *>(qg + (size_t)t * tokq + (pc << 3))
-                                     : static_cast<const void *>(&kZero16),
+                    const int pc = sc ^ kswz<NKC>(r);
+                    dma16(r <= rlb ? static_cast<const void *>(qc + (__umul24(r, tokq_u) + (unsigned)(pc << 3)))
+                                   : static_cast<const void *>(&kZero16),
                           Qs(pb) + kk * 512);
                 } else if (k < NA + NDK + NDO) {
-                    const int kk = k - NA - NDK, pos = kk * 64 + l;
-                    const int t = cb * C + pos / 2;
-                    dma16(t <= tlast ? static_cast<const void *>(og + (size_t)t * tokv + (pos & 1) * 8)
-                                     : static_cast<const void *>(&kZero16),
+                    const int kk = k - NA - NDK, pos = kk * 64 + l, r = pos / 2;
+                    dma16(r <= rlb ? static_cast<const void *>(oc + (__umul24(r, tokv_u) + (unsigned)((pos & 1) * 8)))
+                                   : static_cast<const void *>(&kZero16),
                           dOs(pb) + kk * 512);
                 } else {
                     if (l < C / 4) dma16(gtg + (size_t)cb * NGATE + l * 4, gB(pb));   // e^G

@@ -191,10 +191,14 @@ hipError_t dp_bwd_launch(const BwdChunkArgs &ba, int dk, void *workspace, hipStr
 }
 
 // The chunkwise path takes bf16 inputs with Dk in {32, 64, 128} and Dv a
-// multiple of 32 up to 128.
-bool chunk_bwd_eligible(int T, int Dk, int Dv, int dtype) {
+// multiple of 32 up to 128, and token rows (H Dk and H Dv elements) below
+// 2^24 elements: its staging forms row offsets with 24-bit multiplies.
+bool chunk_bwd_strides_ok(int H, int K, int Dv) {
+    return (size_t)H * K < (1u << 24) && (size_t)H * Dv < (1u << 24);
+}
+bool chunk_bwd_eligible(int T, int H, int Dk, int Dv, int dtype) {
     return dtype == GDN_DTYPE_BF16 && T > 0 && (Dk == 32 || Dk == 64 || Dk == 128) && Dv % 32 == 0 && Dv >= 32 &&
-           Dv <= 128;
+           Dv <= 128 && chunk_bwd_strides_ok(H, Dk, Dv);
 }
 
 size_t chunk_bwd_workspace(int B, int T, int H, int Dk, int Dv) { return bwd_layout(B, T, H, Dk, Dv).total; }
@@ -252,7 +256,9 @@ hipError_t chunk_bwd_launch(const void *q, const void *k, const void *v, const f
 }  // namespace gdn
 
 extern "C" size_t deltaproduct_bwd_workspace_bytes(int B, int T, int H, int r, int dk, int Dv, int dtype) {
-    if (B < 0 || T < 0 || H < 0 || r != 2 || dtype != GDN_DTYPE_BF16 || !gdn::dp_bwd_eligible(dk, Dv)) return 0;
+    if (B < 0 || T < 0 || H < 0 || r != 2 || dtype != GDN_DTYPE_BF16 || !gdn::dp_bwd_eligible(dk, Dv) ||
+        !gdn::chunk_bwd_strides_ok(H, 2 * dk, Dv))
+        return 0;
     return gdn::dp_bwd_workspace(B, T, H, dk, Dv);
 }
 
@@ -302,6 +308,8 @@ extern "C" int deltaproduct_bwd(const void *q, const void *k, const void *v, con
     GDN_REQUIRE(workspace && gdn::aligned(workspace, 256), GDN_EINVAL,
                 "%s: workspace must be a 256-byte aligned device pointer", name);
     GDN_REQUIRE((size_t)B * H * ((T + 63) / 64) < (1u << 31), GDN_EUNSUPPORTED, "%s: too many chunks", name);
+    GDN_REQUIRE(gdn::chunk_bwd_strides_ok(H, 2 * sub_dk, Dv), GDN_EUNSUPPORTED,
+                "%s: token rows of H * K or H * Dv elements must be below 2^24", name);
     gdn::BwdChunkArgs ba = {};
     gdn::ChunkArgs &a = ba.a;
     a.q = q;

@@ -466,7 +466,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
 
 namespace gdn {
 // chunk_bwd.hip: the chunkwise MFMA path
-bool chunk_bwd_eligible(int T, int Dk, int Dv, int dtype);
+bool chunk_bwd_eligible(int T, int H, int Dk, int Dv, int dtype);
 size_t chunk_bwd_workspace(int B, int T, int H, int Dk, int Dv);
 hipError_t chunk_bwd_launch(const void *q, const void *k, const void *v, const float *beta, const float *g,
                             float scale, const float *h0, const void *dout, const float *dhT, float *dq, float *dk,
@@ -476,7 +476,7 @@ hipError_t chunk_bwd_launch(const void *q, const void *k, const void *v, const f
 
 extern "C" size_t gdn_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int dtype) {
     if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return 0;
-    if (gdn::chunk_bwd_eligible(T, Dk, Dv, dtype)) return gdn::chunk_bwd_workspace(B, T, H, Dk, Dv);
+    if (gdn::chunk_bwd_eligible(T, H, Dk, Dv, dtype)) return gdn::chunk_bwd_workspace(B, T, H, Dk, Dv);
     return gdn::bwd_workspace(B, T, H, Dk, Dv);
 }
 
@@ -508,7 +508,7 @@ extern "C" int gdn_bwd(const void *q, const void *k, const void *v, const float 
     }
     GDN_REQUIRE((!h0 || gdn::aligned(h0, 4)) && (!dhT || gdn::aligned(dhT, 4)) && (!dh0 || gdn::aligned(dh0, 4)),
                 GDN_EINVAL, "%s: misaligned state pointer", name);
-    const bool chunked = gdn::chunk_bwd_eligible(T, Dk, Dv, dtype);
+    const bool chunked = gdn::chunk_bwd_eligible(T, H, Dk, Dv, dtype);
     const size_t need = chunked ? gdn::chunk_bwd_workspace(B, T, H, Dk, Dv) : gdn::bwd_workspace(B, T, H, Dk, Dv);
     GDN_REQUIRE(workspace_bytes >= need, GDN_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", name,
                 workspace_bytes, need);

@@ -357,7 +357,7 @@ size_t gdn_prep_bwd_workspace_bytes(int B, int N, int H, int D);
  * chunk backward kernels of this rule: prepare_dv, dhu, dqkw, WY backward).
  *
  * bf16 inputs with Dk in {32, 64, 128} and Dv a multiple of 32 up to 128
- * (and T > 0) take the chunkwise path, 64-token chunks on MFMA: the chunk
+ * (and T > 0, H Dk and H Dv below 2^24) take the chunkwise path, 64-token chunks on MFMA: the chunk
  * prep (T = (I + A)^-1, its transpose, the transposed causal scores), the
  * forward state pass keeping every chunk's start state S and residual
  * R = V - e^G K S, the reverse pass over the chunks,
@@ -430,8 +430,8 @@ int gdn_bwd(const void *q, const void *k, const void *v,
  *   dlog_decay      (B, T, H)       float32
  *   dh0             (B, H, 2*dk, Dv) float32, nullable (not stored)
  * Supported: bf16 inputs, r = 2, M[0][0] = M[1][1] = 1 and M[0][1] = 0,
- * dk in {32, 64, 128}, Dv a multiple of 32 from 32 to 128, any T >= 0
- * (T = 0 gives dh0 = dhT).  Other masks, types and widths return
+ * dk in {32, 64, 128}, Dv a multiple of 32 from 32 to 128, H 2 dk and
+ * H Dv below 2^24, any T >= 0 (T = 0 gives dh0 = dhT).  Other masks, types and widths return
  * GDN_EUNSUPPORTED.  q, k, v, dout, dq, dk, dv 16-byte aligned; h0, dhT,
  * dh0 16-byte; the other tensors 4-byte; workspace 256-byte aligned.  The
  * work space (deltaproduct_bwd_workspace_bytes, 0 for an unsupported

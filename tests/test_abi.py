@@ -128,6 +128,22 @@ def test_bwd_rejects_bad_arguments(lib):
                        None, None, None, 0, 8, 2, 64, 64, 1, None, 0, None) == 0   # B = 0: nothing to do
 
 
+def test_bwd_chunk_path_row_stride_limit(lib):
+    # the chunkwise backward forms row offsets with 24-bit multiplies: token
+    # rows of H*Dk (or H*Dv) elements from 2^24 on leave it for the token
+    # path (whose work space is the fp32 query's) or, for the DeltaProduct
+    # backward, are refused (work space 0)
+    T, D = 64, 128
+    h_max = (1 << 24) // D
+    chunk_below = lib.gdn_bwd_workspace_bytes(1, T, h_max - 1, D, D, 1)
+    token_below = lib.gdn_bwd_workspace_bytes(1, T, h_max - 1, D, D, 0)
+    assert chunk_below > 0 and chunk_below != token_below
+    assert lib.gdn_bwd_workspace_bytes(1, T, h_max, D, D, 1) == lib.gdn_bwd_workspace_bytes(1, T, h_max, D, D, 0)
+    h_dp = (1 << 24) // (2 * D)
+    assert lib.deltaproduct_bwd_workspace_bytes(1, T, h_dp - 1, 2, D, D, 1) > 0
+    assert lib.deltaproduct_bwd_workspace_bytes(1, T, h_dp, 2, D, D, 1) == 0
+
+
 # ---------------------------------------------------------------------------
 # Every combination include/gdn.h declares supported has a kernel, and the
 # rest are refused: probed without launching (fake, aligned pointers and no
