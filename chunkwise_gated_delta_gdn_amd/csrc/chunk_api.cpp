@@ -58,6 +58,10 @@ size_t dp2_workspace(int dk, int B, int T, int H, int Dv, const gdn::ChunkImpl &
     return f > g ? f : g;
 }
 
+// Token rows (H*K or H*Dv elements) below 2^24: the state passes form
+// row offsets with 24-bit multiplies.
+bool rows_ok(int H, int K, int Dv) { return (size_t)H * K < (1u << 24) && (size_t)H * Dv < (1u << 24); }
+
 bool find_impl(int dtype, int r, int KD, int chunk, gdn::ChunkImpl *impl) {
     if (dtype == GDN_DTYPE_F32) return gdn::find_chunk_f32(KD, chunk, r, impl);
     if (r == 1) return gdn::find_chunk_bf16_r1(KD, chunk, impl);
@@ -87,6 +91,9 @@ int chunk_common(const void *q, const void *k, const void *v, const float *beta,
     GDN_REQUIRE(chunk == 16 || chunk == 32 || chunk == 64, GDN_EUNSUPPORTED,
                 "%s: chunk=%d (supported: 16, 32, 64)", name, chunk);
     GDN_REQUIRE(chunk * r <= 64, GDN_EUNSUPPORTED, "%s: chunk*r=%d exceeds 64", name, chunk * r);
+    GDN_REQUIRE(rows_ok(H, r * dk, Dv), GDN_EUNSUPPORTED,
+                "%s: token rows of H*K=%zu or H*Dv=%zu elements (at most 2^24 - 1)", name, (size_t)H * r * dk,
+                (size_t)H * Dv);
     GDN_REQUIRE(isfinite(scale), GDN_EINVAL, "%s: scale is not finite", name);
     const size_t ntok = (size_t)B * T * H;
     if (ntok > 0) {
@@ -192,7 +199,7 @@ extern "C" int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v
 
 extern "C" size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, int dtype) {
     gdn::ChunkImpl impl;
-    if (B < 0 || T < 0 || H < 0 || Dv <= 0 || Dk <= 0 || Dk % 16 || Dk > 256 ||
+    if (B < 0 || T < 0 || H < 0 || Dv <= 0 || Dk <= 0 || Dk % 16 || Dk > 256 || !rows_ok(H, Dk, Dv) ||
         !find_impl(dtype, 1, padded_key_width(1, Dk), chunk, &impl))
         return 0;
     return impl.workspace(B, T, H, Dv);
@@ -210,7 +217,7 @@ extern "C" int deltaproduct_chunk_fwd(const void *q, const void *k, const void *
 extern "C" size_t deltaproduct_chunk_fwd_workspace_bytes(int B, int T, int H, int r, int dk, int Dv,
                                                          int chunk, int dtype) {
     gdn::ChunkImpl impl;
-    if (B < 0 || T < 0 || H < 0 || Dv <= 0 || dk <= 0 || dk % 16 || r * dk > 256 ||
+    if (B < 0 || T < 0 || H < 0 || Dv <= 0 || dk <= 0 || dk % 16 || r * dk > 256 || !rows_ok(H, r * dk, Dv) ||
         !find_impl(dtype, r, padded_key_width(r, dk), chunk, &impl))
         return 0;
     if (r == 2 && dtype == GDN_DTYPE_BF16) return dp2_workspace(dk, B, T, H, Dv, impl);

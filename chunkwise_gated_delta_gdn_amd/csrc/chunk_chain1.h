@@ -426,24 +426,31 @@ void chunk_chain1_kernel(ChunkArgs args) {
         // a buffer no one reads) into buffers c % NB.  Rows of the prep's
         // outputs past T are zero; K and V rows past T are clamped to T-1:
         // they only meet zero columns of T diag(beta), and V_new is zero there.
+        // Addresses: the chunk's base (scalar) plus a 32-bit per-lane offset,
+        // a row below 64 times a token-row stride below 2^24 elements (the
+        // entry points refuse longer rows): a 24-bit multiply per load
+        // instead of 64-bit products (these waves' issue time counts).
         auto stage = [&](int c) {
             const int p = c % S::NB;
             c = min(c, NT - 1);
+            const int rl = tlast - c * C;       // last valid row of the chunk
+            const unsigned tokq_u = (unsigned)tokq, tokv_u = (unsigned)tokv;
+            const u16 *kc = kg + (size_t)c * C * tokq, *vc = vg + (size_t)c * C * tokv;
+            const u16 *tc = tg + (size_t)c * C * C;
 #pragma unroll
             for (int k = LI; k < NDMA; k += NLW) {
                 if (k < NDK) {                  // K: row r (token), stored piece j holds piece j ^ kswz(r)
                     const int pos = k * 64 + l, r = pos / NKC, sc = pos % NKC;
-                    const int t = min(c * C + r, tlast), pc = sc ^ kswz<NKC>(r);
-                    dma16(pc * 8 < kw ? static_cast<const void *>(kg + (size_t)t * tokq + (pc << 3))
+                    const int pc = sc ^ kswz<NKC>(r);
+                    dma16(pc * 8 < kw ? static_cast<const void *>(kc + (__umul24(min(r, rl), tokq_u) + (unsigned)(pc << 3)))
                                       : static_cast<const void *>(&kZero16),
                           Ks(p) + k * 512);
                 } else if (k < NDK + NDT) {     // T diag(beta): row r (token)
                     const int kk = k - NDK, pos = kk * 64 + l, r = pos / (C / 8), sc = pos % (C / 8);
-                    dma16(tg + (size_t)c * C * C + r * C + ((sc ^ (r & TSW)) << 3), Tb(p) + kk * 512);
+                    dma16(tc + (unsigned)(r * C + ((sc ^ (r & TSW)) << 3)), Tb(p) + kk * 512);
                 } else if (k < NDK + NDT + NDV) {   // V slice: token pos / 2, half pos % 2
                     const int kk = k - NDK - NDT, pos = kk * 64 + l;
-                    const int t = min(c * C + pos / 2, tlast);
-                    dma16(vg + (size_t)t * tokv + (pos & 1) * 8, BVs(p) + kk * 512);
+                    dma16(vc + (__umul24(min(pos / 2, rl), tokv_u) + (unsigned)((pos & 1) * 8)), BVs(p) + kk * 512);
                 } else {                            // gate table
                     if (l < NGV) dma16(gtg + (size_t)c * S::NGATE + l * 4, gate(p));
                 }

@@ -104,10 +104,11 @@ int gdn_abi_version(void);
  * Supported: Dk and Dv multiples of 16 with Dv <= 256 and
  *   bf16 inputs:  Dk <= 256 at chunk 16 or 32, Dk <= 128 at chunk 64;
  *   fp32 inputs:  Dk <= 256 at chunk 16 or 32, Dk <= 64 at chunk 64;
- * any T >= 0 (a last chunk shorter than `chunk` is handled).  A Dk that is
- * not a power of two runs the next power of two's kernels with the extra
- * features read as zero (e.g. Dk = 112 as 128).  16-byte aligned tensor
- * pointers.  Other combinations return GDN_EUNSUPPORTED.
+ * any T >= 0 (a last chunk shorter than `chunk` is handled); token rows of
+ * H*Dk and H*Dv elements below 2^24.  A Dk that is not a power of two runs
+ * the next power of two's kernels with the extra features read as zero
+ * (e.g. Dk = 112 as 128).  16-byte aligned tensor pointers.  Other
+ * combinations return GDN_EUNSUPPORTED (the work-space query returns 0).
  */
 int gdn_chunk_fwd(const void *q, const void *k, const void *v,
                   const float *beta, const float *log_decay, float scale,
@@ -166,7 +167,8 @@ int gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
  *   o          (B, T, H, Dv)   out_dtype
  * Supported: r = 1 as gdn_chunk_fwd; r = 2 with dk in {16, 32, 64, 128}
  * and chunk in {16, 32} (bf16 and fp32 inputs); Dv a multiple of 16 up to
- * 256.  Other combinations return GDN_EUNSUPPORTED.
+ * 256; H*r*dk and H*Dv below 2^24.  Other combinations return
+ * GDN_EUNSUPPORTED.
  */
 int deltaproduct_chunk_fwd(const void *q, const void *k, const void *v,
                            const float *beta, const float *log_decay,

@@ -128,6 +128,21 @@ def test_bwd_rejects_bad_arguments(lib):
                        None, None, None, 0, 8, 2, 64, 64, 1, None, 0, None) == 0   # B = 0: nothing to do
 
 
+def test_chunk_row_stride_limit(lib):
+    # the state passes form row offsets with 24-bit multiplies: token rows of
+    # 2^24 elements or more are refused before any launch (query 0, -2)
+    T, D = 64, 128
+    h_max = (1 << 24) // D
+    assert lib.gdn_chunk_fwd_workspace_bytes(1, T, h_max - 1, D, D, 64, 1) > 0
+    assert lib.gdn_chunk_fwd_workspace_bytes(1, T, h_max, D, D, 64, 1) == 0
+    h_dp = (1 << 24) // (2 * D)                  # two sub-keys of D
+    assert lib.deltaproduct_chunk_fwd_workspace_bytes(1, T, h_dp - 1, 2, D, D, 32, 1) > 0
+    assert lib.deltaproduct_chunk_fwd_workspace_bytes(1, T, h_dp, 2, D, D, 32, 1) == 0
+    fake = ctypes.c_void_p(4096)
+    assert _chunk(lib, T=T, H=h_max, Dk=D, Dv=D, q=fake, k=fake, v=fake, beta=fake, g=fake, o=fake) == -2
+    assert b"2^24" in lib.gdn_last_error()
+
+
 def test_bwd_chunk_path_row_stride_limit(lib):
     # the chunkwise backward forms row offsets with 24-bit multiplies: token
     # rows of H*Dk (or H*Dv) elements from 2^24 on leave it for the token
