@@ -468,6 +468,14 @@ void chunk_chain1_kernel(ChunkArgs args) {
         floatx4 op[NTW];                        // DPM 2: the first pass's output of those tokens
         u32x4 af[NTW][NTT];                     // ERR: A~ fragments of each tile (P's layout)
         floatx4 vq[NTW];                        // ERR: v' of the previous chunk (4 columns of one token)
+        // DPM 1 -> 2: the first pass's output in the order the second pass's
+        // output waves read it: per (chunk, value slice, token tile) a 1 KiB
+        // block, lane l's four values (token 16 tile + l%16, columns 4 (l/16)
+        // .. +3 of the slice) at 16 l bytes -- a whole-line load per wave
+        // instead of 64-byte pieces of 16 token rows (rows past T unused)
+        auto tile_off = [&](int c, int tile) {
+            return ((((size_t)bh * NT + c) * nvb + vb) * NTT + tile) * 256 + 4 * l;
+        };
         // operands of chunk c's output, used one iteration later
         auto load_qp = [&](int c) {
 #pragma unroll
@@ -497,7 +505,7 @@ void chunk_chain1_kernel(ChunkArgs args) {
                     for (int tj = 0; tj <= tw(i); ++tj) af[i][tj] = __builtin_bit_cast(u32x4, ac[tj * 64]);
                 }
                 if constexpr (DPM == 2)
-                    op[i] = *reinterpret_cast<const floatx4 *>(args.oprev + (((size_t)b * T + t) * H + h) * Dv + v0 + 4 * g);
+                    op[i] = *reinterpret_cast<const floatx4 *>(args.oprev + tile_off(c, tw(i)));
             }
         };
         // O^T of chunk c: a1 = S_start^T Q^T, a2 = V_new^T P^T (buffers c & 1);
@@ -557,7 +565,9 @@ void chunk_chain1_kernel(ChunkArgs args) {
                 const int tt = c * C + tw(i) * 16 + c16;
                 if (tt < T) {
                     const size_t off = (((size_t)b * T + tt) * H + h) * Dv + v0 + 4 * g;
-                    if (args.out_bf16)
+                    if constexpr (DPM == 1)     // the first pass's output, in tile order
+                        *reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(args.o) + tile_off(c, tw(i))) = ov[i];
+                    else if (args.out_bf16)
                         *reinterpret_cast<uint2 *>(reinterpret_cast<u16 *>(args.o) + off) =
                             uint2{cvt2_bf16(ov[i][0], ov[i][1]), cvt2_bf16(ov[i][2], ov[i][3])};
                     else

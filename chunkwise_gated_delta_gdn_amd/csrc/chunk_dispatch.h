@@ -186,7 +186,9 @@ size_t dp2_workspace_bytes(int B, int T, int H, int Dv) {
     const size_t prep = 2 * ((chunk_workspace_bytes<false, KD, C, 1>(B, T, H) + 255) & ~(size_t)255);
     const size_t at = chunk_pfrag_bytes<false, KD, C, 1>(B, T, H);
     const size_t vo = ((size_t)B * T * H * Dv * 4 + 255) & ~(size_t)255;
-    return prep + at + 2 * vo;
+    // the first output in tile order: whole 64-token chunks
+    const size_t oo = (size_t)B * H * ((T + C - 1) / C) * C * Dv * 4;
+    return prep + at + vo + oo;
 }
 
 template <int KD>
