@@ -96,7 +96,7 @@ DpBwdLayout dp_bwd_layout(int B, int T, int H, int dk, int Dv) {
     D.dxst = o;   o += al256(n * BC * Dv * 4);
     D.atil = o;   o += al256(n * NLOW * 64 * 16);
     D.atilT = o;  o += al256(n * NLOW * 64 * 16);
-    D.vprime = o; o += al256((size_t)B * T * H * Dv * 4);
+    D.vprime = o; o += al256(n * BC * Dv * 4);      // v' in tile order (whole chunks)
     D.total = o;
     return D;
 }

@@ -190,6 +190,12 @@ void chunk_chain1_kernel(ChunkArgs args) {
     auto St = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_ST + p * S::SZ_ST); };
     auto Vn = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_VN + p * S::SZ_VN); };
     auto Wt = [&](int p) { return reinterpret_cast<float *>(smem + S::OFF_WT + p * S::SZ_VN); };
+    // DeltaProduct hand-offs between passes in the work space (v' from
+    // DPM 1 / 5 to DPM 2 / 4, the first output from DPM 1 to DPM 2), in tile
+    // order: per (chunk, value slice, token tile) a 1 KiB block whose 16
+    // bytes at 16 l are output lane l's four values (token 16 tile + l%16,
+    // columns 4 (l/16) .. +3 of the slice).  Blocks cover whole chunks.
+    auto tile_base = [&](int c, int tile) { return ((((size_t)bh * NT + c) * nvb + vb) * NTT + tile) * 256; };
 
     if (w == 0) {
         // =================================================================
@@ -222,15 +228,16 @@ void chunk_chain1_kernel(ChunkArgs args) {
         // VIN: this lane's values v' (rows tt*16 + 4g + e, column c16) of
         // the next chunk, loaded one iteration ahead
         floatx4 vpre[NTT];
+        // (row 4g + e of token tile tt, column c16: the writer's lane
+        // 16 (c16 / 4) + 4g + e, its value c16 % 4; rows past T hold finite
+        // values that meet zero columns of T diag(beta) only)
         auto load_vin = [&](int c) {
-            const float *vp = args.vin + (((size_t)b * T) * H + h) * Dv + v0 + c16;
 #pragma unroll
-            for (int tt = 0; tt < NTT; ++tt)
+            for (int tt = 0; tt < NTT; ++tt) {
+                const float *vp = args.vin + tile_base(c, tt) + (c16 >> 2) * 64 + (c16 & 3);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = min(c * C + tt * 16 + 4 * g + e, tlast);
-                    vpre[tt][e] = vp[(size_t)t * H * Dv];
-                }
+                for (int e = 0; e < 4; ++e) vpre[tt][e] = vp[(4 * g + e) * 4];
+            }
         };
         if constexpr (VIN) load_vin(0);
         __syncthreads();
@@ -468,14 +475,9 @@ void chunk_chain1_kernel(ChunkArgs args) {
         floatx4 op[NTW];                        // DPM 2: the first pass's output of those tokens
         u32x4 af[NTW][NTT];                     // ERR: A~ fragments of each tile (P's layout)
         floatx4 vq[NTW];                        // ERR: v' of the previous chunk (4 columns of one token)
-        // DPM 1 -> 2: the first pass's output in the order the second pass's
-        // output waves read it: per (chunk, value slice, token tile) a 1 KiB
-        // block, lane l's four values (token 16 tile + l%16, columns 4 (l/16)
-        // .. +3 of the slice) at 16 l bytes -- a whole-line load per wave
-        // instead of 64-byte pieces of 16 token rows (rows past T unused)
-        auto tile_off = [&](int c, int tile) {
-            return ((((size_t)bh * NT + c) * nvb + vb) * NTT + tile) * 256 + 4 * l;
-        };
+        // DPM 1 -> 2 hand-offs in tile order (whole-line accesses per wave
+        // instead of 64-byte pieces of 16 token rows)
+        auto tile_off = [&](int c, int tile) { return tile_base(c, tile) + 4 * l; };
         // operands of chunk c's output, used one iteration later
         auto load_qp = [&](int c) {
 #pragma unroll
@@ -572,8 +574,9 @@ void chunk_chain1_kernel(ChunkArgs args) {
                             uint2{cvt2_bf16(ov[i][0], ov[i][1]), cvt2_bf16(ov[i][2], ov[i][3])};
                     else
                         *reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(args.o) + off) = ov[i];
-                    if constexpr (ERR) *reinterpret_cast<floatx4 *>(args.vout + off) = vq[i];
                 }
+                // v' of every row (rows past T finite: read as the next pass's values)
+                if constexpr (ERR) *reinterpret_cast<floatx4 *>(args.vout + tile_off(c, tw(i))) = vq[i];
             }
         };
 
@@ -693,9 +696,8 @@ void chunk_chain1_kernel(ChunkArgs args) {
                         floatx4 x;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) x[e] = wt[(4 * g + e) * LDVF] - mc * a3[e];
-                        const int t = c * C + twi(i) * 16 + c16;
-                        if (t < T)
-                            *reinterpret_cast<floatx4 *>(args.vout + (((size_t)b * T + t) * H + h) * Dv + v0 + 4 * g) = x;
+                        // v' of every row, in tile order (read as the next pass's values)
+                        *reinterpret_cast<floatx4 *>(args.vout + tile_base(c, twi(i)) + 4 * l) = x;
                     }
                 };
                 load_af(0);

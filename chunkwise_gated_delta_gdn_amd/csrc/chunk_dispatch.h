@@ -185,10 +185,9 @@ size_t dp2_workspace_bytes(int B, int T, int H, int Dv) {
     constexpr int C = 64;
     const size_t prep = 2 * ((chunk_workspace_bytes<false, KD, C, 1>(B, T, H) + 255) & ~(size_t)255);
     const size_t at = chunk_pfrag_bytes<false, KD, C, 1>(B, T, H);
-    const size_t vo = ((size_t)B * T * H * Dv * 4 + 255) & ~(size_t)255;
-    // the first output in tile order: whole 64-token chunks
-    const size_t oo = (size_t)B * H * ((T + C - 1) / C) * C * Dv * 4;
-    return prep + at + vo + oo;
+    // v' and the first output, in tile order: whole 64-token chunks
+    const size_t vo = (size_t)B * H * ((T + C - 1) / C) * C * Dv * 4;
+    return prep + at + 2 * vo;
 }
 
 template <int KD>
@@ -202,7 +201,7 @@ hipError_t launch_dp2(const ChunkArgs &args, hipStream_t stream) {
     a.pfrag = ws + chunk_tmat_bytes<false, KD, C, 1>(a.B, a.T, a.H);
     a.gtab = static_cast<char *>(a.pfrag) + chunk_pfrag_bytes<false, KD, C, 1>(a.B, a.T, a.H);
     char *at = ws + 2 * subws;
-    const size_t vo = ((size_t)a.B * a.T * a.H * a.Dv * 4 + 255) & ~(size_t)255;
+    const size_t vo = (size_t)nbh * NT * C * a.Dv * 4;    // v' in tile order (whole chunks)
     float *vprime = reinterpret_cast<float *>(at + chunk_pfrag_bytes<false, KD, C, 1>(a.B, a.T, a.H));
     float *o0 = reinterpret_cast<float *>(reinterpret_cast<char *>(vprime) + vo);
     const int nchunks = 2 * nbh * NT, nwg = (nchunks + 3) / 4;     // both sub-keys
