@@ -433,12 +433,12 @@ int gdn_bwd(const void *q, const void *k, const void *v,
  *   dh0             (B, H, 2*dk, Dv) float32, nullable (not stored)
  * Supported: bf16 inputs, r = 2, M[0][0] = M[1][1] = 1 and M[0][1] = 0,
  * dk in {32, 64, 128}, Dv a multiple of 32 from 32 to 128, H 2 dk and
- * H Dv below 2^24, any T >= 0 (T = 0 gives dh0 = dhT).  Other masks, types and widths return
- * GDN_EUNSUPPORTED.  q, k, v, dout, dq, dk, dv 16-byte aligned; h0, dhT,
+ * H Dv below 2^24, any T >= 0 (T = 0 gives dh0 = dhT).  Other masks,
+ * types and widths return GDN_EUNSUPPORTED.  q, k, v, dout, dq, dk, dv 16-byte aligned; h0, dhT,
  * dh0 16-byte; the other tensors 4-byte; workspace 256-byte aligned.  The
  * work space (deltaproduct_bwd_workspace_bytes, 0 for an unsupported
  * shape) holds gdn_bwd's chunkwise regions for each sub-key, A~ in two
- * fragment layouts and v' (B*T*H*Dv floats).
+ * fragment layouts and v' (B*H*ceil(T/64)*64*Dv floats).
  */
 size_t deltaproduct_bwd_workspace_bytes(int B, int T, int H, int r, int dk, int Dv, int dtype);
 int deltaproduct_bwd(const void *q, const void *k, const void *v,
