@@ -57,6 +57,7 @@ struct BwdChunkArgs {
     float *dsst;             // gradient of the state leaving each chunk, (B*H, NT, Dk, Dv) fp32
     float *dxst;             // dX per chunk, (B*H, NT, Dv/16, 64 lanes, 16) fp32, accumulator order
     const float *dvprev;     // DeltaProduct first pass: the second pass's gradient of v', (B, T, H, Dv)
+    int nfirst;              // chunk_bgrad_kernel: workgroups in its first round (one per CU)
 };
 
 // ---------------------------------------------------------------------------
@@ -692,6 +693,14 @@ __global__ __launch_bounds__(BGradShape<KD>::NTHR) void chunk_bgrad_kernel(BwdCh
     const ChunkArgs &args = ba.a;
     const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Every other workgroup of the first round starts ~12k cycles late.  All
+    // workgroups of a round would otherwise issue their loads together and
+    // then compute together, leaving HBM idle in between; the offset carries
+    // over to the later rounds (the next workgroup starts where one ends).
+    if ((int)blockIdx.x < ba.nfirst && (blockIdx.x & 1)) {
+        __builtin_amdgcn_s_sleep(127);
+        __builtin_amdgcn_s_sleep(63);
+    }
     const int T = args.T, H = args.H, Dv = args.Dv;
     const int NT = (T + C - 1) / C;
     const int nvs = Dv / 16, nmv = Dv / 32, nfs = KD / 16;

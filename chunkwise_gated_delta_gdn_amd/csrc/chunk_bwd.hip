@@ -66,6 +66,7 @@ hipError_t launch(BwdChunkArgs ba, char *ws, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_bchain_kernel<KD>), dim3(cgrid), dim3(BChainShape<KD>::NTHR), 0, s, ba);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    ba.nfirst = num_cus();
     hipLaunchKernelGGL((chunk_bgrad_kernel<KD>), dim3(nbh * NT), dim3(BGradShape<KD>::NTHR), 0, s, ba);
     return hipGetLastError();
 }
@@ -153,6 +154,7 @@ hipError_t launch_dp(BwdChunkArgs ba, char *ws, hipStream_t s) {
     // the backward of sub-key 1 (dv gets the gradient of v')
     hipLaunchKernelGGL((chunk_bchain_kernel<KD, false>), dim3(cgrid), dim3(BChainShape<KD>::NTHR), 0, s, b1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    b1.nfirst = num_cus();
     hipLaunchKernelGGL((chunk_bgrad_kernel<KD, false>), dim3(nbh * NT), dim3(BGradShape<KD>::NTHR), 0, s, b1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // the backward of sub-key 0 with dE = m dv'
@@ -161,6 +163,7 @@ hipError_t launch_dp(BwdChunkArgs ba, char *ws, hipStream_t s) {
     b0.dvprev = ba.dv;
     hipLaunchKernelGGL((chunk_bchain_kernel<KD, true>), dim3(cgrid), dim3(BChainShape<KD>::NTHR), 0, s, b0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    b0.nfirst = num_cus();
     hipLaunchKernelGGL((chunk_bgrad_kernel<KD, true>), dim3(nbh * NT), dim3(BGradShape<KD>::NTHR), 0, s, b0);
     return hipGetLastError();
 }
