@@ -325,8 +325,9 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="run only the copy calibration kernel")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(how the path would shard is described in DESIGN.md)"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1 "
+                                   "(every kernel here works on one device's share; nothing "
+                                   "crosses GPUs)"}))
         sys.exit(2)
 
     import numpy as np
