@@ -149,6 +149,20 @@ __device__ __forceinline__ void dma16(const void *src, void *lds_base) {
     __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_base, 16, 0, 0);
 }
 
+// Which LDS-direct loads of an iteration staging wave LI issues.  With two
+// staging waves at C = 64, wave 3 (alone on its SIMD) takes two of every three
+// and wave 5 (beside output wave 1) the third; otherwise they alternate.
+template <int NTT, int NLW, int LI>
+__host__ __device__ constexpr bool dma_mine(int k) {
+    return NLW == 1 || (NTT == 4 ? (LI == 0 ? k % 3 != 2 : k % 3 == 2) : k % NLW == LI);
+}
+template <int NTT, int NLW, int LI, int NDMA>
+__host__ __device__ constexpr int dma_count() {
+    int n = 0;
+    for (int k = 0; k < NDMA; ++k) n += dma_mine<NTT, NLW, LI>(k) ? 1 : 0;
+    return n;
+}
+
 template <int KD, int C, int DPM = 0, bool DUAL = false>
 __global__ __launch_bounds__((Chain1Shape<KD, C, DUAL>::NTHR)) __attribute__((amdgpu_waves_per_eu(DUAL ? 2 : 1)))
 void chunk_chain1_kernel(ChunkArgs args) {
@@ -411,7 +425,7 @@ void chunk_chain1_kernel(ChunkArgs args) {
     // Roles: OA, OB = token tiles of the output (-1: none); LI = staging
     // index (-1: none).  Staging of chunk c+2 in iteration c: NDMA LDS-direct wave
     // loads of 1 KiB (K, T diag(beta), the V slice, the gate table),
-    // load k on staging wave k % NLW, waited for before the barrier.
+    // load k on the staging wave dma_mine picks, waited for before the barrier.
     constexpr int NLW = S::NLW;
     constexpr int NLOW = NTT * (NTT + 1) / 2;
     constexpr int NGV = S::NGATE / 4;           // 16-byte vectors of a gate table
@@ -445,7 +459,8 @@ void chunk_chain1_kernel(ChunkArgs args) {
             const u16 *kc = kg + (size_t)c * C * tokq, *vc = vg + (size_t)c * C * tokv;
             const u16 *tc = tg + (size_t)c * C * C;
 #pragma unroll
-            for (int k = LI; k < NDMA; k += NLW) {
+            for (int k = 0; k < NDMA; ++k) {
+                if (!dma_mine<NTT, NLW, LI>(k)) continue;
                 if (k < NDK) {                  // K: row r (token), stored piece j holds piece j ^ kswz(r)
                     const int pos = k * 64 + l, r = pos / NKC, sc = pos % NKC;
                     const int pc = sc ^ kswz<NKC>(r);
@@ -591,7 +606,7 @@ void chunk_chain1_kernel(ChunkArgs args) {
         // issues unconditionally after the previous staging (its Q and P
         // loads, then this staging), so that staging is always complete.  An
         // output-only wave stages nothing and waits for none of its own.
-        constexpr int NMINE = LOAD ? (NDMA - LI + NLW - 1) / NLW : 0;
+        constexpr int NMINE = LOAD ? dma_count<NTT, NLW, (LI < 0 ? 0 : LI), NDMA>() : 0;
         constexpr int NPF = (TW0 + 1) + (NTW > 1 ? TW1 + 1 : 0);   // P (and A~) fragment loads
         constexpr int NQP = TILE ? NTW * NKS + NPF * (ERR ? 2 : 1) : 0;
         // (two staging buffers: the staging of this iteration completes at its barrier)
